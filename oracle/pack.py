@@ -1,0 +1,155 @@
+"""Int4 packing: the natural two-per-byte layout and the tile-packed layouts.
+
+Sources:
+  [P5] Format: a quantized layer stores its weight as an INT8 container of
+       shape [rows, cols/2] holding signed INT4 values.
+  [P1] intro: packed signed INT4 weights, two per byte.
+  [P3] Key Technical Optimizations, tile-packed weight format: weights are
+       reorganised from the natural layout into tiles of 128 output rows by
+       64 input channels, (N/128, K/64, 32, 128) bytes, with group scales laid
+       out (N/128, K/64, 128).
+
+Readings where the pages are silent:
+  * nibble order: byte j of a row holds element 2j in its low nibble and
+    element 2j+1 in its high nibble, each as a 4-bit two's-complement value
+    (unsigned 0..15 for unsigned / asymmetric codes);
+  * the outer tiling is the pages' [N/128][K/64] grid of 4096-byte tiles; the
+    byte order INSIDE a tile is this project's own choice, made so that one
+    64-lane matrix-core operand fragment is 512 (or 256) contiguous bytes:
+
+    W4A4 tile (symmetric int4, k-chunks of 16 values):
+        tile byte  nb*512 + l*8 + j,  nb in [0,8), l in [0,64), j in [0,8)
+        <- natural byte (row 16*nb + l%16 of the tile, byte 8*(l//16) + j of
+           the tile's 32-byte k slice)
+    W4A8 tile (asymmetric uint4, k-groups of 16):
+        tile byte  kg*1024 + nb*256 + l*4 + j,  kg, nb in [0,4), l in [0,64), j in [0,4)
+        <- natural byte (row 32*nb + l%32 of the tile, byte 8*kg + 4*(l//32) + j)
+
+  * per-group scales of the W4A4 g64 format: float32 [N/128][K/64][128]
+    (the pages' wscales layout); W4A8 g16 scales (fp16) and zero points
+    (one byte each) : [N/128][K/64][4][128].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    """codes int [rows, K] (signed in [-8,7] or unsigned in [0,15]) -> uint8 [rows, K/2]."""
+    c = np.asarray(codes).astype(np.int64)
+    rows, K = c.shape
+    if K % 2:
+        raise ValueError("K must be even")
+    lo = c[:, 0::2] & 0xF
+    hi = c[:, 1::2] & 0xF
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_int4(packed: np.ndarray, signed: bool = True) -> np.ndarray:
+    """uint8 [rows, K/2] -> int8/uint8 [rows, K] (inverse of pack_int4)."""
+    p = np.asarray(packed, dtype=np.uint8).astype(np.int64)
+    rows, half = p.shape
+    out = np.empty((rows, 2 * half), dtype=np.int64)
+    out[:, 0::2] = p & 0xF
+    out[:, 1::2] = (p >> 4) & 0xF
+    if signed:
+        out = np.where(out >= 8, out - 16, out)
+        return out.astype(np.int8)
+    return out.astype(np.uint8)
+
+
+def _check_tiles(N: int, K: int):
+    if N % 128 or K % 64:
+        raise ValueError("tile packing needs N % 128 == 0 and K % 64 == 0")
+
+
+def tile_pack_w4a4(packed: np.ndarray) -> np.ndarray:
+    """natural uint8 [N, K/2] -> tile-packed uint8 [N/128, K/64, 4096]."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    N, half = packed.shape
+    K = 2 * half
+    _check_tiles(N, K)
+    out = np.empty((N // 128, K // 64, 4096), dtype=np.uint8)
+    for tn in range(N // 128):
+        for kt in range(K // 64):
+            tile = packed[128 * tn:128 * tn + 128, 32 * kt:32 * kt + 32]   # [128 rows, 32 bytes]
+            for nb in range(8):
+                for lane in range(64):
+                    row = 16 * nb + lane % 16
+                    col = 8 * (lane // 16)
+                    o = nb * 512 + lane * 8
+                    out[tn, kt, o:o + 8] = tile[row, col:col + 8]
+    return out
+
+
+def tile_unpack_w4a4(tiles: np.ndarray) -> np.ndarray:
+    """Inverse of tile_pack_w4a4."""
+    tiles = np.asarray(tiles, dtype=np.uint8)
+    TN, TK, _ = tiles.shape
+    out = np.empty((TN * 128, TK * 32), dtype=np.uint8)
+    for tn in range(TN):
+        for kt in range(TK):
+            for nb in range(8):
+                for lane in range(64):
+                    row = 128 * tn + 16 * nb + lane % 16
+                    col = 32 * kt + 8 * (lane // 16)
+                    o = nb * 512 + lane * 8
+                    out[row, col:col + 8] = tiles[tn, kt, o:o + 8]
+    return out
+
+
+def tile_pack_w4a8(packed: np.ndarray) -> np.ndarray:
+    """natural uint8 [N, K/2] (uint4 codes) -> tile-packed uint8 [N/128, K/64, 4096]."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    N, half = packed.shape
+    K = 2 * half
+    _check_tiles(N, K)
+    out = np.empty((N // 128, K // 64, 4096), dtype=np.uint8)
+    for tn in range(N // 128):
+        for kt in range(K // 64):
+            tile = packed[128 * tn:128 * tn + 128, 32 * kt:32 * kt + 32]
+            for kg in range(4):
+                for nb in range(4):
+                    for lane in range(64):
+                        row = 32 * nb + lane % 32
+                        col = 8 * kg + 4 * (lane // 32)
+                        o = kg * 1024 + nb * 256 + lane * 4
+                        out[tn, kt, o:o + 4] = tile[row, col:col + 4]
+    return out
+
+
+def tile_unpack_w4a8(tiles: np.ndarray) -> np.ndarray:
+    tiles = np.asarray(tiles, dtype=np.uint8)
+    TN, TK, _ = tiles.shape
+    out = np.empty((TN * 128, TK * 32), dtype=np.uint8)
+    for tn in range(TN):
+        for kt in range(TK):
+            for kg in range(4):
+                for nb in range(4):
+                    for lane in range(64):
+                        row = 128 * tn + 32 * nb + lane % 32
+                        col = 32 * kt + 8 * kg + 4 * (lane // 32)
+                        o = kg * 1024 + nb * 256 + lane * 4
+                        out[row, col:col + 4] = tiles[tn, kt, o:o + 4]
+    return out
+
+
+def tile_pack_g64_scales(scales: np.ndarray) -> np.ndarray:
+    """float32 [N, K/64] -> [N/128, K/64, 128]: element (tn, kt, i) is the
+    scale of row 128*tn + i for k-group kt."""
+    s = np.asarray(scales, dtype=np.float32)
+    N, G = s.shape
+    return np.ascontiguousarray(s.reshape(N // 128, 128, G).transpose(0, 2, 1))
+
+
+def tile_pack_g16(per_group: np.ndarray) -> np.ndarray:
+    """[N, K/16] per-(row, 16-group) values -> [N/128, K/64, 4, 128]:
+    element (tn, kt, kg, i) belongs to row 128*tn + i and group 4*kt + kg."""
+    a = np.asarray(per_group)
+    N, G = a.shape
+    return np.ascontiguousarray(a.reshape(N // 128, 128, G // 4, 4).transpose(0, 2, 3, 1))
+
+
+def pack_zeros_u4(zeros: np.ndarray) -> np.ndarray:
+    """uint4 zero points [N, K/16] -> natural two-per-byte [N, K/32]."""
+    return pack_int4(zeros.astype(np.int64))

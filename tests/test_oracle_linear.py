@@ -1,0 +1,123 @@
+"""Pins of oracle.linear (epilogues and the composed linears).
+
+Closed forms and special cases:
+  * unit scales give y = acc exactly;
+  * a g64 epilogue whose group scales are all equal reduces to the scalar one;
+  * an exactly low-rank W gives an all-zero residual and y = low-rank branch;
+  * the unsigned shift correction recovers the unshifted product;
+  * the quantized linears approximate the float product, ranked
+    int8 < w4a8 < w4a4 by relative error as on the W4A8-ConvRot card's
+    per-layer table (a ranking, not a threshold);
+  * rotation of BOTH operands is what makes W4A4 survive outlier channels
+    (the purpose of ConvRot, [P1] intro).
+"""
+import json
+import os
+
+import numpy as np
+
+from oracle import linear, gemm, quant, pack
+import workloads as wl
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_facts.json")))
+
+
+def _rel(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def test_unit_scales_identity():
+    g = np.random.default_rng(30)
+    acc = g.integers(-600000, 600000, size=(7, 9))
+    y = linear.epilogue_scalar(acc, np.ones(1, np.float32), "tensor", np.ones(1, np.float32), "tensor")
+    assert np.array_equal(y, acc.astype(np.float32))
+
+
+def test_g64_equal_scales_reduce_to_scalar():
+    g = np.random.default_rng(31)
+    a = g.integers(-7, 8, size=(4, 256))
+    w = g.integers(-7, 8, size=(5, 256))
+    P = gemm.group_partials(a, w, 64)
+    sa, sw = np.float32(0.37), np.float32(0.011)
+    y1 = linear.epilogue_g64(P, np.full((4, 4), sa), np.full((5, 4), sw))
+    y2 = linear.epilogue_scalar(P.sum(axis=2), np.array([sa]), "tensor", np.array([sw]), "tensor")
+    assert np.array_equal(y1, y2)
+
+
+def test_exact_low_rank_weight():
+    g = np.random.default_rng(32)
+    M, N, K, R = 8, 128, 256, 4
+    l1 = wl.bf16_bits_from_f32((g.standard_normal((N, R)) * 0.1).astype(np.float32))
+    l2 = wl.bf16_bits_from_f32(np.eye(R, K, dtype=np.float32))           # exact low rank
+    w = wl.bf16_bits_from_f32(wl.f32_from_bf16_bits(l1) @ wl.f32_from_bf16_bits(l2))
+    resid = wl.bf16_bits_from_f32(wl.f32_from_bf16_bits(w) - wl.f32_from_bf16_bits(l1) @ wl.f32_from_bf16_bits(l2))
+    x = wl.activation(99, 0, M, K)
+    out = linear.w4a4_linear(x, resid, rot_group=0, a_gran="row_group", w_gran="row_group",
+                             group=64, l1_bits=l1, l2_bits=l2)
+    assert np.all(out["w"]["values"] == 0)
+    lr = wl.f32_from_bf16_bits(x).astype(np.float64) @ (wl.f32_from_bf16_bits(l1).astype(np.float64)
+                                                        @ wl.f32_from_bf16_bits(l2).astype(np.float64)).T
+    assert _rel(out["y"], lr) < 4e-3            # only the bf16 rounding of la remains
+
+
+def test_shift_correction_recovers_unshifted_product():
+    shift = GOLD["post_gelu_shift"]["value"]
+    M, N, K = 16, 128, 512
+    x = wl.gelu_activation(98, 0, M, K)
+    w = wl.weight(98, 1, N, K)
+    ref = linear.float_linear(x, w)
+    shifted = linear.w4a4_linear(x, w, rot_group=0, a_gran="row_group", w_gran="row_group",
+                                 group=64, shift=shift)
+    # without the correction the output is off by shift * rowsum(W_hat)
+    assert _rel(shifted["y"], ref) < 0.2
+    wsum = shifted["w"]["wsum"].astype(np.float64)
+    uncorrected = shifted["y"] + shift * wsum[None, :]
+    assert _rel(uncorrected, ref) > 2 * _rel(shifted["y"], ref)
+
+
+def test_error_ranking_matches_pages():
+    ranking = GOLD["per_layer_rel_error_median"]["value"]
+    assert ranking["bf16"] < ranking["w4a8"] < ranking["w4a4"]
+    M, N, K = 64, 256, 512
+    x = wl.activation(97, 0, M, K)
+    w = wl.weight(97, 1, N, K)
+    ref = linear.float_linear(x, w)
+    e8 = _rel(linear.int8_linear(x, w)["y"], ref)
+    e48 = _rel(linear.w4a8_linear(x, w)["y"], ref)
+    e44 = _rel(linear.w4a4_linear(x, w)["y"], ref)
+    assert e8 < e48 < e44
+    assert e44 < 0.5
+
+
+def test_rotation_rescues_outliers():
+    M, N, K = 64, 256, 512
+    x = wl.activation(96, 0, M, K, n_outliers=5, outlier_scale=20.0)
+    w = wl.weight(96, 1, N, K)
+    ref = linear.float_linear(x, w)
+    rot = _rel(linear.w4a4_linear(x, w, rot_group=256)["y"], ref)
+    plain = _rel(linear.w4a4_linear(x, w, rot_group=0)["y"], ref)
+    assert rot < plain
+
+
+def test_raw_equals_exact_integer_product():
+    M, N, K = 32, 128, 512
+    x = wl.activation(95, 0, M, K)
+    w = wl.weight(95, 1, N, K)
+    out = linear.w4a4_linear(x, w)
+    qa = pack.unpack_int4(out["x"]["codes"], True)
+    qw = pack.unpack_int4(pack.tile_unpack_w4a4(out["w"]["tiles"]), True)
+    assert np.array_equal(out["raw"], qa.astype(np.int64) @ qw.astype(np.int64).T)
+    o8 = linear.w4a8_linear(x, w)
+    z = np.repeat(o8["w"]["zeros"].astype(np.int64), 16, axis=1)
+    qw8 = pack.unpack_int4(pack.tile_unpack_w4a8(o8["w"]["tiles"]), False).astype(np.int64) - z
+    assert np.array_equal(o8["raw"], o8["x"]["values"].astype(np.int64) @ qw8.T)
+
+
+def test_lora_down_rounding():
+    x = wl.activation(94, 0, 4, 256)
+    l2 = wl.weight(94, 1, 8, 256, std=0.05)
+    la32 = linear.lora_down(x, l2, act_f32=True)
+    la16 = linear.lora_down(x, l2, act_f32=False)
+    exact = wl.f32_from_bf16_bits(x).astype(np.float64) @ wl.f32_from_bf16_bits(l2).astype(np.float64).T
+    assert np.allclose(la32, exact, rtol=1e-6, atol=1e-6)
+    assert np.array_equal(la16, wl.f32_from_bf16_bits(wl.bf16_bits_from_f32(la32)))

@@ -1,0 +1,125 @@
+"""Pins of oracle.pack and oracle.gemm.
+
+[P5] Format fixes the natural container ([rows, cols/2] bytes holding signed
+INT4); [P3] Tile-Packed Weight Format fixes the outer tiling (N/128, K/64)
+of 32x128-byte tiles and the (N/128, K/64, 128) group-scale layout. The
+integer GEMM is pinned against a pure-Python triple loop and numpy's int64
+matmul (a library routine), independently of the float64-BLAS evaluation.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import pack, gemm
+
+HERE = os.path.dirname(__file__)
+GOLD = json.load(open(os.path.join(HERE, "golden", "pages_facts.json")))
+
+
+def _read_pack_example():
+    codes, byts = {}, {}
+    for line in open(os.path.join(HERE, "golden", "pack_int4_example.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        key, vals = line.split(":")
+        kind, idx = key.split()
+        if kind == "codes":
+            codes[int(idx)] = [int(t) for t in vals.split()]
+        else:
+            byts[int(idx)] = [int(t, 16) for t in vals.split()]
+    return (np.array([codes[0], codes[1]]), np.array([byts[0], byts[1]], dtype=np.uint8))
+
+
+def test_pack_int4_hand_example():
+    codes, expect = _read_pack_example()
+    got = pack.pack_int4(codes)
+    assert got.shape == (2, 4)                      # [rows, cols/2]
+    assert np.array_equal(got, expect)
+    assert np.array_equal(pack.unpack_int4(got, signed=True), codes)
+
+
+def test_pack_round_trip_signed_and_unsigned():
+    g = np.random.default_rng(20)
+    s = g.integers(-8, 8, size=(5, 64))
+    u = g.integers(0, 16, size=(5, 64))
+    assert np.array_equal(pack.unpack_int4(pack.pack_int4(s), True), s)
+    assert np.array_equal(pack.unpack_int4(pack.pack_int4(u), False), u)
+
+
+def test_tile_pack_w4a4_shape_position_and_round_trip():
+    shape = GOLD["tile_shape_bytes"]["value"]
+    assert shape[2] * shape[3] == 4096
+    g = np.random.default_rng(21)
+    nat = g.integers(0, 256, size=(256, 128), dtype=np.uint8)          # N=256, K=256
+    t = pack.tile_pack_w4a4(nat)
+    assert t.shape == (256 // 128, 256 // 64, 4096)
+    assert np.array_equal(pack.tile_unpack_w4a4(t), nat)
+    # hand position check: natural (row 17, byte 9) of tile (0, 0):
+    # row 17 -> n-block 1, lane%16 = 1; byte 9 -> chunk 1, j = 1 -> lane 17,
+    # offset 1*512 + 17*8 + 1 = 649
+    assert t[0, 0, 649] == nat[17, 9]
+    # natural (row 128+5, byte 32*3 + 30) -> tile (1, 3): nb 0, lane 3*16+5 = 53, j 6
+    assert t[1, 3, 53 * 8 + 6] == nat[133, 126]
+
+
+def test_tile_pack_w4a8_position_and_round_trip():
+    g = np.random.default_rng(22)
+    nat = g.integers(0, 256, size=(128, 64), dtype=np.uint8)           # N=128, K=128
+    t = pack.tile_pack_w4a8(nat)
+    assert np.array_equal(pack.tile_unpack_w4a8(t), nat)
+    # natural (row 70, byte 32 + 13): k-tile 1, byte 13 -> kg 1, half 1 (bytes 12..15), j 1;
+    # row 70 -> nb 2, lane%32 = 6 -> lane 32 + 6 = 38; offset 1024 + 2*256 + 38*4 + 1
+    assert t[0, 1, 1024 + 512 + 152 + 1] == nat[70, 45]
+
+
+def test_group_scale_tiles():
+    s = np.arange(256 * 8, dtype=np.float32).reshape(256, 8)      # N=256, K=512 (g64)
+    t = pack.tile_pack_g64_scales(s)
+    assert t.shape == (2, 8, 128)
+    assert t[1, 5, 7] == s[128 + 7, 5]
+    z = np.arange(128 * 16).reshape(128, 16)                        # N=128, K=256 (g16)
+    tz = pack.tile_pack_g16(z)
+    assert tz.shape == (1, 4, 4, 128)
+    assert tz[0, 2, 3, 9] == z[9, 11]
+
+
+def _triple_loop(a, b):
+    M, K = len(a), len(a[0])
+    N = len(b)
+    return [[sum(int(a[m][k]) * int(b[n][k]) for k in range(K)) for n in range(N)] for m in range(M)]
+
+
+def test_int_gemm_vs_triple_loop():
+    g = np.random.default_rng(23)
+    a = g.integers(-7, 8, size=(3, 40))
+    b = g.integers(-7, 8, size=(5, 40))
+    assert np.array_equal(gemm.int_gemm(a, b), np.array(_triple_loop(a.tolist(), b.tolist())))
+
+
+def test_int_gemm_vs_numpy_int64():
+    g = np.random.default_rng(24)
+    a = g.integers(-127, 128, size=(33, 3072))
+    b = g.integers(-127, 128, size=(70, 3072))
+    assert np.array_equal(gemm.int_gemm(a, b), a.astype(np.int64) @ b.astype(np.int64).T)
+
+
+def test_group_partials_sum_and_zero_points():
+    g = np.random.default_rng(25)
+    a = g.integers(-127, 128, size=(4, 64))
+    w = g.integers(0, 16, size=(6, 64))
+    z = g.integers(0, 16, size=(6, 4))
+    P = gemm.group_partials(a, w, 16, z)
+    assert P.shape == (4, 6, 4)
+    wz = w - np.repeat(z, 16, axis=1)
+    assert np.array_equal(P.sum(axis=2), a @ wz.T)
+    # one entry by hand-level brute force
+    m, n, gg = 2, 3, 1
+    assert P[m, n, gg] == sum(int(a[m, k]) * (int(w[n, k]) - int(z[n, gg])) for k in range(16, 32))
+
+
+def test_exactness_bound_guard():
+    a = np.full((1, 8), 2 ** 26, dtype=np.int64)
+    with pytest.raises(ValueError):
+        gemm.int_gemm(a, a)
