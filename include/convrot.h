@@ -1,0 +1,267 @@
+/*
+ * convrot.h - C ABI of the ConvRot-rotated low-bit quantized linear layer
+ *             for AMD Instinct MI355X (gfx950).
+ *
+ * The method (from the pages this library follows, cited by title/section):
+ *   - "Qwen-Image-Edit-2511 - INT4 tensorwise W4A4 (+ConvRot, mixed int8
+ *     fallback)", intro and Measurements: weights are packed signed INT4 (two
+ *     per byte), rotated offline with a group-256 regular Hadamard (ConvRot);
+ *     activations are rotated online with the same matrix and quantized
+ *     dynamically; an INT8 tensorwise format serves the sensitive layers.
+ *   - "Qwen-Image-Edit-2511-W4A8-ConvRot", build table / file layout:
+ *     asymmetric 4-bit weights, group 16, ConvRot 256, 8-bit activations.
+ *   - "Qwen-Image-Edit-2511 INT4 (ComfyUI Optimized)", Quantization Method,
+ *     Key Technical Optimizations, Kernel Engineering: the two-call structure
+ *     (quantize, then scaled matmul), the tile-packed weight format
+ *     (N/128, K/64, 32, 128) with (N/128, K/64, 128) group scales, a low-rank
+ *     branch whose down-projection is computed once with the quantization
+ *     and whose up-projection is fused into the GEMM epilogue, an unsigned
+ *     post-GELU activation path shifted by +0.171875, and an FP32 switch for
+ *     the low-rank activations.
+ *   - "Qwen3-4B - ConvRot W4A4 (ComfyUI text encoder)", Format / Hardware:
+ *     the [rows, cols/2] INT4 container with a float32 [rows] scale, and the
+ *     rule that a missing native path is refused rather than replaced by
+ *     dequantized math.
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer owned by the caller. The library
+ *     never allocates, frees or synchronizes; all work is enqueued on `stream`
+ *     (NULL = the default stream) and returns immediately.
+ *   - Arguments are validated BEFORE any HIP call. On any error nothing is
+ *     enqueued and a status is returned; the library never aborts.
+ *   - The device must be gfx950; otherwise CR_ERR_UNSUPPORTED_ARCH. There is
+ *     no fallback path of any kind (no dequantized or CPU math).
+ *   - bf16 = IEEE bfloat16 bit patterns; all matrices are row-major with the
+ *     leading dimension in elements; every pointer must be 16-byte aligned.
+ *   - int4 codes, natural layout: [rows, K/2] bytes, element 2j in the low
+ *     nibble of byte j, element 2j+1 in the high nibble, two's complement for
+ *     signed codes (unsigned 0..15 for unsigned / asymmetric codes).
+ *   - Rotation: the unnormalised regular Hadamard H (entries +-1, H H^T =
+ *     256 I, rows summing to 16, H = (D S D) with S Sylvester and D[j] =
+ *     (-1)^(#zero base-4 digits of j)) is applied to each contiguous group of
+ *     256 columns, in float32, in the butterfly order h = 1, 2, ..., 128.
+ *     The orthonormal factor 1/16 is carried by the stored scale, so
+ *     scale * code approximates the orthonormally rotated value.
+ *   - Quantization (symmetric): A = max |v| over the scale group,
+ *     r = fl32(qmax / A), code = clamp(rint_half_even(fl32(v * r)), -qmax,
+ *     qmax), scale = fl32(A / qmax) (times 1/16 when rotated); an all-zero
+ *     group has scale 0 and zero codes. qmax = 7 (INT4) or 127 (INT8).
+ */
+#ifndef CONVROT_H
+#define CONVROT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum cr_status {
+  CR_OK = 0,
+  CR_ERR_INVALID_ARGUMENT = 1,    /* null / misaligned pointer, bad enum, negative size   */
+  CR_ERR_UNSUPPORTED_SHAPE = 2,   /* K, N or group alignment not met, sizes out of range    */
+  CR_ERR_UNSUPPORTED_FORMAT = 3,  /* "format not available": this qtype/granularity combo   */
+  CR_ERR_NO_DEVICE = 4,           /* no HIP device visible                                  */
+  CR_ERR_UNSUPPORTED_ARCH = 5,    /* current device is not gfx950: refused, no fallback     */
+  CR_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes below the *_workspace_size() result    */
+  CR_ERR_HIP = 7                  /* a HIP runtime call failed; see convrot_last_hip_error() */
+} cr_status;
+
+typedef enum cr_qtype {
+  CR_Q_SYM_INT4 = 0,             /* signed codes in [-7, 7], packed two per byte            */
+  CR_Q_SYM_INT8 = 1,             /* signed codes in [-127, 127], one byte each              */
+  CR_Q_UNSIGNED_INT4_SHIFT = 2,  /* codes of v + shift in [0, 15] (post-GELU path, no rotation) */
+  CR_Q_ASYM_UINT4 = 3            /* weights only: uint4 codes, fp16 scale and uint4 zero per group of 16 */
+} cr_qtype;
+
+typedef enum cr_gran {
+  CR_GRAN_TENSOR = 0,     /* one scale, float32 [1]                                          */
+  CR_GRAN_ROW = 1,        /* one scale per row (token or output channel), float32 [rows]     */
+  CR_GRAN_ROW_GROUP = 2   /* one per row and q_group columns: float32 [rows, K/q_group]      */
+} cr_gran;
+
+typedef enum cr_out {
+  CR_OUT_BF16 = 0,        /* y rounded half-to-even to bf16                                   */
+  CR_OUT_F32 = 1,         /* y as float32                                                     */
+  CR_OUT_I32_RAW = 2      /* the exact integer sum_k qa*(qw - z); scales/epilogue skipped     */
+} cr_out;
+
+/* Status text, e.g. "format not available" for CR_ERR_UNSUPPORTED_FORMAT. */
+const char* convrot_status_string(cr_status status);
+/* The hipError_t value behind the last CR_ERR_HIP on this thread (0 if none). */
+int convrot_last_hip_error(void);
+/* CR_OK when a gfx950 device is current; CR_ERR_NO_DEVICE / CR_ERR_UNSUPPORTED_ARCH otherwise. */
+cr_status convrot_device_check(void);
+
+/* Dispatch counters: kernel launches per entry point (index = order of the
+ * entry points below: 0 rotate_quantize, 1 pack, 2 w4a4, 3 w4a8, 4 int8)
+ * and the count of non-native fallbacks, which is always 0 because no
+ * fallback exists. Process-wide, thread-safe. */
+typedef struct cr_counters {
+  uint64_t launches[8];
+  uint64_t fallbacks;
+} cr_counters;
+void convrot_get_counters(cr_counters* out);
+void convrot_reset_counters(void);
+
+/* ------------------------------------------------------------------------
+ * convrot_rotate_quantize - online rotation + dynamic quantization of
+ * activations, and the offline rotation + quantization of weights.
+ *
+ * Cites: "Qwen-Image-Edit-2511 - INT4 tensorwise W4A4" page, intro (rotate
+ * online, quantize dynamically, same rotation offline on the weights);
+ * "Qwen-Image-Edit-2511 INT4 (ComfyUI Optimized)", Key Technical
+ * Optimizations (quantization and LoRA-down computed once and shared by split
+ * projections) and Kernel Engineering (unsigned +0.171875 post-GELU path,
+ * LoRA-down staged in bf16); Environment Variables (FP32 LoRA activations).
+ *
+ *   x            bf16 [rows, K], leading dimension ldx >= K
+ *   rot_group    256 (rotate each 256-column group) or 0 (no rotation)
+ *   qtype/gran/q_group, supported combinations:
+ *       rot 256: SYM_INT4 or SYM_INT8 with TENSOR, ROW or ROW_GROUP(q_group 64);
+ *                ASYM_UINT4 with ROW_GROUP(q_group 16)
+ *       rot 0:   SYM_INT4 with ROW_GROUP(64); UNSIGNED_INT4_SHIFT with ROW_GROUP(64)
+ *       anything else returns CR_ERR_UNSUPPORTED_FORMAT.
+ *   shift        UNSIGNED_INT4_SHIFT only: codes quantize v + shift (e.g. 0.171875)
+ *   lora_down    optional bf16 [R, K] (R == 32) with rot 0: also writes
+ *                lora_act[m, r] = sum_k x[m, k] * lora_down[r, k] (float32
+ *                accumulation of the unshifted, unrotated input), stored as
+ *                bf16 (lora_act_f32 = 0) or float32 (1), [rows, R] row-major
+ *   codes        SYM_INT4 / UNSIGNED / ASYM: uint8 [rows, K/2] natural int4;
+ *                SYM_INT8: int8 [rows, K]
+ *   scales       float32 [1] | [rows] | [rows, K/q_group]; ASYM: fp16 [rows, K/16]
+ *   zeros        ASYM only: uint8 [rows, K/32], two uint4 zero points per byte
+ *                (group 2j low nibble); NULL otherwise
+ *   workspace    device scratch of at least convrot_rq_workspace_size(...)
+ *                bytes (needed by TENSOR granularity; may be NULL when that
+ *                size is 0). Contents on entry are ignored.
+ * Shape: rows >= 1, K % 256 == 0 when rotating, K % 64 == 0 otherwise,
+ *        K <= 32768.
+ * Result is deterministic and bit-identical to the reference definition for
+ * finite inputs. Concurrent calls sharing one workspace race.
+ */
+size_t convrot_rq_workspace_size(int64_t rows, int64_t K, int rot_group,
+                                 cr_qtype qtype, cr_gran gran, int q_group);
+
+cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx,
+                                  int rot_group, cr_qtype qtype, cr_gran gran, int q_group,
+                                  float shift,
+                                  const void* lora_down, int R, void* lora_act, int lora_act_f32,
+                                  void* codes, void* scales, void* zeros,
+                                  void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * w4_pack_weights - natural int4 weight codes -> tile-packed layout.
+ *
+ * Cites: "Qwen-Image-Edit-2511 INT4 (ComfyUI Optimized)", Tile-Packed Weight
+ * Format (outer (N/128, K/64) grid of 32x128-byte tiles; group scales as
+ * (N/128, K/64, 128)); "Qwen3-4B ConvRot W4A4" page, Format (natural
+ * [rows, cols/2] container).
+ *
+ *   codes    natural uint8 [N, K/2] as written by convrot_rotate_quantize
+ *   qtype    SYM_INT4 (W4A4 formats) or ASYM_UINT4 (W4A8 g16 format)
+ *   gran     SYM_INT4: TENSOR, ROW or ROW_GROUP(q_group 64); ASYM: ROW_GROUP(16)
+ *   scales   as written by convrot_rotate_quantize for that (qtype, gran)
+ *   zeros    ASYM only: uint8 [N, K/32]
+ * Outputs (sizes from w4_packed_bytes):
+ *   packed         uint8 [N/128][K/64][4096]  (inner byte order: one 64-lane
+ *                  matrix-core operand fragment per 512 B (SYM) / 256 B (ASYM))
+ *   packed_scales  ROW_GROUP(64): float32 [N/128][K/64][128];
+ *                  ASYM: fp16 [N/128][K/64][4][128]; NULL for TENSOR / ROW
+ *   packed_zeros   ASYM: uint8 [N/128][K/64][4][128], one zero point per byte; else NULL
+ *   w_sum          optional float32 [N]: sum_k of the dequantized weight row
+ *                  (SYM_INT4 only), the correction vector of the unsigned
+ *                  shift path (float32 accumulation)
+ * Shape: N % 128 == 0, K % 64 == 0 (K % 256 for ROW_GROUP 64 is not required).
+ */
+size_t w4_packed_bytes(int64_t N, int64_t K, cr_qtype qtype, cr_gran gran, int q_group,
+                       int which /* 0 packed codes, 1 packed scales, 2 packed zeros */);
+
+cr_status w4_pack_weights(const void* codes, const void* scales, const void* zeros,
+                          int64_t N, int64_t K, cr_qtype qtype, cr_gran gran, int q_group,
+                          void* packed, void* packed_scales, void* packed_zeros, float* w_sum,
+                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * w4a4_gemm - INT4 activations x tile-packed INT4 weights on int8 matrix
+ * cores (exact int4 -> int8 widening, int32 accumulation) with a fused
+ * epilogue.
+ *
+ * Cites: "Qwen-Image-Edit-2511 - INT4 tensorwise W4A4" page, Measurements
+ * (fused rotation + INT4 matmul with a rank-one scale); "Qwen-Image-Edit-2511
+ * INT4 (ComfyUI Optimized)", Fused LoRA-Up Epilogue, Kernel Engineering
+ * (unsigned shifted activations, scale staging).
+ *
+ *   a_codes     uint8 [M, K/2] natural int4 (signed, or unsigned when a_unsigned)
+ *   a_scales    float32: TENSOR [1], ROW [M], ROW_GROUP(64) [M, K/64]
+ *   a_unsigned  1 for UNSIGNED_INT4_SHIFT codes: y -= a_shift * w_sum[n]
+ *   w_packed    from w4_pack_weights (SYM_INT4)
+ *   w_scales    TENSOR [1], ROW [N], ROW_GROUP(64): packed [N/128][K/64][128]
+ *   scale pairs: (TENSOR|ROW) x (TENSOR|ROW), or ROW_GROUP x ROW_GROUP (group 64)
+ *   w_sum       float32 [N], required iff a_unsigned
+ *   lora_act    optional [M, R] (bf16, or float32 if lora_act_f32), R == 32;
+ *   lora_up     bf16 [N, R] (row n = output channel): y += lora_act @ lora_up^T
+ *   bias        optional bf16 [N]
+ *   out         CR_OUT_BF16: bf16 [M, ldc]; CR_OUT_F32: float32; CR_OUT_I32_RAW:
+ *               int32 sum_k qa*qw (lora/bias/scales ignored)
+ * Epilogue: y = s_a s_w acc  (or sum_g a_s[m,g] w_s[n,g] P[m,n,g]) - shift
+ * term + low-rank + bias, evaluated in float32, stored once.
+ * Shape: M >= 1, N % 128 == 0, K % 128 == 0, K <= 32768, ldc >= N (ldc % 8 == 0).
+ * workspace: unused (pass NULL, 0).
+ */
+cr_status w4a4_gemm(const void* a_codes, const float* a_scales, cr_gran a_gran,
+                    int a_unsigned, float a_shift,
+                    const void* w_packed, const float* w_scales, cr_gran w_gran,
+                    const float* w_sum,
+                    const void* lora_act, int lora_act_f32, const void* lora_up, int R,
+                    const void* bias,
+                    void* out, cr_out out_type, int64_t ldc,
+                    int64_t M, int64_t N, int64_t K,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * w4a8_gemm - per-token INT8 activations x asymmetric uint4 g16 weights.
+ *
+ * Cites: "Qwen-Image-Edit-2511-W4A8-ConvRot" card, build table and file
+ * layout (asym_w4a8_int8, group_size 16, convrot_groupsize 256).
+ *
+ *   a_codes    int8 [M, K] (SYM_INT8 from convrot_rotate_quantize)
+ *   a_scales   float32 ROW [M] (or TENSOR [1])
+ *   w_packed, w_scales (fp16), w_zeros (uint8): from w4_pack_weights (ASYM_UINT4)
+ *   y[m, n] = s_a[m] * sum_g s_w[n, g] * sum_{k in g} qa[m,k] (qw[n,k] - z[n,g]) + bias[n]
+ *   CR_OUT_I32_RAW gives sum_k qa (qw - z) exactly.
+ * Shape: M >= 1, N % 128 == 0, K % 128 == 0, K <= 32768, ldc >= N (ldc % 8 == 0). group must be 16.
+ */
+cr_status w4a8_gemm(const void* a_codes, const float* a_scales, cr_gran a_gran,
+                    const void* w_packed, const void* w_scales, const void* w_zeros, int group,
+                    const void* bias, void* out, cr_out out_type, int64_t ldc,
+                    int64_t M, int64_t N, int64_t K,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * int8_tensorwise_gemm - INT8 x INT8 with per-tensor scales (the INT8
+ * fallback layers of the mixed recipe, with or without ConvRot).
+ *
+ * Cites: "Qwen-Image-Edit-2511 - INT4 tensorwise W4A4" page, intro (value /
+ * output projections and adaLN modulation kept as int8_tensorwise) and
+ * Measurements (int8_tensorwise kernels); "Qwen Image 2.1 - Hybrid W4A8 /
+ * INT8 ConvRot", Quantization recipe.
+ *
+ *   a_codes int8 [M, K]; a_scale float32 [1]; w int8 [N, K] natural; w_scale float32 [1]
+ *   y = s_a s_w sum_k qa qw + bias
+ * Shape: M >= 1, N % 128 == 0, K % 128 == 0, K <= 32768, ldc >= N (ldc % 8 == 0).
+ */
+cr_status int8_tensorwise_gemm(const void* a_codes, const float* a_scale,
+                               const void* w, const float* w_scale,
+                               const void* bias, void* out, cr_out out_type, int64_t ldc,
+                               int64_t M, int64_t N, int64_t K,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVROT_H */

@@ -171,7 +171,7 @@ def prepare_w4a4(w_bits, rot_group=256, gran="tensor", q_group=None):
 
 def prepare_w4a8(w_bits, rot_group=256, group=16):
     r = rotate_quantize(w_bits, rot_group, "asym_u4", "row_group", group)
-    r["tiles"] = pack.tile_pack_w4a8(r["codes"])
+    r["tiles"] = pack.tile_pack_w4a8(r["values"])
     r["scales_tiles"] = pack.tile_pack_g16(r["scales"])
     r["zeros_tiles"] = pack.tile_pack_g16(r["zeros"])
     return r

@@ -22,8 +22,10 @@ Readings where the pages are silent:
         <- natural byte (row 16*nb + l%16 of the tile, byte 8*(l//16) + j of
            the tile's 32-byte k slice)
     W4A8 tile (asymmetric uint4, k-groups of 16):
-        tile byte  kg*1024 + nb*256 + l*4 + j,  kg, nb in [0,4), l in [0,64), j in [0,4)
-        <- natural byte (row 32*nb + l%32 of the tile, byte 8*kg + 4*(l//32) + j)
+        tile byte  kg*1024 + nb*256 + l*4 + i,  kg, nb in [0,4), l in [0,64), i in [0,4)
+        = code (row, k0+i) | code (row, k0+4+i) << 4, row 32*nb + l%32 of the
+          tile, k0 = 16*kg + 8*(l//32) in the tile (so a lane's low nibbles
+          are 4 consecutive k and its high nibbles the next 4)
 
   * per-group scales of the W4A4 g64 format: float32 [N/128][K/64][128]
     (the pages' wscales layout); W4A8 g16 scales (fp16) and zero points
@@ -98,39 +100,45 @@ def tile_unpack_w4a4(tiles: np.ndarray) -> np.ndarray:
     return out
 
 
-def tile_pack_w4a8(packed: np.ndarray) -> np.ndarray:
-    """natural uint8 [N, K/2] (uint4 codes) -> tile-packed uint8 [N/128, K/64, 4096]."""
-    packed = np.asarray(packed, dtype=np.uint8)
-    N, half = packed.shape
-    K = 2 * half
+def tile_pack_w4a8(values: np.ndarray) -> np.ndarray:
+    """uint4 codes [N, K] (values 0..15) -> tile-packed uint8 [N/128, K/64, 4096].
+    Byte kg*1024 + nb*256 + lane*4 + i of tile (tn, kt) holds code
+    (row, k0 + i) in its low nibble and (row, k0 + 4 + i) in its high nibble,
+    with row = 128*tn + 32*nb + lane%32 and k0 = 64*kt + 16*kg + 8*(lane//32)."""
+    v = np.asarray(values).astype(np.int64)
+    N, K = v.shape
     _check_tiles(N, K)
     out = np.empty((N // 128, K // 64, 4096), dtype=np.uint8)
     for tn in range(N // 128):
         for kt in range(K // 64):
-            tile = packed[128 * tn:128 * tn + 128, 32 * kt:32 * kt + 32]
             for kg in range(4):
                 for nb in range(4):
                     for lane in range(64):
-                        row = 32 * nb + lane % 32
-                        col = 8 * kg + 4 * (lane // 32)
+                        row = 128 * tn + 32 * nb + lane % 32
+                        k0 = 64 * kt + 16 * kg + 8 * (lane // 32)
                         o = kg * 1024 + nb * 256 + lane * 4
-                        out[tn, kt, o:o + 4] = tile[row, col:col + 4]
+                        for i in range(4):
+                            out[tn, kt, o + i] = (v[row, k0 + i] & 0xF) | ((v[row, k0 + 4 + i] & 0xF) << 4)
     return out
 
 
 def tile_unpack_w4a8(tiles: np.ndarray) -> np.ndarray:
+    """Inverse of tile_pack_w4a8: uint8 codes [N, K]."""
     tiles = np.asarray(tiles, dtype=np.uint8)
     TN, TK, _ = tiles.shape
-    out = np.empty((TN * 128, TK * 32), dtype=np.uint8)
+    out = np.empty((TN * 128, TK * 64), dtype=np.uint8)
     for tn in range(TN):
         for kt in range(TK):
             for kg in range(4):
                 for nb in range(4):
                     for lane in range(64):
                         row = 128 * tn + 32 * nb + lane % 32
-                        col = 32 * kt + 8 * kg + 4 * (lane // 32)
+                        k0 = 64 * kt + 16 * kg + 8 * (lane // 32)
                         o = kg * 1024 + nb * 256 + lane * 4
-                        out[row, col:col + 4] = tiles[tn, kt, o:o + 4]
+                        for i in range(4):
+                            b = int(tiles[tn, kt, o + i])
+                            out[row, k0 + i] = b & 0xF
+                            out[row, k0 + 4 + i] = b >> 4
     return out
 
 

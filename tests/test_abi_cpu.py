@@ -1,0 +1,146 @@
+"""The C-ABI library loads, exports every symbol include/convrot.h declares,
+and rejects bad arguments with the documented status BEFORE touching a
+device. No compute call runs here (no GPU in this environment); a call with
+valid arguments reaches the device check and reports the missing device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "convrot.h")
+LIB = os.path.join(ROOT, "w4a8_rotated_quantized_amd", "libconvrot.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libconvrot.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted({n for n in names if n not in ("if", "while", "sizeof")})
+
+
+def test_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    names = _declared_functions()
+    assert {"convrot_rotate_quantize", "w4_pack_weights", "w4a4_gemm", "w4a8_gemm",
+            "int8_tensorwise_gemm"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+@pytest.fixture(scope="module")
+def cr():
+    import w4a8_rotated_quantized_amd as m
+    return m
+
+
+class _FakeDev:
+    """Stands in for a device tensor: a 16-byte aligned non-null address that
+    is never dereferenced (validation happens before any device access)."""
+    def __init__(self, addr=0x10000):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+def _p(v):
+    return ctypes.c_void_p(v)
+
+
+A = 0x10000  # aligned fake device address
+
+
+def test_status_strings(cr):
+    assert cr.status_string(3) == "format not available"
+    assert "gfx950" in cr.status_string(5)
+    assert cr.status_string(0) == "ok"
+
+
+def test_counters_have_no_fallback(cr):
+    c = cr.get_counters()
+    assert c["fallbacks"] == 0
+
+
+def test_device_check_reports_no_device_here(cr):
+    assert cr.device_check() in (4, 5)
+
+
+def _rq(cr, x=A, rows=64, K=512, ldx=512, rot=256, q=0, g=0, qg=0, lora=None, R=0, la=None,
+        codes=A, scales=A, zeros=None, ws=A, wsb=1 << 20):
+    return cr.lib.convrot_rotate_quantize(_p(x), rows, K, ldx, rot, q, g, qg, 0.0, _p(lora), R, _p(la), 0,
+                                          _p(codes), _p(scales), _p(zeros), _p(ws), wsb, None)
+
+
+def test_rq_validation(cr):
+    assert _rq(cr, x=None) == 1                              # null input
+    assert _rq(cr, x=A + 4) == 1                             # misaligned
+    assert _rq(cr, K=300, ldx=304) == 2                      # K % 256 with rotation
+    assert _rq(cr, ldx=500) == 2                             # ldx < K
+    assert _rq(cr, rows=0) == 2
+    assert _rq(cr, K=65536, ldx=65536) == 2                  # above K limit
+    assert _rq(cr, rot=128) == 3                             # group size not available
+    assert _rq(cr, q=2) == 3                                 # shift path needs rot 0
+    assert _rq(cr, q=3, g=2, qg=16) == 1                     # asym needs zeros
+    assert _rq(cr, q=3, g=0) == 3                            # asym needs ROW_GROUP(16)
+    assert _rq(cr, g=2, qg=32) == 3                          # group 32 not available
+    assert _rq(cr, rot=0, g=0) == 3                          # rot 0 needs ROW_GROUP(64)
+    assert _rq(cr, rot=0, g=2, qg=64, lora=A, R=16, la=A) == 3   # rank must be 32
+    assert _rq(cr, rot=256, lora=A, R=32, la=A) == 3          # low rank only without rotation
+    assert _rq(cr, wsb=0) == 6                               # TENSOR needs workspace
+    assert _rq(cr) == 4                                      # valid -> device check (no GPU here)
+    assert _rq(cr, rot=0, g=2, qg=64, ws=None, wsb=0) == 4
+
+
+def test_rq_workspace_size(cr):
+    n = cr.convrot_rq_workspace_size(4096, 3072, 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
+    assert n > 0 and n % 4 == 0
+    assert cr.convrot_rq_workspace_size(4096, 3072, 256, cr.Q.SYM_INT4, cr.GRAN.ROW) == 0
+
+
+def test_pack_validation(cr):
+    L = cr.lib
+    assert L.w4_pack_weights(_p(A), _p(A), None, 100, 512, 0, 0, 0, _p(A), None, None, None, None) == 2
+    assert L.w4_pack_weights(None, _p(A), None, 128, 512, 0, 0, 0, _p(A), None, None, None, None) == 1
+    assert L.w4_pack_weights(_p(A), _p(A), None, 128, 512, 0, 2, 32, _p(A), _p(A), None, None, None) == 3
+    assert L.w4_pack_weights(_p(A), _p(A), None, 128, 512, 3, 2, 16, _p(A), _p(A), _p(A), None, None) == 1
+    assert L.w4_pack_weights(_p(A), _p(A), None, 128, 512, 1, 0, 0, _p(A), None, None, None, None) == 3
+    assert L.w4_pack_weights(_p(A), _p(A), None, 128, 512, 0, 0, 0, _p(A), None, None, None, None) == 4
+    assert cr.w4_packed_bytes(256, 512, 0, 0, 0, 0) == 256 * 256
+    assert cr.w4_packed_bytes(256, 512, 0, 2, 64, 1) == 256 * 8 * 4
+    assert cr.w4_packed_bytes(256, 512, 3, 2, 16, 2) == 256 * 32
+
+
+def _w4a4(cr, a=A, ag=0, wg=0, uns=0, wsum=None, la=None, lu=None, R=0, out=A, ot=0, ldc=256,
+          M=64, N=256, K=512):
+    return cr.lib.w4a4_gemm(_p(a), _p(A), ag, uns, 0.0, _p(A), _p(A), wg, _p(wsum), _p(la), 0, _p(lu), R,
+                            None, _p(out), ot, ldc, M, N, K, None, 0, None)
+
+
+def test_gemm_validation(cr):
+    assert _w4a4(cr, a=None) == 1
+    assert _w4a4(cr, N=200, ldc=200) == 2
+    assert _w4a4(cr, K=192) == 2
+    assert _w4a4(cr, ldc=128) == 2
+    assert _w4a4(cr, M=0) == 2
+    assert _w4a4(cr, ag=2, wg=0) == 3                        # group x tensor scales
+    assert _w4a4(cr, uns=1) == 1                             # unsigned needs w_sum
+    assert _w4a4(cr, la=A, lu=None, R=32) == 3
+    assert _w4a4(cr, la=A, lu=A, R=16) == 3
+    assert _w4a4(cr, ot=5) == 1
+    assert _w4a4(cr) == 4
+    L = cr.lib
+    assert L.w4a8_gemm(_p(A), _p(A), 1, _p(A), _p(A), _p(A), 32, None, _p(A), 0, 256, 64, 256, 512,
+                       None, 0, None) == 3
+    assert L.w4a8_gemm(_p(A), _p(A), 2, _p(A), _p(A), _p(A), 16, None, _p(A), 0, 256, 64, 256, 512,
+                       None, 0, None) == 3
+    assert L.w4a8_gemm(_p(A), _p(A), 1, _p(A), _p(A), _p(A), 16, None, _p(A), 0, 256, 64, 256, 512,
+                       None, 0, None) == 4
+    assert L.int8_tensorwise_gemm(_p(A), None, _p(A), _p(A), None, _p(A), 0, 256, 64, 256, 512,
+                                  None, 0, None) == 1
+    assert L.int8_tensorwise_gemm(_p(A), _p(A), _p(A), _p(A), None, _p(A), 0, 256, 64, 256, 512,
+                                  None, 0, None) == 4

@@ -1,0 +1,193 @@
+"""GPU parity of the GEMM entry points against the CPU oracle.
+
+The GEMMs are fed the ORACLE's codes, scales and packed weights (uploaded),
+so these tests isolate the GEMM kernels from the quantizer and the packer.
+Bar: int32 results (CR_OUT_I32_RAW) bit-exact; bf16 output within 2e-3
+relative L2 of the oracle's float32 epilogue; float32 output within 1e-5.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import workloads as wl  # noqa: E402
+from oracle import linear as ol, gemm as og  # noqa: E402
+from tests.gpu_helpers import bf16_dev, dev, host, rel_l2, bf16_to_f32, say  # noqa: E402
+
+GR = {"tensor": 0, "row": 1, "row_group": 2}
+
+
+@pytest.fixture(scope="module")
+def cr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import w4a8_rotated_quantized_amd as m
+    assert m.device_check() == 0
+    return m
+
+
+def _check_out(y_bf16, y_f32, ref_y):
+    yb = bf16_to_f32(host(y_bf16))
+    assert rel_l2(yb, ref_y) <= 2e-3, rel_l2(yb, ref_y)
+    assert rel_l2(host(y_f32), ref_y) <= 1e-5, rel_l2(host(y_f32), ref_y)
+
+
+W4A4_CASES = [
+    # M, N, K, a_gran, w_gran
+    (1, 256, 512, "tensor", "tensor"),
+    (17, 384, 3072, "tensor", "row"),
+    (64, 256, 512, "row", "tensor"),
+    (100, 256, 1024, "tensor", "tensor"),
+    (256, 384, 3072, "row", "row"),
+    (300, 512, 768, "tensor", "tensor"),
+    (129, 128, 12288, "tensor", "tensor"),
+]
+
+
+@pytest.mark.parametrize("case", W4A4_CASES)
+def test_w4a4_tensor_row(cr, case):
+    M, N, K, ag, wg = case
+    say(f"w4a4 {case}")
+    xb = wl.activation(21, M + N + K, M, K, n_outliers=3, outlier_scale=20.0)
+    wb = wl.weight(21, 7 + M + N + K, N, K)
+    bias = wl.weight(21, 9, 1, N, std=0.5)[0]
+    wp = ol.prepare_w4a4(wb, 256, wg)
+    ref = ol.w4a4_linear(xb, wb, 256, ag, wg, wprep=wp)
+    ref_b = ol.w4a4_linear(xb, wb, 256, ag, wg, bias_bits=bias, wprep=wp)
+    a = dev(ref["x"]["codes"])
+    sa = dev(np.asarray(ref["x"]["scales"], np.float32).reshape(-1))
+    w = dev(wp["tiles"].reshape(-1))
+    sw = dev(np.asarray(wp["scales"], np.float32).reshape(-1))
+    raw = cr.w4a4_gemm(a, sa, GR[ag], w, sw, GR[wg], M, N, K, out_type=2)
+    assert np.array_equal(host(raw).astype(np.int64), ref["raw"])
+    yb = cr.w4a4_gemm(a, sa, GR[ag], w, sw, GR[wg], M, N, K, out_type=0)
+    yf = cr.w4a4_gemm(a, sa, GR[ag], w, sw, GR[wg], M, N, K, out_type=1)
+    _check_out(yb, yf, ref["y"])
+    ybias = cr.w4a4_gemm(a, sa, GR[ag], w, sw, GR[wg], M, N, K, bias=bf16_dev(bias), out_type=1)
+    assert rel_l2(host(ybias), ref_b["y"]) <= 1e-5
+
+
+def test_w4a4_ldc_padding(cr):
+    M, N, K = 70, 256, 512
+    xb = wl.activation(22, 0, M, K)
+    wb = wl.weight(22, 1, N, K)
+    ref = ol.w4a4_linear(xb, wb)
+    out = torch.full((M, N + 64), 7.0, dtype=torch.float32, device="cuda")
+    cr.w4a4_gemm(dev(ref["x"]["codes"]), dev(ref["x"]["scales"]), 0, dev(ref["w"]["tiles"].reshape(-1)),
+                 dev(ref["w"]["scales"]), 0, M, N, K, out_type=1, out=out)
+    o = host(out)
+    assert rel_l2(o[:, :N], ref["y"]) <= 1e-5
+    assert np.all(o[:, N:] == 7.0)          # nothing written past N
+
+
+G64_CASES = [
+    # M, N, K, unsigned, lora(None|bf16|f32), bias
+    (16, 256, 512, False, None, False),
+    (40, 384, 1024, True, None, False),
+    (200, 256, 3072, False, "bf16", True),
+    (130, 384, 1024, True, "bf16", False),
+    (64, 256, 512, True, "f32", True),
+    (257, 128, 768, False, "f32", False),
+]
+
+
+@pytest.mark.parametrize("case", G64_CASES)
+def test_w4a4_group64_lowrank(cr, case):
+    M, N, K, uns, lora, use_bias = case
+    say(f"w4a4 g64 {case}")
+    shift = 0.171875 if uns else 0.0
+    xb = wl.gelu_activation(23, M + K, M, K) if uns else wl.activation(23, M + K, M, K)
+    wb = wl.weight(23, N + K, N, K)
+    l1 = l2 = None
+    if lora:
+        l1, l2, wb = wl.lowrank_split(wb, 32)
+    bias = wl.weight(23, 5, 1, N, std=0.5)[0] if use_bias else None
+    wp = ol.prepare_w4a4(wb, 0, "row_group", 64)
+    ref = ol.w4a4_linear(xb, wb, 0, "row_group", "row_group", 64, shift, l1, l2,
+                         act_f32=(lora == "f32"), bias_bits=bias, wprep=wp)
+    a = dev(ref["x"]["codes"])
+    sa = dev(ref["x"]["scales"])
+    w = dev(wp["tiles"].reshape(-1))
+    sw = dev(wp["scales_tiles"].reshape(-1))
+    wsum = dev(wp["wsum"])
+    la = lu = None
+    if lora:
+        la = dev(ref["la"]) if lora == "f32" else bf16_dev(wl.bf16_bits_from_f32(ref["la"]))
+        lu = bf16_dev(l1)
+    kw = dict(a_unsigned=uns, a_shift=shift, w_sum=wsum, lora_act=la, lora_up=lu,
+              bias=None if bias is None else bf16_dev(bias))
+    raw = cr.w4a4_gemm(a, sa, 2, w, sw, 2, M, N, K, out_type=2, **kw)
+    assert np.array_equal(host(raw).astype(np.int64), ref["raw"])
+    yb = cr.w4a4_gemm(a, sa, 2, w, sw, 2, M, N, K, out_type=0, **kw)
+    yf = cr.w4a4_gemm(a, sa, 2, w, sw, 2, M, N, K, out_type=1, **kw)
+    _check_out(yb, yf, ref["y"])
+
+
+INT8_CASES = [(2, 256, 3072), (33, 384, 512), (64, 128, 256), (190, 256, 1024), (512, 384, 3072)]
+
+
+@pytest.mark.parametrize("case", INT8_CASES)
+def test_int8_tensorwise(cr, case):
+    M, N, K = case
+    say(f"int8 {case}")
+    xb = wl.activation(24, M + K, M, K, n_outliers=2, outlier_scale=15.0)
+    wb = wl.weight(24, N + K, N, K)
+    ref = ol.int8_linear(xb, wb)
+    a = dev(ref["x"]["codes"])
+    sa = dev(ref["x"]["scales"])
+    w = dev(ref["w"]["codes"])
+    sw = dev(ref["w"]["scales"])
+    raw = cr.int8_tensorwise_gemm(a, sa, w, sw, M, N, K, out_type=2)
+    assert np.array_equal(host(raw).astype(np.int64), ref["raw"])
+    yb = cr.int8_tensorwise_gemm(a, sa, w, sw, M, N, K, out_type=0)
+    yf = cr.int8_tensorwise_gemm(a, sa, w, sw, M, N, K, out_type=1)
+    _check_out(yb, yf, ref["y"])
+
+
+W4A8_CASES = [(1, 128, 512), (50, 256, 1024), (128, 256, 3072), (333, 384, 768)]
+
+
+@pytest.mark.parametrize("case", W4A8_CASES)
+def test_w4a8(cr, case):
+    M, N, K = case
+    say(f"w4a8 {case}")
+    xb = wl.activation(25, M + K, M, K)
+    wb = wl.weight(25, N + K, N, K)
+    bias = wl.weight(25, 3, 1, N, std=0.5)[0]
+    wp = ol.prepare_w4a8(wb)
+    ref = ol.w4a8_linear(xb, wb, wprep=wp)
+    ref_b = ol.w4a8_linear(xb, wb, bias_bits=bias, wprep=wp)
+    a = dev(ref["x"]["codes"])
+    sa = dev(ref["x"]["scales"])
+    w = dev(wp["tiles"].reshape(-1))
+    sw = dev(wp["scales_tiles"].reshape(-1))
+    zw = dev(wp["zeros_tiles"].reshape(-1))
+    raw = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, out_type=2)
+    assert np.array_equal(host(raw).astype(np.int64), ref["raw"])
+    yb = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, out_type=0)
+    yf = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, out_type=1)
+    _check_out(yb, yf, ref["y"])
+    ybias = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, bias=bf16_dev(bias), out_type=1)
+    assert rel_l2(host(ybias), ref_b["y"]) <= 1e-5
+
+
+def test_extreme_codes_no_overflow(cr):
+    # all codes at +-qmax over the largest K: the int32 accumulators must stay exact
+    M, N, K = 64, 128, 32768
+    qa = np.full((M, K), 7, np.int64)
+    qa[::2] = -7
+    qw = np.full((N, K), -7, np.int64)
+    from oracle import pack as opack
+    a = dev(opack.pack_int4(qa))
+    w = dev(opack.tile_pack_w4a4(opack.pack_int4(qw)).reshape(-1))
+    one = dev(np.ones(1, np.float32))
+    raw = cr.w4a4_gemm(a, one, 0, w, one, 0, M, N, K, out_type=2)
+    assert np.array_equal(host(raw).astype(np.int64), og.int_gemm(qa, qw))
+    # int8: 127 * 127 * 16384 = 264,257,536 < 2^31
+    K8 = 16384
+    q8 = np.full((M, K8), 127, np.int64)
+    w8 = np.full((N, K8), -127, np.int64)
+    raw8 = cr.int8_tensorwise_gemm(dev(q8.astype(np.int8)), one, dev(w8.astype(np.int8)), one, M, N, K8,
+                                   out_type=2)
+    assert np.array_equal(host(raw8).astype(np.int64), og.int_gemm(q8, w8))

@@ -1,0 +1,170 @@
+"""GPU parity of convrot_rotate_quantize and w4_pack_weights against the
+CPU oracle: codes, scales, zero points and packed bytes must be bit-exact;
+the LoRA-down activations (float32 matrix-core accumulation in another order)
+agree to a float32-sum tolerance before and one bf16 ulp after rounding."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import workloads as wl  # noqa: E402
+from oracle import linear as ol, pack as opack  # noqa: E402
+from tests.gpu_helpers import bf16_dev, dev, host, bytes_of, say  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def cr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import w4a8_rotated_quantized_amd as m
+    assert m.device_check() == 0, "device is not gfx950"
+    return m
+
+
+QT = {"int4": 0, "int8": 1}
+GR = {"tensor": 0, "row": 1, "row_group": 2}
+
+ROT_SHAPES = [(64, 512), (37, 3072), (300, 768), (5, 256), (129, 12288)]
+
+
+@pytest.mark.parametrize("qt", ["int4", "int8"])
+@pytest.mark.parametrize("gran", ["tensor", "row", "row_group"])
+@pytest.mark.parametrize("shape", ROT_SHAPES)
+def test_rotate_quantize_sym(cr, qt, gran, shape):
+    rows, K = shape
+    say(f"rq sym {qt} {gran} {shape}")
+    xb = wl.activation(11, rows * 7 + K, rows, K, n_outliers=max(1, K // 200), outlier_scale=25.0)
+    qg = 64 if gran == "row_group" else 0
+    ref = ol.rotate_quantize(xb, 256, qt, gran, qg or None)
+    codes, scales, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), 256, QT[qt], GR[gran], qg)
+    assert np.array_equal(host(codes).reshape(ref["codes"].shape).view(np.uint8),
+                          ref["codes"].view(np.uint8)), "codes differ"
+    assert np.array_equal(host(scales).reshape(-1).view(np.uint32),
+                          np.asarray(ref["scales"], np.float32).reshape(-1).view(np.uint32)), "scales differ"
+
+
+def test_rotate_quantize_strided_rows_and_zero_rows(cr):
+    rows, K, ldx = 40, 1024, 1024 + 64
+    xb = wl.activation(12, 0, rows, ldx)
+    xb[3, :] = 0          # an all-zero row: scale 0, codes 0
+    xb[7, :K] = 0
+    full = bf16_dev(xb)
+    view = full[:, :K]
+    for gran in ("row", "tensor", "row_group"):
+        qg = 64 if gran == "row_group" else 0
+        ref = ol.rotate_quantize(np.ascontiguousarray(xb[:, :K]), 256, "int4", gran, qg or None)
+        codes, scales, _, _ = cr.convrot_rotate_quantize(view, 256, 0, GR[gran], qg)
+        assert np.array_equal(host(codes), ref["codes"])
+        assert np.array_equal(host(scales).reshape(-1), np.asarray(ref["scales"]).reshape(-1))
+
+
+def test_rotate_quantize_subnormal_and_tiny_inputs(cr):
+    rows, K = 8, 512
+    g = np.random.default_rng(5)
+    # inputs around the float32 normal/subnormal boundary; every scale group
+    # keeps qmax / max|v| finite (the documented domain), while the stored
+    # scales (max|v| / qmax / 16) fall into the subnormal range
+    x = (g.standard_normal((rows, K)) * 1e-38).astype(np.float32)
+    xb = wl.bf16_bits_from_f32(x)
+    for qt in ("int4", "int8"):
+        ref = ol.rotate_quantize(xb, 256, qt, "row")
+        codes, scales, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), 256, QT[qt], 1)
+        assert np.array_equal(host(codes).view(np.uint8), ref["codes"].view(np.uint8))
+        assert np.array_equal(host(scales).view(np.uint32), ref["scales"].view(np.uint32))
+
+
+@pytest.mark.parametrize("shape", [(128, 512), (384, 3072), (256, 12288)])
+def test_rotate_quantize_asym_weights(cr, shape):
+    N, K = shape
+    say(f"rq asym {shape}")
+    wb = wl.weight(13, N + K, N, K)
+    wb[5, 16:32] = 0      # a constant group
+    ref = ol.rotate_quantize(wb, 256, "asym_u4", "row_group", 16)
+    codes, scales, zeros, _ = cr.convrot_rotate_quantize(bf16_dev(wb), 256, 3, 2, 16)
+    assert np.array_equal(host(codes), ref["codes"])
+    assert np.array_equal(host(scales).view(np.uint16), ref["scales"].view(np.uint16))
+    assert np.array_equal(host(zeros), ref["zeros_packed"])
+
+
+@pytest.mark.parametrize("unsigned", [False, True])
+@pytest.mark.parametrize("lora", [None, "bf16", "f32"])
+@pytest.mark.parametrize("shape", [(16, 256), (45, 3072), (200, 1024)])
+def test_rotate_quantize_plain_g64(cr, unsigned, lora, shape):
+    rows, K = shape
+    say(f"rq plain unsigned={unsigned} lora={lora} {shape}")
+    if unsigned:
+        xb = wl.gelu_activation(14, rows + K, rows, K)
+    else:
+        xb = wl.activation(14, rows + K, rows, K)
+    shift = 0.171875 if unsigned else 0.0
+    ref = ol.rotate_quantize(xb, 0, "uint4_shift" if unsigned else "int4", "row_group", 64, shift)
+    l2 = wl.weight(14, 999, 32, K, std=0.05) if lora else None
+    codes, scales, _, la = cr.convrot_rotate_quantize(
+        bf16_dev(xb), 0, 2 if unsigned else 0, 2, 64, shift=shift,
+        lora_down=None if l2 is None else bf16_dev(l2), lora_act_f32=(lora == "f32"))
+    assert np.array_equal(host(codes), ref["codes"])
+    assert np.array_equal(host(scales).view(np.uint32), ref["scales"].view(np.uint32))
+    if lora:
+        la_ref32 = ol.lora_down(xb, l2, act_f32=True).astype(np.float64)
+        mag = np.abs(wl.f32_from_bf16_bits(xb)).astype(np.float64) @ np.abs(wl.f32_from_bf16_bits(l2)).astype(np.float64).T
+        got = host(la)
+        if lora == "f32":
+            assert np.all(np.abs(got - la_ref32) <= mag * 2 ** -20 + 1e-30)
+        else:
+            gotf = wl.f32_from_bf16_bits(got).astype(np.float64)
+            ulp = np.abs(la_ref32) * 2.0 ** -7 + mag * 2 ** -20
+            assert np.all(np.abs(gotf - la_ref32) <= ulp + 1e-30)
+
+
+@pytest.mark.parametrize("gran", ["tensor", "row", "row_group"])
+@pytest.mark.parametrize("shape", [(128, 512), (384, 3072)])
+def test_pack_w4a4(cr, gran, shape):
+    N, K = shape
+    say(f"pack w4a4 {gran} {shape}")
+    wb = wl.weight(15, N + K, N, K)
+    rot = 0 if gran == "row_group" else 256
+    qg = 64 if gran == "row_group" else None
+    ref = ol.prepare_w4a4(wb, rot, gran, qg)
+    codes, scales, _, _ = cr.convrot_rotate_quantize(bf16_dev(wb), rot, 0, GR[gran], qg or 0)
+    packed, pscales, _, wsum = cr.w4_pack_weights(codes, scales, N, K, 0, GR[gran], qg or 0, want_wsum=True)
+    assert np.array_equal(bytes_of(packed), ref["tiles"].reshape(-1))
+    if gran == "row_group":
+        assert np.array_equal(host(pscales).reshape(-1), ref["scales_tiles"].reshape(-1))
+    w = host(wsum)
+    assert np.allclose(w, ref["wsum"], rtol=1e-5, atol=1e-5 * np.abs(ref["wsum"]).max())
+
+
+@pytest.mark.parametrize("shape", [(128, 512), (256, 3072)])
+def test_pack_w4a8(cr, shape):
+    N, K = shape
+    say(f"pack w4a8 {shape}")
+    wb = wl.weight(16, N + K, N, K)
+    ref = ol.prepare_w4a8(wb)
+    codes, scales, zeros, _ = cr.convrot_rotate_quantize(bf16_dev(wb), 256, 3, 2, 16)
+    packed, pscales, pzeros, _ = cr.w4_pack_weights(codes, scales, N, K, 3, 2, 16, zeros=zeros)
+    assert np.array_equal(bytes_of(packed), ref["tiles"].reshape(-1))
+    assert np.array_equal(host(pscales).view(np.uint16).reshape(-1), ref["scales_tiles"].view(np.uint16).reshape(-1))
+    assert np.array_equal(host(pzeros).reshape(-1), ref["zeros_tiles"].reshape(-1))
+
+
+def test_pack_sampled_tiles_full_size(cr):
+    # full-size MLP-up weight (12288 x 3072): GPU pack vs oracle pack of sampled tiles
+    N, K = 12288, 3072
+    wb = wl.weight(17, 0, N, K)
+    codes, scales, zeros, _ = cr.convrot_rotate_quantize(bf16_dev(wb), 256, 3, 2, 16)
+    packed, _, _, _ = cr.w4_pack_weights(codes, scales, N, K, 3, 2, 16, zeros=zeros)
+    tiles = bytes_of(packed).reshape(N // 128, K // 64, 4096)
+    g = np.random.default_rng(0)
+    for tn, kt in zip(g.integers(0, N // 128, 6), g.integers(0, K // 64, 6)):
+        sub = ol.rotate_quantize(wb[128 * tn:128 * tn + 128], 256, "asym_u4", "row_group", 16)["values"]
+        ref = opack.tile_pack_w4a8(np.ascontiguousarray(sub[:, 64 * kt:64 * kt + 64]))
+        assert np.array_equal(tiles[tn, kt], ref[0, 0])
+
+
+def test_determinism(cr):
+    xb = wl.activation(18, 0, 333, 3072, n_outliers=10, outlier_scale=30.0)
+    x = bf16_dev(xb)
+    a = cr.convrot_rotate_quantize(x, 256, 0, 0)
+    b = cr.convrot_rotate_quantize(x, 256, 0, 0)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])

@@ -109,7 +109,7 @@ def test_raw_equals_exact_integer_product():
     assert np.array_equal(out["raw"], qa.astype(np.int64) @ qw.astype(np.int64).T)
     o8 = linear.w4a8_linear(x, w)
     z = np.repeat(o8["w"]["zeros"].astype(np.int64), 16, axis=1)
-    qw8 = pack.unpack_int4(pack.tile_unpack_w4a8(o8["w"]["tiles"]), False).astype(np.int64) - z
+    qw8 = pack.tile_unpack_w4a8(o8["w"]["tiles"]).astype(np.int64) - z
     assert np.array_equal(o8["raw"], o8["x"]["values"].astype(np.int64) @ qw8.T)
 
 

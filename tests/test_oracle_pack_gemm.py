@@ -66,12 +66,15 @@ def test_tile_pack_w4a4_shape_position_and_round_trip():
 
 def test_tile_pack_w4a8_position_and_round_trip():
     g = np.random.default_rng(22)
-    nat = g.integers(0, 256, size=(128, 64), dtype=np.uint8)           # N=128, K=128
-    t = pack.tile_pack_w4a8(nat)
-    assert np.array_equal(pack.tile_unpack_w4a8(t), nat)
-    # natural (row 70, byte 32 + 13): k-tile 1, byte 13 -> kg 1, half 1 (bytes 12..15), j 1;
-    # row 70 -> nb 2, lane%32 = 6 -> lane 32 + 6 = 38; offset 1024 + 2*256 + 38*4 + 1
-    assert t[0, 1, 1024 + 512 + 152 + 1] == nat[70, 45]
+    vals = g.integers(0, 16, size=(128, 128)).astype(np.uint8)         # N=128, K=128
+    t = pack.tile_pack_w4a8(vals)
+    assert t.shape == (1, 2, 4096)
+    assert np.array_equal(pack.tile_unpack_w4a8(t), vals)
+    # code (row 70, k 64 + 16 + 8 + 2): k-tile 1, kg 1, lane half 1, i 2;
+    # row 70 -> nb 2, lane 32 + 6 = 38; byte 1024 + 512 + 38*4 + 2, low nibble;
+    # its high nibble is k + 4
+    b = int(t[0, 1, 1024 + 512 + 152 + 2])
+    assert b & 0xF == vals[70, 90] and b >> 4 == vals[70, 94]
 
 
 def test_group_scale_tiles():

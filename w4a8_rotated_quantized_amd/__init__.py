@@ -1,0 +1,237 @@
+"""Thin Python binding of libconvrot.so, the gfx950 ConvRot low-bit linear.
+
+Argument marshalling only: every step of the path runs in the HIP kernels
+behind the C ABI declared in include/convrot.h. PyTorch provides device
+memory and the current stream. There is no fallback: if the library is
+missing this module raises at import, and every non-OK status raises
+ConvRotError with the library's status text.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "ConvRotError", "lib", "Q", "GRAN", "OUT",
+    "convrot_rotate_quantize", "w4_pack_weights", "w4a4_gemm", "w4a8_gemm",
+    "int8_tensorwise_gemm", "convrot_rq_workspace_size", "w4_packed_bytes",
+    "get_counters", "reset_counters", "device_check", "status_string",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libconvrot.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run __graft_entry__.build() "
+        "(hipcc --offload-arch=gfx950). There is no non-HIP fallback.")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+
+class Q:
+    SYM_INT4 = 0
+    SYM_INT8 = 1
+    UNSIGNED_INT4_SHIFT = 2
+    ASYM_UINT4 = 3
+
+
+class GRAN:
+    TENSOR = 0
+    ROW = 1
+    ROW_GROUP = 2
+
+
+class OUT:
+    BF16 = 0
+    F32 = 1
+    I32_RAW = 2
+
+
+class _Counters(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_uint64 * 8), ("fallbacks", ctypes.c_uint64)]
+
+
+_vp, _i64, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "convrot_status_string": (ctypes.c_char_p, [_i]),
+    "convrot_last_hip_error": (_i, []),
+    "convrot_device_check": (_i, []),
+    "convrot_get_counters": (None, [ctypes.POINTER(_Counters)]),
+    "convrot_reset_counters": (None, []),
+    "convrot_rq_workspace_size": (_sz, [_i64, _i64, _i, _i, _i, _i]),
+    "convrot_rotate_quantize": (_i, [_vp, _i64, _i64, _i64, _i, _i, _i, _i, _f, _vp, _i, _vp, _i,
+                                     _vp, _vp, _vp, _vp, _sz, _vp]),
+    "w4_packed_bytes": (_sz, [_i64, _i64, _i, _i, _i, _i]),
+    "w4_pack_weights": (_i, [_vp, _vp, _vp, _i64, _i64, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "w4a4_gemm": (_i, [_vp, _vp, _i, _i, _f, _vp, _vp, _i, _vp, _vp, _i, _vp, _i, _vp,
+                       _vp, _i, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
+    "w4a8_gemm": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _i, _i64, _i64, _i64, _i64,
+                       _vp, _sz, _vp]),
+    "int8_tensorwise_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i64, _i64, _i64, _i64,
+                                  _vp, _sz, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class ConvRotError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.convrot_status_string(status).decode()
+        if status == 7:
+            msg += f" (hipError {lib.convrot_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+
+
+def status_string(status: int) -> str:
+    return lib.convrot_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise ConvRotError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def device_check() -> int:
+    return lib.convrot_device_check()
+
+
+def get_counters():
+    c = _Counters()
+    lib.convrot_get_counters(ctypes.byref(c))
+    return {"rotate_quantize": c.launches[0], "pack": c.launches[1], "w4a4": c.launches[2],
+            "w4a8": c.launches[3], "int8": c.launches[4], "fallbacks": c.fallbacks}
+
+
+def reset_counters():
+    lib.convrot_reset_counters()
+
+
+def convrot_rq_workspace_size(rows, K, rot_group, qtype, gran, q_group=0) -> int:
+    return lib.convrot_rq_workspace_size(rows, K, rot_group, qtype, gran, q_group)
+
+
+def w4_packed_bytes(N, K, qtype, gran, q_group, which) -> int:
+    return lib.w4_packed_bytes(N, K, qtype, gran, q_group, which)
+
+
+def _scale_numel(rows, K, qtype, gran, q_group):
+    if gran == GRAN.TENSOR:
+        return (1,)
+    if gran == GRAN.ROW:
+        return (rows,)
+    return (rows, K // q_group)
+
+
+def convrot_rotate_quantize(x, rot_group=256, qtype=Q.SYM_INT4, gran=GRAN.TENSOR, q_group=0,
+                            shift=0.0, lora_down=None, lora_act_f32=False,
+                            codes=None, scales=None, zeros=None, lora_act=None, workspace=None,
+                            stream=None):
+    """x: bf16 [rows, K] (row stride may exceed K). Returns
+    (codes, scales, zeros, lora_act); outputs are allocated when not given."""
+    rows, K = x.shape
+    ldx = x.stride(0)
+    dev = x.device
+    if codes is None:
+        if qtype == Q.SYM_INT8:
+            codes = torch.empty((rows, K), dtype=torch.int8, device=dev)
+        else:
+            codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        sdt = torch.float16 if qtype == Q.ASYM_UINT4 else torch.float32
+        scales = torch.empty(_scale_numel(rows, K, qtype, gran, q_group), dtype=sdt, device=dev)
+    if zeros is None and qtype == Q.ASYM_UINT4:
+        zeros = torch.empty((rows, K // 32), dtype=torch.uint8, device=dev)
+    R = 0
+    if lora_down is not None:
+        R = lora_down.shape[0]
+        if lora_act is None:
+            lora_act = torch.empty((rows, R), dtype=torch.float32 if lora_act_f32 else torch.bfloat16,
+                                   device=dev)
+    need = convrot_rq_workspace_size(rows, K, rot_group, qtype, gran, q_group)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.convrot_rotate_quantize(_ptr(x), rows, K, ldx, rot_group, qtype, gran, q_group,
+                                     float(shift), _ptr(lora_down), R, _ptr(lora_act),
+                                     int(bool(lora_act_f32)), _ptr(codes), _ptr(scales), _ptr(zeros),
+                                     _ptr(workspace), wsb, _stream(stream))
+    _check(st, "convrot_rotate_quantize")
+    return codes, scales, zeros, lora_act
+
+
+def w4_pack_weights(codes, scales, N, K, qtype=Q.SYM_INT4, gran=GRAN.TENSOR, q_group=0, zeros=None,
+                    want_wsum=False, stream=None):
+    """Returns (packed, packed_scales, packed_zeros, w_sum)."""
+    dev = codes.device
+    packed = torch.empty(w4_packed_bytes(N, K, qtype, gran, q_group, 0), dtype=torch.uint8, device=dev)
+    nsc = w4_packed_bytes(N, K, qtype, gran, q_group, 1)
+    packed_scales = None
+    if nsc:
+        packed_scales = torch.empty(nsc, dtype=torch.uint8, device=dev)
+    nz = w4_packed_bytes(N, K, qtype, gran, q_group, 2)
+    packed_zeros = torch.empty(nz, dtype=torch.uint8, device=dev) if nz else None
+    w_sum = torch.empty(N, dtype=torch.float32, device=dev) if want_wsum else None
+    st = lib.w4_pack_weights(_ptr(codes), _ptr(scales), _ptr(zeros), N, K, qtype, gran, q_group,
+                             _ptr(packed), _ptr(packed_scales), _ptr(packed_zeros), _ptr(w_sum),
+                             _stream(stream))
+    _check(st, "w4_pack_weights")
+    if packed_scales is not None:
+        packed_scales = packed_scales.view(torch.float16 if qtype == Q.ASYM_UINT4 else torch.float32)
+    return packed, packed_scales, packed_zeros, w_sum
+
+
+def _out(M, N, out_type, dev, out):
+    if out is not None:
+        return out
+    dt = {OUT.BF16: torch.bfloat16, OUT.F32: torch.float32, OUT.I32_RAW: torch.int32}[out_type]
+    return torch.empty((M, N), dtype=dt, device=dev)
+
+
+def w4a4_gemm(a_codes, a_scales, a_gran, w_packed, w_scales, w_gran, M, N, K,
+              a_unsigned=False, a_shift=0.0, w_sum=None, lora_act=None, lora_up=None,
+              bias=None, out_type=OUT.BF16, out=None, stream=None):
+    out = _out(M, N, out_type, a_codes.device, out)
+    lora_f32 = int(lora_act is not None and lora_act.dtype == torch.float32)
+    R = 0 if lora_up is None else lora_up.shape[1]
+    st = lib.w4a4_gemm(_ptr(a_codes), _ptr(a_scales), a_gran, int(bool(a_unsigned)), float(a_shift),
+                       _ptr(w_packed), _ptr(w_scales), w_gran, _ptr(w_sum),
+                       _ptr(lora_act), lora_f32, _ptr(lora_up), R, _ptr(bias),
+                       _ptr(out), out_type, out.stride(0), M, N, K, None, 0, _stream(stream))
+    _check(st, "w4a4_gemm")
+    return out
+
+
+def w4a8_gemm(a_codes, a_scales, a_gran, w_packed, w_scales, w_zeros, M, N, K, group=16,
+              bias=None, out_type=OUT.BF16, out=None, stream=None):
+    out = _out(M, N, out_type, a_codes.device, out)
+    st = lib.w4a8_gemm(_ptr(a_codes), _ptr(a_scales), a_gran, _ptr(w_packed), _ptr(w_scales),
+                       _ptr(w_zeros), group, _ptr(bias), _ptr(out), out_type, out.stride(0),
+                       M, N, K, None, 0, _stream(stream))
+    _check(st, "w4a8_gemm")
+    return out
+
+
+def int8_tensorwise_gemm(a_codes, a_scale, w, w_scale, M, N, K, bias=None, out_type=OUT.BF16,
+                         out=None, stream=None):
+    out = _out(M, N, out_type, a_codes.device, out)
+    st = lib.int8_tensorwise_gemm(_ptr(a_codes), _ptr(a_scale), _ptr(w), _ptr(w_scale), _ptr(bias),
+                                  _ptr(out), out_type, out.stride(0), M, N, K, None, 0,
+                                  _stream(stream))
+    _check(st, "int8_tensorwise_gemm")
+    return out

@@ -1,0 +1,365 @@
+// C-ABI host layer: argument validation (before any HIP call), device /
+// architecture check, dispatch to the gfx950 kernels, status strings and
+// dispatch counters.
+//
+// "Qwen3-4B ConvRot W4A4" page, Hardware: a converter that runs only when the
+// native kernels resolve, because a dequantizing backend would silently stand
+// in for them; "Qwen-Image-Edit-2511 - INT4 tensorwise W4A4" page, Runtime
+// requirement: an unsupported format fails with a clear "format not
+// available" error. Both are this layer's conventions: no fallback exists,
+// unsupported inputs return a status. Dispatch counting follows the kernel
+// call / dequantize counts of the Qwen3-4B page ("What it actually looks like").
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/convrot.h"
+#include "kernels.h"
+
+namespace {
+
+std::atomic<uint64_t> g_launch[8];
+thread_local int g_last_hip = 0;
+
+enum { E_RQ = 0, E_PACK = 1, E_W4A4 = 2, E_W4A8 = 3, E_INT8 = 4 };
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+cr_status hip_fail(hipError_t e) {
+  g_last_hip = (int)e;
+  return CR_ERR_HIP;
+}
+
+// per-device cache: 0 unknown, 1 gfx950, 2 other
+std::mutex g_dev_mu;
+int g_dev_kind[64];
+
+cr_status device_check() {
+  int count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return CR_ERR_NO_DEVICE;
+  }
+  int dev = 0;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= 64) return CR_ERR_NO_DEVICE;
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_dev_kind[dev] == 0) {
+      hipDeviceProp_t prop;
+      e = hipGetDeviceProperties(&prop, dev);
+      if (e != hipSuccess) return hip_fail(e);
+      g_dev_kind[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    }
+    if (g_dev_kind[dev] != 1) return CR_ERR_UNSUPPORTED_ARCH;
+  }
+  return CR_OK;
+}
+
+cr_status finish_launch(hipError_t e, int entry, uint64_t n) {
+  if (e != hipSuccess) return hip_fail(e);
+  g_launch[entry].fetch_add(n, std::memory_order_relaxed);
+  return CR_OK;
+}
+
+constexpr int64_t KMAX = 32768;
+constexpr int64_t DIM_MAX = (int64_t)1 << 31;
+
+}  // namespace
+
+extern "C" {
+
+const char* convrot_status_string(cr_status s) {
+  switch (s) {
+    case CR_OK: return "ok";
+    case CR_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case CR_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case CR_ERR_UNSUPPORTED_FORMAT: return "format not available";
+    case CR_ERR_NO_DEVICE: return "no HIP device";
+    case CR_ERR_UNSUPPORTED_ARCH: return "device is not gfx950 (MI355X); no fallback path exists";
+    case CR_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case CR_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int convrot_last_hip_error(void) { return g_last_hip; }
+
+cr_status convrot_device_check(void) { return device_check(); }
+
+void convrot_get_counters(cr_counters* out) {
+  if (!out) return;
+  for (int i = 0; i < 8; ++i) out->launches[i] = g_launch[i].load(std::memory_order_relaxed);
+  out->fallbacks = 0;
+}
+
+void convrot_reset_counters(void) {
+  for (int i = 0; i < 8; ++i) g_launch[i].store(0, std::memory_order_relaxed);
+}
+
+// ---------------------------------------------------------------------------
+// rotate + quantize
+// ---------------------------------------------------------------------------
+static cr_status rq_validate(const void* x, int64_t rows, int64_t K, int64_t ldx, int rot_group,
+                             cr_qtype qtype, cr_gran gran, int q_group, const void* lora_down, int R,
+                             const void* lora_act, const void* codes, const void* scales, const void* zeros) {
+  if (!x || !codes || !scales) return CR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return CR_ERR_INVALID_ARGUMENT;
+  if ((int)qtype < 0 || (int)qtype > 3 || (int)gran < 0 || (int)gran > 2) return CR_ERR_INVALID_ARGUMENT;
+  if (rows < 1 || K < 1 || ldx < K || rows >= DIM_MAX || ldx >= DIM_MAX) return CR_ERR_UNSUPPORTED_SHAPE;
+  if (ldx % 8 != 0 || K > KMAX) return CR_ERR_UNSUPPORTED_SHAPE;
+  if (rot_group != 0 && rot_group != 256) return CR_ERR_UNSUPPORTED_FORMAT;
+  if (rot_group == 256) {
+    if (K % 256 != 0) return CR_ERR_UNSUPPORTED_SHAPE;
+    if (lora_down) return CR_ERR_UNSUPPORTED_FORMAT;
+    if (qtype == CR_Q_SYM_INT4 || qtype == CR_Q_SYM_INT8) {
+      if (gran == CR_GRAN_ROW_GROUP && q_group != 64) return CR_ERR_UNSUPPORTED_FORMAT;
+    } else if (qtype == CR_Q_ASYM_UINT4) {
+      if (gran != CR_GRAN_ROW_GROUP || q_group != 16) return CR_ERR_UNSUPPORTED_FORMAT;
+      if (!zeros || !aligned16(zeros)) return CR_ERR_INVALID_ARGUMENT;
+    } else {
+      return CR_ERR_UNSUPPORTED_FORMAT;   // the shift path is for unrotated post-GELU inputs
+    }
+  } else {
+    if (K % 64 != 0) return CR_ERR_UNSUPPORTED_SHAPE;
+    if (!(qtype == CR_Q_SYM_INT4 || qtype == CR_Q_UNSIGNED_INT4_SHIFT)) return CR_ERR_UNSUPPORTED_FORMAT;
+    if (gran != CR_GRAN_ROW_GROUP || q_group != 64) return CR_ERR_UNSUPPORTED_FORMAT;
+    if (lora_down) {
+      if (R != 32) return CR_ERR_UNSUPPORTED_FORMAT;
+      if (!lora_act || !aligned16(lora_down) || !aligned16(lora_act)) return CR_ERR_INVALID_ARGUMENT;
+    }
+  }
+  return CR_OK;
+}
+
+size_t convrot_rq_workspace_size(int64_t rows, int64_t K, int rot_group, cr_qtype qtype, cr_gran gran,
+                                 int q_group) {
+  (void)q_group;
+  if (rot_group != 256 || gran != CR_GRAN_TENSOR || rows < 1 || K < 256 || K % 256) return 0;
+  if (!(qtype == CR_Q_SYM_INT4 || qtype == CR_Q_SYM_INT8)) return 0;
+  cr::RQGeometry g = cr::rq_geometry(rows, K, 0);
+  return (size_t)g.nblk * sizeof(float);
+}
+
+cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx, int rot_group,
+                                  cr_qtype qtype, cr_gran gran, int q_group, float shift,
+                                  const void* lora_down, int R, void* lora_act, int lora_act_f32,
+                                  void* codes, void* scales, void* zeros, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  cr_status st = rq_validate(x, rows, K, ldx, rot_group, qtype, gran, q_group, lora_down, R, lora_act,
+                             codes, scales, zeros);
+  if (st != CR_OK) return st;
+  const size_t need = convrot_rq_workspace_size(rows, K, rot_group, qtype, gran, q_group);
+  if (need > 0) {
+    if (!workspace || !aligned16(workspace)) return CR_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < need) return CR_ERR_WORKSPACE_TOO_SMALL;
+  }
+  st = device_check();
+  if (st != CR_OK) return st;
+  cr::RQParams p{};
+  p.x = static_cast<const uint16_t*>(x);
+  p.rows = rows;
+  p.K = K;
+  p.ldx = ldx;
+  p.rot_group = rot_group;
+  p.qtype = qtype;
+  p.gran = gran;
+  p.q_group = q_group;
+  p.shift = shift;
+  p.lora_down = static_cast<const uint16_t*>(lora_down);
+  p.R = R;
+  p.lora_act = lora_act;
+  p.lora_f32 = lora_act_f32;
+  p.codes = codes;
+  p.scales = scales;
+  p.zeros = zeros;
+  p.ws = static_cast<float*>(workspace);
+  const uint64_t nl = (rot_group == 256 && gran == CR_GRAN_TENSOR && qtype != CR_Q_ASYM_UINT4) ? 2 : 1;
+  return finish_launch(cr::launch_rotate_quantize(p, stream), E_RQ, nl);
+}
+
+// ---------------------------------------------------------------------------
+// weight packing
+// ---------------------------------------------------------------------------
+size_t w4_packed_bytes(int64_t N, int64_t K, cr_qtype qtype, cr_gran gran, int q_group, int which) {
+  if (N < 128 || K < 64 || N % 128 || K % 64) return 0;
+  switch (which) {
+    case 0: return (size_t)(N * K / 2);
+    case 1:
+      if (qtype == CR_Q_ASYM_UINT4) return (size_t)(N * (K / 16) * 2);
+      if (gran == CR_GRAN_ROW_GROUP && q_group == 64) return (size_t)(N * (K / 64) * 4);
+      return 0;
+    case 2: return qtype == CR_Q_ASYM_UINT4 ? (size_t)(N * (K / 16)) : 0;
+  }
+  return 0;
+}
+
+cr_status w4_pack_weights(const void* codes, const void* scales, const void* zeros, int64_t N, int64_t K,
+                          cr_qtype qtype, cr_gran gran, int q_group, void* packed, void* packed_scales,
+                          void* packed_zeros, float* w_sum, hipStream_t stream) {
+  if (!codes || !packed || !scales) return CR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(codes) || !aligned16(packed) || !aligned16(scales)) return CR_ERR_INVALID_ARGUMENT;
+  if ((int)qtype < 0 || (int)qtype > 3 || (int)gran < 0 || (int)gran > 2) return CR_ERR_INVALID_ARGUMENT;
+  if (N < 128 || K < 64 || N % 128 || K % 64 || K > KMAX || N >= DIM_MAX) return CR_ERR_UNSUPPORTED_SHAPE;
+  if (qtype == CR_Q_SYM_INT4) {
+    if (gran == CR_GRAN_ROW_GROUP) {
+      if (q_group != 64) return CR_ERR_UNSUPPORTED_FORMAT;
+      if (!packed_scales || !aligned16(packed_scales)) return CR_ERR_INVALID_ARGUMENT;
+    }
+    if (w_sum && !aligned16(w_sum)) return CR_ERR_INVALID_ARGUMENT;
+  } else if (qtype == CR_Q_ASYM_UINT4) {
+    if (gran != CR_GRAN_ROW_GROUP || q_group != 16) return CR_ERR_UNSUPPORTED_FORMAT;
+    if (!zeros || !packed_scales || !packed_zeros) return CR_ERR_INVALID_ARGUMENT;
+    if (!aligned16(zeros) || !aligned16(packed_scales) || !aligned16(packed_zeros)) return CR_ERR_INVALID_ARGUMENT;
+    if (w_sum) return CR_ERR_UNSUPPORTED_FORMAT;
+  } else {
+    return CR_ERR_UNSUPPORTED_FORMAT;
+  }
+  cr_status st = device_check();
+  if (st != CR_OK) return st;
+  cr::PackParams p{};
+  p.codes = static_cast<const uint8_t*>(codes);
+  p.scales = scales;
+  p.zeros = static_cast<const uint8_t*>(zeros);
+  p.N = N;
+  p.K = K;
+  p.qtype = qtype;
+  p.gran = gran;
+  p.q_group = q_group;
+  p.packed = static_cast<uint8_t*>(packed);
+  p.packed_scales = packed_scales;
+  p.packed_zeros = static_cast<uint8_t*>(packed_zeros);
+  p.w_sum = w_sum;
+  uint64_t nl = 1 + (qtype == CR_Q_ASYM_UINT4 ? 1 : 0) + (gran == CR_GRAN_ROW_GROUP && qtype == CR_Q_SYM_INT4) +
+                (w_sum ? 1 : 0);
+  return finish_launch(cr::launch_pack(p, stream), E_PACK, nl);
+}
+
+// ---------------------------------------------------------------------------
+// GEMMs
+// ---------------------------------------------------------------------------
+static cr_status gemm_common(const void* a, const void* w, const void* out, cr_out out_type, int64_t ldc,
+                             int64_t M, int64_t N, int64_t K, const void* bias) {
+  if (!a || !w || !out) return CR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(a) || !aligned16(w) || !aligned16(out)) return CR_ERR_INVALID_ARGUMENT;
+  if (bias && !aligned16(bias)) return CR_ERR_INVALID_ARGUMENT;
+  if ((int)out_type < 0 || (int)out_type > 2) return CR_ERR_INVALID_ARGUMENT;
+  if (M < 1 || N < 128 || K < 128 || N % 128 || K % 128 || K > KMAX) return CR_ERR_UNSUPPORTED_SHAPE;
+  if (M >= DIM_MAX || N >= DIM_MAX || ldc < N || ldc % 8 != 0 || ldc >= DIM_MAX) return CR_ERR_UNSUPPORTED_SHAPE;
+  return CR_OK;
+}
+
+cr_status w4a4_gemm(const void* a_codes, const float* a_scales, cr_gran a_gran, int a_unsigned, float a_shift,
+                    const void* w_packed, const float* w_scales, cr_gran w_gran, const float* w_sum,
+                    const void* lora_act, int lora_act_f32, const void* lora_up, int R, const void* bias,
+                    void* out, cr_out out_type, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  cr_status st = gemm_common(a_codes, w_packed, out, out_type, ldc, M, N, K, bias);
+  if (st != CR_OK) return st;
+  if (!a_scales || !w_scales || !aligned16(a_scales) || !aligned16(w_scales)) return CR_ERR_INVALID_ARGUMENT;
+  if ((int)a_gran < 0 || (int)a_gran > 2 || (int)w_gran < 0 || (int)w_gran > 2) return CR_ERR_INVALID_ARGUMENT;
+  const bool grouped = a_gran == CR_GRAN_ROW_GROUP;
+  if (grouped != (w_gran == CR_GRAN_ROW_GROUP)) return CR_ERR_UNSUPPORTED_FORMAT;
+  if (a_unsigned) {
+    if (!w_sum || !aligned16(w_sum)) return CR_ERR_INVALID_ARGUMENT;
+  }
+  if (lora_act || lora_up) {
+    if (!lora_act || !lora_up || R != 32) return CR_ERR_UNSUPPORTED_FORMAT;
+    if (!aligned16(lora_act) || !aligned16(lora_up)) return CR_ERR_INVALID_ARGUMENT;
+  }
+  st = device_check();
+  if (st != CR_OK) return st;
+  cr::GemmParams p{};
+  p.a = static_cast<const uint8_t*>(a_codes);
+  p.a_scales = a_scales;
+  p.a_gran = a_gran;
+  p.act = a_unsigned ? cr::ACT_U4 : cr::ACT_S4;
+  p.a_shift = a_shift;
+  p.w = static_cast<const uint8_t*>(w_packed);
+  p.w_scales = w_scales;
+  p.w_gran = w_gran;
+  p.wgt = cr::WGT_S4T;
+  p.w_sum = w_sum;
+  p.lora_act = lora_act;
+  p.lora_f32 = lora_act_f32;
+  p.lora_up = static_cast<const uint16_t*>(lora_up);
+  p.R = R;
+  p.bias = static_cast<const uint16_t*>(bias);
+  p.out = out;
+  p.out_type = out_type;
+  p.ldc = ldc;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.grouped = grouped ? 1 : 0;
+  return finish_launch(cr::launch_gemm_int(p, stream), E_W4A4, 1);
+}
+
+cr_status w4a8_gemm(const void* a_codes, const float* a_scales, cr_gran a_gran, const void* w_packed,
+                    const void* w_scales, const void* w_zeros, int group, const void* bias, void* out,
+                    cr_out out_type, int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  cr_status st = gemm_common(a_codes, w_packed, out, out_type, ldc, M, N, K, bias);
+  if (st != CR_OK) return st;
+  if (!a_scales || !w_scales || !w_zeros) return CR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(a_scales) || !aligned16(w_scales) || !aligned16(w_zeros)) return CR_ERR_INVALID_ARGUMENT;
+  if (group != 16) return CR_ERR_UNSUPPORTED_FORMAT;
+  if (!(a_gran == CR_GRAN_ROW || a_gran == CR_GRAN_TENSOR)) return CR_ERR_UNSUPPORTED_FORMAT;
+  st = device_check();
+  if (st != CR_OK) return st;
+  cr::GemmParams p{};
+  p.a = static_cast<const uint8_t*>(a_codes);
+  p.a_scales = a_scales;
+  p.a_gran = a_gran;
+  p.act = cr::ACT_I8;
+  p.w = static_cast<const uint8_t*>(w_packed);
+  p.w_scales16 = static_cast<const uint16_t*>(w_scales);
+  p.w_zeros = static_cast<const uint8_t*>(w_zeros);
+  p.bias = static_cast<const uint16_t*>(bias);
+  p.out = out;
+  p.out_type = out_type;
+  p.ldc = ldc;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  return finish_launch(cr::launch_gemm_w4a8(p, stream), E_W4A8, 1);
+}
+
+cr_status int8_tensorwise_gemm(const void* a_codes, const float* a_scale, const void* w, const float* w_scale,
+                               const void* bias, void* out, cr_out out_type, int64_t ldc, int64_t M, int64_t N,
+                               int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  cr_status st = gemm_common(a_codes, w, out, out_type, ldc, M, N, K, bias);
+  if (st != CR_OK) return st;
+  if (!a_scale || !w_scale || !aligned16(a_scale) || !aligned16(w_scale)) return CR_ERR_INVALID_ARGUMENT;
+  st = device_check();
+  if (st != CR_OK) return st;
+  cr::GemmParams p{};
+  p.a = static_cast<const uint8_t*>(a_codes);
+  p.a_scales = a_scale;
+  p.a_gran = CR_GRAN_TENSOR;
+  p.act = cr::ACT_I8;
+  p.w = static_cast<const uint8_t*>(w);
+  p.w_scales = w_scale;
+  p.w_gran = CR_GRAN_TENSOR;
+  p.wgt = cr::WGT_I8N;
+  p.bias = static_cast<const uint16_t*>(bias);
+  p.out = out;
+  p.out_type = out_type;
+  p.ldc = ldc;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  return finish_launch(cr::launch_gemm_int(p, stream), E_INT8, 1);
+}
+
+}  // extern "C"

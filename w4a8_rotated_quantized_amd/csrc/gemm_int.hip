@@ -1,0 +1,538 @@
+// Integer-matrix-core GEMMs of the ConvRot low-bit linear (gfx950):
+//   W4A4: int4 activations x tile-packed int4 weights (tensorwise, per-row or
+//         per-64-group scales, unsigned shifted activations, fused low-rank
+//         up-projection, bias);
+//   INT8: int8 activations x natural int8 weights (tensorwise).
+//
+// "Qwen-Image-Edit-2511 - INT4 tensorwise W4A4" page, Measurements: a fused
+// INT4 matmul with a rank-one (s_a x s_w) rescale; intro: INT8 tensorwise
+// layers in the same model. "Qwen-Image-Edit-2511 INT4 (ComfyUI Optimized)",
+// Key Technical Optimizations and Kernel Engineering: tile-packed weights,
+// LoRA-up fused into the epilogue, scales staged in shared memory, unsigned
+// post-GELU activations with a +0.171875 shift.
+//
+// gfx950 has no int4 matrix instruction, so int4 codes are widened exactly to
+// int8 in registers: a signed nibble q becomes the byte 16*q (a mask, no
+// shift), so one v_mfma_i32_16x16x64_i8 accumulates 256 * sum(qa*qw) (or
+// 16 * sum for unsigned activation bytes), and the true integer is recovered
+// by an exact arithmetic right shift.
+//
+// Operand roles: the MFMA A operand is the weight (16 output channels n),
+// the B operand the activation (16 tokens m). Each lane of the 16x16 result
+// then holds one token and four consecutive output channels, so a bf16
+// result leaves as one 8-byte store.
+#include "common.h"
+#include "kernels.h"
+
+namespace cr {
+
+template <int ACT>
+CR_DEV v4i widen_act(const uint8_t* lds) {
+  if constexpr (ACT == ACT_I8) {
+    return *reinterpret_cast<const v4i*>(lds);
+  } else {
+    u32x2 x = *reinterpret_cast<const u32x2*>(lds);
+    return ACT == ACT_S4 ? widen_s4x16(x) : widen_u4(x);
+  }
+}
+template <int WGT>
+CR_DEV v4i widen_wgt(const uint8_t* lds) {
+  if constexpr (WGT == WGT_I8N) {
+    return *reinterpret_cast<const v4i*>(lds);
+  } else {
+    return widen_s4x16(*reinterpret_cast<const u32x2*>(lds));
+  }
+}
+// right shift that recovers sum(qa*qw) from the widened accumulation
+template <int ACT, int WGT>
+constexpr int acc_shift() {
+  return (ACT == ACT_S4 ? 4 : 0) + (WGT == WGT_S4T ? 4 : 0);
+}
+
+CR_DEV v4i mfma_i8(v4i a, v4i b, v4i c) { return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0); }
+
+// ---------------------------------------------------------------------------
+// Fused epilogue for one 16x16 block: lane holds token m and channels n..n+3.
+// ---------------------------------------------------------------------------
+struct EpiCtx {
+  float sa_t;   // TENSOR activation scale
+  float sw_t;   // TENSOR weight scale
+};
+
+template <int OUT>
+CR_DEV void store4(const GemmParams& p, int64_t m, int64_t n, const float (&y)[4], const int (&raw)[4]) {
+  if (m >= p.M) return;
+  if constexpr (OUT == CR_OUT_I32_RAW) {
+    *reinterpret_cast<v4i*>(reinterpret_cast<int32_t*>(p.out) + m * p.ldc + n) = v4i{raw[0], raw[1], raw[2], raw[3]};
+  } else if constexpr (OUT == CR_OUT_F32) {
+    *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.out) + m * p.ldc + n) = v4f{y[0], y[1], y[2], y[3]};
+  } else {
+    u32x2 o;
+    o[0] = f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
+    o[1] = f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + m * p.ldc + n) = o;
+  }
+}
+
+// y += lora_act[m, :] . lora_up[n..n+3, :] for the 16x16 block (tokens mb.., channels nb..)
+CR_DEV void lora_up_block(const GemmParams& p, int64_t mb, int64_t nb, int l, float (&y)[4]) {
+  const int64_t mrow = (mb + (l & 15) < p.M) ? mb + (l & 15) : p.M - 1;
+  const int64_t nrow = nb + (l & 15);
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  if (!p.lora_f32) {
+    const uint16_t* la = reinterpret_cast<const uint16_t*>(p.lora_act) + mrow * 32 + (l >> 4) * 8;
+    const uint16_t* lu = p.lora_up + nrow * 32 + (l >> 4) * 8;
+    v8bf a = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(lu));
+    v8bf b = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(la));
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  } else {
+    const float* la = reinterpret_cast<const float*>(p.lora_act) + mrow * 32;
+    const uint16_t* lu = p.lora_up + nrow * 32;
+#pragma unroll
+    for (int r0 = 0; r0 < 32; r0 += 4) {
+      float a = __uint_as_float((uint32_t)lu[r0 + (l >> 4)] << 16);
+      float b = la[r0 + (l >> 4)];
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] += acc[i];
+}
+
+// Everything after the float value s_a*s_w*acc (or the group sum) is known.
+template <int OUT>
+CR_DEV void finish_block(const GemmParams& p, int64_t m, int64_t n, int64_t mb, int l, float (&y)[4],
+                         const int (&raw)[4]) {
+  if constexpr (OUT != CR_OUT_I32_RAW) {
+    if (p.act == ACT_U4) {
+      const v4f ws = *reinterpret_cast<const v4f*>(p.w_sum + n);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[i] = __builtin_fmaf(-p.a_shift, ws[i], y[i]);
+    }
+    if (p.lora_act) lora_up_block(p, mb, n - (l >> 4) * 4, l, y);
+    if (p.bias) {
+      u32x2 b = *reinterpret_cast<const u32x2*>(p.bias + n);
+      y[0] += bf16_lo(b[0]);
+      y[1] += bf16_hi(b[0]);
+      y[2] += bf16_lo(b[1]);
+      y[3] += bf16_hi(b[1]);
+    }
+  }
+  store4<OUT>(p, m, n, y, raw);
+}
+
+// ---------------------------------------------------------------------------
+// Large-M kernel: BM x BN block tile, WM x WN waves, BK = 128 per stage
+// (two 64-deep k-tiles), double-buffered LDS. LDS operand layout per stage:
+// [k-tile][16-row block][64 lanes][frag bytes], i.e. fragment order, so every
+// fragment read is 64 consecutive 8/16-byte words.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int ACT, int WGT, bool GROUPED, int OUT>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_big_kernel(GemmParams p) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int FM = BM / WM / 16;
+  constexpr int FN = BN / WN / 16;
+  constexpr int AFB = (ACT == ACT_I8) ? 16 : 8;
+  constexpr int WFB = (WGT == WGT_I8N) ? 16 : 8;
+  constexpr int A_ST = 2 * (BM / 16) * 64 * AFB;
+  constexpr int W_ST = 2 * (BN / 16) * 64 * WFB;
+  constexpr bool GRP = GROUPED && OUT != CR_OUT_I32_RAW;
+  constexpr int S_ST = GRP ? 2 * (BM + BN) * 4 : 0;
+  constexpr int STAGE = A_ST + W_ST + S_ST;
+  constexpr int SH = acc_shift<ACT, WGT>();
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int l = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+
+  // block -> tile, XCD-aware: consecutive block ids land on different XCDs,
+  // so give each XCD a contiguous range of tiles, ordered in bands of 8 tile
+  // rows walked column by column (neighbouring tiles share operands in L2).
+  const int ntm = (int)((p.M + BM - 1) / BM);
+  const int ntn = (int)(p.N / BN);
+  const int ntiles = ntm * ntn;
+  int t = blockIdx.x;
+  if ((ntiles & 7) == 0) t = (t & 7) * (ntiles >> 3) + (t >> 3);
+  constexpr int GM = 8;
+  const int band = t / (GM * ntn);
+  const int rows_in_band = min(GM, ntm - band * GM);
+  const int within = t - band * GM * ntn;
+  const int tn = within / rows_in_band;
+  const int tm = band * GM + within % rows_in_band;
+  const int64_t m0 = (int64_t)tm * BM;
+  const int64_t n0 = (int64_t)tn * BN;
+  const int64_t K = p.K;
+  const int nkb = (int)(K / 128);
+
+  // ---- global -> register prefetch descriptors ----
+  constexpr int A_PIECES = (ACT == ACT_I8) ? BM * 8 : BM * 4;    // 16-byte pieces per stage
+  constexpr int W_PIECES = (WGT == WGT_I8N) ? BN * 8 : BN * 4;
+  constexpr int PA = (A_PIECES + NT - 1) / NT;
+  constexpr int PW = (W_PIECES + NT - 1) / NT;
+  u32x4 ra[PA], rw[PW];
+  float rs[GRP ? (2 * (BM + BN) + NT - 1) / NT : 1];
+
+  auto gload = [&](int kb) {
+    const int64_t k0 = (int64_t)kb * 128;
+#pragma unroll
+    for (int j = 0; j < PA; ++j) {
+      int pc = tid + j * NT;
+      if (pc < A_PIECES) {
+        if constexpr (ACT == ACT_I8) {
+          int row = pc >> 3, part = pc & 7;
+          int64_t m = imin64(m0 + row, p.M - 1);
+          ra[j] = *reinterpret_cast<const u32x4*>(p.a + m * K + k0 + part * 16);
+        } else {
+          int row = pc >> 2, part = pc & 3;
+          int64_t m = imin64(m0 + row, p.M - 1);
+          ra[j] = *reinterpret_cast<const u32x4*>(p.a + m * (K / 2) + k0 / 2 + part * 16);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+      int pc = tid + j * NT;
+      if (pc < W_PIECES) {
+        if constexpr (WGT == WGT_I8N) {
+          int row = pc >> 3, part = pc & 7;
+          rw[j] = *reinterpret_cast<const u32x4*>(p.w + (n0 + row) * K + k0 + part * 16);
+        } else {
+          int chunk = pc >> 5, off = (pc & 31) * 16;
+          int kt = chunk / (BN / 16), nb = chunk % (BN / 16);
+          int64_t n = n0 + 16 * nb;
+          rw[j] = *reinterpret_cast<const u32x4*>(p.w + ((n >> 7) * (K / 64) + k0 / 64 + kt) * 4096 +
+                                                  ((n & 127) >> 4) * 512 + off);
+        }
+      }
+    }
+    if constexpr (GRP) {
+      const int64_t G = K / 64;
+#pragma unroll
+      for (int j = 0; j < (int)(sizeof(rs) / sizeof(float)); ++j) {
+        int idx = tid + j * NT;
+        if (idx < 2 * BM) {
+          int kt = idx / BM, r = idx % BM;
+          int64_t m = imin64(m0 + r, p.M - 1);
+          rs[j] = p.a_scales[m * G + kb * 2 + kt];
+        } else if (idx < 2 * (BM + BN)) {
+          int q = idx - 2 * BM;
+          int kt = q / BN, c = q % BN;
+          int64_t n = n0 + c;
+          rs[j] = p.w_scales[((n >> 7) * G + kb * 2 + kt) * 128 + (n & 127)];
+        }
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint8_t* As = smem + buf * STAGE;
+    uint8_t* Ws = As + A_ST;
+#pragma unroll
+    for (int j = 0; j < PA; ++j) {
+      int pc = tid + j * NT;
+      if (pc < A_PIECES) {
+        if constexpr (ACT == ACT_I8) {
+          int row = pc >> 3, part = pc & 7;
+          int kt = part >> 2, c = part & 3;
+          *reinterpret_cast<u32x4*>(As + ((kt * (BM / 16) + (row >> 4)) * 64 + c * 16 + (row & 15)) * 16) = ra[j];
+        } else {
+          int row = pc >> 2, part = pc & 3;
+          int kt = part >> 1, c = (part & 1) * 2;
+          uint8_t* base = As + (kt * (BM / 16) + (row >> 4)) * 512;
+          *reinterpret_cast<u32x2*>(base + (c * 16 + (row & 15)) * 8) = u32x2{ra[j][0], ra[j][1]};
+          *reinterpret_cast<u32x2*>(base + ((c + 1) * 16 + (row & 15)) * 8) = u32x2{ra[j][2], ra[j][3]};
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+      int pc = tid + j * NT;
+      if (pc < W_PIECES) {
+        if constexpr (WGT == WGT_I8N) {
+          int row = pc >> 3, part = pc & 7;
+          int kt = part >> 2, c = part & 3;
+          *reinterpret_cast<u32x4*>(Ws + ((kt * (BN / 16) + (row >> 4)) * 64 + c * 16 + (row & 15)) * 16) = rw[j];
+        } else {
+          *reinterpret_cast<u32x4*>(Ws + pc * 16) = rw[j];
+        }
+      }
+    }
+    if constexpr (GRP) {
+      float* Ss = reinterpret_cast<float*>(Ws + W_ST);
+#pragma unroll
+      for (int j = 0; j < (int)(sizeof(rs) / sizeof(float)); ++j) {
+        int idx = tid + j * NT;
+        if (idx < 2 * (BM + BN)) Ss[idx] = rs[j];
+      }
+    }
+  };
+
+  v4i acc[FM][FN];
+  float yacc[GRP ? FM : 1][GRP ? FN : 1][4];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+  if constexpr (GRP) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yacc[i][j][e] = 0.f;
+  }
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
+    if (kb + 1 < nkb) gload(kb + 1);
+    const uint8_t* As = smem + buf * STAGE;
+    const uint8_t* Ws = As + A_ST;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      v4i wv[FN], av[FM];
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        wv[j] = widen_wgt<WGT>(Ws + ((kt * (BN / 16) + wn * FN + j) * 64 + l) * WFB);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        av[i] = widen_act<ACT>(As + ((kt * (BM / 16) + wm * FM + i) * 64 + l) * AFB);
+      if constexpr (GRP) {
+        const float* Ss = reinterpret_cast<const float*>(Ws + W_ST);
+        float sa[FM];
+        v4f sw[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) sa[i] = Ss[kt * BM + (wm * FM + i) * 16 + (l & 15)];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          sw[j] = *reinterpret_cast<const v4f*>(Ss + 2 * BM + kt * BN + (wn * FN + j) * 16 + (l >> 4) * 4);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            v4i pp = mfma_i8(wv[j], av[i], v4i{0, 0, 0, 0});
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              yacc[i][j][e] = __builtin_fmaf((float)(pp[e] >> SH) * sw[j][e], sa[i], yacc[i][j][e]);
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma_i8(wv[j], av[i], acc[i][j]);
+      }
+    }
+    if (kb + 1 < nkb) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue ----
+  const float sa_t = (!GRP && p.a_gran == CR_GRAN_TENSOR) ? p.a_scales[0] : 0.f;
+  const float sw_t = (!GRP && p.w_gran == CR_GRAN_TENSOR) ? p.w_scales[0] : 0.f;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t mb = m0 + (wm * FM + i) * 16;
+    const int64_t m = mb + (l & 15);
+    const int64_t mc = m < p.M ? m : p.M - 1;
+    float sa = 0.f;
+    if constexpr (!GRP && OUT != CR_OUT_I32_RAW) sa = (p.a_gran == CR_GRAN_TENSOR) ? sa_t : p.a_scales[mc];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = n0 + (wn * FN + j) * 16 + (l >> 4) * 4;
+      float y[4];
+      int raw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) raw[e] = acc[i][j][e] >> SH;
+      if constexpr (GRP) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = yacc[i][j][e];
+      } else if constexpr (OUT != CR_OUT_I32_RAW) {
+        v4f sw;
+        if (p.w_gran == CR_GRAN_TENSOR) sw = v4f{sw_t, sw_t, sw_t, sw_t};
+        else sw = *reinterpret_cast<const v4f*>(p.w_scales + n);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = (float)raw[e] * (sa * sw[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = 0.f;
+      }
+      finish_block<OUT>(p, m, n, mb, l, y, raw);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Small-M kernel (M <= 64): weight streaming. A block owns 16 output channels;
+// its 4 waves split the 64-deep k-tiles round robin, fragments come straight
+// from global memory (the tile-packed weight fragment is 512 contiguous
+// bytes), partial sums are reduced through LDS in a fixed order.
+// ---------------------------------------------------------------------------
+template <int FM, int ACT, int WGT, bool GROUPED, int OUT>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
+  constexpr bool GRP = GROUPED && OUT != CR_OUT_I32_RAW;
+  constexpr int SH = acc_shift<ACT, WGT>();
+  constexpr int U = 4;
+  __shared__ __attribute__((aligned(16))) int red[4][FM][64][4];
+  const int tid = threadIdx.x;
+  const int l = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t K = p.K;
+  const int nkt = (int)(K / 64);
+  const int64_t G = K / 64;
+
+  int64_t mrow[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) mrow[i] = imin64((int64_t)(i * 16 + (l & 15)), p.M - 1);
+
+  v4i acc[FM];
+  float yacc[FM][4];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    acc[i] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) yacc[i][e] = 0.f;
+  }
+
+  for (int kt0 = wave * U; kt0 < nkt; kt0 += 4 * U) {
+    u32x4 wr[U], ar[U][FM];
+    float sa[U][FM];
+    v4f sw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kt = kt0 + u;
+      if (kt >= nkt) break;
+      if constexpr (WGT == WGT_I8N) {
+        wr[u] = *reinterpret_cast<const u32x4*>(p.w + (n0 + (l & 15)) * K + kt * 64 + (l >> 4) * 16);
+      } else {
+        u32x2 t = *reinterpret_cast<const u32x2*>(p.w + ((n0 >> 7) * (K / 64) + kt) * 4096 +
+                                                  ((n0 & 127) >> 4) * 512 + l * 8);
+        wr[u] = u32x4{t[0], t[1], 0u, 0u};
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        if constexpr (ACT == ACT_I8) {
+          ar[u][i] = *reinterpret_cast<const u32x4*>(p.a + mrow[i] * K + kt * 64 + (l >> 4) * 16);
+        } else {
+          u32x2 t = *reinterpret_cast<const u32x2*>(p.a + mrow[i] * (K / 2) + kt * 32 + (l >> 4) * 8);
+          ar[u][i] = u32x4{t[0], t[1], 0u, 0u};
+        }
+        if constexpr (GRP) sa[u][i] = p.a_scales[mrow[i] * G + kt];
+      }
+      if constexpr (GRP) {
+        const int64_t n = n0 + (l >> 4) * 4;
+        sw[u] = *reinterpret_cast<const v4f*>(p.w_scales + ((n >> 7) * G + kt) * 128 + (n & 127));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kt = kt0 + u;
+      if (kt >= nkt) break;
+      v4i wv;
+      if constexpr (WGT == WGT_I8N) wv = __builtin_bit_cast(v4i, wr[u]);
+      else wv = widen_s4x16(u32x2{wr[u][0], wr[u][1]});
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        v4i av;
+        if constexpr (ACT == ACT_I8) av = __builtin_bit_cast(v4i, ar[u][i]);
+        else if constexpr (ACT == ACT_S4) av = widen_s4x16(u32x2{ar[u][i][0], ar[u][i][1]});
+        else av = widen_u4(u32x2{ar[u][i][0], ar[u][i][1]});
+        if constexpr (GRP) {
+          v4i pp = mfma_i8(wv, av, v4i{0, 0, 0, 0});
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            yacc[i][e] = __builtin_fmaf((float)(pp[e] >> SH) * sw[u][e], sa[u][i], yacc[i][e]);
+        } else {
+          acc[i] = mfma_i8(wv, av, acc[i]);
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[wave][i][l][e] = GRP ? __float_as_int(yacc[i][e]) : acc[i][e];
+  __syncthreads();
+  if (wave < FM) {
+    const int i = wave;
+    float y[4];
+    int raw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (GRP) {
+        y[e] = ((__int_as_float(red[0][i][l][e]) + __int_as_float(red[1][i][l][e])) +
+                __int_as_float(red[2][i][l][e])) + __int_as_float(red[3][i][l][e]);
+        raw[e] = 0;
+      } else {
+        int s = red[0][i][l][e] + red[1][i][l][e] + red[2][i][l][e] + red[3][i][l][e];
+        raw[e] = s >> SH;
+      }
+    }
+    const int64_t mb = i * 16;
+    const int64_t m = mb + (l & 15);
+    const int64_t n = n0 + (l >> 4) * 4;
+    if constexpr (!GRP && OUT != CR_OUT_I32_RAW) {
+      const int64_t mc = m < p.M ? m : p.M - 1;
+      float sa = (p.a_gran == CR_GRAN_TENSOR) ? p.a_scales[0] : p.a_scales[mc];
+      v4f sw;
+      if (p.w_gran == CR_GRAN_TENSOR) {
+        float t = p.w_scales[0];
+        sw = v4f{t, t, t, t};
+      } else {
+        sw = *reinterpret_cast<const v4f*>(p.w_scales + n);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = (float)raw[e] * (sa * sw[e]);
+    } else if constexpr (!GRP) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = 0.f;
+    }
+    finish_block<OUT>(p, m, n, mb, l, y, raw);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+template <int ACT, int WGT, bool GROUPED, int OUT>
+static hipError_t launch_kind(const GemmParams& p, hipStream_t s) {
+  if (p.M <= 64) {
+    const int fm = (int)((p.M + 15) / 16);
+    dim3 grid((unsigned)(p.N / 16));
+    switch (fm) {
+      case 1: hipLaunchKernelGGL((gemm_skinny_kernel<1, ACT, WGT, GROUPED, OUT>), grid, dim3(256), 0, s, p); break;
+      case 2: hipLaunchKernelGGL((gemm_skinny_kernel<2, ACT, WGT, GROUPED, OUT>), grid, dim3(256), 0, s, p); break;
+      case 3: hipLaunchKernelGGL((gemm_skinny_kernel<3, ACT, WGT, GROUPED, OUT>), grid, dim3(256), 0, s, p); break;
+      default: hipLaunchKernelGGL((gemm_skinny_kernel<4, ACT, WGT, GROUPED, OUT>), grid, dim3(256), 0, s, p); break;
+    }
+    return hipGetLastError();
+  }
+  constexpr int BM = 128, BN = 128;
+  const int64_t tiles = ((p.M + BM - 1) / BM) * (p.N / BN);
+  hipLaunchKernelGGL((gemm_big_kernel<BM, BN, 2, 2, ACT, WGT, GROUPED, OUT>), dim3((unsigned)tiles), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int ACT, int WGT, bool GROUPED>
+static hipError_t launch_out(const GemmParams& p, hipStream_t s) {
+  switch (p.out_type) {
+    case CR_OUT_BF16: return launch_kind<ACT, WGT, GROUPED, CR_OUT_BF16>(p, s);
+    case CR_OUT_F32: return launch_kind<ACT, WGT, GROUPED, CR_OUT_F32>(p, s);
+    default: return launch_kind<ACT, WGT, GROUPED, CR_OUT_I32_RAW>(p, s);
+  }
+}
+
+hipError_t launch_gemm_int(const GemmParams& p, hipStream_t s) {
+  if (p.wgt == WGT_I8N) return launch_out<ACT_I8, WGT_I8N, false>(p, s);
+  if (p.act == ACT_U4) {
+    return p.grouped ? launch_out<ACT_U4, WGT_S4T, true>(p, s) : launch_out<ACT_U4, WGT_S4T, false>(p, s);
+  }
+  return p.grouped ? launch_out<ACT_S4, WGT_S4T, true>(p, s) : launch_out<ACT_S4, WGT_S4T, false>(p, s);
+}
+
+}  // namespace cr

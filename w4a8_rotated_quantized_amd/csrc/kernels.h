@@ -1,0 +1,84 @@
+// Internal interface between the C-ABI host layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/convrot.h"
+
+namespace cr {
+
+struct RQParams {
+  const uint16_t* x;
+  int64_t rows, K, ldx;
+  int rot_group, qtype, gran, q_group;
+  float shift;
+  const uint16_t* lora_down;
+  int R;
+  void* lora_act;
+  int lora_f32;
+  void* codes;
+  void* scales;
+  void* zeros;
+  float* ws;            // per-block maxima (TENSOR granularity)
+  int nblk;             // blocks of the TENSOR passes
+  int G;                // 256-groups per row
+  int64_t total_groups; // rows * G
+  int rpb;              // rows per block (ROW granularity)
+};
+
+struct RQGeometry {
+  int gps;       // 256-groups per 16-lane segment
+  int rpb;       // rows per block (ROW)
+  int64_t nblk;  // blocks
+};
+
+// gran_kind: 0/1 TENSOR passes, 2 ROW, 3 ROW_GROUP(64), 4 ASYM(16)
+RQGeometry rq_geometry(int64_t rows, int64_t K, int gran_kind);
+hipError_t launch_rotate_quantize(RQParams p, hipStream_t s);
+
+struct PackParams {
+  const uint8_t* codes;
+  const void* scales;
+  const uint8_t* zeros;
+  int64_t N, K;
+  int qtype, gran, q_group;
+  uint8_t* packed;
+  void* packed_scales;
+  uint8_t* packed_zeros;
+  float* w_sum;
+};
+hipError_t launch_pack(const PackParams& p, hipStream_t s);
+
+enum ActKind { ACT_S4 = 0, ACT_U4 = 1, ACT_I8 = 2 };
+enum WgtKind { WGT_S4T = 0, WGT_I8N = 1 };
+
+struct GemmParams {
+  const uint8_t* a;          // activation codes
+  const float* a_scales;
+  int a_gran;
+  int act;                   // ActKind
+  float a_shift;
+  const uint8_t* w;          // tile-packed int4 or natural int8
+  const float* w_scales;
+  int w_gran;
+  int wgt;                   // WgtKind
+  const float* w_sum;
+  const void* lora_act;
+  int lora_f32;
+  const uint16_t* lora_up;
+  int R;
+  const uint16_t* bias;
+  void* out;
+  int out_type;
+  int64_t ldc;
+  int64_t M, N, K;
+  int grouped;               // ROW_GROUP(64) x ROW_GROUP(64)
+  // W4A8 only
+  const uint16_t* w_scales16;
+  const uint8_t* w_zeros;
+};
+hipError_t launch_gemm_int(const GemmParams& p, hipStream_t s);
+hipError_t launch_gemm_w4a8(const GemmParams& p, hipStream_t s);
+
+}  // namespace cr

@@ -1,0 +1,137 @@
+// Weight packer (gfx950): natural int4 codes -> tile-packed fragments.
+//
+// "Qwen-Image-Edit-2511 INT4 (ComfyUI Optimized)", Tile-Packed Weight Format:
+// weights reorganised into an (N/128, K/64) grid of 32 x 128-byte tiles with
+// (N/128, K/64, 128) group scales. "Qwen3-4B ConvRot W4A4" page, Format: the
+// natural [rows, cols/2] INT4 container. Offline (once per layer).
+//
+// Inner tile orders (this library's choice: one matrix-core operand fragment
+// of 64 lanes is contiguous):
+//   SYM_INT4: tile byte nb*512 + l*8 + j <- natural byte (row 16 nb + l%16,
+//             tile byte column 8 (l/16) + j)
+//   ASYM_UINT4: tile byte kg*1024 + nb*256 + l*4 + i holds the nibbles of
+//             k0 + i (low) and k0 + 4 + i (high), k0 = 16 kg + 8 (l/32), row
+//             32 nb + l%32, so widening a lane's word gives natural k order.
+#include "common.h"
+#include "kernels.h"
+
+namespace cr {
+
+__global__ __launch_bounds__(256) void pack_sym_kernel(PackParams p) {
+  const int64_t K = p.K;
+  const int64_t chunks = p.N * K / 16;           // 8-byte chunks
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= chunks) return;
+  // tile-order index: c = ((tile * 8 + nb) * 64 + l)
+  const int l = (int)(c & 63);
+  const int nb = (int)((c >> 6) & 7);
+  const int64_t tile = c >> 9;
+  const int64_t ktn = K / 64;
+  const int64_t tn = tile / ktn, kt = tile % ktn;
+  const int64_t row = tn * 128 + nb * 16 + (l & 15);
+  const int64_t col = kt * 32 + (l >> 4) * 8;
+  *reinterpret_cast<u32x2*>(p.packed + c * 8) =
+      *reinterpret_cast<const u32x2*>(p.codes + row * (K / 2) + col);
+}
+
+__global__ __launch_bounds__(256) void pack_asym_kernel(PackParams p) {
+  const int64_t K = p.K;
+  const int64_t words = p.N * K / 8;             // 4-byte words
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= words) return;
+  // c = ((tile * 4 + kg) * 4 + nb) * 64 + l
+  const int l = (int)(c & 63);
+  const int nb = (int)((c >> 6) & 3);
+  const int kg = (int)((c >> 8) & 3);
+  const int64_t tile = c >> 10;
+  const int64_t ktn = K / 64;
+  const int64_t tn = tile / ktn, kt = tile % ktn;
+  const int64_t row = tn * 128 + nb * 32 + (l & 31);
+  const int64_t k0 = kt * 64 + kg * 16 + (l >> 5) * 8;
+  // natural bytes k0/2 .. k0/2+3 hold nibbles k0..k0+7 (even k low)
+  const uint32_t x = *reinterpret_cast<const uint32_t*>(p.codes + row * (K / 2) + k0 / 2);
+  uint32_t out = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t lo = (x >> (4 * i)) & 0xF;        // k0 + i
+    uint32_t hi = (x >> (4 * (i + 4))) & 0xF;  // k0 + 4 + i
+    out |= (lo | (hi << 4)) << (8 * i);
+  }
+  reinterpret_cast<uint32_t*>(p.packed)[c] = out;
+}
+
+// g64 scales [N, K/64] -> [N/128][K/64][128]
+__global__ __launch_bounds__(256) void pack_g64_scales_kernel(PackParams p) {
+  const int64_t G = p.K / 64;
+  const int64_t total = p.N * G;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= total) return;
+  const int64_t i = c & 127, g = (c >> 7) % G, tn = (c >> 7) / G;
+  reinterpret_cast<float*>(p.packed_scales)[c] =
+      reinterpret_cast<const float*>(p.scales)[(tn * 128 + i) * G + g];
+}
+
+// g16 scales (fp16 [N, K/16]) and zeros (packed uint4 [N, K/32]) -> [N/128][K/64][4][128]
+__global__ __launch_bounds__(256) void pack_g16_meta_kernel(PackParams p) {
+  const int64_t G = p.K / 16;
+  const int64_t total = p.N * G;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= total) return;
+  const int64_t i = c & 127;
+  const int64_t kg = (c >> 7) & 3;
+  const int64_t tk = c >> 9;                      // tile index tn * (K/64) + kt
+  const int64_t ktn = p.K / 64;
+  const int64_t tn = tk / ktn, kt = tk % ktn;
+  const int64_t row = tn * 128 + i;
+  const int64_t g = kt * 4 + kg;
+  reinterpret_cast<uint16_t*>(p.packed_scales)[c] = reinterpret_cast<const uint16_t*>(p.scales)[row * G + g];
+  const uint8_t zb = p.zeros[row * (p.K / 32) + g / 2];
+  p.packed_zeros[c] = (g & 1) ? (zb >> 4) : (zb & 0xF);
+}
+
+// w_sum[n] = sum_k dequantized weight, summed group by group in k order.
+__global__ __launch_bounds__(256) void wsum_kernel(PackParams p) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= p.N) return;
+  const int64_t K = p.K;
+  const uint8_t* row = p.codes + n * (K / 2);
+  const float* sc = reinterpret_cast<const float*>(p.scales);
+  float acc = 0.f;
+  if (p.gran == CR_GRAN_ROW_GROUP) {
+    for (int64_t g = 0; g < K / 64; ++g) {
+      int s = 0;
+      for (int j = 0; j < 32; ++j) {
+        int b = row[g * 32 + j];
+        s += ((b & 0xF) ^ 8) - 8;
+        s += ((b >> 4) ^ 8) - 8;
+      }
+      acc += (float)s * sc[n * (K / 64) + g];
+    }
+  } else {
+    int s = 0;
+    for (int64_t j = 0; j < K / 2; ++j) {
+      int b = row[j];
+      s += ((b & 0xF) ^ 8) - 8;
+      s += ((b >> 4) ^ 8) - 8;
+    }
+    acc = (float)s * (p.gran == CR_GRAN_TENSOR ? sc[0] : sc[n]);
+  }
+  p.w_sum[n] = acc;
+}
+
+static inline unsigned nblocks(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+hipError_t launch_pack(const PackParams& p, hipStream_t s) {
+  if (p.qtype == CR_Q_ASYM_UINT4) {
+    hipLaunchKernelGGL(pack_asym_kernel, dim3(nblocks(p.N * p.K / 8)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(pack_g16_meta_kernel, dim3(nblocks(p.N * p.K / 16)), dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(pack_sym_kernel, dim3(nblocks(p.N * p.K / 16)), dim3(256), 0, s, p);
+  if (p.gran == CR_GRAN_ROW_GROUP)
+    hipLaunchKernelGGL(pack_g64_scales_kernel, dim3(nblocks(p.N * p.K / 64)), dim3(256), 0, s, p);
+  if (p.w_sum) hipLaunchKernelGGL(wsum_kernel, dim3(nblocks(p.N)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace cr
