@@ -1,0 +1,239 @@
+"""Benchmark of the ConvRot W4A4 tensorwise linear on one MI355X.
+
+Workload (the single MMDiT projection of the Qwen-Image MMDiT, per the
+per-family shape table of the "Qwen-Image-Edit-2511-W4A8-ConvRot" card):
+X bf16 [M, 3072] with M in {4096, 32} (image tokens and the small-token
+case), N(0,1) with 15 outlier channels x30, W [3072, 3072] ~ N(0, 0.02)
+prepared offline (rotated, quantized to INT4, tile-packed; untimed).
+
+One step = the whole hot path for both token counts, inputs resident in HBM:
+    rotate+quantize(X_4096) -> w4a4_gemm(4096)  ->  bf16 [4096, 3072]
+    rotate+quantize(X_32)   -> w4a4_gemm(32)    ->  bf16 [32, 3072]
+Every step uses a different copy of all buffers (inputs, weights, codes,
+outputs; ~10 copies, over 2x the 256 MB last-level cache), so each step
+reads cold HBM data.
+
+Metric: effective TOPS = sum 2*M*N*K / step time (the fused
+rotate+quantize+W4 GEMM throughput), also given as % of the 5.0 POP/s dense
+INT8 matrix peak. The roofline object reports the dominant kernel (the
+M=4096 GEMM) against that peak; its duration comes from HIP events around
+each of its launches on the launch stream. The CPU baseline is the numpy
+oracle running the same step on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0       # MI355X dense INT8 matrix peak (5.0 POP/s)
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+M_BIG, M_SMALL, N, K = 4096, 32, 3072, 3072
+GEMM_SOURCES = ["gemm_int.hip", "common.h", "kernels.h"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def source_sha(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "w4a8_rotated_quantized_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per launch of the dominant kernel, from the committed
+    rocprofv3 counter summary, only if the kernel source is unchanged."""
+    p = os.path.join(ROOT, "profiles", "w4a4_gemm_m4096_n3072_k3072_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("source_sha") != source_sha(GEMM_SOURCES):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(budget_s):
+    """The oracle (numpy) running the same step on the host, repeated until
+    about budget_s seconds have passed."""
+    import numpy as np
+    import workloads as wl
+    from oracle import linear as ol, gemm as og
+    xb_big = wl.activation(2, 0, M_BIG, K, n_outliers=15, outlier_scale=30.0)
+    xb_small = wl.activation(2, 2, M_SMALL, K, n_outliers=15, outlier_scale=30.0)
+    wp = ol.prepare_w4a4(wl.weight(2, 1, N, K))
+    try:
+        import threadpoolctl
+        np.ones((64, 64)) @ np.ones((64, 64))
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for xb in (xb_big, xb_small):
+            r = ol.rotate_quantize(xb, 256, "int4", "tensor")
+            acc = og.int_gemm(r["values"], wp["values"])
+            ol.epilogue_scalar(acc, r["scales"], "tensor", wp["scales"], "tensor")
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    ops = 2.0 * (M_BIG + M_SMALL) * N * K * reps
+    return {"value": ops / el / 1e12, "unit": "TOPS", "cores": int(cores), "kind": "oracle",
+            "sample": f"{reps} full oracle step(s) (M=4096 and M=32, K=N=3072) in {el:.1f} s "
+                      f"(numpy; elementwise stages single-threaded, BLAS threads={cores})"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path has no multi-GPU part); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import w4a8_rotated_quantized_amd as cr
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(3)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def bf16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    xb_big = wl.activation(2, 0, M_BIG, K, n_outliers=15, outlier_scale=30.0)
+    xb_small = wl.activation(2, 2, M_SMALL, K, n_outliers=15, outlier_scale=30.0)
+    wb = wl.weight(2, 1, N, K)
+
+    # offline weight preparation (untimed)
+    w = bf16(wb)
+    wc, ws, _, _ = cr.convrot_rotate_quantize(w, 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
+    wp, _, _, _ = cr.w4_pack_weights(wc, ws, N, K, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
+
+    # rotating buffer sets
+    per_set = M_BIG * K * 2 + M_BIG * K // 2 + M_BIG * N * 2 + N * K // 2
+    nsets = max(2, int(np.ceil(600e6 / per_set)))
+    sets = []
+    xbig0, xsmall0 = bf16(xb_big), bf16(xb_small)
+    for _ in range(nsets):
+        s = {
+            "xb": xbig0.clone(), "xs": xsmall0.clone(), "wp": wp.clone(), "ws": ws.clone(),
+            "cb": torch.empty((M_BIG, K // 2), dtype=torch.uint8, device=dev),
+            "cs": torch.empty((M_SMALL, K // 2), dtype=torch.uint8, device=dev),
+            "sb": torch.empty(1, dtype=torch.float32, device=dev),
+            "ss": torch.empty(1, dtype=torch.float32, device=dev),
+            "wsb": torch.empty(cr.convrot_rq_workspace_size(M_BIG, K, 256, 0, 0), dtype=torch.uint8, device=dev),
+            "wss": torch.empty(cr.convrot_rq_workspace_size(M_SMALL, K, 256, 0, 0), dtype=torch.uint8, device=dev),
+            "yb": torch.empty((M_BIG, N), dtype=torch.bfloat16, device=dev),
+            "ys": torch.empty((M_SMALL, N), dtype=torch.bfloat16, device=dev),
+        }
+        sets.append(s)
+
+    ev = {}
+
+    def step(i, record):
+        s = sets[i % nsets]
+        if record:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            e[0].record(stream)
+        cr.convrot_rotate_quantize(s["xb"], 256, 0, 0, codes=s["cb"], scales=s["sb"], workspace=s["wsb"])
+        if record:
+            e[1].record(stream)
+        cr.w4a4_gemm(s["cb"], s["sb"], 0, s["wp"], s["ws"], 0, M_BIG, N, K, out=s["yb"])
+        if record:
+            e[2].record(stream)
+        cr.convrot_rotate_quantize(s["xs"], 256, 0, 0, codes=s["cs"], scales=s["ss"], workspace=s["wss"])
+        if record:
+            e[3].record(stream)
+        cr.w4a4_gemm(s["cs"], s["ss"], 0, s["wp"], s["ws"], 0, M_SMALL, N, K, out=s["ys"])
+        if record:
+            e[4].record(stream)
+            ev.setdefault("e", []).append(e)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+
+    # timed region 1: plain back-to-back steps (the headline number)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i, False)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+
+    # timed region 2: the same steps with events around every kernel call
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    parts = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev["e"]])
+    rq_big, gemm_big, rq_small, gemm_small = (float(np.mean(parts[:, j])) for j in range(4))
+
+    ops_step = 2.0 * (M_BIG + M_SMALL) * N * K
+    eff_tops = ops_step / (ms_step * 1e-3) / 1e12
+    gemm_tops = 2.0 * M_BIG * N * K / (gemm_big * 1e-3) / 1e12
+    rq_bytes = M_BIG * K * 2 + M_BIG * K // 2 + 4
+    rq_gbs = rq_bytes / (rq_big * 1e-3) / 1e9
+    small_bytes = N * K // 2 + M_SMALL * K // 2 + M_SMALL * N * 2
+    traffic = traffic_from_profile()
+
+    line = {
+        "metric": "effective TOPS of fused rotate+quant+W4 GEMM (% INT8 MFMA peak); GB/s",
+        "value": round(eff_tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4",
+        "data": "synthetic",
+        "config": {"workload": "MMDiT projection, W4A4 tensorwise ConvRot group 256, "
+                               "X bf16 [M, 3072] (M = 4096 and 32), W [3072, 3072]",
+                   "M": [M_BIG, M_SMALL], "N": N, "K": K, "rot_group": 256,
+                   "buffer_sets": nsets},
+        "pct_int8_peak": round(100.0 * eff_tops / INT8_PEAK_TOPS, 2),
+        "kernels_us": {"rq_m4096": round(rq_big * 1e3, 2), "gemm_m4096": round(gemm_big * 1e3, 2),
+                       "rq_m32": round(rq_small * 1e3, 2), "gemm_m32": round(gemm_small * 1e3, 2)},
+        "rq_m4096_GBps": round(rq_gbs, 1),
+        "rq_m4096_pct_hbm": round(100.0 * rq_gbs / HBM_PEAK_GBS, 1),
+        "gemm_m4096_TOPS": round(gemm_tops, 1),
+        "gemm_m32_GBps": round(small_bytes / (gemm_small * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": INT8_PEAK_TOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
