@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 INT8_PEAK_TOPS = 5000.0       # MI355X dense INT8 matrix peak (5.0 POP/s)
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 M_BIG, M_SMALL, N, K = 4096, 32, 3072, 3072
-GEMM_SOURCES = ["gemm_int.hip", "common.h", "kernels.h"]
+GEMM_SOURCES = ["gemm_w4a4.hip", "epilogue.h", "common.h", "kernels.h"]
 
 
 def parse():
@@ -140,8 +140,8 @@ def main():
     for _ in range(nsets):
         s = {
             "xb": xbig0.clone(), "xs": xsmall0.clone(), "wp": wp.clone(), "ws": ws.clone(),
-            "cb": torch.empty((M_BIG, K // 2), dtype=torch.uint8, device=dev),
-            "cs": torch.empty((M_SMALL, K // 2), dtype=torch.uint8, device=dev),
+            "cb": torch.empty(((M_BIG + 15) // 16, K // 64, 512), dtype=torch.uint8, device=dev),
+            "cs": torch.empty(((M_SMALL + 15) // 16, K // 64, 512), dtype=torch.uint8, device=dev),
             "sb": torch.empty(1, dtype=torch.float32, device=dev),
             "ss": torch.empty(1, dtype=torch.float32, device=dev),
             "wsb": torch.empty(cr.convrot_rq_workspace_size(M_BIG, K, 256, 0, 0), dtype=torch.uint8, device=dev),
@@ -158,13 +158,15 @@ def main():
         if record:
             e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
             e[0].record(stream)
-        cr.convrot_rotate_quantize(s["xb"], 256, 0, 0, codes=s["cb"], scales=s["sb"], workspace=s["wsb"])
+        cr.convrot_rotate_quantize(s["xb"], 256, 0, 0, layout=cr.LAYOUT.TILED, codes=s["cb"], scales=s["sb"],
+                                   workspace=s["wsb"])
         if record:
             e[1].record(stream)
         cr.w4a4_gemm(s["cb"], s["sb"], 0, s["wp"], s["ws"], 0, M_BIG, N, K, out=s["yb"])
         if record:
             e[2].record(stream)
-        cr.convrot_rotate_quantize(s["xs"], 256, 0, 0, codes=s["cs"], scales=s["ss"], workspace=s["wss"])
+        cr.convrot_rotate_quantize(s["xs"], 256, 0, 0, layout=cr.LAYOUT.TILED, codes=s["cs"], scales=s["ss"],
+                                   workspace=s["wss"])
         if record:
             e[3].record(stream)
         cr.w4a4_gemm(s["cs"], s["ss"], 0, s["wp"], s["ws"], 0, M_SMALL, N, K, out=s["ys"])

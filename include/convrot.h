@@ -88,6 +88,14 @@ typedef enum cr_out {
   CR_OUT_I32_RAW = 2      /* the exact integer sum_k qa*(qw - z); scales/epilogue skipped     */
 } cr_out;
 
+typedef enum cr_layout {
+  CR_LAYOUT_NATURAL = 0,  /* int4 codes [rows, K/2], row-major                                 */
+  CR_LAYOUT_TILED = 1     /* int4 codes [ceil(rows/16)][K/64][512 B]: byte l*8 + j of block    */
+                          /* (b, kt) is natural byte (row 16b + l%16, 32kt + 8(l/16) + j), the */
+                          /* operand-fragment order of the W4A4 GEMM; rows past `rows` in the  */
+                          /* last block are left unwritten (allocate ceil(rows/16)*16 rows)    */
+} cr_layout;
+
 /* Status text, e.g. "format not available" for CR_ERR_UNSUPPORTED_FORMAT. */
 const char* convrot_status_string(cr_status status);
 /* The hipError_t value behind the last CR_ERR_HIP on this thread (0 if none). */
@@ -131,12 +139,17 @@ void convrot_reset_counters(void);
  *                bf16 (lora_act_f32 = 0) or float32 (1), [rows, R] row-major
  *   codes        SYM_INT4 / UNSIGNED / ASYM: uint8 [rows, K/2] natural int4;
  *                SYM_INT8: int8 [rows, K]
+ *   layout       CR_LAYOUT_NATURAL, or CR_LAYOUT_TILED for SYM_INT4 / UNSIGNED
+ *                codes (the input layout of w4a4_gemm's fast path)
  *   scales       float32 [1] | [rows] | [rows, K/q_group]; ASYM: fp16 [rows, K/16]
  *   zeros        ASYM only: uint8 [rows, K/32], two uint4 zero points per byte
  *                (group 2j low nibble); NULL otherwise
  *   workspace    device scratch of at least convrot_rq_workspace_size(...)
  *                bytes (needed by TENSOR granularity; may be NULL when that
- *                size is 0). Contents on entry are ignored.
+ *                size is 0). Contents on entry are ignored; it receives one
+ *                maximum per block of the first of the two launches that
+ *                per-tensor scaling takes. Calls sharing a workspace must not
+ *                run concurrently.
  * Shape: rows >= 1, K % 256 == 0 when rotating, K % 64 == 0 otherwise,
  *        K <= 32768.
  * Result is deterministic and bit-identical to the reference definition for
@@ -149,7 +162,7 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
                                   int rot_group, cr_qtype qtype, cr_gran gran, int q_group,
                                   float shift,
                                   const void* lora_down, int R, void* lora_act, int lora_act_f32,
-                                  void* codes, void* scales, void* zeros,
+                                  void* codes, cr_layout layout, void* scales, void* zeros,
                                   void* workspace, size_t workspace_bytes,
                                   hipStream_t stream);
 
@@ -195,7 +208,8 @@ cr_status w4_pack_weights(const void* codes, const void* scales, const void* zer
  * INT4 (ComfyUI Optimized)", Fused LoRA-Up Epilogue, Kernel Engineering
  * (unsigned shifted activations, scale staging).
  *
- *   a_codes     uint8 [M, K/2] natural int4 (signed, or unsigned when a_unsigned)
+ *   a_codes     int4 codes (signed, or unsigned when a_unsigned) in a_layout:
+ *               CR_LAYOUT_TILED (fast path) or CR_LAYOUT_NATURAL [M, K/2]
  *   a_scales    float32: TENSOR [1], ROW [M], ROW_GROUP(64) [M, K/64]
  *   a_unsigned  1 for UNSIGNED_INT4_SHIFT codes: y -= a_shift * w_sum[n]
  *   w_packed    from w4_pack_weights (SYM_INT4)
@@ -209,10 +223,11 @@ cr_status w4_pack_weights(const void* codes, const void* scales, const void* zer
  *               int32 sum_k qa*qw (lora/bias/scales ignored)
  * Epilogue: y = s_a s_w acc  (or sum_g a_s[m,g] w_s[n,g] P[m,n,g]) - shift
  * term + low-rank + bias, evaluated in float32, stored once.
- * Shape: M >= 1, N % 128 == 0, K % 128 == 0, K <= 32768, ldc >= N (ldc % 8 == 0).
+ * Shape: M >= 1, N % 128 == 0, K % 128 == 0, K <= 32768, ldc >= N (ldc % 8 == 0),
+ * M*K/2 and N*K/2 below 2^32 bytes.
  * workspace: unused (pass NULL, 0).
  */
-cr_status w4a4_gemm(const void* a_codes, const float* a_scales, cr_gran a_gran,
+cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scales, cr_gran a_gran,
                     int a_unsigned, float a_shift,
                     const void* w_packed, const float* w_scales, cr_gran w_gran,
                     const float* w_sum,

@@ -27,6 +27,9 @@ Readings where the pages are silent:
           tile, k0 = 16*kg + 8*(l//32) in the tile (so a lane's low nibbles
           are 4 consecutive k and its high nibbles the next 4)
 
+  * activation codes may also be stored tiled: [ceil(M/16)][K/64][512 B],
+    byte l*8 + j <- natural byte (row 16*b + l%16, byte 8*(l//16) + j of the
+    32-byte k-tile slice), i.e. the weight tile's fragment order;
   * per-group scales of the W4A4 g64 format: float32 [N/128][K/64][128]
     (the pages' wscales layout); W4A8 g16 scales (fp16) and zero points
     (one byte each) : [N/128][K/64][4][128].
@@ -140,6 +143,44 @@ def tile_unpack_w4a8(tiles: np.ndarray) -> np.ndarray:
                             out[row, k0 + i] = b & 0xF
                             out[row, k0 + 4 + i] = b >> 4
     return out
+
+
+def tile_pack_a(packed: np.ndarray) -> np.ndarray:
+    """Activation codes, natural uint8 [M, K/2] -> tiled uint8 [ceil(M/16), K/64, 512]:
+    byte l*8 + j of block (b, kt) <- natural byte (row 16*b + l%16, 32*kt + 8*(l//16) + j),
+    the 16-row analogue of the W4A4 weight tile (one operand fragment per
+    512 bytes). Rows past M in the last block are zero here (the library
+    leaves them unwritten)."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    M, half = packed.shape
+    K = 2 * half
+    if K % 64:
+        raise ValueError("K % 64 != 0")
+    MB = (M + 15) // 16
+    out = np.zeros((MB, K // 64, 512), dtype=np.uint8)
+    for b in range(MB):
+        for kt in range(K // 64):
+            for lane in range(64):
+                row = 16 * b + lane % 16
+                if row >= M:
+                    continue
+                col = 32 * kt + 8 * (lane // 16)
+                out[b, kt, lane * 8:lane * 8 + 8] = packed[row, col:col + 8]
+    return out
+
+
+def tile_unpack_a(tiles: np.ndarray, M: int) -> np.ndarray:
+    """Inverse of tile_pack_a (first M rows)."""
+    tiles = np.asarray(tiles, dtype=np.uint8)
+    MB, KT, _ = tiles.shape
+    out = np.zeros((MB * 16, KT * 32), dtype=np.uint8)
+    for b in range(MB):
+        for kt in range(KT):
+            for lane in range(64):
+                row = 16 * b + lane % 16
+                col = 32 * kt + 8 * (lane // 16)
+                out[row, col:col + 8] = tiles[b, kt, lane * 8:lane * 8 + 8]
+    return out[:M]
 
 
 def tile_pack_g64_scales(scales: np.ndarray) -> np.ndarray:

@@ -71,9 +71,9 @@ def test_device_check_reports_no_device_here(cr):
 
 
 def _rq(cr, x=A, rows=64, K=512, ldx=512, rot=256, q=0, g=0, qg=0, lora=None, R=0, la=None,
-        codes=A, scales=A, zeros=None, ws=A, wsb=1 << 20):
+        codes=A, scales=A, zeros=None, ws=A, wsb=1 << 20, layout=0):
     return cr.lib.convrot_rotate_quantize(_p(x), rows, K, ldx, rot, q, g, qg, 0.0, _p(lora), R, _p(la), 0,
-                                          _p(codes), _p(scales), _p(zeros), _p(ws), wsb, None)
+                                          _p(codes), layout, _p(scales), _p(zeros), _p(ws), wsb, None)
 
 
 def test_rq_validation(cr):
@@ -92,6 +92,9 @@ def test_rq_validation(cr):
     assert _rq(cr, rot=0, g=2, qg=64, lora=A, R=16, la=A) == 3   # rank must be 32
     assert _rq(cr, rot=256, lora=A, R=32, la=A) == 3          # low rank only without rotation
     assert _rq(cr, wsb=0) == 6                               # TENSOR needs workspace
+    assert _rq(cr, q=1, layout=1) == 3                       # tiled layout is for int4 codes
+    assert _rq(cr, layout=2) == 1
+    assert _rq(cr, layout=1) == 4
     assert _rq(cr) == 4                                      # valid -> device check (no GPU here)
     assert _rq(cr, rot=0, g=2, qg=64, ws=None, wsb=0) == 4
 
@@ -116,8 +119,8 @@ def test_pack_validation(cr):
 
 
 def _w4a4(cr, a=A, ag=0, wg=0, uns=0, wsum=None, la=None, lu=None, R=0, out=A, ot=0, ldc=256,
-          M=64, N=256, K=512):
-    return cr.lib.w4a4_gemm(_p(a), _p(A), ag, uns, 0.0, _p(A), _p(A), wg, _p(wsum), _p(la), 0, _p(lu), R,
+          M=64, N=256, K=512, layout=1):
+    return cr.lib.w4a4_gemm(_p(a), layout, _p(A), ag, uns, 0.0, _p(A), _p(A), wg, _p(wsum), _p(la), 0, _p(lu), R,
                             None, _p(out), ot, ldc, M, N, K, None, 0, None)
 
 
@@ -132,6 +135,8 @@ def test_gemm_validation(cr):
     assert _w4a4(cr, la=A, lu=None, R=32) == 3
     assert _w4a4(cr, la=A, lu=A, R=16) == 3
     assert _w4a4(cr, ot=5) == 1
+    assert _w4a4(cr, layout=3) == 1
+    assert _w4a4(cr, M=1 << 20, K=32768, ldc=256) == 2        # M*K/2 beyond 32-bit offsets
     assert _w4a4(cr) == 4
     L = cr.lib
     assert L.w4a8_gemm(_p(A), _p(A), 1, _p(A), _p(A), _p(A), 32, None, _p(A), 0, 256, 64, 256, 512,

@@ -12,7 +12,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 import workloads as wl  # noqa: E402
-from oracle import linear as ol, gemm as og  # noqa: E402
+from oracle import linear as ol, gemm as og, pack as opack  # noqa: E402
 from tests.gpu_helpers import bf16_dev, dev, host, rel_l2, bf16_to_f32, say  # noqa: E402
 
 GR = {"tensor": 0, "row": 1, "row_group": 2}
@@ -36,6 +36,8 @@ def _check_out(y_bf16, y_f32, ref_y):
 W4A4_CASES = [
     # M, N, K, a_gran, w_gran
     (1, 256, 512, "tensor", "tensor"),
+    (200, 384, 3072, "tensor", "tensor"),     # 128x192 tiles, ragged M
+    (77, 768, 256, "row", "tensor"),          # one stage (K = 256: two 128-deep stages)
     (17, 384, 3072, "tensor", "row"),
     (64, 256, 512, "row", "tensor"),
     (100, 256, 1024, "tensor", "tensor"),
@@ -61,6 +63,11 @@ def test_w4a4_tensor_row(cr, case):
     sw = dev(np.asarray(wp["scales"], np.float32).reshape(-1))
     raw = cr.w4a4_gemm(a, sa, GR[ag], w, sw, GR[wg], M, N, K, out_type=2)
     assert np.array_equal(host(raw).astype(np.int64), ref["raw"])
+    at = dev(opack.tile_pack_a(ref["x"]["codes"]))
+    raw_t = cr.w4a4_gemm(at, sa, GR[ag], w, sw, GR[wg], M, N, K, out_type=2)
+    assert np.array_equal(host(raw_t).astype(np.int64), ref["raw"])
+    yt = cr.w4a4_gemm(at, sa, GR[ag], w, sw, GR[wg], M, N, K, out_type=1)
+    assert rel_l2(host(yt), ref["y"]) <= 1e-5
     yb = cr.w4a4_gemm(a, sa, GR[ag], w, sw, GR[wg], M, N, K, out_type=0)
     yf = cr.w4a4_gemm(a, sa, GR[ag], w, sw, GR[wg], M, N, K, out_type=1)
     _check_out(yb, yf, ref["y"])
@@ -89,6 +96,7 @@ G64_CASES = [
     (130, 384, 1024, True, "bf16", False),
     (64, 256, 512, True, "f32", True),
     (257, 128, 768, False, "f32", False),
+    (100, 384, 128, False, None, True),      # a single 128-deep stage
 ]
 
 
@@ -119,6 +127,10 @@ def test_w4a4_group64_lowrank(cr, case):
               bias=None if bias is None else bf16_dev(bias))
     raw = cr.w4a4_gemm(a, sa, 2, w, sw, 2, M, N, K, out_type=2, **kw)
     assert np.array_equal(host(raw).astype(np.int64), ref["raw"])
+    at = dev(opack.tile_pack_a(ref["x"]["codes"]))
+    assert np.array_equal(host(cr.w4a4_gemm(at, sa, 2, w, sw, 2, M, N, K, out_type=2, **kw)).astype(np.int64),
+                          ref["raw"])
+    assert rel_l2(host(cr.w4a4_gemm(at, sa, 2, w, sw, 2, M, N, K, out_type=1, **kw)), ref["y"]) <= 1e-5
     yb = cr.w4a4_gemm(a, sa, 2, w, sw, 2, M, N, K, out_type=0, **kw)
     yf = cr.w4a4_gemm(a, sa, 2, w, sw, 2, M, N, K, out_type=1, **kw)
     _check_out(yb, yf, ref["y"])

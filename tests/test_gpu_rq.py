@@ -42,6 +42,10 @@ def test_rotate_quantize_sym(cr, qt, gran, shape):
                           ref["codes"].view(np.uint8)), "codes differ"
     assert np.array_equal(host(scales).reshape(-1).view(np.uint32),
                           np.asarray(ref["scales"], np.float32).reshape(-1).view(np.uint32)), "scales differ"
+    if qt == "int4":
+        tcodes, tscales, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), 256, 0, GR[gran], qg, layout=1)
+        assert np.array_equal(opack.tile_unpack_a(host(tcodes), rows), ref["codes"]), "tiled codes differ"
+        assert np.array_equal(host(tscales).reshape(-1), np.asarray(ref["scales"]).reshape(-1))
 
 
 def test_rotate_quantize_strided_rows_and_zero_rows(cr):
@@ -105,6 +109,9 @@ def test_rotate_quantize_plain_g64(cr, unsigned, lora, shape):
         lora_down=None if l2 is None else bf16_dev(l2), lora_act_f32=(lora == "f32"))
     assert np.array_equal(host(codes), ref["codes"])
     assert np.array_equal(host(scales).view(np.uint32), ref["scales"].view(np.uint32))
+    tcodes, _, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), 0, 2 if unsigned else 0, 2, 64, shift=shift,
+                                                 layout=1)
+    assert np.array_equal(opack.tile_unpack_a(host(tcodes), rows), ref["codes"])
     if lora:
         la_ref32 = ol.lora_down(xb, l2, act_f32=True).astype(np.float64)
         mag = np.abs(wl.f32_from_bf16_bits(xb)).astype(np.float64) @ np.abs(wl.f32_from_bf16_bits(l2)).astype(np.float64).T

@@ -77,6 +77,17 @@ def test_tile_pack_w4a8_position_and_round_trip():
     assert b & 0xF == vals[70, 90] and b >> 4 == vals[70, 94]
 
 
+def test_tile_pack_a_position_and_round_trip():
+    g = np.random.default_rng(26)
+    nat = g.integers(0, 256, size=(37, 128), dtype=np.uint8)           # M=37 (ragged), K=256
+    t = pack.tile_pack_a(nat)
+    assert t.shape == (3, 4, 512)
+    assert np.array_equal(pack.tile_unpack_a(t, 37), nat)
+    # natural (row 21, byte 32*2 + 19): block 1, k-tile 2, chunk 2, j 3 -> lane 2*16 + 5 = 37
+    assert t[1, 2, 37 * 8 + 3] == nat[21, 83]
+    assert np.all(t[2, :, :] [:, [l * 8 + j for l in range(64) if 32 + l % 16 >= 37 for j in range(8)]] == 0)
+
+
 def test_group_scale_tiles():
     s = np.arange(256 * 8, dtype=np.float32).reshape(256, 8)      # N=256, K=512 (g64)
     t = pack.tile_pack_g64_scales(s)

@@ -14,7 +14,7 @@ import os
 import torch
 
 __all__ = [
-    "ConvRotError", "lib", "Q", "GRAN", "OUT",
+    "ConvRotError", "lib", "Q", "GRAN", "OUT", "LAYOUT",
     "convrot_rotate_quantize", "w4_pack_weights", "w4a4_gemm", "w4a8_gemm",
     "int8_tensorwise_gemm", "convrot_rq_workspace_size", "w4_packed_bytes",
     "get_counters", "reset_counters", "device_check", "status_string",
@@ -50,6 +50,11 @@ class OUT:
     I32_RAW = 2
 
 
+class LAYOUT:
+    NATURAL = 0
+    TILED = 1
+
+
 class _Counters(ctypes.Structure):
     _fields_ = [("launches", ctypes.c_uint64 * 8), ("fallbacks", ctypes.c_uint64)]
 
@@ -63,10 +68,10 @@ _SIGS = {
     "convrot_reset_counters": (None, []),
     "convrot_rq_workspace_size": (_sz, [_i64, _i64, _i, _i, _i, _i]),
     "convrot_rotate_quantize": (_i, [_vp, _i64, _i64, _i64, _i, _i, _i, _i, _f, _vp, _i, _vp, _i,
-                                     _vp, _vp, _vp, _vp, _sz, _vp]),
+                                     _vp, _i, _vp, _vp, _vp, _sz, _vp]),
     "w4_packed_bytes": (_sz, [_i64, _i64, _i, _i, _i, _i]),
     "w4_pack_weights": (_i, [_vp, _vp, _vp, _i64, _i64, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
-    "w4a4_gemm": (_i, [_vp, _vp, _i, _i, _f, _vp, _vp, _i, _vp, _vp, _i, _vp, _i, _vp,
+    "w4a4_gemm": (_i, [_vp, _i, _vp, _i, _i, _f, _vp, _vp, _i, _vp, _vp, _i, _vp, _i, _vp,
                        _vp, _i, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
     "w4a8_gemm": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _i, _i64, _i64, _i64, _i64,
                        _vp, _sz, _vp]),
@@ -139,17 +144,20 @@ def _scale_numel(rows, K, qtype, gran, q_group):
 
 
 def convrot_rotate_quantize(x, rot_group=256, qtype=Q.SYM_INT4, gran=GRAN.TENSOR, q_group=0,
-                            shift=0.0, lora_down=None, lora_act_f32=False,
+                            shift=0.0, lora_down=None, lora_act_f32=False, layout=LAYOUT.NATURAL,
                             codes=None, scales=None, zeros=None, lora_act=None, workspace=None,
                             stream=None):
     """x: bf16 [rows, K] (row stride may exceed K). Returns
-    (codes, scales, zeros, lora_act); outputs are allocated when not given."""
+    (codes, scales, zeros, lora_act); outputs are allocated when not given.
+    Tiled int4 codes come back as uint8 [ceil(rows/16), K/64, 512]."""
     rows, K = x.shape
     ldx = x.stride(0)
     dev = x.device
     if codes is None:
         if qtype == Q.SYM_INT8:
             codes = torch.empty((rows, K), dtype=torch.int8, device=dev)
+        elif layout == LAYOUT.TILED:
+            codes = torch.empty(((rows + 15) // 16, K // 64, 512), dtype=torch.uint8, device=dev)
         else:
             codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev)
     if scales is None:
@@ -169,7 +177,7 @@ def convrot_rotate_quantize(x, rot_group=256, qtype=Q.SYM_INT4, gran=GRAN.TENSOR
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.convrot_rotate_quantize(_ptr(x), rows, K, ldx, rot_group, qtype, gran, q_group,
                                      float(shift), _ptr(lora_down), R, _ptr(lora_act),
-                                     int(bool(lora_act_f32)), _ptr(codes), _ptr(scales), _ptr(zeros),
+                                     int(bool(lora_act_f32)), _ptr(codes), int(layout), _ptr(scales), _ptr(zeros),
                                      _ptr(workspace), wsb, _stream(stream))
     _check(st, "convrot_rotate_quantize")
     return codes, scales, zeros, lora_act
@@ -205,11 +213,14 @@ def _out(M, N, out_type, dev, out):
 
 def w4a4_gemm(a_codes, a_scales, a_gran, w_packed, w_scales, w_gran, M, N, K,
               a_unsigned=False, a_shift=0.0, w_sum=None, lora_act=None, lora_up=None,
-              bias=None, out_type=OUT.BF16, out=None, stream=None):
+              bias=None, out_type=OUT.BF16, out=None, a_layout=None, stream=None):
+    """a_layout defaults to TILED when a_codes is 3-D ([M/16, K/64, 512]), else NATURAL."""
+    if a_layout is None:
+        a_layout = LAYOUT.TILED if a_codes.dim() == 3 else LAYOUT.NATURAL
     out = _out(M, N, out_type, a_codes.device, out)
     lora_f32 = int(lora_act is not None and lora_act.dtype == torch.float32)
     R = 0 if lora_up is None else lora_up.shape[1]
-    st = lib.w4a4_gemm(_ptr(a_codes), _ptr(a_scales), a_gran, int(bool(a_unsigned)), float(a_shift),
+    st = lib.w4a4_gemm(_ptr(a_codes), int(a_layout), _ptr(a_scales), a_gran, int(bool(a_unsigned)), float(a_shift),
                        _ptr(w_packed), _ptr(w_scales), w_gran, _ptr(w_sum),
                        _ptr(lora_act), lora_f32, _ptr(lora_up), R, _ptr(bias),
                        _ptr(out), out_type, out.stride(0), M, N, K, None, 0, _stream(stream))

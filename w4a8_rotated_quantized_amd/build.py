@@ -10,12 +10,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libconvrot.so")
-SOURCES = ["rq.hip", "pack.hip", "gemm_int.hip", "gemm_w4a8.hip", "abi.cpp"]
+SOURCES = ["rq.hip", "pack.hip", "gemm_w4a4.hip", "gemm_int.hip", "gemm_w4a8.hip", "abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
     "-ffp-contract=off",
+    # matrix-core accumulators stay in arch VGPRs (no per-MFMA AGPR copies of
+    # loop-carried accumulators)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     # packed fp32 VALU ops stay off: hipcc would otherwise form them from float code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",

@@ -142,17 +142,20 @@ size_t convrot_rq_workspace_size(int64_t rows, int64_t K, int rot_group, cr_qtyp
   if (rot_group != 256 || gran != CR_GRAN_TENSOR || rows < 1 || K < 256 || K % 256) return 0;
   if (!(qtype == CR_Q_SYM_INT4 || qtype == CR_Q_SYM_INT8)) return 0;
   cr::RQGeometry g = cr::rq_geometry(rows, K, 0);
-  return (size_t)g.nblk * sizeof(float);
+  return (size_t)g.nblk * sizeof(float);     // one maximum per block of the first pass
 }
 
 cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx, int rot_group,
                                   cr_qtype qtype, cr_gran gran, int q_group, float shift,
                                   const void* lora_down, int R, void* lora_act, int lora_act_f32,
-                                  void* codes, void* scales, void* zeros, void* workspace,
+                                  void* codes, cr_layout layout, void* scales, void* zeros, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
   cr_status st = rq_validate(x, rows, K, ldx, rot_group, qtype, gran, q_group, lora_down, R, lora_act,
                              codes, scales, zeros);
   if (st != CR_OK) return st;
+  if ((int)layout < 0 || (int)layout > 1) return CR_ERR_INVALID_ARGUMENT;
+  if (layout == CR_LAYOUT_TILED && !(qtype == CR_Q_SYM_INT4 || qtype == CR_Q_UNSIGNED_INT4_SHIFT))
+    return CR_ERR_UNSUPPORTED_FORMAT;
   const size_t need = convrot_rq_workspace_size(rows, K, rot_group, qtype, gran, q_group);
   if (need > 0) {
     if (!workspace || !aligned16(workspace)) return CR_ERR_INVALID_ARGUMENT;
@@ -178,6 +181,7 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
   p.scales = scales;
   p.zeros = zeros;
   p.ws = static_cast<float*>(workspace);
+  p.tiled = layout == CR_LAYOUT_TILED ? 1 : 0;
   const uint64_t nl = (rot_group == 256 && gran == CR_GRAN_TENSOR && qtype != CR_Q_ASYM_UINT4) ? 2 : 1;
   return finish_launch(cr::launch_rotate_quantize(p, stream), E_RQ, nl);
 }
@@ -253,7 +257,8 @@ static cr_status gemm_common(const void* a, const void* w, const void* out, cr_o
   return CR_OK;
 }
 
-cr_status w4a4_gemm(const void* a_codes, const float* a_scales, cr_gran a_gran, int a_unsigned, float a_shift,
+cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scales, cr_gran a_gran,
+                    int a_unsigned, float a_shift,
                     const void* w_packed, const float* w_scales, cr_gran w_gran, const float* w_sum,
                     const void* lora_act, int lora_act_f32, const void* lora_up, int R, const void* bias,
                     void* out, cr_out out_type, int64_t ldc, int64_t M, int64_t N, int64_t K,
@@ -264,6 +269,9 @@ cr_status w4a4_gemm(const void* a_codes, const float* a_scales, cr_gran a_gran, 
   if (st != CR_OK) return st;
   if (!a_scales || !w_scales || !aligned16(a_scales) || !aligned16(w_scales)) return CR_ERR_INVALID_ARGUMENT;
   if ((int)a_gran < 0 || (int)a_gran > 2 || (int)w_gran < 0 || (int)w_gran > 2) return CR_ERR_INVALID_ARGUMENT;
+  if ((int)a_layout < 0 || (int)a_layout > 1) return CR_ERR_INVALID_ARGUMENT;
+  if (((M + 15) / 16) * 16 * (K / 2) >= ((int64_t)1 << 32) || N * (K / 2) >= ((int64_t)1 << 32))
+    return CR_ERR_UNSUPPORTED_SHAPE;
   const bool grouped = a_gran == CR_GRAN_ROW_GROUP;
   if (grouped != (w_gran == CR_GRAN_ROW_GROUP)) return CR_ERR_UNSUPPORTED_FORMAT;
   if (a_unsigned) {
@@ -298,7 +306,8 @@ cr_status w4a4_gemm(const void* a_codes, const float* a_scales, cr_gran a_gran, 
   p.N = N;
   p.K = K;
   p.grouped = grouped ? 1 : 0;
-  return finish_launch(cr::launch_gemm_int(p, stream), E_W4A4, 1);
+  p.a_tiled = a_layout == CR_LAYOUT_TILED ? 1 : 0;
+  return finish_launch(cr::launch_gemm_w4a4(p, stream), E_W4A4, 1);
 }
 
 cr_status w4a8_gemm(const void* a_codes, const float* a_scales, cr_gran a_gran, const void* w_packed,

@@ -20,20 +20,22 @@ struct RQParams {
   void* codes;
   void* scales;
   void* zeros;
-  float* ws;            // per-block maxima (TENSOR granularity)
+  float* ws;            // TENSOR: per-block maxima (two-pass) or barrier word + maxima (cooperative)
   int nblk;             // blocks of the TENSOR passes
   int G;                // 256-groups per row
-  int64_t total_groups; // rows * G
-  int rpb;              // rows per block (ROW granularity)
+  int rpb;              // rows per block (16 >> lg_spr)
+  int lg_spr;           // log2(16-lane segments per row)
+  int tiled;            // int4 codes in the [rows/16][K/64][512 B] fragment layout
 };
 
 struct RQGeometry {
   int gps;       // 256-groups per 16-lane segment
-  int rpb;       // rows per block (ROW)
-  int64_t nblk;  // blocks
+  int lg_spr;    // log2(segments per row)
+  int rpb;       // rows per block
+  int64_t gx, gy, nblk;  // grid (group tiles x row tiles) and its size
 };
 
-// gran_kind: 0/1 TENSOR passes, 2 ROW, 3 ROW_GROUP(64), 4 ASYM(16)
+// gran_kind: 0/1 TENSOR passes, 2 ROW (whole rows per block), 3 ROW_GROUP(64), 4 ASYM(16)
 RQGeometry rq_geometry(int64_t rows, int64_t K, int gran_kind);
 hipError_t launch_rotate_quantize(RQParams p, hipStream_t s);
 
@@ -74,11 +76,13 @@ struct GemmParams {
   int64_t ldc;
   int64_t M, N, K;
   int grouped;               // ROW_GROUP(64) x ROW_GROUP(64)
+  int a_tiled;               // int4 activation codes in the [M/16][K/64][512 B] layout
   // W4A8 only
   const uint16_t* w_scales16;
   const uint8_t* w_zeros;
 };
-hipError_t launch_gemm_int(const GemmParams& p, hipStream_t s);
+hipError_t launch_gemm_int(const GemmParams& p, hipStream_t s);   // INT8 x INT8
+hipError_t launch_gemm_w4a4(const GemmParams& p, hipStream_t s);  // INT4 x tile-packed INT4
 hipError_t launch_gemm_w4a8(const GemmParams& p, hipStream_t s);
 
 }  // namespace cr

@@ -8,13 +8,12 @@
 // "Qwen-Image-Edit-2511-W4A8-ConvRot" card, file layout.
 //
 // Rotation layout. A 256-element group is held by the 16 lanes of one DPP
-// row, 16 fp32 values per lane. Element index bits b0 b1 b6 b7 live in the
-// register index e = b0 + 2 b1 + 4 b6 + 8 b7; bits b2..b5 live in the lane.
-// The lane <-> bits map uses the XOR patterns a single DPP move provides
-// inside a row (lane^1, lane^2, lane^7, lane^8):
-//     L = b2*1 ^ b3*2 ^ b4*7 ^ b5*8.
-// Each lane loads 4 x 8 contiguous bytes (elements b0,b1 for each b6,b7), so
-// one load instruction of a row covers 128 contiguous bytes.
+// row, 16 fp32 values per lane. Element index bits b0..b3 are the register
+// index e (each lane owns 16 contiguous elements: two 16-byte loads, one
+// 8-byte (int4) or 16-byte (int8) code store); bits b4..b7 live in the lane,
+// with the lane <-> bits map chosen so that every cross-lane partner is one
+// DPP move inside a row (lane^1, lane^2, lane^7, lane^8):
+//     L = b4*1 ^ b5*2 ^ b6*7 ^ b7*8.
 //
 // Butterfly order is h = 1, 2, 4, ..., 128 (bits b0..b7), each a float32
 // add/sub, matching the reference definition exactly. Cross-lane stages use
@@ -22,9 +21,15 @@
 // (an exact product, so the single rounding equals that of x +- partner).
 // The lane then holds sigma * (true value) with sigma = +-1 a per-lane
 // constant; the digit-sign vector D splits into a per-register part (digits
-// b0b1 and b6b7, applied as compile-time negations) and a per-lane part
-// (digits b2b3 and b4b5, folded into sigma). All of it is undone exactly by
+// b1b0 and b3b2, applied as compile-time negations) and a per-lane part
+// (digits b5b4 and b7b6, folded into sigma). All of it is undone exactly by
 // the sign of the quantization multiplier (fl(s*v*r) = s*fl(v*r)).
+//
+// Scale granularities: per tensor (a first launch writes one maximum per
+// block, a second recomputes the rotation and quantizes with the maximum of
+// those; a single pass with a grid-wide barrier measured slower on MI355X
+// because of the barrier's cross-XCD atomics), per row (blocks own whole
+// rows), per 64-group (a quad of lanes), asymmetric per 16-group (one lane).
 #include "common.h"
 #include "kernels.h"
 
@@ -33,24 +38,28 @@ namespace cr {
 // f(d) of the digit-sign vector: -1 for a zero base-4 digit.
 CR_DEV float fdig(int d) { return d == 0 ? -1.f : 1.f; }
 constexpr float fdig_c(int d) { return d == 0 ? -1.f : 1.f; }
-// per-register part of D: digits (b1 b0) and (b7 b6) of e = b0 + 2b1 + 4b6 + 8b7
+// per-register part of D: digits (b1 b0) and (b3 b2) of e = b0 + 2b1 + 4b2 + 8b3
 constexpr bool dreg_neg(int e) { return fdig_c(e & 3) * fdig_c(e >> 2) < 0; }
 
 struct LaneRot {
-  int gL;          // element bits b2..b5 of this lane, packed (b2 + 2b3 + 4b4 + 8b5)
-  float c[4];      // cross-lane butterfly multipliers for bits b2..b5
+  int gL;          // element bits b4..b7 of this lane, packed (b4 + 2b5 + 4b6 + 8b7)
+  float c[4];      // cross-lane butterfly multipliers for bits b4..b7
   float tau;       // final per-lane sign
 };
 
 CR_DEV LaneRot lane_rot(int L) {
   LaneRot r;
-  const int b2 = (L ^ (L >> 2)) & 1;
-  const int b3 = ((L >> 1) ^ (L >> 2)) & 1;
-  const int b4 = (L >> 2) & 1;
-  const int b5 = (L >> 3) & 1;
-  r.gL = b2 | (b3 << 1) | (b4 << 2) | (b5 << 3);
-  const int bits[4] = {b2, b3, b4, b5};
-  // stage s flips element bit b_{2+s}; digit of that bit is (b3 b2) for s<2, (b5 b4) for s>=2
+  const int b4 = (L ^ (L >> 2)) & 1;
+  const int b5 = ((L >> 1) ^ (L >> 2)) & 1;
+  const int b6 = (L >> 2) & 1;
+  const int b7 = (L >> 3) & 1;
+  r.gL = b4 | (b5 << 1) | (b6 << 2) | (b7 << 3);
+  const int bits[4] = {b4, b5, b6, b7};
+  // stage s flips element bit b_{4+s}; its digit is (b5 b4) for s < 2, (b7 b6) for s >= 2.
+  // With sigma the per-lane sign (true = sigma * stored): the lane holding
+  // bit 0 keeps sigma and adds sigma_L*sigma_P*partner; the lane holding bit 1
+  // computes partner - self = -sigma_L*(self - sigma_L*sigma_P*partner) and
+  // flips sigma. sigma_L*sigma_P only depends on the digit-sign factors.
   for (int s = 0; s < 4; ++s) {
     int lo = (s < 2) ? 0 : 2;
     int d = bits[lo] + 2 * bits[lo + 1];
@@ -62,7 +71,7 @@ CR_DEV LaneRot lane_rot(int L) {
   return r;
 }
 
-// In-register butterflies over register bit `rb` (1, 2, 4, 8).
+// In-register butterflies over register bit RB (1, 2, 4, 8).
 template <int RB>
 CR_DEV void bfly_reg(float (&v)[16]) {
 #pragma unroll
@@ -95,222 +104,189 @@ CR_BFLY_LANE(bfly_lane_x2, "quad_perm:[2,3,0,1]")
 CR_BFLY_LANE(bfly_lane_x7, "row_half_mirror")
 CR_BFLY_LANE(bfly_lane_x8, "row_ror:8")
 
-// Loads one 256-group of bf16 (row pointer p at the group start) and rotates it.
-// Returns stored values (sigma * H x per element, before the final signs).
-CR_DEV void load_group(const uint16_t* __restrict__ p, int gL, u32x2 (&w)[4]) {
+// bf16 words (2 x 16 bytes = elements 0..15 of this lane) -> rotated values
+CR_DEV void rotate_group(const u32x4 (&w)[2], const LaneRot& lr, float (&v)[16]) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    w[q] = *reinterpret_cast<const u32x2*>(p + q * 64 + gL * 4);
-}
-
-CR_DEV void rotate_group(const u32x2 (&w)[4], const LaneRot& lr, float (&v)[16]) {
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    float t0 = bf16_lo(w[q][0]), t1 = bf16_hi(w[q][0]);
-    float t2 = bf16_lo(w[q][1]), t3 = bf16_hi(w[q][1]);
-    v[4 * q + 0] = dreg_neg(4 * q + 0) ? -t0 : t0;
-    v[4 * q + 1] = dreg_neg(4 * q + 1) ? -t1 : t1;
-    v[4 * q + 2] = dreg_neg(4 * q + 2) ? -t2 : t2;
-    v[4 * q + 3] = dreg_neg(4 * q + 3) ? -t3 : t3;
-  }
+    for (int j = 0; j < 4; ++j) {
+      const int e = 8 * h + 2 * j;
+      float lo = bf16_lo(w[h][j]), hi = bf16_hi(w[h][j]);
+      v[e] = dreg_neg(e) ? -lo : lo;
+      v[e + 1] = dreg_neg(e + 1) ? -hi : hi;
+    }
   bfly_reg<1>(v);                      // h = 1   (b0)
   bfly_reg<2>(v);                      // h = 2   (b1)
-  bfly_lane_x1(v, lr.c[0]);            // h = 4   (b2): partner lane ^ 1
-  bfly_lane_x2(v, lr.c[1]);            // h = 8   (b3): partner lane ^ 2
-  bfly_lane_x7(v, lr.c[2]);            // h = 16  (b4): partner lane ^ 7
-  bfly_lane_x8(v, lr.c[3]);            // h = 32  (b5): partner lane ^ 8
-  bfly_reg<4>(v);                      // h = 64  (b6)
-  bfly_reg<8>(v);                      // h = 128 (b7)
+  bfly_reg<4>(v);                      // h = 4   (b2)
+  bfly_reg<8>(v);                      // h = 8   (b3)
+  bfly_lane_x1(v, lr.c[0]);            // h = 16  (b4): partner lane ^ 1
+  bfly_lane_x2(v, lr.c[1]);            // h = 32  (b5): partner lane ^ 2
+  bfly_lane_x7(v, lr.c[2]);            // h = 64  (b6): partner lane ^ 7
+  bfly_lane_x8(v, lr.c[3]);            // h = 128 (b7): partner lane ^ 8
 }
 
-// code bits: fl(fl(v * r) + 1.5*2^23); low bits are the rounded integer
+// code bits: fl(fl(v * r) + 1.5*2^23); the low byte is the rounded integer
 CR_DEV uint32_t qbits(float v, float r) {
   return __float_as_uint(__fadd_rn(__fmul_rn(v, r), CR_MAGIC_RNE));
 }
 
-// Store the 16 codes of a rotated group for symmetric INT4 / INT8.
-// rsgn = tau * r (per-lane signed multiplier); per-register sign from D.
+// low bytes of four words -> one word (v_perm_b32 x3)
+CR_DEV uint32_t gather4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  uint32_t t = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);
+  uint32_t u = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);
+  return __builtin_amdgcn_perm(u, t, 0x05040100u);
+}
+
+// Quantize and store the 16 codes of one lane (elements 16*gL .. 16*gL+15 of
+// the group) at dst (16 bytes for INT8, 8 bytes for INT4).
+// rs = tau * r; the per-register sign of D is applied as a negated multiplier.
 template <int QT>
-CR_DEV void quant_store_sym(const float (&v)[16], float rsgn, uint8_t* __restrict__ dst_group, int gL) {
+CR_DEV void quant_store(const float (&v)[16], float rs, uint8_t* __restrict__ dst) {
   uint32_t b[16];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) b[e] = qbits(v[e], dreg_neg(e) ? -rsgn : rsgn);
-  if (QT == CR_Q_SYM_INT4) {
+  for (int e = 0; e < 16; ++e) b[e] = qbits(v[e], dreg_neg(e) ? -rs : rs);
+  if constexpr (QT == CR_Q_SYM_INT8) {
+    u32x4 o;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t h = (b[4 * q] & 0xF) | ((b[4 * q + 1] & 0xF) << 4) | ((b[4 * q + 2] & 0xF) << 8) |
-                   ((b[4 * q + 3] & 0xF) << 12);
-      *reinterpret_cast<uint16_t*>(dst_group + q * 32 + gL * 2) = (uint16_t)h;
-    }
+    for (int j = 0; j < 4; ++j) o[j] = gather4(b[4 * j], b[4 * j + 1], b[4 * j + 2], b[4 * j + 3]);
+    *reinterpret_cast<u32x4*>(dst) = o;
   } else {
+    u32x2 o;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t h = (b[4 * q] & 0xFF) | ((b[4 * q + 1] & 0xFF) << 8) | ((b[4 * q + 2] & 0xFF) << 16) |
-                   ((b[4 * q + 3] & 0xFF) << 24);
-      *reinterpret_cast<uint32_t*>(dst_group + q * 64 + gL * 4) = h;
+    for (int h = 0; h < 2; ++h) {
+      const int e = 8 * h;
+      uint32_t ev = gather4(b[e], b[e + 2], b[e + 4], b[e + 6]);
+      uint32_t od = gather4(b[e + 1], b[e + 3], b[e + 5], b[e + 7]);
+      o[h] = (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
     }
+    *reinterpret_cast<u32x2*>(dst) = o;
+  }
+}
+
+// Address of one lane's codes: natural rows, or (INT4 only) the tiled
+// fragment layout [rows/16][K/64][64 lanes x 8 B] where the lane's 16
+// elements (k = 256 grp + 16 gL ...) are chunk gL%4 of k-tile 4 grp + gL/4.
+template <int QT>
+CR_DEV uint8_t* code_dst(const RQParams& a, int64_t row, int grp, int gL) {
+  if constexpr (QT == CR_Q_SYM_INT8) {
+    return reinterpret_cast<uint8_t*>(a.codes) + row * a.K + grp * 256 + gL * 16;
+  } else {
+    if (a.tiled)
+      return reinterpret_cast<uint8_t*>(a.codes) + ((row >> 4) * (a.K / 64) + grp * 4 + (gL >> 2)) * 512 +
+             ((gL & 3) * 16 + (row & 15)) * 8;
+    return reinterpret_cast<uint8_t*>(a.codes) + row * (a.K / 2) + grp * 128 + gL * 8;
   }
 }
 
 // ---------------------------------------------------------------------------
-// rq_rot: rotation on. GR: 0 = TENSOR pass 1 (block max), 1 = TENSOR pass 2,
-// 2 = ROW, 3 = ROW_GROUP(64), 4 = ASYM ROW_GROUP(16).
-// Work: each block owns 16*GPS group slots; slot (i, seg) -> i*16 + seg.
-// ROW: a block owns rpb whole rows (slots past rpb*G idle).
+// rq_rot: rotation on.
+//   GR = RG_T1: per-tensor pass 1 (block maxima); RG_T2: pass 2 (global max
+//   from the block maxima, rotation recomputed, quantize); RG_ROW; RG_G64;
+//   RG_ASYM.
+// Work: segment s of block (bx, by) owns row bx*rpb + (s >> lg_spr) and the
+// groups by*spr*GPS + (s & (spr-1)) + spr*i, i < GPS (spr = 2^lg_spr).
 // ---------------------------------------------------------------------------
 enum { RG_T1 = 0, RG_T2 = 1, RG_ROW = 2, RG_G64 = 3, RG_ASYM = 4 };
 
 template <int QT, int GR, int GPS>
 __global__ __launch_bounds__(256) void rq_rot_kernel(RQParams a) {
-  __shared__ float red[16];
-  __shared__ unsigned rowmax[16 * 8];
+  __shared__ float red[8];
+  __shared__ unsigned rowmax[16];
   const int tid = threadIdx.x;
   const int seg = tid >> 4;
   const int L = tid & 15;
   const LaneRot lr = lane_rot(L);
-  const int G = a.G;
   const float qmax = (QT == CR_Q_SYM_INT8) ? 127.f : 7.f;
+  const int lg = a.lg_spr;
+  const int spr = 1 << lg;
+  const int rl = seg >> lg;
+  const int64_t row = (int64_t)blockIdx.x * a.rpb + rl;
+  const bool row_ok = rl < a.rpb && row < a.rows;
+  const int g0 = (int)blockIdx.y * (spr * GPS) + (seg & (spr - 1));
+  const uint16_t* xr = a.x + (row_ok ? row : 0) * a.ldx + lr.gL * 16;
 
-  int64_t row[GPS];
-  int grp[GPS];
   bool ok[GPS];
+  u32x4 w[GPS][2];
 #pragma unroll
   for (int i = 0; i < GPS; ++i) {
-    if (GR == RG_ROW) {
-      int local = i * 16 + seg;
-      int rl = local / G;
-      row[i] = (int64_t)blockIdx.x * a.rpb + rl;
-      grp[i] = local - rl * G;
-      ok[i] = (rl < a.rpb) && (row[i] < a.rows);
-    } else {
-      int64_t gi = (int64_t)blockIdx.x * (16 * GPS) + i * 16 + seg;
-      ok[i] = gi < a.total_groups;
-      row[i] = ok[i] ? gi / G : 0;
-      grp[i] = ok[i] ? (int)(gi - row[i] * G) : 0;
-    }
-  }
-
-  u32x2 w[GPS][4];
-#pragma unroll
-  for (int i = 0; i < GPS; ++i) {
+    const int grp = g0 + spr * i;
+    ok[i] = row_ok && grp < a.G;
     if (ok[i]) {
-      load_group(a.x + row[i] * a.ldx + (int64_t)grp[i] * 256, lr.gL, w[i]);
+      w[i][0] = *reinterpret_cast<const u32x4*>(xr + grp * 256);
+      w[i][1] = *reinterpret_cast<const u32x4*>(xr + grp * 256 + 8);
     } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) w[i][q] = u32x2{0u, 0u};
+      w[i][0] = u32x4{0u, 0u, 0u, 0u};
+      w[i][1] = u32x4{0u, 0u, 0u, 0u};
     }
   }
-
   float v[GPS][16];
 #pragma unroll
   for (int i = 0; i < GPS; ++i) rotate_group(w[i], lr, v[i]);
 
-  if (GR == RG_T1 || GR == RG_T2 || GR == RG_ROW) {
-    // ---------------- max over the scale group ----------------
-    float gm[GPS];
+  const int64_t crow_i = row_ok ? row : 0;
+
+  if constexpr (GR == RG_T1 || GR == RG_T2 || GR == RG_ROW) {
+    float m = 0.f;
 #pragma unroll
-    for (int i = 0; i < GPS; ++i) {
-      float m = 0.f;
+    for (int i = 0; i < GPS; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[i][e]));
-      gm[i] = row16_max(m);
-    }
+      for (int e = 0; e < 16; e += 2) m = amax3(m, fabsf(v[i][e]), fabsf(v[i][e + 1]));
+    m = row16_max(m);
     float A;
-    if (GR == RG_ROW) {
-      if (tid < 16 * 8) rowmax[tid] = 0u;
+    if constexpr (GR == RG_ROW) {
+      if (tid < 16) rowmax[tid] = 0u;
       __syncthreads();
-#pragma unroll
-      for (int i = 0; i < GPS; ++i)
-        if (ok[i] && L == 0) atomicMax(&rowmax[(i * 16 + seg) / G], __float_as_uint(gm[i]));
+      if (L == 0 && row_ok) atomicMax(&rowmax[rl], __float_as_uint(m));
       __syncthreads();
+      A = __uint_as_float(rowmax[rl]);
+      if (row_ok && (seg & (spr - 1)) == 0 && L == 0) {
+        float s = (A > 0.f) ? __fmul_rn(div_rn(A, qmax), 0.0625f) : 0.f;
+        reinterpret_cast<float*>(a.scales)[row] = s;
+      }
     } else {
-      float m = 0.f;
-#pragma unroll
-      for (int i = 0; i < GPS; ++i) m = fmaxf(m, gm[i]);
       m = fmaxf(m, __shfl_xor(m, 16));
       m = fmaxf(m, __shfl_xor(m, 32));
       if ((tid & 63) == 0) red[tid >> 6] = m;
       __syncthreads();
-      float bm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-      if (GR == RG_T1) {
-        if (tid == 0) a.ws[blockIdx.x] = bm;
+      const float bm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      const unsigned bid = blockIdx.x * gridDim.y + blockIdx.y;
+      const unsigned nblk = gridDim.x * gridDim.y;
+      if constexpr (GR == RG_T1) {
+        if (tid == 0) a.ws[bid] = bm;
         return;
       }
-      // pass 2: global max over the pass-1 block maxima
       float t = 0.f;
-      for (int j = tid; j < a.nblk; j += 256) t = fmaxf(t, a.ws[j]);
+      for (unsigned j = tid; j < nblk; j += 256) t = fmaxf(t, a.ws[j]);
       t = wave_max(t);
-      __syncthreads();
       if ((tid & 63) == 0) red[4 + (tid >> 6)] = t;
       __syncthreads();
       A = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
-      if (blockIdx.x == 0 && tid == 0) {
+      if (bid == 0 && tid == 0) {
         float s = (A > 0.f) ? __fmul_rn(div_rn(A, qmax), 0.0625f) : 0.f;
         reinterpret_cast<float*>(a.scales)[0] = s;
       }
     }
+    const float r = (A > 0.f) ? div_rn(qmax, A) : 0.f;
+#pragma unroll
+    for (int i = 0; i < GPS; ++i)
+      if (ok[i]) quant_store<QT>(v[i], lr.tau * r, code_dst<QT>(a, crow_i, g0 + spr * i, lr.gL));
+  } else if constexpr (GR == RG_G64) {
+    // 64-group = bits b0..b5: the quad of lanes sharing (b6, b7) = (L2, L3)
 #pragma unroll
     for (int i = 0; i < GPS; ++i) {
-      if (!ok[i]) continue;
-      float Ai = A;
-      if (GR == RG_ROW) {
-        int rl = (i * 16 + seg) / G;
-        Ai = __uint_as_float(rowmax[rl]);
-        if (L == 0 && grp[i] == 0) {
-          float s = (Ai > 0.f) ? __fmul_rn(div_rn(Ai, qmax), 0.0625f) : 0.f;
-          reinterpret_cast<float*>(a.scales)[row[i]] = s;
-        }
+      float m = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) m = amax3(m, fabsf(v[i][e]), fabsf(v[i][e + 1]));
+      m = quad_max(m);
+      const int grp = g0 + spr * i;
+      if (ok[i] && (L & 3) == 0) {
+        float s = (m > 0.f) ? __fmul_rn(div_rn(m, qmax), 0.0625f) : 0.f;
+        reinterpret_cast<float*>(a.scales)[row * (a.K / 64) + grp * 4 + (L >> 2)] = s;
       }
-      float r = (Ai > 0.f) ? div_rn(qmax, Ai) : 0.f;
-      uint8_t* dst = reinterpret_cast<uint8_t*>(a.codes) +
-                     row[i] * (QT == CR_Q_SYM_INT4 ? a.K / 2 : a.K) +
-                     (int64_t)grp[i] * (QT == CR_Q_SYM_INT4 ? 128 : 256);
-      quant_store_sym<QT>(v[i], lr.tau * r, dst, lr.gL);
+      const float r = (m > 0.f) ? div_rn(qmax, m) : 0.f;
+      if (ok[i]) quant_store<QT>(v[i], lr.tau * r, code_dst<QT>(a, crow_i, grp, lr.gL));
     }
-  } else if (GR == RG_G64) {
-    // 64-groups inside a 256-group: elements with fixed (b6, b7) = registers 4q..4q+3
-#pragma unroll
-    for (int i = 0; i < GPS; ++i) {
-      float rq[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float m = amax3(fabsf(v[i][4 * q]), fabsf(v[i][4 * q + 1]),
-                        fmaxf(fabsf(v[i][4 * q + 2]), fabsf(v[i][4 * q + 3])));
-        m = row16_max(m);
-        rq[q] = (m > 0.f) ? div_rn(qmax, m) : 0.f;
-        if (ok[i] && L == 0) {
-          float s = (m > 0.f) ? __fmul_rn(div_rn(m, qmax), 0.0625f) : 0.f;
-          reinterpret_cast<float*>(a.scales)[row[i] * (a.K / 64) + grp[i] * 4 + q] = s;
-        }
-      }
-      if (!ok[i]) continue;
-      uint32_t b[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float rs = lr.tau * rq[e >> 2];
-        b[e] = qbits(v[i][e], dreg_neg(e) ? -rs : rs);
-      }
-      uint8_t* dst = reinterpret_cast<uint8_t*>(a.codes) +
-                     row[i] * (QT == CR_Q_SYM_INT4 ? a.K / 2 : a.K) +
-                     (int64_t)grp[i] * (QT == CR_Q_SYM_INT4 ? 128 : 256);
-      if (QT == CR_Q_SYM_INT4) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t h = (b[4 * q] & 0xF) | ((b[4 * q + 1] & 0xF) << 4) | ((b[4 * q + 2] & 0xF) << 8) |
-                       ((b[4 * q + 3] & 0xF) << 12);
-          *reinterpret_cast<uint16_t*>(dst + q * 32 + lr.gL * 2) = (uint16_t)h;
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t h = (b[4 * q] & 0xFF) | ((b[4 * q + 1] & 0xFF) << 8) |
-                       ((b[4 * q + 2] & 0xFF) << 16) | ((b[4 * q + 3] & 0xFF) << 24);
-          *reinterpret_cast<uint32_t*>(dst + q * 64 + lr.gL * 4) = h;
-        }
-      }
-    }
-  } else {  // RG_ASYM: asymmetric uint4 per 16 consecutive rotated channels
-    // 16-group = bits b0..b3: registers 4q..4q+3 of the quad of lanes sharing L>>2.
+  } else {  // RG_ASYM: asymmetric uint4 per 16 consecutive rotated channels = one lane
 #pragma unroll
     for (int i = 0; i < GPS; ++i) {
       float t[16];
@@ -319,42 +295,33 @@ __global__ __launch_bounds__(256) void rq_rot_kernel(RQParams a) {
         float s = dreg_neg(e) ? -lr.tau : lr.tau;
         t[e] = __fmul_rn(__fmul_rn(v[i][e], s), 0.0625f);
       }
-      uint32_t hw[4];
+      float mn = t[0], mx = t[0];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float mn = fminf(fminf(t[4 * q], t[4 * q + 1]), fminf(t[4 * q + 2], t[4 * q + 3]));
-        float mx = fmaxf(fmaxf(t[4 * q], t[4 * q + 1]), fmaxf(t[4 * q + 2], t[4 * q + 3]));
-        float lo = fminf(0.f, quad_min(mn));
-        float hi = fmaxf(0.f, quad_max(mx));
-        _Float16 s16 = (_Float16)div_rn(__fsub_rn(hi, lo), 15.f);
-        bool cst = (hi == lo) || (s16 == (_Float16)0.f);
-        if (cst) s16 = (_Float16)1.f;
-        float sf = (float)s16;
-        float z = cst ? 0.f : fminf(fmaxf(rintf(div_rn(-lo, sf)), 0.f), 15.f);
-        uint32_t h = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float qq = cst ? 0.f : fminf(fmaxf(rintf(div_rn(t[4 * q + j], sf)) + z, 0.f), 15.f);
-          h |= ((uint32_t)qq) << (4 * j);
-        }
-        hw[q] = h;
-        // group index inside the 256-group: b4 + 2 b5 + 4 q = (L >> 2) + 4 q
-        int gq = (L >> 2) + 4 * q;
-        uint32_t zi = (uint32_t)z;
-        uint32_t zn = __shfl_down(zi, 4, 16);       // partner quad (gq + 1)
-        if (ok[i] && (L & 3) == 0) {
-          reinterpret_cast<_Float16*>(a.scales)[row[i] * (a.K / 16) + grp[i] * 16 + gq] = s16;
-          if (((L >> 2) & 1) == 0) {
-            reinterpret_cast<uint8_t*>(a.zeros)[row[i] * (a.K / 32) + (grp[i] * 16 + gq) / 2] =
-                (uint8_t)(zi | (zn << 4));
-          }
-        }
+      for (int e = 1; e < 16; ++e) {
+        mn = fminf(mn, t[e]);
+        mx = fmaxf(mx, t[e]);
       }
-      if (!ok[i]) continue;
-      uint8_t* dst = reinterpret_cast<uint8_t*>(a.codes) + row[i] * (a.K / 2) + (int64_t)grp[i] * 128;
+      const float lo = fminf(0.f, mn), hi = fmaxf(0.f, mx);
+      _Float16 s16 = (_Float16)div_rn(__fsub_rn(hi, lo), 15.f);
+      const bool cst = (hi == lo) || (s16 == (_Float16)0.f);
+      if (cst) s16 = (_Float16)1.f;
+      const float sf = (float)s16;
+      const float z = cst ? 0.f : fminf(fmaxf(rintf(div_rn(-lo, sf)), 0.f), 15.f);
+      u32x2 o = {0u, 0u};
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<uint16_t*>(dst + q * 32 + lr.gL * 2) = (uint16_t)hw[q];
+      for (int e = 0; e < 16; ++e) {
+        float qq = cst ? 0.f : fminf(fmaxf(rintf(div_rn(t[e], sf)) + z, 0.f), 15.f);
+        o[e >> 3] |= ((uint32_t)qq) << (4 * (e & 7));
+      }
+      const uint32_t zi = (uint32_t)z;
+      const uint32_t zp = (uint32_t)dpp_i<DPP_QUAD_1032>((int)zi);   // group gL ^ 1
+      const int grp = g0 + spr * i;
+      if (ok[i]) {
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(a.codes) + crow_i * (a.K / 2) + grp * 128 + 8 * lr.gL) = o;
+        reinterpret_cast<_Float16*>(a.scales)[row * (a.K / 16) + grp * 16 + lr.gL] = s16;
+        if ((lr.gL & 1) == 0)
+          reinterpret_cast<uint8_t*>(a.zeros)[row * (a.K / 32) + grp * 8 + lr.gL / 2] = (uint8_t)(zi | (zp << 4));
+      }
     }
   }
 }
@@ -441,9 +408,16 @@ __global__ __launch_bounds__(256) void rq_plain_kernel(RQParams a) {
       out[e >> 3] |= b << (4 * (e & 7));
     }
     if (rok) {
-      uint8_t* dst = reinterpret_cast<uint8_t*>(a.codes) + row * (a.K / 2) + t * 32;
-      *reinterpret_cast<uint32_t*>(dst + c * 4) = out[0];
-      *reinterpret_cast<uint32_t*>(dst + 16 + c * 4) = out[1];
+      if (a.tiled) {
+        // elements 64t + 32h + 8c .. +8 are half (c&1) of chunk 2h + c/2 of k-tile t
+        uint8_t* dst = reinterpret_cast<uint8_t*>(a.codes) + ((row >> 4) * (a.K / 64) + t) * 512 + rl * 8 + (c & 1) * 4;
+        *reinterpret_cast<uint32_t*>(dst + (c >> 1) * 128) = out[0];
+        *reinterpret_cast<uint32_t*>(dst + (2 + (c >> 1)) * 128) = out[1];
+      } else {
+        uint8_t* dst = reinterpret_cast<uint8_t*>(a.codes) + row * (a.K / 2) + t * 32;
+        *reinterpret_cast<uint32_t*>(dst + c * 4) = out[0];
+        *reinterpret_cast<uint32_t*>(dst + 16 + c * 4) = out[1];
+      }
     }
   }
   if (LORA) {
@@ -469,52 +443,53 @@ __global__ __launch_bounds__(256) void rq_plain_kernel(RQParams a) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+
+// Block geometry: spr segments per row, gps groups per segment, rpb rows per
+// block (16 / spr). ROW granularity needs a whole row per block.
+RQGeometry rq_geometry(int64_t rows, int64_t K, int gran_kind) {
+  RQGeometry g{};
+  const int64_t G = K / 256;
+  const int cand_gps[5] = {1, 2, 3, 4, 8};
+  double best = -1.0;
+  for (int lg = 0; lg <= 4; ++lg) {
+    const int spr = 1 << lg;
+    for (int c = 0; c < 5; ++c) {
+      const int gps = cand_gps[c];
+      const int64_t slots = (int64_t)spr * gps;
+      if (gran_kind == 2 && slots < G) continue;           // ROW: the row must fit
+      const int64_t gx = (G + slots - 1) / slots;
+      double util = (double)G / (double)(gx * slots);
+      // prefer 3-4 groups per segment (loads in flight, fewer blocks) on ties
+      double score = util + (gps >= 3 && gps <= 4 ? 1e-3 : 0.0) + (gx == 1 ? 1e-4 : 0.0);
+      if (score > best) {
+        best = score;
+        g.gps = gps;
+        g.lg_spr = lg;
+        g.gx = gx;
+      }
+    }
+  }
+  g.rpb = 16 >> g.lg_spr;
+  g.gy = (rows + g.rpb - 1) / g.rpb;
+  g.nblk = g.gx * g.gy;
+  return g;
+}
+
 template <int QT, int GR, int GPS>
-static hipError_t launch_rot(const RQParams& p, int nblk, hipStream_t s) {
-  hipLaunchKernelGGL((rq_rot_kernel<QT, GR, GPS>), dim3(nblk), dim3(256), 0, s, p);
+static hipError_t launch_rot(const RQParams& p, const RQGeometry& g, hipStream_t s) {
+  hipLaunchKernelGGL((rq_rot_kernel<QT, GR, GPS>), dim3((unsigned)g.gy, (unsigned)g.gx), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 template <int QT, int GR>
-static hipError_t launch_rot_gps(const RQParams& p, int gps, int nblk, hipStream_t s) {
-  switch (gps) {
-    case 1: return launch_rot<QT, GR, 1>(p, nblk, s);
-    case 2: return launch_rot<QT, GR, 2>(p, nblk, s);
-    case 3: return launch_rot<QT, GR, 3>(p, nblk, s);
-    case 4: return launch_rot<QT, GR, 4>(p, nblk, s);
-    default: return launch_rot<QT, GR, 8>(p, nblk, s);
+static hipError_t launch_rot_gps(const RQParams& p, const RQGeometry& g, hipStream_t s) {
+  switch (g.gps) {
+    case 1: return launch_rot<QT, GR, 1>(p, g, s);
+    case 2: return launch_rot<QT, GR, 2>(p, g, s);
+    case 3: return launch_rot<QT, GR, 3>(p, g, s);
+    case 4: return launch_rot<QT, GR, 4>(p, g, s);
+    default: return launch_rot<QT, GR, 8>(p, g, s);
   }
-}
-
-// Block geometry shared by the host-side workspace sizing and the launch.
-RQGeometry rq_geometry(int64_t rows, int64_t K, int gran_kind) {
-  RQGeometry g{};
-  const int64_t G = K / 256;
-  if (gran_kind == RG_ROW) {
-    // whole rows per block: pick the slot count (1, 2, 3, 4 or 8 groups per
-    // 16-lane segment) that leaves the fewest idle slots
-    const int cand[5] = {1, 2, 3, 4, 8};
-    double best = -1.0;
-    for (int i = 0; i < 5; ++i) {
-      int64_t slots = 16 * cand[i];
-      if (slots < G) continue;
-      int64_t rpb = slots / G;
-      if (rpb > 128) rpb = 128;
-      double util = (double)(rpb * G) / (double)slots;
-      if (util > best + 1e-9) {
-        best = util;
-        g.gps = cand[i];
-        g.rpb = (int)rpb;
-      }
-    }
-    g.nblk = g.rpb ? (rows + g.rpb - 1) / g.rpb : 0;
-  } else {
-    g.gps = 3;
-    g.rpb = 0;
-    int64_t tot = rows * G;
-    g.nblk = (tot + 16 * g.gps - 1) / (16 * g.gps);
-  }
-  return g;
 }
 
 hipError_t launch_rotate_quantize(RQParams p, hipStream_t s) {
@@ -531,33 +506,39 @@ hipError_t launch_rotate_quantize(RQParams p, hipStream_t s) {
     return hipGetLastError();
   }
   p.G = (int)(p.K / 256);
-  p.total_groups = p.rows * p.G;
   if (p.qtype == CR_Q_ASYM_UINT4) {
     RQGeometry g = rq_geometry(p.rows, p.K, RG_ASYM);
-    return launch_rot<CR_Q_ASYM_UINT4, RG_ASYM, 3>(p, (int)g.nblk, s);
+    p.lg_spr = g.lg_spr;
+    p.rpb = g.rpb;
+    return launch_rot_gps<CR_Q_ASYM_UINT4, RG_ASYM>(p, g, s);
   }
   if (p.gran == CR_GRAN_TENSOR) {
     RQGeometry g = rq_geometry(p.rows, p.K, RG_T1);
+    p.lg_spr = g.lg_spr;
+    p.rpb = g.rpb;
     p.nblk = (int)g.nblk;
     hipError_t e;
     if (p.qtype == CR_Q_SYM_INT4) {
-      e = launch_rot<CR_Q_SYM_INT4, RG_T1, 3>(p, p.nblk, s);
+      e = launch_rot_gps<CR_Q_SYM_INT4, RG_T1>(p, g, s);
       if (e != hipSuccess) return e;
-      return launch_rot<CR_Q_SYM_INT4, RG_T2, 3>(p, p.nblk, s);
+      return launch_rot_gps<CR_Q_SYM_INT4, RG_T2>(p, g, s);
     }
-    e = launch_rot<CR_Q_SYM_INT8, RG_T1, 3>(p, p.nblk, s);
+    e = launch_rot_gps<CR_Q_SYM_INT8, RG_T1>(p, g, s);
     if (e != hipSuccess) return e;
-    return launch_rot<CR_Q_SYM_INT8, RG_T2, 3>(p, p.nblk, s);
+    return launch_rot_gps<CR_Q_SYM_INT8, RG_T2>(p, g, s);
   }
   if (p.gran == CR_GRAN_ROW) {
     RQGeometry g = rq_geometry(p.rows, p.K, RG_ROW);
+    p.lg_spr = g.lg_spr;
     p.rpb = g.rpb;
-    if (p.qtype == CR_Q_SYM_INT4) return launch_rot_gps<CR_Q_SYM_INT4, RG_ROW>(p, g.gps, (int)g.nblk, s);
-    return launch_rot_gps<CR_Q_SYM_INT8, RG_ROW>(p, g.gps, (int)g.nblk, s);
+    if (p.qtype == CR_Q_SYM_INT4) return launch_rot_gps<CR_Q_SYM_INT4, RG_ROW>(p, g, s);
+    return launch_rot_gps<CR_Q_SYM_INT8, RG_ROW>(p, g, s);
   }
   RQGeometry g = rq_geometry(p.rows, p.K, RG_G64);
-  if (p.qtype == CR_Q_SYM_INT4) return launch_rot<CR_Q_SYM_INT4, RG_G64, 3>(p, (int)g.nblk, s);
-  return launch_rot<CR_Q_SYM_INT8, RG_G64, 3>(p, (int)g.nblk, s);
+  p.lg_spr = g.lg_spr;
+  p.rpb = g.rpb;
+  if (p.qtype == CR_Q_SYM_INT4) return launch_rot_gps<CR_Q_SYM_INT4, RG_G64>(p, g, s);
+  return launch_rot_gps<CR_Q_SYM_INT8, RG_G64>(p, g, s);
 }
 
 }  // namespace cr
