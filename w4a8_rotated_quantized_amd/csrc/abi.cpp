@@ -141,8 +141,7 @@ size_t convrot_rq_workspace_size(int64_t rows, int64_t K, int rot_group, cr_qtyp
   (void)q_group;
   if (rot_group != 256 || gran != CR_GRAN_TENSOR || rows < 1 || K < 256 || K % 256) return 0;
   if (!(qtype == CR_Q_SYM_INT4 || qtype == CR_Q_SYM_INT8)) return 0;
-  cr::RQGeometry g = cr::rq_geometry(rows, K, 0);
-  return (size_t)g.nblk * sizeof(float);     // one maximum per block of the first pass
+  return (size_t)cr::rq_tensor_grid(rows, K) * sizeof(float);   // one maximum per block of the first pass
 }
 
 cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx, int rot_group,

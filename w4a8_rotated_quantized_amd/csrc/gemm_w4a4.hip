@@ -267,17 +267,22 @@ __global__ __launch_bounds__(WM * WN * 64, MINB) void gemm_w4a4_kernel(GemmParam
 }
 
 // ---------------------------------------------------------------------------
-// Small-M kernel (M <= 64): weight streaming. A block owns 16 output
-// channels; its 4 waves take the 64-deep k-tiles round robin; every
-// fragment is a contiguous 512-byte run read straight from global memory;
-// partial sums are reduced through LDS in a fixed order.
+// Small-M kernel (M <= 64): weight streaming, bound by the weight bytes.
+// A block owns 16 output channels; its SK_WAVES waves take the 64-deep
+// k-tiles round robin, each issuing the loads of up to 4 k-tiles before
+// its first matrix op (at K = 3072 one round of loads covers the whole K);
+// every fragment is a contiguous 512-byte run read straight from global
+// memory; partial sums are reduced through LDS in a fixed order.
 // ---------------------------------------------------------------------------
+constexpr int SK_WAVES = 16;
+
 template <int FM, int ACT, bool A_TILED, bool GROUPED, int OUT>
-__global__ __launch_bounds__(256) void gemm_w4a4_skinny_kernel(GemmParams p) {
+__global__ __launch_bounds__(SK_WAVES * 64) void gemm_w4a4_skinny_kernel(GemmParams p) {
   constexpr bool GRP = GROUPED && OUT != CR_OUT_I32_RAW;
   constexpr int SH = (ACT == ACT_S4) ? 8 : 4;
-  constexpr int U = 4;
-  __shared__ __attribute__((aligned(16))) int red[4][FM][64][4];
+  constexpr int U = (GRP && FM == 4) ? 3 : 4;   // k-tiles in flight per wave (register budget of 1024 threads)
+  constexpr int NW = SK_WAVES;
+  __shared__ __attribute__((aligned(16))) int red[NW][FM][64][4];
   const int tid = threadIdx.x;
   const int l = tid & 63;
   const int wave = tid >> 6;
@@ -300,7 +305,7 @@ __global__ __launch_bounds__(256) void gemm_w4a4_skinny_kernel(GemmParams p) {
   }
   const uint8_t* wbase = p.w + (n0 >> 7) * G * 4096 + ((n0 & 127) >> 4) * 512 + l * 8;
 
-  for (int kt0 = wave * U; kt0 < nkt; kt0 += 4 * U) {
+  for (int kt0 = wave * U; kt0 < nkt; kt0 += NW * U) {
     u32x2 wr[U], ar[U][FM];
     float sa[U][FM];
     v4f sw[U];
@@ -354,12 +359,16 @@ __global__ __launch_bounds__(256) void gemm_w4a4_skinny_kernel(GemmParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if constexpr (GRP) {
-        y[e] = ((__int_as_float(red[0][i][l][e]) + __int_as_float(red[1][i][l][e])) +
-                __int_as_float(red[2][i][l][e])) + __int_as_float(red[3][i][l][e]);
+        float t = __int_as_float(red[0][i][l][e]);
+#pragma unroll
+        for (int w = 1; w < NW; ++w) t += __int_as_float(red[w][i][l][e]);
+        y[e] = t;
         raw[e] = 0;
       } else {
-        const int s = red[0][i][l][e] + red[1][i][l][e] + red[2][i][l][e] + red[3][i][l][e];
-        raw[e] = s >> SH;
+        int t = red[0][i][l][e];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) t += red[w][i][l][e];
+        raw[e] = t >> SH;
       }
     }
     const int64_t mb = i * 16;
@@ -394,10 +403,10 @@ static hipError_t launch_w4a4_kind(const GemmParams& p, hipStream_t s) {
     const int fm = (int)((p.M + 15) / 16);
     const dim3 grid((unsigned)(p.N / 16));
     switch (fm) {
-      case 1: hipLaunchKernelGGL((gemm_w4a4_skinny_kernel<1, ACT, AT, GROUPED, OUT>), grid, dim3(256), 0, s, p); break;
-      case 2: hipLaunchKernelGGL((gemm_w4a4_skinny_kernel<2, ACT, AT, GROUPED, OUT>), grid, dim3(256), 0, s, p); break;
-      case 3: hipLaunchKernelGGL((gemm_w4a4_skinny_kernel<3, ACT, AT, GROUPED, OUT>), grid, dim3(256), 0, s, p); break;
-      default: hipLaunchKernelGGL((gemm_w4a4_skinny_kernel<4, ACT, AT, GROUPED, OUT>), grid, dim3(256), 0, s, p); break;
+      case 1: hipLaunchKernelGGL((gemm_w4a4_skinny_kernel<1, ACT, AT, GROUPED, OUT>), grid, dim3(SK_WAVES * 64), 0, s, p); break;
+      case 2: hipLaunchKernelGGL((gemm_w4a4_skinny_kernel<2, ACT, AT, GROUPED, OUT>), grid, dim3(SK_WAVES * 64), 0, s, p); break;
+      case 3: hipLaunchKernelGGL((gemm_w4a4_skinny_kernel<3, ACT, AT, GROUPED, OUT>), grid, dim3(SK_WAVES * 64), 0, s, p); break;
+      default: hipLaunchKernelGGL((gemm_w4a4_skinny_kernel<4, ACT, AT, GROUPED, OUT>), grid, dim3(SK_WAVES * 64), 0, s, p); break;
     }
     return hipGetLastError();
   }

@@ -20,7 +20,7 @@ struct RQParams {
   void* codes;
   void* scales;
   void* zeros;
-  float* ws;            // TENSOR: per-block maxima (two-pass) or barrier word + maxima (cooperative)
+  float* ws;            // TENSOR: one maximum per block of the first of the two passes
   int nblk;             // blocks of the TENSOR passes
   int G;                // 256-groups per row
   int rpb;              // rows per block (16 >> lg_spr)
@@ -35,8 +35,9 @@ struct RQGeometry {
   int64_t gx, gy, nblk;  // grid (group tiles x row tiles) and its size
 };
 
-// gran_kind: 0/1 TENSOR passes, 2 ROW (whole rows per block), 3 ROW_GROUP(64), 4 ASYM(16)
+// gran_kind: 2 ROW (whole rows per block), 3 ROW_GROUP(64), 4 ASYM(16)
 RQGeometry rq_geometry(int64_t rows, int64_t K, int gran_kind);
+int rq_tensor_grid(int64_t rows, int64_t K);   // blocks of each per-tensor pass (one float of workspace each)
 hipError_t launch_rotate_quantize(RQParams p, hipStream_t s);
 
 struct PackParams {

@@ -179,18 +179,15 @@ CR_DEV uint8_t* code_dst(const RQParams& a, int64_t row, int grp, int gL) {
 }
 
 // ---------------------------------------------------------------------------
-// rq_rot: rotation on.
-//   GR = RG_T1: per-tensor pass 1 (block maxima); RG_T2: pass 2 (global max
-//   from the block maxima, rotation recomputed, quantize); RG_ROW; RG_G64;
-//   RG_ASYM.
+// rq_rot: rotation on, one launch: per-row scales (RG_ROW), per-64-group
+// scales (RG_G64) and asymmetric 16-group weights (RG_ASYM).
 // Work: segment s of block (bx, by) owns row bx*rpb + (s >> lg_spr) and the
 // groups by*spr*GPS + (s & (spr-1)) + spr*i, i < GPS (spr = 2^lg_spr).
 // ---------------------------------------------------------------------------
-enum { RG_T1 = 0, RG_T2 = 1, RG_ROW = 2, RG_G64 = 3, RG_ASYM = 4 };
+enum { RG_ROW = 2, RG_G64 = 3, RG_ASYM = 4 };
 
 template <int QT, int GR, int GPS>
 __global__ __launch_bounds__(256) void rq_rot_kernel(RQParams a) {
-  __shared__ float red[8];
   __shared__ unsigned rowmax[16];
   const int tid = threadIdx.x;
   const int seg = tid >> 4;
@@ -225,46 +222,21 @@ __global__ __launch_bounds__(256) void rq_rot_kernel(RQParams a) {
 
   const int64_t crow_i = row_ok ? row : 0;
 
-  if constexpr (GR == RG_T1 || GR == RG_T2 || GR == RG_ROW) {
+  if constexpr (GR == RG_ROW) {
     float m = 0.f;
 #pragma unroll
     for (int i = 0; i < GPS; ++i)
 #pragma unroll
       for (int e = 0; e < 16; e += 2) m = amax3(m, fabsf(v[i][e]), fabsf(v[i][e + 1]));
     m = row16_max(m);
-    float A;
-    if constexpr (GR == RG_ROW) {
-      if (tid < 16) rowmax[tid] = 0u;
-      __syncthreads();
-      if (L == 0 && row_ok) atomicMax(&rowmax[rl], __float_as_uint(m));
-      __syncthreads();
-      A = __uint_as_float(rowmax[rl]);
-      if (row_ok && (seg & (spr - 1)) == 0 && L == 0) {
-        float s = (A > 0.f) ? __fmul_rn(div_rn(A, qmax), 0.0625f) : 0.f;
-        reinterpret_cast<float*>(a.scales)[row] = s;
-      }
-    } else {
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
-      if ((tid & 63) == 0) red[tid >> 6] = m;
-      __syncthreads();
-      const float bm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-      const unsigned bid = blockIdx.x * gridDim.y + blockIdx.y;
-      const unsigned nblk = gridDim.x * gridDim.y;
-      if constexpr (GR == RG_T1) {
-        if (tid == 0) a.ws[bid] = bm;
-        return;
-      }
-      float t = 0.f;
-      for (unsigned j = tid; j < nblk; j += 256) t = fmaxf(t, a.ws[j]);
-      t = wave_max(t);
-      if ((tid & 63) == 0) red[4 + (tid >> 6)] = t;
-      __syncthreads();
-      A = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
-      if (bid == 0 && tid == 0) {
-        float s = (A > 0.f) ? __fmul_rn(div_rn(A, qmax), 0.0625f) : 0.f;
-        reinterpret_cast<float*>(a.scales)[0] = s;
-      }
+    if (tid < 16) rowmax[tid] = 0u;
+    __syncthreads();
+    if (L == 0 && row_ok) atomicMax(&rowmax[rl], __float_as_uint(m));
+    __syncthreads();
+    const float A = __uint_as_float(rowmax[rl]);
+    if (row_ok && (seg & (spr - 1)) == 0 && L == 0) {
+      float sc = (A > 0.f) ? __fmul_rn(div_rn(A, qmax), 0.0625f) : 0.f;
+      reinterpret_cast<float*>(a.scales)[row] = sc;
     }
     const float r = (A > 0.f) ? div_rn(qmax, A) : 0.f;
 #pragma unroll
@@ -322,6 +294,96 @@ __global__ __launch_bounds__(256) void rq_rot_kernel(RQParams a) {
         if ((lr.gL & 1) == 0)
           reinterpret_cast<uint8_t*>(a.zeros)[row * (a.K / 32) + grp * 8 + lr.gL / 2] = (uint8_t)(zi | (zp << 4));
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// rq_tensor: per-tensor scale with rotation on, two launches over the same
+// block -> data map (pass 1 then re-reads X from the L2 of the XCD that
+// read it in pass 0; the input fits the chip's combined L2 at C2 sizes).
+// Block b owns 16 rows, row block b / GC, and J consecutive 256-groups
+// starting at group (b % GC) * J (GC = ceil(G / J)); segment seg (16 lanes)
+// takes row seg. A segment reads J * 512 contiguous bytes of its row, and a
+// block writes whole J * 2 KB runs of the tiled code layout from one CU
+// (spreading the 16 rows of a run over blocks on different XCDs turns the
+// code stores into 8-byte partial-line writes from several L2s).
+//   PASS 0: max |H x| of the block -> ws[blockIdx.x].
+//   PASS 1: A = max over ws[0 .. gridDim.x), rotation recomputed, codes.
+// All J loads are issued first and each group is rotated as soon as its
+// data is in. Rows past the end are clamped to the last row and groups past
+// the end to the last group, which keeps every load and store free of
+// branches (a conditional memory operation makes the compiler wait for all
+// loads in flight before any arithmetic), leaves the maximum unchanged and
+// rewrites identical code bytes.
+// ---------------------------------------------------------------------------
+template <int QT, int PASS, int J, int NWS>
+__global__ __launch_bounds__(256) void rq_tensor_kernel(RQParams a) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int seg = tid >> 4;
+  const LaneRot lr = lane_rot(tid & 15);
+  const float qmax = (QT == CR_Q_SYM_INT8) ? 127.f : 7.f;
+  const int G = a.G;
+  const int GC = (G + J - 1) / J;
+  const int64_t row = imin64((int64_t)(blockIdx.x / (unsigned)GC) * 16 + seg, a.rows - 1);
+  const int g0 = (int)(blockIdx.x % (unsigned)GC) * J;
+  const uint16_t* xr = a.x + row * a.ldx + lr.gL * 16;
+
+  // PASS 1: the block maxima of pass 0 are loaded before the rows (NWS
+  // unconditional loads per thread, clamped indices), so that waiting for
+  // them leaves the row loads in flight; NWS = 0 is the loop for grids
+  // beyond 256 * 16 blocks.
+  float t = 0.f;
+  if constexpr (PASS == 1) {
+    const int gd = (int)gridDim.x;
+    if constexpr (NWS > 0) {
+#pragma unroll
+      for (int i = 0; i < NWS; ++i) t = fmaxf(t, a.ws[min(tid + 256 * i, gd - 1)]);
+    } else {
+      for (int i = tid; i < gd; i += 256) t = fmaxf(t, a.ws[i]);
+    }
+  }
+
+  int grp[J];
+  u32x4 w[J][2];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    grp[j] = min(g0 + j, G - 1);
+    const uint16_t* px = xr + grp[j] * 256;
+    w[j][0] = *reinterpret_cast<const u32x4*>(px);
+    w[j][1] = *reinterpret_cast<const u32x4*>(px + 8);
+  }
+  __builtin_amdgcn_sched_barrier(0);   // every load issued before the first use
+
+  if constexpr (PASS == 0) {
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      float v[16];
+      rotate_group(w[j], lr, v);
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) m = amax3(m, fabsf(v[e]), fabsf(v[e + 1]));
+    }
+    m = wave_max(m);
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    if (tid == 0) a.ws[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  } else {
+    t = wave_max(t);
+    if ((tid & 63) == 0) red[tid >> 6] = t;
+    __syncthreads();
+    const float A = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (blockIdx.x == 0 && tid == 0) {
+      const float sc = (A > 0.f) ? __fmul_rn(div_rn(A, qmax), 0.0625f) : 0.f;
+      reinterpret_cast<float*>(a.scales)[0] = sc;
+    }
+    const float rq = lr.tau * ((A > 0.f) ? div_rn(qmax, A) : 0.f);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      float v[16];
+      rotate_group(w[j], lr, v);
+      quant_store<QT>(v, rq, code_dst<QT>(a, row, grp[j], lr.gL));
     }
   }
 }
@@ -492,6 +554,40 @@ static hipError_t launch_rot_gps(const RQParams& p, const RQGeometry& g, hipStre
   }
 }
 
+// Per-tensor passes: J groups per segment, J = 4 when that still gives at
+// least 512 blocks, else fewer (small token counts).
+static int rq_tensor_j(int64_t rows, int64_t K) {
+  const int64_t units = ((rows + 15) / 16) * (K / 256);
+  if (units >= 4 * 512) return 4;
+  if (units >= 2 * 256) return 2;
+  return 1;
+}
+int rq_tensor_grid(int64_t rows, int64_t K) {   // blocks of each pass (one workspace float each)
+  const int J = rq_tensor_j(rows, K);
+  const int64_t G = K / 256;
+  return (int)(((rows + 15) / 16) * ((G + J - 1) / J));
+}
+
+template <int QT, int PASS, int J>
+static void launch_tensor_j(const RQParams& p, int gd, hipStream_t s) {
+  const int nws = (p.nblk + 255) / 256;
+  if (PASS == 0 || nws <= 1) hipLaunchKernelGGL((rq_tensor_kernel<QT, PASS, J, 1>), dim3(gd), dim3(256), 0, s, p);
+  else if (nws <= 4) hipLaunchKernelGGL((rq_tensor_kernel<QT, PASS, J, 4>), dim3(gd), dim3(256), 0, s, p);
+  else if (nws <= 16) hipLaunchKernelGGL((rq_tensor_kernel<QT, PASS, J, 16>), dim3(gd), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((rq_tensor_kernel<QT, PASS, J, 0>), dim3(gd), dim3(256), 0, s, p);
+}
+
+template <int QT, int PASS>
+static hipError_t launch_tensor(const RQParams& p, int gd, int J, hipStream_t s) {
+  switch (J) {
+    case 1: launch_tensor_j<QT, PASS, 1>(p, gd, s); break;
+    case 2: launch_tensor_j<QT, PASS, 2>(p, gd, s); break;
+    case 8: launch_tensor_j<QT, PASS, 8>(p, gd, s); break;
+    default: launch_tensor_j<QT, PASS, 4>(p, gd, s); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_rotate_quantize(RQParams p, hipStream_t s) {
   if (p.rot_group == 0) {
     const int nblk = (int)((p.rows + 15) / 16);
@@ -513,19 +609,19 @@ hipError_t launch_rotate_quantize(RQParams p, hipStream_t s) {
     return launch_rot_gps<CR_Q_ASYM_UINT4, RG_ASYM>(p, g, s);
   }
   if (p.gran == CR_GRAN_TENSOR) {
-    RQGeometry g = rq_geometry(p.rows, p.K, RG_T1);
-    p.lg_spr = g.lg_spr;
-    p.rpb = g.rpb;
-    p.nblk = (int)g.nblk;
+    const int gd0 = rq_tensor_grid(p.rows, p.K);
+    const int gd1 = gd0;
+    const int J = rq_tensor_j(p.rows, p.K);
+    p.nblk = gd0;
     hipError_t e;
     if (p.qtype == CR_Q_SYM_INT4) {
-      e = launch_rot_gps<CR_Q_SYM_INT4, RG_T1>(p, g, s);
+      e = launch_tensor<CR_Q_SYM_INT4, 0>(p, gd0, J, s);
       if (e != hipSuccess) return e;
-      return launch_rot_gps<CR_Q_SYM_INT4, RG_T2>(p, g, s);
+      return launch_tensor<CR_Q_SYM_INT4, 1>(p, gd1, J, s);
     }
-    e = launch_rot_gps<CR_Q_SYM_INT8, RG_T1>(p, g, s);
+    e = launch_tensor<CR_Q_SYM_INT8, 0>(p, gd0, J, s);
     if (e != hipSuccess) return e;
-    return launch_rot_gps<CR_Q_SYM_INT8, RG_T2>(p, g, s);
+    return launch_tensor<CR_Q_SYM_INT8, 1>(p, gd1, J, s);
   }
   if (p.gran == CR_GRAN_ROW) {
     RQGeometry g = rq_geometry(p.rows, p.K, RG_ROW);
