@@ -68,6 +68,9 @@ def test_w4a4_tensor_row(cr, case):
     assert np.array_equal(host(raw_t).astype(np.int64), ref["raw"])
     yt = cr.w4a4_gemm(at, sa, GR[ag], w, sw, GR[wg], M, N, K, out_type=1)
     assert rel_l2(host(yt), ref["y"]) <= 1e-5
+    _check_out(cr.w4a4_gemm(at, sa, GR[ag], w, sw, GR[wg], M, N, K, out_type=0), yt, ref["y"])
+    ybias_t = cr.w4a4_gemm(at, sa, GR[ag], w, sw, GR[wg], M, N, K, bias=bf16_dev(bias), out_type=1)
+    assert rel_l2(host(ybias_t), ref_b["y"]) <= 1e-5
     yb = cr.w4a4_gemm(a, sa, GR[ag], w, sw, GR[wg], M, N, K, out_type=0)
     yf = cr.w4a4_gemm(a, sa, GR[ag], w, sw, GR[wg], M, N, K, out_type=1)
     _check_out(yb, yf, ref["y"])
