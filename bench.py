@@ -101,6 +101,60 @@ def cpu_baseline(budget_s):
                       f"(numpy; elementwise stages single-threaded, BLAS threads={cores})"}
 
 
+def setup(dev, nbytes_target=600e6):
+    """Weights prepared offline (untimed) and enough buffer sets of every
+    tensor that consecutive steps touch cold HBM data."""
+    import numpy as np
+    import torch
+    import w4a8_rotated_quantized_amd as cr
+    import workloads as wl
+
+    def bf16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    xb_big = wl.activation(2, 0, M_BIG, K, n_outliers=15, outlier_scale=30.0)
+    xb_small = wl.activation(2, 2, M_SMALL, K, n_outliers=15, outlier_scale=30.0)
+    wb = wl.weight(2, 1, N, K)
+    w = bf16(wb)
+    wc, ws, _, _ = cr.convrot_rotate_quantize(w, 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
+    wp, _, _, _ = cr.w4_pack_weights(wc, ws, N, K, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
+    per_set = M_BIG * K * 2 + M_BIG * K // 2 + M_BIG * N * 2 + N * K // 2
+    nsets = max(2, int(np.ceil(nbytes_target / per_set)))
+    sets = []
+    xbig0, xsmall0 = bf16(xb_big), bf16(xb_small)
+    for _ in range(nsets):
+        sets.append({
+            "xb": xbig0.clone(), "xs": xsmall0.clone(), "wp": wp.clone(), "ws": ws.clone(),
+            "cb": torch.empty(((M_BIG + 15) // 16, K // 64, 512), dtype=torch.uint8, device=dev),
+            "cs": torch.empty(((M_SMALL + 15) // 16, K // 64, 512), dtype=torch.uint8, device=dev),
+            "sb": torch.empty(1, dtype=torch.float32, device=dev),
+            "ss": torch.empty(1, dtype=torch.float32, device=dev),
+            "wsb": torch.empty(cr.convrot_rq_workspace_size(M_BIG, K, 256, 0, 0), dtype=torch.uint8, device=dev),
+            "wss": torch.empty(cr.convrot_rq_workspace_size(M_SMALL, K, 256, 0, 0), dtype=torch.uint8, device=dev),
+            "yb": torch.empty((M_BIG, N), dtype=torch.bfloat16, device=dev),
+            "ys": torch.empty((M_SMALL, N), dtype=torch.bfloat16, device=dev),
+        })
+    return sets
+
+
+def rq_big(cr, s):
+    cr.convrot_rotate_quantize(s["xb"], 256, 0, 0, layout=cr.LAYOUT.TILED, codes=s["cb"], scales=s["sb"],
+                               workspace=s["wsb"])
+
+
+def gemm_big(cr, s):
+    cr.w4a4_gemm(s["cb"], s["sb"], 0, s["wp"], s["ws"], 0, M_BIG, N, K, out=s["yb"])
+
+
+def rq_small(cr, s):
+    cr.convrot_rotate_quantize(s["xs"], 256, 0, 0, layout=cr.LAYOUT.TILED, codes=s["cs"], scales=s["ss"],
+                               workspace=s["wss"])
+
+
+def gemm_small(cr, s):
+    cr.w4a4_gemm(s["cs"], s["ss"], 0, s["wp"], s["ws"], 0, M_SMALL, N, K, out=s["ys"])
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -111,7 +165,6 @@ def main():
     import numpy as np
     import torch
     import w4a8_rotated_quantized_amd as cr
-    import workloads as wl
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -119,37 +172,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
-
-    def bf16(a):
-        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-
-    xb_big = wl.activation(2, 0, M_BIG, K, n_outliers=15, outlier_scale=30.0)
-    xb_small = wl.activation(2, 2, M_SMALL, K, n_outliers=15, outlier_scale=30.0)
-    wb = wl.weight(2, 1, N, K)
-
-    # offline weight preparation (untimed)
-    w = bf16(wb)
-    wc, ws, _, _ = cr.convrot_rotate_quantize(w, 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
-    wp, _, _, _ = cr.w4_pack_weights(wc, ws, N, K, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
-
-    # rotating buffer sets
-    per_set = M_BIG * K * 2 + M_BIG * K // 2 + M_BIG * N * 2 + N * K // 2
-    nsets = max(2, int(np.ceil(600e6 / per_set)))
-    sets = []
-    xbig0, xsmall0 = bf16(xb_big), bf16(xb_small)
-    for _ in range(nsets):
-        s = {
-            "xb": xbig0.clone(), "xs": xsmall0.clone(), "wp": wp.clone(), "ws": ws.clone(),
-            "cb": torch.empty(((M_BIG + 15) // 16, K // 64, 512), dtype=torch.uint8, device=dev),
-            "cs": torch.empty(((M_SMALL + 15) // 16, K // 64, 512), dtype=torch.uint8, device=dev),
-            "sb": torch.empty(1, dtype=torch.float32, device=dev),
-            "ss": torch.empty(1, dtype=torch.float32, device=dev),
-            "wsb": torch.empty(cr.convrot_rq_workspace_size(M_BIG, K, 256, 0, 0), dtype=torch.uint8, device=dev),
-            "wss": torch.empty(cr.convrot_rq_workspace_size(M_SMALL, K, 256, 0, 0), dtype=torch.uint8, device=dev),
-            "yb": torch.empty((M_BIG, N), dtype=torch.bfloat16, device=dev),
-            "ys": torch.empty((M_SMALL, N), dtype=torch.bfloat16, device=dev),
-        }
-        sets.append(s)
+    sets = setup(dev)
+    nsets = len(sets)
 
     ev = {}
 
@@ -158,18 +182,16 @@ def main():
         if record:
             e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
             e[0].record(stream)
-        cr.convrot_rotate_quantize(s["xb"], 256, 0, 0, layout=cr.LAYOUT.TILED, codes=s["cb"], scales=s["sb"],
-                                   workspace=s["wsb"])
+        rq_big(cr, s)
         if record:
             e[1].record(stream)
-        cr.w4a4_gemm(s["cb"], s["sb"], 0, s["wp"], s["ws"], 0, M_BIG, N, K, out=s["yb"])
+        gemm_big(cr, s)
         if record:
             e[2].record(stream)
-        cr.convrot_rotate_quantize(s["xs"], 256, 0, 0, layout=cr.LAYOUT.TILED, codes=s["cs"], scales=s["ss"],
-                                   workspace=s["wss"])
+        rq_small(cr, s)
         if record:
             e[3].record(stream)
-        cr.w4a4_gemm(s["cs"], s["ss"], 0, s["wp"], s["ws"], 0, M_SMALL, N, K, out=s["ys"])
+        gemm_small(cr, s)
         if record:
             e[4].record(stream)
             ev.setdefault("e", []).append(e)
@@ -194,13 +216,13 @@ def main():
         step(i, True)
     torch.cuda.synchronize()
     parts = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev["e"]])
-    rq_big, gemm_big, rq_small, gemm_small = (float(np.mean(parts[:, j])) for j in range(4))
+    t_rq_big, t_gemm_big, t_rq_small, t_gemm_small = (float(np.mean(parts[:, j])) for j in range(4))
 
     ops_step = 2.0 * (M_BIG + M_SMALL) * N * K
     eff_tops = ops_step / (ms_step * 1e-3) / 1e12
-    gemm_tops = 2.0 * M_BIG * N * K / (gemm_big * 1e-3) / 1e12
+    gemm_tops = 2.0 * M_BIG * N * K / (t_gemm_big * 1e-3) / 1e12
     rq_bytes = M_BIG * K * 2 + M_BIG * K // 2 + 4
-    rq_gbs = rq_bytes / (rq_big * 1e-3) / 1e9
+    rq_gbs = rq_bytes / (t_rq_big * 1e-3) / 1e9
     small_bytes = N * K // 2 + M_SMALL * K // 2 + M_SMALL * N * 2
     traffic = traffic_from_profile()
 
@@ -222,12 +244,12 @@ def main():
                    "M": [M_BIG, M_SMALL], "N": N, "K": K, "rot_group": 256,
                    "buffer_sets": nsets},
         "pct_int8_peak": round(100.0 * eff_tops / INT8_PEAK_TOPS, 2),
-        "kernels_us": {"rq_m4096": round(rq_big * 1e3, 2), "gemm_m4096": round(gemm_big * 1e3, 2),
-                       "rq_m32": round(rq_small * 1e3, 2), "gemm_m32": round(gemm_small * 1e3, 2)},
+        "kernels_us": {"rq_m4096": round(t_rq_big * 1e3, 2), "gemm_m4096": round(t_gemm_big * 1e3, 2),
+                       "rq_m32": round(t_rq_small * 1e3, 2), "gemm_m32": round(t_gemm_small * 1e3, 2)},
         "rq_m4096_GBps": round(rq_gbs, 1),
         "rq_m4096_pct_hbm": round(100.0 * rq_gbs / HBM_PEAK_GBS, 1),
         "gemm_m4096_TOPS": round(gemm_tops, 1),
-        "gemm_m32_GBps": round(small_bytes / (gemm_small * 1e-3) / 1e9, 1),
+        "gemm_m32_GBps": round(small_bytes / (t_gemm_small * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": INT8_PEAK_TOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
                      "traffic": traffic},
