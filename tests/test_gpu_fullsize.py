@@ -67,3 +67,149 @@ def test_c2_full_pipeline(cr, c2_weights, M):
     y = bf16_to_f32(host(cr.w4a4_gemm(codes, sa, 0, packed, ws, 0, M, N, K)))
     ref_y = ol.epilogue_scalar(ref_raw, xa["scales"], "tensor", wp["scales"], "tensor")
     assert rel_l2(y[rows], ref_y) <= 2e-3
+
+
+# ---------------------------------------------------------------------------
+# the other workloads at full size (sampled outputs)
+# ---------------------------------------------------------------------------
+
+def _rows(M, n, seed):
+    return np.sort(np.random.default_rng(seed).choice(M, size=min(M, n), replace=False))
+
+
+def _cols(N, n, seed):
+    return np.sort(np.random.default_rng(seed + 1).choice(N, size=min(N, n), replace=False))
+
+
+def _lin(cfg, name):
+    w = wl.CONFIGS[cfg]()
+    return w, [l for l in w.linears if l.name == name][0]
+
+
+def test_c3_w4a8_full(cr):
+    """W4A8: X [8192, 3072] int8 per token, W [12288, 3072] asym uint4 g16."""
+    w, lin = _lin("c3", "mlp_up")
+    M, N, K = lin.M, lin.N, lin.K
+    say(f"c3 full {M}x{N}x{K}")
+    xb, wb = wl.act_bits(w, lin.x_id), wl.weight_bits(w, lin)
+    xa = ol.rotate_quantize(xb, 256, "int8", "row")
+    wp = ol.prepare_w4a8(wb)
+    a, sa, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), 256, cr.Q.SYM_INT8, cr.GRAN.ROW)
+    assert np.array_equal(host(a), xa["codes"])
+    assert np.array_equal(host(sa).view(np.uint32), np.asarray(xa["scales"], np.float32).view(np.uint32))
+    wc, ws, wz, _ = cr.convrot_rotate_quantize(bf16_dev(wb), 256, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16)
+    packed, pscales, pzeros, _ = cr.w4_pack_weights(wc, ws, N, K, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16, zeros=wz)
+    assert np.array_equal(bytes_of(packed), wp["tiles"].reshape(-1))
+    assert np.array_equal(host(pscales).view(np.uint16).reshape(-1), wp["scales_tiles"].view(np.uint16).reshape(-1))
+    assert np.array_equal(host(pzeros).reshape(-1), wp["zeros_tiles"].reshape(-1))
+    rows, cols = _rows(M, 16, 31), _cols(N, 1024, 31)
+    raw = host(cr.w4a8_gemm(a, sa, cr.GRAN.ROW, packed, pscales, pzeros, M, N, K, out_type=cr.OUT.I32_RAW))
+    zexp = np.repeat(wp["zeros"].astype(np.int64), 16, axis=1)
+    ref_raw = og.int_gemm(xa["values"][rows], wp["values"].astype(np.int64) - zexp)
+    assert np.array_equal(raw[rows].astype(np.int64), ref_raw)
+    y = bf16_to_f32(host(cr.w4a8_gemm(a, sa, cr.GRAN.ROW, packed, pscales, pzeros, M, N, K)))
+    P = og.group_partials(xa["values"][rows], wp["values"][cols], 16, wp["zeros"][cols])
+    ref_y = ol.epilogue_g16(P, np.asarray(xa["scales"])[rows], "row", wp["scales"][cols])
+    assert rel_l2(y[np.ix_(rows, cols)], ref_y) <= 2e-3
+
+
+def _int8_layer(cr, w, lin, rows_n=32):
+    M, N, K = lin.M, lin.N, lin.K
+    xb, wb = wl.act_bits(w, lin.x_id), wl.weight_bits(w, lin)
+    xa = ol.rotate_quantize(xb, 256, "int8", "tensor")
+    wq = ol.rotate_quantize(wb, 256, "int8", "tensor")
+    ws_need = cr.convrot_rq_workspace_size(M, K, 256, cr.Q.SYM_INT8, cr.GRAN.TENSOR)
+    a, sa, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), 256, cr.Q.SYM_INT8, cr.GRAN.TENSOR)
+    assert ws_need > 0
+    assert np.array_equal(host(a), xa["codes"])
+    assert host(sa)[0] == np.float32(xa["scales"]).reshape(-1)[0]
+    wc, wsc, _, _ = cr.convrot_rotate_quantize(bf16_dev(wb), 256, cr.Q.SYM_INT8, cr.GRAN.TENSOR)
+    assert np.array_equal(host(wc), wq["codes"])
+    rows = _rows(M, rows_n, 41)
+    raw = host(cr.int8_tensorwise_gemm(a, sa, wc, wsc, M, N, K, out_type=cr.OUT.I32_RAW))
+    ref_raw = og.int_gemm(xa["values"][rows], wq["values"])
+    assert np.array_equal(raw[rows].astype(np.int64), ref_raw)
+    y = bf16_to_f32(host(cr.int8_tensorwise_gemm(a, sa, wc, wsc, M, N, K)))
+    ref_y = ol.epilogue_scalar(ref_raw, xa["scales"], "tensor", wq["scales"], "tensor")
+    assert rel_l2(y[rows], ref_y) <= 2e-3
+
+
+def _w4a4_layer(cr, w, lin, rows_n=32):
+    M, N, K = lin.M, lin.N, lin.K
+    xb, wb = wl.act_bits(w, lin.x_id), wl.weight_bits(w, lin)
+    xa = ol.rotate_quantize(xb, 256, "int4", "tensor")
+    wp = ol.prepare_w4a4(wb)
+    codes, sa, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR,
+                                                 layout=cr.LAYOUT.TILED)
+    assert np.array_equal(opack.tile_unpack_a(bytes_of(codes).reshape((M + 15) // 16, K // 64, 512), M),
+                          xa["codes"])
+    assert host(sa)[0] == np.float32(xa["scales"]).reshape(-1)[0]
+    wc, ws, _, _ = cr.convrot_rotate_quantize(bf16_dev(wb), 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
+    packed, _, _, _ = cr.w4_pack_weights(wc, ws, N, K)
+    assert np.array_equal(bytes_of(packed), wp["tiles"].reshape(-1))
+    rows = _rows(M, rows_n, 51)
+    raw = host(cr.w4a4_gemm(codes, sa, 0, packed, ws, 0, M, N, K, out_type=cr.OUT.I32_RAW))
+    ref_raw = og.int_gemm(xa["values"][rows], wp["values"])
+    assert np.array_equal(raw[rows].astype(np.int64), ref_raw)
+    y = bf16_to_f32(host(cr.w4a4_gemm(codes, sa, 0, packed, ws, 0, M, N, K)))
+    ref_y = ol.epilogue_scalar(ref_raw, xa["scales"], "tensor", wp["scales"], "tensor")
+    assert rel_l2(y[rows], ref_y) <= 2e-3
+
+
+@pytest.mark.parametrize("name", ["img_v", "img_mod"])
+def test_c4_int8_layers_full(cr, name):
+    w, lin = _lin("c4", name)
+    say(f"c4 full {name} {lin.M}x{lin.N}x{lin.K}")
+    _int8_layer(cr, w, lin)
+
+
+@pytest.mark.parametrize("name", ["img_mlp_up", "img_mlp_down", "txt_q"])
+def test_c4_w4a4_layers_full(cr, name):
+    w, lin = _lin("c4", name)
+    say(f"c4 full {name} {lin.M}x{lin.N}x{lin.K}")
+    _w4a4_layer(cr, w, lin)
+
+
+@pytest.mark.parametrize("name", ["qkv", "mlp_down"])
+def test_c5_lowrank_g64_full(cr, name):
+    """Low-rank corrected W4A4 with 64-group scales (no rotation): rank-32
+    branch with the down-projection fused into the quantizer and the
+    up-projection into the GEMM epilogue; MLP down takes the unsigned
+    post-GELU path with the 0.171875 shift."""
+    w, lin = _lin("c5", name)
+    M, N, K = lin.M, lin.N, lin.K
+    shift = lin.unsigned_shift
+    uns = shift != 0.0
+    say(f"c5 full {name} {M}x{N}x{K}")
+    xb = wl.act_bits(w, lin.x_id)
+    l1, l2, r = wl.lowrank_bits(w, lin)
+    xa = ol.rotate_quantize(xb, 0, "uint4_shift" if uns else "int4", "row_group", 64, shift)
+    la_ref = ol.lora_down(xb, l2)
+    wp = ol.prepare_w4a4(r, 0, "row_group", 64)
+    qt = cr.Q.UNSIGNED_INT4_SHIFT if uns else cr.Q.SYM_INT4
+    codes, sa, _, la = cr.convrot_rotate_quantize(bf16_dev(xb), 0, qt, cr.GRAN.ROW_GROUP, 64, shift=shift,
+                                                  lora_down=bf16_dev(l2), layout=cr.LAYOUT.TILED)
+    assert np.array_equal(opack.tile_unpack_a(bytes_of(codes).reshape((M + 15) // 16, K // 64, 512), M),
+                          xa["codes"])
+    assert np.array_equal(host(sa).view(np.uint32), np.asarray(xa["scales"], np.float32).view(np.uint32))
+    # low-rank activations: bf16 of a float32 sum taken in another order -> within one bf16 ulp
+    la_ref32 = ol.lora_down(xb, l2, act_f32=True).astype(np.float64)
+    mag = np.abs(wl.f32_from_bf16_bits(xb)).astype(np.float64) @ np.abs(wl.f32_from_bf16_bits(l2)).astype(np.float64).T
+    got_la = wl.f32_from_bf16_bits(host(la)).astype(np.float64)
+    assert np.all(np.abs(got_la - la_ref32) <= np.abs(la_ref32) * 2.0 ** -7 + mag * 2 ** -20 + 1e-30)
+    wc, ws, _, _ = cr.convrot_rotate_quantize(bf16_dev(r), 0, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64)
+    packed, pscales, _, wsum = cr.w4_pack_weights(wc, ws, N, K, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64,
+                                                  want_wsum=True)
+    assert np.array_equal(bytes_of(packed), wp["tiles"].reshape(-1))
+    assert np.array_equal(host(pscales).reshape(-1), wp["scales_tiles"].reshape(-1))
+    kw = dict(a_unsigned=uns, a_shift=shift, w_sum=wsum)
+    rows, cols = _rows(M, 16, 61), _cols(N, 1024, 61)
+    raw = host(cr.w4a4_gemm(codes, sa, 2, packed, pscales, 2, M, N, K, out_type=cr.OUT.I32_RAW, **kw))
+    ref_raw = og.int_gemm(xa["values"][rows], wp["values"])
+    assert np.array_equal(raw[rows].astype(np.int64), ref_raw)
+    y = bf16_to_f32(host(cr.w4a4_gemm(codes, sa, 2, packed, pscales, 2, M, N, K, lora_act=la,
+                                      lora_up=bf16_dev(l1), **kw)))
+    P = og.group_partials(xa["values"][rows], wp["values"][cols], 64)
+    ref_y = ol.epilogue_g64(P, np.asarray(xa["scales"])[rows], np.asarray(wp["scales"])[cols], shift,
+                            np.asarray(wp["wsum"])[cols], la_ref[rows], l1[cols])
+    assert rel_l2(y[np.ix_(rows, cols)], ref_y) <= 2e-3

@@ -201,3 +201,32 @@ CONFIGS = {
     "c4": _c4,
     "c5": _c5,
 }
+
+
+# --------------------------------------------------------------------------
+# per-workload tensors (shared by the full-size tests and the benchmark, so
+# both draw exactly the same inputs)
+# --------------------------------------------------------------------------
+
+def act_bits(w: Workload, name: str) -> np.ndarray:
+    """bf16 bits of activation tensor `name` of workload `w`."""
+    M, K, kind, n_out, scale = w.acts[name]
+    tid = 100 + sorted(w.acts).index(name)
+    if kind == "gelu":
+        return gelu_activation(w.config_id, tid, M, K)
+    return activation(w.config_id, tid, M, K, n_out, scale)
+
+
+def weight_bits(w: Workload, lin: LinearSpec) -> np.ndarray:
+    """bf16 bits [N, K] of the weight of linear `lin` of workload `w`."""
+    tid = 200 + [l.name for l in w.linears].index(lin.name)
+    return weight(w.config_id, tid, lin.N, lin.K)
+
+
+def lowrank_bits(w: Workload, lin: LinearSpec):
+    """(L1 [N, rank], L2 [rank, K], R [N, K]) bf16 bits of a low-rank-corrected
+    linear: the rank-`lin.rank` split of its weight (see lowrank_split)."""
+    return lowrank_split(weight_bits(w, lin), lin.rank)
+
+
+__all__ += ["Workload", "act_bits", "weight_bits", "lowrank_bits"]
