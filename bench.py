@@ -20,7 +20,9 @@ M=4096 GEMM) against that peak; its duration comes from HIP events around
 each of its launches on the launch stream. The CPU baseline is the numpy
 oracle running the same step on this host.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--workload c2|c1|c3|c4|c5]
+(--workload other than c2 prints that workload's throughput line instead;
+see bench_workloads.py)
 """
 import argparse
 import hashlib
@@ -45,6 +47,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--workload", default="c2",
+                    help="c2 (default: the headline line), or c1 / c3 / c4 / c5 for the other workloads' "
+                         "throughput lines (bench_workloads.py)")
     return ap.parse_args()
 
 
@@ -161,6 +166,12 @@ def main():
         print(f"bench.py measures one GPU only (the path has no multi-GPU part); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload != "c2":
+        import bench_workloads
+        for name in args.workload.split(","):
+            bench_workloads.run(name, args.steps, args.warmup)
+        return
 
     import numpy as np
     import torch

@@ -427,6 +427,168 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// INT8 main kernel: operands straight from global memory into LDS. For
+// v_mfma_i32_16x16x64_i8 a lane's operand is 16 consecutive k-bytes of one
+// row, which in the natural row-major int8 layout are contiguous, so each
+// lane of a global_load_lds_dwordx4 fetches exactly its fragment bytes
+// (row 16 b + l % 16, k-bytes 64 kt + 16 (l / 16)) and one wave instruction
+// fills one 1 KB operand fragment. Two-stage LDS ring of two 64-deep
+// k-tiles, one bare s_barrier per stage after explicit vmcnt/lgkmcnt waits
+// (the fence of __syncthreads() would also wait for the next stage's loads).
+// No widening: int8 codes feed the matrix cores directly.
+// Block 128 x 128, 2 x 2 waves of 64 x 64, two blocks per CU (64 KB of LDS
+// each).
+// ---------------------------------------------------------------------------
+typedef const void __attribute__((address_space(1)))* gas_ptr_i8;
+typedef void __attribute__((address_space(3)))* las_ptr_i8;
+
+template <int N>
+CR_DEV void wait_vmcnt_lgkm0_i8() {   // s_waitcnt vmcnt(N) lgkmcnt(0)
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+template <int OUT>
+__global__ __launch_bounds__(256, 2) void gemm_int8_lds_kernel(GemmParams p) {
+  constexpr int BM = 128, BN = 128, BKT = 2, S = 2;
+  constexpr int WN = 2, NW = 4;
+  constexpr int FM = BM / 2 / 16, FN = BN / WN / 16;
+  constexpr int A_ST = BM * 64 * BKT, W_ST = BN * 64 * BKT, STAGE = A_ST + W_ST;
+  constexpr int NA = A_ST / 1024, NWL = W_ST / 1024;
+  static_assert(NA % NW == 0 && NWL % NW == 0, "wave-loads split evenly over the waves");
+  constexpr int LA = NA / NW, LW = NWL / NW;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem_i8[];
+  uint8_t* smem = smem_i8;
+
+  const int tid = threadIdx.x;
+  const int l = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+
+  const int ntm = (int)((p.M + BM - 1) / BM);
+  const int ntn = (int)(p.N / BN);
+  const int ntiles = ntm * ntn;
+  int t = (int)blockIdx.x;
+  if (ntiles % 8 == 0) t = (t & 7) * (ntiles / 8) + (t >> 3);
+  constexpr int GM = 8;
+  const int band = t / (GM * ntn);
+  const int rows_in_band = min(GM, ntm - band * GM);
+  const int within = t - band * GM * ntn;
+  const int tn = within / rows_in_band;
+  const int tm = band * GM + within % rows_in_band;
+  const int64_t m0 = (int64_t)tm * BM;
+  const int64_t n0 = (int64_t)tn * BN;
+  const int64_t K = p.K;
+  const int nkb = (int)(K / (64 * BKT));
+
+  // wave-load wl of the A (W) part is fragment (row block wl / BKT, k-tile wl % BKT)
+  int64_t offa[LA], offw[LW];
+#pragma unroll
+  for (int j = 0; j < LA; ++j) {
+    const int wl = wave + NW * j;
+    const int64_t m = imin64(m0 + (wl / BKT) * 16 + (l & 15), p.M - 1);   // rows past M: never stored
+    offa[j] = m * K + (wl % BKT) * 64 + (l >> 4) * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < LW; ++j) {
+    const int wl = wave + NW * j;
+    offw[j] = (n0 + (wl / BKT) * 16 + (l & 15)) * K + (wl % BKT) * 64 + (l >> 4) * 16;
+  }
+  auto issue = [&](int kb) {
+    uint8_t* st = smem + (kb % S) * STAGE;
+    const int64_t k0 = (int64_t)kb * (BKT * 64);
+#pragma unroll
+    for (int j = 0; j < LA; ++j)
+      __builtin_amdgcn_global_load_lds((gas_ptr_i8)(p.a + offa[j] + k0), (las_ptr_i8)(st + (wave + NW * j) * 1024),
+                                       16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < LW; ++j)
+      __builtin_amdgcn_global_load_lds((gas_ptr_i8)(p.w + offw[j] + k0),
+                                       (las_ptr_i8)(st + A_ST + (wave + NW * j) * 1024), 16, 0, 0);
+  };
+
+  v4i acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+  issue(0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    static_assert(S == 2, "the wait below assumes one stage in flight behind the current one");
+    wait_vmcnt_lgkm0_i8<0>();
+    __builtin_amdgcn_s_barrier();
+    if (kb + 1 < nkb) issue(kb + 1);
+    const uint8_t* As = smem + (kb % S) * STAGE;
+    const uint8_t* Ws = As + A_ST;
+    v4i ra[2][FM], rw[2][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) ra[0][i] = *reinterpret_cast<const v4i*>(As + ((wm * FM + i) * BKT) * 1024 + l * 16);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) rw[0][j] = *reinterpret_cast<const v4i*>(Ws + ((wn * FN + j) * BKT) * 1024 + l * 16);
+#pragma unroll
+    for (int kt = 0; kt < BKT; ++kt) {
+      const int cb = kt & 1;
+      if (kt + 1 < BKT) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          ra[cb ^ 1][i] = *reinterpret_cast<const v4i*>(As + ((wm * FM + i) * BKT + kt + 1) * 1024 + l * 16);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          rw[cb ^ 1][j] = *reinterpret_cast<const v4i*>(Ws + ((wn * FN + j) * BKT + kt + 1) * 1024 + l * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(rw[cb][j], ra[cb][i], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  const float sa_t = (p.a_gran == CR_GRAN_TENSOR) ? p.a_scales[0] : 0.f;
+  const float sw_t = (p.w_gran == CR_GRAN_TENSOR) ? p.w_scales[0] : 0.f;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t mb = m0 + (wm * FM + i) * 16;
+    const int64_t m = mb + (l & 15);
+    const int64_t mc = m < p.M ? m : p.M - 1;
+    float sa = 0.f;
+    if constexpr (OUT != CR_OUT_I32_RAW) sa = (p.a_gran == CR_GRAN_TENSOR) ? sa_t : p.a_scales[mc];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = n0 + (wn * FN + j) * 16 + (l >> 4) * 4;
+      float y[4];
+      int raw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) raw[e] = acc[i][j][e];
+      if constexpr (OUT != CR_OUT_I32_RAW) {
+        v4f sw;
+        if (p.w_gran == CR_GRAN_TENSOR) sw = v4f{sw_t, sw_t, sw_t, sw_t};
+        else sw = *reinterpret_cast<const v4f*>(p.w_scales + n);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = (float)raw[e] * (sa * sw[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = 0.f;
+      }
+      finish_block<OUT>(p, m, n, mb, l, y, raw);
+    }
+  }
+}
+
+template <int OUT>
+static hipError_t launch_int8_lds(const GemmParams& p, hipStream_t s) {
+  constexpr int lds = 2 * (128 * 64 * 2 + 128 * 64 * 2);
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)gemm_int8_lds_kernel<OUT>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  const int64_t tiles = ((p.M + 127) / 128) * (p.N / 128);
+  hipLaunchKernelGGL((gemm_int8_lds_kernel<OUT>), dim3((unsigned)tiles), dim3(256), lds, s, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
 template <int ACT, int WGT, bool GROUPED, int OUT>
@@ -442,10 +604,15 @@ static hipError_t launch_kind(const GemmParams& p, hipStream_t s) {
     }
     return hipGetLastError();
   }
-  constexpr int BM = 128, BN = 128;
-  const int64_t tiles = ((p.M + BM - 1) / BM) * (p.N / BN);
-  hipLaunchKernelGGL((gemm_big_kernel<BM, BN, 2, 2, ACT, WGT, GROUPED, OUT>), dim3((unsigned)tiles), dim3(256), 0, s, p);
-  return hipGetLastError();
+  if constexpr (ACT == ACT_I8 && WGT == WGT_I8N && !GROUPED) {
+    return launch_int8_lds<OUT>(p, s);
+  } else {
+    constexpr int BM = 128, BN = 128;
+    const int64_t tiles = ((p.M + BM - 1) / BM) * (p.N / BN);
+    hipLaunchKernelGGL((gemm_big_kernel<BM, BN, 2, 2, ACT, WGT, GROUPED, OUT>), dim3((unsigned)tiles), dim3(256), 0,
+                       s, p);
+    return hipGetLastError();
+  }
 }
 
 template <int ACT, int WGT, bool GROUPED>
