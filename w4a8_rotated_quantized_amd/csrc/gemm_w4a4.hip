@@ -293,15 +293,24 @@ CR_DEV void wait_vmcnt_lgkm0() {
 
 constexpr int LDS_BM = 128, LDS_BN = 128, LDS_BKT = 2, LDS_S = 2;
 
-template <int ACT, int OUT>
-__global__ __launch_bounds__(256, 3) void gemm_w4a4_lds_kernel(GemmParams p) {
+// GRP: 64-group scales (the float epilogue runs per k-tile). A stage then
+// also holds the scales of its two k-tiles: activation scales [2][BM] (4-byte
+// pieces from the row-major [M, K/64] array) and weight scales [2][BN] (one
+// 1 KB piece of the tile-packed [N/128][K/64][128] array).
+template <int ACT, int OUT, bool GRP>
+__global__ __launch_bounds__(256, GRP ? 2 : 3) void gemm_w4a4_lds_kernel(GemmParams p) {
   constexpr int BM = LDS_BM, BN = LDS_BN, BKT = LDS_BKT, S = LDS_S;
   constexpr int WN = 2, NW = 4;
   constexpr int FM = BM / 2 / 16, FN = BN / WN / 16;
-  constexpr int A_ST = BM * 32 * BKT, W_ST = BN * 32 * BKT, STAGE = A_ST + W_ST;
+  constexpr int A_ST = BM * 32 * BKT, W_ST = BN * 32 * BKT;
+  constexpr int SA_ST = GRP ? BKT * BM * 4 : 0, SW_ST = GRP ? BKT * BN * 4 : 0;
+  constexpr int STAGE = A_ST + W_ST + SA_ST + SW_ST;
   constexpr int NA = A_ST / 1024, NWL = W_ST / 1024;   // 1 KB wave-loads per stage
   static_assert(NA % NW == 0 && NWL % NW == 0, "wave-loads split evenly over the waves");
-  constexpr int LA = NA / NW, LW = NWL / NW, LPW = LA + LW;
+  static_assert(SW_ST == 0 || SW_ST == 1024, "weight scales of a stage are one wave-load");
+  constexpr int LA = NA / NW, LW = NWL / NW;
+  constexpr int LSA = SA_ST / 256 / NW;                // 256-byte (4 B per lane) wave-loads per wave
+  static_assert(SA_ST % (256 * NW) == 0, "activation scales split evenly over the waves");
   constexpr int SH = (ACT == ACT_S4) ? 8 : 4;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
 
@@ -346,6 +355,18 @@ __global__ __launch_bounds__(256, 3) void gemm_w4a4_lds_kernel(GemmParams p) {
     const int64_t n16 = n0 / 16 + nb;
     offw[j] = (uint32_t)(((n16 >> 3) * KT + kt) * 4096 + (n16 & 7) * 512 + r * 16);
   }
+  // scales (GRP): activation-scale entry e = kt * BM + r of a stage is
+  // a_scales[(m0 + r) * K/64 + BKT * kb + kt]; the weight scales of a stage
+  // are the 1 KB run ((n0 / 128) * K/64 + BKT * kb) * 512 of the packed array
+  int64_t offsa[GRP ? LSA : 1];
+  if constexpr (GRP) {
+#pragma unroll
+    for (int j = 0; j < LSA; ++j) {
+      const int e = (wave + NW * j) * 64 + l;
+      const int kt = e / BM, r = e % BM;
+      offsa[j] = imin64(m0 + r, p.M - 1) * KT + kt;
+    }
+  }
   auto issue = [&](int kb) {
     uint8_t* st = smem + (kb % S) * STAGE;
     const uint8_t* ga = p.a + (size_t)kb * (BKT * 512);
@@ -357,13 +378,33 @@ __global__ __launch_bounds__(256, 3) void gemm_w4a4_lds_kernel(GemmParams p) {
     for (int j = 0; j < LW; ++j)
       __builtin_amdgcn_global_load_lds((gas_ptr)(gw + offw[j]), (las_ptr)(st + A_ST + (wave + NW * j) * 1024), 16, 0,
                                        0);
+    if constexpr (GRP) {
+      uint8_t* ss = st + A_ST + W_ST;
+#pragma unroll
+      for (int j = 0; j < LSA; ++j)
+        __builtin_amdgcn_global_load_lds((gas_ptr)(p.a_scales + offsa[j] + (int64_t)kb * BKT),
+                                         (las_ptr)(ss + (wave + NW * j) * 256), 4, 0, 0);
+      if (wave == 0)
+        __builtin_amdgcn_global_load_lds(
+            (gas_ptr)(reinterpret_cast<const uint8_t*>(p.w_scales) + ((n0 >> 7) * KT + (int64_t)kb * BKT) * 512 + l * 16),
+            (las_ptr)(ss + SA_ST), 16, 0, 0);
+    }
   };
 
-  v4i acc[FM][FN];
+  v4i acc[GRP ? 1 : FM][GRP ? 1 : FN];
+  float yacc[GRP ? FM : 1][GRP ? FN : 1][4];
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < (GRP ? 1 : FM); ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < (GRP ? 1 : FN); ++j) acc[i][j] = v4i{0, 0, 0, 0};
+  if constexpr (GRP) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yacc[i][j][e] = 0.f;
+  }
 
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
@@ -395,16 +436,59 @@ __global__ __launch_bounds__(256, 3) void gemm_w4a4_lds_kernel(GemmParams p) {
       v4i wv[FN];
 #pragma unroll
       for (int j = 0; j < FN; ++j) wv[j] = widen_s4x16(rw[cb][j]);
+      if constexpr (GRP) {
+        // y += P * a_s * w_s for this 64-deep group; the widening factor
+        // 2^SH is folded into the weight scale (exact: a power of two)
+        const float* Ss = reinterpret_cast<const float*>(Ws + W_ST);
+        float sa[FM];
+        v4f sw[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const v4i av = widen_a4<ACT>(ra[cb][i]);
+        for (int i = 0; i < FM; ++i) sa[i] = Ss[kt * BM + (wm * FM + i) * 16 + (l & 15)];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[j], av, acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j) {
+          sw[j] = *reinterpret_cast<const v4f*>(Ss + BKT * BM + kt * BN + (wn * FN + j) * 16 + (l >> 4) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sw[j][e] *= 1.0f / (float)(1 << SH);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const v4i av = widen_a4<ACT>(ra[cb][i]);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const v4i pp = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[j], av, v4i{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) yacc[i][j][e] = __builtin_fmaf((float)pp[e] * sw[j][e], sa[i], yacc[i][j][e]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const v4i av = widen_a4<ACT>(ra[cb][i]);
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[j], av, acc[i][j], 0, 0, 0);
+        }
       }
     }
   }
 
+  if constexpr (GRP) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t mb = m0 + (wm * FM + i) * 16;
+      const int64_t m = mb + (l & 15);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int64_t n = n0 + (wn * FN + j) * 16 + (l >> 4) * 4;
+        const int raw[4] = {0, 0, 0, 0};
+        finish_block<OUT>(p, m, n, mb, l, yacc[i][j], raw);
+      }
+    }
+    return;
+  }
+
   // ---- epilogue (tensor or row scales) ----
+  if constexpr (!GRP) {
   const float sa_t = (p.a_gran == CR_GRAN_TENSOR) ? p.a_scales[0] : 0.f;
   const float sw_t = (p.w_gran == CR_GRAN_TENSOR) ? p.w_scales[0] : 0.f;
 #pragma unroll
@@ -433,6 +517,7 @@ __global__ __launch_bounds__(256, 3) void gemm_w4a4_lds_kernel(GemmParams p) {
       }
       finish_block<OUT>(p, m, n, mb, l, y, raw);
     }
+  }
   }
 }
 
@@ -580,9 +665,10 @@ static hipError_t launch_w4a4_kind(const GemmParams& p, hipStream_t s) {
     }
     return hipGetLastError();
   }
-  if constexpr (AT && !(GROUPED && OUT != CR_OUT_I32_RAW)) {
+  if constexpr (AT) {
+    constexpr bool GRPK = GROUPED && OUT != CR_OUT_I32_RAW;
     const int64_t tiles = ((p.M + LDS_BM - 1) / LDS_BM) * (p.N / LDS_BN);
-    hipLaunchKernelGGL((gemm_w4a4_lds_kernel<ACT, OUT>), dim3((unsigned)tiles), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemm_w4a4_lds_kernel<ACT, OUT, GRPK>), dim3((unsigned)tiles), dim3(256), 0, s, p);
     return hipGetLastError();
   }
   // 128 x 128 tiles, two blocks per CU (measured on MI355X at M=4096,
