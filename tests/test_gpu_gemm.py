@@ -27,10 +27,18 @@ def cr():
     return m
 
 
-def _check_out(y_bf16, y_f32, ref_y):
+def _check_out(y_bf16, y_f32, ref_y, f32_tol=1e-5):
     yb = bf16_to_f32(host(y_bf16))
     assert rel_l2(yb, ref_y) <= 2e-3, rel_l2(yb, ref_y)
-    assert rel_l2(host(y_f32), ref_y) <= 1e-5, rel_l2(host(y_f32), ref_y)
+    assert rel_l2(host(y_f32), ref_y) <= f32_tol, rel_l2(host(y_f32), ref_y)
+
+
+# The W4A8 float outputs come from weights dequantized to fp16(s * (q - z)) on
+# the fp16 matrix cores: one rounding per weight, |delta| <= 2^-11, which for
+# uncorrelated errors gives a relative L2 of about 2^-11 / sqrt(3) = 2.8e-4 on
+# the float32 output. The bar for it is 1e-3; the bf16 bar stays 2e-3 and the
+# exact int32 output (int8 matrix cores) stays bit-exact.
+W4A8_F32_TOL = 1e-3
 
 
 W4A4_CASES = [
@@ -182,9 +190,9 @@ def test_w4a8(cr, case):
     assert np.array_equal(host(raw).astype(np.int64), ref["raw"])
     yb = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, out_type=0)
     yf = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, out_type=1)
-    _check_out(yb, yf, ref["y"])
+    _check_out(yb, yf, ref["y"], f32_tol=W4A8_F32_TOL)
     ybias = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, bias=bf16_dev(bias), out_type=1)
-    assert rel_l2(host(ybias), ref_b["y"]) <= 1e-5
+    assert rel_l2(host(ybias), ref_b["y"]) <= W4A8_F32_TOL
 
 
 def test_extreme_codes_no_overflow(cr):
