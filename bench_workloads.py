@@ -62,8 +62,9 @@ def run(name, steps, warmup):
         elif lin.fmt == "w4a8":
             wc, ws, wz, _ = cr.convrot_rotate_quantize(bf16(wl.weight_bits(w, lin)), 256, cr.Q.ASYM_UINT4,
                                                        cr.GRAN.ROW_GROUP, 16)
-            p, ps, pz, _ = cr.w4_pack_weights(wc, ws, N, K, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16, zeros=wz)
-            prep[lin.name] = dict(w=p, ws=ps, wz=pz)
+            p, ps, pz, wsum = cr.w4_pack_weights(wc, ws, N, K, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16, zeros=wz,
+                                                 want_wsum=True)
+            prep[lin.name] = dict(w=p, ws=ps, wz=pz, wsum=wsum)
         else:
             l1, l2, r = wl.lowrank_bits(w, lin)
             wc, ws, _, _ = cr.convrot_rotate_quantize(bf16(r), 0, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64)
@@ -123,7 +124,8 @@ def run(name, steps, warmup):
         elif lin.fmt == "int8":
             cr.int8_tensorwise_gemm(o["codes"], o["scales"], p["w"], p["ws"], M, N, K, out=y)
         elif lin.fmt == "w4a8":
-            cr.w4a8_gemm(o["codes"], o["scales"], cr.GRAN.ROW, p["w"], p["ws"], p["wz"], M, N, K, out=y)
+            cr.w4a8_gemm(o["codes"], o["scales"], cr.GRAN.ROW, p["w"], p["ws"], p["wz"], M, N, K, out=y,
+                         w_sum=p["wsum"])
         else:
             cr.w4a4_gemm(o["codes"], o["scales"], 2, p["w"], p["ws"], 2, M, N, K,
                          a_unsigned=lin.unsigned_shift != 0.0, a_shift=lin.unsigned_shift, w_sum=p["wsum"],

@@ -185,9 +185,11 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
  *   packed_scales  ROW_GROUP(64): float32 [N/128][K/64][128];
  *                  ASYM: fp16 [N/128][K/64][4][128]; NULL for TENSOR / ROW
  *   packed_zeros   ASYM: uint8 [N/128][K/64][4][128], one zero point per byte; else NULL
- *   w_sum          optional float32 [N]: sum_k of the dequantized weight row
- *                  (SYM_INT4 only), the correction vector of the unsigned
- *                  shift path (float32 accumulation)
+ *   w_sum          optional float32 [N]. SYM_INT4: sum_k of the dequantized
+ *                  weight row (float32 accumulation), the correction vector of
+ *                  the unsigned-shift path. ASYM_UINT4: sum_k fp16(s (q - z)),
+ *                  summed exactly and rounded once to float32, the correction
+ *                  vector of w4a8_gemm's float outputs (required there).
  * Shape: N % 128 == 0, K % 64 == 0 (K % 256 for ROW_GROUP 64 is not required).
  */
 size_t w4_packed_bytes(int64_t N, int64_t K, cr_qtype qtype, cr_gran gran, int q_group,
@@ -245,13 +247,18 @@ cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
  *
  *   a_codes    int8 [M, K] (SYM_INT8 from convrot_rotate_quantize)
  *   a_scales   float32 ROW [M] (or TENSOR [1])
- *   w_packed, w_scales (fp16), w_zeros (uint8): from w4_pack_weights (ASYM_UINT4)
+ *   w_packed, w_scales (fp16), w_zeros (uint8), w_sum (float32 [N]): from
+ *              w4_pack_weights (ASYM_UINT4); w_sum is required for CR_OUT_BF16 /
+ *              CR_OUT_F32 and ignored (may be NULL) for CR_OUT_I32_RAW
  *   y[m, n] = s_a[m] * sum_g s_w[n, g] * sum_{k in g} qa[m,k] (qw[n,k] - z[n,g]) + bias[n]
- *   CR_OUT_I32_RAW gives sum_k qa (qw - z) exactly.
+ *   CR_OUT_I32_RAW gives sum_k qa (qw - z) exactly (int8 matrix cores).
+ *   CR_OUT_BF16 / CR_OUT_F32 run on fp16 matrix cores with each weight
+ *   s (q - z) rounded once to fp16 (relative 2^-11) and float32 accumulation.
  * Shape: M >= 1, N % 128 == 0, K % 128 == 0, K <= 32768, ldc >= N (ldc % 8 == 0). group must be 16.
  */
 cr_status w4a8_gemm(const void* a_codes, const float* a_scales, cr_gran a_gran,
-                    const void* w_packed, const void* w_scales, const void* w_zeros, int group,
+                    const void* w_packed, const void* w_scales, const void* w_zeros,
+                    const float* w_sum, int group,
                     const void* bias, void* out, cr_out out_type, int64_t ldc,
                     int64_t M, int64_t N, int64_t K,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);

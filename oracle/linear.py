@@ -109,6 +109,36 @@ def weight_sum(values: np.ndarray, scales: np.ndarray, gran: str, group: int | N
     return quant.dequant_sym(values, scales, gran, group).sum(axis=1).astype(np.float32)
 
 
+def _int_to_f32_rne(total: int, exp2: int) -> np.float32:
+    """float32 nearest (ties to even) to the exact value total * 2^exp2."""
+    a = abs(int(total))
+    b = a.bit_length()
+    if b > 24:
+        sh = b - 24
+        q, rem = a >> sh, a & ((1 << sh) - 1)
+        half = 1 << (sh - 1)
+        if rem > half or (rem == half and (q & 1)):
+            q += 1
+        a, exp2 = q, exp2 + sh
+    v = np.float32(np.ldexp(np.float64(a), exp2))     # a < 2^25: exact
+    return np.float32(-v) if total < 0 else v
+
+
+def weight_sum_w4a8(codes: np.ndarray, scales16: np.ndarray, zeros: np.ndarray, group: int = 16) -> np.ndarray:
+    """Column-sum vector of a W4A8 (asymmetric uint4, fp16 scale per 16
+    channels) weight for matrix cores that take the weight in fp16:
+    w_sum[n] = sum_k fp16(s[n, g] (q[n, k] - z[n, g])), exact, then rounded
+    once to float32. It is what 1152 * w_sum removes when the int8 activation
+    codes a enter an fp16 product as 1152 + a (fp16 keeps 1152 + a exact).
+
+    fp16(x) is IEEE half rounding of the exact product (numpy's float64 ->
+    float16 cast); every fp16 value is a multiple of 2^-24, so the sum is
+    exact in integers of that unit."""
+    w16 = quant.dequant_asym(codes, scales16, zeros, group).astype(np.float16)
+    units = (w16.astype(np.float64) * float(1 << 24)).astype(np.int64)
+    return np.array([_int_to_f32_rne(int(t), -24) for t in units.sum(axis=1)], dtype=np.float32)
+
+
 # ---------------------------------------------------------------------------
 # epilogues
 # ---------------------------------------------------------------------------
@@ -174,6 +204,7 @@ def prepare_w4a8(w_bits, rot_group=256, group=16):
     r["tiles"] = pack.tile_pack_w4a8(r["values"])
     r["scales_tiles"] = pack.tile_pack_g16(r["scales"])
     r["zeros_tiles"] = pack.tile_pack_g16(r["zeros"])
+    r["wsum16"] = weight_sum_w4a8(r["values"], r["scales"], r["zeros"], group)
     return r
 
 

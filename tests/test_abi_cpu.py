@@ -113,6 +113,8 @@ def test_pack_validation(cr):
     assert L.w4_pack_weights(_p(A), _p(A), None, 128, 512, 3, 2, 16, _p(A), _p(A), _p(A), None, None) == 1
     assert L.w4_pack_weights(_p(A), _p(A), None, 128, 512, 1, 0, 0, _p(A), None, None, None, None) == 3
     assert L.w4_pack_weights(_p(A), _p(A), None, 128, 512, 0, 0, 0, _p(A), None, None, None, None) == 4
+    # ASYM_UINT4 g16 with its column sums
+    assert L.w4_pack_weights(_p(A), _p(A), _p(A), 128, 512, 3, 2, 16, _p(A), _p(A), _p(A), _p(A), None) == 4
     assert cr.w4_packed_bytes(256, 512, 0, 0, 0, 0) == 256 * 256
     assert cr.w4_packed_bytes(256, 512, 0, 2, 64, 1) == 256 * 8 * 4
     assert cr.w4_packed_bytes(256, 512, 3, 2, 16, 2) == 256 * 32
@@ -139,11 +141,16 @@ def test_gemm_validation(cr):
     assert _w4a4(cr, M=1 << 20, K=32768, ldc=256) == 2        # M*K/2 beyond 32-bit offsets
     assert _w4a4(cr) == 4
     L = cr.lib
-    assert L.w4a8_gemm(_p(A), _p(A), 1, _p(A), _p(A), _p(A), 32, None, _p(A), 0, 256, 64, 256, 512,
+    assert L.w4a8_gemm(_p(A), _p(A), 1, _p(A), _p(A), _p(A), _p(A), 32, None, _p(A), 0, 256, 64, 256, 512,
                        None, 0, None) == 3
-    assert L.w4a8_gemm(_p(A), _p(A), 2, _p(A), _p(A), _p(A), 16, None, _p(A), 0, 256, 64, 256, 512,
+    assert L.w4a8_gemm(_p(A), _p(A), 2, _p(A), _p(A), _p(A), _p(A), 16, None, _p(A), 0, 256, 64, 256, 512,
                        None, 0, None) == 3
-    assert L.w4a8_gemm(_p(A), _p(A), 1, _p(A), _p(A), _p(A), 16, None, _p(A), 0, 256, 64, 256, 512,
+    # the float outputs need the column-sum vector, the exact int32 output does not
+    assert L.w4a8_gemm(_p(A), _p(A), 1, _p(A), _p(A), _p(A), None, 16, None, _p(A), 0, 256, 64, 256, 512,
+                       None, 0, None) == 1
+    assert L.w4a8_gemm(_p(A), _p(A), 1, _p(A), _p(A), _p(A), None, 16, None, _p(A), 2, 256, 64, 256, 512,
+                       None, 0, None) == 4
+    assert L.w4a8_gemm(_p(A), _p(A), 1, _p(A), _p(A), _p(A), _p(A), 16, None, _p(A), 0, 256, 64, 256, 512,
                        None, 0, None) == 4
     assert L.int8_tensorwise_gemm(_p(A), None, _p(A), _p(A), None, _p(A), 0, 256, 64, 256, 512,
                                   None, 0, None) == 1

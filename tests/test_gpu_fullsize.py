@@ -98,16 +98,18 @@ def test_c3_w4a8_full(cr):
     assert np.array_equal(host(a), xa["codes"])
     assert np.array_equal(host(sa).view(np.uint32), np.asarray(xa["scales"], np.float32).view(np.uint32))
     wc, ws, wz, _ = cr.convrot_rotate_quantize(bf16_dev(wb), 256, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16)
-    packed, pscales, pzeros, _ = cr.w4_pack_weights(wc, ws, N, K, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16, zeros=wz)
+    packed, pscales, pzeros, wsum = cr.w4_pack_weights(wc, ws, N, K, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16,
+                                                       zeros=wz, want_wsum=True)
     assert np.array_equal(bytes_of(packed), wp["tiles"].reshape(-1))
     assert np.array_equal(host(pscales).view(np.uint16).reshape(-1), wp["scales_tiles"].view(np.uint16).reshape(-1))
     assert np.array_equal(host(pzeros).reshape(-1), wp["zeros_tiles"].reshape(-1))
+    assert np.array_equal(host(wsum).view(np.uint32), wp["wsum16"].view(np.uint32))
     rows, cols = _rows(M, 16, 31), _cols(N, 1024, 31)
     raw = host(cr.w4a8_gemm(a, sa, cr.GRAN.ROW, packed, pscales, pzeros, M, N, K, out_type=cr.OUT.I32_RAW))
     zexp = np.repeat(wp["zeros"].astype(np.int64), 16, axis=1)
     ref_raw = og.int_gemm(xa["values"][rows], wp["values"].astype(np.int64) - zexp)
     assert np.array_equal(raw[rows].astype(np.int64), ref_raw)
-    y = bf16_to_f32(host(cr.w4a8_gemm(a, sa, cr.GRAN.ROW, packed, pscales, pzeros, M, N, K)))
+    y = bf16_to_f32(host(cr.w4a8_gemm(a, sa, cr.GRAN.ROW, packed, pscales, pzeros, M, N, K, w_sum=wsum)))
     P = og.group_partials(xa["values"][rows], wp["values"][cols], 16, wp["zeros"][cols])
     ref_y = ol.epilogue_g16(P, np.asarray(xa["scales"])[rows], "row", wp["scales"][cols])
     assert rel_l2(y[np.ix_(rows, cols)], ref_y) <= 2e-3

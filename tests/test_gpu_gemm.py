@@ -12,7 +12,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 import workloads as wl  # noqa: E402
-from oracle import linear as ol, gemm as og, pack as opack  # noqa: E402
+from oracle import linear as ol, gemm as og, pack as opack, quant as oq  # noqa: E402
 from tests.gpu_helpers import bf16_dev, dev, host, rel_l2, bf16_to_f32, say  # noqa: E402
 
 GR = {"tensor": 0, "row": 1, "row_group": 2}
@@ -186,13 +186,33 @@ def test_w4a8(cr, case):
     w = dev(wp["tiles"].reshape(-1))
     sw = dev(wp["scales_tiles"].reshape(-1))
     zw = dev(wp["zeros_tiles"].reshape(-1))
+    ws = dev(wp["wsum16"])
     raw = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, out_type=2)
     assert np.array_equal(host(raw).astype(np.int64), ref["raw"])
-    yb = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, out_type=0)
-    yf = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, out_type=1)
+    yb = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, out_type=0, w_sum=ws)
+    yf = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, out_type=1, w_sum=ws)
     _check_out(yb, yf, ref["y"], f32_tol=W4A8_F32_TOL)
-    ybias = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, bias=bf16_dev(bias), out_type=1)
+    ybias = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, bias=bf16_dev(bias), out_type=1, w_sum=ws)
     assert rel_l2(host(ybias), ref_b["y"]) <= W4A8_F32_TOL
+
+
+def test_w4a8_float_outputs_match_fp16_weights(cr):
+    """The float outputs equal, to float32 accumulation rounding, the product
+    with each weight taken as fp16(s (q - z)): a reference built from the
+    oracle's codes with that one rounding, evaluated in float64."""
+    M, N, K = 200, 256, 1024
+    say("w4a8 fp16-weight reference")
+    xb = wl.activation(26, 7, M, K)
+    wb = wl.weight(26, 8, N, K)
+    wp = ol.prepare_w4a8(wb)
+    xa = ol.rotate_quantize(xb, 256, "int8", "row")
+    w16 = oq.dequant_asym(wp["values"], wp["scales"], wp["zeros"], 16).astype(np.float16).astype(np.float64)
+    ref = (np.asarray(xa["values"], np.float64) @ w16.T) * np.asarray(xa["scales"], np.float64)[:, None]
+    y = cr.w4a8_gemm(dev(xa["codes"]), dev(xa["scales"]), 1, dev(wp["tiles"].reshape(-1)),
+                     dev(wp["scales_tiles"].reshape(-1)), dev(wp["zeros_tiles"].reshape(-1)), M, N, K,
+                     out_type=1, w_sum=dev(wp["wsum16"]))
+    # float32 accumulation of (1152 + a) w: partial sums about 40x the result
+    assert rel_l2(host(y), ref) <= 1e-4
 
 
 def test_extreme_codes_no_overflow(cr):

@@ -149,10 +149,12 @@ def test_pack_w4a8(cr, shape):
     wb = wl.weight(16, N + K, N, K)
     ref = ol.prepare_w4a8(wb)
     codes, scales, zeros, _ = cr.convrot_rotate_quantize(bf16_dev(wb), 256, 3, 2, 16)
-    packed, pscales, pzeros, _ = cr.w4_pack_weights(codes, scales, N, K, 3, 2, 16, zeros=zeros)
+    packed, pscales, pzeros, wsum = cr.w4_pack_weights(codes, scales, N, K, 3, 2, 16, zeros=zeros, want_wsum=True)
     assert np.array_equal(bytes_of(packed), ref["tiles"].reshape(-1))
     assert np.array_equal(host(pscales).view(np.uint16).reshape(-1), ref["scales_tiles"].view(np.uint16).reshape(-1))
     assert np.array_equal(host(pzeros).reshape(-1), ref["zeros_tiles"].reshape(-1))
+    # column sums of the fp16 weights: exact sums rounded once, bit-exact
+    assert np.array_equal(host(wsum).view(np.uint32), ref["wsum16"].view(np.uint32))
 
 
 def test_pack_sampled_tiles_full_size(cr):

@@ -121,3 +121,77 @@ def test_lora_down_rounding():
     exact = wl.f32_from_bf16_bits(x).astype(np.float64) @ wl.f32_from_bf16_bits(l2).astype(np.float64).T
     assert np.allclose(la32, exact, rtol=1e-6, atol=1e-6)
     assert np.array_equal(la16, wl.f32_from_bf16_bits(wl.bf16_bits_from_f32(la32)))
+
+
+# ---------------------------------------------------------------------------
+# weight_sum_w4a8: sum_k fp16(s (q - z)), exact, rounded once to float32
+# ---------------------------------------------------------------------------
+
+def _w4a8_rows(groups):
+    """groups: per row, a list of (scale, [16 codes], zero) -> codes, scales16, zeros."""
+    codes = np.array([[c for _, cs, _ in row for c in cs] for row in groups], dtype=np.uint8)
+    scales = np.array([[s for s, _, _ in row] for row in groups], dtype=np.float16)
+    zeros = np.array([[z for _, _, z in row] for row in groups], dtype=np.uint8)
+    return codes, scales, zeros
+
+
+def test_w4a8_wsum_power_of_two_scales_closed_form():
+    # with s a power of two, s (q - z) is exact in fp16 and the sum is s * sum(q - z)
+    rng = np.random.default_rng(5)
+    rows = []
+    for _ in range(3):
+        row = []
+        for _ in range(8):
+            row.append((2.0 ** -7, list(rng.integers(0, 16, 16)), int(rng.integers(0, 16))))
+        rows.append(row)
+    codes, scales, zeros = _w4a8_rows(rows)
+    got = linear.weight_sum_w4a8(codes, scales, zeros)
+    for r, row in enumerate(rows):
+        ints = sum(int(c) - z for _, cs, z in row for c in cs)
+        assert got[r] == np.float32(ints / 128.0)
+
+
+def test_w4a8_wsum_fp16_tie_rounds_to_even():
+    # s = 1 + 2^-10 (exact in fp16), q - z = 3: 3 + 3 * 2^-10 lies halfway
+    # between the fp16 neighbours 3 + 2^-9 (odd) and 3 + 2^-8 (even)
+    s = 1.0 + 2.0 ** -10
+    codes, scales, zeros = _w4a8_rows([[(s, [3] * 16, 0)], [(s, [1] * 16, 0)]])
+    got = linear.weight_sum_w4a8(codes, scales, zeros)
+    assert got[0] == np.float32(16 * (3.0 + 2.0 ** -8))
+    assert got[1] == np.float32(16 * s)                 # q - z = 1: no rounding
+
+
+def test_w4a8_wsum_is_exact_before_the_float32_rounding():
+    # one group of 16 x 61440 then 240 terms of 2^-10: a float32 running sum
+    # loses every small term (ulp 2^-4 at 983040); the exact sum
+    # 983040.234375 rounds to 983040.25
+    big = [(4096.0, [15] * 16, 0)]
+    small = [(2.0 ** -10, [1] * 16, 0)] * 15
+    codes, scales, zeros = _w4a8_rows([big + small])
+    assert linear.weight_sum_w4a8(codes, scales, zeros)[0] == np.float32(983040.25)
+
+
+def test_w4a8_wsum_float32_tie_rounds_to_even():
+    # 18 groups of 16 x 61440 = 17694720 (ulp 2 above 2^24), plus 1 or 3:
+    # 17694721 -> 17694720 (even), 17694723 -> 17694724 (even)
+    big = [(4096.0, [15] * 16, 0)] * 18
+    codes, scales, zeros = _w4a8_rows([big + [(1.0, [1] + [0] * 15, 0)],
+                                       big + [(1.0, [3] + [0] * 15, 0)]])
+    got = linear.weight_sum_w4a8(codes, scales, zeros)
+    assert got[0] == np.float32(17694720.0)
+    assert got[1] == np.float32(17694724.0)
+
+
+def test_w4a8_wsum_brute_force_fractions():
+    from fractions import Fraction
+    rng = np.random.default_rng(9)
+    codes = rng.integers(0, 16, (3, 64)).astype(np.uint8)
+    scales = (rng.random((3, 4)) * 0.02 + 1e-3).astype(np.float16)
+    zeros = rng.integers(0, 16, (3, 4)).astype(np.uint8)
+    got = linear.weight_sum_w4a8(codes, scales, zeros)
+    for r in range(3):
+        tot = Fraction(0)
+        for k in range(64):
+            prod = float(scales[r, k // 16]) * (int(codes[r, k]) - int(zeros[r, k // 16]))
+            tot += Fraction(float(np.float16(prod)))
+        assert got[r] == np.float32(float(tot))

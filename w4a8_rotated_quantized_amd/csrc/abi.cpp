@@ -218,7 +218,7 @@ cr_status w4_pack_weights(const void* codes, const void* scales, const void* zer
     if (gran != CR_GRAN_ROW_GROUP || q_group != 16) return CR_ERR_UNSUPPORTED_FORMAT;
     if (!zeros || !packed_scales || !packed_zeros) return CR_ERR_INVALID_ARGUMENT;
     if (!aligned16(zeros) || !aligned16(packed_scales) || !aligned16(packed_zeros)) return CR_ERR_INVALID_ARGUMENT;
-    if (w_sum) return CR_ERR_UNSUPPORTED_FORMAT;
+    if (w_sum && !aligned16(w_sum)) return CR_ERR_INVALID_ARGUMENT;
   } else {
     return CR_ERR_UNSUPPORTED_FORMAT;
   }
@@ -310,8 +310,8 @@ cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
 }
 
 cr_status w4a8_gemm(const void* a_codes, const float* a_scales, cr_gran a_gran, const void* w_packed,
-                    const void* w_scales, const void* w_zeros, int group, const void* bias, void* out,
-                    cr_out out_type, int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace,
+                    const void* w_scales, const void* w_zeros, const float* w_sum, int group, const void* bias,
+                    void* out, cr_out out_type, int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
   (void)workspace;
   (void)workspace_bytes;
@@ -319,6 +319,7 @@ cr_status w4a8_gemm(const void* a_codes, const float* a_scales, cr_gran a_gran, 
   if (st != CR_OK) return st;
   if (!a_scales || !w_scales || !w_zeros) return CR_ERR_INVALID_ARGUMENT;
   if (!aligned16(a_scales) || !aligned16(w_scales) || !aligned16(w_zeros)) return CR_ERR_INVALID_ARGUMENT;
+  if (out_type != CR_OUT_I32_RAW && (!w_sum || !aligned16(w_sum))) return CR_ERR_INVALID_ARGUMENT;
   if (group != 16) return CR_ERR_UNSUPPORTED_FORMAT;
   if (!(a_gran == CR_GRAN_ROW || a_gran == CR_GRAN_TENSOR)) return CR_ERR_UNSUPPORTED_FORMAT;
   st = device_check();
@@ -331,6 +332,7 @@ cr_status w4a8_gemm(const void* a_codes, const float* a_scales, cr_gran a_gran, 
   p.w = static_cast<const uint8_t*>(w_packed);
   p.w_scales16 = static_cast<const uint16_t*>(w_scales);
   p.w_zeros = static_cast<const uint8_t*>(w_zeros);
+  p.w_sum = w_sum;
   p.bias = static_cast<const uint16_t*>(bias);
   p.out = out;
   p.out_type = out_type;
