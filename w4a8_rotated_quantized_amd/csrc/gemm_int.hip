@@ -427,51 +427,52 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// INT8 main kernel: operands straight from global memory into LDS. For
-// v_mfma_i32_16x16x64_i8 a lane's operand is 16 consecutive k-bytes of one
-// row, which in the natural row-major int8 layout are contiguous, so each
-// lane of a global_load_lds_dwordx4 fetches exactly its fragment bytes
-// (row 16 b + l % 16, k-bytes 64 kt + 16 (l / 16)) and one wave instruction
-// fills one 1 KB operand fragment. Two-stage LDS ring of two 64-deep
-// k-tiles, one bare s_barrier per stage after explicit vmcnt/lgkmcnt waits
-// (the fence of __syncthreads() would also wait for the next stage's loads).
-// No widening: int8 codes feed the matrix cores directly.
-// Block 128 x 128, 2 x 2 waves of 64 x 64, two blocks per CU (64 KB of LDS
-// each).
+// INT8 main kernel (M > 64): v_mfma_i32_32x32x32_i8, whose operand is 16
+// consecutive k-bytes of one row per lane (lanes 0-31 k 0..15, lanes 32-63
+// k 16..31 of the 32-deep step), so both operands keep their natural
+// row-major int8 layout all the way into the matrix cores.
+// Block 256 tokens x 128 channels, 4 waves of 128 x 64 (4 x 2 blocks of
+// 32 x 32, int32 accumulators in VGPRs), two blocks per CU. Each 64-deep
+// k-tile is one stage of a 3-stage LDS ring filled by 16-byte
+// global_load_lds pieces: 256 activation rows and 128 weight rows of 64
+// bytes, the four 16-byte slots of a row XOR-swizzled by the row index so
+// that the 32 rows of a fragment read land on distinct banks. Each wave
+// issues six loads per stage and waits (vmcnt) only for the stage it is
+// about to use, then one bare s_barrier per stage.
+// Operand roles: A = weights (32 channels), B = activations (32 tokens), so a
+// lane ends with one token and 4 consecutive channels per 8 accumulators:
+// one activation scale and one 8-byte bf16 (16-byte int32 / float) store.
 // ---------------------------------------------------------------------------
 typedef const void __attribute__((address_space(1)))* gas_ptr_i8;
 typedef void __attribute__((address_space(3)))* las_ptr_i8;
 
 template <int N>
-CR_DEV void wait_vmcnt_lgkm0_i8() {   // s_waitcnt vmcnt(N) lgkmcnt(0)
+CR_DEV void wait_vmcnt_i8() {   // s_waitcnt vmcnt(N), other counters untouched
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+
+// 16-byte slot of k-chunk c (0..3) in row r of a 64-byte stage row
+CR_DEV int i8_slot(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
 
 template <int OUT>
 __global__ __launch_bounds__(256, 2) void gemm_int8_lds_kernel(GemmParams p) {
-  constexpr int BM = 128, BN = 128, BKT = 2, S = 2;
-  constexpr int WN = 2, NW = 4;
-  constexpr int FM = BM / 2 / 16, FN = BN / WN / 16;
-  constexpr int A_ST = BM * 64 * BKT, W_ST = BN * 64 * BKT, STAGE = A_ST + W_ST;
-  constexpr int NA = A_ST / 1024, NWL = W_ST / 1024;
-  static_assert(NA % NW == 0 && NWL % NW == 0, "wave-loads split evenly over the waves");
-  constexpr int LA = NA / NW, LW = NWL / NW;
+  constexpr int BM = 256, BN = 128, NS = 3;
+  constexpr int A_ST = BM * 64, W_ST = BN * 64, STAGE = A_ST + W_ST;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem_i8[];
   uint8_t* smem = smem_i8;
 
   const int tid = threadIdx.x;
   const int l = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN;
-  const int wn = wave % WN;
+  const int wm = wave >> 1, wn = wave & 1;
 
   const int ntm = (int)((p.M + BM - 1) / BM);
   const int ntn = (int)(p.N / BN);
   const int ntiles = ntm * ntn;
   int t = (int)blockIdx.x;
-  if (ntiles % 8 == 0) t = (t & 7) * (ntiles / 8) + (t >> 3);
-  constexpr int GM = 8;
+  if ((ntiles & 7) == 0) t = (t & 7) * (ntiles >> 3) + (t >> 3);
+  constexpr int GM = 4;
   const int band = t / (GM * ntn);
   const int rows_in_band = min(GM, ntm - band * GM);
   const int within = t - band * GM * ntn;
@@ -480,110 +481,135 @@ __global__ __launch_bounds__(256, 2) void gemm_int8_lds_kernel(GemmParams p) {
   const int64_t m0 = (int64_t)tm * BM;
   const int64_t n0 = (int64_t)tn * BN;
   const int64_t K = p.K;
-  const int nkb = (int)(K / (64 * BKT));
+  const int nst = (int)(K / 64);
 
-  // wave-load wl of the A (W) part is fragment (row block wl / BKT, k-tile wl % BKT)
-  int64_t offa[LA], offw[LW];
+  // wave-load j: rows 16 (wave + 4 j) + l / 4 of the stage, slot l % 4
+  int64_t offa[4], offw[2];
 #pragma unroll
-  for (int j = 0; j < LA; ++j) {
-    const int wl = wave + NW * j;
-    const int64_t m = imin64(m0 + (wl / BKT) * 16 + (l & 15), p.M - 1);   // rows past M: never stored
-    offa[j] = m * K + (wl % BKT) * 64 + (l >> 4) * 16;
+  for (int j = 0; j < 4; ++j) {
+    const int r = 16 * (wave + 4 * j) + (l >> 2);
+    offa[j] = imin64(m0 + r, p.M - 1) * K + 16 * i8_slot(r, l & 3);   // rows past M: never stored
   }
 #pragma unroll
-  for (int j = 0; j < LW; ++j) {
-    const int wl = wave + NW * j;
-    offw[j] = (n0 + (wl / BKT) * 16 + (l & 15)) * K + (wl % BKT) * 64 + (l >> 4) * 16;
+  for (int j = 0; j < 2; ++j) {
+    const int r = 16 * (wave + 4 * j) + (l >> 2);
+    offw[j] = (n0 + r) * K + 16 * i8_slot(r, l & 3);
   }
-  auto issue = [&](int kb) {
-    uint8_t* st = smem + (kb % S) * STAGE;
-    const int64_t k0 = (int64_t)kb * (BKT * 64);
+  auto issue = [&](int s) {
+    uint8_t* st = smem + (s % NS) * STAGE;
+    const int64_t k0 = (int64_t)s * 64;
 #pragma unroll
-    for (int j = 0; j < LA; ++j)
-      __builtin_amdgcn_global_load_lds((gas_ptr_i8)(p.a + offa[j] + k0), (las_ptr_i8)(st + (wave + NW * j) * 1024),
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds((gas_ptr_i8)(p.a + offa[j] + k0), (las_ptr_i8)(st + (wave + 4 * j) * 1024),
                                        16, 0, 0);
 #pragma unroll
-    for (int j = 0; j < LW; ++j)
+    for (int j = 0; j < 2; ++j)
       __builtin_amdgcn_global_load_lds((gas_ptr_i8)(p.w + offw[j] + k0),
-                                       (las_ptr_i8)(st + A_ST + (wave + NW * j) * 1024), 16, 0, 0);
+                                       (las_ptr_i8)(st + A_ST + (wave + 4 * j) * 1024), 16, 0, 0);
   };
 
-  v4i acc[FM][FN];
+  v16i acc[4][2];
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+  // fragment rows: activations wm*128 + 32 i + l % 32, weights wn*64 + 32 j + l % 32
+  const int lr = l & 31, h = l >> 5;
+  const int fl = ((lr >> 1) ^ (lr >> 3)) & 3;
+  int abase[2], wbase[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int c = 2 * ks + h;                       // 16-byte k-chunk of this lane in step ks
+    abase[ks] = (wm * 128 + lr) * 64 + 16 * (c ^ fl);
+    wbase[ks] = A_ST + (wn * 64 + lr) * 64 + 16 * (c ^ fl);
+  }
 
   issue(0);
-  for (int kb = 0; kb < nkb; ++kb) {
-    static_assert(S == 2, "the wait below assumes one stage in flight behind the current one");
-    wait_vmcnt_lgkm0_i8<0>();
+  if (nst > 1) issue(1);
+  for (int s = 0; s < nst; ++s) {
+    if (s + 1 < nst) wait_vmcnt_i8<6>();
+    else wait_vmcnt_i8<0>();
     __builtin_amdgcn_s_barrier();
-    if (kb + 1 < nkb) issue(kb + 1);
-    const uint8_t* As = smem + (kb % S) * STAGE;
-    const uint8_t* Ws = As + A_ST;
-    v4i ra[2][FM], rw[2][FN];
+    if (s + 2 < nst) issue(s + 2);
+    const uint8_t* st = smem + (s % NS) * STAGE;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) ra[0][i] = *reinterpret_cast<const v4i*>(As + ((wm * FM + i) * BKT) * 1024 + l * 16);
+    for (int ks = 0; ks < 2; ++ks) {
+      v4i fa[4], fw[2];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) rw[0][j] = *reinterpret_cast<const v4i*>(Ws + ((wn * FN + j) * BKT) * 1024 + l * 16);
+      for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const v4i*>(st + abase[ks] + i * 2048);
 #pragma unroll
-    for (int kt = 0; kt < BKT; ++kt) {
-      const int cb = kt & 1;
-      if (kt + 1 < BKT) {
+      for (int j = 0; j < 2; ++j) fw[j] = *reinterpret_cast<const v4i*>(st + wbase[ks] + j * 2048);
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-          ra[cb ^ 1][i] = *reinterpret_cast<const v4i*>(As + ((wm * FM + i) * BKT + kt + 1) * 1024 + l * 16);
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          rw[cb ^ 1][j] = *reinterpret_cast<const v4i*>(Ws + ((wn * FN + j) * BKT + kt + 1) * 1024 + l * 16);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(rw[cb][j], ra[cb][i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[j], fa[i], acc[i][j], 0, 0, 0);
     }
   }
 
-  const float sa_t = (p.a_gran == CR_GRAN_TENSOR) ? p.a_scales[0] : 0.f;
-  const float sw_t = (p.w_gran == CR_GRAN_TENSOR) ? p.w_scales[0] : 0.f;
+  // lane owns token m = l % 32 of each 32 x 32 block and channels 8 (r / 4) + 4 h + r % 4.
+  // Every epilogue input is loaded before the first store (a load between
+  // stores would make each later store wait for the earlier ones).
+  float sa[4];
+  v4f sw[2][4];
+  u32x2 bw[2][4];
+  if constexpr (OUT != CR_OUT_I32_RAW) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int64_t mb = m0 + (wm * FM + i) * 16;
-    const int64_t m = mb + (l & 15);
-    const int64_t mc = m < p.M ? m : p.M - 1;
-    float sa = 0.f;
-    if constexpr (OUT != CR_OUT_I32_RAW) sa = (p.a_gran == CR_GRAN_TENSOR) ? sa_t : p.a_scales[mc];
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = imin64(m0 + wm * 128 + i * 32 + lr, p.M - 1);
+      sa[i] = p.a_scales[p.a_gran == CR_GRAN_TENSOR ? 0 : m];
+    }
+    const bool wrow = p.w_gran != CR_GRAN_TENSOR;
+    const float sw_t = p.w_scales[0];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t n = n0 + (wn * FN + j) * 16 + (l >> 4) * 4;
-      float y[4];
-      int raw[4];
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) raw[e] = acc[i][j][e];
-      if constexpr (OUT != CR_OUT_I32_RAW) {
-        v4f sw;
-        if (p.w_gran == CR_GRAN_TENSOR) sw = v4f{sw_t, sw_t, sw_t, sw_t};
-        else sw = *reinterpret_cast<const v4f*>(p.w_scales + n);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = (float)raw[e] * (sa * sw[e]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = 0.f;
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = n0 + (wn * 2 + j) * 32 + 8 * q + 4 * h;
+        sw[j][q] = wrow ? *reinterpret_cast<const v4f*>(p.w_scales + n) : v4f{sw_t, sw_t, sw_t, sw_t};
+        bw[j][q] = p.bias ? *reinterpret_cast<const u32x2*>(p.bias + n) : u32x2{0u, 0u};
       }
-      finish_block<OUT>(p, m, n, mb, l, y, raw);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t n = n0 + (wn * 2 + j) * 32 + 8 * q + 4 * h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + wm * 128 + i * 32 + lr;
+        if (m >= p.M) continue;
+        if constexpr (OUT == CR_OUT_I32_RAW) {
+          *reinterpret_cast<v4i*>(reinterpret_cast<int32_t*>(p.out) + m * p.ldc + n) =
+              v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        } else {
+          const float b[4] = {bf16_lo(bw[j][q][0]), bf16_hi(bw[j][q][0]), bf16_lo(bw[j][q][1]), bf16_hi(bw[j][q][1])};
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = (float)acc[i][j][4 * q + e] * (sa[i] * sw[j][q][e]) + b[e];
+          if constexpr (OUT == CR_OUT_F32) {
+            *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.out) + m * p.ldc + n) = v4f{y[0], y[1], y[2], y[3]};
+          } else {
+            u32x2 o;
+            o[0] = f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
+            o[1] = f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16);
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + m * p.ldc + n) = o;
+          }
+        }
+      }
     }
   }
 }
 
 template <int OUT>
 static hipError_t launch_int8_lds(const GemmParams& p, hipStream_t s) {
-  constexpr int lds = 2 * (128 * 64 * 2 + 128 * 64 * 2);
+  constexpr int lds = 3 * (256 * 64 + 128 * 64);
   static const hipError_t attr =
       hipFuncSetAttribute((const void*)gemm_int8_lds_kernel<OUT>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  const int64_t tiles = ((p.M + 127) / 128) * (p.N / 128);
+  const int64_t tiles = ((p.M + 255) / 256) * (p.N / 128);
   hipLaunchKernelGGL((gemm_int8_lds_kernel<OUT>), dim3((unsigned)tiles), dim3(256), lds, s, p);
   return hipGetLastError();
 }
