@@ -271,14 +271,16 @@ __global__ __launch_bounds__(WM * WN * 64, MINB) void gemm_w4a4_kernel(GemmParam
 // operands go straight from global memory into LDS (global_load_lds_dwordx4:
 // each wave instruction moves 64 arbitrary 16-byte pieces into 1 KB of
 // contiguous LDS, no staging registers), through a ring of LDS_S stages of
-// two 64-deep k-tiles. One barrier per stage: each wave waits for its own
-// loads of the stage (vmcnt) and its own LDS reads (lgkmcnt), then s_barrier
+// two 64-deep k-tiles (LDS_S - 1 stages in flight). One barrier per stage:
+// each wave waits for its own loads of the stage (vmcnt: the loads of later
+// stages stay in flight) and its own LDS reads (lgkmcnt), then s_barrier
 // makes the stage visible to every wave and frees the slot the next loads
 // go into. The fence that __syncthreads() adds would also wait for the
 // loads of later stages, so the barrier is issued bare.
 // Block 128 x 128, 2 x 2 waves of 64 x 64, three blocks per CU (measured on
 // MI355X at M=4096, N=K=3072: 42.5 us against 49.6 us for the register-
-// staged kernel).
+// staged kernel). Three stages (48 KB per block) measured slower: 46 us at
+// that shape, 270 against 234 us at 8192 x 12288 x 3072.
 // ---------------------------------------------------------------------------
 typedef const void __attribute__((address_space(1)))* gas_ptr;
 typedef void __attribute__((address_space(3)))* las_ptr;
@@ -291,7 +293,22 @@ CR_DEV void wait_vmcnt_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
-constexpr int LDS_BM = 128, LDS_BN = 128, LDS_BKT = 2, LDS_S = 2;
+// Wait until at most AHEAD_MAX stages' loads of this wave (L each) remain in
+// flight, for `ahead` later stages already issued (0 <= ahead <= 2).
+template <int L>
+CR_DEV void wait_stage(int ahead) {
+  if (ahead >= 2) wait_vmcnt_lgkm0<2 * L>();
+  else if (ahead == 1) wait_vmcnt_lgkm0<L>();
+  else wait_vmcnt_lgkm0<0>();
+}
+
+#ifndef CR_W4A4_LDS_S
+#define CR_W4A4_LDS_S 2
+#endif
+#ifndef CR_W4A4_LDS_BKT
+#define CR_W4A4_LDS_BKT 2
+#endif
+constexpr int LDS_BM = 128, LDS_BN = 128, LDS_BKT = CR_W4A4_LDS_BKT, LDS_S = CR_W4A4_LDS_S;
 
 // GRP: 64-group scales (the float epilogue runs per k-tile). A stage then
 // also holds the scales of its two k-tiles: activation scales [2][BM] (4-byte
@@ -410,9 +427,12 @@ __global__ __launch_bounds__(256, GRP ? 2 : 3) void gemm_w4a4_lds_kernel(GemmPar
   for (int s = 0; s < S - 1; ++s)
     if (s < nkb) issue(s);
 
+  static_assert(S >= 2 && S <= 4, "stages in flight behind the current one: 0 to 2");
+  constexpr int LST = LA + LW + (GRP ? LSA : 0);        // loads per stage of a wave (+1 for wave 0 with GRP)
   for (int kb = 0; kb < nkb; ++kb) {
-    static_assert(S == 2, "the wait below assumes one stage in flight behind the current one");
-    wait_vmcnt_lgkm0<0>();
+    const int ahead = min(S - 2, nkb - 1 - kb);         // later stages already issued
+    if (GRP && wave == 0) wait_stage<LST + 1>(ahead);
+    else wait_stage<LST>(ahead);
     __builtin_amdgcn_s_barrier();
     if (kb + S - 1 < nkb) issue(kb + S - 1);
     const uint8_t* As = smem + (kb % S) * STAGE;
