@@ -126,10 +126,15 @@ void convrot_reset_counters(void);
  * LoRA-down staged in bf16); Environment Variables (FP32 LoRA activations).
  *
  *   x            bf16 [rows, K], leading dimension ldx >= K
- *   rot_group    256 (rotate each 256-column group) or 0 (no rotation)
+ *   rot_group    256 (rotate each 256-column group with the regular Hadamard
+ *                matrix of order 256), 16, 64 or 1024 (the other ConvRot group
+ *                sizes of the W4A4 recipe: "Qwen-Image-Edit-2511-W4A8-ConvRot"
+ *                card, group-size notes), or 0 (no rotation). The stored scale
+ *                carries the factor 1/sqrt(rot_group).
  *   qtype/gran/q_group, supported combinations:
- *       rot 256: SYM_INT4 or SYM_INT8 with TENSOR, ROW or ROW_GROUP(q_group 64);
- *                ASYM_UINT4 with ROW_GROUP(q_group 16)
+ *       rot 16/64/256/1024: SYM_INT4 or SYM_INT8 with TENSOR, ROW or
+ *                ROW_GROUP(q_group 64);
+ *       rot 256: also ASYM_UINT4 with ROW_GROUP(q_group 16)
  *       rot 0:   SYM_INT4 with ROW_GROUP(64); UNSIGNED_INT4_SHIFT with ROW_GROUP(64)
  *       anything else returns CR_ERR_UNSUPPORTED_FORMAT.
  *   shift        UNSIGNED_INT4_SHIFT only: codes quantize v + shift (e.g. 0.171875)
@@ -150,8 +155,8 @@ void convrot_reset_counters(void);
  *                maximum per block of the first of the two launches that
  *                per-tensor scaling takes. Calls sharing a workspace must not
  *                run concurrently.
- * Shape: rows >= 1, K % 256 == 0 when rotating, K % 64 == 0 otherwise,
- *        K <= 32768.
+ * Shape: rows >= 1, K % 256 == 0 and K % rot_group == 0 when rotating,
+ *        K % 64 == 0 otherwise, K <= 32768.
  * Result is deterministic and bit-identical to the reference definition for
  * finite inputs. Concurrent calls sharing one workspace race.
  */

@@ -84,6 +84,11 @@ def test_rq_validation(cr):
     assert _rq(cr, rows=0) == 2
     assert _rq(cr, K=65536, ldx=65536) == 2                  # above K limit
     assert _rq(cr, rot=128) == 3                             # group size not available
+    assert _rq(cr, rot=32) == 3
+    for rot in (16, 64, 1024):                               # the other ConvRot groups (power-of-four sizes)
+        assert _rq(cr, rot=rot, K=1024, ldx=1024) == 4
+    assert _rq(cr, rot=1024, K=512, ldx=512) == 2            # K % 1024 with the 1024 rotation
+    assert _rq(cr, rot=64, q=3, g=2, qg=16, zeros=A) == 3    # asymmetric g16 weights: 256 only
     assert _rq(cr, q=2) == 3                                 # shift path needs rot 0
     assert _rq(cr, q=3, g=2, qg=16) == 1                     # asym needs zeros
     assert _rq(cr, q=3, g=0) == 3                            # asym needs ROW_GROUP(16)
@@ -103,6 +108,9 @@ def test_rq_workspace_size(cr):
     n = cr.convrot_rq_workspace_size(4096, 3072, 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
     assert n > 0 and n % 4 == 0
     assert cr.convrot_rq_workspace_size(4096, 3072, 256, cr.Q.SYM_INT4, cr.GRAN.ROW) == 0
+    for rot in (16, 64, 1024):
+        assert cr.convrot_rq_workspace_size(4096, 3072, rot, cr.Q.SYM_INT4, cr.GRAN.TENSOR) > 0
+    assert cr.convrot_rq_workspace_size(4096, 2560, 1024, cr.Q.SYM_INT4, cr.GRAN.TENSOR) == 0
 
 
 def test_pack_validation(cr):

@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 
 import workloads as wl  # noqa: E402
 from oracle import linear as ol, gemm as og, pack as opack, quant as oq  # noqa: E402
-from tests.gpu_helpers import bf16_dev, dev, host, rel_l2, bf16_to_f32, say  # noqa: E402
+from tests.gpu_helpers import bf16_dev, bytes_of, dev, host, rel_l2, bf16_to_f32, say  # noqa: E402
 
 GR = {"tensor": 0, "row": 1, "row_group": 2}
 
@@ -84,6 +84,28 @@ def test_w4a4_tensor_row(cr, case):
     _check_out(yb, yf, ref["y"])
     ybias = cr.w4a4_gemm(a, sa, GR[ag], w, sw, GR[wg], M, N, K, bias=bf16_dev(bias), out_type=1)
     assert rel_l2(host(ybias), ref_b["y"]) <= 1e-5
+
+
+@pytest.mark.parametrize("rot", [16, 64, 1024])
+def test_w4a4_layer_other_group_sizes(cr, rot):
+    """A whole W4A4 layer on the GPU path with the ConvRot groups of 16, 64
+    and 1024: both operands rotated and quantized by convrot_rotate_quantize,
+    weights packed by w4_pack_weights; the raw int32 result is bit-exact and
+    the output matches the oracle's layer."""
+    M, N, K = 200, 384, 3072
+    say(f"w4a4 layer rot {rot}")
+    xb = wl.activation(27, rot, M, K, n_outliers=3, outlier_scale=20.0)
+    wb = wl.weight(27, rot + 1, N, K)
+    ref = ol.w4a4_linear(xb, wb, rot, "tensor", "tensor")
+    a, sa, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), rot, 0, 0, layout=1)
+    wc, ws, _, _ = cr.convrot_rotate_quantize(bf16_dev(wb), rot, 0, 0)
+    w = cr.w4_pack_weights(wc, ws, N, K)[0]
+    assert np.array_equal(bytes_of(w), ref["w"]["tiles"].reshape(-1))
+    raw = cr.w4a4_gemm(a, sa, 0, w, ws, 0, M, N, K, out_type=2)
+    assert np.array_equal(host(raw).astype(np.int64), ref["raw"])
+    yf = cr.w4a4_gemm(a, sa, 0, w, ws, 0, M, N, K, out_type=1)
+    yb = cr.w4a4_gemm(a, sa, 0, w, ws, 0, M, N, K, out_type=0)
+    _check_out(yb, yf, ref["y"])
 
 
 def test_w4a4_ldc_padding(cr):

@@ -48,6 +48,31 @@ def test_rotate_quantize_sym(cr, qt, gran, shape):
         assert np.array_equal(host(tscales).reshape(-1), np.asarray(ref["scales"]).reshape(-1))
 
 
+# The other ConvRot group sizes of the W4A4 recipe: 16 and 64 lie inside one
+# 256-element chunk of a lane segment, 1024 spans four chunks of one segment.
+GROUP_SHAPES = [(64, 1024), (37, 3072), (300, 2048), (129, 12288)]
+
+
+@pytest.mark.parametrize("rot", [16, 64, 1024])
+@pytest.mark.parametrize("qt", ["int4", "int8"])
+@pytest.mark.parametrize("gran", ["tensor", "row", "row_group"])
+@pytest.mark.parametrize("shape", GROUP_SHAPES)
+def test_rotate_quantize_group_sizes(cr, rot, qt, gran, shape):
+    rows, K = shape
+    say(f"rq rot {rot} {qt} {gran} {shape}")
+    xb = wl.activation(15, rows * 3 + K + rot, rows, K, n_outliers=max(1, K // 200), outlier_scale=25.0)
+    qg = 64 if gran == "row_group" else 0
+    ref = ol.rotate_quantize(xb, rot, qt, gran, qg or None)
+    codes, scales, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), rot, QT[qt], GR[gran], qg)
+    assert np.array_equal(host(codes).reshape(ref["codes"].shape).view(np.uint8),
+                          ref["codes"].view(np.uint8)), "codes differ"
+    assert np.array_equal(host(scales).reshape(-1).view(np.uint32),
+                          np.asarray(ref["scales"], np.float32).reshape(-1).view(np.uint32)), "scales differ"
+    if qt == "int4":
+        tcodes, _, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), rot, 0, GR[gran], qg, layout=1)
+        assert np.array_equal(opack.tile_unpack_a(host(tcodes), rows), ref["codes"]), "tiled codes differ"
+
+
 def test_rotate_quantize_strided_rows_and_zero_rows(cr):
     rows, K, ldx = 40, 1024, 1024 + 64
     xb = wl.activation(12, 0, rows, ldx)

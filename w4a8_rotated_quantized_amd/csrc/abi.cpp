@@ -112,13 +112,15 @@ static cr_status rq_validate(const void* x, int64_t rows, int64_t K, int64_t ldx
   if ((int)qtype < 0 || (int)qtype > 3 || (int)gran < 0 || (int)gran > 2) return CR_ERR_INVALID_ARGUMENT;
   if (rows < 1 || K < 1 || ldx < K || rows >= DIM_MAX || ldx >= DIM_MAX) return CR_ERR_UNSUPPORTED_SHAPE;
   if (ldx % 8 != 0 || K > KMAX) return CR_ERR_UNSUPPORTED_SHAPE;
-  if (rot_group != 0 && rot_group != 256) return CR_ERR_UNSUPPORTED_FORMAT;
-  if (rot_group == 256) {
-    if (K % 256 != 0) return CR_ERR_UNSUPPORTED_SHAPE;
+  if (rot_group != 0 && rot_group != 16 && rot_group != 64 && rot_group != 256 && rot_group != 1024)
+    return CR_ERR_UNSUPPORTED_FORMAT;
+  if (rot_group != 0) {
+    if (K % 256 != 0 || K % rot_group != 0) return CR_ERR_UNSUPPORTED_SHAPE;
     if (lora_down) return CR_ERR_UNSUPPORTED_FORMAT;
     if (qtype == CR_Q_SYM_INT4 || qtype == CR_Q_SYM_INT8) {
       if (gran == CR_GRAN_ROW_GROUP && q_group != 64) return CR_ERR_UNSUPPORTED_FORMAT;
     } else if (qtype == CR_Q_ASYM_UINT4) {
+      if (rot_group != 256) return CR_ERR_UNSUPPORTED_FORMAT;   // the W4A8 format is defined with 256
       if (gran != CR_GRAN_ROW_GROUP || q_group != 16) return CR_ERR_UNSUPPORTED_FORMAT;
       if (!zeros || !aligned16(zeros)) return CR_ERR_INVALID_ARGUMENT;
     } else {
@@ -139,9 +141,10 @@ static cr_status rq_validate(const void* x, int64_t rows, int64_t K, int64_t ldx
 size_t convrot_rq_workspace_size(int64_t rows, int64_t K, int rot_group, cr_qtype qtype, cr_gran gran,
                                  int q_group) {
   (void)q_group;
-  if (rot_group != 256 || gran != CR_GRAN_TENSOR || rows < 1 || K < 256 || K % 256) return 0;
+  if (rot_group == 0 || gran != CR_GRAN_TENSOR || rows < 1 || K < 256 || K % 256) return 0;
+  if (!(rot_group == 16 || rot_group == 64 || rot_group == 256 || (rot_group == 1024 && K % 1024 == 0))) return 0;
   if (!(qtype == CR_Q_SYM_INT4 || qtype == CR_Q_SYM_INT8)) return 0;
-  return (size_t)cr::rq_tensor_grid(rows, K) * sizeof(float);   // one maximum per block of the first pass
+  return (size_t)cr::rq_tensor_grid(rows, K, rot_group) * sizeof(float);   // one maximum per block of the first pass
 }
 
 cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx, int rot_group,
@@ -181,7 +184,7 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
   p.zeros = zeros;
   p.ws = static_cast<float*>(workspace);
   p.tiled = layout == CR_LAYOUT_TILED ? 1 : 0;
-  const uint64_t nl = (rot_group == 256 && gran == CR_GRAN_TENSOR && qtype != CR_Q_ASYM_UINT4) ? 2 : 1;
+  const uint64_t nl = (rot_group != 0 && gran == CR_GRAN_TENSOR && qtype != CR_Q_ASYM_UINT4) ? 2 : 1;
   return finish_launch(cr::launch_rotate_quantize(p, stream), E_RQ, nl);
 }
 

@@ -35,9 +35,10 @@ struct RQGeometry {
   int64_t gx, gy, nblk;  // grid (group tiles x row tiles) and its size
 };
 
-// gran_kind: 2 ROW (whole rows per block), 3 ROW_GROUP(64), 4 ASYM(16)
-RQGeometry rq_geometry(int64_t rows, int64_t K, int gran_kind);
-int rq_tensor_grid(int64_t rows, int64_t K);   // blocks of each per-tensor pass (one float of workspace each)
+// gran_kind: 2 ROW (whole rows per block), 3 ROW_GROUP(64), 4 ASYM(16); nr: rotation group size
+RQGeometry rq_geometry(int64_t rows, int64_t K, int gran_kind, int nr);
+// blocks of each per-tensor pass (one float of workspace each) for rotation group nr
+int rq_tensor_grid(int64_t rows, int64_t K, int nr);
 hipError_t launch_rotate_quantize(RQParams p, hipStream_t s);
 
 struct PackParams {

@@ -47,6 +47,17 @@ struct LaneRot {
   float tau;       // final per-lane sign
 };
 
+// Rotation sizes n = 4^d: 16, 64 and 256 live inside one 256-element chunk
+// (a 16-lane segment); 1024 is four consecutive chunks held by the same lanes.
+template <int NR>
+struct RotSize {
+  static_assert(NR == 16 || NR == 64 || NR == 256 || NR == 1024, "rotation group of 16, 64, 256 or 1024");
+  static constexpr int digits = NR == 16 ? 2 : NR == 64 ? 3 : NR == 256 ? 4 : 5;
+  static constexpr int lane_bits = NR == 16 ? 0 : NR == 64 ? 2 : 4;     // element bits b4.. inside the group
+  static constexpr float inv_sqrt = NR == 16 ? 0.25f : NR == 64 ? 0.125f : NR == 256 ? 0.0625f : 0.03125f;
+};
+
+template <int NR>
 CR_DEV LaneRot lane_rot(int L) {
   LaneRot r;
   const int b4 = (L ^ (L >> 2)) & 1;
@@ -67,7 +78,9 @@ CR_DEV LaneRot lane_rot(int L) {
     float sign = bits[s] ? -1.f : 1.f;
     r.c[s] = sign * fdig(d) * fdig(dp);
   }
-  r.tau = (__popc(r.gL) & 1) ? -1.f : 1.f;
+  // overall sign (-1)^d times the flips of the lane stages inside the group
+  constexpr int lane_mask = (1 << RotSize<NR>::lane_bits) - 1;
+  r.tau = ((RotSize<NR>::digits + __popc(r.gL & lane_mask)) & 1) ? -1.f : 1.f;
   return r;
 }
 
@@ -104,7 +117,11 @@ CR_BFLY_LANE(bfly_lane_x2, "quad_perm:[2,3,0,1]")
 CR_BFLY_LANE(bfly_lane_x7, "row_half_mirror")
 CR_BFLY_LANE(bfly_lane_x8, "row_ror:8")
 
-// bf16 words (2 x 16 bytes = elements 0..15 of this lane) -> rotated values
+// bf16 words (2 x 16 bytes = elements 0..15 of this lane) -> the butterfly
+// stages of an NR-point group that lie inside one 256-element chunk
+// (all of them for NR <= 256). NEG negates the chunk first (NR = 1024: the
+// digit (b9 b8) of D for chunk 0 of each group).
+template <int NR, bool NEG = false>
 CR_DEV void rotate_group(const u32x4 (&w)[2], const LaneRot& lr, float (&v)[16]) {
 #pragma unroll
   for (int h = 0; h < 2; ++h)
@@ -112,18 +129,48 @@ CR_DEV void rotate_group(const u32x4 (&w)[2], const LaneRot& lr, float (&v)[16])
     for (int j = 0; j < 4; ++j) {
       const int e = 8 * h + 2 * j;
       float lo = bf16_lo(w[h][j]), hi = bf16_hi(w[h][j]);
-      v[e] = dreg_neg(e) ? -lo : lo;
-      v[e + 1] = dreg_neg(e + 1) ? -hi : hi;
+      v[e] = (dreg_neg(e) != NEG) ? -lo : lo;
+      v[e + 1] = (dreg_neg(e + 1) != NEG) ? -hi : hi;
     }
   bfly_reg<1>(v);                      // h = 1   (b0)
   bfly_reg<2>(v);                      // h = 2   (b1)
   bfly_reg<4>(v);                      // h = 4   (b2)
   bfly_reg<8>(v);                      // h = 8   (b3)
-  bfly_lane_x1(v, lr.c[0]);            // h = 16  (b4): partner lane ^ 1
-  bfly_lane_x2(v, lr.c[1]);            // h = 32  (b5): partner lane ^ 2
-  bfly_lane_x7(v, lr.c[2]);            // h = 64  (b6): partner lane ^ 7
-  bfly_lane_x8(v, lr.c[3]);            // h = 128 (b7): partner lane ^ 8
+  if constexpr (NR >= 64) {
+    bfly_lane_x1(v, lr.c[0]);          // h = 16  (b4): partner lane ^ 1
+    bfly_lane_x2(v, lr.c[1]);          // h = 32  (b5): partner lane ^ 2
+  }
+  if constexpr (NR >= 256) {
+    bfly_lane_x7(v, lr.c[2]);          // h = 64  (b6): partner lane ^ 7
+    bfly_lane_x8(v, lr.c[3]);          // h = 128 (b7): partner lane ^ 8
+  }
 }
+
+// NR = 1024: the last two stages (h = 256, 512: bits b8, b9 = the chunk index
+// within the group) between the NC chunks a lane holds, NC a multiple of 4
+// (chunks 4q .. 4q+3 form one group). The chunks share the lane's sign, so
+// plain float32 sums of the stored values are the butterflies.
+template <int NC>
+CR_DEV void bfly_chunks(float (&v)[NC][16]) {
+  static_assert(NC % 4 == 0, "whole 1024-groups");
+#pragma unroll
+  for (int q = 0; q < NC; q += 4)
+#pragma unroll
+    for (int hb = 1; hb <= 2; hb <<= 1)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j & hb) continue;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float a = v[q + j][e], b = v[q + j + hb][e];
+          v[q + j][e] = __fadd_rn(a, b);
+          v[q + j + hb][e] = __fsub_rn(a, b);
+        }
+      }
+}
+
+// sign of chunk c of a 1024-group in D (its digit b9 b8 = c % 4)
+CR_DEV constexpr bool chunk_neg(int c) { return (c & 3) == 0; }
 
 // code bits: fl(fl(v * r) + 1.5*2^23); the low byte is the rounded integer
 CR_DEV uint32_t qbits(float v, float r) {
@@ -186,27 +233,34 @@ CR_DEV uint8_t* code_dst(const RQParams& a, int64_t row, int grp, int gL) {
 // ---------------------------------------------------------------------------
 enum { RG_ROW = 2, RG_G64 = 3, RG_ASYM = 4 };
 
-template <int QT, int GR, int GPS>
+template <int QT, int GR, int GPS, int NR>
 __global__ __launch_bounds__(256) void rq_rot_kernel(RQParams a) {
+  static_assert(GR != RG_ASYM || NR == 256, "asymmetric g16 weights use the 256 rotation");
+  static_assert(NR != 1024 || GPS % 4 == 0, "a 1024-group is four chunks of one segment");
   __shared__ unsigned rowmax[16];
   const int tid = threadIdx.x;
   const int seg = tid >> 4;
   const int L = tid & 15;
-  const LaneRot lr = lane_rot(L);
+  const LaneRot lr = lane_rot<NR>(L);
+  constexpr float post = RotSize<NR>::inv_sqrt;
   const float qmax = (QT == CR_Q_SYM_INT8) ? 127.f : 7.f;
   const int lg = a.lg_spr;
   const int spr = 1 << lg;
   const int rl = seg >> lg;
   const int64_t row = (int64_t)blockIdx.x * a.rpb + rl;
   const bool row_ok = rl < a.rpb && row < a.rows;
-  const int g0 = (int)blockIdx.y * (spr * GPS) + (seg & (spr - 1));
+  // chunk i of the segment: groups interleaved over the segments of a row,
+  // or (NR = 1024) GPS consecutive chunks, whole 1024-groups
+  const int g0 = (NR == 1024) ? (int)blockIdx.y * (spr * GPS) + (seg & (spr - 1)) * GPS
+                              : (int)blockIdx.y * (spr * GPS) + (seg & (spr - 1));
+  const int gstep = (NR == 1024) ? 1 : spr;
   const uint16_t* xr = a.x + (row_ok ? row : 0) * a.ldx + lr.gL * 16;
 
   bool ok[GPS];
   u32x4 w[GPS][2];
 #pragma unroll
   for (int i = 0; i < GPS; ++i) {
-    const int grp = g0 + spr * i;
+    const int grp = g0 + gstep * i;
     ok[i] = row_ok && grp < a.G;
     if (ok[i]) {
       w[i][0] = *reinterpret_cast<const u32x4*>(xr + grp * 256);
@@ -218,7 +272,15 @@ __global__ __launch_bounds__(256) void rq_rot_kernel(RQParams a) {
   }
   float v[GPS][16];
 #pragma unroll
-  for (int i = 0; i < GPS; ++i) rotate_group(w[i], lr, v[i]);
+  for (int i = 0; i < GPS; ++i) {
+    if (NR == 1024 && chunk_neg(i)) rotate_group<NR, true>(w[i], lr, v[i]);
+    else rotate_group<NR>(w[i], lr, v[i]);
+  }
+  if constexpr (NR == 1024) bfly_chunks<GPS>(v);
+  // quantization multiplier sign of chunk i (lane sign, and D's chunk digit for 1024)
+  float csg[GPS];
+#pragma unroll
+  for (int i = 0; i < GPS; ++i) csg[i] = (NR == 1024 && chunk_neg(i)) ? -lr.tau : lr.tau;
 
   const int64_t crow_i = row_ok ? row : 0;
 
@@ -235,13 +297,13 @@ __global__ __launch_bounds__(256) void rq_rot_kernel(RQParams a) {
     __syncthreads();
     const float A = __uint_as_float(rowmax[rl]);
     if (row_ok && (seg & (spr - 1)) == 0 && L == 0) {
-      float sc = (A > 0.f) ? __fmul_rn(div_rn(A, qmax), 0.0625f) : 0.f;
+      float sc = (A > 0.f) ? __fmul_rn(div_rn(A, qmax), post) : 0.f;
       reinterpret_cast<float*>(a.scales)[row] = sc;
     }
     const float r = (A > 0.f) ? div_rn(qmax, A) : 0.f;
 #pragma unroll
     for (int i = 0; i < GPS; ++i)
-      if (ok[i]) quant_store<QT>(v[i], lr.tau * r, code_dst<QT>(a, crow_i, g0 + spr * i, lr.gL));
+      if (ok[i]) quant_store<QT>(v[i], csg[i] * r, code_dst<QT>(a, crow_i, g0 + gstep * i, lr.gL));
   } else if constexpr (GR == RG_G64) {
     // 64-group = bits b0..b5: the quad of lanes sharing (b6, b7) = (L2, L3)
 #pragma unroll
@@ -250,13 +312,13 @@ __global__ __launch_bounds__(256) void rq_rot_kernel(RQParams a) {
 #pragma unroll
       for (int e = 0; e < 16; e += 2) m = amax3(m, fabsf(v[i][e]), fabsf(v[i][e + 1]));
       m = quad_max(m);
-      const int grp = g0 + spr * i;
+      const int grp = g0 + gstep * i;
       if (ok[i] && (L & 3) == 0) {
-        float s = (m > 0.f) ? __fmul_rn(div_rn(m, qmax), 0.0625f) : 0.f;
+        float s = (m > 0.f) ? __fmul_rn(div_rn(m, qmax), post) : 0.f;
         reinterpret_cast<float*>(a.scales)[row * (a.K / 64) + grp * 4 + (L >> 2)] = s;
       }
       const float r = (m > 0.f) ? div_rn(qmax, m) : 0.f;
-      if (ok[i]) quant_store<QT>(v[i], lr.tau * r, code_dst<QT>(a, crow_i, grp, lr.gL));
+      if (ok[i]) quant_store<QT>(v[i], csg[i] * r, code_dst<QT>(a, crow_i, grp, lr.gL));
     }
   } else {  // RG_ASYM: asymmetric uint4 per 16 consecutive rotated channels = one lane
 #pragma unroll
@@ -265,7 +327,7 @@ __global__ __launch_bounds__(256) void rq_rot_kernel(RQParams a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         float s = dreg_neg(e) ? -lr.tau : lr.tau;
-        t[e] = __fmul_rn(__fmul_rn(v[i][e], s), 0.0625f);
+        t[e] = __fmul_rn(__fmul_rn(v[i][e], s), post);
       }
       float mn = t[0], mx = t[0];
 #pragma unroll
@@ -287,7 +349,7 @@ __global__ __launch_bounds__(256) void rq_rot_kernel(RQParams a) {
       }
       const uint32_t zi = (uint32_t)z;
       const uint32_t zp = (uint32_t)dpp_i<DPP_QUAD_1032>((int)zi);   // group gL ^ 1
-      const int grp = g0 + spr * i;
+      const int grp = g0 + gstep * i;
       if (ok[i]) {
         *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(a.codes) + crow_i * (a.K / 2) + grp * 128 + 8 * lr.gL) = o;
         reinterpret_cast<_Float16*>(a.scales)[row * (a.K / 16) + grp * 16 + lr.gL] = s16;
@@ -317,12 +379,13 @@ __global__ __launch_bounds__(256) void rq_rot_kernel(RQParams a) {
 // loads in flight before any arithmetic), leaves the maximum unchanged and
 // rewrites identical code bytes.
 // ---------------------------------------------------------------------------
-template <int QT, int PASS, int J, int NWS>
+template <int QT, int PASS, int J, int NWS, int NR>
 __global__ __launch_bounds__(256) void rq_tensor_kernel(RQParams a) {
+  static_assert(NR != 1024 || J % 4 == 0, "a 1024-group is four chunks of one segment");
   __shared__ float red[4];
   const int tid = threadIdx.x;
   const int seg = tid >> 4;
-  const LaneRot lr = lane_rot(tid & 15);
+  const LaneRot lr = lane_rot<NR>(tid & 15);
   const float qmax = (QT == CR_Q_SYM_INT8) ? 127.f : 7.f;
   const int G = a.G;
   const int GC = (G + J - 1) / J;
@@ -356,12 +419,28 @@ __global__ __launch_bounds__(256) void rq_tensor_kernel(RQParams a) {
   }
   __builtin_amdgcn_sched_barrier(0);   // every load issued before the first use
 
+  // NR = 1024: all J chunks stay in registers for the two cross-chunk stages
+  float vall[NR == 1024 ? J : 1][16];
+  if constexpr (NR == 1024) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      if (chunk_neg(j)) rotate_group<NR, true>(w[j], lr, vall[j]);
+      else rotate_group<NR>(w[j], lr, vall[j]);
+    }
+    bfly_chunks<J>(vall);
+  }
+
   if constexpr (PASS == 0) {
     float m = 0.f;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       float v[16];
-      rotate_group(w[j], lr, v);
+      if constexpr (NR == 1024) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = vall[j][e];
+      } else {
+        rotate_group<NR>(w[j], lr, v);
+      }
 #pragma unroll
       for (int e = 0; e < 16; e += 2) m = amax3(m, fabsf(v[e]), fabsf(v[e + 1]));
     }
@@ -375,15 +454,19 @@ __global__ __launch_bounds__(256) void rq_tensor_kernel(RQParams a) {
     __syncthreads();
     const float A = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     if (blockIdx.x == 0 && tid == 0) {
-      const float sc = (A > 0.f) ? __fmul_rn(div_rn(A, qmax), 0.0625f) : 0.f;
+      const float sc = (A > 0.f) ? __fmul_rn(div_rn(A, qmax), RotSize<NR>::inv_sqrt) : 0.f;
       reinterpret_cast<float*>(a.scales)[0] = sc;
     }
     const float rq = lr.tau * ((A > 0.f) ? div_rn(qmax, A) : 0.f);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      float v[16];
-      rotate_group(w[j], lr, v);
-      quant_store<QT>(v, rq, code_dst<QT>(a, row, grp[j], lr.gL));
+      if constexpr (NR == 1024) {
+        quant_store<QT>(vall[j], chunk_neg(j) ? -rq : rq, code_dst<QT>(a, row, grp[j], lr.gL));
+      } else {
+        float v[16];
+        rotate_group<NR>(w[j], lr, v);
+        quant_store<QT>(v, rq, code_dst<QT>(a, row, grp[j], lr.gL));
+      }
     }
   }
 }
@@ -508,15 +591,19 @@ __global__ __launch_bounds__(256) void rq_plain_kernel(RQParams a) {
 
 // Block geometry: spr segments per row, gps groups per segment, rpb rows per
 // block (16 / spr). ROW granularity needs a whole row per block.
-RQGeometry rq_geometry(int64_t rows, int64_t K, int gran_kind) {
+RQGeometry rq_geometry(int64_t rows, int64_t K, int gran_kind, int nr) {
   RQGeometry g{};
   const int64_t G = K / 256;
+  // chunks per segment: any for the 256 rotation; 1 or 4 for 16 and 64 (fewer
+  // kernel instances); 4 for 1024 (one whole group per segment)
   const int cand_gps[5] = {1, 2, 3, 4, 8};
   double best = -1.0;
   for (int lg = 0; lg <= 4; ++lg) {
     const int spr = 1 << lg;
     for (int c = 0; c < 5; ++c) {
       const int gps = cand_gps[c];
+      if (nr == 1024 && gps != 4) continue;
+      if ((nr == 16 || nr == 64) && gps != 1 && gps != 4) continue;
       const int64_t slots = (int64_t)spr * gps;
       if (gran_kind == 2 && slots < G) continue;           // ROW: the row must fit
       const int64_t gx = (G + slots - 1) / slots;
@@ -537,55 +624,107 @@ RQGeometry rq_geometry(int64_t rows, int64_t K, int gran_kind) {
   return g;
 }
 
-template <int QT, int GR, int GPS>
+template <int QT, int GR, int GPS, int NR>
 static hipError_t launch_rot(const RQParams& p, const RQGeometry& g, hipStream_t s) {
-  hipLaunchKernelGGL((rq_rot_kernel<QT, GR, GPS>), dim3((unsigned)g.gy, (unsigned)g.gx), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((rq_rot_kernel<QT, GR, GPS, NR>), dim3((unsigned)g.gy, (unsigned)g.gx), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
-template <int QT, int GR>
+template <int QT, int GR, int NR>
 static hipError_t launch_rot_gps(const RQParams& p, const RQGeometry& g, hipStream_t s) {
-  switch (g.gps) {
-    case 1: return launch_rot<QT, GR, 1>(p, g, s);
-    case 2: return launch_rot<QT, GR, 2>(p, g, s);
-    case 3: return launch_rot<QT, GR, 3>(p, g, s);
-    case 4: return launch_rot<QT, GR, 4>(p, g, s);
-    default: return launch_rot<QT, GR, 8>(p, g, s);
+  if constexpr (NR == 1024) {
+    return launch_rot<QT, GR, 4, NR>(p, g, s);
+  } else if constexpr (NR != 256) {
+    if (g.gps == 4) return launch_rot<QT, GR, 4, NR>(p, g, s);
+    return launch_rot<QT, GR, 1, NR>(p, g, s);
+  } else {
+    switch (g.gps) {
+      case 1: return launch_rot<QT, GR, 1, NR>(p, g, s);
+      case 2: return launch_rot<QT, GR, 2, NR>(p, g, s);
+      case 3: return launch_rot<QT, GR, 3, NR>(p, g, s);
+      case 8: return launch_rot<QT, GR, 8, NR>(p, g, s);
+      default: return launch_rot<QT, GR, 4, NR>(p, g, s);
+    }
   }
 }
 
-// Per-tensor passes: J groups per segment, J = 4 when that still gives at
-// least 512 blocks, else fewer (small token counts).
-static int rq_tensor_j(int64_t rows, int64_t K) {
+static int rq_tensor_j(int64_t rows, int64_t K, int nr) {
   const int64_t units = ((rows + 15) / 16) * (K / 256);
+  if (nr == 1024) return 4;                       // one whole group per segment
+  if (nr != 256) return units >= 2 * 256 ? 4 : 1;
   if (units >= 4 * 512) return 4;
   if (units >= 2 * 256) return 2;
   return 1;
 }
-int rq_tensor_grid(int64_t rows, int64_t K) {   // blocks of each pass (one workspace float each)
-  const int J = rq_tensor_j(rows, K);
+int rq_tensor_grid(int64_t rows, int64_t K, int nr) {   // blocks of each pass (one workspace float each)
+  const int J = rq_tensor_j(rows, K, nr);
   const int64_t G = K / 256;
   return (int)(((rows + 15) / 16) * ((G + J - 1) / J));
 }
 
-template <int QT, int PASS, int J>
+template <int QT, int PASS, int J, int NR>
 static void launch_tensor_j(const RQParams& p, int gd, hipStream_t s) {
   const int nws = (p.nblk + 255) / 256;
-  if (PASS == 0 || nws <= 1) hipLaunchKernelGGL((rq_tensor_kernel<QT, PASS, J, 1>), dim3(gd), dim3(256), 0, s, p);
-  else if (nws <= 4) hipLaunchKernelGGL((rq_tensor_kernel<QT, PASS, J, 4>), dim3(gd), dim3(256), 0, s, p);
-  else if (nws <= 16) hipLaunchKernelGGL((rq_tensor_kernel<QT, PASS, J, 16>), dim3(gd), dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((rq_tensor_kernel<QT, PASS, J, 0>), dim3(gd), dim3(256), 0, s, p);
+  if (PASS == 0 || nws <= 1) hipLaunchKernelGGL((rq_tensor_kernel<QT, PASS, J, 1, NR>), dim3(gd), dim3(256), 0, s, p);
+  else if (nws <= 4) hipLaunchKernelGGL((rq_tensor_kernel<QT, PASS, J, 4, NR>), dim3(gd), dim3(256), 0, s, p);
+  else if (nws <= 16) hipLaunchKernelGGL((rq_tensor_kernel<QT, PASS, J, 16, NR>), dim3(gd), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((rq_tensor_kernel<QT, PASS, J, 0, NR>), dim3(gd), dim3(256), 0, s, p);
 }
 
-template <int QT, int PASS>
+template <int QT, int PASS, int NR>
 static hipError_t launch_tensor(const RQParams& p, int gd, int J, hipStream_t s) {
-  switch (J) {
-    case 1: launch_tensor_j<QT, PASS, 1>(p, gd, s); break;
-    case 2: launch_tensor_j<QT, PASS, 2>(p, gd, s); break;
-    case 8: launch_tensor_j<QT, PASS, 8>(p, gd, s); break;
-    default: launch_tensor_j<QT, PASS, 4>(p, gd, s); break;
+  if constexpr (NR == 1024) {
+    launch_tensor_j<QT, PASS, 4, NR>(p, gd, s);
+  } else if constexpr (NR != 256) {
+    if (J == 4) launch_tensor_j<QT, PASS, 4, NR>(p, gd, s);
+    else launch_tensor_j<QT, PASS, 1, NR>(p, gd, s);
+  } else {
+    switch (J) {
+      case 1: launch_tensor_j<QT, PASS, 1, NR>(p, gd, s); break;
+      case 2: launch_tensor_j<QT, PASS, 2, NR>(p, gd, s); break;
+      case 8: launch_tensor_j<QT, PASS, 8, NR>(p, gd, s); break;
+      default: launch_tensor_j<QT, PASS, 4, NR>(p, gd, s); break;
+    }
   }
   return hipGetLastError();
+}
+
+// rotated paths for one rotation size: per tensor (two launches), per row,
+// per 64-group; asymmetric g16 weights only with the 256 rotation
+template <int NR>
+static hipError_t launch_rotated(RQParams p, hipStream_t s) {
+  if constexpr (NR == 256) {
+    if (p.qtype == CR_Q_ASYM_UINT4) {
+      RQGeometry g = rq_geometry(p.rows, p.K, RG_ASYM, NR);
+      p.lg_spr = g.lg_spr;
+      p.rpb = g.rpb;
+      return launch_rot_gps<CR_Q_ASYM_UINT4, RG_ASYM, NR>(p, g, s);
+    }
+  }
+  if (p.gran == CR_GRAN_TENSOR) {
+    const int gd = rq_tensor_grid(p.rows, p.K, NR);
+    const int J = rq_tensor_j(p.rows, p.K, NR);
+    p.nblk = gd;
+    hipError_t e;
+    if (p.qtype == CR_Q_SYM_INT4) {
+      e = launch_tensor<CR_Q_SYM_INT4, 0, NR>(p, gd, J, s);
+      if (e != hipSuccess) return e;
+      return launch_tensor<CR_Q_SYM_INT4, 1, NR>(p, gd, J, s);
+    }
+    e = launch_tensor<CR_Q_SYM_INT8, 0, NR>(p, gd, J, s);
+    if (e != hipSuccess) return e;
+    return launch_tensor<CR_Q_SYM_INT8, 1, NR>(p, gd, J, s);
+  }
+  const int kind = (p.gran == CR_GRAN_ROW) ? RG_ROW : RG_G64;
+  RQGeometry g = rq_geometry(p.rows, p.K, kind, NR);
+  p.lg_spr = g.lg_spr;
+  p.rpb = g.rpb;
+  if (kind == RG_ROW) {
+    if (p.qtype == CR_Q_SYM_INT4) return launch_rot_gps<CR_Q_SYM_INT4, RG_ROW, NR>(p, g, s);
+    return launch_rot_gps<CR_Q_SYM_INT8, RG_ROW, NR>(p, g, s);
+  }
+  if (p.qtype == CR_Q_SYM_INT4) return launch_rot_gps<CR_Q_SYM_INT4, RG_G64, NR>(p, g, s);
+  return launch_rot_gps<CR_Q_SYM_INT8, RG_G64, NR>(p, g, s);
 }
 
 hipError_t launch_rotate_quantize(RQParams p, hipStream_t s) {
@@ -602,39 +741,12 @@ hipError_t launch_rotate_quantize(RQParams p, hipStream_t s) {
     return hipGetLastError();
   }
   p.G = (int)(p.K / 256);
-  if (p.qtype == CR_Q_ASYM_UINT4) {
-    RQGeometry g = rq_geometry(p.rows, p.K, RG_ASYM);
-    p.lg_spr = g.lg_spr;
-    p.rpb = g.rpb;
-    return launch_rot_gps<CR_Q_ASYM_UINT4, RG_ASYM>(p, g, s);
+  switch (p.rot_group) {
+    case 16: return launch_rotated<16>(p, s);
+    case 64: return launch_rotated<64>(p, s);
+    case 1024: return launch_rotated<1024>(p, s);
+    default: return launch_rotated<256>(p, s);
   }
-  if (p.gran == CR_GRAN_TENSOR) {
-    const int gd0 = rq_tensor_grid(p.rows, p.K);
-    const int gd1 = gd0;
-    const int J = rq_tensor_j(p.rows, p.K);
-    p.nblk = gd0;
-    hipError_t e;
-    if (p.qtype == CR_Q_SYM_INT4) {
-      e = launch_tensor<CR_Q_SYM_INT4, 0>(p, gd0, J, s);
-      if (e != hipSuccess) return e;
-      return launch_tensor<CR_Q_SYM_INT4, 1>(p, gd1, J, s);
-    }
-    e = launch_tensor<CR_Q_SYM_INT8, 0>(p, gd0, J, s);
-    if (e != hipSuccess) return e;
-    return launch_tensor<CR_Q_SYM_INT8, 1>(p, gd1, J, s);
-  }
-  if (p.gran == CR_GRAN_ROW) {
-    RQGeometry g = rq_geometry(p.rows, p.K, RG_ROW);
-    p.lg_spr = g.lg_spr;
-    p.rpb = g.rpb;
-    if (p.qtype == CR_Q_SYM_INT4) return launch_rot_gps<CR_Q_SYM_INT4, RG_ROW>(p, g, s);
-    return launch_rot_gps<CR_Q_SYM_INT8, RG_ROW>(p, g, s);
-  }
-  RQGeometry g = rq_geometry(p.rows, p.K, RG_G64);
-  p.lg_spr = g.lg_spr;
-  p.rpb = g.rpb;
-  if (p.qtype == CR_Q_SYM_INT4) return launch_rot_gps<CR_Q_SYM_INT4, RG_G64>(p, g, s);
-  return launch_rot_gps<CR_Q_SYM_INT8, RG_G64>(p, g, s);
 }
 
 }  // namespace cr
