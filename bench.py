@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 INT8_PEAK_TOPS = 5000.0       # MI355X dense INT8 matrix peak (5.0 POP/s)
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 M_BIG, M_SMALL, N, K = 4096, 32, 3072, 3072
+ROT = 256          # ConvRot group size (--rot-group: 16, 64, 256 or 1024)
 GEMM_SOURCES = ["gemm_w4a4.hip", "epilogue.h", "common.h", "kernels.h"]
 
 
@@ -47,6 +48,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--rot-group", type=int, default=256, choices=(16, 64, 256, 1024),
+                    help="ConvRot group size of the c2 line (256 is the configuration the metric is quoted on)")
     ap.add_argument("--workload", default="c2",
                     help="c2 (default: the headline line), or c1 / c3 / c4 / c5 for the other workloads' "
                          "throughput lines (bench_workloads.py)")
@@ -82,7 +85,7 @@ def cpu_baseline(budget_s):
     from oracle import linear as ol, gemm as og
     xb_big = wl.activation(2, 0, M_BIG, K, n_outliers=15, outlier_scale=30.0)
     xb_small = wl.activation(2, 2, M_SMALL, K, n_outliers=15, outlier_scale=30.0)
-    wp = ol.prepare_w4a4(wl.weight(2, 1, N, K))
+    wp = ol.prepare_w4a4(wl.weight(2, 1, N, K), ROT)
     try:
         import threadpoolctl
         np.ones((64, 64)) @ np.ones((64, 64))
@@ -93,7 +96,7 @@ def cpu_baseline(budget_s):
     reps, t0 = 0, time.perf_counter()
     while True:
         for xb in (xb_big, xb_small):
-            r = ol.rotate_quantize(xb, 256, "int4", "tensor")
+            r = ol.rotate_quantize(xb, ROT, "int4", "tensor")
             acc = og.int_gemm(r["values"], wp["values"])
             ol.epilogue_scalar(acc, r["scales"], "tensor", wp["scales"], "tensor")
         reps += 1
@@ -121,7 +124,7 @@ def setup(dev, nbytes_target=600e6):
     xb_small = wl.activation(2, 2, M_SMALL, K, n_outliers=15, outlier_scale=30.0)
     wb = wl.weight(2, 1, N, K)
     w = bf16(wb)
-    wc, ws, _, _ = cr.convrot_rotate_quantize(w, 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
+    wc, ws, _, _ = cr.convrot_rotate_quantize(w, ROT, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
     wp, _, _, _ = cr.w4_pack_weights(wc, ws, N, K, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
     per_set = M_BIG * K * 2 + M_BIG * K // 2 + M_BIG * N * 2 + N * K // 2
     nsets = max(2, int(np.ceil(nbytes_target / per_set)))
@@ -134,8 +137,8 @@ def setup(dev, nbytes_target=600e6):
             "cs": torch.empty(((M_SMALL + 15) // 16, K // 64, 512), dtype=torch.uint8, device=dev),
             "sb": torch.empty(1, dtype=torch.float32, device=dev),
             "ss": torch.empty(1, dtype=torch.float32, device=dev),
-            "wsb": torch.empty(cr.convrot_rq_workspace_size(M_BIG, K, 256, 0, 0), dtype=torch.uint8, device=dev),
-            "wss": torch.empty(cr.convrot_rq_workspace_size(M_SMALL, K, 256, 0, 0), dtype=torch.uint8, device=dev),
+            "wsb": torch.empty(cr.convrot_rq_workspace_size(M_BIG, K, ROT, 0, 0), dtype=torch.uint8, device=dev),
+            "wss": torch.empty(cr.convrot_rq_workspace_size(M_SMALL, K, ROT, 0, 0), dtype=torch.uint8, device=dev),
             "yb": torch.empty((M_BIG, N), dtype=torch.bfloat16, device=dev),
             "ys": torch.empty((M_SMALL, N), dtype=torch.bfloat16, device=dev),
         })
@@ -143,7 +146,7 @@ def setup(dev, nbytes_target=600e6):
 
 
 def rq_big(cr, s):
-    cr.convrot_rotate_quantize(s["xb"], 256, 0, 0, layout=cr.LAYOUT.TILED, codes=s["cb"], scales=s["sb"],
+    cr.convrot_rotate_quantize(s["xb"], ROT, 0, 0, layout=cr.LAYOUT.TILED, codes=s["cb"], scales=s["sb"],
                                workspace=s["wsb"])
 
 
@@ -152,7 +155,7 @@ def gemm_big(cr, s):
 
 
 def rq_small(cr, s):
-    cr.convrot_rotate_quantize(s["xs"], 256, 0, 0, layout=cr.LAYOUT.TILED, codes=s["cs"], scales=s["ss"],
+    cr.convrot_rotate_quantize(s["xs"], ROT, 0, 0, layout=cr.LAYOUT.TILED, codes=s["cs"], scales=s["ss"],
                                workspace=s["wss"])
 
 
@@ -161,7 +164,9 @@ def gemm_small(cr, s):
 
 
 def main():
+    global ROT
     args = parse()
+    ROT = args.rot_group
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path has no multi-GPU part); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -250,9 +255,9 @@ def main():
         "vs_baseline": None,
         "dtype": "int4",
         "data": "synthetic",
-        "config": {"workload": "MMDiT projection, W4A4 tensorwise ConvRot group 256, "
+        "config": {"workload": f"MMDiT projection, W4A4 tensorwise ConvRot group {ROT}, "
                                "X bf16 [M, 3072] (M = 4096 and 32), W [3072, 3072]",
-                   "M": [M_BIG, M_SMALL], "N": N, "K": K, "rot_group": 256,
+                   "M": [M_BIG, M_SMALL], "N": N, "K": K, "rot_group": ROT,
                    "buffer_sets": nsets},
         "pct_int8_peak": round(100.0 * eff_tops / INT8_PEAK_TOPS, 2),
         "kernels_us": {"rq_m4096": round(t_rq_big * 1e3, 2), "gemm_m4096": round(t_gemm_big * 1e3, 2),

@@ -17,11 +17,20 @@ HBM_PEAK_GBS = 8000.0
 
 
 def _plan(w):
-    """RQ passes (x_id, kind) and GEMMs for workload w."""
+    """RQ passes (x_id, kind) and GEMMs for workload w. An activation that
+    feeds both per-tensor INT4 and INT8 layers is quantized once, to both
+    (convrot_rotate_quantize_dual)."""
+    def kind_of(lin):
+        return {"w4a4": "int4_tensor", "int8": "int8_tensor", "w4a8": "int8_row",
+                "w4a4_g64": ("u4_g64" if lin.unsigned_shift else "s4_g64")}[lin.fmt]
+    kinds = {}
+    for lin in w.linears:
+        kinds.setdefault(lin.x_id, set()).add(kind_of(lin))
     rq, gemms = [], []
     for lin in w.linears:
-        kind = {"w4a4": "int4_tensor", "int8": "int8_tensor", "w4a8": "int8_row",
-                "w4a4_g64": ("u4_g64" if lin.unsigned_shift else "s4_g64")}[lin.fmt]
+        kind = kind_of(lin)
+        if kind in ("int4_tensor", "int8_tensor") and {"int4_tensor", "int8_tensor"} <= kinds[lin.x_id]:
+            kind = "dual_tensor"
         key = (lin.x_id, kind, lin.name if lin.fmt == "w4a4_g64" else "")
         if key not in rq:
             rq.append(key)
@@ -87,6 +96,12 @@ def run(name, steps, warmup):
             o = dict(codes=torch.empty((M, K), dtype=torch.int8, device=dev),
                      scales=torch.empty(1, dtype=torch.float32, device=dev),
                      ws=torch.empty(cr.convrot_rq_workspace_size(M, K, 256, 1, 0), dtype=torch.uint8, device=dev))
+        elif kind == "dual_tensor":
+            o = dict(codes=torch.empty(((M + 15) // 16, K // 64, 512), dtype=torch.uint8, device=dev),
+                     scales=torch.empty(1, dtype=torch.float32, device=dev),
+                     codes8=torch.empty((M, K), dtype=torch.int8, device=dev),
+                     scales8=torch.empty(1, dtype=torch.float32, device=dev),
+                     ws=torch.empty(cr.convrot_rq_workspace_size(M, K, 256, 0, 0), dtype=torch.uint8, device=dev))
         elif kind == "int8_row":
             o = dict(codes=torch.empty((M, K), dtype=torch.int8, device=dev),
                      scales=torch.empty(M, dtype=torch.float32, device=dev), ws=None)
@@ -106,6 +121,9 @@ def run(name, steps, warmup):
         elif kind == "int8_tensor":
             cr.convrot_rotate_quantize(x, 256, cr.Q.SYM_INT8, cr.GRAN.TENSOR, codes=o["codes"],
                                        scales=o["scales"], workspace=o["ws"])
+        elif kind == "dual_tensor":
+            cr.convrot_rotate_quantize_dual(x, 256, layout4=cr.LAYOUT.TILED, codes4=o["codes"], scale4=o["scales"],
+                                            codes8=o["codes8"], scale8=o["scales8"], workspace=o["ws"])
         elif kind == "int8_row":
             cr.convrot_rotate_quantize(x, 256, cr.Q.SYM_INT8, cr.GRAN.ROW, codes=o["codes"], scales=o["scales"])
         else:
@@ -122,7 +140,8 @@ def run(name, steps, warmup):
         if lin.fmt == "w4a4":
             cr.w4a4_gemm(o["codes"], o["scales"], 0, p["w"], p["ws"], 0, M, N, K, out=y)
         elif lin.fmt == "int8":
-            cr.int8_tensorwise_gemm(o["codes"], o["scales"], p["w"], p["ws"], M, N, K, out=y)
+            a8, s8 = (o["codes8"], o["scales8"]) if "codes8" in o else (o["codes"], o["scales"])
+            cr.int8_tensorwise_gemm(a8, s8, p["w"], p["ws"], M, N, K, out=y)
         elif lin.fmt == "w4a8":
             cr.w4a8_gemm(o["codes"], o["scales"], cr.GRAN.ROW, p["w"], p["ws"], p["wz"], M, N, K, out=y,
                          w_sum=p["wsum"])
@@ -180,7 +199,7 @@ def run(name, steps, warmup):
         x_id, kind, _ = key
         M, K = w.acts[x_id][0], w.acts[x_id][1]
         us = kern[f"rq:{x_id}:{kind}"]
-        out_b = M * K // (1 if kind.startswith("int8") else 2)
+        out_b = M * K // (1 if kind.startswith("int8") else 2) + (M * K if kind == "dual_tensor" else 0)
         rqs[f"{x_id}:{kind}"] = {"us": us, "GBps": round((M * K * 2 + out_b) / us / 1e3, 1)}
     dom = max(layers, key=lambda n: layers[n]["us"])
     eff = ops / (ms * 1e-3) / 1e12

@@ -172,6 +172,34 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
                                   hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * convrot_rotate_quantize_dual - per-tensor INT4 and INT8 codes of the same
+ * rotated activation, from one rotation.
+ *
+ * Cites: "Qwen-Image-Edit-2511 INT4 (ComfyUI Optimized)", Key Technical
+ * Optimizations (quantize an activation once and share it between the
+ * projections that read it); "Qwen-Image-Edit-2511 - INT4 tensorwise W4A4"
+ * page, intro (Q/K projections in INT4, value projection in INT8 tensorwise,
+ * all reading the same attention input).
+ *
+ * Equivalent, bit for bit, to convrot_rotate_quantize(x, ..., rot_group,
+ * SYM_INT4, TENSOR, codes4, layout4, scale4) followed by the same call with
+ * SYM_INT8, TENSOR, codes8 (natural int8 [rows, K]), scale8: both share the
+ * maximum of the rotated tensor, which is computed once (two launches
+ * instead of four).
+ *   codes4   uint8 int4 codes, layout4 CR_LAYOUT_NATURAL [rows, K/2] or
+ *            CR_LAYOUT_TILED; scale4 float32 [1]
+ *   codes8   int8 [rows, K]; scale8 float32 [1]
+ *   workspace  at least convrot_rq_workspace_size(rows, K, rot_group,
+ *            SYM_INT4, TENSOR, 0) bytes
+ *   rot_group  16, 64, 256 or 1024 (0 returns CR_ERR_UNSUPPORTED_FORMAT)
+ * Shape and alignment as convrot_rotate_quantize.
+ */
+cr_status convrot_rotate_quantize_dual(const void* x, int64_t rows, int64_t K, int64_t ldx, int rot_group,
+                                       void* codes4, cr_layout layout4, float* scale4,
+                                       void* codes8, float* scale8,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * w4_pack_weights - natural int4 weight codes -> tile-packed layout.
  *
  * Cites: "Qwen-Image-Edit-2511 INT4 (ComfyUI Optimized)", Tile-Packed Weight

@@ -104,6 +104,23 @@ def test_rq_validation(cr):
     assert _rq(cr, rot=0, g=2, qg=64, ws=None, wsb=0) == 4
 
 
+def test_rq_dual_validation(cr):
+    L = cr.lib
+    def dual(rot=256, x=A, c8=A, s8=A, ws=A, wsb=1 << 20, layout=1, K=1024):
+        return L.convrot_rotate_quantize_dual(_p(x), 64, K, K, rot, _p(A), layout, _p(A), _p(c8), _p(s8), _p(ws),
+                                              wsb, None)
+    assert dual(rot=0) == 3                  # the rotated per-tensor path only
+    assert dual(x=None) == 1
+    assert dual(c8=None) == 1
+    assert dual(s8=A + 4) == 1               # misaligned
+    assert dual(layout=2) == 1
+    assert dual(ws=None) == 1
+    assert dual(wsb=0) == 6
+    assert dual(K=300) == 2
+    for rot in (16, 64, 256, 1024):
+        assert dual(rot=rot) == 4            # valid -> device check (no GPU here)
+
+
 def test_rq_workspace_size(cr):
     n = cr.convrot_rq_workspace_size(4096, 3072, 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
     assert n > 0 and n % 4 == 0

@@ -73,6 +73,25 @@ def test_rotate_quantize_group_sizes(cr, rot, qt, gran, shape):
         assert np.array_equal(opack.tile_unpack_a(host(tcodes), rows), ref["codes"]), "tiled codes differ"
 
 
+@pytest.mark.parametrize("rot", [256, 64, 1024])
+@pytest.mark.parametrize("shape", [(37, 3072), (300, 1024), (129, 12288)])
+def test_rotate_quantize_dual(cr, rot, shape):
+    """One rotation, per-tensor INT4 (tiled) and INT8 codes: both sets and
+    scales equal the oracle's separate quantizations bit for bit."""
+    rows, K = shape
+    say(f"rq dual rot {rot} {shape}")
+    xb = wl.activation(19, rows + K + rot, rows, K, n_outliers=max(1, K // 200), outlier_scale=25.0)
+    r4 = ol.rotate_quantize(xb, rot, "int4", "tensor")
+    r8 = ol.rotate_quantize(xb, rot, "int8", "tensor")
+    c4, s4, c8, s8 = cr.convrot_rotate_quantize_dual(bf16_dev(xb), rot, layout4=1)
+    assert np.array_equal(opack.tile_unpack_a(host(c4), rows), r4["codes"])
+    assert np.array_equal(host(s4).view(np.uint32), np.asarray(r4["scales"], np.float32).reshape(-1).view(np.uint32))
+    assert np.array_equal(host(c8).view(np.uint8), r8["codes"].view(np.uint8))
+    assert np.array_equal(host(s8).view(np.uint32), np.asarray(r8["scales"], np.float32).reshape(-1).view(np.uint32))
+    n4, _, _, _ = cr.convrot_rotate_quantize_dual(bf16_dev(xb), rot, layout4=0)
+    assert np.array_equal(host(n4), r4["codes"])
+
+
 def test_rotate_quantize_strided_rows_and_zero_rows(cr):
     rows, K, ldx = 40, 1024, 1024 + 64
     xb = wl.activation(12, 0, rows, ldx)

@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "ConvRotError", "lib", "Q", "GRAN", "OUT", "LAYOUT",
-    "convrot_rotate_quantize", "w4_pack_weights", "w4a4_gemm", "w4a8_gemm",
+    "convrot_rotate_quantize", "convrot_rotate_quantize_dual", "w4_pack_weights", "w4a4_gemm", "w4a8_gemm",
     "int8_tensorwise_gemm", "convrot_rq_workspace_size", "w4_packed_bytes",
     "get_counters", "reset_counters", "device_check", "status_string",
 ]
@@ -69,6 +69,7 @@ _SIGS = {
     "convrot_rq_workspace_size": (_sz, [_i64, _i64, _i, _i, _i, _i]),
     "convrot_rotate_quantize": (_i, [_vp, _i64, _i64, _i64, _i, _i, _i, _i, _f, _vp, _i, _vp, _i,
                                      _vp, _i, _vp, _vp, _vp, _sz, _vp]),
+    "convrot_rotate_quantize_dual": (_i, [_vp, _i64, _i64, _i64, _i, _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "w4_packed_bytes": (_sz, [_i64, _i64, _i, _i, _i, _i]),
     "w4_pack_weights": (_i, [_vp, _vp, _vp, _i64, _i64, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "w4a4_gemm": (_i, [_vp, _i, _vp, _i, _i, _f, _vp, _vp, _i, _vp, _vp, _i, _vp, _i, _vp,
@@ -181,6 +182,32 @@ def convrot_rotate_quantize(x, rot_group=256, qtype=Q.SYM_INT4, gran=GRAN.TENSOR
                                      _ptr(workspace), wsb, _stream(stream))
     _check(st, "convrot_rotate_quantize")
     return codes, scales, zeros, lora_act
+
+
+def convrot_rotate_quantize_dual(x, rot_group=256, layout4=LAYOUT.NATURAL, codes4=None, scale4=None,
+                                 codes8=None, scale8=None, workspace=None, stream=None):
+    """Per-tensor INT4 and INT8 codes of one rotation of x (bf16 [rows, K]).
+    Returns (codes4, scale4, codes8, scale8)."""
+    rows, K = x.shape
+    dev = x.device
+    if codes4 is None:
+        shape = ((rows + 15) // 16, K // 64, 512) if layout4 == LAYOUT.TILED else (rows, K // 2)
+        codes4 = torch.empty(shape, dtype=torch.uint8, device=dev)
+    if scale4 is None:
+        scale4 = torch.empty(1, dtype=torch.float32, device=dev)
+    if codes8 is None:
+        codes8 = torch.empty((rows, K), dtype=torch.int8, device=dev)
+    if scale8 is None:
+        scale8 = torch.empty(1, dtype=torch.float32, device=dev)
+    if workspace is None:
+        need = convrot_rq_workspace_size(rows, K, rot_group, Q.SYM_INT4, GRAN.TENSOR, 0)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size()
+    st = lib.convrot_rotate_quantize_dual(_ptr(x), rows, K, x.stride(0), rot_group, _ptr(codes4), int(layout4),
+                                          _ptr(scale4), _ptr(codes8), _ptr(scale8), _ptr(workspace), wsb,
+                                          _stream(stream))
+    _check(st, "convrot_rotate_quantize_dual")
+    return codes4, scale4, codes8, scale8
 
 
 def w4_pack_weights(codes, scales, N, K, qtype=Q.SYM_INT4, gran=GRAN.TENSOR, q_group=0, zeros=None,

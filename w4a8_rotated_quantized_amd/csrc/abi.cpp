@@ -188,6 +188,37 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
   return finish_launch(cr::launch_rotate_quantize(p, stream), E_RQ, nl);
 }
 
+cr_status convrot_rotate_quantize_dual(const void* x, int64_t rows, int64_t K, int64_t ldx, int rot_group,
+                                       void* codes4, cr_layout layout4, float* scale4, void* codes8, float* scale8,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (rot_group == 0) return CR_ERR_UNSUPPORTED_FORMAT;       // the per-tensor rotated path only
+  cr_status st = rq_validate(x, rows, K, ldx, rot_group, CR_Q_SYM_INT4, CR_GRAN_TENSOR, 0, nullptr, 0, nullptr,
+                             codes4, scale4, nullptr);
+  if (st != CR_OK) return st;
+  if (!codes8 || !scale8 || !aligned16(codes8) || !aligned16(scale8)) return CR_ERR_INVALID_ARGUMENT;
+  if ((int)layout4 < 0 || (int)layout4 > 1) return CR_ERR_INVALID_ARGUMENT;
+  const size_t need = convrot_rq_workspace_size(rows, K, rot_group, CR_Q_SYM_INT4, CR_GRAN_TENSOR, 0);
+  if (!workspace || !aligned16(workspace)) return CR_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < need) return CR_ERR_WORKSPACE_TOO_SMALL;
+  st = device_check();
+  if (st != CR_OK) return st;
+  cr::RQParams p{};
+  p.x = static_cast<const uint16_t*>(x);
+  p.rows = rows;
+  p.K = K;
+  p.ldx = ldx;
+  p.rot_group = rot_group;
+  p.qtype = CR_Q_SYM_INT4;
+  p.gran = CR_GRAN_TENSOR;
+  p.codes = codes4;
+  p.scales = scale4;
+  p.codes8 = codes8;
+  p.scales8 = scale8;
+  p.ws = static_cast<float*>(workspace);
+  p.tiled = layout4 == CR_LAYOUT_TILED ? 1 : 0;
+  return finish_launch(cr::launch_rotate_quantize_dual(p, stream), E_RQ, 2);
+}
+
 // ---------------------------------------------------------------------------
 // weight packing
 // ---------------------------------------------------------------------------

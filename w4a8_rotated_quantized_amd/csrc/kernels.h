@@ -26,6 +26,8 @@ struct RQParams {
   int rpb;              // rows per block (16 >> lg_spr)
   int lg_spr;           // log2(16-lane segments per row)
   int tiled;            // int4 codes in the [rows/16][K/64][512 B] fragment layout
+  void* codes8;         // dual output: int8 codes [rows, K] (codes / scales hold the int4 set)
+  void* scales8;
 };
 
 struct RQGeometry {
@@ -40,6 +42,8 @@ RQGeometry rq_geometry(int64_t rows, int64_t K, int gran_kind, int nr);
 // blocks of each per-tensor pass (one float of workspace each) for rotation group nr
 int rq_tensor_grid(int64_t rows, int64_t K, int nr);
 hipError_t launch_rotate_quantize(RQParams p, hipStream_t s);
+// per-tensor INT4 and INT8 codes of one rotation (two launches)
+hipError_t launch_rotate_quantize_dual(RQParams p, hipStream_t s);
 
 struct PackParams {
   const uint8_t* codes;

@@ -372,6 +372,8 @@ __global__ __launch_bounds__(256) void rq_rot_kernel(RQParams a) {
 // code stores into 8-byte partial-line writes from several L2s).
 //   PASS 0: max |H x| of the block -> ws[blockIdx.x].
 //   PASS 1: A = max over ws[0 .. gridDim.x), rotation recomputed, codes.
+//   PASS 2: as PASS 1, writing the INT4 codes (codes, scales) and the INT8
+//           codes of the same rotated values (codes8, scales8).
 // All J loads are issued first and each group is rotated as soon as its
 // data is in. Rows past the end are clamped to the last row and groups past
 // the end to the last group, which keeps every load and store free of
@@ -398,7 +400,7 @@ __global__ __launch_bounds__(256) void rq_tensor_kernel(RQParams a) {
   // them leaves the row loads in flight; NWS = 0 is the loop for grids
   // beyond 256 * 16 blocks.
   float t = 0.f;
-  if constexpr (PASS == 1) {
+  if constexpr (PASS >= 1) {
     const int gd = (int)gridDim.x;
     if constexpr (NWS > 0) {
 #pragma unroll
@@ -456,17 +458,27 @@ __global__ __launch_bounds__(256) void rq_tensor_kernel(RQParams a) {
     if (blockIdx.x == 0 && tid == 0) {
       const float sc = (A > 0.f) ? __fmul_rn(div_rn(A, qmax), RotSize<NR>::inv_sqrt) : 0.f;
       reinterpret_cast<float*>(a.scales)[0] = sc;
+      if constexpr (PASS == 2) {
+        const float sc8 = (A > 0.f) ? __fmul_rn(div_rn(A, 127.f), RotSize<NR>::inv_sqrt) : 0.f;
+        reinterpret_cast<float*>(a.scales8)[0] = sc8;
+      }
     }
     const float rq = lr.tau * ((A > 0.f) ? div_rn(qmax, A) : 0.f);
+    const float rq8 = lr.tau * ((A > 0.f) ? div_rn(127.f, A) : 0.f);   // PASS 2 only
+    RQParams a8 = a;
+    a8.codes = a.codes8;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
+      float v[16];
       if constexpr (NR == 1024) {
-        quant_store<QT>(vall[j], chunk_neg(j) ? -rq : rq, code_dst<QT>(a, row, grp[j], lr.gL));
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = vall[j][e];
       } else {
-        float v[16];
         rotate_group<NR>(w[j], lr, v);
-        quant_store<QT>(v, rq, code_dst<QT>(a, row, grp[j], lr.gL));
       }
+      const float sg = (NR == 1024 && chunk_neg(j)) ? -1.f : 1.f;
+      quant_store<QT>(v, sg * rq, code_dst<QT>(a, row, grp[j], lr.gL));
+      if constexpr (PASS == 2) quant_store<CR_Q_SYM_INT8>(v, sg * rq8, code_dst<CR_Q_SYM_INT8>(a8, row, grp[j], lr.gL));
     }
   }
 }
@@ -725,6 +737,26 @@ static hipError_t launch_rotated(RQParams p, hipStream_t s) {
   }
   if (p.qtype == CR_Q_SYM_INT4) return launch_rot_gps<CR_Q_SYM_INT4, RG_G64, NR>(p, g, s);
   return launch_rot_gps<CR_Q_SYM_INT8, RG_G64, NR>(p, g, s);
+}
+
+template <int NR>
+static hipError_t launch_dual(RQParams p, hipStream_t s) {
+  const int gd = rq_tensor_grid(p.rows, p.K, NR);
+  const int J = rq_tensor_j(p.rows, p.K, NR);
+  p.nblk = gd;
+  hipError_t e = launch_tensor<CR_Q_SYM_INT4, 0, NR>(p, gd, J, s);
+  if (e != hipSuccess) return e;
+  return launch_tensor<CR_Q_SYM_INT4, 2, NR>(p, gd, J, s);
+}
+
+hipError_t launch_rotate_quantize_dual(RQParams p, hipStream_t s) {
+  p.G = (int)(p.K / 256);
+  switch (p.rot_group) {
+    case 16: return launch_dual<16>(p, s);
+    case 64: return launch_dual<64>(p, s);
+    case 1024: return launch_dual<1024>(p, s);
+    default: return launch_dual<256>(p, s);
+  }
 }
 
 hipError_t launch_rotate_quantize(RQParams p, hipStream_t s) {
