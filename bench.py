@@ -20,7 +20,7 @@ M=4096 GEMM) against that peak; its duration comes from HIP events around
 each of its launches on the launch stream. The CPU baseline is the numpy
 oracle running the same step on this host.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--workload c2|c1|c3|c4|c5]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--rot-group 256] [--workload c2|c1|c3|c4|c5|c2a8]
 (--workload other than c2 prints that workload's throughput line instead;
 see bench_workloads.py)
 """
@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--rot-group", type=int, default=256, choices=(16, 64, 256, 1024),
                     help="ConvRot group size of the c2 line (256 is the configuration the metric is quoted on)")
     ap.add_argument("--workload", default="c2",
-                    help="c2 (default: the headline line), or c1 / c3 / c4 / c5 for the other workloads' "
+                    help="c2 (default: the headline line), or c1 / c3 / c4 / c5 / c2a8 for the other workloads' "
                          "throughput lines (bench_workloads.py)")
     return ap.parse_args()
 

@@ -21,7 +21,7 @@ def _plan(w):
     feeds both per-tensor INT4 and INT8 layers is quantized once, to both
     (convrot_rotate_quantize_dual)."""
     def kind_of(lin):
-        return {"w4a4": "int4_tensor", "int8": "int8_tensor", "w4a8": "int8_row",
+        return {"w4a4": "int4_tensor", "int8": "int8_tensor", "w4a8": "int8_row", "a8w4": "int8_row",
                 "w4a4_g64": ("u4_g64" if lin.unsigned_shift else "s4_g64")}[lin.fmt]
     kinds = {}
     for lin in w.linears:
@@ -62,7 +62,7 @@ def run(name, steps, warmup):
     prep = {}
     for lin in w.linears:
         N, K = lin.N, lin.K
-        if lin.fmt == "w4a4":
+        if lin.fmt in ("w4a4", "a8w4"):
             wc, ws, _, _ = cr.convrot_rotate_quantize(bf16(wl.weight_bits(w, lin)), 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
             prep[lin.name] = dict(w=cr.w4_pack_weights(wc, ws, N, K)[0], ws=ws)
         elif lin.fmt == "int8":
@@ -139,6 +139,9 @@ def run(name, steps, warmup):
         M, N, K = lin.M, lin.N, lin.K
         if lin.fmt == "w4a4":
             cr.w4a4_gemm(o["codes"], o["scales"], 0, p["w"], p["ws"], 0, M, N, K, out=y)
+        elif lin.fmt == "a8w4":
+            cr.w4a4_gemm(o["codes"], o["scales"], cr.GRAN.ROW, p["w"], p["ws"], 0, M, N, K, out=y,
+                         a_layout=cr.LAYOUT.INT8)
         elif lin.fmt == "int8":
             a8, s8 = (o["codes8"], o["scales8"]) if "codes8" in o else (o["codes"], o["scales"])
             cr.int8_tensorwise_gemm(a8, s8, p["w"], p["ws"], M, N, K, out=y)
@@ -207,7 +210,7 @@ def run(name, steps, warmup):
         "metric": "effective TOPS of fused rotate+quant+W4 GEMM (% INT8 MFMA peak); GB/s",
         "value": round(eff, 2), "unit": "TOPS", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int4" if name != "c3" else "int8/int4", "data": "synthetic",
+        "dtype": "int4" if name not in ("c3", "c2a8") else "int8/int4", "data": "synthetic",
         "config": {"workload": w.name, "layers": len(w.linears), "total_GOP": round(ops / 1e9, 1)},
         "pct_int8_peak": round(100.0 * eff / INT8_PEAK_TOPS, 2),
         "gemm": layers, "rotate_quantize": rqs,

@@ -90,10 +90,12 @@ typedef enum cr_out {
 
 typedef enum cr_layout {
   CR_LAYOUT_NATURAL = 0,  /* int4 codes [rows, K/2], row-major                                 */
-  CR_LAYOUT_TILED = 1     /* int4 codes [ceil(rows/16)][K/64][512 B]: byte l*8 + j of block    */
+  CR_LAYOUT_TILED = 1,    /* int4 codes [ceil(rows/16)][K/64][512 B]: byte l*8 + j of block    */
                           /* (b, kt) is natural byte (row 16b + l%16, 32kt + 8(l/16) + j), the */
                           /* operand-fragment order of the W4A4 GEMM; rows past `rows` in the  */
                           /* last block are left unwritten (allocate ceil(rows/16)*16 rows)    */
+  CR_LAYOUT_INT8 = 2      /* w4a4_gemm only: int8 codes [rows, K] row-major (SYM_INT8), the    */
+                          /* 8-bit-activation branch for W4A4-format weights                   */
 } cr_layout;
 
 /* Status text, e.g. "format not available" for CR_ERR_UNSUPPORTED_FORMAT. */
@@ -244,7 +246,11 @@ cr_status w4_pack_weights(const void* codes, const void* scales, const void* zer
  * (unsigned shifted activations, scale staging).
  *
  *   a_codes     int4 codes (signed, or unsigned when a_unsigned) in a_layout:
- *               CR_LAYOUT_TILED (fast path) or CR_LAYOUT_NATURAL [M, K/2]
+ *               CR_LAYOUT_TILED (fast path) or CR_LAYOUT_NATURAL [M, K/2];
+ *               or CR_LAYOUT_INT8: int8 codes [M, K] (SYM_INT8, TENSOR or ROW
+ *               scales), the 8-bit-activation branch for these weights
+ *               ("Qwen3-4B ConvRot W4A4" page, INT8 branch comparison): no
+ *               a_unsigned, no 64-group scales and no low-rank branch with it
  *   a_scales    float32: TENSOR [1], ROW [M], ROW_GROUP(64) [M, K/64]
  *   a_unsigned  1 for UNSIGNED_INT4_SHIFT codes: y -= a_shift * w_sum[n]
  *   w_packed    from w4_pack_weights (SYM_INT4)

@@ -236,6 +236,18 @@ def int8_linear(x_bits, w_bits, rot_group=256, bias_bits=None):
     return {"y": y, "raw": raw, "x": xa, "w": wq}
 
 
+def a8w4_linear(x_bits, w_bits, rot_group=256, a_gran="row", w_gran="tensor", bias_bits=None, wprep=None):
+    """8-bit activations (symmetric INT8, per token or per tensor) against
+    W4A4-format weights (symmetric INT4, per tensor or per row): the INT8
+    branch the "Qwen3-4B ConvRot W4A4" page compares with the INT4 one,
+    y = s_a[m] s_w[n] sum_k qa qw + b."""
+    xa = rotate_quantize(x_bits, rot_group, "int8", a_gran)
+    wp = wprep if wprep is not None else prepare_w4a4(w_bits, rot_group, w_gran)
+    raw = gemm.int_gemm(xa["values"], wp["values"])
+    y = epilogue_scalar(raw, xa["scales"], a_gran, wp["scales"], w_gran, bias_bits=bias_bits)
+    return {"y": y, "raw": raw, "x": xa, "w": wp}
+
+
 def w4a8_linear(x_bits, w_bits, rot_group=256, group=16, bias_bits=None, wprep=None):
     xa = rotate_quantize(x_bits, rot_group, "int8", "row")
     wp = wprep if wprep is not None else prepare_w4a8(w_bits, rot_group, group)

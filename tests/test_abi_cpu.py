@@ -163,6 +163,10 @@ def test_gemm_validation(cr):
     assert _w4a4(cr, la=A, lu=A, R=16) == 3
     assert _w4a4(cr, ot=5) == 1
     assert _w4a4(cr, layout=3) == 1
+    assert _w4a4(cr, layout=2, uns=1, wsum=A) == 3           # 8-bit activations: signed only
+    assert _w4a4(cr, layout=2, ag=2, wg=2) == 3              # no 64-group scales with them
+    assert _w4a4(cr, layout=2, la=A, lu=A, R=32) == 3        # no low-rank branch with them
+    assert _w4a4(cr, layout=2, ag=1) == 4
     assert _w4a4(cr, M=1 << 20, K=32768, ldc=256) == 2        # M*K/2 beyond 32-bit offsets
     assert _w4a4(cr) == 4
     L = cr.lib

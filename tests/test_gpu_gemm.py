@@ -108,6 +108,36 @@ def test_w4a4_layer_other_group_sizes(cr, rot):
     _check_out(yb, yf, ref["y"])
 
 
+A8W4_CASES = [(1, 256, 512, "row", "tensor"), (50, 384, 3072, "row", "row"), (200, 256, 1024, "tensor", "tensor"),
+              (333, 512, 768, "row", "tensor")]
+
+
+@pytest.mark.parametrize("case", A8W4_CASES)
+def test_a8w4(cr, case):
+    """8-bit per-token activations x W4A4-format weights (w4a4_gemm with
+    CR_LAYOUT_INT8): int32 bit-exact, outputs to the float bars."""
+    M, N, K, ag, wg = case
+    say(f"a8w4 {case}")
+    xb = wl.activation(28, M + K, M, K, n_outliers=3, outlier_scale=20.0)
+    wb = wl.weight(28, N + K, N, K)
+    bias = wl.weight(28, 3, 1, N, std=0.5)[0]
+    wp = ol.prepare_w4a4(wb, 256, wg)
+    ref = ol.a8w4_linear(xb, wb, 256, ag, wg, wprep=wp)
+    ref_b = ol.a8w4_linear(xb, wb, 256, ag, wg, bias_bits=bias, wprep=wp)
+    a, sa, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), 256, cr.Q.SYM_INT8, GR[ag])
+    assert np.array_equal(host(a).view(np.uint8), ref["x"]["codes"].view(np.uint8))
+    w = dev(wp["tiles"].reshape(-1))
+    sw = dev(np.asarray(wp["scales"], np.float32).reshape(-1))
+    kw = dict(a_layout=cr.LAYOUT.INT8)
+    raw = cr.w4a4_gemm(a, sa, GR[ag], w, sw, GR[wg], M, N, K, out_type=2, **kw)
+    assert np.array_equal(host(raw).astype(np.int64), ref["raw"])
+    yf = cr.w4a4_gemm(a, sa, GR[ag], w, sw, GR[wg], M, N, K, out_type=1, **kw)
+    yb = cr.w4a4_gemm(a, sa, GR[ag], w, sw, GR[wg], M, N, K, out_type=0, **kw)
+    _check_out(yb, yf, ref["y"])
+    ybias = cr.w4a4_gemm(a, sa, GR[ag], w, sw, GR[wg], M, N, K, bias=bf16_dev(bias), out_type=1, **kw)
+    assert rel_l2(host(ybias), ref_b["y"]) <= 1e-5
+
+
 def test_w4a4_ldc_padding(cr):
     M, N, K = 70, 256, 512
     xb = wl.activation(22, 0, M, K)

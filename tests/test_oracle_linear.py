@@ -195,3 +195,22 @@ def test_w4a8_wsum_brute_force_fractions():
             prod = float(scales[r, k // 16]) * (int(codes[r, k]) - int(zeros[r, k // 16]))
             tot += Fraction(float(np.float16(prod)))
         assert got[r] == np.float32(float(tot))
+
+
+def test_a8w4_linear_brute_force():
+    # 8-bit activations x W4A4 weights, against a float64 triple loop over the
+    # oracle's own codes and scales (checks the composition: granularities,
+    # which scale goes with which axis, the bias)
+    xb = wl.activation(31, 0, 3, 512)
+    wb = wl.weight(31, 1, 128, 512)                   # tile packing wants N % 128 == 0
+    bias = wl.weight(31, 2, 1, 128, std=0.5)[0]
+    r = linear.a8w4_linear(xb, wb, 256, "row", "row", bias_bits=bias)
+    qa, sa = r["x"]["values"], np.asarray(r["x"]["scales"], np.float64)
+    qw, sw = r["w"]["values"], np.asarray(r["w"]["scales"], np.float64)
+    assert qa.min() >= -127 and qa.max() <= 127 and qw.min() >= -7 and qw.max() <= 7
+    bf = (bias.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for m in range(3):
+        for n in (0, 1, 77, 127):
+            acc = sum(int(qa[m, k]) * int(qw[n, k]) for k in range(512))
+            assert r["raw"][m, n] == acc
+            assert np.isclose(r["y"][m, n], sa[m] * sw[n] * acc + bf[n], rtol=1e-6, atol=0)

@@ -53,6 +53,7 @@ class OUT:
 class LAYOUT:
     NATURAL = 0
     TILED = 1
+    INT8 = 2
 
 
 class _Counters(ctypes.Structure):

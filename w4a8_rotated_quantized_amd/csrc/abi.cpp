@@ -302,11 +302,13 @@ cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
   if (st != CR_OK) return st;
   if (!a_scales || !w_scales || !aligned16(a_scales) || !aligned16(w_scales)) return CR_ERR_INVALID_ARGUMENT;
   if ((int)a_gran < 0 || (int)a_gran > 2 || (int)w_gran < 0 || (int)w_gran > 2) return CR_ERR_INVALID_ARGUMENT;
-  if ((int)a_layout < 0 || (int)a_layout > 1) return CR_ERR_INVALID_ARGUMENT;
-  if (((M + 15) / 16) * 16 * (K / 2) >= ((int64_t)1 << 32) || N * (K / 2) >= ((int64_t)1 << 32))
+  if ((int)a_layout < 0 || (int)a_layout > 2) return CR_ERR_INVALID_ARGUMENT;
+  const bool a8 = a_layout == CR_LAYOUT_INT8;
+  if (((M + 15) / 16) * 16 * (a8 ? K : K / 2) >= ((int64_t)1 << 32) || N * (K / 2) >= ((int64_t)1 << 32))
     return CR_ERR_UNSUPPORTED_SHAPE;
   const bool grouped = a_gran == CR_GRAN_ROW_GROUP;
   if (grouped != (w_gran == CR_GRAN_ROW_GROUP)) return CR_ERR_UNSUPPORTED_FORMAT;
+  if (a8 && (a_unsigned || grouped || lora_act || lora_up)) return CR_ERR_UNSUPPORTED_FORMAT;
   if (a_unsigned) {
     if (!w_sum || !aligned16(w_sum)) return CR_ERR_INVALID_ARGUMENT;
   }
@@ -320,7 +322,7 @@ cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
   p.a = static_cast<const uint8_t*>(a_codes);
   p.a_scales = a_scales;
   p.a_gran = a_gran;
-  p.act = a_unsigned ? cr::ACT_U4 : cr::ACT_S4;
+  p.act = a8 ? cr::ACT_I8 : (a_unsigned ? cr::ACT_U4 : cr::ACT_S4);
   p.a_shift = a_shift;
   p.w = static_cast<const uint8_t*>(w_packed);
   p.w_scales = w_scales;
@@ -340,6 +342,7 @@ cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
   p.K = K;
   p.grouped = grouped ? 1 : 0;
   p.a_tiled = a_layout == CR_LAYOUT_TILED ? 1 : 0;
+  if (a8) return finish_launch(cr::launch_gemm_a8w4(p, stream), E_W4A4, 1);
   return finish_launch(cr::launch_gemm_w4a4(p, stream), E_W4A4, 1);
 }
 

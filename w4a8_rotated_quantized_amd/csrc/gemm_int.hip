@@ -35,6 +35,25 @@ CR_DEV v4i widen_act(const uint8_t* lds) {
     return ACT == ACT_S4 ? widen_s4x16(x) : widen_u4(x);
   }
 }
+// The int4 widening above emits a lane's 16 k-values in the order (even k of
+// the first 8, odd k of the first 8, even of the second 8, odd of the second
+// 8). Int8 activation codes that meet such weights are put in the same order
+// (a dot product does not depend on the order of its terms).
+CR_DEV v4i i8_in_s4_order(v4i a) {
+  v4i r;
+  r[0] = (int)__builtin_amdgcn_perm((uint32_t)a[1], (uint32_t)a[0], 0x06040200u);
+  r[1] = (int)__builtin_amdgcn_perm((uint32_t)a[1], (uint32_t)a[0], 0x07050301u);
+  r[2] = (int)__builtin_amdgcn_perm((uint32_t)a[3], (uint32_t)a[2], 0x06040200u);
+  r[3] = (int)__builtin_amdgcn_perm((uint32_t)a[3], (uint32_t)a[2], 0x07050301u);
+  return r;
+}
+template <int ACT, int WGT>
+CR_DEV v4i act_operand(const uint8_t* lds) {
+  const v4i a = widen_act<ACT>(lds);
+  if constexpr (ACT == ACT_I8 && WGT == WGT_S4T) return i8_in_s4_order(a);
+  else return a;
+}
+
 template <int WGT>
 CR_DEV v4i widen_wgt(const uint8_t* lds) {
   if constexpr (WGT == WGT_I8N) {
@@ -230,7 +249,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_big_kernel(GemmParams p) {
         wv[j] = widen_wgt<WGT>(Ws + ((kt * (BN / 16) + wn * FN + j) * 64 + l) * WFB);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        av[i] = widen_act<ACT>(As + ((kt * (BM / 16) + wm * FM + i) * 64 + l) * AFB);
+        av[i] = act_operand<ACT, WGT>(As + ((kt * (BM / 16) + wm * FM + i) * 64 + l) * AFB);
       if constexpr (GRP) {
         const float* Ss = reinterpret_cast<const float*>(Ws + W_ST);
         float sa[FM];
@@ -368,7 +387,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         v4i av;
-        if constexpr (ACT == ACT_I8) av = __builtin_bit_cast(v4i, ar[u][i]);
+        if constexpr (ACT == ACT_I8 && WGT == WGT_S4T) av = i8_in_s4_order(__builtin_bit_cast(v4i, ar[u][i]));
+        else if constexpr (ACT == ACT_I8) av = __builtin_bit_cast(v4i, ar[u][i]);
         else if constexpr (ACT == ACT_S4) av = widen_s4x16(u32x2{ar[u][i][0], ar[u][i][1]});
         else av = widen_u4(u32x2{ar[u][i][0], ar[u][i][1]});
         if constexpr (GRP) {
@@ -652,6 +672,14 @@ static hipError_t launch_out(const GemmParams& p, hipStream_t s) {
 
 hipError_t launch_gemm_int(const GemmParams& p, hipStream_t s) {
   return launch_out<ACT_I8, WGT_I8N, false>(p, s);
+}
+
+// 8-bit activations x W4A4-format weights: the int4 weights widen to 16 q
+// as in the W4A4 GEMM, the activation codes enter the matrix cores as they
+// are, and an arithmetic shift by 4 returns the exact sum (the generic
+// weight-streaming kernel for M <= 64, the register-staged one above).
+hipError_t launch_gemm_a8w4(const GemmParams& p, hipStream_t s) {
+  return launch_out<ACT_I8, WGT_S4T, false>(p, s);
 }
 
 }  // namespace cr

@@ -88,6 +88,7 @@ struct GemmParams {
   const uint8_t* w_zeros;
 };
 hipError_t launch_gemm_int(const GemmParams& p, hipStream_t s);   // INT8 x INT8
+hipError_t launch_gemm_a8w4(const GemmParams& p, hipStream_t s);  // INT8 x tile-packed INT4
 hipError_t launch_gemm_w4a4(const GemmParams& p, hipStream_t s);  // INT4 x tile-packed INT4
 hipError_t launch_gemm_w4a8(const GemmParams& p, hipStream_t s);
 

@@ -118,7 +118,8 @@ class LinearSpec:
 
     fmt: "w4a4" (INT4 x INT4, tensorwise), "int8" (INT8 x INT8, tensorwise),
          "w4a8" (asym uint4 g16 weights x per-token int8 activations),
-         "w4a4_g64" (low-rank corrected, per-64-group scales)
+         "w4a4_g64" (low-rank corrected, per-64-group scales),
+         "a8w4" (W4A4-format weights, tensorwise, x per-token int8 activations)
     x_id: which activation tensor feeds it (layers that share an input share
           one rotate+quantize pass).
     """
@@ -193,6 +194,16 @@ def _c5(M: int = 8192):
     return w
 
 
+def _c2a8():
+    """The MMDiT projection of C2 on the 8-bit-activation branch: the same
+    W4A4-format weights against per-token INT8 activations (M = 4096 and 32)."""
+    w = Workload(2, "MMDiT projection, W4A4-format weights x per-token INT8 activations, (4096 + 32)x3072x3072")
+    for M in (4096, 32):
+        w.acts[f"x{M}"] = (M, 3072, "normal", 15, 30.0)
+        w.linears.append(LinearSpec(f"proj{M}", "a8w4", M, 3072, 3072, f"x{M}"))
+    return w
+
+
 CONFIGS = {
     "c1": _c1,
     "c2_m32": lambda: _c2(32),
@@ -200,6 +211,7 @@ CONFIGS = {
     "c3": _c3,
     "c4": _c4,
     "c5": _c5,
+    "c2a8": _c2a8,
 }
 
 
