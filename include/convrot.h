@@ -140,10 +140,15 @@ void convrot_reset_counters(void);
  *       rot 0:   SYM_INT4 with ROW_GROUP(64); UNSIGNED_INT4_SHIFT with ROW_GROUP(64)
  *       anything else returns CR_ERR_UNSUPPORTED_FORMAT.
  *   shift        UNSIGNED_INT4_SHIFT only: codes quantize v + shift (e.g. 0.171875)
- *   lora_down    optional bf16 [R, K] (R == 32) with rot 0: also writes
- *                lora_act[m, r] = sum_k x[m, k] * lora_down[r, k] (float32
+ *   lora_down    optional bf16 [R, K], R = 32 or 64 (not with ASYM_UINT4): also
+ *                writes lora_act[m, r] = sum_k x[m, k] * lora_down[r, k] (float32
  *                accumulation of the unshifted, unrotated input), stored as
- *                bf16 (lora_act_f32 = 0) or float32 (1), [rows, R] row-major
+ *                bf16 (lora_act_f32 = 0) or float32 (1), [rows, R] row-major.
+ *                Without rotation it is fused into the quantization pass; with
+ *                rotation it is one more launch over the same input (the
+ *                low-rank bypass of a LoRA kept beside quantized weights:
+ *                "Qwen-Image-Edit-2511-W4A8-ConvRot" card, passage on LoRA merge
+ *                versus bypass)
  *   codes        SYM_INT4 / UNSIGNED / ASYM: uint8 [rows, K/2] natural int4;
  *                SYM_INT8: int8 [rows, K]
  *   layout       CR_LAYOUT_NATURAL, or CR_LAYOUT_TILED for SYM_INT4 / UNSIGNED
@@ -257,7 +262,7 @@ cr_status w4_pack_weights(const void* codes, const void* scales, const void* zer
  *   w_scales    TENSOR [1], ROW [N], ROW_GROUP(64): packed [N/128][K/64][128]
  *   scale pairs: (TENSOR|ROW) x (TENSOR|ROW), or ROW_GROUP x ROW_GROUP (group 64)
  *   w_sum       float32 [N], required iff a_unsigned
- *   lora_act    optional [M, R] (bf16, or float32 if lora_act_f32), R == 32;
+ *   lora_act    optional [M, R] (bf16, or float32 if lora_act_f32), R = 32 or 64;
  *   lora_up     bf16 [N, R] (row n = output channel): y += lora_act @ lora_up^T
  *   bias        optional bf16 [N]
  *   out         CR_OUT_BF16: bf16 [M, ldc]; CR_OUT_F32: float32; CR_OUT_I32_RAW:
@@ -289,7 +294,11 @@ cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
  *   w_packed, w_scales (fp16), w_zeros (uint8), w_sum (float32 [N]): from
  *              w4_pack_weights (ASYM_UINT4); w_sum is required for CR_OUT_BF16 /
  *              CR_OUT_F32 and ignored (may be NULL) for CR_OUT_I32_RAW
- *   y[m, n] = s_a[m] * sum_g s_w[n, g] * sum_{k in g} qa[m,k] (qw[n,k] - z[n,g]) + bias[n]
+ *   lora_act   optional bf16 [M, R] (R = 32 or 64, e.g. from convrot_rotate_quantize's
+ *              lora_down with rotation), with lora_up bf16 [N, R]: the low-rank bypass
+ *              of a LoRA kept beside the quantized weight ("Qwen-Image-Edit-2511-W4A8-
+ *              ConvRot" card, passage on LoRA merge versus bypass): y += la @ lora_up^T
+ *   y[m, n] = s_a[m] * sum_g s_w[n, g] * sum_{k in g} qa[m,k] (qw[n,k] - z[n,g]) (+ low rank) + bias[n]
  *   CR_OUT_I32_RAW gives sum_k qa (qw - z) exactly (int8 matrix cores).
  *   CR_OUT_BF16 / CR_OUT_F32 run on fp16 matrix cores with each weight
  *   s (q - z) rounded once to fp16 (relative 2^-11) and float32 accumulation.
@@ -298,6 +307,7 @@ cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
 cr_status w4a8_gemm(const void* a_codes, const float* a_scales, cr_gran a_gran,
                     const void* w_packed, const void* w_scales, const void* w_zeros,
                     const float* w_sum, int group,
+                    const void* lora_act, const void* lora_up, int R,
                     const void* bias, void* out, cr_out out_type, int64_t ldc,
                     int64_t M, int64_t N, int64_t K,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);

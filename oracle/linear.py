@@ -166,12 +166,12 @@ def epilogue_g64(P, a_scales, w_scales, shift=0.0, wsum=None, la=None, l1_bits=N
     return _finish(y, shift, wsum, la, l1_bits, bias_bits)
 
 
-def epilogue_g16(P, a_scales, a_gran, w_scales16, bias_bits=None) -> np.ndarray:
+def epilogue_g16(P, a_scales, a_gran, w_scales16, bias_bits=None, la=None, l1_bits=None) -> np.ndarray:
     M, N, G = P.shape
     sa = _scale_vec(a_scales, a_gran, M)
     w = np.asarray(w_scales16, dtype=np.float64)
     y = sa[:, None] * np.einsum("ng,mng->mn", w, P.astype(np.float64))
-    return _finish(y, 0.0, None, None, None, bias_bits)
+    return _finish(y, 0.0, None, la, l1_bits, bias_bits)
 
 
 def _finish(y, shift, wsum, la, l1_bits, bias_bits):
@@ -248,12 +248,15 @@ def a8w4_linear(x_bits, w_bits, rot_group=256, a_gran="row", w_gran="tensor", bi
     return {"y": y, "raw": raw, "x": xa, "w": wp}
 
 
-def w4a8_linear(x_bits, w_bits, rot_group=256, group=16, bias_bits=None, wprep=None):
+def w4a8_linear(x_bits, w_bits, rot_group=256, group=16, bias_bits=None, wprep=None, l1_bits=None, l2_bits=None):
+    """l1_bits [N, R] / l2_bits [R, K] (bf16): a LoRA kept as a bf16 bypass
+    beside the quantized weight, y += (X L2^T) L1^T with X the unrotated input."""
     xa = rotate_quantize(x_bits, rot_group, "int8", "row")
     wp = wprep if wprep is not None else prepare_w4a8(w_bits, rot_group, group)
+    la = lora_down(x_bits, l2_bits) if l2_bits is not None else None
     P = gemm.group_partials(xa["values"], wp["values"], group, wp["zeros"])
-    y = epilogue_g16(P, xa["scales"], "row", wp["scales"], bias_bits)
-    return {"y": y, "raw": P.sum(axis=2), "x": xa, "w": wp}
+    y = epilogue_g16(P, xa["scales"], "row", wp["scales"], bias_bits, la, l1_bits)
+    return {"y": y, "raw": P.sum(axis=2), "x": xa, "w": wp, "la": la}
 
 
 def float_linear(x_bits, w_bits) -> np.ndarray:

@@ -94,8 +94,11 @@ def test_rq_validation(cr):
     assert _rq(cr, q=3, g=0) == 3                            # asym needs ROW_GROUP(16)
     assert _rq(cr, g=2, qg=32) == 3                          # group 32 not available
     assert _rq(cr, rot=0, g=0) == 3                          # rot 0 needs ROW_GROUP(64)
-    assert _rq(cr, rot=0, g=2, qg=64, lora=A, R=16, la=A) == 3   # rank must be 32
-    assert _rq(cr, rot=256, lora=A, R=32, la=A) == 3          # low rank only without rotation
+    assert _rq(cr, rot=0, g=2, qg=64, lora=A, R=16, la=A) == 3   # rank must be 32 or 64
+    assert _rq(cr, rot=256, lora=A, R=32, la=A) == 4          # low rank beside the rotation (bypass)
+    assert _rq(cr, rot=256, lora=A, R=64, la=A) == 4
+    assert _rq(cr, rot=256, lora=A, R=64) == 1                # needs its output
+    assert _rq(cr, q=3, g=2, qg=16, zeros=A, lora=A, R=32, la=A) == 3   # not for asymmetric weights
     assert _rq(cr, wsb=0) == 6                               # TENSOR needs workspace
     assert _rq(cr, q=1, layout=1) == 3                       # tiled layout is for int4 codes
     assert _rq(cr, layout=2) == 1
@@ -161,6 +164,7 @@ def test_gemm_validation(cr):
     assert _w4a4(cr, uns=1) == 1                             # unsigned needs w_sum
     assert _w4a4(cr, la=A, lu=None, R=32) == 3
     assert _w4a4(cr, la=A, lu=A, R=16) == 3
+    assert _w4a4(cr, la=A, lu=A, R=64) == 4
     assert _w4a4(cr, ot=5) == 1
     assert _w4a4(cr, layout=3) == 1
     assert _w4a4(cr, layout=2, uns=1, wsum=A) == 3           # 8-bit activations: signed only
@@ -170,17 +174,19 @@ def test_gemm_validation(cr):
     assert _w4a4(cr, M=1 << 20, K=32768, ldc=256) == 2        # M*K/2 beyond 32-bit offsets
     assert _w4a4(cr) == 4
     L = cr.lib
-    assert L.w4a8_gemm(_p(A), _p(A), 1, _p(A), _p(A), _p(A), _p(A), 32, None, _p(A), 0, 256, 64, 256, 512,
-                       None, 0, None) == 3
-    assert L.w4a8_gemm(_p(A), _p(A), 2, _p(A), _p(A), _p(A), _p(A), 16, None, _p(A), 0, 256, 64, 256, 512,
-                       None, 0, None) == 3
+    def w4a8(ag=1, wsum=A, group=16, la=None, lu=None, R=0, ot=0):
+        return L.w4a8_gemm(_p(A), _p(A), ag, _p(A), _p(A), _p(A), _p(wsum), group, _p(la), _p(lu), R, None, _p(A),
+                           ot, 256, 64, 256, 512, None, 0, None)
+    assert w4a8(group=32) == 3
+    assert w4a8(ag=2) == 3
     # the float outputs need the column-sum vector, the exact int32 output does not
-    assert L.w4a8_gemm(_p(A), _p(A), 1, _p(A), _p(A), _p(A), None, 16, None, _p(A), 0, 256, 64, 256, 512,
-                       None, 0, None) == 1
-    assert L.w4a8_gemm(_p(A), _p(A), 1, _p(A), _p(A), _p(A), None, 16, None, _p(A), 2, 256, 64, 256, 512,
-                       None, 0, None) == 4
-    assert L.w4a8_gemm(_p(A), _p(A), 1, _p(A), _p(A), _p(A), _p(A), 16, None, _p(A), 0, 256, 64, 256, 512,
-                       None, 0, None) == 4
+    assert w4a8(wsum=None) == 1
+    assert w4a8(wsum=None, ot=2) == 4
+    # low-rank bypass: rank 32 or 64, both factors
+    assert w4a8(la=A, lu=A, R=16) == 3
+    assert w4a8(la=A, R=32) == 3
+    assert w4a8(la=A, lu=A, R=64) == 4
+    assert w4a8() == 4
     assert L.int8_tensorwise_gemm(_p(A), None, _p(A), _p(A), None, _p(A), 0, 256, 64, 256, 512,
                                   None, 0, None) == 1
     assert L.int8_tensorwise_gemm(_p(A), _p(A), _p(A), _p(A), None, _p(A), 0, 256, 64, 256, 512,

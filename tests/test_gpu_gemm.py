@@ -248,6 +248,58 @@ def test_w4a8(cr, case):
     assert rel_l2(host(ybias), ref_b["y"]) <= W4A8_F32_TOL
 
 
+@pytest.mark.parametrize("R", [32, 64])
+def test_w4a8_lora_bypass(cr, R):
+    """A LoRA kept as a bf16 low-rank branch beside the W4A8 weight: la from
+    the rotate+quantize call on the unrotated input, the up-projection fused
+    into the GEMM epilogue; the output against the oracle's linear with the
+    same branch (bf16 la)."""
+    M, N, K = 333, 256, 3072
+    say(f"w4a8 lora R={R}")
+    xb = wl.activation(29, R, M, K)
+    wb = wl.weight(29, R + 1, N, K)
+    l1 = wl.weight(29, R + 2, N, R, std=0.05)
+    l2 = wl.weight(29, R + 3, R, K, std=0.05)
+    bias = wl.weight(29, R + 4, 1, N, std=0.5)[0]
+    wp = ol.prepare_w4a8(wb)
+    ref = ol.w4a8_linear(xb, wb, wprep=wp, l1_bits=l1, l2_bits=l2, bias_bits=bias)
+    a, sa, _, la = cr.convrot_rotate_quantize(bf16_dev(xb), 256, cr.Q.SYM_INT8, cr.GRAN.ROW, lora_down=bf16_dev(l2))
+    assert np.array_equal(host(a).view(np.uint8), ref["x"]["codes"].view(np.uint8))
+    args = (a, sa, 1, dev(wp["tiles"].reshape(-1)), dev(wp["scales_tiles"].reshape(-1)),
+            dev(wp["zeros_tiles"].reshape(-1)), M, N, K)
+    kw = dict(w_sum=dev(wp["wsum16"]), lora_act=la, lora_up=bf16_dev(l1), bias=bf16_dev(bias))
+    yf = cr.w4a8_gemm(*args, out_type=1, **kw)
+    yb = cr.w4a8_gemm(*args, out_type=0, **kw)
+    _check_out(yb, yf, ref["y"], f32_tol=W4A8_F32_TOL)
+    plain = cr.w4a8_gemm(*args, out_type=1, w_sum=kw["w_sum"], bias=kw["bias"])
+    assert rel_l2(host(yf) - host(plain), ref["y"] - ol.w4a8_linear(xb, wb, wprep=wp, bias_bits=bias)["y"]) <= 1e-2
+
+
+@pytest.mark.parametrize("R", [32, 64])
+def test_w4a4_lora_rank(cr, R):
+    """W4A4 tensorwise with ConvRot and a rank-R bypass (la from the rotated
+    rotate+quantize call), against the oracle's linear."""
+    M, N, K = 200, 384, 3072
+    say(f"w4a4 lora R={R}")
+    xb = wl.activation(30, R, M, K, n_outliers=3, outlier_scale=20.0)
+    wb = wl.weight(30, R + 1, N, K)
+    l1 = wl.weight(30, R + 2, N, R, std=0.05)
+    l2 = wl.weight(30, R + 3, R, K, std=0.05)
+    wp = ol.prepare_w4a4(wb, 256, "tensor")
+    ref = ol.w4a4_linear(xb, wb, 256, "tensor", "tensor", l1_bits=l1, l2_bits=l2, wprep=wp)
+    a, sa, _, la = cr.convrot_rotate_quantize(bf16_dev(xb), 256, 0, 0, layout=1, lora_down=bf16_dev(l2))
+    w = dev(wp["tiles"].reshape(-1))
+    sw = dev(np.asarray(wp["scales"], np.float32).reshape(-1))
+    # the epilogue on the oracle's la (identical inputs): float32 bar
+    la_ref = bf16_dev(wl.bf16_bits_from_f32(ref["la"]))
+    yf = cr.w4a4_gemm(a, sa, 0, w, sw, 0, M, N, K, lora_act=la_ref, lora_up=bf16_dev(l1), out_type=1)
+    yb = cr.w4a4_gemm(a, sa, 0, w, sw, 0, M, N, K, lora_act=la_ref, lora_up=bf16_dev(l1), out_type=0)
+    _check_out(yb, yf, ref["y"])
+    # end to end with the GPU's la (its bf16 rounding may differ by one ulp): bf16 bar
+    ye = cr.w4a4_gemm(a, sa, 0, w, sw, 0, M, N, K, lora_act=la, lora_up=bf16_dev(l1), out_type=0)
+    assert rel_l2(bf16_to_f32(host(ye)), ref["y"]) <= 2e-3
+
+
 def test_w4a8_float_outputs_match_fp16_weights(cr):
     """The float outputs equal, to float32 accumulation rounding, the product
     with each weight taken as fp16(s (q - z)): a reference built from the

@@ -92,6 +92,48 @@ def test_rotate_quantize_dual(cr, rot, shape):
     assert np.array_equal(host(n4), r4["codes"])
 
 
+def _check_lora_act(la, xb, l2, f32):
+    la_ref32 = ol.lora_down(xb, l2, act_f32=True).astype(np.float64)
+    mag = np.abs(wl.f32_from_bf16_bits(xb)).astype(np.float64) @ np.abs(wl.f32_from_bf16_bits(l2)).astype(np.float64).T
+    got = host(la)
+    if f32:
+        assert np.all(np.abs(got - la_ref32) <= mag * 2 ** -20 + 1e-30)
+    else:
+        gotf = wl.f32_from_bf16_bits(got).astype(np.float64)
+        assert np.all(np.abs(gotf - la_ref32) <= np.abs(la_ref32) * 2.0 ** -7 + mag * 2 ** -20 + 1e-30)
+
+
+@pytest.mark.parametrize("R", [32, 64])
+@pytest.mark.parametrize("mode", [("int4", "tensor"), ("int8", "row"), ("int4", "row_group")])
+def test_rotate_quantize_with_lora_down(cr, R, mode):
+    """Rotation on plus the low-rank down-projection of the unrotated input
+    (the LoRA bypass): codes and scales bit-exact, la to float32-sum bounds."""
+    qt, gran = mode
+    rows, K = 150, 3072
+    say(f"rq rot 256 + lora R={R} {mode}")
+    xb = wl.activation(20, R, rows, K, n_outliers=10, outlier_scale=20.0)
+    l2 = wl.weight(20, 500 + R, R, K, std=0.05)
+    qg = 64 if gran == "row_group" else 0
+    ref = ol.rotate_quantize(xb, 256, qt, gran, qg or None)
+    for f32 in (False, True):
+        codes, scales, _, la = cr.convrot_rotate_quantize(bf16_dev(xb), 256, QT[qt], GR[gran], qg,
+                                                          lora_down=bf16_dev(l2), lora_act_f32=f32)
+        assert np.array_equal(host(codes).reshape(ref["codes"].shape).view(np.uint8), ref["codes"].view(np.uint8))
+        assert np.array_equal(host(scales).reshape(-1).view(np.uint32),
+                              np.asarray(ref["scales"], np.float32).reshape(-1).view(np.uint32))
+        _check_lora_act(la, xb, l2, f32)
+
+
+def test_rotate_quantize_plain_lora_rank64(cr):
+    rows, K = 77, 1024
+    xb = wl.activation(21, 0, rows, K)
+    l2 = wl.weight(21, 1, 64, K, std=0.05)
+    ref = ol.rotate_quantize(xb, 0, "int4", "row_group", 64)
+    codes, scales, _, la = cr.convrot_rotate_quantize(bf16_dev(xb), 0, 0, 2, 64, lora_down=bf16_dev(l2))
+    assert np.array_equal(host(codes), ref["codes"])
+    _check_lora_act(la, xb, l2, False)
+
+
 def test_rotate_quantize_strided_rows_and_zero_rows(cr):
     rows, K, ldx = 40, 1024, 1024 + 64
     xb = wl.activation(12, 0, rows, ldx)

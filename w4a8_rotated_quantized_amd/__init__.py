@@ -75,7 +75,7 @@ _SIGS = {
     "w4_pack_weights": (_i, [_vp, _vp, _vp, _i64, _i64, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "w4a4_gemm": (_i, [_vp, _i, _vp, _i, _i, _f, _vp, _vp, _i, _vp, _vp, _i, _vp, _i, _vp,
                        _vp, _i, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
-    "w4a8_gemm": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _i64, _i64, _i64, _i64,
+    "w4a8_gemm": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _i, _i64, _i64, _i64, _i64,
                        _vp, _sz, _vp]),
     "int8_tensorwise_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i64, _i64, _i64, _i64,
                                   _vp, _sz, _vp]),
@@ -257,12 +257,15 @@ def w4a4_gemm(a_codes, a_scales, a_gran, w_packed, w_scales, w_gran, M, N, K,
 
 
 def w4a8_gemm(a_codes, a_scales, a_gran, w_packed, w_scales, w_zeros, M, N, K, group=16,
-              bias=None, out_type=OUT.BF16, out=None, stream=None, w_sum=None):
+              bias=None, out_type=OUT.BF16, out=None, stream=None, w_sum=None, lora_act=None, lora_up=None):
     """w_sum (float32 [N], from w4_pack_weights(..., want_wsum=True)) is
-    required for the bf16 / float32 outputs."""
+    required for the bf16 / float32 outputs. lora_act bf16 [M, R] with
+    lora_up bf16 [N, R] (R = 32 or 64) adds the low-rank bypass."""
     out = _out(M, N, out_type, a_codes.device, out)
+    R = 0 if lora_up is None else lora_up.shape[1]
     st = lib.w4a8_gemm(_ptr(a_codes), _ptr(a_scales), a_gran, _ptr(w_packed), _ptr(w_scales),
-                       _ptr(w_zeros), _ptr(w_sum), group, _ptr(bias), _ptr(out), out_type, out.stride(0),
+                       _ptr(w_zeros), _ptr(w_sum), group, _ptr(lora_act), _ptr(lora_up), R, _ptr(bias),
+                       _ptr(out), out_type, out.stride(0),
                        M, N, K, None, 0, _stream(stream))
     _check(st, "w4a8_gemm")
     return out

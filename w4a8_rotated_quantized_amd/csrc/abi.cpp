@@ -114,9 +114,13 @@ static cr_status rq_validate(const void* x, int64_t rows, int64_t K, int64_t ldx
   if (ldx % 8 != 0 || K > KMAX) return CR_ERR_UNSUPPORTED_SHAPE;
   if (rot_group != 0 && rot_group != 16 && rot_group != 64 && rot_group != 256 && rot_group != 1024)
     return CR_ERR_UNSUPPORTED_FORMAT;
+  if (lora_down) {
+    if (R != 32 && R != 64) return CR_ERR_UNSUPPORTED_FORMAT;
+    if (!lora_act || !aligned16(lora_down) || !aligned16(lora_act)) return CR_ERR_INVALID_ARGUMENT;
+    if (qtype == CR_Q_ASYM_UINT4) return CR_ERR_UNSUPPORTED_FORMAT;   // weights have no low-rank input branch
+  }
   if (rot_group != 0) {
     if (K % 256 != 0 || K % rot_group != 0) return CR_ERR_UNSUPPORTED_SHAPE;
-    if (lora_down) return CR_ERR_UNSUPPORTED_FORMAT;
     if (qtype == CR_Q_SYM_INT4 || qtype == CR_Q_SYM_INT8) {
       if (gran == CR_GRAN_ROW_GROUP && q_group != 64) return CR_ERR_UNSUPPORTED_FORMAT;
     } else if (qtype == CR_Q_ASYM_UINT4) {
@@ -130,10 +134,6 @@ static cr_status rq_validate(const void* x, int64_t rows, int64_t K, int64_t ldx
     if (K % 64 != 0) return CR_ERR_UNSUPPORTED_SHAPE;
     if (!(qtype == CR_Q_SYM_INT4 || qtype == CR_Q_UNSIGNED_INT4_SHIFT)) return CR_ERR_UNSUPPORTED_FORMAT;
     if (gran != CR_GRAN_ROW_GROUP || q_group != 64) return CR_ERR_UNSUPPORTED_FORMAT;
-    if (lora_down) {
-      if (R != 32) return CR_ERR_UNSUPPORTED_FORMAT;
-      if (!lora_act || !aligned16(lora_down) || !aligned16(lora_act)) return CR_ERR_INVALID_ARGUMENT;
-    }
   }
   return CR_OK;
 }
@@ -184,7 +184,8 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
   p.zeros = zeros;
   p.ws = static_cast<float*>(workspace);
   p.tiled = layout == CR_LAYOUT_TILED ? 1 : 0;
-  const uint64_t nl = (rot_group != 0 && gran == CR_GRAN_TENSOR && qtype != CR_Q_ASYM_UINT4) ? 2 : 1;
+  const uint64_t nl = ((rot_group != 0 && gran == CR_GRAN_TENSOR && qtype != CR_Q_ASYM_UINT4) ? 2 : 1) +
+                      ((rot_group != 0 && lora_down) ? 1 : 0);
   return finish_launch(cr::launch_rotate_quantize(p, stream), E_RQ, nl);
 }
 
@@ -313,7 +314,7 @@ cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
     if (!w_sum || !aligned16(w_sum)) return CR_ERR_INVALID_ARGUMENT;
   }
   if (lora_act || lora_up) {
-    if (!lora_act || !lora_up || R != 32) return CR_ERR_UNSUPPORTED_FORMAT;
+    if (!lora_act || !lora_up || (R != 32 && R != 64)) return CR_ERR_UNSUPPORTED_FORMAT;
     if (!aligned16(lora_act) || !aligned16(lora_up)) return CR_ERR_INVALID_ARGUMENT;
   }
   st = device_check();
@@ -347,7 +348,8 @@ cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
 }
 
 cr_status w4a8_gemm(const void* a_codes, const float* a_scales, cr_gran a_gran, const void* w_packed,
-                    const void* w_scales, const void* w_zeros, const float* w_sum, int group, const void* bias,
+                    const void* w_scales, const void* w_zeros, const float* w_sum, int group,
+                    const void* lora_act, const void* lora_up, int R, const void* bias,
                     void* out, cr_out out_type, int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
   (void)workspace;
@@ -357,6 +359,10 @@ cr_status w4a8_gemm(const void* a_codes, const float* a_scales, cr_gran a_gran, 
   if (!a_scales || !w_scales || !w_zeros) return CR_ERR_INVALID_ARGUMENT;
   if (!aligned16(a_scales) || !aligned16(w_scales) || !aligned16(w_zeros)) return CR_ERR_INVALID_ARGUMENT;
   if (out_type != CR_OUT_I32_RAW && (!w_sum || !aligned16(w_sum))) return CR_ERR_INVALID_ARGUMENT;
+  if (lora_act || lora_up) {
+    if (!lora_act || !lora_up || (R != 32 && R != 64)) return CR_ERR_UNSUPPORTED_FORMAT;
+    if (!aligned16(lora_act) || !aligned16(lora_up)) return CR_ERR_INVALID_ARGUMENT;
+  }
   if (group != 16) return CR_ERR_UNSUPPORTED_FORMAT;
   if (!(a_gran == CR_GRAN_ROW || a_gran == CR_GRAN_TENSOR)) return CR_ERR_UNSUPPORTED_FORMAT;
   st = device_check();
@@ -370,6 +376,9 @@ cr_status w4a8_gemm(const void* a_codes, const float* a_scales, cr_gran a_gran, 
   p.w_scales16 = static_cast<const uint16_t*>(w_scales);
   p.w_zeros = static_cast<const uint8_t*>(w_zeros);
   p.w_sum = w_sum;
+  p.lora_act = lora_act;
+  p.lora_up = static_cast<const uint16_t*>(lora_up);
+  p.R = R;
   p.bias = static_cast<const uint16_t*>(bias);
   p.out = out;
   p.out_type = out_type;

@@ -32,17 +32,19 @@ CR_DEV void lora_up_block(const GemmParams& p, int64_t mb, int64_t nb, int l, fl
   const int64_t mrow = (mb + (l & 15) < p.M) ? mb + (l & 15) : p.M - 1;
   const int64_t nrow = nb + (l & 15);
   v4f acc = {0.f, 0.f, 0.f, 0.f};
+  const int R = p.R;                       // 32 or 64
   if (!p.lora_f32) {
-    const uint16_t* la = reinterpret_cast<const uint16_t*>(p.lora_act) + mrow * 32 + (l >> 4) * 8;
-    const uint16_t* lu = p.lora_up + nrow * 32 + (l >> 4) * 8;
-    v8bf a = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(lu));
-    v8bf b = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(la));
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    for (int r0 = 0; r0 < R; r0 += 32) {
+      const uint16_t* la = reinterpret_cast<const uint16_t*>(p.lora_act) + mrow * R + r0 + (l >> 4) * 8;
+      const uint16_t* lu = p.lora_up + nrow * R + r0 + (l >> 4) * 8;
+      v8bf a = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(lu));
+      v8bf b = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(la));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
   } else {
-    const float* la = reinterpret_cast<const float*>(p.lora_act) + mrow * 32;
-    const uint16_t* lu = p.lora_up + nrow * 32;
-#pragma unroll
-    for (int r0 = 0; r0 < 32; r0 += 4) {
+    const float* la = reinterpret_cast<const float*>(p.lora_act) + mrow * R;
+    const uint16_t* lu = p.lora_up + nrow * R;
+    for (int r0 = 0; r0 < R; r0 += 4) {
       float a = __uint_as_float((uint32_t)lu[r0 + (l >> 4)] << 16);
       float b = la[r0 + (l >> 4)];
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);

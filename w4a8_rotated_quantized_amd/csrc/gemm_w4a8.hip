@@ -340,9 +340,11 @@ __global__ __launch_bounds__(256, 2) void gemm_w4a8_h_kernel(GemmParams p) {
 
   // D = W . A^T per 32 x 32 block: lane owns token m = l % 32 and channels
   // 8 (r / 4) + 4 (l / 32) + r % 4. The activations entered as 1152 + a, so
-  // 1152 * w_sum[n] comes off first. Every epilogue input is loaded up front
-  // and unconditionally (a missing bias reads w_sum's memory and is zeroed),
-  // so no store waits on a load.
+  // 1152 * w_sum[n] comes off first. Phase 1 turns every accumulator into its
+  // output value in place, phase 2 stores them: all epilogue loads (scales,
+  // column sums, bias, low-rank operands) are issued before the first store,
+  // so no load waits on a store. A missing bias reads w_sum's memory and is
+  // zeroed.
   float sa[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -365,17 +367,45 @@ __global__ __launch_bounds__(256, 2) void gemm_w4a8_h_kernel(GemmParams p) {
   for (int j = 0; j < 2; ++j) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int64_t n = n0 + (wn * 2 + j) * 32 + 8 * q + 4 * h;
       const v4f c = cw[j][q] * 1152.f;
       const u32x2 bb = has_bias ? bw[j][q] : u32x2{0u, 0u};
       const v4f b = v4f{bf16_lo(bb[0]), bf16_hi(bb[0]), bf16_lo(bb[1]), bf16_hi(bb[1])};
 #pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[i][j][4 * q + t] = (acc[i][j][4 * q + t] - c[t]) * sa[i] + b[t];
+    }
+  }
+  if (p.lora_act) {
+    // low-rank branch: y[m, n] += sum_r la[m, r] L1[n, r], one
+    // v_mfma_f32_32x32x16_bf16 per 16 ranks and 32 x 32 block, whose result
+    // layout is that of the main accumulators
+    const uint16_t* la = reinterpret_cast<const uint16_t*>(p.lora_act);
+    const int R = p.R;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint16_t* lu = p.lora_up + (n0 + (wn * 2 + j) * 32 + lr) * R + 8 * h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t* lam = la + imin64(m0 + wm * 128 + i * 32 + lr, p.M - 1) * R + 8 * h;
+        for (int r0 = 0; r0 < R; r0 += 16)        // accumulates onto the finished outputs
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(lu + r0)),
+              __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(lam + r0)), acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);          // one block's operands live at a time
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t n = n0 + (wn * 2 + j) * 32 + 8 * q + 4 * h;
+#pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t m = m0 + wm * 128 + i * 32 + lr;
-        float y[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) y[t] = (acc[i][j][4 * q + t] - c[t]) * sa[i] + b[t];
         if (m >= p.M) continue;
+        const float y[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         if constexpr (OUT == CR_OUT_F32) {
           *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.out) + m * p.ldc + n) = v4f{y[0], y[1], y[2], y[3]};
         } else {

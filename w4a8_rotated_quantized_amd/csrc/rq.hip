@@ -490,9 +490,12 @@ __global__ __launch_bounds__(256) void rq_tensor_kernel(RQParams a) {
 // slice. Lane l: row l%16, 8-element chunk l/16 of each 32-column half; this
 // is also the A-operand layout of the 16x16x32 bf16 MFMA used for LoRA-down.
 // ---------------------------------------------------------------------------
-template <bool UNSIGNED, bool LORA>
+template <bool UNSIGNED, bool LORA, int R = 32, bool QUANT = true>
 __global__ __launch_bounds__(256) void rq_plain_kernel(RQParams a) {
-  __shared__ float lred[4][16][32];
+  static_assert(R == 32 || R == 64, "low-rank branch of rank 32 or 64");
+  static_assert(QUANT || LORA, "nothing to do");
+  constexpr int RB = R / 16;
+  __shared__ float lred[LORA ? 4 : 1][16][LORA ? R : 1];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int l = tid & 63;
@@ -505,7 +508,9 @@ __global__ __launch_bounds__(256) void rq_plain_kernel(RQParams a) {
   const int nsl = (int)(a.K / 64);
   const float sh = a.shift;
   const float qmax = UNSIGNED ? 15.f : 7.f;
-  v4f acc[2] = {v4f{0, 0, 0, 0}, v4f{0, 0, 0, 0}};
+  v4f acc[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) acc[rb] = v4f{0, 0, 0, 0};
 
   for (int t = wave; t < nsl; t += 4) {
     u32x4 w0 = *reinterpret_cast<const u32x4*>(xr + t * 64 + c * 8);
@@ -519,80 +524,82 @@ __global__ __launch_bounds__(256) void rq_plain_kernel(RQParams a) {
       v[8 + 2 * j + 1] = bf16_hi(w1[j]);
     }
     if (LORA) {
-      // la += X[16 rows, 64 cols] @ L2^T[64 cols, 32 ranks]
+      // la += X[16 rows, 64 cols] @ L2^T[64 cols, R ranks]
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         u32x4 xa = h ? w1 : w0;
         v8bf afr = __builtin_bit_cast(v8bf, xa);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < RB; ++rb) {
           const uint16_t* lp = a.lora_down + (int64_t)(rb * 16 + rl) * a.K + t * 64 + h * 32 + c * 8;
           u32x4 lb = *reinterpret_cast<const u32x4*>(lp);
           acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(v8bf, lb), acc[rb], 0, 0, 0);
         }
       }
     }
-    float m = 0.f;
-    if (UNSIGNED) {
+    if constexpr (QUANT) {
+      float m = 0.f;
+      if (UNSIGNED) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          v[e] = __fadd_rn(v[e], sh);
+          m = fmaxf(m, v[e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[e]));
+      }
+      // max over the 4 lanes of this row (l, l^16, l^32, l^48)
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      const float r = (m > 0.f) ? div_rn(qmax, m) : 0.f;
+      if (rok && c == 0) {
+        float s = (m > 0.f) ? div_rn(m, qmax) : 0.f;
+        reinterpret_cast<float*>(a.scales)[row * nsl + t] = s;
+      }
+      uint32_t out[2] = {0u, 0u};
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        v[e] = __fadd_rn(v[e], sh);
-        m = fmaxf(m, v[e]);
+        uint32_t b;
+        if (UNSIGNED) {
+          float p = rintf(__fmul_rn(v[e], r));
+          p = fminf(fmaxf(p, 0.f), 15.f);
+          b = (uint32_t)p;
+        } else {
+          b = qbits(v[e], r) & 0xF;
+        }
+        out[e >> 3] |= b << (4 * (e & 7));
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[e]));
-    }
-    // max over the 4 lanes of this row (l, l^16, l^32, l^48)
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
-    const float r = (m > 0.f) ? div_rn(qmax, m) : 0.f;
-    if (rok && c == 0) {
-      float s = (m > 0.f) ? div_rn(m, qmax) : 0.f;
-      reinterpret_cast<float*>(a.scales)[row * nsl + t] = s;
-    }
-    uint32_t out[2] = {0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      uint32_t b;
-      if (UNSIGNED) {
-        float p = rintf(__fmul_rn(v[e], r));
-        p = fminf(fmaxf(p, 0.f), 15.f);
-        b = (uint32_t)p;
-      } else {
-        b = qbits(v[e], r) & 0xF;
-      }
-      out[e >> 3] |= b << (4 * (e & 7));
-    }
-    if (rok) {
-      if (a.tiled) {
-        // elements 64t + 32h + 8c .. +8 are half (c&1) of chunk 2h + c/2 of k-tile t
-        uint8_t* dst = reinterpret_cast<uint8_t*>(a.codes) + ((row >> 4) * (a.K / 64) + t) * 512 + rl * 8 + (c & 1) * 4;
-        *reinterpret_cast<uint32_t*>(dst + (c >> 1) * 128) = out[0];
-        *reinterpret_cast<uint32_t*>(dst + (2 + (c >> 1)) * 128) = out[1];
-      } else {
-        uint8_t* dst = reinterpret_cast<uint8_t*>(a.codes) + row * (a.K / 2) + t * 32;
-        *reinterpret_cast<uint32_t*>(dst + c * 4) = out[0];
-        *reinterpret_cast<uint32_t*>(dst + 16 + c * 4) = out[1];
+      if (rok) {
+        if (a.tiled) {
+          // elements 64t + 32h + 8c .. +8 are half (c&1) of chunk 2h + c/2 of k-tile t
+          uint8_t* dst = reinterpret_cast<uint8_t*>(a.codes) + ((row >> 4) * (a.K / 64) + t) * 512 + rl * 8 + (c & 1) * 4;
+          *reinterpret_cast<uint32_t*>(dst + (c >> 1) * 128) = out[0];
+          *reinterpret_cast<uint32_t*>(dst + (2 + (c >> 1)) * 128) = out[1];
+        } else {
+          uint8_t* dst = reinterpret_cast<uint8_t*>(a.codes) + row * (a.K / 2) + t * 32;
+          *reinterpret_cast<uint32_t*>(dst + c * 4) = out[0];
+          *reinterpret_cast<uint32_t*>(dst + 16 + c * 4) = out[1];
+        }
       }
     }
   }
-  if (LORA) {
+  if constexpr (LORA) {
     // output fragment: lane l holds rank rb*16 + l%16, rows 4*(l/16) + j
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) lred[wave][4 * c + j][rb * 16 + rl] = acc[rb][j];
     __syncthreads();
-    for (int idx = tid; idx < 16 * 32; idx += 256) {
-      int rr = idx >> 5, rk = idx & 31;
+    for (int idx = tid; idx < 16 * R; idx += 256) {
+      int rr = idx / R, rk = idx % R;
       int64_t orow = (int64_t)blockIdx.x * 16 + rr;
       if (orow >= a.rows) continue;
       float s = ((lred[0][rr][rk] + lred[1][rr][rk]) + lred[2][rr][rk]) + lred[3][rr][rk];
       if (a.lora_f32)
-        reinterpret_cast<float*>(a.lora_act)[orow * 32 + rk] = s;
+        reinterpret_cast<float*>(a.lora_act)[orow * R + rk] = s;
       else
-        reinterpret_cast<uint16_t*>(a.lora_act)[orow * 32 + rk] = (uint16_t)f32_to_bf16_bits(s);
+        reinterpret_cast<uint16_t*>(a.lora_act)[orow * R + rk] = (uint16_t)f32_to_bf16_bits(s);
     }
   }
 }
@@ -760,25 +767,33 @@ hipError_t launch_rotate_quantize_dual(RQParams p, hipStream_t s) {
 }
 
 hipError_t launch_rotate_quantize(RQParams p, hipStream_t s) {
+  const int nblk = (int)((p.rows + 15) / 16);
+  const bool lora = p.lora_down != nullptr;
   if (p.rot_group == 0) {
-    const int nblk = (int)((p.rows + 15) / 16);
-    const bool lora = p.lora_down != nullptr;
     if (p.qtype == CR_Q_UNSIGNED_INT4_SHIFT) {
-      if (lora) hipLaunchKernelGGL((rq_plain_kernel<true, true>), dim3(nblk), dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((rq_plain_kernel<true, false>), dim3(nblk), dim3(256), 0, s, p);
+      if (!lora) hipLaunchKernelGGL((rq_plain_kernel<true, false>), dim3(nblk), dim3(256), 0, s, p);
+      else if (p.R == 64) hipLaunchKernelGGL((rq_plain_kernel<true, true, 64>), dim3(nblk), dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((rq_plain_kernel<true, true, 32>), dim3(nblk), dim3(256), 0, s, p);
     } else {
-      if (lora) hipLaunchKernelGGL((rq_plain_kernel<false, true>), dim3(nblk), dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((rq_plain_kernel<false, false>), dim3(nblk), dim3(256), 0, s, p);
+      if (!lora) hipLaunchKernelGGL((rq_plain_kernel<false, false>), dim3(nblk), dim3(256), 0, s, p);
+      else if (p.R == 64) hipLaunchKernelGGL((rq_plain_kernel<false, true, 64>), dim3(nblk), dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((rq_plain_kernel<false, true, 32>), dim3(nblk), dim3(256), 0, s, p);
     }
     return hipGetLastError();
   }
   p.G = (int)(p.K / 256);
+  hipError_t e;
   switch (p.rot_group) {
-    case 16: return launch_rotated<16>(p, s);
-    case 64: return launch_rotated<64>(p, s);
-    case 1024: return launch_rotated<1024>(p, s);
-    default: return launch_rotated<256>(p, s);
+    case 16: e = launch_rotated<16>(p, s); break;
+    case 64: e = launch_rotated<64>(p, s); break;
+    case 1024: e = launch_rotated<1024>(p, s); break;
+    default: e = launch_rotated<256>(p, s); break;
   }
+  if (e != hipSuccess || !lora) return e;
+  // the low-rank down-projection reads the unrotated input: one more launch
+  if (p.R == 64) hipLaunchKernelGGL((rq_plain_kernel<false, true, 64, false>), dim3(nblk), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((rq_plain_kernel<false, true, 32, false>), dim3(nblk), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace cr
