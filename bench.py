@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--rot-group", type=int, default=256, choices=(16, 64, 256, 1024),
                     help="ConvRot group size of the c2 line (256 is the configuration the metric is quoted on)")
     ap.add_argument("--workload", default="c2",
-                    help="c2 (default: the headline line), or c1 / c3 / c4 / c5 / c2a8 for the other workloads' "
+                    help="c2 (default: the headline line), or c1 / c3 / c4 / c5 / c2a8 / merge for the other workloads' "
                          "throughput lines (bench_workloads.py)")
     return ap.parse_args()
 

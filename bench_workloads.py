@@ -38,7 +38,57 @@ def _plan(w):
     return rq, gemms
 
 
+def run_merge(steps, warmup):
+    """LoRA merge into a W4A8 weight (12288 x 3072, asym uint4 g16, ConvRot
+    256) with a rank-64 delta: dequantize + delta, rotate + quantize again,
+    pack; one JSON line with the time per merge and the bytes it moves."""
+    import numpy as np
+    import torch
+    import w4a8_rotated_quantized_amd as cr
+    import workloads as wl
+    dev = torch.device("cuda:0")
+    N, K, R = 12288, 3072, 64
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    w = wl.CONFIGS["c3"]()
+    wb = bf16(wl.weight_bits(w, w.linears[0]))
+    up, down = bf16(wl.weight(3, 700, N, R, std=0.05)), bf16(wl.weight(3, 701, R, K, std=0.05))
+    codes, scales, zeros, _ = cr.convrot_rotate_quantize(wb, 256, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16)
+    merged = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    c2, s2, z2 = torch.empty_like(codes), torch.empty_like(scales), torch.empty_like(zeros)
+
+    def step():
+        cr.convrot_dequantize_weights(codes, scales, N, K, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16, 256, zeros=zeros,
+                                      delta_up=up, delta_down=down, out=merged)
+        cr.convrot_rotate_quantize(merged, 256, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16, codes=c2, scales=s2, zeros=z2)
+        cr.w4_pack_weights(c2, s2, N, K, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16, zeros=z2, want_wsum=True)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # bytes: codes + scales + zeros in, bf16 weight out and back in, new codes/scales/zeros, packed set
+    q_bytes = N * K // 2 + N * K // 16 * 2 + N * K // 32
+    moved = q_bytes + 2 * N * K + 2 * N * K + q_bytes + (N * K // 2 + N * K // 16 * 3 + 4 * N) + R * (N + K) * 2
+    print(json.dumps({
+        "metric": "LoRA merge into a quantized weight (dequantize + rank-64 delta + requantize + pack)",
+        "value": round(ms, 4), "unit": "ms per merge", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "higher_is_better": False, "data": "synthetic",
+        "config": {"workload": "W4A8 asym g16 weight 12288x3072, ConvRot 256, LoRA rank 64"},
+        "GBps": round(moved / ms / 1e6, 1)}))
+
+
 def run(name, steps, warmup):
+    if name == "merge":
+        return run_merge(steps, warmup)
     import numpy as np
     import torch
     import w4a8_rotated_quantized_amd as cr

@@ -241,6 +241,37 @@ cr_status w4_pack_weights(const void* codes, const void* scales, const void* zer
                           hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * convrot_dequantize_weights - quantized weights back to bf16 in the
+ * original (unrotated) basis, plus an optional low-rank delta: merging a LoRA
+ * into quantized weights.
+ *
+ * Cites: "Qwen-Image-Edit-2511-W4A8-ConvRot" card, passage on LoRA merge
+ * versus bypass (a LoRA loaded onto a quantized weight dequantizes it, adds
+ * the delta and quantizes the result again).
+ *
+ *   codes      natural codes as written by convrot_rotate_quantize: int4
+ *              [N, K/2] (SYM_INT4, ASYM_UINT4) or int8 [N, K] (SYM_INT8)
+ *   scales     float32 [1] / [N] / [N, K/64] (SYM_INT4 TENSOR / ROW /
+ *              ROW_GROUP(64)), float32 [1] / [N] (SYM_INT8); ASYM_UINT4 g16:
+ *              fp16 [N, K/16] with zeros uint8 [N, K/32]
+ *   rot_group  the rotation the weights were quantized with (0, 16, 64, 256,
+ *              1024; ASYM: 0 or 256)
+ *   delta_up   optional bf16 [N, R] and delta_down bf16 [R, K] (1 <= R <= 256):
+ *              adds sum_j up[n, j] down[j, k]
+ *   out        bf16 [N, K]
+ * Per element (float32, fixed order, one bf16 rounding at the end):
+ *   r = fl(s q) (ASYM: s16 (q - z), exact); w = H r / sqrt(rot_group) per
+ *   group with the forward rotation's butterflies (H / sqrt(n) is its own
+ *   inverse); d = sum over j in increasing order of up[n, j] down[j, k];
+ *   out = bf16_rne(fl(w + d)) (a zero as +0). Requantize with convrot_rotate_quantize and
+ *   w4_pack_weights. Shape: K % 256 == 0 and K % rot_group == 0.
+ */
+cr_status convrot_dequantize_weights(const void* codes, const void* scales, const void* zeros,
+                                     int64_t N, int64_t K, cr_qtype qtype, cr_gran gran, int q_group,
+                                     int rot_group, const void* delta_up, const void* delta_down, int R,
+                                     void* out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * w4a4_gemm - INT4 activations x tile-packed INT4 weights on int8 matrix
  * cores (exact int4 -> int8 widening, int32 accumulation) with a fused
  * epilogue.

@@ -139,6 +139,47 @@ def weight_sum_w4a8(codes: np.ndarray, scales16: np.ndarray, zeros: np.ndarray, 
     return np.array([_int_to_f32_rne(int(t), -24) for t in units.sum(axis=1)], dtype=np.float32)
 
 
+def dequantize_weights(values, scales, qtype, gran, group=None, zeros=None, rot_group=256,
+                       up_bits=None, down_bits=None) -> np.ndarray:
+    """Quantized weights back to bf16 bits [N, K] in the unrotated basis, plus
+    an optional low-rank delta up @ down (a LoRA merged into the weight; the
+    "Qwen-Image-Edit-2511-W4A8-ConvRot" card's passage on LoRA merge versus
+    bypass: dequantize, add the delta, quantize again).
+
+    Float32 throughout, in this order: r = fl(s * q) (asymmetric: s16 (q - z),
+    exact); w = rotate(r) / sqrt(n) (H / sqrt(n) is its own inverse; the
+    forward rotation's butterflies); d accumulated over the ranks in
+    increasing order (bf16 products are exact in float32); one bf16 rounding
+    of fl(w + d). Zeros are +0 (the rotation's sign bookkeeping is free to
+    produce either)."""
+    q = np.asarray(values)
+    N, K = q.shape
+    if qtype == "asym_u4":
+        r = quant.dequant_asym(q, scales, zeros, group).astype(np.float32)
+    else:
+        s = np.asarray(scales, dtype=np.float32)
+        if gran == "tensor":
+            sv = np.full((N, K), s.reshape(-1)[0], dtype=np.float32)
+        elif gran == "row":
+            sv = np.repeat(s.reshape(N, 1), K, axis=1)
+        else:
+            sv = np.repeat(s.reshape(N, K // group), group, axis=1)
+        r = (sv * q.astype(np.float32)).astype(np.float32)
+    w = r
+    if rot_group:
+        w = (hadamard.rotate(r, rot_group) * np.float32(1.0 / np.sqrt(rot_group))).astype(np.float32)
+    if up_bits is not None:
+        up, down = _f32(up_bits), _f32(down_bits)
+        d = np.zeros((N, K), dtype=np.float32)
+        for j in range(up.shape[1]):
+            d = (d + up[:, j:j + 1] * down[j:j + 1, :]).astype(np.float32)
+        w = (w + d).astype(np.float32)
+    w = (w + np.float32(0.0)).astype(np.float32)          # a zero comes out as +0
+    b = np.ascontiguousarray(w, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return b.astype(np.uint16)
+
+
 # ---------------------------------------------------------------------------
 # epilogues
 # ---------------------------------------------------------------------------

@@ -124,6 +124,27 @@ def test_rq_dual_validation(cr):
         assert dual(rot=rot) == 4            # valid -> device check (no GPU here)
 
 
+def test_dequantize_validation(cr):
+    L = cr.lib
+    def deq(codes=A, scales=A, zeros=None, N=128, K=1024, q=0, g=0, qg=0, rot=256, up=None, down=None, R=0, out=A):
+        return L.convrot_dequantize_weights(_p(codes), _p(scales), _p(zeros), N, K, q, g, qg, rot, _p(up), _p(down),
+                                            R, _p(out), None)
+    assert deq(codes=None) == 1
+    assert deq(out=A + 8) == 1
+    assert deq(K=1000) == 2
+    assert deq(rot=128) == 3
+    assert deq(rot=1024, K=1536) == 2
+    assert deq(q=2) == 3                         # activation-only format
+    assert deq(q=1, g=2, qg=64) == 3             # int8 weights: tensor or row
+    assert deq(q=3, g=2, qg=16) == 1             # asymmetric: needs zeros
+    assert deq(q=3, g=2, qg=16, zeros=A, rot=64) == 3
+    assert deq(up=A, R=16) == 1                  # both factors
+    assert deq(up=A, down=A, R=0) == 1
+    assert deq(up=A, down=A, R=16) == 4
+    assert deq(q=3, g=2, qg=16, zeros=A) == 4
+    assert deq() == 4
+
+
 def test_rq_workspace_size(cr):
     n = cr.convrot_rq_workspace_size(4096, 3072, 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
     assert n > 0 and n % 4 == 0

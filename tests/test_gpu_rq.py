@@ -134,6 +134,55 @@ def test_rotate_quantize_plain_lora_rank64(cr):
     _check_lora_act(la, xb, l2, False)
 
 
+MERGE_CASES = [("int4", "tensor", 256), ("int4", "row", 1024), ("int4", "row_group", 64), ("int8", "tensor", 256),
+               ("int8", "row", 16), ("int4", "tensor", 0), ("asym_u4", "row_group", 256)]
+
+
+@pytest.mark.parametrize("case", MERGE_CASES)
+@pytest.mark.parametrize("R", [0, 16, 64])
+def test_dequantize_weights_merge(cr, case, R):
+    """Quantized weights back to bf16 in the unrotated basis plus a low-rank
+    delta (a LoRA merge): bit-exact against the oracle."""
+    qt, gran, rot = case
+    N, K = 256, 3072
+    say(f"dequantize {case} R={R}")
+    wb = wl.weight(22, rot + R, N, K)
+    qg = {"row_group": 16 if qt == "asym_u4" else 64}.get(gran)
+    ref = ol.rotate_quantize(wb, rot, qt, gran, qg)
+    QQ = {"int4": 0, "int8": 1, "asym_u4": 3}[qt]
+    codes = dev(np.ascontiguousarray(ref["codes"]))
+    scales = dev(np.ascontiguousarray(ref["scales"]))
+    zeros = dev(ref["zeros_packed"]) if qt == "asym_u4" else None
+    up = wl.weight(22, 900 + R, N, R, std=0.05) if R else None
+    down = wl.weight(22, 901 + R, R, K, std=0.05) if R else None
+    out = cr.convrot_dequantize_weights(codes, scales, N, K, QQ, GR[gran], qg or 0, rot, zeros=zeros,
+                                        delta_up=None if up is None else bf16_dev(up),
+                                        delta_down=None if down is None else bf16_dev(down))
+    want = ol.dequantize_weights(ref["values"], ref["scales"], qt, gran, qg, ref.get("zeros"), rot, up, down)
+    assert np.array_equal(host(out).view(np.uint16), want)
+
+
+def test_lora_merge_round_trip(cr):
+    """The whole merge on the GPU path: quantize (ConvRot 256, INT4 per
+    tensor), dequantize + delta, quantize and pack again; codes, scale and the
+    packed tiles equal the oracle's same steps."""
+    N, K, R = 384, 3072, 32
+    wb = wl.weight(23, 0, N, K)
+    up, down = wl.weight(23, 1, N, R, std=0.05), wl.weight(23, 2, R, K, std=0.05)
+    codes, scales, _, _ = cr.convrot_rotate_quantize(bf16_dev(wb), 256, 0, 0)
+    merged = cr.convrot_dequantize_weights(codes, scales, N, K, 0, 0, 0, 256, delta_up=bf16_dev(up),
+                                           delta_down=bf16_dev(down))
+    c2, s2, _, _ = cr.convrot_rotate_quantize(merged, 256, 0, 0)
+    packed = cr.w4_pack_weights(c2, s2, N, K)[0]
+    r0 = ol.rotate_quantize(wb, 256, "int4", "tensor")
+    mb = ol.dequantize_weights(r0["values"], r0["scales"], "int4", "tensor", None, None, 256, up, down)
+    r1 = ol.prepare_w4a4(mb, 256, "tensor")
+    assert np.array_equal(host(merged).view(np.uint16), mb)
+    assert np.array_equal(host(c2), r1["codes"])
+    assert np.array_equal(host(s2).view(np.uint32), np.asarray(r1["scales"], np.float32).reshape(-1).view(np.uint32))
+    assert np.array_equal(bytes_of(packed), r1["tiles"].reshape(-1))
+
+
 def test_rotate_quantize_strided_rows_and_zero_rows(cr):
     rows, K, ldx = 40, 1024, 1024 + 64
     xb = wl.activation(12, 0, rows, ldx)

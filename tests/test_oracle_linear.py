@@ -214,3 +214,51 @@ def test_a8w4_linear_brute_force():
             acc = sum(int(qa[m, k]) * int(qw[n, k]) for k in range(512))
             assert r["raw"][m, n] == acc
             assert np.isclose(r["y"][m, n], sa[m] * sw[n] * acc + bf[n], rtol=1e-6, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# dequantize_weights (LoRA merge)
+# ---------------------------------------------------------------------------
+
+def _bf16_value(bits):
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_dequantize_without_rotation_is_scale_times_code():
+    rng = np.random.default_rng(41)
+    q = rng.integers(-7, 8, (3, 256))
+    out = linear.dequantize_weights(q, np.array([2.0 ** -3], np.float32), "int4", "tensor", rot_group=0)
+    assert np.array_equal(_bf16_value(out), q * 2.0 ** -3)
+
+
+def test_dequantize_undoes_the_rotation_exactly_on_small_integers():
+    # with s = 1 and small integer codes, H q / 4 (n = 16) is exact and bf16-representable:
+    # the butterflies must reproduce the explicit regular Hadamard product
+    from oracle import hadamard
+    rng = np.random.default_rng(42)
+    q = rng.integers(-7, 8, (2, 256))
+    out = linear.dequantize_weights(q, np.array([1.0], np.float32), "int4", "tensor", rot_group=16)
+    H = hadamard.regular_hadamard(16)
+    ref = np.concatenate([q[:, 16 * g:16 * g + 16] @ H.T for g in range(16)], axis=1) / 4.0
+    assert np.array_equal(_bf16_value(out), ref)
+
+
+def test_dequantize_adds_the_low_rank_delta():
+    rng = np.random.default_rng(43)
+    q = rng.integers(-7, 8, (4, 256))
+    up = rng.integers(-3, 4, (4, 2)).astype(np.float32)
+    down = rng.integers(-3, 4, (2, 256)).astype(np.float32)
+    to_bits = lambda a: (a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    out = linear.dequantize_weights(q, np.array([0.5], np.float32), "int4", "tensor", rot_group=0,
+                                    up_bits=to_bits(up), down_bits=to_bits(down))
+    assert np.array_equal(_bf16_value(out), q * 0.5 + up.astype(np.float64) @ down.astype(np.float64))
+
+
+def test_dequantize_inverts_quantization_within_its_error():
+    wb = wl.weight(44, 0, 128, 1024)
+    for rot in (256, 64):
+        r = linear.rotate_quantize(wb, rot, "int8", "row")
+        back = _bf16_value(linear.dequantize_weights(r["values"], r["scales"], "int8", "row", rot_group=rot))
+        w = _bf16_value(wb)
+        err = np.linalg.norm(back - w) / np.linalg.norm(w)
+        assert err < 0.01, err              # int8 per-row codes: about 0.4 % relative

@@ -15,7 +15,8 @@ import torch
 
 __all__ = [
     "ConvRotError", "lib", "Q", "GRAN", "OUT", "LAYOUT",
-    "convrot_rotate_quantize", "convrot_rotate_quantize_dual", "w4_pack_weights", "w4a4_gemm", "w4a8_gemm",
+    "convrot_rotate_quantize", "convrot_rotate_quantize_dual", "convrot_dequantize_weights", "w4_pack_weights",
+    "w4a4_gemm", "w4a8_gemm",
     "int8_tensorwise_gemm", "convrot_rq_workspace_size", "w4_packed_bytes",
     "get_counters", "reset_counters", "device_check", "status_string",
 ]
@@ -71,6 +72,7 @@ _SIGS = {
     "convrot_rotate_quantize": (_i, [_vp, _i64, _i64, _i64, _i, _i, _i, _i, _f, _vp, _i, _vp, _i,
                                      _vp, _i, _vp, _vp, _vp, _sz, _vp]),
     "convrot_rotate_quantize_dual": (_i, [_vp, _i64, _i64, _i64, _i, _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "convrot_dequantize_weights": (_i, [_vp, _vp, _vp, _i64, _i64, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp]),
     "w4_packed_bytes": (_sz, [_i64, _i64, _i, _i, _i, _i]),
     "w4_pack_weights": (_i, [_vp, _vp, _vp, _i64, _i64, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "w4a4_gemm": (_i, [_vp, _i, _vp, _i, _i, _f, _vp, _vp, _i, _vp, _vp, _i, _vp, _i, _vp,
@@ -209,6 +211,19 @@ def convrot_rotate_quantize_dual(x, rot_group=256, layout4=LAYOUT.NATURAL, codes
                                           _stream(stream))
     _check(st, "convrot_rotate_quantize_dual")
     return codes4, scale4, codes8, scale8
+
+
+def convrot_dequantize_weights(codes, scales, N, K, qtype=Q.SYM_INT4, gran=GRAN.TENSOR, q_group=0, rot_group=256,
+                               zeros=None, delta_up=None, delta_down=None, out=None, stream=None):
+    """Quantized weights (natural codes) -> bf16 [N, K] in the unrotated basis,
+    plus delta_up [N, R] @ delta_down [R, K] when given (the LoRA merge)."""
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=codes.device)
+    R = 0 if delta_up is None else delta_up.shape[1]
+    st = lib.convrot_dequantize_weights(_ptr(codes), _ptr(scales), _ptr(zeros), N, K, qtype, gran, q_group,
+                                        rot_group, _ptr(delta_up), _ptr(delta_down), R, _ptr(out), _stream(stream))
+    _check(st, "convrot_dequantize_weights")
+    return out
 
 
 def w4_pack_weights(codes, scales, N, K, qtype=Q.SYM_INT4, gran=GRAN.TENSOR, q_group=0, zeros=None,

@@ -221,6 +221,53 @@ cr_status convrot_rotate_quantize_dual(const void* x, int64_t rows, int64_t K, i
 }
 
 // ---------------------------------------------------------------------------
+// weight dequantization (LoRA merge)
+// ---------------------------------------------------------------------------
+cr_status convrot_dequantize_weights(const void* codes, const void* scales, const void* zeros, int64_t N, int64_t K,
+                                     cr_qtype qtype, cr_gran gran, int q_group, int rot_group,
+                                     const void* delta_up, const void* delta_down, int R, void* out,
+                                     hipStream_t stream) {
+  if (!codes || !scales || !out) return CR_ERR_INVALID_ARGUMENT;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(out)) return CR_ERR_INVALID_ARGUMENT;
+  if ((int)qtype < 0 || (int)qtype > 3 || (int)gran < 0 || (int)gran > 2) return CR_ERR_INVALID_ARGUMENT;
+  if (N < 1 || K < 256 || K % 256 || K > KMAX || N >= DIM_MAX) return CR_ERR_UNSUPPORTED_SHAPE;
+  if (rot_group != 0 && rot_group != 16 && rot_group != 64 && rot_group != 256 && rot_group != 1024)
+    return CR_ERR_UNSUPPORTED_FORMAT;
+  if (rot_group && K % rot_group) return CR_ERR_UNSUPPORTED_SHAPE;
+  if (qtype == CR_Q_SYM_INT4) {
+    if (gran == CR_GRAN_ROW_GROUP && q_group != 64) return CR_ERR_UNSUPPORTED_FORMAT;
+  } else if (qtype == CR_Q_SYM_INT8) {
+    if (gran == CR_GRAN_ROW_GROUP) return CR_ERR_UNSUPPORTED_FORMAT;
+  } else if (qtype == CR_Q_ASYM_UINT4) {
+    if (gran != CR_GRAN_ROW_GROUP || q_group != 16) return CR_ERR_UNSUPPORTED_FORMAT;
+    if (rot_group != 0 && rot_group != 256) return CR_ERR_UNSUPPORTED_FORMAT;
+    if (!zeros || !aligned16(zeros)) return CR_ERR_INVALID_ARGUMENT;
+  } else {
+    return CR_ERR_UNSUPPORTED_FORMAT;                 // activation-only format
+  }
+  if (delta_up || delta_down) {
+    if (!delta_up || !delta_down || R < 1 || R > 256) return CR_ERR_INVALID_ARGUMENT;
+    if (!aligned16(delta_up) || !aligned16(delta_down)) return CR_ERR_INVALID_ARGUMENT;
+  }
+  cr_status st = device_check();
+  if (st != CR_OK) return st;
+  cr::MergeParams p{};
+  p.codes = static_cast<const uint8_t*>(codes);
+  p.scales = scales;
+  p.zeros = static_cast<const uint8_t*>(zeros);
+  p.N = N;
+  p.K = K;
+  p.qtype = qtype;
+  p.gran = gran;
+  p.rot_group = rot_group;
+  p.up = static_cast<const uint16_t*>(delta_up);
+  p.down = static_cast<const uint16_t*>(delta_down);
+  p.R = delta_up ? R : 0;
+  p.out = static_cast<uint16_t*>(out);
+  return finish_launch(cr::launch_merge(p, stream), E_PACK, 1);
+}
+
+// ---------------------------------------------------------------------------
 // weight packing
 // ---------------------------------------------------------------------------
 size_t w4_packed_bytes(int64_t N, int64_t K, cr_qtype qtype, cr_gran gran, int q_group, int which) {

@@ -58,6 +58,19 @@ struct PackParams {
 };
 hipError_t launch_pack(const PackParams& p, hipStream_t s);
 
+struct MergeParams {
+  const uint8_t* codes;      // natural codes: int4 [N, K/2] (SYM_INT4, ASYM_UINT4) or int8 [N, K]
+  const void* scales;        // float32 [1] / [N] / [N, K/64]; fp16 [N, K/16] for ASYM_UINT4
+  const uint8_t* zeros;      // ASYM_UINT4: [N, K/32]
+  int64_t N, K;
+  int qtype, gran, rot_group;
+  const uint16_t* up;        // optional bf16 [N, R]
+  const uint16_t* down;      // bf16 [R, K]
+  int R;
+  uint16_t* out;             // bf16 [N, K]
+};
+hipError_t launch_merge(const MergeParams& p, hipStream_t s);
+
 enum ActKind { ACT_S4 = 0, ACT_U4 = 1, ACT_I8 = 2 };
 enum WgtKind { WGT_S4T = 0, WGT_I8N = 1 };
 
