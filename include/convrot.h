@@ -140,6 +140,15 @@ void convrot_reset_counters(void);
  *       rot 0:   SYM_INT4 with ROW_GROUP(64); UNSIGNED_INT4_SHIFT with ROW_GROUP(64)
  *       anything else returns CR_ERR_UNSUPPORTED_FORMAT.
  *   shift        UNSIGNED_INT4_SHIFT only: codes quantize v + shift (e.g. 0.171875)
+ *   smooth       optional float32 [K]: per-channel multiplier applied to x first,
+ *                v = fl(x * smooth[k]), before the shift and the rotation (the
+ *                smoothing factor of "Qwen-Image-Edit-2511 INT4 (ComfyUI
+ *                Optimized)", Key Technical Optimizations, shared by split
+ *                projections; the caller passes the multiplier the activation
+ *                needs, the weight columns carry its inverse). Supported without
+ *                rotation, and with the 256 rotation for ROW / ROW_GROUP(64)
+ *                scales; elsewhere CR_ERR_UNSUPPORTED_FORMAT. The low-rank
+ *                down-projection reads the unsmoothed input.
  *   lora_down    optional bf16 [R, K], R = 32 or 64 (not with ASYM_UINT4): also
  *                writes lora_act[m, r] = sum_k x[m, k] * lora_down[r, k] (float32
  *                accumulation of the unshifted, unrotated input), stored as
@@ -172,7 +181,7 @@ size_t convrot_rq_workspace_size(int64_t rows, int64_t K, int rot_group,
 
 cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx,
                                   int rot_group, cr_qtype qtype, cr_gran gran, int q_group,
-                                  float shift,
+                                  float shift, const float* smooth,
                                   const void* lora_down, int R, void* lora_act, int lora_act_f32,
                                   void* codes, cr_layout layout, void* scales, void* zeros,
                                   void* workspace, size_t workspace_bytes,

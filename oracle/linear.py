@@ -53,8 +53,12 @@ def _bf16_round(x: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def rotate_quantize(x_bits: np.ndarray, rot_group: int, qtype: str, gran: str,
-                    q_group: int | None = None, shift: float = 0.0):
-    """x_bits: bf16 bit patterns [rows, K].
+                    q_group: int | None = None, shift: float = 0.0, smooth: np.ndarray | None = None):
+    """x_bits: bf16 bit patterns [rows, K]. smooth: optional float32 [K]
+    per-channel multiplier applied to the input before anything else,
+    v = fl(x * smooth[k]) (the smoothing factor of [P3] Key Technical
+    Optimizations, given as the multiplier the activation needs; the matching
+    weight columns carry its inverse offline).
     qtype: 'int4' | 'int8' | 'uint4_shift' | 'asym_u4'.
     Returns a dict with
       'values' : the codes as integers [rows, K]
@@ -64,6 +68,8 @@ def rotate_quantize(x_bits: np.ndarray, rot_group: int, qtype: str, gran: str,
       'zeros'  : asym_u4 only, uint8 [rows, K/16] (one per group) and
       'zeros_packed' : [rows, K/32] two per byte."""
     x = _f32(x_bits)
+    if smooth is not None:
+        x = (x * np.asarray(smooth, dtype=np.float32)[None, :]).astype(np.float32)
     if rot_group:
         v = hadamard.rotate(x, rot_group)
         post = np.float32(1.0 / np.sqrt(rot_group))          # exact power of two

@@ -71,9 +71,9 @@ def test_device_check_reports_no_device_here(cr):
 
 
 def _rq(cr, x=A, rows=64, K=512, ldx=512, rot=256, q=0, g=0, qg=0, lora=None, R=0, la=None,
-        codes=A, scales=A, zeros=None, ws=A, wsb=1 << 20, layout=0):
-    return cr.lib.convrot_rotate_quantize(_p(x), rows, K, ldx, rot, q, g, qg, 0.0, _p(lora), R, _p(la), 0,
-                                          _p(codes), layout, _p(scales), _p(zeros), _p(ws), wsb, None)
+        codes=A, scales=A, zeros=None, ws=A, wsb=1 << 20, layout=0, smooth=None):
+    return cr.lib.convrot_rotate_quantize(_p(x), rows, K, ldx, rot, q, g, qg, 0.0, _p(smooth), _p(lora), R, _p(la),
+                                          0, _p(codes), layout, _p(scales), _p(zeros), _p(ws), wsb, None)
 
 
 def test_rq_validation(cr):
@@ -102,6 +102,12 @@ def test_rq_validation(cr):
     assert _rq(cr, wsb=0) == 6                               # TENSOR needs workspace
     assert _rq(cr, q=1, layout=1) == 3                       # tiled layout is for int4 codes
     assert _rq(cr, layout=2) == 1
+    assert _rq(cr, smooth=A, g=1) == 4                       # smoothing: rotation 256 with row scales
+    assert _rq(cr, smooth=A, g=2, qg=64) == 4
+    assert _rq(cr, smooth=A) == 3                            # not with per-tensor scales
+    assert _rq(cr, smooth=A, rot=64, g=1) == 3               # nor other rotation sizes
+    assert _rq(cr, smooth=A + 4, g=1) == 1                   # misaligned
+    assert _rq(cr, smooth=A, rot=0, g=2, qg=64, ws=None, wsb=0) == 4
     assert _rq(cr, layout=1) == 4
     assert _rq(cr) == 4                                      # valid -> device check (no GPU here)
     assert _rq(cr, rot=0, g=2, qg=64, ws=None, wsb=0) == 4

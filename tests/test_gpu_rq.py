@@ -183,6 +183,34 @@ def test_lora_merge_round_trip(cr):
     assert np.array_equal(bytes_of(packed), r1["tiles"].reshape(-1))
 
 
+SMOOTH_CASES = [(256, "int4", "row"), (256, "int8", "row_group"), (256, "int8", "row"), (0, "int4", "row_group"),
+                (0, "uint4_shift", "row_group")]
+
+
+@pytest.mark.parametrize("case", SMOOTH_CASES)
+@pytest.mark.parametrize("shape", [(37, 3072), (300, 1024)])
+def test_rotate_quantize_smoothing(cr, case, shape):
+    """A per-channel smoothing multiplier before the rotation (and before the
+    unsigned shift): codes and scales bit-exact against the oracle."""
+    rot, qt, gran = case
+    rows, K = shape
+    say(f"rq smooth {case} {shape}")
+    g = np.random.default_rng(rows + K + rot)
+    m = (g.random(K) * 1.5 + 0.25).astype(np.float32)
+    if qt == "uint4_shift":
+        xb = wl.gelu_activation(24, rows + K, rows, K)
+    else:
+        xb = wl.activation(24, rows + K, rows, K, n_outliers=5, outlier_scale=20.0)
+    qg = 64 if gran == "row_group" else 0
+    shift = 0.171875 if qt == "uint4_shift" else 0.0
+    ref = ol.rotate_quantize(xb, rot, qt, gran, qg or None, shift, smooth=m)
+    QQ = {"int4": 0, "int8": 1, "uint4_shift": 2}[qt]
+    codes, scales, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), rot, QQ, GR[gran], qg, shift=shift, smooth=dev(m))
+    assert np.array_equal(host(codes).reshape(ref["codes"].shape).view(np.uint8), ref["codes"].view(np.uint8))
+    assert np.array_equal(host(scales).reshape(-1).view(np.uint32),
+                          np.asarray(ref["scales"], np.float32).reshape(-1).view(np.uint32))
+
+
 def test_rotate_quantize_strided_rows_and_zero_rows(cr):
     rows, K, ldx = 40, 1024, 1024 + 64
     xb = wl.activation(12, 0, rows, ldx)

@@ -262,3 +262,45 @@ def test_dequantize_inverts_quantization_within_its_error():
         w = _bf16_value(wb)
         err = np.linalg.norm(back - w) / np.linalg.norm(w)
         assert err < 0.01, err              # int8 per-row codes: about 0.4 % relative
+
+
+# ---------------------------------------------------------------------------
+# smoothing vector
+# ---------------------------------------------------------------------------
+
+def test_smoothing_by_ones_changes_nothing():
+    xb = wl.activation(45, 0, 16, 512)
+    a = linear.rotate_quantize(xb, 256, "int4", "row")
+    b = linear.rotate_quantize(xb, 256, "int4", "row", smooth=np.ones(512, np.float32))
+    assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["scales"], b["scales"])
+
+
+def test_smoothing_by_powers_of_two_scales_each_channel():
+    # a power-of-two multiplier per channel is exact: smoothing x equals
+    # quantizing the bf16 tensor x * m built directly, channel by channel
+    xb = wl.activation(46, 0, 8, 512)
+    m = (2.0 ** np.random.default_rng(3).integers(-3, 4, 512)).astype(np.float32)
+    x = linear._f32(xb) * m[None, :]
+    xm = (x.view(np.uint32) >> 16).astype(np.uint16)             # exact: bf16 times 2^j
+    for rot, gran, qg in ((256, "row", None), (0, "row_group", 64)):
+        a = linear.rotate_quantize(xb, rot, "int4", gran, qg, smooth=m)
+        b = linear.rotate_quantize(xm, rot, "int4", gran, qg)
+        assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["scales"], b["scales"])
+
+
+def test_smoothing_with_inverse_on_weights_preserves_the_product():
+    # (x diag(m)) (W diag(1/m))^T = x W^T: with m a power of two per channel
+    # the float products are equal up to the quantization of each side
+    xb = wl.activation(47, 0, 32, 512)
+    wb = wl.weight(47, 1, 128, 512)
+    m = (2.0 ** np.random.default_rng(4).integers(-2, 3, 512)).astype(np.float32)
+    w = linear._f32(wb) / m[None, :]
+    wm = (w.view(np.uint32) >> 16).astype(np.uint16)
+    ref = linear.float_linear(xb, wb)
+    xa = linear.rotate_quantize(xb, 256, "int8", "row", smooth=m)
+    wq = linear.rotate_quantize(wm, 256, "int8", "row")
+    y = linear.epilogue_scalar(gemm.int_gemm(xa["values"], wq["values"]), xa["scales"], "row",
+                               wq["scales"], "row")
+    # quantization error of a few percent; a multiplier on the wrong axis (or a
+    # missing inverse) would leave an error of order one
+    assert np.linalg.norm(y - ref) / np.linalg.norm(ref) < 0.1

@@ -69,7 +69,7 @@ _SIGS = {
     "convrot_get_counters": (None, [ctypes.POINTER(_Counters)]),
     "convrot_reset_counters": (None, []),
     "convrot_rq_workspace_size": (_sz, [_i64, _i64, _i, _i, _i, _i]),
-    "convrot_rotate_quantize": (_i, [_vp, _i64, _i64, _i64, _i, _i, _i, _i, _f, _vp, _i, _vp, _i,
+    "convrot_rotate_quantize": (_i, [_vp, _i64, _i64, _i64, _i, _i, _i, _i, _f, _vp, _vp, _i, _vp, _i,
                                      _vp, _i, _vp, _vp, _vp, _sz, _vp]),
     "convrot_rotate_quantize_dual": (_i, [_vp, _i64, _i64, _i64, _i, _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "convrot_dequantize_weights": (_i, [_vp, _vp, _vp, _i64, _i64, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp]),
@@ -150,7 +150,7 @@ def _scale_numel(rows, K, qtype, gran, q_group):
 def convrot_rotate_quantize(x, rot_group=256, qtype=Q.SYM_INT4, gran=GRAN.TENSOR, q_group=0,
                             shift=0.0, lora_down=None, lora_act_f32=False, layout=LAYOUT.NATURAL,
                             codes=None, scales=None, zeros=None, lora_act=None, workspace=None,
-                            stream=None):
+                            stream=None, smooth=None):
     """x: bf16 [rows, K] (row stride may exceed K). Returns
     (codes, scales, zeros, lora_act); outputs are allocated when not given.
     Tiled int4 codes come back as uint8 [ceil(rows/16), K/64, 512]."""
@@ -180,7 +180,7 @@ def convrot_rotate_quantize(x, rot_group=256, qtype=Q.SYM_INT4, gran=GRAN.TENSOR
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.convrot_rotate_quantize(_ptr(x), rows, K, ldx, rot_group, qtype, gran, q_group,
-                                     float(shift), _ptr(lora_down), R, _ptr(lora_act),
+                                     float(shift), _ptr(smooth), _ptr(lora_down), R, _ptr(lora_act),
                                      int(bool(lora_act_f32)), _ptr(codes), int(layout), _ptr(scales), _ptr(zeros),
                                      _ptr(workspace), wsb, _stream(stream))
     _check(st, "convrot_rotate_quantize")

@@ -148,7 +148,7 @@ size_t convrot_rq_workspace_size(int64_t rows, int64_t K, int rot_group, cr_qtyp
 }
 
 cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx, int rot_group,
-                                  cr_qtype qtype, cr_gran gran, int q_group, float shift,
+                                  cr_qtype qtype, cr_gran gran, int q_group, float shift, const float* smooth,
                                   const void* lora_down, int R, void* lora_act, int lora_act_f32,
                                   void* codes, cr_layout layout, void* scales, void* zeros, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
@@ -158,6 +158,12 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
   if ((int)layout < 0 || (int)layout > 1) return CR_ERR_INVALID_ARGUMENT;
   if (layout == CR_LAYOUT_TILED && !(qtype == CR_Q_SYM_INT4 || qtype == CR_Q_UNSIGNED_INT4_SHIFT))
     return CR_ERR_UNSUPPORTED_FORMAT;
+  if (smooth) {   // without rotation, or the 256 rotation with per-row / per-64-group scales
+    if (!aligned16(smooth)) return CR_ERR_INVALID_ARGUMENT;
+    if (rot_group != 0 && !(rot_group == 256 && (gran == CR_GRAN_ROW || gran == CR_GRAN_ROW_GROUP) &&
+                            (qtype == CR_Q_SYM_INT4 || qtype == CR_Q_SYM_INT8)))
+      return CR_ERR_UNSUPPORTED_FORMAT;
+  }
   const size_t need = convrot_rq_workspace_size(rows, K, rot_group, qtype, gran, q_group);
   if (need > 0) {
     if (!workspace || !aligned16(workspace)) return CR_ERR_INVALID_ARGUMENT;
@@ -175,6 +181,7 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
   p.gran = gran;
   p.q_group = q_group;
   p.shift = shift;
+  p.smooth = smooth;
   p.lora_down = static_cast<const uint16_t*>(lora_down);
   p.R = R;
   p.lora_act = lora_act;

@@ -28,6 +28,7 @@ struct RQParams {
   int tiled;            // int4 codes in the [rows/16][K/64][512 B] fragment layout
   void* codes8;         // dual output: int8 codes [rows, K] (codes / scales hold the int4 set)
   void* scales8;
+  const float* smooth;  // optional per-channel multiplier [K] applied to x first
 };
 
 struct RQGeometry {

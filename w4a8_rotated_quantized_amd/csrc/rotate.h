@@ -115,14 +115,25 @@ CR_DEV void butterflies(float (&v)[16], const LaneRot& lr) {
 // bf16 words (2 x 16 bytes = elements 0..15 of this lane) -> the same stages.
 // NEG negates the chunk first (NR = 1024: the digit (b9 b8) of D for chunk 0
 // of each group).
-template <int NR, bool NEG = false>
-CR_DEV void rotate_group(const u32x4 (&w)[2], const LaneRot& lr, float (&v)[16]) {
+// SM: multiply by the per-channel factors sm[0..15] of these elements first
+// (one float32 rounding per element, before any butterfly).
+template <int NR, bool NEG = false, bool SM = false>
+CR_DEV void rotate_group(const u32x4 (&w)[2], const LaneRot& lr, float (&v)[16], const float* sm = nullptr) {
+  v4f m[4];
+  if constexpr (SM) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m[q] = reinterpret_cast<const v4f*>(sm)[q];
+  }
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = 8 * h + 2 * j;
       float lo = bf16_lo(w[h][j]), hi = bf16_hi(w[h][j]);
+      if constexpr (SM) {
+        lo = __fmul_rn(lo, m[e >> 2][e & 3]);
+        hi = __fmul_rn(hi, m[(e + 1) >> 2][(e + 1) & 3]);
+      }
       v[e] = (dreg_neg(e) != NEG) ? -lo : lo;
       v[e + 1] = (dreg_neg(e + 1) != NEG) ? -hi : hi;
     }

@@ -97,9 +97,10 @@ CR_DEV uint8_t* code_dst(const RQParams& a, int64_t row, int grp, int gL) {
 // ---------------------------------------------------------------------------
 enum { RG_ROW = 2, RG_G64 = 3, RG_ASYM = 4 };
 
-template <int QT, int GR, int GPS, int NR>
+template <int QT, int GR, int GPS, int NR, bool SM = false>
 __global__ __launch_bounds__(256) void rq_rot_kernel(RQParams a) {
   static_assert(GR != RG_ASYM || NR == 256, "asymmetric g16 weights use the 256 rotation");
+  static_assert(!SM || NR != 1024, "smoothing with the 1024 rotation is not built");
   static_assert(NR != 1024 || GPS % 4 == 0, "a 1024-group is four chunks of one segment");
   __shared__ unsigned rowmax[16];
   const int tid = threadIdx.x;
@@ -137,8 +138,14 @@ __global__ __launch_bounds__(256) void rq_rot_kernel(RQParams a) {
   float v[GPS][16];
 #pragma unroll
   for (int i = 0; i < GPS; ++i) {
-    if (NR == 1024 && chunk_neg(i)) rotate_group<NR, true>(w[i], lr, v[i]);
-    else rotate_group<NR>(w[i], lr, v[i]);
+    if constexpr (SM) {
+      const int grp = min(g0 + gstep * i, a.G - 1);
+      rotate_group<NR, false, true>(w[i], lr, v[i], a.smooth + grp * 256 + lr.gL * 16);
+    } else if (NR == 1024 && chunk_neg(i)) {
+      rotate_group<NR, true>(w[i], lr, v[i]);
+    } else {
+      rotate_group<NR>(w[i], lr, v[i]);
+    }
   }
   if constexpr (NR == 1024) bfly_chunks<GPS>(v);
   // quantization multiplier sign of chunk i (lane sign, and D's chunk digit for 1024)
@@ -354,7 +361,7 @@ __global__ __launch_bounds__(256) void rq_tensor_kernel(RQParams a) {
 // slice. Lane l: row l%16, 8-element chunk l/16 of each 32-column half; this
 // is also the A-operand layout of the 16x16x32 bf16 MFMA used for LoRA-down.
 // ---------------------------------------------------------------------------
-template <bool UNSIGNED, bool LORA, int R = 32, bool QUANT = true>
+template <bool UNSIGNED, bool LORA, int R = 32, bool QUANT = true, bool SM = false>
 __global__ __launch_bounds__(256) void rq_plain_kernel(RQParams a) {
   static_assert(R == 32 || R == 64, "low-rank branch of rank 32 or 64");
   static_assert(QUANT || LORA, "nothing to do");
@@ -386,6 +393,18 @@ __global__ __launch_bounds__(256) void rq_plain_kernel(RQParams a) {
       v[2 * j + 1] = bf16_hi(w0[j]);
       v[8 + 2 * j] = bf16_lo(w1[j]);
       v[8 + 2 * j + 1] = bf16_hi(w1[j]);
+    }
+    if constexpr (SM) {   // elements t*64 + c*8 + 0..7 and t*64 + 32 + c*8 + 0..7
+      const v4f* m0 = reinterpret_cast<const v4f*>(a.smooth + t * 64 + c * 8);
+      const v4f* m1 = reinterpret_cast<const v4f*>(a.smooth + t * 64 + 32 + c * 8);
+      const v4f ma = m0[0], mb = m0[1], mc = m1[0], md = m1[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = __fmul_rn(v[e], ma[e]);
+        v[4 + e] = __fmul_rn(v[4 + e], mb[e]);
+        v[8 + e] = __fmul_rn(v[8 + e], mc[e]);
+        v[12 + e] = __fmul_rn(v[12 + e], md[e]);
+      }
     }
     if (LORA) {
       // la += X[16 rows, 64 cols] @ L2^T[64 cols, R ranks]
@@ -602,6 +621,32 @@ static hipError_t launch_rotated(RQParams p, hipStream_t s) {
   RQGeometry g = rq_geometry(p.rows, p.K, kind, NR);
   p.lg_spr = g.lg_spr;
   p.rpb = g.rpb;
+  if constexpr (NR == 256) {
+    if (p.smooth) {   // 1 or 4 chunks per segment (the choice the 16 / 64 rotations make)
+      g = rq_geometry(p.rows, p.K, kind, 16);
+      p.lg_spr = g.lg_spr;
+      p.rpb = g.rpb;
+      const dim3 grid((unsigned)g.gy, (unsigned)g.gx);
+      if (g.gps == 4) {
+        if (kind == RG_ROW) {
+          if (p.qtype == CR_Q_SYM_INT4) hipLaunchKernelGGL((rq_rot_kernel<CR_Q_SYM_INT4, RG_ROW, 4, 256, true>), grid, dim3(256), 0, s, p);
+          else hipLaunchKernelGGL((rq_rot_kernel<CR_Q_SYM_INT8, RG_ROW, 4, 256, true>), grid, dim3(256), 0, s, p);
+        } else {
+          if (p.qtype == CR_Q_SYM_INT4) hipLaunchKernelGGL((rq_rot_kernel<CR_Q_SYM_INT4, RG_G64, 4, 256, true>), grid, dim3(256), 0, s, p);
+          else hipLaunchKernelGGL((rq_rot_kernel<CR_Q_SYM_INT8, RG_G64, 4, 256, true>), grid, dim3(256), 0, s, p);
+        }
+      } else {
+        if (kind == RG_ROW) {
+          if (p.qtype == CR_Q_SYM_INT4) hipLaunchKernelGGL((rq_rot_kernel<CR_Q_SYM_INT4, RG_ROW, 1, 256, true>), grid, dim3(256), 0, s, p);
+          else hipLaunchKernelGGL((rq_rot_kernel<CR_Q_SYM_INT8, RG_ROW, 1, 256, true>), grid, dim3(256), 0, s, p);
+        } else {
+          if (p.qtype == CR_Q_SYM_INT4) hipLaunchKernelGGL((rq_rot_kernel<CR_Q_SYM_INT4, RG_G64, 1, 256, true>), grid, dim3(256), 0, s, p);
+          else hipLaunchKernelGGL((rq_rot_kernel<CR_Q_SYM_INT8, RG_G64, 1, 256, true>), grid, dim3(256), 0, s, p);
+        }
+      }
+      return hipGetLastError();
+    }
+  }
   if (kind == RG_ROW) {
     if (p.qtype == CR_Q_SYM_INT4) return launch_rot_gps<CR_Q_SYM_INT4, RG_ROW, NR>(p, g, s);
     return launch_rot_gps<CR_Q_SYM_INT8, RG_ROW, NR>(p, g, s);
@@ -630,20 +675,24 @@ hipError_t launch_rotate_quantize_dual(RQParams p, hipStream_t s) {
   }
 }
 
+template <bool UNSIGNED, bool SM>
+static hipError_t launch_plain(const RQParams& p, int nblk, bool lora, hipStream_t s) {
+  if (!lora) hipLaunchKernelGGL((rq_plain_kernel<UNSIGNED, false, 32, true, SM>), dim3(nblk), dim3(256), 0, s, p);
+  else if (p.R == 64) hipLaunchKernelGGL((rq_plain_kernel<UNSIGNED, true, 64, true, SM>), dim3(nblk), dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((rq_plain_kernel<UNSIGNED, true, 32, true, SM>), dim3(nblk), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_rotate_quantize(RQParams p, hipStream_t s) {
   const int nblk = (int)((p.rows + 15) / 16);
   const bool lora = p.lora_down != nullptr;
   if (p.rot_group == 0) {
-    if (p.qtype == CR_Q_UNSIGNED_INT4_SHIFT) {
-      if (!lora) hipLaunchKernelGGL((rq_plain_kernel<true, false>), dim3(nblk), dim3(256), 0, s, p);
-      else if (p.R == 64) hipLaunchKernelGGL((rq_plain_kernel<true, true, 64>), dim3(nblk), dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((rq_plain_kernel<true, true, 32>), dim3(nblk), dim3(256), 0, s, p);
-    } else {
-      if (!lora) hipLaunchKernelGGL((rq_plain_kernel<false, false>), dim3(nblk), dim3(256), 0, s, p);
-      else if (p.R == 64) hipLaunchKernelGGL((rq_plain_kernel<false, true, 64>), dim3(nblk), dim3(256), 0, s, p);
-      else hipLaunchKernelGGL((rq_plain_kernel<false, true, 32>), dim3(nblk), dim3(256), 0, s, p);
+    if (p.smooth) {
+      if (p.qtype == CR_Q_UNSIGNED_INT4_SHIFT) return launch_plain<true, true>(p, nblk, lora, s);
+      return launch_plain<false, true>(p, nblk, lora, s);
     }
-    return hipGetLastError();
+    if (p.qtype == CR_Q_UNSIGNED_INT4_SHIFT) return launch_plain<true, false>(p, nblk, lora, s);
+    return launch_plain<false, false>(p, nblk, lora, s);
   }
   p.G = (int)(p.K / 256);
   hipError_t e;
