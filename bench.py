@@ -13,14 +13,20 @@ Every step uses a different copy of all buffers (inputs, weights, codes,
 outputs; ~10 copies, over 2x the 256 MB last-level cache), so each step
 reads cold HBM data.
 
+The INT4 codes travel as fp6 E2M3 values and the GEMMs run on the fp6
+matrix cores (exact: see gemm_f6.hip); `--cores int8` runs the int8-core
+path instead (int4 tile-packed codes widened to bytes).
+
 Metric: effective TOPS = sum 2*M*N*K / step time (the fused
 rotate+quantize+W4 GEMM throughput), also given as % of the 5.0 POP/s dense
 INT8 matrix peak. The roofline object reports the dominant kernel (the
-M=4096 GEMM) against that peak; its duration comes from HIP events around
-each of its launches on the launch stream. The CPU baseline is the numpy
-oracle running the same step on this host.
+M=4096 GEMM) against the dense peak of the matrix instruction it runs on
+(fp6: 10.1 PFLOP/s; int8: 5.0 POP/s); its duration comes from HIP events
+around each of its launches on the launch stream. The CPU baseline is the
+numpy oracle running the same step on this host.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--rot-group 256] [--workload c2|c1|c3|c4|c5|c2a8]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--rot-group 256] [--cores fp6|int8]
+                       [--workload c2|c1|c3|c4|c5|c2a8]
 (--workload other than c2 prints that workload's throughput line instead;
 see bench_workloads.py)
 """
@@ -35,10 +41,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0       # MI355X dense INT8 matrix peak (5.0 POP/s)
+FP6_PEAK_TOPS = 10100.0       # MI355X dense fp6 / fp4 matrix peak (10.1 PFLOP/s)
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 M_BIG, M_SMALL, N, K = 4096, 32, 3072, 3072
 ROT = 256          # ConvRot group size (--rot-group: 16, 64, 256 or 1024)
-GEMM_SOURCES = ["gemm_w4a4.hip", "epilogue.h", "common.h", "kernels.h"]
+CORES = "fp6"      # matrix cores of the W4A4 GEMMs (--cores)
+GEMM_SOURCES = {"fp6": ["gemm_f6.hip", "epilogue.h", "common.h", "kernels.h"],
+                "int8": ["gemm_w4a4.hip", "epilogue.h", "common.h", "kernels.h"]}
+TRAFFIC_PROFILE = {"fp6": "w4a4_f6_gemm_m4096_n3072_k3072_traffic.json",
+                   "int8": "w4a4_gemm_m4096_n3072_k3072_traffic.json"}
 
 
 def parse():
@@ -50,6 +61,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--rot-group", type=int, default=256, choices=(16, 64, 256, 1024),
                     help="ConvRot group size of the c2 line (256 is the configuration the metric is quoted on)")
+    ap.add_argument("--cores", default="fp6", choices=("fp6", "int8"),
+                    help="matrix cores of the W4A4 GEMMs: fp6 (E2M3 codes, default) or int8 (widened int4)")
     ap.add_argument("--workload", default="c2",
                     help="c2 (default: the headline line), or c1 / c3 / c4 / c5 / c2a8 / merge for the other workloads' "
                          "throughput lines (bench_workloads.py)")
@@ -67,12 +80,12 @@ def source_sha(names):
 def traffic_from_profile():
     """HBM bytes per launch of the dominant kernel, from the committed
     rocprofv3 counter summary, only if the kernel source is unchanged."""
-    p = os.path.join(ROOT, "profiles", "w4a4_gemm_m4096_n3072_k3072_traffic.json")
+    p = os.path.join(ROOT, "profiles", TRAFFIC_PROFILE[CORES])
     if not os.path.exists(p):
         return None
     with open(p) as f:
         d = json.load(f)
-    if d.get("source_sha") != source_sha(GEMM_SOURCES):
+    if d.get("source_sha") != source_sha(GEMM_SOURCES[CORES]):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -125,7 +138,12 @@ def setup(dev, nbytes_target=600e6):
     wb = wl.weight(2, 1, N, K)
     w = bf16(wb)
     wc, ws, _, _ = cr.convrot_rotate_quantize(w, ROT, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
-    wp, _, _, _ = cr.w4_pack_weights(wc, ws, N, K, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
+    if CORES == "fp6":
+        wp = cr.w4_pack_weights_f6(wc, N, K)
+        code_shape = lambda m: ((m + 31) // 32, K // 64, 1536)   # noqa: E731
+    else:
+        wp, _, _, _ = cr.w4_pack_weights(wc, ws, N, K, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
+        code_shape = lambda m: ((m + 15) // 16, K // 64, 512)    # noqa: E731
     per_set = M_BIG * K * 2 + M_BIG * K // 2 + M_BIG * N * 2 + N * K // 2
     nsets = max(2, int(np.ceil(nbytes_target / per_set)))
     sets = []
@@ -133,8 +151,8 @@ def setup(dev, nbytes_target=600e6):
     for _ in range(nsets):
         sets.append({
             "xb": xbig0.clone(), "xs": xsmall0.clone(), "wp": wp.clone(), "ws": ws.clone(),
-            "cb": torch.empty(((M_BIG + 15) // 16, K // 64, 512), dtype=torch.uint8, device=dev),
-            "cs": torch.empty(((M_SMALL + 15) // 16, K // 64, 512), dtype=torch.uint8, device=dev),
+            "cb": torch.empty(code_shape(M_BIG), dtype=torch.uint8, device=dev),
+            "cs": torch.empty(code_shape(M_SMALL), dtype=torch.uint8, device=dev),
             "sb": torch.empty(1, dtype=torch.float32, device=dev),
             "ss": torch.empty(1, dtype=torch.float32, device=dev),
             "wsb": torch.empty(cr.convrot_rq_workspace_size(M_BIG, K, ROT, 0, 0), dtype=torch.uint8, device=dev),
@@ -145,8 +163,12 @@ def setup(dev, nbytes_target=600e6):
     return sets
 
 
+def _layout(cr):
+    return cr.LAYOUT.F6 if CORES == "fp6" else cr.LAYOUT.TILED
+
+
 def rq_big(cr, s):
-    cr.convrot_rotate_quantize(s["xb"], ROT, 0, 0, layout=cr.LAYOUT.TILED, codes=s["cb"], scales=s["sb"],
+    cr.convrot_rotate_quantize(s["xb"], ROT, 0, 0, layout=_layout(cr), codes=s["cb"], scales=s["sb"],
                                workspace=s["wsb"])
 
 
@@ -155,7 +177,7 @@ def gemm_big(cr, s):
 
 
 def rq_small(cr, s):
-    cr.convrot_rotate_quantize(s["xs"], ROT, 0, 0, layout=cr.LAYOUT.TILED, codes=s["cs"], scales=s["ss"],
+    cr.convrot_rotate_quantize(s["xs"], ROT, 0, 0, layout=_layout(cr), codes=s["cs"], scales=s["ss"],
                                workspace=s["wss"])
 
 
@@ -164,9 +186,10 @@ def gemm_small(cr, s):
 
 
 def main():
-    global ROT
+    global ROT, CORES
     args = parse()
     ROT = args.rot_group
+    CORES = args.cores
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path has no multi-GPU part); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -175,7 +198,7 @@ def main():
     if args.workload != "c2":
         import bench_workloads
         for name in args.workload.split(","):
-            bench_workloads.run(name, args.steps, args.warmup)
+            bench_workloads.run(name, args.steps, args.warmup, cores=args.cores)
         return
 
     import numpy as np
@@ -241,6 +264,7 @@ def main():
     rq_gbs = rq_bytes / (t_rq_big * 1e-3) / 1e9
     small_bytes = N * K // 2 + M_SMALL * K // 2 + M_SMALL * N * 2
     traffic = traffic_from_profile()
+    peak = FP6_PEAK_TOPS if CORES == "fp6" else INT8_PEAK_TOPS
 
     line = {
         "metric": "effective TOPS of fused rotate+quant+W4 GEMM (% INT8 MFMA peak); GB/s",
@@ -258,7 +282,7 @@ def main():
         "config": {"workload": f"MMDiT projection, W4A4 tensorwise ConvRot group {ROT}, "
                                "X bf16 [M, 3072] (M = 4096 and 32), W [3072, 3072]",
                    "M": [M_BIG, M_SMALL], "N": N, "K": K, "rot_group": ROT,
-                   "buffer_sets": nsets},
+                   "matrix_cores": CORES, "buffer_sets": nsets},
         "pct_int8_peak": round(100.0 * eff_tops / INT8_PEAK_TOPS, 2),
         "kernels_us": {"rq_m4096": round(t_rq_big * 1e3, 2), "gemm_m4096": round(t_gemm_big * 1e3, 2),
                        "rq_m32": round(t_rq_small * 1e3, 2), "gemm_m32": round(t_gemm_small * 1e3, 2)},
@@ -266,8 +290,8 @@ def main():
         "rq_m4096_pct_hbm": round(100.0 * rq_gbs / HBM_PEAK_GBS, 1),
         "gemm_m4096_TOPS": round(gemm_tops, 1),
         "gemm_m32_GBps": round(small_bytes / (t_gemm_small * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": INT8_PEAK_TOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(gemm_tops / peak, 4),
                      "traffic": traffic},
     }
     if not args.no_cpu:

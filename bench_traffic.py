@@ -1,5 +1,7 @@
-"""HBM traffic of the benchmark's dominant kernel (the M=4096 W4A4 GEMM),
-from rocprofv3 counters, calibrated against a plain copy kernel.
+"""HBM traffic of the benchmark's dominant kernel (the M=4096 W4A4 GEMM,
+on the fp6 matrix cores by default, or the int8-core kernel with a trailing
+`int8` argument), from rocprofv3 counters, calibrated against a plain copy
+kernel.
 
 Two subcommands:
 
@@ -11,7 +13,8 @@ Two subcommands:
              `rocprofv3 --pmc WRITE_SIZE` (one counter group per pass).
 
   summarize  reads the two counter CSVs and writes
-             profiles/w4a4_gemm_m4096_n3072_k3072_traffic.json (read by
+             profiles/w4a4_f6_gemm_m4096_n3072_k3072_traffic.json (int8:
+             profiles/w4a4_gemm_m4096_n3072_k3072_traffic.json; read by
              bench.py for roofline.traffic) and a short .md summary.
 
 FETCH_SIZE and WRITE_SIZE (KiB per dispatch) count L2 <-> memory-fabric
@@ -37,8 +40,11 @@ import bench  # noqa: E402
 
 COPY_MIB = 256
 LAUNCHES = 10
-OUT_JSON = os.path.join(ROOT, "profiles", "w4a4_gemm_m4096_n3072_k3072_traffic.json")
-OUT_MD = os.path.join(ROOT, "profiles", "w4a4_gemm_m4096_n3072_k3072_traffic.md")
+KERNEL = {"fp6": "gemm_f6_kernel", "int8": "gemm_w4a4"}
+
+
+def _out(ext):
+    return os.path.join(ROOT, "profiles", bench.TRAFFIC_PROFILE[bench.CORES].replace(".json", ext))
 
 
 def run():
@@ -73,7 +79,7 @@ def _read(dirname, counter):
         name = r["Kernel_Name"]
         if "neg_kernel" in name or ("elementwise" in name and "neg" in name.lower()):
             copy.append(v)
-        elif "gemm_w4a4" in name:
+        elif KERNEL[bench.CORES] in name:
             gemm.append(v)
     if not copy or not gemm:
         raise SystemExit(f"{counter}: copy or GEMM dispatches missing in {f[0]}")
@@ -89,10 +95,13 @@ def summarize(dfetch, dwrite):
     kw = sorted(cw)[len(cw) // 2] / copy_bytes
     fetch = sum(gf) / len(gf) / kf
     write = sum(gw) / len(gw) / kw
-    alg = bench.M_BIG * bench.K // 2 + bench.N * bench.K // 2 + bench.M_BIG * bench.N * 2
+    code_bytes = (3 * bench.K // 4) if bench.CORES == "fp6" else bench.K // 2   # per row: fp6 or int4 codes
+    alg = bench.M_BIG * code_bytes + bench.N * code_bytes + bench.M_BIG * bench.N * 2
+    kname = ("gemm_f6_kernel<256, 192, ...> (fp6 E2M3 operands)" if bench.CORES == "fp6"
+             else "gemm_w4a4_lds_kernel (int4 operands widened to int8)")
     d = {
-        "kernel": "gemm_w4a4_lds_kernel (M=4096, N=3072, K=3072, tensorwise, bf16 out)",
-        "source_sha": bench.source_sha(bench.GEMM_SOURCES),
+        "kernel": f"{kname} (M=4096, N=3072, K=3072, tensorwise, bf16 out)",
+        "source_sha": bench.source_sha(bench.GEMM_SOURCES[bench.CORES]),
         "fetch_bytes_per_launch": round(fetch),
         "write_bytes_per_launch": round(write),
         "hbm_bytes_per_launch": round(fetch + write),
@@ -100,33 +109,34 @@ def summarize(dfetch, dwrite):
         "copy_calibration": {"bytes": copy_bytes, "fetch_factor": round(kf, 4), "write_factor": round(kw, 4)},
         "launches_counted": len(gf),
     }
-    with open(OUT_JSON, "w") as f:
+    arg = "" if bench.CORES == "fp6" else " int8"
+    with open(_out(".json"), "w") as f:
         json.dump(d, f, indent=1)
-    with open(OUT_MD, "w") as f:
-        f.write("# HBM traffic: W4A4 GEMM, M=4096, N=K=3072 (benchmarked kernel)\n\n")
+    with open(_out(".md"), "w") as f:
+        f.write(f"# HBM traffic: W4A4 GEMM on the {bench.CORES} matrix cores, M=4096, N=K=3072 (benchmarked kernel)\n\n")
         f.write("Commands (from /tmp with TMPDIR=/tmp, REPO = repository root):\n\n")
         f.write("    rocprofv3 --pmc FETCH_SIZE -d $REPO/gpurun_out/tf -o tf --output-format csv -- "
-                "python3 $REPO/bench_traffic.py run\n")
+                f"python3 $REPO/bench_traffic.py run{arg}\n")
         f.write("    rocprofv3 --pmc WRITE_SIZE -d $REPO/gpurun_out/tw -o tw --output-format csv -- "
-                "python3 $REPO/bench_traffic.py run\n")
-        f.write("    python3 $REPO/bench_traffic.py summarize $REPO/gpurun_out/tf $REPO/gpurun_out/tw\n\n")
+                f"python3 $REPO/bench_traffic.py run{arg}\n")
+        f.write(f"    python3 $REPO/bench_traffic.py summarize $REPO/gpurun_out/tf $REPO/gpurun_out/tw{arg}\n\n")
         f.write(f"Copy-kernel calibration ({COPY_MIB} MiB read + {COPY_MIB} MiB written by torch.neg): "
                 f"FETCH_SIZE reads {kf:.4f} x the bytes read, WRITE_SIZE {kw:.4f} x the bytes written.\n\n")
         f.write("| per GEMM launch | bytes |\n|---|---|\n")
         f.write(f"| fetched (calibrated) | {fetch/1e6:.2f} MB |\n")
         f.write(f"| written (calibrated) | {write/1e6:.2f} MB |\n")
         f.write(f"| total | {(fetch + write)/1e6:.2f} MB |\n")
-        f.write(f"| algorithmic (A 4-bit codes + packed weights + bf16 output) | {alg/1e6:.2f} MB |\n\n")
-        f.write("The fetched bytes exceed the operand bytes because each of the 8 XCDs has its own 4 MB L2: "
-                "with the XCD-aware tile map each XCD computes a 1024 x 1536 sub-rectangle of the output and "
-                "fetches its activation rows (1.5 MB) and weight columns (2.4 MB) once, 8 x 3.9 MB = 31.5 MB; "
-                "the repeats across XCDs come from the 256 MB last-level cache. The written bytes are the bf16 "
-                "output exactly.\n\n")
+        f.write(f"| algorithmic (activation codes + packed weights + bf16 output) | {alg/1e6:.2f} MB |\n\n")
+        f.write("Each of the 8 XCDs has its own 4 MB L2; with the XCD-aware tile map every XCD fetches the "
+                "activation rows and weight columns of its part of the output, so operand bytes repeat across "
+                "XCDs (served by the 256 MB last-level cache). The written bytes are the bf16 output.\n\n")
         f.write(f"Kernel source hash: `{d['source_sha']}` ({len(gf)} launches counted).\n")
     print(json.dumps(d))
 
 
 if __name__ == "__main__":
+    if sys.argv[-1] in ("fp6", "int8"):
+        bench.CORES = sys.argv.pop()
     if len(sys.argv) >= 2 and sys.argv[1] == "run":
         run()
     elif len(sys.argv) == 4 and sys.argv[1] == "summarize":

@@ -86,7 +86,9 @@ def run_merge(steps, warmup):
         "GBps": round(moved / ms / 1e6, 1)}))
 
 
-def run(name, steps, warmup):
+def run(name, steps, warmup, cores="fp6"):
+    """cores: matrix cores of the per-tensor W4A4 layers, "fp6" (E2M3
+    fragments) or "int8" (tile-packed int4 widened to bytes)."""
     if name == "merge":
         return run_merge(steps, warmup)
     import numpy as np
@@ -102,6 +104,7 @@ def run(name, steps, warmup):
     stream = torch.cuda.current_stream()
     w = wl.CONFIGS[name]()
     rq_plan, gemm_plan = _plan(w)
+    f6 = cores == "fp6"
 
     def bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -114,7 +117,10 @@ def run(name, steps, warmup):
         N, K = lin.N, lin.K
         if lin.fmt in ("w4a4", "a8w4"):
             wc, ws, _, _ = cr.convrot_rotate_quantize(bf16(wl.weight_bits(w, lin)), 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
-            prep[lin.name] = dict(w=cr.w4_pack_weights(wc, ws, N, K)[0], ws=ws)
+            if lin.fmt == "w4a4" and f6:
+                prep[lin.name] = dict(w=cr.w4_pack_weights_f6(wc, N, K), ws=ws)
+            else:
+                prep[lin.name] = dict(w=cr.w4_pack_weights(wc, ws, N, K)[0], ws=ws)
         elif lin.fmt == "int8":
             wc, ws, _, _ = cr.convrot_rotate_quantize(bf16(wl.weight_bits(w, lin)), 256, cr.Q.SYM_INT8, cr.GRAN.TENSOR)
             prep[lin.name] = dict(w=wc, ws=ws)
@@ -132,14 +138,19 @@ def run(name, steps, warmup):
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
-    # RQ outputs, allocated once
+    # RQ outputs, allocated once; per-tensor INT4 codes in the layout of the cores used
+    lay4 = cr.LAYOUT.F6 if f6 else cr.LAYOUT.TILED
+
+    def c4_shape(M, K):
+        return ((M + 31) // 32, K // 64, 1536) if f6 else ((M + 15) // 16, K // 64, 512)
+
     rq_out = {}
     for key in rq_plan:
         x_id, kind, lname = key
         M, K = w.acts[x_id][0], w.acts[x_id][1]
         x = acts[x_id]
         if kind == "int4_tensor":
-            o = dict(codes=torch.empty(((M + 15) // 16, K // 64, 512), dtype=torch.uint8, device=dev),
+            o = dict(codes=torch.empty(c4_shape(M, K), dtype=torch.uint8, device=dev),
                      scales=torch.empty(1, dtype=torch.float32, device=dev),
                      ws=torch.empty(cr.convrot_rq_workspace_size(M, K, 256, 0, 0), dtype=torch.uint8, device=dev))
         elif kind == "int8_tensor":
@@ -147,7 +158,7 @@ def run(name, steps, warmup):
                      scales=torch.empty(1, dtype=torch.float32, device=dev),
                      ws=torch.empty(cr.convrot_rq_workspace_size(M, K, 256, 1, 0), dtype=torch.uint8, device=dev))
         elif kind == "dual_tensor":
-            o = dict(codes=torch.empty(((M + 15) // 16, K // 64, 512), dtype=torch.uint8, device=dev),
+            o = dict(codes=torch.empty(c4_shape(M, K), dtype=torch.uint8, device=dev),
                      scales=torch.empty(1, dtype=torch.float32, device=dev),
                      codes8=torch.empty((M, K), dtype=torch.int8, device=dev),
                      scales8=torch.empty(1, dtype=torch.float32, device=dev),
@@ -166,13 +177,13 @@ def run(name, steps, warmup):
         x_id, kind, lname = key
         o, x = rq_out[key], acts[x_id]
         if kind == "int4_tensor":
-            cr.convrot_rotate_quantize(x, 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR, layout=cr.LAYOUT.TILED,
+            cr.convrot_rotate_quantize(x, 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR, layout=lay4,
                                        codes=o["codes"], scales=o["scales"], workspace=o["ws"])
         elif kind == "int8_tensor":
             cr.convrot_rotate_quantize(x, 256, cr.Q.SYM_INT8, cr.GRAN.TENSOR, codes=o["codes"],
                                        scales=o["scales"], workspace=o["ws"])
         elif kind == "dual_tensor":
-            cr.convrot_rotate_quantize_dual(x, 256, layout4=cr.LAYOUT.TILED, codes4=o["codes"], scale4=o["scales"],
+            cr.convrot_rotate_quantize_dual(x, 256, layout4=lay4, codes4=o["codes"], scale4=o["scales"],
                                             codes8=o["codes8"], scale8=o["scales8"], workspace=o["ws"])
         elif kind == "int8_row":
             cr.convrot_rotate_quantize(x, 256, cr.Q.SYM_INT8, cr.GRAN.ROW, codes=o["codes"], scales=o["scales"])
@@ -261,7 +272,8 @@ def run(name, steps, warmup):
         "value": round(eff, 2), "unit": "TOPS", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "int4" if name not in ("c3", "c2a8") else "int8/int4", "data": "synthetic",
-        "config": {"workload": w.name, "layers": len(w.linears), "total_GOP": round(ops / 1e9, 1)},
+        "config": {"workload": w.name, "layers": len(w.linears), "total_GOP": round(ops / 1e9, 1),
+                   "w4a4_matrix_cores": cores},
         "pct_int8_peak": round(100.0 * eff / INT8_PEAK_TOPS, 2),
         "gemm": layers, "rotate_quantize": rqs,
         "dominant_gemm": {"layer": dom, **layers[dom], "frac_int8_peak": round(layers[dom]["TOPS"] / INT8_PEAK_TOPS, 4)},

@@ -94,8 +94,17 @@ typedef enum cr_layout {
                           /* (b, kt) is natural byte (row 16b + l%16, 32kt + 8(l/16) + j), the */
                           /* operand-fragment order of the W4A4 GEMM; rows past `rows` in the  */
                           /* last block are left unwritten (allocate ceil(rows/16)*16 rows)    */
-  CR_LAYOUT_INT8 = 2      /* w4a4_gemm only: int8 codes [rows, K] row-major (SYM_INT8), the    */
+  CR_LAYOUT_INT8 = 2,     /* w4a4_gemm only: int8 codes [rows, K] row-major (SYM_INT8), the    */
                           /* 8-bit-activation branch for W4A4-format weights                   */
+  CR_LAYOUT_F6 = 3        /* signed int4 codes (values -7..7) as fp6 E2M3 (bit 5 sign, bits    */
+                          /* 4:3 exponent with bias 1, bits 2:0 mantissa; every code is exact) */
+                          /* in 32 x 64 operand fragments [ceil(rows/32)][K/64][1536 B]: lane  */
+                          /* l (0..63) of a fragment covers row 32b + l%32 and columns          */
+                          /* 64kt + 32(l/32) + i, i = 0..31, field i at bits 6i..6i+5 of its 24 */
+                          /* bytes, bytes 0..15 at l*16 and bytes 16..23 at 1024 + l*8. Input   */
+                          /* of the fp6 matrix-core W4A4 GEMM (weights from w4_pack_weights_f6);*/
+                          /* rows past `rows` in the last block are left unwritten (allocate    */
+                          /* ceil(rows/32)*32 rows)                                              */
 } cr_layout;
 
 /* Status text, e.g. "format not available" for CR_ERR_UNSUPPORTED_FORMAT. */
@@ -161,7 +170,9 @@ void convrot_reset_counters(void);
  *   codes        SYM_INT4 / UNSIGNED / ASYM: uint8 [rows, K/2] natural int4;
  *                SYM_INT8: int8 [rows, K]
  *   layout       CR_LAYOUT_NATURAL, or CR_LAYOUT_TILED for SYM_INT4 / UNSIGNED
- *                codes (the input layout of w4a4_gemm's fast path)
+ *                codes (the input layout of w4a4_gemm's int8-core path), or
+ *                CR_LAYOUT_F6 for SYM_INT4 with the rotation on (the input of
+ *                w4a4_gemm's fp6-core path; ceil(rows/32)(K/64) 1536 bytes)
  *   scales       float32 [1] | [rows] | [rows, K/q_group]; ASYM: fp16 [rows, K/16]
  *   zeros        ASYM only: uint8 [rows, K/32], two uint4 zero points per byte
  *                (group 2j low nibble); NULL otherwise
@@ -202,8 +213,8 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
  * SYM_INT8, TENSOR, codes8 (natural int8 [rows, K]), scale8: both share the
  * maximum of the rotated tensor, which is computed once (two launches
  * instead of four).
- *   codes4   uint8 int4 codes, layout4 CR_LAYOUT_NATURAL [rows, K/2] or
- *            CR_LAYOUT_TILED; scale4 float32 [1]
+ *   codes4   uint8 int4 codes, layout4 CR_LAYOUT_NATURAL [rows, K/2],
+ *            CR_LAYOUT_TILED or CR_LAYOUT_F6; scale4 float32 [1]
  *   codes8   int8 [rows, K]; scale8 float32 [1]
  *   workspace  at least convrot_rq_workspace_size(rows, K, rot_group,
  *            SYM_INT4, TENSOR, 0) bytes
@@ -248,6 +259,24 @@ cr_status w4_pack_weights(const void* codes, const void* scales, const void* zer
                           int64_t N, int64_t K, cr_qtype qtype, cr_gran gran, int q_group,
                           void* packed, void* packed_scales, void* packed_zeros, float* w_sum,
                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * w4_pack_weights_f6 - natural signed int4 weight codes -> CR_LAYOUT_F6
+ * fragments, the weight operand of w4a4_gemm with a_layout CR_LAYOUT_F6.
+ *
+ * Cites: "Qwen-Image-Edit-2511 INT4 (ComfyUI Optimized)", Tile-Packed Weight
+ * Format (weights reorganised offline into the GEMM's operand tiles);
+ * "Qwen3-4B ConvRot W4A4" page, Format (natural [rows, cols/2] container).
+ *
+ *   codes    natural uint8 [N, K/2] SYM_INT4 codes (low nibble = even column);
+ *            every code must lie in [-7, 7] (a -8 nibble has no exact E2M3
+ *            value and is not checked)
+ *   packed   uint8, w4_packed_f6_bytes(N, K) = (N/32)(K/64) 1536 bytes
+ * The weight scales (TENSOR [1] or ROW [N]) are used as they are.
+ * Shape: N % 128 == 0, K % 128 == 0. One launch on `stream`.
+ */
+size_t w4_packed_f6_bytes(int64_t N, int64_t K);
+cr_status w4_pack_weights_f6(const void* codes, int64_t N, int64_t K, void* packed, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * convrot_dequantize_weights - quantized weights back to bf16 in the
@@ -295,10 +324,17 @@ cr_status convrot_dequantize_weights(const void* codes, const void* scales, cons
  *               or CR_LAYOUT_INT8: int8 codes [M, K] (SYM_INT8, TENSOR or ROW
  *               scales), the 8-bit-activation branch for these weights
  *               ("Qwen3-4B ConvRot W4A4" page, INT8 branch comparison): no
- *               a_unsigned, no 64-group scales and no low-rank branch with it
+ *               a_unsigned, no 64-group scales and no low-rank branch with it;
+ *               or CR_LAYOUT_F6: fp6 E2M3 fragments (signed codes) with
+ *               w_packed from w4_pack_weights_f6, run on the fp6 matrix cores
+ *               (the products and their float32 sums are exact integers for
+ *               K <= 32768, so every output equals the int8-core path's):
+ *               TENSOR or ROW scales on both sides, no a_unsigned, no
+ *               low-rank branch
  *   a_scales    float32: TENSOR [1], ROW [M], ROW_GROUP(64) [M, K/64]
  *   a_unsigned  1 for UNSIGNED_INT4_SHIFT codes: y -= a_shift * w_sum[n]
- *   w_packed    from w4_pack_weights (SYM_INT4)
+ *   w_packed    from w4_pack_weights (SYM_INT4); from w4_pack_weights_f6
+ *               with CR_LAYOUT_F6 activations
  *   w_scales    TENSOR [1], ROW [N], ROW_GROUP(64): packed [N/128][K/64][128]
  *   scale pairs: (TENSOR|ROW) x (TENSOR|ROW), or ROW_GROUP x ROW_GROUP (group 64)
  *   w_sum       float32 [N], required iff a_unsigned

@@ -202,3 +202,81 @@ def tile_pack_g16(per_group: np.ndarray) -> np.ndarray:
 def pack_zeros_u4(zeros: np.ndarray) -> np.ndarray:
     """uint4 zero points [N, K/16] -> natural two-per-byte [N, K/32]."""
     return pack_int4(zeros.astype(np.int64))
+
+
+# ---------------------------------------------------------------------------
+# fp6 E2M3 fragments: the operand layout of the fp6 matrix-core W4A4 GEMM.
+#
+# Not from the pages: E2M3 is the OCP Microscaling (MX) FP6 format -- sign bit
+# 5, exponent bits 4:3 with bias 1, mantissa bits 2:0; a normal value
+# (e >= 1) is (-1)^s 2^(e-1) (1 + m/8), a subnormal (e = 0) is (-1)^s m/8, and
+# there is no Inf or NaN. Every integer in [-7, 7] (a symmetric INT4 code) is
+# an E2M3 value, so the format carries the codes exactly.
+#
+# Layout (this project's choice, one 64-lane operand fragment of the
+# 32x32x64 matrix-core instruction per 1536 bytes): [ceil(rows/32)][K/64][1536 B];
+# lane l of fragment (b, kt) holds row 32b + l%32 and columns
+# 64kt + 32(l//32) + i, i = 0..31, as 32 six-bit fields, field i at bits
+# 6i..6i+5 of a 24-byte little-endian string; bytes 0..15 of it are stored at
+# l*16, bytes 16..23 at 1024 + l*8. Rows past `rows` are zero here (the
+# library leaves them unwritten).
+# ---------------------------------------------------------------------------
+def e2m3_value(code) -> np.ndarray:
+    """The real value of E2M3 codes (uint, 0..63), by the format's definition."""
+    c = np.asarray(code).astype(np.int64)
+    s = np.where((c >> 5) & 1, -1.0, 1.0)
+    e = (c >> 3) & 3
+    m = c & 7
+    mag = np.where(e == 0, m / 8.0, np.ldexp(1.0 + m / 8.0, e - 1))
+    return s * mag
+
+
+def e2m3_code_of_int(q) -> np.ndarray:
+    """The E2M3 code of integers in [-7, 7] (zero as +0)."""
+    q = np.asarray(q).astype(np.int64)
+    if np.any(np.abs(q) > 7):
+        raise ValueError("integer outside [-7, 7] has no exact E2M3 code")
+    a = np.abs(q)
+    e = np.zeros_like(a)
+    nz = a > 0
+    e[nz] = np.floor(np.log2(a[nz])).astype(np.int64) + 1      # a = 2^(e-1) (1 + m/8)
+    m = np.zeros_like(a)
+    m[nz] = (a[nz] * 8) // (1 << (e[nz] - 1)) - 8
+    code = (e << 3) | m
+    return np.where(q < 0, code | 32, code).astype(np.uint8)
+
+
+def f6_pack(codes: np.ndarray) -> np.ndarray:
+    """Signed int4 codes int [rows, K] (values in [-7, 7]) -> uint8
+    [ceil(rows/32), K/64, 1536] fp6 E2M3 fragments (layout above)."""
+    c = np.asarray(codes).astype(np.int64)
+    rows, K = c.shape
+    if K % 64:
+        raise ValueError("K % 64 != 0")
+    MB, KT = (rows + 31) // 32, K // 64
+    f = np.zeros((MB * 32, K), dtype=np.int64)
+    f[:rows] = e2m3_code_of_int(c)
+    # [b, r, kt, h, i] -> [b, kt, lane = 32 h + r, i]
+    f = f.reshape(MB, 32, KT, 2, 32).transpose(0, 2, 3, 1, 4).reshape(MB, KT, 64, 32)
+    # four 6-bit fields -> three bytes, little-endian
+    g = f.reshape(MB, KT, 64, 8, 4)
+    v = g[..., 0] | (g[..., 1] << 6) | (g[..., 2] << 12) | (g[..., 3] << 18)
+    lane_bytes = np.stack([v & 0xFF, (v >> 8) & 0xFF, (v >> 16) & 0xFF], axis=-1).reshape(MB, KT, 64, 24)
+    out = np.zeros((MB, KT, 1536), dtype=np.uint8)
+    out[:, :, :1024] = lane_bytes[..., :16].reshape(MB, KT, 1024)
+    out[:, :, 1024:] = lane_bytes[..., 16:].reshape(MB, KT, 512)
+    return out
+
+
+def f6_unpack(frags: np.ndarray, rows: int) -> np.ndarray:
+    """Inverse of f6_pack: uint8 [MB, K/64, 1536] -> the real values of the
+    first `rows` rows, float64 [rows, K] (integers for codes written by f6_pack)."""
+    fr = np.asarray(frags, dtype=np.uint8)
+    MB, KT, _ = fr.shape
+    lane_bytes = np.concatenate([fr[:, :, :1024].reshape(MB, KT, 64, 16),
+                                 fr[:, :, 1024:].reshape(MB, KT, 64, 8)], axis=-1).astype(np.int64)
+    t = lane_bytes.reshape(MB, KT, 64, 8, 3)
+    v = t[..., 0] | (t[..., 1] << 8) | (t[..., 2] << 16)
+    f = np.stack([(v >> (6 * j)) & 63 for j in range(4)], axis=-1).reshape(MB, KT, 64, 32)
+    val = e2m3_value(f).reshape(MB, KT, 2, 32, 32).transpose(0, 3, 1, 2, 4).reshape(MB * 32, KT * 64)
+    return val[:rows]

@@ -102,6 +102,11 @@ def test_rq_validation(cr):
     assert _rq(cr, wsb=0) == 6                               # TENSOR needs workspace
     assert _rq(cr, q=1, layout=1) == 3                       # tiled layout is for int4 codes
     assert _rq(cr, layout=2) == 1
+    assert _rq(cr, layout=4) == 1
+    assert _rq(cr, layout=3) == 4                            # fp6 fragments of rotated int4 codes
+    assert _rq(cr, layout=3, g=1) == 4
+    assert _rq(cr, layout=3, q=1) == 3                       # not for int8 codes
+    assert _rq(cr, layout=3, rot=0, g=2, qg=64, ws=None, wsb=0) == 3   # nor without the rotation
     assert _rq(cr, smooth=A, g=1) == 4                       # smoothing: rotation 256 with row scales
     assert _rq(cr, smooth=A, g=2, qg=64) == 4
     assert _rq(cr, smooth=A) == 3                            # not with per-tensor scales
@@ -123,6 +128,7 @@ def test_rq_dual_validation(cr):
     assert dual(c8=None) == 1
     assert dual(s8=A + 4) == 1               # misaligned
     assert dual(layout=2) == 1
+    assert dual(layout=3) == 4               # fp6 fragments for the int4 set
     assert dual(ws=None) == 1
     assert dual(wsb=0) == 6
     assert dual(K=300) == 2
@@ -171,6 +177,13 @@ def test_pack_validation(cr):
     # ASYM_UINT4 g16 with its column sums
     assert L.w4_pack_weights(_p(A), _p(A), _p(A), 128, 512, 3, 2, 16, _p(A), _p(A), _p(A), _p(A), None) == 4
     assert cr.w4_packed_bytes(256, 512, 0, 0, 0, 0) == 256 * 256
+    assert cr.w4_packed_f6_bytes(256, 512) == 256 * 512 * 3 // 4
+    assert cr.w4_packed_f6_bytes(96, 512) == 0
+    assert L.w4_pack_weights_f6(_p(A), 128, 512, _p(A), None) == 4
+    assert L.w4_pack_weights_f6(_p(A), 100, 512, _p(A), None) == 2
+    assert L.w4_pack_weights_f6(_p(A), 128, 448, _p(A), None) == 2
+    assert L.w4_pack_weights_f6(None, 128, 512, _p(A), None) == 1
+    assert L.w4_pack_weights_f6(_p(A), 128, 512, _p(A + 4), None) == 1
     assert cr.w4_packed_bytes(256, 512, 0, 2, 64, 1) == 256 * 8 * 4
     assert cr.w4_packed_bytes(256, 512, 3, 2, 16, 2) == 256 * 32
 
@@ -193,7 +206,12 @@ def test_gemm_validation(cr):
     assert _w4a4(cr, la=A, lu=A, R=16) == 3
     assert _w4a4(cr, la=A, lu=A, R=64) == 4
     assert _w4a4(cr, ot=5) == 1
-    assert _w4a4(cr, layout=3) == 1
+    assert _w4a4(cr, layout=4) == 1
+    assert _w4a4(cr, layout=3) == 4                          # fp6 fragments, tensor scales
+    assert _w4a4(cr, layout=3, ag=1, wg=1) == 4
+    assert _w4a4(cr, layout=3, ag=2, wg=2) == 3              # fp6: no 64-group scales
+    assert _w4a4(cr, layout=3, uns=1, wsum=A) == 3           # fp6: signed codes only
+    assert _w4a4(cr, layout=3, la=A, lu=A, R=32) == 3        # fp6: no low-rank branch
     assert _w4a4(cr, layout=2, uns=1, wsum=A) == 3           # 8-bit activations: signed only
     assert _w4a4(cr, layout=2, ag=2, wg=2) == 3              # no 64-group scales with them
     assert _w4a4(cr, layout=2, la=A, lu=A, R=32) == 3        # no low-rank branch with them

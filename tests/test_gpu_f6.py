@@ -1,0 +1,177 @@
+"""GPU parity of the fp6 matrix-core W4A4 path (CR_LAYOUT_F6) against the
+CPU oracle.
+
+The fp6 path carries the same integer codes as the int8-core path, as E2M3
+values in 32 x 64 fragments (oracle.pack.f6_pack defines the layout). Bars:
+codes and packed bytes bit-exact (decoded to integers for the rows the
+library writes); int32 results bit-exact; float32 output within 1e-5 and bf16
+within 2e-3 relative L2 of the oracle's float32 epilogue.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import workloads as wl  # noqa: E402
+from oracle import linear as ol, pack as opack  # noqa: E402
+from tests.gpu_helpers import bf16_dev, bytes_of, dev, host, rel_l2, bf16_to_f32, say  # noqa: E402
+
+GR = {"tensor": 0, "row": 1, "row_group": 2}
+F6 = 3
+
+
+@pytest.fixture(scope="module")
+def cr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import w4a8_rotated_quantized_amd as m
+    assert m.device_check() == 0
+    return m
+
+
+@pytest.mark.parametrize("shape", [(128, 128), (256, 512), (384, 3072), (128, 12288)])
+def test_pack_weights_f6_bytes(cr, shape):
+    N, K = shape
+    say(f"f6 pack {shape}")
+    rng = np.random.default_rng(N + K)
+    q = rng.integers(-7, 8, size=(N, K))
+    q[0, :8] = [7, -7, 0, 1, -1, 3, -5, 6]
+    packed = cr.w4_pack_weights_f6(dev(opack.pack_int4(q)), N, K)
+    assert cr.w4_packed_f6_bytes(N, K) == packed.numel()
+    assert np.array_equal(bytes_of(packed), opack.f6_pack(q).reshape(-1))
+
+
+RQ_SHAPES = [(64, 512), (37, 3072), (300, 768), (5, 256), (129, 12288)]
+
+
+@pytest.mark.parametrize("rot", [256, 16, 64, 1024])
+@pytest.mark.parametrize("gran", ["tensor", "row", "row_group"])
+@pytest.mark.parametrize("shape", RQ_SHAPES)
+def test_rotate_quantize_f6(cr, rot, gran, shape):
+    rows, K = shape
+    if K % rot:
+        pytest.skip("K not a multiple of the rotation")
+    say(f"rq f6 rot {rot} {gran} {shape}")
+    xb = wl.activation(31, rows * 5 + K + rot, rows, K, n_outliers=max(1, K // 200), outlier_scale=25.0)
+    qg = 64 if gran == "row_group" else 0
+    ref = ol.rotate_quantize(xb, rot, "int4", gran, qg or None)
+    codes, scales, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), rot, 0, GR[gran], qg, layout=F6)
+    assert tuple(codes.shape) == ((rows + 31) // 32, K // 64, 1536)
+    assert np.array_equal(opack.f6_unpack(host(codes), rows), ref["values"]), "fp6 codes differ"
+    # the written rows' bytes are the oracle's encoding (+0 for zero codes)
+    want = opack.f6_pack(ref["values"])
+    got = host(codes)
+    full = rows // 32
+    assert np.array_equal(got[:full], want[:full])
+    assert np.array_equal(host(scales).reshape(-1).view(np.uint32),
+                          np.asarray(ref["scales"], np.float32).reshape(-1).view(np.uint32)), "scales differ"
+
+
+@pytest.mark.parametrize("rot", [256, 1024])
+def test_rotate_quantize_dual_f6(cr, rot):
+    rows, K = 300, 3072
+    say(f"rq dual f6 rot {rot}")
+    xb = wl.activation(33, rot, rows, K, n_outliers=10, outlier_scale=25.0)
+    r4 = ol.rotate_quantize(xb, rot, "int4", "tensor")
+    r8 = ol.rotate_quantize(xb, rot, "int8", "tensor")
+    c4, s4, c8, s8 = cr.convrot_rotate_quantize_dual(bf16_dev(xb), rot, layout4=F6)
+    assert np.array_equal(opack.f6_unpack(host(c4), rows), r4["values"])
+    assert np.array_equal(host(c8), r8["codes"])
+    assert host(s4)[0] == np.float32(r4["scales"]).reshape(-1)[0]
+    assert host(s8)[0] == np.float32(r8["scales"]).reshape(-1)[0]
+
+
+F6_CASES = [
+    # M, N, K, a_gran, w_gran
+    (1, 256, 512, "tensor", "tensor"),        # small-M kernel
+    (17, 384, 3072, "tensor", "row"),
+    (33, 128, 1024, "row", "row"),
+    (64, 256, 512, "row", "tensor"),
+    (65, 256, 512, "tensor", "tensor"),       # tiled kernel from here on; one ragged 32-row block
+    (77, 768, 256, "row", "tensor"),          # two 128-deep stages
+    (200, 384, 3072, "tensor", "tensor"),
+    (256, 384, 3072, "row", "row"),
+    (300, 512, 768, "tensor", "tensor"),
+    (129, 128, 12288, "tensor", "tensor"),
+]
+
+
+@pytest.mark.parametrize("case", F6_CASES)
+def test_w4a4_f6_gemm(cr, case):
+    M, N, K, ag, wg = case
+    say(f"w4a4 f6 {case}")
+    xb = wl.activation(41, M + N + K, M, K, n_outliers=3, outlier_scale=20.0)
+    wb = wl.weight(41, 7 + M + N + K, N, K)
+    bias = wl.weight(41, 9, 1, N, std=0.5)[0]
+    wp = ol.prepare_w4a4(wb, 256, wg)
+    ref = ol.w4a4_linear(xb, wb, 256, ag, wg, wprep=wp)
+    ref_b = ol.w4a4_linear(xb, wb, 256, ag, wg, bias_bits=bias, wprep=wp)
+    a = dev(opack.f6_pack(ref["x"]["values"]))
+    w = dev(opack.f6_pack(wp["values"]))
+    sa = dev(np.asarray(ref["x"]["scales"], np.float32).reshape(-1))
+    sw = dev(np.asarray(wp["scales"], np.float32).reshape(-1))
+    raw = cr.w4a4_gemm(a, sa, GR[ag], w, sw, GR[wg], M, N, K, out_type=2)
+    assert np.array_equal(host(raw).astype(np.int64), ref["raw"])
+    yf = cr.w4a4_gemm(a, sa, GR[ag], w, sw, GR[wg], M, N, K, out_type=1)
+    assert rel_l2(host(yf), ref["y"]) <= 1e-5
+    yb = cr.w4a4_gemm(a, sa, GR[ag], w, sw, GR[wg], M, N, K, out_type=0)
+    assert rel_l2(bf16_to_f32(host(yb)), ref["y"]) <= 2e-3
+    ybias = cr.w4a4_gemm(a, sa, GR[ag], w, sw, GR[wg], M, N, K, bias=bf16_dev(bias), out_type=1)
+    assert rel_l2(host(ybias), ref_b["y"]) <= 1e-5
+    # the same float32 epilogue as the int8-core path: identical outputs
+    at = dev(opack.tile_pack_a(ref["x"]["codes"]))
+    wt = dev(wp["tiles"].reshape(-1))
+    yf8 = cr.w4a4_gemm(at, sa, GR[ag], wt, sw, GR[wg], M, N, K, out_type=1)
+    assert np.array_equal(host(yf).view(np.uint32), host(yf8).view(np.uint32))
+
+
+def test_w4a4_f6_ldc_padding(cr):
+    M, N, K, ldc = 150, 256, 512, 264
+    say("w4a4 f6 ldc")
+    rng = np.random.default_rng(5)
+    qa = rng.integers(-7, 8, size=(M, K))
+    qw = rng.integers(-7, 8, size=(N, K))
+    out = torch.full((M, ldc), -1, dtype=torch.int32, device="cuda")
+    sa = dev(np.ones(1, np.float32))
+    cr.w4a4_gemm(dev(opack.f6_pack(qa)), sa, 0, dev(opack.f6_pack(qw)), sa, 0, M, N, K, out_type=2,
+                 out=out[:, :N].as_strided((M, N), (ldc, 1)))
+    o = host(out)
+    assert np.array_equal(o[:, :N].astype(np.int64), qa @ qw.T)
+    assert np.all(o[:, N:] == -1)
+
+
+def test_w4a4_f6_layer_on_gpu(cr):
+    """Whole layer on the GPU path: both operands rotated and quantized by
+    convrot_rotate_quantize into fp6 fragments (weights also through
+    w4_pack_weights_f6 from natural codes), GEMM on the fp6 cores."""
+    M, N, K = 200, 384, 3072
+    say("w4a4 f6 layer")
+    xb = wl.activation(43, 1, M, K, n_outliers=3, outlier_scale=20.0)
+    wb = wl.weight(43, 2, N, K)
+    ref = ol.w4a4_linear(xb, wb, 256, "tensor", "row")
+    a, sa, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), 256, 0, 0, layout=F6)
+    wf, ws, _, _ = cr.convrot_rotate_quantize(bf16_dev(wb), 256, 0, 1, layout=F6)
+    wn, _, _, _ = cr.convrot_rotate_quantize(bf16_dev(wb), 256, 0, 1)
+    wp = cr.w4_pack_weights_f6(wn, N, K)
+    assert np.array_equal(bytes_of(wp), bytes_of(wf))
+    raw = cr.w4a4_gemm(a, sa, 0, wf, ws, 1, M, N, K, out_type=2)
+    assert np.array_equal(host(raw).astype(np.int64), ref["raw"])
+    yb = cr.w4a4_gemm(a, sa, 0, wf, ws, 1, M, N, K, out_type=0)
+    assert rel_l2(bf16_to_f32(host(yb)), ref["y"]) <= 2e-3
+
+
+def test_f6_rejects_unsupported(cr):
+    M, N, K = 64, 128, 256
+    a = torch.zeros(((M + 31) // 32, K // 64, 1536), dtype=torch.uint8, device="cuda")
+    w = torch.zeros((N // 32, K // 64, 1536), dtype=torch.uint8, device="cuda")
+    s = torch.ones(M * (K // 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(cr.ConvRotError, match="format not available"):
+        cr.w4a4_gemm(a, s, 2, w, s, 2, M, N, K)              # 64-group scales
+    with pytest.raises(cr.ConvRotError, match="format not available"):
+        cr.w4a4_gemm(a, s, 0, w, s, 0, M, N, K, a_unsigned=True, a_shift=0.171875, w_sum=s)
+    x = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(cr.ConvRotError, match="format not available"):
+        cr.convrot_rotate_quantize(x, 0, 0, 2, 64, layout=F6)   # no rotation
+    with pytest.raises(cr.ConvRotError, match="format not available"):
+        cr.convrot_rotate_quantize(x, 256, 1, 0, 0, layout=F6)  # INT8 codes

@@ -69,6 +69,33 @@ def test_c2_full_pipeline(cr, c2_weights, M):
     assert rel_l2(y[rows], ref_y) <= 2e-3
 
 
+@pytest.mark.parametrize("M", [4096, 32])
+def test_c2_full_pipeline_f6(cr, c2_weights, M):
+    """The benchmarked path on the fp6 matrix cores: GPU rotate+quantize into
+    fp6 fragments, weights packed to fp6 fragments, GEMM (256 x 192 blocks at
+    M = 4096, the small-M kernel at 32)."""
+    N = K = 3072
+    say(f"c2 full size fp6 M={M}")
+    wp, _, ws = c2_weights
+    wc, _, _, _ = cr.convrot_rotate_quantize(bf16_dev(wl.weight(2, 1, N, K)), 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
+    wf = cr.w4_pack_weights_f6(wc, N, K)
+    assert np.array_equal(bytes_of(wf), opack.f6_pack(wp["values"]).reshape(-1))
+    xb = wl.activation(2, 0 if M == 4096 else 2, M, K, n_outliers=15, outlier_scale=30.0)
+    xa = ol.rotate_quantize(xb, 256, "int4", "tensor")
+    codes, sa, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR,
+                                                 layout=cr.LAYOUT.F6)
+    assert np.array_equal(opack.f6_unpack(host(codes), M), xa["values"])
+    assert host(sa)[0] == np.float32(xa["scales"]).reshape(-1)[0]
+    rng = np.random.default_rng(4321)
+    rows = np.sort(rng.choice(M, size=min(M, 192), replace=False))
+    raw = host(cr.w4a4_gemm(codes, sa, 0, wf, ws, 0, M, N, K, out_type=cr.OUT.I32_RAW))
+    ref_raw = og.int_gemm(xa["values"][rows], wp["values"])
+    assert np.array_equal(raw[rows].astype(np.int64), ref_raw)
+    y = bf16_to_f32(host(cr.w4a4_gemm(codes, sa, 0, wf, ws, 0, M, N, K)))
+    ref_y = ol.epilogue_scalar(ref_raw, xa["scales"], "tensor", wp["scales"], "tensor")
+    assert rel_l2(y[rows], ref_y) <= 2e-3
+
+
 # ---------------------------------------------------------------------------
 # the other workloads at full size (sampled outputs)
 # ---------------------------------------------------------------------------
@@ -170,6 +197,33 @@ def test_c4_w4a4_layers_full(cr, name):
     w, lin = _lin("c4", name)
     say(f"c4 full {name} {lin.M}x{lin.N}x{lin.K}")
     _w4a4_layer(cr, w, lin)
+
+
+def _w4a4_layer_f6(cr, w, lin, rows_n=32):
+    M, N, K = lin.M, lin.N, lin.K
+    xb, wb = wl.act_bits(w, lin.x_id), wl.weight_bits(w, lin)
+    xa = ol.rotate_quantize(xb, 256, "int4", "tensor")
+    wq = ol.rotate_quantize(wb, 256, "int4", "tensor")
+    codes, sa, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR,
+                                                 layout=cr.LAYOUT.F6)
+    assert np.array_equal(opack.f6_unpack(host(codes), M), xa["values"])
+    wf, ws, _, _ = cr.convrot_rotate_quantize(bf16_dev(wb), 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR,
+                                              layout=cr.LAYOUT.F6)
+    assert np.array_equal(bytes_of(wf), opack.f6_pack(wq["values"]).reshape(-1))
+    rows = _rows(M, rows_n, 53)
+    raw = host(cr.w4a4_gemm(codes, sa, 0, wf, ws, 0, M, N, K, out_type=cr.OUT.I32_RAW))
+    ref_raw = og.int_gemm(xa["values"][rows], wq["values"])
+    assert np.array_equal(raw[rows].astype(np.int64), ref_raw)
+    y = bf16_to_f32(host(cr.w4a4_gemm(codes, sa, 0, wf, ws, 0, M, N, K)))
+    ref_y = ol.epilogue_scalar(ref_raw, xa["scales"], "tensor", wq["scales"], "tensor")
+    assert rel_l2(y[rows], ref_y) <= 2e-3
+
+
+@pytest.mark.parametrize("name", ["img_mlp_up", "img_mlp_down", "txt_q"])
+def test_c4_w4a4_layers_full_f6(cr, name):
+    w, lin = _lin("c4", name)
+    say(f"c4 full fp6 {name} {lin.M}x{lin.N}x{lin.K}")
+    _w4a4_layer_f6(cr, w, lin)
 
 
 @pytest.mark.parametrize("name", ["qkv", "mlp_down"])

@@ -137,3 +137,60 @@ def test_exactness_bound_guard():
     a = np.full((1, 8), 2 ** 26, dtype=np.int64)
     with pytest.raises(ValueError):
         gemm.int_gemm(a, a)
+
+
+# ---------------------------------------------------------------------------
+# fp6 E2M3 fragments (operand format of the fp6 matrix-core GEMM). Pins: the
+# constants the OCP Microscaling FP6 (E2M3) definition fixes, and byte
+# positions derived by hand from the layout definition.
+# ---------------------------------------------------------------------------
+def test_e2m3_format_constants():
+    v = pack.e2m3_value
+    assert v(0b011111) == 7.5          # largest normal: 2^2 * 1.875
+    assert v(0b001000) == 1.0          # smallest normal
+    assert v(0b000111) == 0.875        # largest subnormal
+    assert v(0b000001) == 0.125        # smallest subnormal
+    assert v(0b111111) == -7.5
+    assert v(0b100000) == 0.0 and np.signbit(v(0b100000))
+    vals = v(np.arange(64))
+    assert len(set(vals.tolist())) == 63   # only +0 / -0 coincide
+    assert np.all(np.diff(vals[:32]) > 0)  # codes 0..31 increase with their value
+
+
+def test_e2m3_codes_of_int4_round_trip():
+    q = np.arange(-7, 8)
+    c = pack.e2m3_code_of_int(q)
+    assert np.array_equal(pack.e2m3_value(c), q)
+    assert c[7] == 0 and c.max() < 64      # zero as +0
+    # by hand: 3 = 2^1 * 1.5 (e = 2, m = 4), 5 = 2^2 * 1.25 (e = 3, m = 2), -1 = sign | e = 1
+    assert c[q.tolist().index(3)] == 0b010100
+    assert c[q.tolist().index(5)] == 0b011010
+    assert c[q.tolist().index(-1)] == 0b101000
+    for bad in (8, -8):
+        with pytest.raises(ValueError):
+            pack.e2m3_code_of_int(np.array([bad]))
+
+
+def test_f6_fragment_positions_by_hand():
+    rows, K = 40, 128
+    c = np.zeros((rows, K), dtype=np.int64)
+    c[0, 0] = 1        # block 0, k-tile 0, lane 0, field 0 -> byte 0 bits 0..5
+    c[33, 127] = -7    # block 1, k-tile 1, lane 32 + 1 = 33, field 31 -> lane byte 23 bits 2..7
+    c[5, 70] = 3       # block 0, k-tile 1, lane 5, field 6 -> lane bits 36..41 = byte 4 bits 4..7, byte 5 bits 0..1
+    fr = pack.f6_pack(c)
+    assert fr.shape == (2, 2, 1536)
+    nz = {(int(b), int(t), int(o)): int(fr[b, t, o]) for b, t, o in zip(*np.nonzero(fr))}
+    assert nz == {(0, 0, 0): 0b001000,
+                  (1, 1, 1024 + 33 * 8 + 7): 0b111110 << 2,
+                  (0, 1, 5 * 16 + 4): (0b010100 << 4) & 0xFF,
+                  (0, 1, 5 * 16 + 5): 0b010100 >> 4}
+    assert np.array_equal(pack.f6_unpack(fr, rows), c)
+
+
+def test_f6_round_trip_and_dot_products():
+    rng = np.random.default_rng(11)
+    a = rng.integers(-7, 8, size=(45, 192))
+    w = rng.integers(-7, 8, size=(64, 192))
+    av, wv = pack.f6_unpack(pack.f6_pack(a), 45), pack.f6_unpack(pack.f6_pack(w), 64)
+    assert np.array_equal(av, a) and np.array_equal(wv, w)
+    assert np.array_equal((av @ wv.T).astype(np.int64), gemm.int_gemm(a, w))

@@ -16,6 +16,7 @@ import torch
 __all__ = [
     "ConvRotError", "lib", "Q", "GRAN", "OUT", "LAYOUT",
     "convrot_rotate_quantize", "convrot_rotate_quantize_dual", "convrot_dequantize_weights", "w4_pack_weights",
+    "w4_pack_weights_f6", "w4_packed_f6_bytes",
     "w4a4_gemm", "w4a8_gemm",
     "int8_tensorwise_gemm", "convrot_rq_workspace_size", "w4_packed_bytes",
     "get_counters", "reset_counters", "device_check", "status_string",
@@ -55,6 +56,7 @@ class LAYOUT:
     NATURAL = 0
     TILED = 1
     INT8 = 2
+    F6 = 3
 
 
 class _Counters(ctypes.Structure):
@@ -75,6 +77,8 @@ _SIGS = {
     "convrot_dequantize_weights": (_i, [_vp, _vp, _vp, _i64, _i64, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp]),
     "w4_packed_bytes": (_sz, [_i64, _i64, _i, _i, _i, _i]),
     "w4_pack_weights": (_i, [_vp, _vp, _vp, _i64, _i64, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "w4_packed_f6_bytes": (_sz, [_i64, _i64]),
+    "w4_pack_weights_f6": (_i, [_vp, _i64, _i64, _vp, _vp]),
     "w4a4_gemm": (_i, [_vp, _i, _vp, _i, _i, _f, _vp, _vp, _i, _vp, _vp, _i, _vp, _i, _vp,
                        _vp, _i, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
     "w4a8_gemm": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _i, _i64, _i64, _i64, _i64,
@@ -153,7 +157,8 @@ def convrot_rotate_quantize(x, rot_group=256, qtype=Q.SYM_INT4, gran=GRAN.TENSOR
                             stream=None, smooth=None):
     """x: bf16 [rows, K] (row stride may exceed K). Returns
     (codes, scales, zeros, lora_act); outputs are allocated when not given.
-    Tiled int4 codes come back as uint8 [ceil(rows/16), K/64, 512]."""
+    Tiled int4 codes come back as uint8 [ceil(rows/16), K/64, 512], fp6
+    fragments (layout F6) as uint8 [ceil(rows/32), K/64, 1536]."""
     rows, K = x.shape
     ldx = x.stride(0)
     dev = x.device
@@ -162,6 +167,8 @@ def convrot_rotate_quantize(x, rot_group=256, qtype=Q.SYM_INT4, gran=GRAN.TENSOR
             codes = torch.empty((rows, K), dtype=torch.int8, device=dev)
         elif layout == LAYOUT.TILED:
             codes = torch.empty(((rows + 15) // 16, K // 64, 512), dtype=torch.uint8, device=dev)
+        elif layout == LAYOUT.F6:
+            codes = torch.empty(((rows + 31) // 32, K // 64, 1536), dtype=torch.uint8, device=dev)
         else:
             codes = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev)
     if scales is None:
@@ -194,7 +201,8 @@ def convrot_rotate_quantize_dual(x, rot_group=256, layout4=LAYOUT.NATURAL, codes
     rows, K = x.shape
     dev = x.device
     if codes4 is None:
-        shape = ((rows + 15) // 16, K // 64, 512) if layout4 == LAYOUT.TILED else (rows, K // 2)
+        shape = {LAYOUT.TILED: ((rows + 15) // 16, K // 64, 512),
+                 LAYOUT.F6: ((rows + 31) // 32, K // 64, 1536)}.get(layout4, (rows, K // 2))
         codes4 = torch.empty(shape, dtype=torch.uint8, device=dev)
     if scale4 is None:
         scale4 = torch.empty(1, dtype=torch.float32, device=dev)
@@ -247,6 +255,20 @@ def w4_pack_weights(codes, scales, N, K, qtype=Q.SYM_INT4, gran=GRAN.TENSOR, q_g
     return packed, packed_scales, packed_zeros, w_sum
 
 
+def w4_packed_f6_bytes(N, K) -> int:
+    return lib.w4_packed_f6_bytes(N, K)
+
+
+def w4_pack_weights_f6(codes, N, K, packed=None, stream=None):
+    """Natural signed int4 codes [N, K/2] -> fp6 E2M3 fragments
+    uint8 [N/32, K/64, 1536], the weight operand of the fp6 W4A4 GEMM."""
+    if packed is None:
+        packed = torch.empty((N // 32, K // 64, 1536), dtype=torch.uint8, device=codes.device)
+    st = lib.w4_pack_weights_f6(_ptr(codes), N, K, _ptr(packed), _stream(stream))
+    _check(st, "w4_pack_weights_f6")
+    return packed
+
+
 def _out(M, N, out_type, dev, out):
     if out is not None:
         return out
@@ -257,9 +279,13 @@ def _out(M, N, out_type, dev, out):
 def w4a4_gemm(a_codes, a_scales, a_gran, w_packed, w_scales, w_gran, M, N, K,
               a_unsigned=False, a_shift=0.0, w_sum=None, lora_act=None, lora_up=None,
               bias=None, out_type=OUT.BF16, out=None, a_layout=None, stream=None):
-    """a_layout defaults to TILED when a_codes is 3-D ([M/16, K/64, 512]), else NATURAL."""
+    """a_layout defaults to F6 for [M/32, K/64, 1536] codes (weights from
+    w4_pack_weights_f6), TILED for [M/16, K/64, 512], else NATURAL."""
     if a_layout is None:
-        a_layout = LAYOUT.TILED if a_codes.dim() == 3 else LAYOUT.NATURAL
+        if a_codes.dim() == 3:
+            a_layout = LAYOUT.F6 if a_codes.shape[-1] == 1536 else LAYOUT.TILED
+        else:
+            a_layout = LAYOUT.NATURAL
     out = _out(M, N, out_type, a_codes.device, out)
     lora_f32 = int(lora_act is not None and lora_act.dtype == torch.float32)
     R = 0 if lora_up is None else lora_up.shape[1]

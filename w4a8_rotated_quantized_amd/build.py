@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libconvrot.so")
-SOURCES = ["rq.hip", "pack.hip", "merge.hip", "gemm_w4a4.hip", "gemm_int.hip", "gemm_w4a8.hip", "abi.cpp"]
+SOURCES = ["rq.hip", "pack.hip", "merge.hip", "gemm_w4a4.hip", "gemm_int.hip", "gemm_w4a8.hip", "gemm_f6.hip", "abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

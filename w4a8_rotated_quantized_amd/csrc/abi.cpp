@@ -155,9 +155,14 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
   cr_status st = rq_validate(x, rows, K, ldx, rot_group, qtype, gran, q_group, lora_down, R, lora_act,
                              codes, scales, zeros);
   if (st != CR_OK) return st;
-  if ((int)layout < 0 || (int)layout > 1) return CR_ERR_INVALID_ARGUMENT;
+  if (!((int)layout == CR_LAYOUT_NATURAL || (int)layout == CR_LAYOUT_TILED || (int)layout == CR_LAYOUT_F6))
+    return CR_ERR_INVALID_ARGUMENT;
   if (layout == CR_LAYOUT_TILED && !(qtype == CR_Q_SYM_INT4 || qtype == CR_Q_UNSIGNED_INT4_SHIFT))
     return CR_ERR_UNSUPPORTED_FORMAT;
+  if (layout == CR_LAYOUT_F6) {   // signed INT4 codes of a rotated path; the rows pad to 32
+    if (qtype != CR_Q_SYM_INT4 || rot_group == 0) return CR_ERR_UNSUPPORTED_FORMAT;
+    if (((rows + 31) / 32) * (K / 64) * 1536 >= ((int64_t)1 << 32)) return CR_ERR_UNSUPPORTED_SHAPE;
+  }
   if (smooth) {   // without rotation, or the 256 rotation with per-row / per-64-group scales
     if (!aligned16(smooth)) return CR_ERR_INVALID_ARGUMENT;
     if (rot_group != 0 && !(rot_group == 256 && (gran == CR_GRAN_ROW || gran == CR_GRAN_ROW_GROUP) &&
@@ -190,7 +195,7 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
   p.scales = scales;
   p.zeros = zeros;
   p.ws = static_cast<float*>(workspace);
-  p.tiled = layout == CR_LAYOUT_TILED ? 1 : 0;
+  p.tiled = layout == CR_LAYOUT_TILED ? 1 : (layout == CR_LAYOUT_F6 ? 2 : 0);
   const uint64_t nl = ((rot_group != 0 && gran == CR_GRAN_TENSOR && qtype != CR_Q_ASYM_UINT4) ? 2 : 1) +
                       ((rot_group != 0 && lora_down) ? 1 : 0);
   return finish_launch(cr::launch_rotate_quantize(p, stream), E_RQ, nl);
@@ -204,7 +209,10 @@ cr_status convrot_rotate_quantize_dual(const void* x, int64_t rows, int64_t K, i
                              codes4, scale4, nullptr);
   if (st != CR_OK) return st;
   if (!codes8 || !scale8 || !aligned16(codes8) || !aligned16(scale8)) return CR_ERR_INVALID_ARGUMENT;
-  if ((int)layout4 < 0 || (int)layout4 > 1) return CR_ERR_INVALID_ARGUMENT;
+  if (!((int)layout4 == CR_LAYOUT_NATURAL || (int)layout4 == CR_LAYOUT_TILED || (int)layout4 == CR_LAYOUT_F6))
+    return CR_ERR_INVALID_ARGUMENT;
+  if (layout4 == CR_LAYOUT_F6 && ((rows + 31) / 32) * (K / 64) * 1536 >= ((int64_t)1 << 32))
+    return CR_ERR_UNSUPPORTED_SHAPE;
   const size_t need = convrot_rq_workspace_size(rows, K, rot_group, CR_Q_SYM_INT4, CR_GRAN_TENSOR, 0);
   if (!workspace || !aligned16(workspace)) return CR_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < need) return CR_ERR_WORKSPACE_TOO_SMALL;
@@ -223,7 +231,7 @@ cr_status convrot_rotate_quantize_dual(const void* x, int64_t rows, int64_t K, i
   p.codes8 = codes8;
   p.scales8 = scale8;
   p.ws = static_cast<float*>(workspace);
-  p.tiled = layout4 == CR_LAYOUT_TILED ? 1 : 0;
+  p.tiled = layout4 == CR_LAYOUT_TILED ? 1 : (layout4 == CR_LAYOUT_F6 ? 2 : 0);
   return finish_launch(cr::launch_rotate_quantize_dual(p, stream), E_RQ, 2);
 }
 
@@ -288,6 +296,22 @@ size_t w4_packed_bytes(int64_t N, int64_t K, cr_qtype qtype, cr_gran gran, int q
     case 2: return qtype == CR_Q_ASYM_UINT4 ? (size_t)(N * (K / 16)) : 0;
   }
   return 0;
+}
+
+size_t w4_packed_f6_bytes(int64_t N, int64_t K) {
+  if (N < 128 || K < 128 || N % 128 || K % 128) return 0;
+  return (size_t)((N / 32) * (K / 64) * 1536);
+}
+
+cr_status w4_pack_weights_f6(const void* codes, int64_t N, int64_t K, void* packed, hipStream_t stream) {
+  if (!codes || !packed || !aligned16(codes) || !aligned16(packed)) return CR_ERR_INVALID_ARGUMENT;
+  if (N < 128 || K < 128 || N % 128 || K % 128 || K > KMAX || N >= DIM_MAX) return CR_ERR_UNSUPPORTED_SHAPE;
+  if ((N / 32) * (K / 64) * 1536 >= ((int64_t)1 << 32)) return CR_ERR_UNSUPPORTED_SHAPE;
+  cr_status st = device_check();
+  if (st != CR_OK) return st;
+  return finish_launch(cr::launch_pack_f6(static_cast<const uint8_t*>(codes), N, K, static_cast<uint8_t*>(packed),
+                                          stream),
+                       E_PACK, 1);
 }
 
 cr_status w4_pack_weights(const void* codes, const void* scales, const void* zeros, int64_t N, int64_t K,
@@ -357,9 +381,16 @@ cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
   if (st != CR_OK) return st;
   if (!a_scales || !w_scales || !aligned16(a_scales) || !aligned16(w_scales)) return CR_ERR_INVALID_ARGUMENT;
   if ((int)a_gran < 0 || (int)a_gran > 2 || (int)w_gran < 0 || (int)w_gran > 2) return CR_ERR_INVALID_ARGUMENT;
-  if ((int)a_layout < 0 || (int)a_layout > 2) return CR_ERR_INVALID_ARGUMENT;
+  if ((int)a_layout < 0 || (int)a_layout > 3) return CR_ERR_INVALID_ARGUMENT;
   const bool a8 = a_layout == CR_LAYOUT_INT8;
-  if (((M + 15) / 16) * 16 * (a8 ? K : K / 2) >= ((int64_t)1 << 32) || N * (K / 2) >= ((int64_t)1 << 32))
+  const bool f6 = a_layout == CR_LAYOUT_F6;
+  if (f6) {   // fp6 fragments on both sides: signed codes, per-tensor / per-row scales, no low-rank branch
+    if (a_unsigned || a_gran == CR_GRAN_ROW_GROUP || w_gran == CR_GRAN_ROW_GROUP || lora_act || lora_up)
+      return CR_ERR_UNSUPPORTED_FORMAT;
+    if (((M + 31) / 32) * (K / 64) * 1536 >= ((int64_t)1 << 32) || (N / 32) * (K / 64) * 1536 >= ((int64_t)1 << 32))
+      return CR_ERR_UNSUPPORTED_SHAPE;
+  }
+  if (!f6 && (((M + 15) / 16) * 16 * (a8 ? K : K / 2) >= ((int64_t)1 << 32) || N * (K / 2) >= ((int64_t)1 << 32)))
     return CR_ERR_UNSUPPORTED_SHAPE;
   const bool grouped = a_gran == CR_GRAN_ROW_GROUP;
   if (grouped != (w_gran == CR_GRAN_ROW_GROUP)) return CR_ERR_UNSUPPORTED_FORMAT;
@@ -398,6 +429,7 @@ cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
   p.grouped = grouped ? 1 : 0;
   p.a_tiled = a_layout == CR_LAYOUT_TILED ? 1 : 0;
   if (a8) return finish_launch(cr::launch_gemm_a8w4(p, stream), E_W4A4, 1);
+  if (f6) return finish_launch(cr::launch_gemm_f6(p, stream), E_W4A4, 1);
   return finish_launch(cr::launch_gemm_w4a4(p, stream), E_W4A4, 1);
 }
 

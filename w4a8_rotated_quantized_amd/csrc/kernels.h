@@ -25,7 +25,8 @@ struct RQParams {
   int G;                // 256-groups per row
   int rpb;              // rows per block (16 >> lg_spr)
   int lg_spr;           // log2(16-lane segments per row)
-  int tiled;            // int4 codes in the [rows/16][K/64][512 B] fragment layout
+  int tiled;            // int4 codes: 0 natural, 1 [rows/16][K/64][512 B] int8-core fragments,
+                        // 2 fp6 E2M3 fragments [rows/32][K/64][1536 B]
   void* codes8;         // dual output: int8 codes [rows, K] (codes / scales hold the int4 set)
   void* scales8;
   const float* smooth;  // optional per-channel multiplier [K] applied to x first
@@ -58,6 +59,8 @@ struct PackParams {
   float* w_sum;
 };
 hipError_t launch_pack(const PackParams& p, hipStream_t s);
+// natural int4 [N, K/2] -> fp6 E2M3 fragments [N/32][K/64][1536 B]
+hipError_t launch_pack_f6(const uint8_t* codes, int64_t N, int64_t K, uint8_t* packed, hipStream_t s);
 
 struct MergeParams {
   const uint8_t* codes;      // natural codes: int4 [N, K/2] (SYM_INT4, ASYM_UINT4) or int8 [N, K]
@@ -105,5 +108,6 @@ hipError_t launch_gemm_int(const GemmParams& p, hipStream_t s);   // INT8 x INT8
 hipError_t launch_gemm_a8w4(const GemmParams& p, hipStream_t s);  // INT8 x tile-packed INT4
 hipError_t launch_gemm_w4a4(const GemmParams& p, hipStream_t s);  // INT4 x tile-packed INT4
 hipError_t launch_gemm_w4a8(const GemmParams& p, hipStream_t s);
+hipError_t launch_gemm_f6(const GemmParams& p, hipStream_t s);    // fp6 fragments x fp6 fragments
 
 }  // namespace cr

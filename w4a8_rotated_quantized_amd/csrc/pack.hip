@@ -154,6 +154,43 @@ __global__ __launch_bounds__(256) void wsum_asym_kernel(PackParams p) {
 
 static inline unsigned nblocks(int64_t n) { return (unsigned)((n + 255) / 256); }
 
+// Natural signed int4 codes -> the fp6 E2M3 fragment layout of the fp6
+// matrix-core GEMM ([N/32][K/64][1536 B]; lane l of a fragment holds row
+// l % 32, columns 32 (l / 32) .. +31 of its 64-deep k-tile as six-bit fields,
+// bytes 0..15 at l * 16 and 16..23 at 1024 + l * 8). One thread per lane
+// slot, consecutive threads on consecutive slots. Natural byte j holds
+// columns 2j (low nibble) and 2j + 1 (high), and the conversion interleaves
+// its two sources the same way (field 2i from the first, 2i + 1 from the
+// second), so the fields come out in column order. Codes in [-7, 7] are
+// E2M3 values; the conversion is exact.
+__global__ __launch_bounds__(256) void pack_f6_kernel(const uint8_t* __restrict__ codes, int64_t N, int64_t K,
+                                                      uint8_t* __restrict__ packed) {
+  const int64_t KT = K / 64;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= (N / 32) * KT * 64) return;     // one thread per fragment lane slot
+  const int lm = (int)(c & 63);
+  const int64_t rest = c >> 6;
+  const int64_t kt = rest % KT, rb = rest / KT;
+  const int64_t row = rb * 32 + (lm & 31);
+  const u32x4 x = *reinterpret_cast<const u32x4*>(codes + row * (K / 2) + kt * 32 + (lm >> 5) * 16);
+  v16f lo, hi;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t b = (x[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+    lo[j] = (float)((int)(b << 28) >> 28);
+    hi[j] = (float)((int)(b << 24) >> 28);
+  }
+  const auto o = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(lo, hi, 1.0f);
+  uint8_t* frag = packed + rest * 1536;
+  *reinterpret_cast<u32x4*>(frag + lm * 16) = u32x4{o[0], o[1], o[2], o[3]};
+  *reinterpret_cast<u32x2*>(frag + 1024 + lm * 8) = u32x2{o[4], o[5]};
+}
+
+hipError_t launch_pack_f6(const uint8_t* codes, int64_t N, int64_t K, uint8_t* packed, hipStream_t s) {
+  hipLaunchKernelGGL(pack_f6_kernel, dim3(nblocks((N / 32) * (K / 64) * 64)), dim3(256), 0, s, codes, N, K, packed);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack(const PackParams& p, hipStream_t s) {
   if (p.qtype == CR_Q_ASYM_UINT4) {
     hipLaunchKernelGGL(pack_asym_kernel, dim3(nblocks(p.N * p.K / 8)), dim3(256), 0, s, p);

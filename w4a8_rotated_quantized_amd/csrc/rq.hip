@@ -89,6 +89,44 @@ CR_DEV uint8_t* code_dst(const RQParams& a, int64_t row, int grp, int gL) {
   }
 }
 
+// fp6 E2M3 fragment layout (INT4 codes for the fp6 matrix-core GEMM): the
+// lane's 16 codes (k = 256 grp + 16 gL + e) are half gL & 1 of fragment lane
+// 32 ((gL >> 1) & 1) + row % 32 in the 1536-byte fragment of row block
+// row / 32 and k-tile 4 grp + gL / 4; that lane's bytes 0..15 sit at
+// lane * 16 and bytes 16..23 at 1024 + lane * 8, so half 0 is three words at
+// lane * 16 and half 1 one word at lane * 16 + 12 and two at 1024 + lane * 8.
+// Each code is the rounded integer as a float (adding and removing
+// 1.5 * 2^23 rounds half to even and turns -0 into +0), converted exactly;
+// the conversion interleaves its two sources (field 2i from the first,
+// 2i + 1 from the second).
+CR_DEV void quant_store_f6(const float (&v)[16], float rs, const RQParams& a, int64_t row, int grp, int gL) {
+  v16f s0, s1;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float r0 = dreg_neg(2 * i) ? -rs : rs, r1 = dreg_neg(2 * i + 1) ? -rs : rs;
+    s0[i] = __fsub_rn(__fadd_rn(__fmul_rn(v[2 * i], r0), CR_MAGIC_RNE), CR_MAGIC_RNE);
+    s1[i] = __fsub_rn(__fadd_rn(__fmul_rn(v[2 * i + 1], r1), CR_MAGIC_RNE), CR_MAGIC_RNE);
+    s0[8 + i] = 0.f;
+    s1[8 + i] = 0.f;
+  }
+  const auto o = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(s0, s1, 1.0f);
+  uint8_t* frag = reinterpret_cast<uint8_t*>(a.codes) + ((row >> 5) * (a.K / 64) + grp * 4 + (gL >> 2)) * 1536;
+  const int lm = ((gL >> 1) & 1) * 32 + (int)(row & 31);
+  const bool h = gL & 1;
+  uint32_t* w0 = reinterpret_cast<uint32_t*>(frag + lm * 16 + (h ? 12 : 0));
+  uint32_t* w1 = h ? reinterpret_cast<uint32_t*>(frag + 1024 + lm * 8) : w0 + 1;
+  w0[0] = o[0];
+  w1[0] = o[1];
+  w1[1] = o[2];
+}
+
+// codes of one lane in the layout the parameters ask for
+template <int QT>
+CR_DEV void store_codes(const float (&v)[16], float rs, const RQParams& a, int64_t row, int grp, int gL) {
+  if (QT == CR_Q_SYM_INT4 && a.tiled == 2) quant_store_f6(v, rs, a, row, grp, gL);
+  else quant_store<QT>(v, rs, code_dst<QT>(a, row, grp, gL));
+}
+
 // ---------------------------------------------------------------------------
 // rq_rot: rotation on, one launch: per-row scales (RG_ROW), per-64-group
 // scales (RG_G64) and asymmetric 16-group weights (RG_ASYM).
@@ -174,7 +212,7 @@ __global__ __launch_bounds__(256) void rq_rot_kernel(RQParams a) {
     const float r = (A > 0.f) ? div_rn(qmax, A) : 0.f;
 #pragma unroll
     for (int i = 0; i < GPS; ++i)
-      if (ok[i]) quant_store<QT>(v[i], csg[i] * r, code_dst<QT>(a, crow_i, g0 + gstep * i, lr.gL));
+      if (ok[i]) store_codes<QT>(v[i], csg[i] * r, a, crow_i, g0 + gstep * i, lr.gL);
   } else if constexpr (GR == RG_G64) {
     // 64-group = bits b0..b5: the quad of lanes sharing (b6, b7) = (L2, L3)
 #pragma unroll
@@ -189,7 +227,7 @@ __global__ __launch_bounds__(256) void rq_rot_kernel(RQParams a) {
         reinterpret_cast<float*>(a.scales)[row * (a.K / 64) + grp * 4 + (L >> 2)] = s;
       }
       const float r = (m > 0.f) ? div_rn(qmax, m) : 0.f;
-      if (ok[i]) quant_store<QT>(v[i], csg[i] * r, code_dst<QT>(a, crow_i, grp, lr.gL));
+      if (ok[i]) store_codes<QT>(v[i], csg[i] * r, a, crow_i, grp, lr.gL);
     }
   } else {  // RG_ASYM: asymmetric uint4 per 16 consecutive rotated channels = one lane
 #pragma unroll
@@ -348,7 +386,7 @@ __global__ __launch_bounds__(256) void rq_tensor_kernel(RQParams a) {
         rotate_group<NR>(w[j], lr, v);
       }
       const float sg = (NR == 1024 && chunk_neg(j)) ? -1.f : 1.f;
-      quant_store<QT>(v, sg * rq, code_dst<QT>(a, row, grp[j], lr.gL));
+      store_codes<QT>(v, sg * rq, a, row, grp[j], lr.gL);
       if constexpr (PASS == 2) quant_store<CR_Q_SYM_INT8>(v, sg * rq8, code_dst<CR_Q_SYM_INT8>(a8, row, grp[j], lr.gL));
     }
   }
