@@ -99,25 +99,59 @@ CR_DEV uint8_t* code_dst(const RQParams& a, int64_t row, int grp, int gL) {
 // 1.5 * 2^23 rounds half to even and turns -0 into +0), converted exactly;
 // the conversion interleaves its two sources (field 2i from the first,
 // 2i + 1 from the second).
-CR_DEV void quant_store_f6(const float (&v)[16], float rs, const RQParams& a, int64_t row, int grp, int gL) {
+CR_DEV float f6_qval(float v, float r) {   // the rounded integer code as a float (+0 for zero)
+  return __fsub_rn(__fadd_rn(__fmul_rn(v, r), CR_MAGIC_RNE), CR_MAGIC_RNE);
+}
+
+// codes of two groups' 16 values (the second may be a copy of the first):
+// words 0..2 hold the first group's 16 six-bit fields, words 3..5 the second's
+CR_DEV u32x4 f6_pack2(const float (&v0)[16], float rs0, const float (&v1)[16], float rs1, uint32_t (&w45)[2]) {
   v16f s0, s1;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float r0 = dreg_neg(2 * i) ? -rs : rs, r1 = dreg_neg(2 * i + 1) ? -rs : rs;
-    s0[i] = __fsub_rn(__fadd_rn(__fmul_rn(v[2 * i], r0), CR_MAGIC_RNE), CR_MAGIC_RNE);
-    s1[i] = __fsub_rn(__fadd_rn(__fmul_rn(v[2 * i + 1], r1), CR_MAGIC_RNE), CR_MAGIC_RNE);
-    s0[8 + i] = 0.f;
-    s1[8 + i] = 0.f;
+    s0[i] = f6_qval(v0[2 * i], dreg_neg(2 * i) ? -rs0 : rs0);
+    s1[i] = f6_qval(v0[2 * i + 1], dreg_neg(2 * i + 1) ? -rs0 : rs0);
+    s0[8 + i] = f6_qval(v1[2 * i], dreg_neg(2 * i) ? -rs1 : rs1);
+    s1[8 + i] = f6_qval(v1[2 * i + 1], dreg_neg(2 * i + 1) ? -rs1 : rs1);
   }
   const auto o = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(s0, s1, 1.0f);
-  uint8_t* frag = reinterpret_cast<uint8_t*>(a.codes) + ((row >> 5) * (a.K / 64) + grp * 4 + (gL >> 2)) * 1536;
+  w45[0] = o[4];
+  w45[1] = o[5];
+  return u32x4{o[0], o[1], o[2], o[3]};
+}
+
+CR_DEV uint8_t* f6_frag(const RQParams& a, int64_t row, int grp, int gL) {
+  return reinterpret_cast<uint8_t*>(a.codes) + ((row >> 5) * (a.K / 64) + grp * 4 + (gL >> 2)) * 1536;
+}
+
+// the three words of one lane's half (any lane activity: plain word stores)
+CR_DEV void f6_store_words(uint32_t c0, uint32_t c1, uint32_t c2, const RQParams& a, int64_t row, int grp, int gL) {
+  uint8_t* frag = f6_frag(a, row, grp, gL);
   const int lm = ((gL >> 1) & 1) * 32 + (int)(row & 31);
   const bool h = gL & 1;
   uint32_t* w0 = reinterpret_cast<uint32_t*>(frag + lm * 16 + (h ? 12 : 0));
   uint32_t* w1 = h ? reinterpret_cast<uint32_t*>(frag + 1024 + lm * 8) : w0 + 1;
-  w0[0] = o[0];
-  w1[0] = o[1];
-  w1[1] = o[2];
+  w0[0] = c0;
+  w1[0] = c1;
+  w1[1] = c2;
+}
+
+// the same with all 16 lanes of the DPP row active: the two halves of a
+// fragment lane sit in lanes L and L ^ 1 (gL and gL ^ 1), so half 0 takes its
+// partner's first word and stores the lane's bytes 0..15 at once, and half 1
+// stores bytes 16..23
+CR_DEV void f6_store_pair(uint32_t c0, uint32_t c1, uint32_t c2, const RQParams& a, int64_t row, int grp, int gL) {
+  const uint32_t p0 = (uint32_t)dpp_i<DPP_QUAD_1032>((int)c0);
+  uint8_t* frag = f6_frag(a, row, grp, gL);
+  const int lm = ((gL >> 1) & 1) * 32 + (int)(row & 31);
+  if ((gL & 1) == 0) *reinterpret_cast<u32x4*>(frag + lm * 16) = u32x4{c0, c1, c2, p0};
+  else *reinterpret_cast<u32x2*>(frag + 1024 + lm * 8) = u32x2{c1, c2};
+}
+
+CR_DEV void quant_store_f6(const float (&v)[16], float rs, const RQParams& a, int64_t row, int grp, int gL) {
+  uint32_t w45[2];
+  const u32x4 o = f6_pack2(v, rs, v, rs, w45);
+  f6_store_words(o[0], o[1], o[2], a, row, grp, gL);
 }
 
 // codes of one lane in the layout the parameters ask for
@@ -376,18 +410,47 @@ __global__ __launch_bounds__(256) void rq_tensor_kernel(RQParams a) {
     const float rq8 = lr.tau * ((A > 0.f) ? div_rn(127.f, A) : 0.f);   // PASS 2 only
     RQParams a8 = a;
     a8.codes = a.codes8;
+    if (QT == CR_Q_SYM_INT4 && a.tiled == 2) {
+      // fp6 fragments: two groups per conversion, every lane of the row active
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      float v[16];
-      if constexpr (NR == 1024) {
+      for (int j = 0; j < J; j += 2) {
+        const int j1 = (j + 1 < J) ? j + 1 : j;
+        float v0[16], v1[16];
+        if constexpr (NR == 1024) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) v[e] = vall[j][e];
-      } else {
-        rotate_group<NR>(w[j], lr, v);
+          for (int e = 0; e < 16; ++e) {
+            v0[e] = vall[j][e];
+            v1[e] = vall[j1][e];
+          }
+        } else {
+          rotate_group<NR>(w[j], lr, v0);
+          rotate_group<NR>(w[j1], lr, v1);
+        }
+        const float sg0 = (NR == 1024 && chunk_neg(j)) ? -1.f : 1.f;
+        const float sg1 = (NR == 1024 && chunk_neg(j1)) ? -1.f : 1.f;
+        uint32_t w45[2];
+        const u32x4 o = f6_pack2(v0, sg0 * rq, v1, sg1 * rq, w45);
+        f6_store_pair(o[0], o[1], o[2], a, row, grp[j], lr.gL);
+        if (j + 1 < J) f6_store_pair(o[3], w45[0], w45[1], a, row, grp[j1], lr.gL);
+        if constexpr (PASS == 2) {
+          quant_store<CR_Q_SYM_INT8>(v0, sg0 * rq8, code_dst<CR_Q_SYM_INT8>(a8, row, grp[j], lr.gL));
+          if (j + 1 < J) quant_store<CR_Q_SYM_INT8>(v1, sg1 * rq8, code_dst<CR_Q_SYM_INT8>(a8, row, grp[j1], lr.gL));
+        }
       }
-      const float sg = (NR == 1024 && chunk_neg(j)) ? -1.f : 1.f;
-      store_codes<QT>(v, sg * rq, a, row, grp[j], lr.gL);
-      if constexpr (PASS == 2) quant_store<CR_Q_SYM_INT8>(v, sg * rq8, code_dst<CR_Q_SYM_INT8>(a8, row, grp[j], lr.gL));
+    } else {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        float v[16];
+        if constexpr (NR == 1024) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) v[e] = vall[j][e];
+        } else {
+          rotate_group<NR>(w[j], lr, v);
+        }
+        const float sg = (NR == 1024 && chunk_neg(j)) ? -1.f : 1.f;
+        store_codes<QT>(v, sg * rq, a, row, grp[j], lr.gL);
+        if constexpr (PASS == 2) quant_store<CR_Q_SYM_INT8>(v, sg * rq8, code_dst<CR_Q_SYM_INT8>(a8, row, grp[j], lr.gL));
+      }
     }
   }
 }
