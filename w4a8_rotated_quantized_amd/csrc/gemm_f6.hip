@@ -82,10 +82,11 @@ CR_DEV void f6_wait_stage(int ahead) {   // at most `ahead` later stages (L load
   else f6_wait_vmcnt<0>();
 }
 
-template <int BM, int BN, int WN, int BKT, int S, int MINB, int OUT>
-__global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, MINB) void gemm_f6_kernel(GemmParams p) {
-  constexpr int NW = (BM / 64) * (BN / 64);
-  static_assert(BN / 64 == WN, "waves of 64 x 64");
+template <int BM, int BN, int TM, int TN, int BKT, int S, int MINB, int OUT>
+__global__ __launch_bounds__((BM / (32 * TM)) * (BN / (32 * TN)) * 64, MINB) void gemm_f6_kernel(GemmParams p) {
+  constexpr int WN = BN / (32 * TN);                   // waves along the channels
+  constexpr int NW = (BM / (32 * TM)) * WN;
+  static_assert(BM % (32 * TM) == 0 && BN % (32 * TN) == 0, "whole wave tiles");
   static_assert(S >= 2 && S <= 6, "stages in flight ahead of the current one: 0 to 4");
   constexpr int A_ST = (BM / 32) * BKT * F6_FRAG, W_ST = (BN / 32) * BKT * F6_FRAG;
   constexpr int STAGE = A_ST + W_ST;
@@ -94,8 +95,8 @@ __global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, MINB) void gemm_f6_kern
   constexpr int LPW = (NL + NW - 1) / NW;              // wave-loads of the busiest waves
   constexpr int NHI = NL - (LPW - 1) * NW;             // waves 0 .. NHI-1 take LPW, the others LPW - 1
   constexpr int RUN = BKT * F6_FRAG / 16;              // 16-byte pieces per 32-row block and stage
-  constexpr int RS = 144;                              // epilogue: LDS row stride of a wave's 64 x 64 bf16 tile
-  constexpr int SMEM = (S * STAGE > NW * 64 * RS) ? S * STAGE : NW * 64 * RS;
+  constexpr int RS = TN * 64 + 16;                     // epilogue: LDS row stride of a wave's bf16 tile
+  constexpr int SMEM = (S * STAGE > NW * TM * 32 * RS) ? S * STAGE : NW * TM * 32 * RS;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
   const int tid = threadIdx.x;
@@ -158,11 +159,11 @@ __global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, MINB) void gemm_f6_kern
     }
   };
 
-  v16f acc[2][2];
+  v16f acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+    for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
 
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
@@ -173,37 +174,37 @@ __global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, MINB) void gemm_f6_kern
     if (kb + S - 1 < nkb) issue(kb + S - 1);
     const uint8_t* As = smem + (kb % S) * STAGE;
     const uint8_t* Ws = As + A_ST;
-    v8i av[2][2], wv[2][2];
+    v8i av[2][TM], wv[2][TN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) av[0][i] = frag_f6(As + ((wm * 2 + i) * BKT) * F6_FRAG, l);
+    for (int i = 0; i < TM; ++i) av[0][i] = frag_f6(As + ((wm * TM + i) * BKT) * F6_FRAG, l);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) wv[0][j] = frag_f6(Ws + ((wn * 2 + j) * BKT) * F6_FRAG, l);
+    for (int j = 0; j < TN; ++j) wv[0][j] = frag_f6(Ws + ((wn * TN + j) * BKT) * F6_FRAG, l);
 #pragma unroll
     for (int kt = 0; kt < BKT; ++kt) {
       const int cb = kt & 1;
       if (kt + 1 < BKT) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) av[cb ^ 1][i] = frag_f6(As + ((wm * 2 + i) * BKT + kt + 1) * F6_FRAG, l);
+        for (int i = 0; i < TM; ++i) av[cb ^ 1][i] = frag_f6(As + ((wm * TM + i) * BKT + kt + 1) * F6_FRAG, l);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) wv[cb ^ 1][j] = frag_f6(Ws + ((wn * 2 + j) * BKT + kt + 1) * F6_FRAG, l);
+        for (int j = 0; j < TN; ++j) wv[cb ^ 1][j] = frag_f6(Ws + ((wn * TN + j) * BKT + kt + 1) * F6_FRAG, l);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f6_32(wv[cb][j], av[cb][i], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_f6_32(wv[cb][j], av[cb][i], acc[i][j]);
     }
   }
 
   // ---- epilogue: every input loaded before the first store ----
   if constexpr (OUT == CR_OUT_I32_RAW) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t m = m0 + (wm * 2 + i) * 32 + (l & 31);
+    for (int i = 0; i < TM; ++i) {
+      const int64_t m = m0 + (wm * TM + i) * 32 + (l & 31);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int64_t n = n0 + (wn * 2 + j) * 32 + 8 * g + 4 * (l >> 5);
+          const int64_t n = n0 + (wn * TN + j) * 32 + 8 * g + 4 * (l >> 5);
           float y[4] = {0.f, 0.f, 0.f, 0.f};
           int raw[4];
 #pragma unroll
@@ -214,34 +215,34 @@ __global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, MINB) void gemm_f6_kern
   } else {
     const float sa_t = (p.a_gran == CR_GRAN_TENSOR) ? p.a_scales[0] : 0.f;
     const float sw_t = (p.w_gran == CR_GRAN_TENSOR) ? p.w_scales[0] : 0.f;
-    float sa[2];
-    v4f sw[2][4];
-    u32x2 bias[2][4];
+    float sa[TM];
+    v4f sw[TN][4];
+    u32x2 bias[TN][4];
     if constexpr (OUT == CR_OUT_BF16) {
       // y = s_a s_w acc + bias, rounded to bf16 (v_cvt_pk_bf16_f32, half to
       // even), then the wave's 64 x 64 tile passes through LDS so that every
       // store writes whole 128-byte output rows (the fragment layout would
       // scatter 16-byte pieces over 32 rows per instruction)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int64_t m = m0 + (wm * 2 + i) * 32 + (l & 31);
+      for (int i = 0; i < TM; ++i) {
+        const int64_t m = m0 + (wm * TM + i) * 32 + (l & 31);
         sa[i] = (p.a_gran == CR_GRAN_TENSOR) ? sa_t : p.a_scales[m < p.M ? m : p.M - 1];
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int64_t n = n0 + (wn * 2 + j) * 32 + 8 * g + 4 * (l >> 5);
+          const int64_t n = n0 + (wn * TN + j) * 32 + 8 * g + 4 * (l >> 5);
           sw[j][g] = (p.w_gran == CR_GRAN_TENSOR) ? v4f{sw_t, sw_t, sw_t, sw_t}
                                                   : *reinterpret_cast<const v4f*>(p.w_scales + n);
           bias[j][g] = p.bias ? *reinterpret_cast<const u32x2*>(p.bias + n) : u32x2{0u, 0u};
         }
       __syncthreads();                              // every wave is done with the stage buffers
-      uint8_t* tile = smem + wave * (64 * RS);
+      uint8_t* tile = smem + wave * (TM * 32 * RS);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             float y[4];
@@ -259,38 +260,40 @@ __global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, MINB) void gemm_f6_kern
                 u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
           }
       f6_wait_vmcnt<63>();                          // this wave's tile writes are done (LDS is in order per wave)
+      constexpr int PR = TN * 4;                    // 16-byte pieces per tile row
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int r = (l >> 3) + 8 * q;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * RS + (l & 7) * 16);
-        const int64_t m = m0 + wm * 64 + r;
+      for (int q = 0; q < TM * 32 * PR / 64; ++q) {
+        const int pc = q * 64 + l;
+        const int r = pc / PR, c = pc % PR;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * RS + c * 16);
+        const int64_t m = m0 + wm * TM * 32 + r;
         if (m < p.M)
-          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.out) + m * p.ldc + n0 + wn * 64 + (l & 7) * 8) = v;
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.out) + m * p.ldc + n0 + wn * TN * 32 + c * 8) = v;
       }
       return;
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t m = m0 + (wm * 2 + i) * 32 + (l & 31);
+    for (int i = 0; i < TM; ++i) {
+      const int64_t m = m0 + (wm * TM + i) * 32 + (l & 31);
       sa[i] = (p.a_gran == CR_GRAN_TENSOR) ? sa_t : p.a_scales[m < p.M ? m : p.M - 1];
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t n = n0 + (wn * 2 + j) * 32 + 8 * g + 4 * (l >> 5);
+        const int64_t n = n0 + (wn * TN + j) * 32 + 8 * g + 4 * (l >> 5);
         sw[j][g] = (p.w_gran == CR_GRAN_TENSOR) ? v4f{sw_t, sw_t, sw_t, sw_t}
                                                 : *reinterpret_cast<const v4f*>(p.w_scales + n);
         bias[j][g] = p.bias ? *reinterpret_cast<const u32x2*>(p.bias + n) : u32x2{0u, 0u};
       }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t m = m0 + (wm * 2 + i) * 32 + (l & 31);
+    for (int i = 0; i < TM; ++i) {
+      const int64_t m = m0 + (wm * TM + i) * 32 + (l & 31);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int64_t n = n0 + (wn * 2 + j) * 32 + 8 * g + 4 * (l >> 5);
+          const int64_t n = n0 + (wn * TN + j) * 32 + 8 * g + 4 * (l >> 5);
           float y[4];
           const int raw[4] = {0, 0, 0, 0};
 #pragma unroll
@@ -416,11 +419,11 @@ static hipError_t launch_f6_out(const GemmParams& p, hipStream_t s) {
   // three per CU
   if (p.N % 192 == 0 && ((p.M + 255) / 256) * (p.N / 192) >= 256) {
     const int64_t tiles = ((p.M + 255) / 256) * (p.N / 192);
-    hipLaunchKernelGGL((gemm_f6_kernel<256, 192, 3, 2, 3, 1, OUT>), dim3((unsigned)tiles), dim3(768), 0, s, p);
+    hipLaunchKernelGGL((gemm_f6_kernel<256, 192, 2, 2, 2, 3, 1, OUT>), dim3((unsigned)tiles), dim3(768), 0, s, p);
     return hipGetLastError();
   }
   const int64_t tiles = ((p.M + 127) / 128) * (p.N / 128);
-  hipLaunchKernelGGL((gemm_f6_kernel<128, 128, 2, 2, 2, 3, OUT>), dim3((unsigned)tiles), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_f6_kernel<128, 128, 2, 2, 2, 2, 3, OUT>), dim3((unsigned)tiles), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
