@@ -178,6 +178,9 @@ typedef _Float16 v2h_ __attribute__((ext_vector_type(2)));
 typedef const void __attribute__((address_space(1)))* gas_ptr_w8;
 typedef void __attribute__((address_space(3)))* las_ptr_w8;
 
+typedef float v2f_ __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
 CR_DEV uint32_t h2_sub_mul(uint32_t a, uint32_t b, uint32_t c) {
   return __builtin_bit_cast(uint32_t, (__builtin_bit_cast(v2h_, a) - __builtin_bit_cast(v2h_, b)) *
                                           __builtin_bit_cast(v2h_, c));
@@ -395,6 +398,43 @@ __global__ __launch_bounds__(256, 2) void gemm_w4a8_h_kernel(GemmParams p) {
         __builtin_amdgcn_sched_barrier(0);          // one block's operands live at a time
       }
     }
+  }
+  if constexpr (OUT == CR_OUT_BF16) {
+    // bf16 (v_cvt_pk_bf16_f32, half to even) through LDS in two halves of 64
+    // token rows per wave, so that every store writes whole 128-byte output
+    // rows; the fragment layout would scatter 8-byte pieces over 32 rows per
+    // store instruction
+    constexpr int RS = 144;                          // LDS row stride of a half tile, 16-byte aligned
+    static_assert(4 * 64 * RS <= NS * STAGE, "half tiles fit the stage buffers");
+    __syncthreads();                                 // every wave is done with the stage buffers
+    uint8_t* tile = smem + wave * (64 * RS);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const v16f& a = acc[2 * hh + ii][j];
+            const v2bf lo = __builtin_convertvector((v2f_){a[4 * q], a[4 * q + 1]}, v2bf);
+            const v2bf hi = __builtin_convertvector((v2f_){a[4 * q + 2], a[4 * q + 3]}, v2bf);
+            *reinterpret_cast<u32x2*>(tile + (ii * 32 + lr) * RS + (j * 32 + 8 * q + 4 * h) * 2) =
+                u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+          }
+      // this wave's half tile is complete (LDS keeps a wave's order, so the
+      // next half's writes also land after these reads)
+      __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0)
+#pragma unroll
+      for (int qq = 0; qq < 8; ++qq) {
+        const int r = (l >> 3) + 8 * qq;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * RS + (l & 7) * 16);
+        const int64_t m = m0 + wm * 128 + hh * 64 + r;
+        if (m < p.M)
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.out) + m * p.ldc + n0 + wn * 64 + (l & 7) * 8) = v;
+      }
+    }
+    return;
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
