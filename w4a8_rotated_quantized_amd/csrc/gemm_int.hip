@@ -26,6 +26,9 @@
 
 namespace cr {
 
+typedef float v2f_i __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf_i __attribute__((ext_vector_type(2)));
+
 template <int ACT>
 CR_DEV v4i widen_act(const uint8_t* lds) {
   if constexpr (ACT == ACT_I8) {
@@ -591,6 +594,45 @@ __global__ __launch_bounds__(256, 2) void gemm_int8_lds_kernel(GemmParams p) {
         sw[j][q] = wrow ? *reinterpret_cast<const v4f*>(p.w_scales + n) : v4f{sw_t, sw_t, sw_t, sw_t};
         bw[j][q] = p.bias ? *reinterpret_cast<const u32x2*>(p.bias + n) : u32x2{0u, 0u};
       }
+  }
+  if constexpr (OUT == CR_OUT_BF16) {
+    // bf16 (v_cvt_pk_bf16_f32, half to even) through LDS in two halves of 64
+    // token rows per wave, so that every store writes whole 128-byte output
+    // rows instead of 8-byte pieces spread over 32 rows
+    constexpr int RS = 144;                          // LDS row stride of a half tile, 16-byte aligned
+    static_assert(4 * 64 * RS <= NS * STAGE, "half tiles fit the stage buffers");
+    __syncthreads();                                 // every wave is done with the stage buffers
+    uint8_t* tile = smem + wave * (64 * RS);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int i = 2 * hh + ii;
+            float y[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              y[e] = (float)acc[i][j][4 * q + e] * (sa[i] * sw[j][q][e]) +
+                     ((e & 1) ? bf16_hi(bw[j][q][e >> 1]) : bf16_lo(bw[j][q][e >> 1]));
+            const v2bf_i lo = __builtin_convertvector((v2f_i){y[0], y[1]}, v2bf_i);
+            const v2bf_i hi = __builtin_convertvector((v2f_i){y[2], y[3]}, v2bf_i);
+            *reinterpret_cast<u32x2*>(tile + (ii * 32 + lr) * RS + (j * 32 + 8 * q + 4 * h) * 2) =
+                u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+          }
+      __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0): this wave's half tile is written
+#pragma unroll
+      for (int qq = 0; qq < 8; ++qq) {
+        const int r = (l >> 3) + 8 * qq;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * RS + (l & 7) * 16);
+        const int64_t m = m0 + wm * 128 + hh * 64 + r;
+        if (m < p.M)
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.out) + m * p.ldc + n0 + wn * 64 + (l & 7) * 8) = v;
+      }
+    }
+    return;
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
