@@ -54,10 +54,10 @@ CR_DEV void lora_up_block(const GemmParams& p, int64_t mb, int64_t nb, int l, fl
   for (int i = 0; i < 4; ++i) y[i] += acc[i];
 }
 
-// Everything after the float value s_a*s_w*acc (or the group sum) is known.
+// Everything after the float value s_a*s_w*acc (or the group sum) is known:
+// shift correction, low-rank branch and bias, in place.
 template <int OUT>
-CR_DEV void finish_block(const GemmParams& p, int64_t m, int64_t n, int64_t mb, int l, float (&y)[4],
-                         const int (&raw)[4]) {
+CR_DEV void finish_values(const GemmParams& p, int64_t n, int64_t mb, int l, float (&y)[4]) {
   if constexpr (OUT != CR_OUT_I32_RAW) {
     if (p.act == ACT_U4) {
       const v4f ws = *reinterpret_cast<const v4f*>(p.w_sum + n);
@@ -73,6 +73,12 @@ CR_DEV void finish_block(const GemmParams& p, int64_t m, int64_t n, int64_t mb, 
       y[3] += bf16_hi(b[1]);
     }
   }
+}
+
+template <int OUT>
+CR_DEV void finish_block(const GemmParams& p, int64_t m, int64_t n, int64_t mb, int l, float (&y)[4],
+                         const int (&raw)[4]) {
+  finish_values<OUT>(p, n, mb, l, y);
   store4<OUT>(p, m, n, y, raw);
 }
 

@@ -30,6 +30,9 @@
 
 namespace cr {
 
+typedef float v2f_w __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf_w __attribute__((ext_vector_type(2)));
+
 template <int ACT>
 CR_DEV v4i widen_a4(u32x2 x) {
   return ACT == ACT_S4 ? widen_s4x16(x) : widen_u4(x);
@@ -490,6 +493,66 @@ __global__ __launch_bounds__(256, GRP ? 2 : 3) void gemm_w4a4_lds_kernel(GemmPar
         }
       }
     }
+  }
+
+  if constexpr (OUT == CR_OUT_BF16) {
+    // all values first (scales, shift correction, low-rank branch, bias), then
+    // bf16 through LDS in two halves of 32 token rows per wave, so that every
+    // store writes whole 128-byte output rows (the 16 x 16 fragment layout
+    // would write 32-byte pieces of 16 rows per instruction)
+    float yv[FM][FN][4];
+    const float sa_t = GRP ? 0.f : ((p.a_gran == CR_GRAN_TENSOR) ? p.a_scales[0] : 0.f);
+    const float sw_t = GRP ? 0.f : ((p.w_gran == CR_GRAN_TENSOR) ? p.w_scales[0] : 0.f);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t mb = m0 + (wm * FM + i) * 16;
+      const int64_t mc = imin64(mb + (l & 15), p.M - 1);
+      float sa = 0.f;
+      if constexpr (!GRP) sa = (p.a_gran == CR_GRAN_TENSOR) ? sa_t : p.a_scales[mc];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int64_t n = n0 + (wn * FN + j) * 16 + (l >> 4) * 4;
+        if constexpr (GRP) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) yv[i][j][e] = yacc[i][j][e];
+        } else {
+          v4f sw;
+          if (p.w_gran == CR_GRAN_TENSOR) sw = v4f{sw_t, sw_t, sw_t, sw_t};
+          else sw = *reinterpret_cast<const v4f*>(p.w_scales + n);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) yv[i][j][e] = (float)(acc[i][j][e] >> SH) * (sa * sw[e]);
+        }
+        finish_values<OUT>(p, n, mb, l, yv[i][j]);
+      }
+    }
+    constexpr int RS = 144;                            // LDS row stride of a 32 x 64 half tile
+    static_assert(4 * 32 * RS <= S * STAGE, "half tiles fit the stage buffers");
+    __syncthreads();                                   // every wave is done with the stage buffers
+    uint8_t* tile = smem + wave * (32 * RS);
+#pragma unroll
+    for (int hh = 0; hh < FM / 2; ++hh) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const float* y = yv[2 * hh + ii][j];
+          const v2bf_w lo = __builtin_convertvector((v2f_w){y[0], y[1]}, v2bf_w);
+          const v2bf_w hi = __builtin_convertvector((v2f_w){y[2], y[3]}, v2bf_w);
+          *reinterpret_cast<u32x2*>(tile + (ii * 16 + (l & 15)) * RS + (j * 16 + (l >> 4) * 4) * 2) =
+              u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        }
+      __builtin_amdgcn_s_waitcnt(0xC07F);              // lgkmcnt(0): this wave's half tile is written
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int r = (l >> 3) + 8 * qq;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * RS + (l & 7) * 16);
+        const int64_t m = m0 + wm * FM * 16 + hh * 32 + r;
+        if (m < p.M)
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.out) + m * p.ldc + n0 + wn * FN * 16 + (l & 7) * 8) =
+              v;
+      }
+    }
+    return;
   }
 
   if constexpr (GRP) {
