@@ -246,16 +246,33 @@ def e2m3_code_of_int(q) -> np.ndarray:
     return np.where(q < 0, code | 32, code).astype(np.uint8)
 
 
-def f6_pack(codes: np.ndarray) -> np.ndarray:
-    """Signed int4 codes int [rows, K] (values in [-7, 7]) -> uint8
-    [ceil(rows/32), K/64, 1536] fp6 E2M3 fragments (layout above)."""
+def e2m3_code_of_half(u) -> np.ndarray:
+    """The E2M3 code of u/2 for unsigned codes u in [0, 15]: every half-integer
+    0, 0.5, ..., 7.5 is an E2M3 value (0.5 a subnormal, 7.5 the largest normal)."""
+    u = np.asarray(u).astype(np.int64)
+    if np.any((u < 0) | (u > 15)):
+        raise ValueError("unsigned code outside [0, 15]")
+    out = np.zeros(u.shape, dtype=np.uint8)
+    for code in range(32):                     # the non-negative codes, by value
+        v = e2m3_value(code)
+        hit = (u == int(round(2 * v))) & (2 * v == np.round(2 * v))
+        out[hit & (out == 0)] = code
+    return out
+
+
+def f6_pack(codes: np.ndarray, unsigned: bool = False) -> np.ndarray:
+    """Int4 codes int [rows, K] -> uint8 [ceil(rows/32), K/64, 1536] fp6
+    E2M3 fragments (layout above). Signed codes (values in [-7, 7]) are
+    stored as themselves; unsigned codes u in [0, 15] (the shifted post-GELU
+    path) as the E2M3 value u/2, so a product sum over them is half the
+    integer one (exact)."""
     c = np.asarray(codes).astype(np.int64)
     rows, K = c.shape
     if K % 64:
         raise ValueError("K % 64 != 0")
     MB, KT = (rows + 31) // 32, K // 64
     f = np.zeros((MB * 32, K), dtype=np.int64)
-    f[:rows] = e2m3_code_of_int(c)
+    f[:rows] = e2m3_code_of_half(c) if unsigned else e2m3_code_of_int(c)
     # [b, r, kt, h, i] -> [b, kt, lane = 32 h + r, i]
     f = f.reshape(MB, 32, KT, 2, 32).transpose(0, 2, 3, 1, 4).reshape(MB, KT, 64, 32)
     # four 6-bit fields -> three bytes, little-endian
@@ -270,7 +287,8 @@ def f6_pack(codes: np.ndarray) -> np.ndarray:
 
 def f6_unpack(frags: np.ndarray, rows: int) -> np.ndarray:
     """Inverse of f6_pack: uint8 [MB, K/64, 1536] -> the real values of the
-    first `rows` rows, float64 [rows, K] (integers for codes written by f6_pack)."""
+    first `rows` rows, float64 [rows, K] (the signed codes, or u/2 for
+    unsigned codes)."""
     fr = np.asarray(frags, dtype=np.uint8)
     MB, KT, _ = fr.shape
     lane_bytes = np.concatenate([fr[:, :, :1024].reshape(MB, KT, 64, 16),

@@ -194,3 +194,21 @@ def test_f6_round_trip_and_dot_products():
     av, wv = pack.f6_unpack(pack.f6_pack(a), 45), pack.f6_unpack(pack.f6_pack(w), 64)
     assert np.array_equal(av, a) and np.array_equal(wv, w)
     assert np.array_equal((av @ wv.T).astype(np.int64), gemm.int_gemm(a, w))
+
+
+def test_e2m3_codes_of_unsigned_halves():
+    u = np.arange(16)
+    c = pack.e2m3_code_of_half(u)
+    assert np.array_equal(pack.e2m3_value(c) * 2, u)
+    assert c[1] == 0b000100          # 0.5 = subnormal 4/8
+    assert c[15] == 0b011111         # 7.5 = 2^2 * 1.875, the largest normal
+    assert c[3] == 0b001100          # 1.5 = 2^0 * 1.5
+    for bad in (-1, 16):
+        with pytest.raises(ValueError):
+            pack.e2m3_code_of_half(np.array([bad]))
+    rng = np.random.default_rng(12)
+    a = rng.integers(0, 16, size=(40, 128))
+    w = rng.integers(-7, 8, size=(64, 128))
+    av = pack.f6_unpack(pack.f6_pack(a, unsigned=True), 40)
+    assert np.array_equal(av * 2, a)
+    assert np.array_equal((2 * av @ pack.f6_unpack(pack.f6_pack(w), 64).T).astype(np.int64), gemm.int_gemm(a, w))
