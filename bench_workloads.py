@@ -87,8 +87,8 @@ def run_merge(steps, warmup):
 
 
 def run(name, steps, warmup, cores="fp6"):
-    """cores: matrix cores of the per-tensor W4A4 layers, "fp6" (E2M3
-    fragments) or "int8" (tile-packed int4 widened to bytes)."""
+    """cores: matrix cores of the W4A4 layers (per-tensor and 64-group),
+    "fp6" (E2M3 fragments) or "int8" (tile-packed int4 widened to bytes)."""
     if name == "merge":
         return run_merge(steps, warmup)
     import numpy as np
@@ -134,6 +134,8 @@ def run(name, steps, warmup, cores="fp6"):
             l1, l2, r = wl.lowrank_bits(w, lin)
             wc, ws, _, _ = cr.convrot_rotate_quantize(bf16(r), 0, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64)
             p, ps, _, wsum = cr.w4_pack_weights(wc, ws, N, K, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64, want_wsum=True)
+            if f6:
+                p = cr.w4_pack_weights_f6(wc, N, K)
             prep[lin.name] = dict(w=p, ws=ps, wsum=wsum, l1=bf16(l1), l2=bf16(l2))
     torch.cuda.synchronize()
     setup_s = time.time() - t0
@@ -167,7 +169,7 @@ def run(name, steps, warmup, cores="fp6"):
             o = dict(codes=torch.empty((M, K), dtype=torch.int8, device=dev),
                      scales=torch.empty(M, dtype=torch.float32, device=dev), ws=None)
         else:
-            o = dict(codes=torch.empty(((M + 15) // 16, K // 64, 512), dtype=torch.uint8, device=dev),
+            o = dict(codes=torch.empty(c4_shape(M, K), dtype=torch.uint8, device=dev),
                      scales=torch.empty((M, K // 64), dtype=torch.float32, device=dev), ws=None,
                      la=torch.empty((M, 32), dtype=torch.bfloat16, device=dev))
         rq_out[key] = o
@@ -192,7 +194,7 @@ def run(name, steps, warmup, cores="fp6"):
             uns = kind == "u4_g64"
             cr.convrot_rotate_quantize(x, 0, cr.Q.UNSIGNED_INT4_SHIFT if uns else cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP,
                                        64, shift=lin.unsigned_shift, lora_down=prep[lname]["l2"],
-                                       layout=cr.LAYOUT.TILED, codes=o["codes"], scales=o["scales"],
+                                       layout=lay4, codes=o["codes"], scales=o["scales"],
                                        lora_act=o["la"])
 
     def launch_gemm(lin, key):

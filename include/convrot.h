@@ -97,7 +97,8 @@ typedef enum cr_layout {
   CR_LAYOUT_INT8 = 2,     /* w4a4_gemm only: int8 codes [rows, K] row-major (SYM_INT8), the    */
                           /* 8-bit-activation branch for W4A4-format weights                   */
   CR_LAYOUT_F6 = 3        /* signed int4 codes (values -7..7) as fp6 E2M3 (bit 5 sign, bits    */
-                          /* 4:3 exponent with bias 1, bits 2:0 mantissa; every code is exact) */
+                          /* 4:3 exponent with bias 1, bits 2:0 mantissa; every code is exact; */
+                          /* an unsigned code u in 0..15 is stored as the exact value u/2)     */
                           /* in 32 x 64 operand fragments [ceil(rows/32)][K/64][1536 B]: lane  */
                           /* l (0..63) of a fragment covers row 32b + l%32 and columns          */
                           /* 64kt + 32(l/32) + i, i = 0..31, field i at bits 6i..6i+5 of its 24 */
@@ -171,8 +172,9 @@ void convrot_reset_counters(void);
  *                SYM_INT8: int8 [rows, K]
  *   layout       CR_LAYOUT_NATURAL, or CR_LAYOUT_TILED for SYM_INT4 / UNSIGNED
  *                codes (the input layout of w4a4_gemm's int8-core path), or
- *                CR_LAYOUT_F6 for SYM_INT4 with the rotation on (the input of
- *                w4a4_gemm's fp6-core path; ceil(rows/32)(K/64) 1536 bytes)
+ *                CR_LAYOUT_F6 for SYM_INT4 or UNSIGNED codes (the input of
+ *                w4a4_gemm's fp6-core path; ceil(rows/32)(K/64) 1536 bytes;
+ *                an unsigned code u is stored as the E2M3 value u/2)
  *   scales       float32 [1] | [rows] | [rows, K/q_group]; ASYM: fp16 [rows, K/16]
  *   zeros        ASYM only: uint8 [rows, K/32], two uint4 zero points per byte
  *                (group 2j low nibble); NULL otherwise
@@ -325,12 +327,14 @@ cr_status convrot_dequantize_weights(const void* codes, const void* scales, cons
  *               scales), the 8-bit-activation branch for these weights
  *               ("Qwen3-4B ConvRot W4A4" page, INT8 branch comparison): no
  *               a_unsigned, no 64-group scales and no low-rank branch with it;
- *               or CR_LAYOUT_F6: fp6 E2M3 fragments (signed codes) with
- *               w_packed from w4_pack_weights_f6, run on the fp6 matrix cores
- *               (the products and their float32 sums are exact integers for
- *               K <= 32768, so every output equals the int8-core path's):
- *               TENSOR or ROW scales on both sides, no a_unsigned, no
- *               low-rank branch
+ *               or CR_LAYOUT_F6: fp6 E2M3 fragments (signed codes, or
+ *               unsigned codes as u/2) with w_packed from w4_pack_weights_f6,
+ *               run on the fp6 matrix cores (the products and their float32
+ *               sums are exact, so the int32 output equals the int8-core
+ *               path's): a_unsigned and the low-rank branch need ROW_GROUP(64)
+ *               scales on both sides (w_scales and w_sum then come from
+ *               w4_pack_weights with ROW_GROUP(64)); TENSOR / ROW scales take
+ *               signed codes and no low-rank branch
  *   a_scales    float32: TENSOR [1], ROW [M], ROW_GROUP(64) [M, K/64]
  *   a_unsigned  1 for UNSIGNED_INT4_SHIFT codes: y -= a_shift * w_sum[n]
  *   w_packed    from w4_pack_weights (SYM_INT4); from w4_pack_weights_f6

@@ -106,7 +106,8 @@ def test_rq_validation(cr):
     assert _rq(cr, layout=3) == 4                            # fp6 fragments of rotated int4 codes
     assert _rq(cr, layout=3, g=1) == 4
     assert _rq(cr, layout=3, q=1) == 3                       # not for int8 codes
-    assert _rq(cr, layout=3, rot=0, g=2, qg=64, ws=None, wsb=0) == 3   # nor without the rotation
+    assert _rq(cr, layout=3, rot=0, g=2, qg=64, ws=None, wsb=0) == 4   # 64-group codes without rotation
+    assert _rq(cr, layout=3, rot=0, q=2, g=2, qg=64, ws=None, wsb=0) == 4   # unsigned shifted codes too
     assert _rq(cr, smooth=A, g=1) == 4                       # smoothing: rotation 256 with row scales
     assert _rq(cr, smooth=A, g=2, qg=64) == 4
     assert _rq(cr, smooth=A) == 3                            # not with per-tensor scales
@@ -209,9 +210,11 @@ def test_gemm_validation(cr):
     assert _w4a4(cr, layout=4) == 1
     assert _w4a4(cr, layout=3) == 4                          # fp6 fragments, tensor scales
     assert _w4a4(cr, layout=3, ag=1, wg=1) == 4
-    assert _w4a4(cr, layout=3, ag=2, wg=2) == 3              # fp6: no 64-group scales
-    assert _w4a4(cr, layout=3, uns=1, wsum=A) == 3           # fp6: signed codes only
-    assert _w4a4(cr, layout=3, la=A, lu=A, R=32) == 3        # fp6: no low-rank branch
+    assert _w4a4(cr, layout=3, ag=2, wg=2) == 4              # fp6 with 64-group scales
+    assert _w4a4(cr, layout=3, ag=2, wg=2, uns=1, wsum=A, la=A, lu=A, R=64) == 4
+    assert _w4a4(cr, layout=3, ag=2, wg=0) == 3
+    assert _w4a4(cr, layout=3, uns=1, wsum=A) == 3           # fp6, tensor scales: signed codes only
+    assert _w4a4(cr, layout=3, la=A, lu=A, R=32) == 3        # and no low-rank branch
     assert _w4a4(cr, layout=2, uns=1, wsum=A) == 3           # 8-bit activations: signed only
     assert _w4a4(cr, layout=2, ag=2, wg=2) == 3              # no 64-group scales with them
     assert _w4a4(cr, layout=2, la=A, lu=A, R=32) == 3        # no low-rank branch with them

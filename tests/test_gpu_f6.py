@@ -166,12 +166,111 @@ def test_f6_rejects_unsupported(cr):
     a = torch.zeros(((M + 31) // 32, K // 64, 1536), dtype=torch.uint8, device="cuda")
     w = torch.zeros((N // 32, K // 64, 1536), dtype=torch.uint8, device="cuda")
     s = torch.ones(M * (K // 64), dtype=torch.float32, device="cuda")
+    lr = torch.zeros((M, 32), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(cr.ConvRotError, match="format not available"):
-        cr.w4a4_gemm(a, s, 2, w, s, 2, M, N, K)              # 64-group scales
+        cr.w4a4_gemm(a, s, 2, w, s, 0, M, N, K)              # 64-group scales on one side only
     with pytest.raises(cr.ConvRotError, match="format not available"):
         cr.w4a4_gemm(a, s, 0, w, s, 0, M, N, K, a_unsigned=True, a_shift=0.171875, w_sum=s)
+    with pytest.raises(cr.ConvRotError, match="format not available"):
+        cr.w4a4_gemm(a, s, 1, w, s, 1, M, N, K, lora_act=lr, lora_up=lr[:, :32].contiguous())
     x = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(cr.ConvRotError, match="format not available"):
-        cr.convrot_rotate_quantize(x, 0, 0, 2, 64, layout=F6)   # no rotation
-    with pytest.raises(cr.ConvRotError, match="format not available"):
         cr.convrot_rotate_quantize(x, 256, 1, 0, 0, layout=F6)  # INT8 codes
+
+
+# ---------------------------------------------------------------------------
+# 64-group scales without rotation (the SVDQuant-style low-rank corrected
+# format): quantizer into fp6 fragments, signed or unsigned shifted codes, the
+# low-rank down-projection fused; GEMM with per-group scaling on the fp6 cores.
+# ---------------------------------------------------------------------------
+PLAIN_SHAPES = [(64, 512), (37, 3072), (300, 768), (5, 256), (129, 4096)]
+
+
+@pytest.mark.parametrize("uns", [False, True])
+@pytest.mark.parametrize("rank", [0, 32, 64])
+@pytest.mark.parametrize("shape", PLAIN_SHAPES)
+def test_quantize_g64_f6(cr, uns, rank, shape):
+    rows, K = shape
+    say(f"rq g64 f6 uns {uns} rank {rank} {shape}")
+    shift = 0.171875 if uns else 0.0
+    xb = wl.gelu_activation(37, rows + K + rank, rows, K) if uns else wl.activation(37, rows + K + rank, rows, K)
+    ref = ol.rotate_quantize(xb, 0, "uint4_shift" if uns else "int4", "row_group", 64, shift)
+    qt = cr.Q.UNSIGNED_INT4_SHIFT if uns else cr.Q.SYM_INT4
+    l2 = wl.weight(37, 3, rank, K) if rank else None
+    kw = dict(shift=shift, lora_down=None if l2 is None else bf16_dev(l2))
+    codes, scales, _, la = cr.convrot_rotate_quantize(bf16_dev(xb), 0, qt, cr.GRAN.ROW_GROUP, 64, layout=F6, **kw)
+    assert tuple(codes.shape) == ((rows + 31) // 32, K // 64, 1536)
+    vals = opack.f6_unpack(host(codes), rows) * (2 if uns else 1)
+    assert np.array_equal(vals, ref["values"]), "fp6 codes differ"
+    full = rows // 32
+    assert np.array_equal(host(codes)[:full], opack.f6_pack(ref["values"], unsigned=uns)[:full])
+    assert np.array_equal(host(scales).reshape(-1).view(np.uint32),
+                          np.asarray(ref["scales"], np.float32).reshape(-1).view(np.uint32)), "scales differ"
+    if rank:   # the same fused down-projection as the natural layout's: identical bits
+        _, _, _, la_n = cr.convrot_rotate_quantize(bf16_dev(xb), 0, qt, cr.GRAN.ROW_GROUP, 64, **kw)
+        assert np.array_equal(host(la), host(la_n))
+
+
+F6_G64_CASES = [
+    # M, N, K, unsigned, lora(None|bf16|f32), rank, bias
+    (16, 256, 512, False, None, 0, False),
+    (40, 384, 1024, True, None, 0, False),
+    (200, 256, 3072, False, "bf16", 32, True),
+    (130, 384, 1024, True, "bf16", 32, False),
+    (64, 256, 512, True, "f32", 32, True),
+    (257, 128, 768, False, "f32", 64, False),
+    (300, 512, 1024, True, "bf16", 64, True),
+    (100, 384, 128, False, None, 0, True),      # a single 128-deep stage
+    (1, 128, 256, True, "bf16", 32, True),
+]
+
+
+@pytest.mark.parametrize("case", F6_G64_CASES)
+def test_w4a4_f6_group64(cr, case):
+    M, N, K, uns, lora, rank, use_bias = case
+    say(f"w4a4 f6 g64 {case}")
+    shift = 0.171875 if uns else 0.0
+    xb = wl.gelu_activation(29, M + K, M, K) if uns else wl.activation(29, M + K, M, K)
+    wb = wl.weight(29, N + K, N, K)
+    l1 = l2 = None
+    if lora:
+        l1, l2, wb = wl.lowrank_split(wb, rank)
+    bias = wl.weight(29, 5, 1, N, std=0.5)[0] if use_bias else None
+    wp = ol.prepare_w4a4(wb, 0, "row_group", 64)
+    ref = ol.w4a4_linear(xb, wb, 0, "row_group", "row_group", 64, shift, l1, l2,
+                         act_f32=(lora == "f32"), bias_bits=bias, wprep=wp)
+    a = dev(opack.f6_pack(ref["x"]["values"], unsigned=uns))
+    sa = dev(np.asarray(ref["x"]["scales"], np.float32))
+    w = dev(opack.f6_pack(wp["values"]))
+    sw = dev(wp["scales_tiles"].reshape(-1))
+    wsum = dev(wp["wsum"])
+    la = lu = None
+    if lora:
+        la = dev(ref["la"]) if lora == "f32" else bf16_dev(wl.bf16_bits_from_f32(ref["la"]))
+        lu = bf16_dev(l1)
+    kw = dict(a_unsigned=uns, a_shift=shift, w_sum=wsum, lora_act=la, lora_up=lu,
+              bias=None if bias is None else bf16_dev(bias))
+    raw = cr.w4a4_gemm(a, sa, 2, w, sw, 2, M, N, K, out_type=2, **kw)
+    assert np.array_equal(host(raw).astype(np.int64), ref["raw"])
+    yf = cr.w4a4_gemm(a, sa, 2, w, sw, 2, M, N, K, out_type=1, **kw)
+    assert rel_l2(host(yf), ref["y"]) <= 1e-5
+    yb = cr.w4a4_gemm(a, sa, 2, w, sw, 2, M, N, K, out_type=0, **kw)
+    assert rel_l2(bf16_to_f32(host(yb)), ref["y"]) <= 2e-3
+    # the bf16 output is the float32 one rounded to nearest even
+    assert np.array_equal(host(yb), host(yf.to(torch.bfloat16)))
+
+
+def test_w4a4_f6_group64_ldc_padding(cr):
+    M, N, K, ldc = 150, 256, 512, 264
+    say("w4a4 f6 g64 ldc")
+    rng = np.random.default_rng(6)
+    qa = rng.integers(-7, 8, size=(M, K))
+    qw = rng.integers(-7, 8, size=(N, K))
+    sa = dev(np.ones(M * (K // 64), np.float32))
+    sw = dev(np.ones(N * (K // 64), np.float32))
+    out = torch.full((M, ldc), 7.0, dtype=torch.float32, device="cuda")
+    cr.w4a4_gemm(dev(opack.f6_pack(qa)), sa, 2, dev(opack.f6_pack(qw)), sw, 2, M, N, K, out_type=1,
+                 out=out[:, :N].as_strided((M, N), (ldc, 1)))
+    o = host(out)
+    assert np.array_equal(o[:, :N].astype(np.int64), qa @ qw.T)
+    assert np.all(o[:, N:] == 7.0)

@@ -269,3 +269,39 @@ def test_c5_lowrank_g64_full(cr, name):
     ref_y = ol.epilogue_g64(P, np.asarray(xa["scales"])[rows], np.asarray(wp["scales"])[cols], shift,
                             np.asarray(wp["wsum"])[cols], la_ref[rows], l1[cols])
     assert rel_l2(y[np.ix_(rows, cols)], ref_y) <= 2e-3
+
+
+@pytest.mark.parametrize("name", ["qkv", "mlp_down"])
+def test_c5_lowrank_g64_full_f6(cr, name):
+    """The same layers on the fp6 matrix cores: codes (unsigned ones as u/2)
+    in fp6 fragments from the quantizer, weights through
+    w4_pack_weights_f6, 64-group scales and column sums from w4_pack_weights."""
+    w, lin = _lin("c5", name)
+    M, N, K = lin.M, lin.N, lin.K
+    shift = lin.unsigned_shift
+    uns = shift != 0.0
+    say(f"c5 full fp6 {name} {M}x{N}x{K}")
+    xb = wl.act_bits(w, lin.x_id)
+    l1, l2, r = wl.lowrank_bits(w, lin)
+    xa = ol.rotate_quantize(xb, 0, "uint4_shift" if uns else "int4", "row_group", 64, shift)
+    la_ref = ol.lora_down(xb, l2)
+    wp = ol.prepare_w4a4(r, 0, "row_group", 64)
+    qt = cr.Q.UNSIGNED_INT4_SHIFT if uns else cr.Q.SYM_INT4
+    codes, sa, _, la = cr.convrot_rotate_quantize(bf16_dev(xb), 0, qt, cr.GRAN.ROW_GROUP, 64, shift=shift,
+                                                  lora_down=bf16_dev(l2), layout=cr.LAYOUT.F6)
+    assert np.array_equal(opack.f6_unpack(host(codes), M) * (2 if uns else 1), xa["values"])
+    assert np.array_equal(host(sa).view(np.uint32), np.asarray(xa["scales"], np.float32).view(np.uint32))
+    wc, ws, _, _ = cr.convrot_rotate_quantize(bf16_dev(r), 0, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64)
+    _, pscales, _, wsum = cr.w4_pack_weights(wc, ws, N, K, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64, want_wsum=True)
+    wf = cr.w4_pack_weights_f6(wc, N, K)
+    assert np.array_equal(bytes_of(wf), opack.f6_pack(wp["values"]).reshape(-1))
+    kw = dict(a_unsigned=uns, a_shift=shift, w_sum=wsum)
+    rows, cols = _rows(M, 16, 62), _cols(N, 1024, 62)
+    raw = host(cr.w4a4_gemm(codes, sa, 2, wf, pscales, 2, M, N, K, out_type=cr.OUT.I32_RAW, **kw))
+    assert np.array_equal(raw[rows].astype(np.int64), og.int_gemm(xa["values"][rows], wp["values"]))
+    y = bf16_to_f32(host(cr.w4a4_gemm(codes, sa, 2, wf, pscales, 2, M, N, K, lora_act=la,
+                                      lora_up=bf16_dev(l1), **kw)))
+    P = og.group_partials(xa["values"][rows], wp["values"][cols], 64)
+    ref_y = ol.epilogue_g64(P, np.asarray(xa["scales"])[rows], np.asarray(wp["scales"])[cols], shift,
+                            np.asarray(wp["wsum"])[cols], la_ref[rows], l1[cols])
+    assert rel_l2(y[np.ix_(rows, cols)], ref_y) <= 2e-3

@@ -159,8 +159,8 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
     return CR_ERR_INVALID_ARGUMENT;
   if (layout == CR_LAYOUT_TILED && !(qtype == CR_Q_SYM_INT4 || qtype == CR_Q_UNSIGNED_INT4_SHIFT))
     return CR_ERR_UNSUPPORTED_FORMAT;
-  if (layout == CR_LAYOUT_F6) {   // signed INT4 codes of a rotated path; the rows pad to 32
-    if (qtype != CR_Q_SYM_INT4 || rot_group == 0) return CR_ERR_UNSUPPORTED_FORMAT;
+  if (layout == CR_LAYOUT_F6) {   // signed INT4 codes, or unsigned shifted ones (unrotated); rows pad to 32
+    if (!(qtype == CR_Q_SYM_INT4 || qtype == CR_Q_UNSIGNED_INT4_SHIFT)) return CR_ERR_UNSUPPORTED_FORMAT;
     if (((rows + 31) / 32) * (K / 64) * 1536 >= ((int64_t)1 << 32)) return CR_ERR_UNSUPPORTED_SHAPE;
   }
   if (smooth) {   // without rotation, or the 256 rotation with per-row / per-64-group scales
@@ -384,9 +384,8 @@ cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
   if ((int)a_layout < 0 || (int)a_layout > 3) return CR_ERR_INVALID_ARGUMENT;
   const bool a8 = a_layout == CR_LAYOUT_INT8;
   const bool f6 = a_layout == CR_LAYOUT_F6;
-  if (f6) {   // fp6 fragments on both sides: signed codes, per-tensor / per-row scales, no low-rank branch
-    if (a_unsigned || a_gran == CR_GRAN_ROW_GROUP || w_gran == CR_GRAN_ROW_GROUP || lora_act || lora_up)
-      return CR_ERR_UNSUPPORTED_FORMAT;
+  if (f6) {   // fp6 fragments on both sides; unsigned codes and the low-rank branch with 64-group scales only
+    if (a_gran != CR_GRAN_ROW_GROUP && (a_unsigned || lora_act || lora_up)) return CR_ERR_UNSUPPORTED_FORMAT;
     if (((M + 31) / 32) * (K / 64) * 1536 >= ((int64_t)1 << 32) || (N / 32) * (K / 64) * 1536 >= ((int64_t)1 << 32))
       return CR_ERR_UNSUPPORTED_SHAPE;
   }

@@ -309,6 +309,244 @@ __global__ __launch_bounds__((BM / (32 * TM)) * (BN / (32 * TN)) * 64, MINB) voi
 }
 
 // ---------------------------------------------------------------------------
+// 64-group scales on both sides (the SVDQuant format): one 32 x 32 x 64 matrix
+// op covers exactly one group, so its float32 result P (exact) is scaled
+// right away: y += P * (s_a[m, g] * s_w[n, g]), two VALU ops per output and
+// group. Unsigned shifted activations (codes u in [0, 15]) come as the E2M3
+// values u/2, so P is half the integer sum and the factor 2 joins the scale.
+// Block 128 x 128, 2 x 2 waves of 64 x 64, stages of two k-tiles with their
+// scales (26 KB: activation scales gathered as 4-byte pieces of the row-major
+// [M, K/64] array, weight scales a contiguous 1 KB run of the packed
+// [N/128][K/64][128] array), two in the ring, two blocks per CU (182 VGPRs:
+// the scaled accumulation keeps 64 products beside 64 sums). Epilogue: shift
+// correction, low-rank branch
+// (32 x 32 x 16 bf16 or 32 x 32 x 2 f32 matrix ops onto the outputs), bias,
+// bf16 rows through LDS.
+// ---------------------------------------------------------------------------
+template <bool UNS>
+CR_DEV void f6_lowrank_32(const GemmParams& p, int64_t m0w, int64_t n0w, int l, v16f (&y)[2][2]) {
+  const int lr = l & 31, h = l >> 5;
+  const int R = p.R;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint16_t* lu = p.lora_up + (n0w + j * 32 + lr) * R;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t mr = imin64(m0w + i * 32 + lr, p.M - 1);
+      if (!p.lora_f32) {
+        const uint16_t* la = reinterpret_cast<const uint16_t*>(p.lora_act) + mr * R;
+        for (int r0 = 0; r0 < R; r0 += 16)
+          y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(lu + r0 + 8 * h)),
+              __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(la + r0 + 8 * h)), y[i][j], 0, 0, 0);
+      } else {
+        const float* la = reinterpret_cast<const float*>(p.lora_act) + mr * R;
+        for (int r0 = 0; r0 < R; r0 += 2)
+          y[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float((uint32_t)lu[r0 + h] << 16), la[r0 + h],
+                                                         y[i][j], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+template <int OUT, bool UNS>
+__global__ __launch_bounds__(256, 2) void gemm_f6_grp_kernel(GemmParams p) {
+  constexpr int BM = 128, BN = 128, BKT = 2, NW = 4, WN = 2;
+  constexpr int A_ST = (BM / 32) * BKT * F6_FRAG, W_ST = (BN / 32) * BKT * F6_FRAG;
+  constexpr int SA_ST = BKT * BM * 4, SW_ST = BKT * BN * 4;
+  constexpr int STAGE = A_ST + W_ST + SA_ST + SW_ST;
+  constexpr int NL = (A_ST + W_ST) / 1024, NA = A_ST / 1024, LPW = NL / NW;
+  static_assert(NL % NW == 0 && SA_ST == 256 * NW && SW_ST == 256 * NW, "loads split evenly over the waves");
+  constexpr int RUN = BKT * F6_FRAG / 16;
+  constexpr int RS = 144;                              // epilogue: LDS row stride of a 64 x 64 bf16 tile
+  static_assert(NW * 64 * RS <= 2 * STAGE, "epilogue tiles fit the stage buffers");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int l = tid & 63, lr = l & 31, h = l >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  const int ntm = (int)((p.M + BM - 1) / BM);
+  const int ntn = (int)(p.N / BN);
+  const int ntiles = ntm * ntn;
+  int t = (int)blockIdx.x;
+  if (ntiles % 8 == 0) t = (t & 7) * (ntiles / 8) + (t >> 3);
+  constexpr int GM = 8;
+  const int band = t / (GM * ntn);
+  const int rows_in_band = min(GM, ntm - band * GM);
+  const int within = t - band * GM * ntn;
+  const int tn = within / rows_in_band;
+  const int tm = band * GM + within % rows_in_band;
+  const int64_t m0 = (int64_t)tm * BM;
+  const int64_t n0 = (int64_t)tn * BN;
+  const int64_t KT = p.K / 64;
+  const int nkb = (int)(p.K / (64 * BKT));
+  const int64_t MB = (p.M + 31) / 32;
+
+  const uint8_t* src[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int idx = wave + NW * j;
+    if (idx < NA) {
+      const int pc = idx * 64 + l;
+      const int64_t b = imin64(m0 / 32 + pc / RUN, MB - 1);
+      src[j] = p.a + b * KT * F6_FRAG + (pc % RUN) * 16;
+    } else {
+      const int pc = (idx - NA) * 64 + l;
+      src[j] = p.w + (n0 / 32 + pc / RUN) * KT * F6_FRAG + (pc % RUN) * 16;
+    }
+  }
+  // scale entry e = wave * 64 + l of a stage: k-tile e / 128, row (column) e % 128
+  const int ske = wave * 64 + l;
+  const float* sa_src = p.a_scales + imin64(m0 + ske % BM, p.M - 1) * KT + ske / BM;
+  const float* sw_src = p.w_scales + n0 * KT + ske;   // packed: [N/128][K/64][128]
+  auto issue = [&](int kb) {
+    uint8_t* st = smem + (kb % 2) * STAGE;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j)
+      __builtin_amdgcn_global_load_lds((f6_gptr)(src[j] + (size_t)kb * (BKT * F6_FRAG)),
+                                       (f6_lptr)(st + (wave + NW * j) * 1024), 16, 0, 0);
+    if constexpr (OUT != CR_OUT_I32_RAW) {
+      __builtin_amdgcn_global_load_lds((f6_gptr)(sa_src + kb * BKT), (f6_lptr)(st + A_ST + W_ST + wave * 256), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((f6_gptr)(sw_src + (size_t)kb * (BKT * BN)),
+                                       (f6_lptr)(st + A_ST + W_ST + SA_ST + wave * 256), 4, 0, 0);
+    }
+  };
+  constexpr int LST = LPW + (OUT != CR_OUT_I32_RAW ? 2 : 0);   // loads per wave and stage
+
+  v16f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+  constexpr float UF = UNS ? 2.f : 1.f;
+
+  issue(0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    f6_wait_vmcnt<0>();
+    (void)LST;
+    __builtin_amdgcn_s_barrier();
+    if (kb + 1 < nkb) issue(kb + 1);
+    const uint8_t* As = smem + (kb % 2) * STAGE;
+    const uint8_t* Ws = As + A_ST;
+    const float* Sa = reinterpret_cast<const float*>(As + A_ST + W_ST);
+    const float* Sw = Sa + BKT * BM;
+#pragma unroll
+    for (int kt = 0; kt < BKT; ++kt) {
+      v8i av[2], wv[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) av[i] = frag_f6(As + ((wm * 2 + i) * BKT + kt) * F6_FRAG, l);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) wv[j] = frag_f6(Ws + ((wn * 2 + j) * BKT + kt) * F6_FRAG, l);
+      if constexpr (OUT == CR_OUT_I32_RAW) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f6_32(wv[j], av[i], acc[i][j]);
+      } else {
+        float sa[2];
+        v4f sw[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) sa[i] = Sa[kt * BM + (wm * 2 + i) * 32 + lr] * UF;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            sw[j][g] = *reinterpret_cast<const v4f*>(Sw + kt * BN + (wn * 2 + j) * 32 + 8 * g + 4 * h);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const v16f pp = mfma_f6_32(wv[j], av[i], v16f{});
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                acc[i][j][4 * g + e] = __builtin_fmaf(pp[4 * g + e], sw[j][g][e] * sa[i], acc[i][j][4 * g + e]);
+          }
+      }
+    }
+  }
+
+  const int64_t m0w = m0 + wm * 64, n0w = n0 + wn * 64;
+  if constexpr (OUT == CR_OUT_I32_RAW) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float y[4] = {0.f, 0.f, 0.f, 0.f};
+          int raw[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) raw[e] = (int)(acc[i][j][4 * g + e] * UF);
+          store4<OUT>(p, m0w + i * 32 + lr, n0w + j * 32 + 8 * g + 4 * h, y, raw);
+        }
+    return;
+  } else {
+    // shift correction and bias first (loads before any store), then the low-rank branch
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t n = n0w + j * 32 + 8 * g + 4 * h;
+        v4f c = v4f{0.f, 0.f, 0.f, 0.f};
+        if constexpr (UNS) {
+          const v4f ws = *reinterpret_cast<const v4f*>(p.w_sum + n);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) c[e] = -p.a_shift * ws[e];
+        }
+        const u32x2 bb = p.bias ? *reinterpret_cast<const u32x2*>(p.bias + n) : u32x2{0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          acc[i][j][4 * g + 0] = __builtin_fmaf(1.f, c[0], acc[i][j][4 * g + 0]) + bf16_lo(bb[0]);
+          acc[i][j][4 * g + 1] = __builtin_fmaf(1.f, c[1], acc[i][j][4 * g + 1]) + bf16_hi(bb[0]);
+          acc[i][j][4 * g + 2] = __builtin_fmaf(1.f, c[2], acc[i][j][4 * g + 2]) + bf16_lo(bb[1]);
+          acc[i][j][4 * g + 3] = __builtin_fmaf(1.f, c[3], acc[i][j][4 * g + 3]) + bf16_hi(bb[1]);
+        }
+      }
+    if (p.lora_act) f6_lowrank_32<UNS>(p, m0w, n0w, l, acc);
+    if constexpr (OUT == CR_OUT_F32) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int64_t m = m0w + i * 32 + lr;
+            if (m < p.M)
+              *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.out) + m * p.ldc + n0w + j * 32 + 8 * g + 4 * h) =
+                  v4f{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          }
+    } else {
+      __syncthreads();                                 // every wave is done with the stage buffers
+      uint8_t* tile = smem + wave * (64 * RS);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const v2bf lo = __builtin_convertvector((v2f){acc[i][j][4 * g], acc[i][j][4 * g + 1]}, v2bf);
+            const v2bf hi = __builtin_convertvector((v2f){acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]}, v2bf);
+            *reinterpret_cast<u32x2*>(tile + (i * 32 + lr) * RS + (j * 32 + 8 * g + 4 * h) * 2) =
+                u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+          }
+      f6_wait_vmcnt<63>();                             // this wave's tile writes are done
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int r = (l >> 3) + 8 * q;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * RS + (l & 7) * 16);
+        const int64_t m = m0w + r;
+        if (m < p.M) *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.out) + m * p.ldc + n0w + (l & 7) * 8) = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Small-M kernel (M <= 64): weight streaming. A block owns 16 output channels
 // (half of a 32-row weight block); its SK waves take the 128-deep k-steps
 // round robin and read their fragments straight from global memory in the
@@ -403,6 +641,12 @@ __global__ __launch_bounds__(F6_SK_WAVES * 64) void gemm_f6_skinny_kernel(GemmPa
 
 template <int OUT>
 static hipError_t launch_f6_out(const GemmParams& p, hipStream_t s) {
+  if (p.grouped) {
+    const int64_t tiles = ((p.M + 127) / 128) * (p.N / 128);
+    if (p.act == ACT_U4) hipLaunchKernelGGL((gemm_f6_grp_kernel<OUT, true>), dim3((unsigned)tiles), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((gemm_f6_grp_kernel<OUT, false>), dim3((unsigned)tiles), dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
   if (p.M <= 64) {
     const dim3 grid((unsigned)(p.N / 16));
     switch ((p.M + 15) / 16) {

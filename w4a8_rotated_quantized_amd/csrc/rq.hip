@@ -541,6 +541,53 @@ __global__ __launch_bounds__(256) void rq_plain_kernel(RQParams a) {
         float s = (m > 0.f) ? div_rn(m, qmax) : 0.f;
         reinterpret_cast<float*>(a.scales)[row * nsl + t] = s;
       }
+      if (a.tiled == 2) {
+        // fp6 fragments: signed codes as themselves, unsigned codes u as the
+        // E2M3 value u/2 (exact; the GEMM doubles the product). The lane's
+        // runs (elements 8c.. of each 32-column half) are 48-bit pieces; the
+        // lane with even c joins its piece with that of lane c + 1 (lane ^ 16)
+        // and stores the 96 bits as half c/2 of the fragment lane of its row.
+        v16f s0 = {}, s1 = {};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int e0 = (i < 4) ? 2 * i : 8 + 2 * (i - 4);
+          float q0, q1;
+          if (UNSIGNED) {
+            q0 = 0.5f * fminf(fmaxf(rintf(__fmul_rn(v[e0], r)), 0.f), 15.f);
+            q1 = 0.5f * fminf(fmaxf(rintf(__fmul_rn(v[e0 + 1], r)), 0.f), 15.f);
+          } else {
+            q0 = __fsub_rn(__fadd_rn(__fmul_rn(v[e0], r), CR_MAGIC_RNE), CR_MAGIC_RNE);
+            q1 = __fsub_rn(__fadd_rn(__fmul_rn(v[e0 + 1], r), CR_MAGIC_RNE), CR_MAGIC_RNE);
+          }
+          s0[i] = q0;
+          s1[i] = q1;
+        }
+        const auto o = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(s0, s1, 1.0f);
+        uint32_t ra[2], rb[2];                       // run h: bits 0..31 and 32..47
+        ra[0] = o[0];
+        rb[0] = o[1] & 0xFFFFu;
+        ra[1] = (o[1] >> 16) | (o[2] << 16);
+        rb[1] = o[2] >> 16;
+        uint32_t pa[2], pb[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          pa[h] = (uint32_t)__shfl_xor((int)ra[h], 16);
+          pb[h] = (uint32_t)__shfl_xor((int)rb[h], 16);
+        }
+        if (rok && (c & 1) == 0) {
+          uint8_t* frag = reinterpret_cast<uint8_t*>(a.codes) + ((row >> 5) * (a.K / 64) + t) * 1536;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int lm = 32 * h + (int)(row & 31);
+            uint32_t* w0 = reinterpret_cast<uint32_t*>(frag + lm * 16 + ((c >> 1) ? 12 : 0));
+            uint32_t* w1 = (c >> 1) ? reinterpret_cast<uint32_t*>(frag + 1024 + lm * 8) : w0 + 1;
+            w0[0] = ra[h];
+            w1[0] = rb[h] | (pa[h] << 16);
+            w1[1] = (pa[h] >> 16) | (pb[h] << 16);
+          }
+        }
+        continue;
+      }
       uint32_t out[2] = {0u, 0u};
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
