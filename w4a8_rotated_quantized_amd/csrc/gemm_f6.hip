@@ -35,6 +35,7 @@
 namespace cr {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v32f __attribute__((ext_vector_type(32)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef const void __attribute__((address_space(1)))* f6_gptr;
@@ -414,7 +415,6 @@ __global__ __launch_bounds__(256, 2) void gemm_f6_grp_kernel(GemmParams p) {
                                        (f6_lptr)(st + A_ST + W_ST + SA_ST + wave * 256), 4, 0, 0);
     }
   };
-  constexpr int LST = LPW + (OUT != CR_OUT_I32_RAW ? 2 : 0);   // loads per wave and stage
 
   v16f acc[2][2];
 #pragma unroll
@@ -426,7 +426,6 @@ __global__ __launch_bounds__(256, 2) void gemm_f6_grp_kernel(GemmParams p) {
   issue(0);
   for (int kb = 0; kb < nkb; ++kb) {
     f6_wait_vmcnt<0>();
-    (void)LST;
     __builtin_amdgcn_s_barrier();
     if (kb + 1 < nkb) issue(kb + 1);
     const uint8_t* As = smem + (kb % 2) * STAGE;
@@ -446,26 +445,27 @@ __global__ __launch_bounds__(256, 2) void gemm_f6_grp_kernel(GemmParams p) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f6_32(wv[j], av[i], acc[i][j]);
       } else {
-        float sa[2];
-        v4f sw[2][4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) sa[i] = Sa[kt * BM + (wm * 2 + i) * 32 + lr] * UF;
+        // the scale products s_a[m] s_w[n] of both 32 x 32 tiles of column j
+        // come from one two-block outer-product matrix op (block i = tokens
+        // 32 i .., lane l gives s_a of token l and s_w of channel l % 32), in
+        // the 32 x 32 output layout of the fp6 op: one FMA per output and
+        // group is left on the vector ALUs
+        const float sa = Sa[kt * BM + wm * 64 + l] * UF;
+        v32f c[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            sw[j][g] = *reinterpret_cast<const v4f*>(Sw + kt * BN + (wn * 2 + j) * 32 + 8 * g + 4 * h);
+          c[j] = __builtin_amdgcn_mfma_f32_32x32x1f32(Sw[kt * BN + (wn * 2 + j) * 32 + lr], sa, v32f{}, 0, 0, 0);
+        v16f pp[2][2];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const v16f pp = mfma_f6_32(wv[j], av[i], v16f{});
+          for (int j = 0; j < 2; ++j) pp[i][j] = mfma_f6_32(wv[j], av[i], v16f{});
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                acc[i][j][4 * g + e] = __builtin_fmaf(pp[4 * g + e], sw[j][g][e] * sa[i], acc[i][j][4 * g + e]);
-          }
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(pp[i][j][r], c[j][16 * i + r], acc[i][j][r]);
       }
     }
   }
