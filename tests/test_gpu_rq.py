@@ -92,6 +92,40 @@ def test_rotate_quantize_dual(cr, rot, shape):
     assert np.array_equal(host(n4), r4["codes"])
 
 
+# Per-tensor scales on mid-size inputs (four 256-groups per lane and block,
+# a grid of several hundred blocks, a ragged last 16-row block), every code
+# layout and the dual output.
+MID_SHAPES = [(1531, 4096), (3000, 3072), (4100, 4096)]
+
+
+@pytest.mark.parametrize("rot", [256, 64, 16])
+@pytest.mark.parametrize("shape", MID_SHAPES)
+def test_rotate_quantize_tensor_mid(cr, rot, shape):
+    rows, K = shape
+    say(f"rq tensor mid rot {rot} {shape}")
+    xb = wl.activation(17, rows + K + rot, rows, K, n_outliers=max(1, K // 200), outlier_scale=25.0)
+    r4 = ol.rotate_quantize(xb, rot, "int4", "tensor")
+    r8 = ol.rotate_quantize(xb, rot, "int8", "tensor")
+    s4ref = np.asarray(r4["scales"], np.float32).reshape(-1).view(np.uint32)
+    for layout in (0, 1, 3):
+        codes, scales, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), rot, 0, 0, layout=layout)
+        got = host(codes)
+        if layout == 0:
+            assert np.array_equal(got, r4["codes"]), "natural codes differ"
+        elif layout == 1:
+            assert np.array_equal(opack.tile_unpack_a(got, rows), r4["codes"]), "tiled codes differ"
+        else:
+            assert np.array_equal(opack.f6_unpack(got, rows), r4["values"]), "fp6 codes differ"
+        assert np.array_equal(host(scales).view(np.uint32), s4ref)
+    c8, s8, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), rot, 1, 0)
+    assert np.array_equal(host(c8).view(np.uint8), r8["codes"].view(np.uint8))
+    assert np.array_equal(host(s8).view(np.uint32), np.asarray(r8["scales"], np.float32).reshape(-1).view(np.uint32))
+    d4, ds4, d8, ds8 = cr.convrot_rotate_quantize_dual(bf16_dev(xb), rot, layout4=3)
+    assert np.array_equal(opack.f6_unpack(host(d4), rows), r4["values"])
+    assert np.array_equal(host(ds4).view(np.uint32), s4ref)
+    assert np.array_equal(host(d8).view(np.uint8), r8["codes"].view(np.uint8))
+
+
 def _check_lora_act(la, xb, l2, f32):
     la_ref32 = ol.lora_down(xb, l2, act_f32=True).astype(np.float64)
     mag = np.abs(wl.f32_from_bf16_bits(xb)).astype(np.float64) @ np.abs(wl.f32_from_bf16_bits(l2)).astype(np.float64).T
