@@ -265,7 +265,8 @@ def run(name, steps, warmup, cores="fp6"):
         x_id, kind, _ = key
         M, K = w.acts[x_id][0], w.acts[x_id][1]
         us = kern[f"rq:{x_id}:{kind}"]
-        out_b = M * K // (1 if kind.startswith("int8") else 2) + (M * K if kind == "dual_tensor" else 0)
+        code_b = 1.0 if kind.startswith("int8") else (0.75 if f6 else 0.5)   # fp6 fragments: 6 bits per code
+        out_b = M * K * code_b + (M * K if kind == "dual_tensor" else 0)
         rqs[f"{x_id}:{kind}"] = {"us": us, "GBps": round((M * K * 2 + out_b) / us / 1e3, 1)}
     dom = max(layers, key=lambda n: layers[n]["us"])
     eff = ops / (ms * 1e-3) / 1e12

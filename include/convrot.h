@@ -93,7 +93,7 @@ typedef enum cr_layout {
   CR_LAYOUT_TILED = 1,    /* int4 codes [ceil(rows/16)][K/64][512 B]: byte l*8 + j of block    */
                           /* (b, kt) is natural byte (row 16b + l%16, 32kt + 8(l/16) + j), the */
                           /* operand-fragment order of the W4A4 GEMM; rows past `rows` in the  */
-                          /* last block are left unwritten (allocate ceil(rows/16)*16 rows)    */
+                          /* last block hold unspecified codes (allocate ceil(rows/16)*16 rows)*/
   CR_LAYOUT_INT8 = 2,     /* w4a4_gemm only: int8 codes [rows, K] row-major (SYM_INT8), the    */
                           /* 8-bit-activation branch for W4A4-format weights                   */
   CR_LAYOUT_F6 = 3        /* signed int4 codes (values -7..7) as fp6 E2M3 (bit 5 sign, bits    */
@@ -104,8 +104,8 @@ typedef enum cr_layout {
                           /* 64kt + 32(l/32) + i, i = 0..31, field i at bits 6i..6i+5 of its 24 */
                           /* bytes, bytes 0..15 at l*16 and bytes 16..23 at 1024 + l*8. Input   */
                           /* of the fp6 matrix-core W4A4 GEMM (weights from w4_pack_weights_f6);*/
-                          /* rows past `rows` in the last block are left unwritten (allocate    */
-                          /* ceil(rows/32)*32 rows)                                              */
+                          /* rows past `rows` in the last block hold unspecified codes (any     */
+                          /* 6-bit field is a finite value; allocate ceil(rows/32)*32 rows)      */
 } cr_layout;
 
 /* Status text, e.g. "format not available" for CR_ERR_UNSUPPORTED_FORMAT. */

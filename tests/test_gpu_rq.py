@@ -321,6 +321,37 @@ def test_rotate_quantize_plain_g64(cr, unsigned, lora, shape):
             assert np.all(np.abs(gotf - la_ref32) <= ulp + 1e-30)
 
 
+# Tall inputs take the 32-row blocks of the unrotated quantizer (two 16-row
+# tiles per block share each low-rank fragment): 8170 rows leave the last
+# block's second tile empty, 8190 fill it partly, 8192 exactly.
+@pytest.mark.parametrize("unsigned", [False, True])
+@pytest.mark.parametrize("rows", [8170, 8190, 8192])
+def test_rotate_quantize_plain_g64_tall(cr, unsigned, rows):
+    K = 256 if rows != 8192 else 448
+    say(f"rq plain tall unsigned={unsigned} rows={rows} K={K}")
+    xb = (wl.gelu_activation if unsigned else wl.activation)(16, rows + K, rows, K)
+    shift = 0.171875 if unsigned else 0.0
+    ref = ol.rotate_quantize(xb, 0, "uint4_shift" if unsigned else "int4", "row_group", 64, shift)
+    l2 = wl.weight(16, 77, 32, K, std=0.05)
+    kw = dict(shift=shift, lora_down=bf16_dev(l2))
+    qt = 2 if unsigned else 0
+    codes, scales, _, la = cr.convrot_rotate_quantize(bf16_dev(xb), 0, qt, 2, 64, **kw)
+    assert np.array_equal(host(codes), ref["codes"])
+    assert np.array_equal(host(scales).view(np.uint32), ref["scales"].view(np.uint32))
+    tcodes, tsc, _, tla = cr.convrot_rotate_quantize(bf16_dev(xb), 0, qt, 2, 64, layout=1, **kw)
+    assert np.array_equal(opack.tile_unpack_a(host(tcodes), rows), ref["codes"])
+    fcodes, fsc, _, fla = cr.convrot_rotate_quantize(bf16_dev(xb), 0, qt, 2, 64, layout=3, **kw)
+    assert np.array_equal(opack.f6_unpack(host(fcodes), rows) * (2 if unsigned else 1), ref["values"])
+    for s2 in (tsc, fsc):
+        assert np.array_equal(host(s2).view(np.uint32), ref["scales"].view(np.uint32))
+    la_ref32 = ol.lora_down(xb, l2, act_f32=True).astype(np.float64)
+    mag = np.abs(wl.f32_from_bf16_bits(xb)).astype(np.float64) @ np.abs(wl.f32_from_bf16_bits(l2)).astype(np.float64).T
+    gotf = wl.f32_from_bf16_bits(host(la)).astype(np.float64)
+    assert np.all(np.abs(gotf - la_ref32) <= np.abs(la_ref32) * 2.0 ** -7 + mag * 2 ** -20 + 1e-30)
+    # the three layouts run the same low-rank accumulation
+    assert np.array_equal(host(la), host(tla)) and np.array_equal(host(la), host(fla))
+
+
 @pytest.mark.parametrize("gran", ["tensor", "row", "row_group"])
 @pytest.mark.parametrize("shape", [(128, 512), (384, 3072)])
 def test_pack_w4a4(cr, gran, shape):

@@ -458,175 +458,261 @@ __global__ __launch_bounds__(256) void rq_tensor_kernel(RQParams a) {
 // ---------------------------------------------------------------------------
 // rq_plain: no rotation, ROW_GROUP(64) scales, signed INT4 or unsigned
 // shifted INT4, optional fused LoRA-down (bf16 matrix cores, fp32 accumulate).
-// Block = 4 waves over the same 16 rows, wave w takes every 4th 64-column
-// slice. Lane l: row l%16, 8-element chunk l/16 of each 32-column half; this
-// is also the A-operand layout of the 16x16x32 bf16 MFMA used for LoRA-down.
+// Block = RPB rows (16 or 32) and NWV = 4 RPB / 16 waves; wave w takes the
+// 64-column slices t = w, w + NWV, ... of all RPB rows, as Q = RPB / 16
+// tiles of 16 rows. Lane l: row l%16 of each tile, 8-element chunk l/16 of
+// each 32-column half; this is also the A-operand layout of the 16x16x32
+// bf16 MFMA of the LoRA-down, whose B fragments (read from L2 per slice) then
+// serve Q tiles.
+// Streaming: the next two slices of a wave are in flight while it quantizes
+// one (rounds of three name-rotated buffers; a round's surplus phases redo
+// the wave's last slice: identical stores, no low-rank accumulation), and no
+// load or code store in the loop is conditional: rows past the end are
+// clamped to the last row (their stores rewrite that row's identical bytes).
+// Code stores go through a wave-private LDS image of the slice's output
+// (LAY 1: the Q tiles of 512 bytes; LAY 2: the fp6 fragment rows of these
+// tiles), written back as whole 16-byte pieces of contiguous runs.
+// LAY: code layout (0 natural, 1 tiled int8-core fragments, 2 fp6 fragments).
 // ---------------------------------------------------------------------------
-template <bool UNSIGNED, bool LORA, int R = 32, bool QUANT = true, bool SM = false>
-__global__ __launch_bounds__(256) void rq_plain_kernel(RQParams a) {
+template <int RPB, int R>
+struct PlainSmem {
+  static constexpr int NWV = 4 * RPB / 16;
+  static constexpr int STAGE = 1536;                  // bytes per wave
+  static constexpr int LRED = NWV * RPB * R * 4;      // low-rank partial sums per wave
+  static constexpr int BYTES = (LRED > NWV * STAGE) ? LRED : NWV * STAGE;
+};
+
+template <bool UNSIGNED, bool LORA, int R = 32, bool QUANT = true, bool SM = false, int LAY = 0, int RPB = 16>
+__global__ __launch_bounds__(4 * RPB / 16 * 64) void rq_plain_kernel(RQParams a) {
   static_assert(R == 32 || R == 64, "low-rank branch of rank 32 or 64");
   static_assert(QUANT || LORA, "nothing to do");
+  static_assert(RPB == 16 || RPB == 32, "16 or 32 rows per block");
   constexpr int RB = R / 16;
-  __shared__ float lred[LORA ? 4 : 1][16][LORA ? R : 1];
+  constexpr int Q = RPB / 16;
+  constexpr int NWV = PlainSmem<RPB, R>::NWV;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[PlainSmem<RPB, (LORA ? R : 1)>::BYTES];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int l = tid & 63;
   const int rl = l & 15;
   const int c = l >> 4;
-  const int64_t row = (int64_t)blockIdx.x * 16 + rl;
-  const bool rok = row < a.rows;
-  const int64_t rowc = rok ? row : (a.rows - 1);
-  const uint16_t* xr = a.x + rowc * a.ldx;
+  int64_t rowc[Q];
+  const uint16_t* xr[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int64_t row = (int64_t)blockIdx.x * RPB + 16 * q + rl;
+    rowc[q] = (row < a.rows) ? row : (a.rows - 1);
+    xr[q] = a.x + rowc[q] * a.ldx + c * 8;
+  }
   const int nsl = (int)(a.K / 64);
   const float sh = a.shift;
   const float qmax = UNSIGNED ? 15.f : 7.f;
-  v4f acc[RB];
+  uint8_t* stage = smem + wave * PlainSmem<RPB, R>::STAGE;
+  v4f acc[Q][RB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) acc[rb] = v4f{0, 0, 0, 0};
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc[q][rb] = v4f{0, 0, 0, 0};
 
-  for (int t = wave; t < nsl; t += 4) {
-    u32x4 w0 = *reinterpret_cast<const u32x4*>(xr + t * 64 + c * 8);
-    u32x4 w1 = *reinterpret_cast<const u32x4*>(xr + t * 64 + 32 + c * 8);
-    float v[16];
+  const int nw = (nsl - wave + NWV - 1) / NWV;
+  const int tlast = wave + NWV * (nw - 1);
+  auto tof = [&](int i) { return min(wave + NWV * i, tlast); };
+  auto ld = [&](int t, u32x4 (&w)[Q][2]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[2 * j] = bf16_lo(w0[j]);
-      v[2 * j + 1] = bf16_hi(w0[j]);
-      v[8 + 2 * j] = bf16_lo(w1[j]);
-      v[8 + 2 * j + 1] = bf16_hi(w1[j]);
+    for (int q = 0; q < Q; ++q) {
+      w[q][0] = *reinterpret_cast<const u32x4*>(xr[q] + t * 64);
+      w[q][1] = *reinterpret_cast<const u32x4*>(xr[q] + t * 64 + 32);
     }
-    if constexpr (SM) {   // elements t*64 + c*8 + 0..7 and t*64 + 32 + c*8 + 0..7
-      const v4f* m0 = reinterpret_cast<const v4f*>(a.smooth + t * 64 + c * 8);
-      const v4f* m1 = reinterpret_cast<const v4f*>(a.smooth + t * 64 + 32 + c * 8);
-      const v4f ma = m0[0], mb = m0[1], mc = m1[0], md = m1[1];
+  };
+  auto step = [&](int i, const u32x4 (&cur)[Q][2], u32x4 (&nxt)[Q][2]) {
+    const int t = tof(i);
+    const bool valid = i < nw;
+    // low-rank fragments of this slice (L2 hits), issued before the prefetch
+    // of slice i + 2 so that waiting for them (in-order counter) leaves that
+    // prefetch in flight; consumed after the quantization
+    u32x4 lb[LORA ? 2 : 1][LORA ? RB : 1];
+    if constexpr (LORA) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[e] = __fmul_rn(v[e], ma[e]);
-        v[4 + e] = __fmul_rn(v[4 + e], mb[e]);
-        v[8 + e] = __fmul_rn(v[8 + e], mc[e]);
-        v[12 + e] = __fmul_rn(v[12 + e], md[e]);
-      }
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          lb[h][rb] = *reinterpret_cast<const u32x4*>(a.lora_down + (int64_t)(rb * 16 + rl) * a.K + t * 64 + h * 32 + c * 8);
     }
-    if (LORA) {
-      // la += X[16 rows, 64 cols] @ L2^T[64 cols, R ranks]
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        u32x4 xa = h ? w1 : w0;
-        v8bf afr = __builtin_bit_cast(v8bf, xa);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const uint16_t* lp = a.lora_down + (int64_t)(rb * 16 + rl) * a.K + t * 64 + h * 32 + c * 8;
-          u32x4 lb = *reinterpret_cast<const u32x4*>(lp);
-          acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(v8bf, lb), acc[rb], 0, 0, 0);
-        }
-      }
-    }
+    ld(tof(i + 2), nxt);
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (QUANT) {
-      float m = 0.f;
-      if (UNSIGNED) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          v[e] = __fadd_rn(v[e], sh);
-          m = fmaxf(m, v[e]);
+      for (int q = 0; q < Q; ++q) {
+        const u32x4 w0 = cur[q][0], w1 = cur[q][1];
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[2 * j] = bf16_lo(w0[j]);
+          v[2 * j + 1] = bf16_hi(w0[j]);
+          v[8 + 2 * j] = bf16_lo(w1[j]);
+          v[8 + 2 * j + 1] = bf16_hi(w1[j]);
         }
-      } else {
+        if constexpr (SM) {   // elements t*64 + c*8 + 0..7 and t*64 + 32 + c*8 + 0..7
+          const v4f* m0 = reinterpret_cast<const v4f*>(a.smooth + t * 64 + c * 8);
+          const v4f* m1 = reinterpret_cast<const v4f*>(a.smooth + t * 64 + 32 + c * 8);
+          const v4f ma = m0[0], mb = m0[1], mc = m1[0], md = m1[1];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[e]));
-      }
-      // max over the 4 lanes of this row (l, l^16, l^32, l^48)
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
-      const float r = (m > 0.f) ? div_rn(qmax, m) : 0.f;
-      if (rok && c == 0) {
-        float s = (m > 0.f) ? div_rn(m, qmax) : 0.f;
-        reinterpret_cast<float*>(a.scales)[row * nsl + t] = s;
-      }
-      if (a.tiled == 2) {
-        // fp6 fragments: signed codes as themselves, unsigned codes u as the
-        // E2M3 value u/2 (exact; the GEMM doubles the product). The lane's
-        // runs (elements 8c.. of each 32-column half) are 48-bit pieces; the
-        // lane with even c joins its piece with that of lane c + 1 (lane ^ 16)
-        // and stores the 96 bits as half c/2 of the fragment lane of its row.
-        v16f s0 = {}, s1 = {};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int e0 = (i < 4) ? 2 * i : 8 + 2 * (i - 4);
-          float q0, q1;
-          if (UNSIGNED) {
-            q0 = 0.5f * fminf(fmaxf(rintf(__fmul_rn(v[e0], r)), 0.f), 15.f);
-            q1 = 0.5f * fminf(fmaxf(rintf(__fmul_rn(v[e0 + 1], r)), 0.f), 15.f);
-          } else {
-            q0 = __fsub_rn(__fadd_rn(__fmul_rn(v[e0], r), CR_MAGIC_RNE), CR_MAGIC_RNE);
-            q1 = __fsub_rn(__fadd_rn(__fmul_rn(v[e0 + 1], r), CR_MAGIC_RNE), CR_MAGIC_RNE);
+          for (int e = 0; e < 4; ++e) {
+            v[e] = __fmul_rn(v[e], ma[e]);
+            v[4 + e] = __fmul_rn(v[4 + e], mb[e]);
+            v[8 + e] = __fmul_rn(v[8 + e], mc[e]);
+            v[12 + e] = __fmul_rn(v[12 + e], md[e]);
           }
-          s0[i] = q0;
-          s1[i] = q1;
         }
-        const auto o = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(s0, s1, 1.0f);
-        uint32_t ra[2], rb[2];                       // run h: bits 0..31 and 32..47
-        ra[0] = o[0];
-        rb[0] = o[1] & 0xFFFFu;
-        ra[1] = (o[1] >> 16) | (o[2] << 16);
-        rb[1] = o[2] >> 16;
-        uint32_t pa[2], pb[2];
+        float m = 0.f;
+        if (UNSIGNED) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          pa[h] = (uint32_t)__shfl_xor((int)ra[h], 16);
-          pb[h] = (uint32_t)__shfl_xor((int)rb[h], 16);
+          for (int e = 0; e < 16; ++e) {
+            v[e] = __fadd_rn(v[e], sh);
+            m = fmaxf(m, v[e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(v[e]));
         }
-        if (rok && (c & 1) == 0) {
-          uint8_t* frag = reinterpret_cast<uint8_t*>(a.codes) + ((row >> 5) * (a.K / 64) + t) * 1536;
+        // max over the 4 lanes of this row (l, l^16, l^32, l^48)
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        const float r = (m > 0.f) ? div_rn(qmax, m) : 0.f;
+        reinterpret_cast<float*>(a.scales)[rowc[q] * nsl + t] = (m > 0.f) ? div_rn(m, qmax) : 0.f;
+        if constexpr (LAY == 2) {
+          // fp6: signed codes as themselves, unsigned codes u as the E2M3
+          // value u/2 (exact; the GEMM doubles the product). Run h of this
+          // lane (elements 32h + 8c ..) is quarter c (6 bytes at 6c of 24) of
+          // fragment lane 32h + row % 32; bytes 0..15 of a fragment lane sit
+          // at lane * 16, bytes 16..23 at 1024 + lane * 8.
+          v16f s0 = {}, s1 = {};
+#pragma unroll
+          for (int i2 = 0; i2 < 8; ++i2) {
+            const int e0 = (i2 < 4) ? 2 * i2 : 8 + 2 * (i2 - 4);
+            float q0, q1;
+            if (UNSIGNED) {
+              q0 = 0.5f * fminf(fmaxf(rintf(__fmul_rn(v[e0], r)), 0.f), 15.f);
+              q1 = 0.5f * fminf(fmaxf(rintf(__fmul_rn(v[e0 + 1], r)), 0.f), 15.f);
+            } else {
+              q0 = __fsub_rn(__fadd_rn(__fmul_rn(v[e0], r), CR_MAGIC_RNE), CR_MAGIC_RNE);
+              q1 = __fsub_rn(__fadd_rn(__fmul_rn(v[e0 + 1], r), CR_MAGIC_RNE), CR_MAGIC_RNE);
+            }
+            s0[i2] = q0;
+            s1[i2] = q1;
+          }
+          const auto o = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(s0, s1, 1.0f);
+          // run 0: bits 0..47 of o; run 1: bits 48..95
+          const uint32_t r0a = o[0], r0b = o[1] & 0xFFFFu;
+          const uint32_t r1a = (o[1] >> 16) | (o[2] << 16), r1b = o[2] >> 16;
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const int lm = 32 * h + (int)(row & 31);
-            uint32_t* w0 = reinterpret_cast<uint32_t*>(frag + lm * 16 + ((c >> 1) ? 12 : 0));
-            uint32_t* w1 = (c >> 1) ? reinterpret_cast<uint32_t*>(frag + 1024 + lm * 8) : w0 + 1;
-            w0[0] = ra[h];
-            w1[0] = rb[h] | (pa[h] << 16);
-            w1[1] = (pa[h] >> 16) | (pb[h] << 16);
+            const uint32_t pa = h ? r1a : r0a, pb = h ? r1b : r0b;   // 48 bits: pa (32) then pb (16)
+            const int lm = 32 * h + (int)(rowc[q] & 31);
+            uint8_t* f = stage + lm * 16;
+            uint8_t* g = stage + 1024 + lm * 8;
+            if (c == 0) {            // bytes 0..5
+              *reinterpret_cast<uint32_t*>(f) = pa;
+              *reinterpret_cast<uint16_t*>(f + 4) = (uint16_t)pb;
+            } else if (c == 1) {     // bytes 6..11
+              *reinterpret_cast<uint16_t*>(f + 6) = (uint16_t)pa;
+              *reinterpret_cast<uint32_t*>(f + 8) = (pa >> 16) | (pb << 16);
+            } else if (c == 2) {     // bytes 12..17
+              *reinterpret_cast<uint32_t*>(f + 12) = pa;
+              *reinterpret_cast<uint16_t*>(g) = (uint16_t)pb;
+            } else {                 // bytes 18..23
+              *reinterpret_cast<uint16_t*>(g + 2) = (uint16_t)pa;
+              *reinterpret_cast<uint32_t*>(g + 4) = (pa >> 16) | (pb << 16);
+            }
+          }
+        } else {
+          uint32_t out[2] = {0u, 0u};
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            uint32_t b;
+            if (UNSIGNED) {
+              float p = rintf(__fmul_rn(v[e], r));
+              p = fminf(fmaxf(p, 0.f), 15.f);
+              b = (uint32_t)p;
+            } else {
+              b = qbits(v[e], r) & 0xF;
+            }
+            out[e >> 3] |= b << (4 * (e & 7));
+          }
+          if constexpr (LAY == 1) {
+            // elements 64t + 32h + 8c .. +8 are half (c&1) of chunk 2h + c/2 of k-tile t
+            uint8_t* dst = stage + q * 512 + (int)(rowc[q] & 15) * 8 + (c & 1) * 4;
+            *reinterpret_cast<uint32_t*>(dst + (c >> 1) * 128) = out[0];
+            *reinterpret_cast<uint32_t*>(dst + (2 + (c >> 1)) * 128) = out[1];
+          } else {
+            uint8_t* dst = reinterpret_cast<uint8_t*>(a.codes) + rowc[q] * (a.K / 2) + t * 32;
+            *reinterpret_cast<uint32_t*>(dst + c * 4) = out[0];
+            *reinterpret_cast<uint32_t*>(dst + 16 + c * 4) = out[1];
           }
         }
-        continue;
       }
-      uint32_t out[2] = {0u, 0u};
+      // the staged image back to global memory in 16-byte pieces (LDS
+      // accesses of one wave complete in order: no wait between)
+      if constexpr (LAY == 2) {
+        const int64_t fb = (int64_t)blockIdx.x * RPB / 32;               // 32-row fragment block
+        uint8_t* frag = reinterpret_cast<uint8_t*>(a.codes) + (fb * (a.K / 64) + t) * 1536;
+        const bool mine = (Q == 2) || (((l >> 4) & 1) == (int)(((int64_t)blockIdx.x * RPB / 16) & 1));
+        const u32x4 va = *reinterpret_cast<const u32x4*>(stage + l * 16);
+        const u32x2 vb = *reinterpret_cast<const u32x2*>(stage + 1024 + l * 8);
+        if (mine) {
+          *reinterpret_cast<u32x4*>(frag + l * 16) = va;
+          *reinterpret_cast<u32x2*>(frag + 1024 + l * 8) = vb;
+        }
+      } else if constexpr (LAY == 1) {
+        const int q = l >> 5;                                               // lanes 0..31: tile 0, 32..63: tile 1
+        const int64_t tb = (int64_t)blockIdx.x * Q + q;                     // 16-row tile
+        const u32x4 va = *reinterpret_cast<const u32x4*>(stage + l * 16);
+        if (q < Q && tb * 16 < a.rows)
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(a.codes) + (tb * (a.K / 64) + t) * 512 + (l & 31) * 16) = va;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (LORA && valid) {
+      // la += X[16 rows, 64 cols] @ L2^T[64 cols, R ranks], per 16-row tile
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        uint32_t b;
-        if (UNSIGNED) {
-          float p = rintf(__fmul_rn(v[e], r));
-          p = fminf(fmaxf(p, 0.f), 15.f);
-          b = (uint32_t)p;
-        } else {
-          b = qbits(v[e], r) & 0xF;
+      for (int q = 0; q < Q; ++q)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const v8bf afr = __builtin_bit_cast(v8bf, cur[q][h]);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            acc[q][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, __builtin_bit_cast(v8bf, lb[h][rb]), acc[q][rb], 0, 0, 0);
         }
-        out[e >> 3] |= b << (4 * (e & 7));
-      }
-      if (rok) {
-        if (a.tiled) {
-          // elements 64t + 32h + 8c .. +8 are half (c&1) of chunk 2h + c/2 of k-tile t
-          uint8_t* dst = reinterpret_cast<uint8_t*>(a.codes) + ((row >> 4) * (a.K / 64) + t) * 512 + rl * 8 + (c & 1) * 4;
-          *reinterpret_cast<uint32_t*>(dst + (c >> 1) * 128) = out[0];
-          *reinterpret_cast<uint32_t*>(dst + (2 + (c >> 1)) * 128) = out[1];
-        } else {
-          uint8_t* dst = reinterpret_cast<uint8_t*>(a.codes) + row * (a.K / 2) + t * 32;
-          *reinterpret_cast<uint32_t*>(dst + c * 4) = out[0];
-          *reinterpret_cast<uint32_t*>(dst + 16 + c * 4) = out[1];
-        }
-      }
+    }
+  };
+  if (nw > 0) {
+    u32x4 b0[Q][2], b1[Q][2], b2[Q][2];
+    ld(tof(0), b0);
+    ld(tof(1), b1);
+    for (int i = 0; i < nw; i += 3) {
+      step(i, b0, b2);
+      step(i + 1, b1, b0);
+      step(i + 2, b2, b1);
     }
   }
   if constexpr (LORA) {
-    // output fragment: lane l holds rank rb*16 + l%16, rows 4*(l/16) + j
+    // output fragment: lane l holds rank rb*16 + l%16, rows 4*(l/16) + j of each tile
+    __syncthreads();                                   // the stage buffers become the reduction array
+    float* lred = reinterpret_cast<float*>(smem);      // [NWV][RPB][R]
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int q = 0; q < Q; ++q)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) lred[wave][4 * c + j][rb * 16 + rl] = acc[rb][j];
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lred[(wave * RPB + 16 * q + 4 * c + j) * R + rb * 16 + rl] = acc[q][rb][j];
     __syncthreads();
-    for (int idx = tid; idx < 16 * R; idx += 256) {
-      int rr = idx / R, rk = idx % R;
-      int64_t orow = (int64_t)blockIdx.x * 16 + rr;
+    for (int idx = tid; idx < RPB * R; idx += NWV * 64) {
+      const int rr = idx / R, rk = idx % R;
+      const int64_t orow = (int64_t)blockIdx.x * RPB + rr;
       if (orow >= a.rows) continue;
-      float s = ((lred[0][rr][rk] + lred[1][rr][rk]) + lred[2][rr][rk]) + lred[3][rr][rk];
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) s += lred[(w * RPB + rr) * R + rk];
       if (a.lora_f32)
         reinterpret_cast<float*>(a.lora_act)[orow * R + rk] = s;
       else
@@ -823,12 +909,31 @@ hipError_t launch_rotate_quantize_dual(RQParams p, hipStream_t s) {
   }
 }
 
+template <bool UNSIGNED, bool SM, int LAY, int RPB>
+static hipError_t launch_plain_rpb(const RQParams& p, bool lora, hipStream_t s) {
+  const dim3 grid((unsigned)((p.rows + RPB - 1) / RPB)), block(4 * RPB / 16 * 64);
+  if (!lora)
+    hipLaunchKernelGGL((rq_plain_kernel<UNSIGNED, false, 32, true, SM, LAY, RPB>), grid, block, 0, s, p);
+  else if (p.R == 64)
+    hipLaunchKernelGGL((rq_plain_kernel<UNSIGNED, true, 64, true, SM, LAY, 16>), dim3((unsigned)((p.rows + 15) / 16)),
+                       dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((rq_plain_kernel<UNSIGNED, true, 32, true, SM, LAY, RPB>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+// 32-row blocks (each low-rank fragment read from L2 serves two 16-row
+// tiles) once they still give one block per CU; 16-row blocks otherwise
+template <bool UNSIGNED, bool SM, int LAY>
+static hipError_t launch_plain_lay(const RQParams& p, bool lora, hipStream_t s) {
+  if ((p.rows + 31) / 32 >= 256) return launch_plain_rpb<UNSIGNED, SM, LAY, 32>(p, lora, s);
+  return launch_plain_rpb<UNSIGNED, SM, LAY, 16>(p, lora, s);
+}
 template <bool UNSIGNED, bool SM>
 static hipError_t launch_plain(const RQParams& p, int nblk, bool lora, hipStream_t s) {
-  if (!lora) hipLaunchKernelGGL((rq_plain_kernel<UNSIGNED, false, 32, true, SM>), dim3(nblk), dim3(256), 0, s, p);
-  else if (p.R == 64) hipLaunchKernelGGL((rq_plain_kernel<UNSIGNED, true, 64, true, SM>), dim3(nblk), dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((rq_plain_kernel<UNSIGNED, true, 32, true, SM>), dim3(nblk), dim3(256), 0, s, p);
-  return hipGetLastError();
+  (void)nblk;
+  if (p.tiled == 2) return launch_plain_lay<UNSIGNED, SM, 2>(p, lora, s);
+  if (p.tiled == 1) return launch_plain_lay<UNSIGNED, SM, 1>(p, lora, s);
+  return launch_plain_lay<UNSIGNED, SM, 0>(p, lora, s);
 }
 
 hipError_t launch_rotate_quantize(RQParams p, hipStream_t s) {
