@@ -318,9 +318,9 @@ __global__ __launch_bounds__((BM / (32 * TM)) * (BN / (32 * TN)) * 64, MINB) voi
 // Block 128 x 128, 2 x 2 waves of 64 x 64, stages of two k-tiles with their
 // scales (26 KB: activation scales gathered as 4-byte pieces of the row-major
 // [M, K/64] array, weight scales a contiguous 1 KB run of the packed
-// [N/128][K/64][128] array), two in the ring, two blocks per CU (182 VGPRs:
-// the scaled accumulation keeps 64 products beside 64 sums). Epilogue: shift
-// correction, low-rank branch
+// [N/128][K/64][128] array), two in the ring, three blocks per CU (167
+// VGPRs: one channel column's scale products and group sums are live at a
+// time beside the 64 sums). Epilogue: shift correction, low-rank branch
 // (32 x 32 x 16 bf16 or 32 x 32 x 2 f32 matrix ops onto the outputs), bias,
 // bf16 rows through LDS.
 // ---------------------------------------------------------------------------
@@ -352,7 +352,7 @@ CR_DEV void f6_lowrank_32(const GemmParams& p, int64_t m0w, int64_t n0w, int l, 
 }
 
 template <int OUT, bool UNS>
-__global__ __launch_bounds__(256, 2) void gemm_f6_grp_kernel(GemmParams p) {
+__global__ __launch_bounds__(256, 3) void gemm_f6_grp_kernel(GemmParams p) {
   constexpr int BM = 128, BN = 128, BKT = 2, NW = 4, WN = 2;
   constexpr int A_ST = (BM / 32) * BKT * F6_FRAG, W_ST = (BN / 32) * BKT * F6_FRAG;
   constexpr int SA_ST = BKT * BM * 4, SW_ST = BKT * BN * 4;
@@ -451,21 +451,18 @@ __global__ __launch_bounds__(256, 2) void gemm_f6_grp_kernel(GemmParams p) {
         // the 32 x 32 output layout of the fp6 op: one FMA per output and
         // group is left on the vector ALUs
         const float sa = Sa[kt * BM + wm * 64 + l] * UF;
-        v32f c[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          c[j] = __builtin_amdgcn_mfma_f32_32x32x1f32(Sw[kt * BN + (wn * 2 + j) * 32 + lr], sa, v32f{}, 0, 0, 0);
-        v16f pp[2][2];
+        for (int j = 0; j < 2; ++j) {
+          const v32f c = __builtin_amdgcn_mfma_f32_32x32x1f32(Sw[kt * BN + (wn * 2 + j) * 32 + lr], sa, v32f{}, 0, 0, 0);
+          const v16f p0 = mfma_f6_32(wv[j], av[0], v16f{});
+          const v16f p1 = mfma_f6_32(wv[j], av[1], v16f{});
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) pp[i][j] = mfma_f6_32(wv[j], av[i], v16f{});
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(pp[i][j][r], c[j][16 * i + r], acc[i][j][r]);
+          for (int r = 0; r < 16; ++r) {
+            acc[0][j][r] = __builtin_fmaf(p0[r], c[r], acc[0][j][r]);
+            acc[1][j][r] = __builtin_fmaf(p1[r], c[16 + r], acc[1][j][r]);
+          }
+          asm volatile("" : "+v"(acc[0][j]), "+v"(acc[1][j]));   // one column's products live at a time
+        }
       }
     }
   }
