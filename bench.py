@@ -260,9 +260,10 @@ def main():
     ops_step = 2.0 * (M_BIG + M_SMALL) * N * K
     eff_tops = ops_step / (ms_step * 1e-3) / 1e12
     gemm_tops = 2.0 * M_BIG * N * K / (t_gemm_big * 1e-3) / 1e12
-    rq_bytes = M_BIG * K * 2 + M_BIG * K // 2 + 4
+    rq_bytes = M_BIG * K * 2 + M_BIG * K * (0.75 if CORES == "fp6" else 0.5) + 4   # bf16 in, codes (6 or 4 bits) out
     rq_gbs = rq_bytes / (t_rq_big * 1e-3) / 1e9
-    small_bytes = N * K // 2 + M_SMALL * K // 2 + M_SMALL * N * 2
+    cb = 0.75 if CORES == "fp6" else 0.5                      # bytes per code in the operand layout
+    small_bytes = N * K * cb + M_SMALL * K * cb + M_SMALL * N * 2
     traffic = traffic_from_profile()
     peak = FP6_PEAK_TOPS if CORES == "fp6" else INT8_PEAK_TOPS
 
