@@ -88,12 +88,15 @@ F6_CASES = [
     (17, 384, 3072, "tensor", "row"),
     (33, 128, 1024, "row", "row"),
     (64, 256, 512, "row", "tensor"),
-    (65, 256, 512, "tensor", "tensor"),       # tiled kernel from here on; one ragged 32-row block
+    (65, 256, 512, "tensor", "tensor"),       # tiled kernel from here on (64 x 64 blocks while 128 x 128
+                                              # ones would number fewer than 256); one ragged 32-row block
     (77, 768, 256, "row", "tensor"),          # two 128-deep stages
     (200, 384, 3072, "tensor", "tensor"),
     (256, 384, 3072, "row", "row"),
     (300, 512, 768, "tensor", "tensor"),
     (129, 128, 12288, "tensor", "tensor"),
+    (2100, 2048, 256, "row", "tensor"),       # 128 x 128 blocks (>= 256 of them, N not a multiple of 192)
+    (1300, 3072, 512, "tensor", "row"),       # 256 x 192 blocks would be too few: 128 x 128
 ]
 
 

@@ -664,6 +664,13 @@ static hipError_t launch_f6_out(const GemmParams& p, hipStream_t s) {
     return hipGetLastError();
   }
   const int64_t tiles = ((p.M + 127) / 128) * (p.N / 128);
+  if (tiles < 256) {
+    // mid-size M (e.g. 512 text tokens): 128 x 128 blocks leave most CUs
+    // idle, so 64 x 64 blocks of four 32 x 32 waves, three stages
+    const int64_t t64 = ((p.M + 63) / 64) * (p.N / 64);
+    hipLaunchKernelGGL((gemm_f6_kernel<64, 64, 1, 1, 2, 3, 4, OUT>), dim3((unsigned)t64), dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((gemm_f6_kernel<128, 128, 2, 2, 2, 2, 3, OUT>), dim3((unsigned)tiles), dim3(256), 0, s, p);
   return hipGetLastError();
 }
