@@ -199,7 +199,9 @@ def test_w4a4_group64_lowrank(cr, case):
     _check_out(yb, yf, ref["y"])
 
 
-INT8_CASES = [(2, 256, 3072), (33, 384, 512), (64, 128, 256), (190, 256, 1024), (512, 384, 3072)]
+# M <= 64: weight streaming; above: the direct-to-LDS kernel of 256 x 128
+# blocks (2600 x 3072: 264 of them, a ragged last row block)
+INT8_CASES = [(2, 256, 3072), (33, 384, 512), (64, 128, 256), (190, 256, 1024), (512, 384, 3072), (2600, 3072, 256)]
 
 
 @pytest.mark.parametrize("case", INT8_CASES)
