@@ -225,6 +225,8 @@ F6_G64_CASES = [
     (300, 512, 1024, True, "bf16", 64, True),
     (100, 384, 128, False, None, 0, True),      # a single 128-deep stage
     (1, 128, 256, True, "bf16", 32, True),
+    (1000, 384, 1152, True, "bf16", 32, True),   # ragged 128-row block, nine 128-deep stages
+    (515, 256, 640, False, "f32", 64, False),    # five stages, a 3-row tail
 ]
 
 
