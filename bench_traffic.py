@@ -22,10 +22,10 @@ traffic. Each is scaled by the same counter's reading for the copy kernel
 divided by the copy's known bytes, so `hbm_bytes_per_launch` is in the
 units the copy kernel calibrates.
 
-Commands (from /tmp with TMPDIR=/tmp):
-  rocprofv3 --pmc FETCH_SIZE -d $REPO/gpurun_out/tf -o tf --output-format csv -- python3 $REPO/bench_traffic.py run
-  rocprofv3 --pmc WRITE_SIZE -d $REPO/gpurun_out/tw -o tw --output-format csv -- python3 $REPO/bench_traffic.py run
-  python3 $REPO/bench_traffic.py summarize $REPO/gpurun_out/tf $REPO/gpurun_out/tw
+Commands (from /tmp with TMPDIR=/tmp; OUT = a directory for the counter output):
+  rocprofv3 --pmc FETCH_SIZE -d $OUT/tf -o tf --output-format csv -- python3 $REPO/bench_traffic.py run
+  rocprofv3 --pmc WRITE_SIZE -d $OUT/tw -o tw --output-format csv -- python3 $REPO/bench_traffic.py run
+  python3 $REPO/bench_traffic.py summarize $OUT/tf $OUT/tw
 """
 import csv
 import glob
@@ -114,12 +114,12 @@ def summarize(dfetch, dwrite):
         json.dump(d, f, indent=1)
     with open(_out(".md"), "w") as f:
         f.write(f"# HBM traffic: W4A4 GEMM on the {bench.CORES} matrix cores, M=4096, N=K=3072 (benchmarked kernel)\n\n")
-        f.write("Commands (from /tmp with TMPDIR=/tmp, REPO = repository root):\n\n")
-        f.write("    rocprofv3 --pmc FETCH_SIZE -d $REPO/gpurun_out/tf -o tf --output-format csv -- "
+        f.write("Commands (from /tmp with TMPDIR=/tmp, REPO = repository root, OUT = the counter output directory):\n\n")
+        f.write("    rocprofv3 --pmc FETCH_SIZE -d $OUT/tf -o tf --output-format csv -- "
                 f"python3 $REPO/bench_traffic.py run{arg}\n")
-        f.write("    rocprofv3 --pmc WRITE_SIZE -d $REPO/gpurun_out/tw -o tw --output-format csv -- "
+        f.write("    rocprofv3 --pmc WRITE_SIZE -d $OUT/tw -o tw --output-format csv -- "
                 f"python3 $REPO/bench_traffic.py run{arg}\n")
-        f.write(f"    python3 $REPO/bench_traffic.py summarize $REPO/gpurun_out/tf $REPO/gpurun_out/tw{arg}\n\n")
+        f.write(f"    python3 $REPO/bench_traffic.py summarize $OUT/tf $OUT/tw{arg}\n\n")
         f.write(f"Copy-kernel calibration ({COPY_MIB} MiB read + {COPY_MIB} MiB written by torch.neg): "
                 f"FETCH_SIZE reads {kf:.4f} x the bytes read, WRITE_SIZE {kw:.4f} x the bytes written.\n\n")
         f.write("| per GEMM launch | bytes |\n|---|---|\n")
