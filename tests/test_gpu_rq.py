@@ -260,6 +260,36 @@ def test_rotate_quantize_strided_rows_and_zero_rows(cr):
         assert np.array_equal(host(scales).reshape(-1), np.asarray(ref["scales"]).reshape(-1))
 
 
+@pytest.mark.parametrize("unsigned", [False, True])
+def test_rotate_quantize_plain_strided_rows_and_zero_rows(cr, unsigned):
+    """Unrotated 64-group quantizer on a row-strided view (ldx = K + 64) with
+    all-zero rows, through the 32-row blocks (8170 rows), every code layout
+    and the fused rank-32 down-projection (identical to the contiguous run)."""
+    rows, K, ldx = 8170, 256, 320
+    say(f"rq plain strided unsigned={unsigned}")
+    xb = (wl.gelu_activation if unsigned else wl.activation)(18, 5, rows, ldx)
+    xb[3, :] = 0
+    xb[rows - 1, :K] = 0
+    shift = 0.171875 if unsigned else 0.0
+    qt = 2 if unsigned else 0
+    dense = np.ascontiguousarray(xb[:, :K])
+    ref = ol.rotate_quantize(dense, 0, "uint4_shift" if unsigned else "int4", "row_group", 64, shift)
+    l2 = bf16_dev(wl.weight(18, 6, 32, K, std=0.05))
+    view = bf16_dev(xb)[:, :K]
+    _, _, _, la_dense = cr.convrot_rotate_quantize(bf16_dev(dense), 0, qt, 2, 64, shift=shift, lora_down=l2)
+    for layout in (0, 1, 3):
+        codes, scales, _, la = cr.convrot_rotate_quantize(view, 0, qt, 2, 64, shift=shift, lora_down=l2, layout=layout)
+        got = host(codes)
+        if layout == 0:
+            assert np.array_equal(got, ref["codes"])
+        elif layout == 1:
+            assert np.array_equal(opack.tile_unpack_a(got, rows), ref["codes"])
+        else:
+            assert np.array_equal(opack.f6_unpack(got, rows) * (2 if unsigned else 1), ref["values"])
+        assert np.array_equal(host(scales).view(np.uint32), ref["scales"].view(np.uint32))
+        assert np.array_equal(host(la), host(la_dense))
+
+
 def test_rotate_quantize_subnormal_and_tiny_inputs(cr):
     rows, K = 8, 512
     g = np.random.default_rng(5)
