@@ -24,7 +24,8 @@ M=4096 GEMM) against the dense peak of the matrix instruction it runs on
 (fp6: 10.1 PFLOP/s; int8: 5.0 POP/s); its duration is the mean over K
 back-to-back launches, timed with HIP events on the launch stream
 (kernels_us.gemm_m4096_in_step: events around each launch inside the steps,
-which also hold the launch gap). The CPU baseline is the numpy oracle
+which also hold the launch gap). The M=4096 rotate+quantize (two launches)
+is timed the same way for rq_m4096_GBps. The CPU baseline is the numpy oracle
 running the same step on this host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--rot-group 256] [--cores fp6|int8]
@@ -270,6 +271,14 @@ def main():
     g1.record(stream)
     torch.cuda.synchronize()
     t_gemm_big = g0.elapsed_time(g1) / args.steps
+    # the same for the M=4096 rotate+quantize (its two launches)
+    torch.cuda.synchronize()
+    g0.record(stream)
+    for i in range(args.steps):
+        rq_big(cr, sets[i % nsets])
+    g1.record(stream)
+    torch.cuda.synchronize()
+    t_rq_call, t_rq_big = t_rq_big, g0.elapsed_time(g1) / args.steps
 
     ops_step = 2.0 * (M_BIG + M_SMALL) * N * K
     eff_tops = ops_step / (ms_step * 1e-3) / 1e12
@@ -300,6 +309,7 @@ def main():
                    "matrix_cores": CORES, "buffer_sets": nsets},
         "pct_int8_peak": round(100.0 * eff_tops / INT8_PEAK_TOPS, 2),
         "kernels_us": {"rq_m4096": round(t_rq_big * 1e3, 2), "gemm_m4096": round(t_gemm_big * 1e3, 2),
+                       "rq_m4096_in_step": round(t_rq_call * 1e3, 2),
                        "gemm_m4096_in_step": round(t_gemm_call * 1e3, 2),
                        "rq_m32": round(t_rq_small * 1e3, 2), "gemm_m32": round(t_gemm_small * 1e3, 2)},
         "rq_m4096_GBps": round(rq_gbs, 1),
