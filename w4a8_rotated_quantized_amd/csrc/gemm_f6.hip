@@ -312,9 +312,11 @@ __global__ __launch_bounds__((BM / (32 * TM)) * (BN / (32 * TN)) * 64, MINB) voi
 // ---------------------------------------------------------------------------
 // 64-group scales on both sides (the SVDQuant format): one 32 x 32 x 64 matrix
 // op covers exactly one group, so its float32 result P (exact) is scaled
-// right away: y += P * (s_a[m, g] * s_w[n, g]), two VALU ops per output and
-// group. Unsigned shifted activations (codes u in [0, 15]) come as the E2M3
-// values u/2, so P is half the integer sum and the factor 2 joins the scale.
+// right away: y += P * (s_a[m, g] * s_w[n, g]). The scale products come from
+// a two-block outer-product matrix op (see the loop), which leaves one VALU
+// FMA per output and group. Unsigned shifted activations (codes u in
+// [0, 15]) come as the E2M3 values u/2, so P is half the integer sum and the
+// factor 2 joins the scale.
 // Block 128 x 128, 2 x 2 waves of 64 x 64, stages of two k-tiles with their
 // scales (26 KB: activation scales gathered as 4-byte pieces of the row-major
 // [M, K/64] array, weight scales a contiguous 1 KB run of the packed
