@@ -108,6 +108,7 @@ def test_rq_validation(cr):
     assert _rq(cr, layout=3, q=1) == 3                       # not for int8 codes
     assert _rq(cr, layout=3, rot=0, g=2, qg=64, ws=None, wsb=0) == 4   # 64-group codes without rotation
     assert _rq(cr, layout=3, rot=0, q=2, g=2, qg=64, ws=None, wsb=0) == 4   # unsigned shifted codes too
+    assert _rq(cr, layout=3, q=3, g=2, qg=16, zeros=A) == 3   # asymmetric weight codes: no fp6 layout
     assert _rq(cr, smooth=A, g=1) == 4                       # smoothing: rotation 256 with row scales
     assert _rq(cr, smooth=A, g=2, qg=64) == 4
     assert _rq(cr, smooth=A) == 3                            # not with per-tensor scales
@@ -213,6 +214,8 @@ def test_gemm_validation(cr):
     assert _w4a4(cr, layout=3, ag=2, wg=2) == 4              # fp6 with 64-group scales
     assert _w4a4(cr, layout=3, ag=2, wg=2, uns=1, wsum=A, la=A, lu=A, R=64) == 4
     assert _w4a4(cr, layout=3, ag=2, wg=0) == 3
+    assert _w4a4(cr, layout=3, ag=2, wg=2, uns=1) == 1        # unsigned codes need the column sums
+    assert _w4a4(cr, layout=3, ag=2, wg=2, la=A, lu=A, R=16) == 3   # rank 32 or 64 only
     assert _w4a4(cr, layout=3, uns=1, wsum=A) == 3           # fp6, tensor scales: signed codes only
     assert _w4a4(cr, layout=3, la=A, lu=A, R=32) == 3        # and no low-rank branch
     assert _w4a4(cr, layout=2, uns=1, wsum=A) == 3           # 8-bit activations: signed only
