@@ -21,7 +21,7 @@ def _plan(w):
     feeds both per-tensor INT4 and INT8 layers is quantized once, to both
     (convrot_rotate_quantize_dual)."""
     def kind_of(lin):
-        return {"w4a4": "int4_tensor", "int8": "int8_tensor", "w4a8": "int8_row", "a8w4": "int8_row",
+        return {"w4a4": "int4_tensor", "int8": "int8_tensor", "w4a8": "int8_row_f16", "a8w4": "int8_row",
                 "w4a4_g64": ("u4_g64" if lin.unsigned_shift else "s4_g64")}[lin.fmt]
     kinds = {}
     for lin in w.linears:
@@ -63,7 +63,7 @@ def run_merge(steps, warmup):
         cr.convrot_dequantize_weights(codes, scales, N, K, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16, 256, zeros=zeros,
                                       delta_up=up, delta_down=down, out=merged)
         cr.convrot_rotate_quantize(merged, 256, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16, codes=c2, scales=s2, zeros=z2)
-        cr.w4_pack_weights(c2, s2, N, K, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16, zeros=z2, want_wsum=True)
+        cr.w4_pack_weights(c2, s2, N, K, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16, zeros=z2)
 
     for _ in range(warmup):
         step()
@@ -127,9 +127,8 @@ def run(name, steps, warmup, cores="fp6"):
         elif lin.fmt == "w4a8":
             wc, ws, wz, _ = cr.convrot_rotate_quantize(bf16(wl.weight_bits(w, lin)), 256, cr.Q.ASYM_UINT4,
                                                        cr.GRAN.ROW_GROUP, 16)
-            p, ps, pz, wsum = cr.w4_pack_weights(wc, ws, N, K, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16, zeros=wz,
-                                                 want_wsum=True)
-            prep[lin.name] = dict(w=p, ws=ps, wz=pz, wsum=wsum)
+            p, ps, pz, _ = cr.w4_pack_weights(wc, ws, N, K, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16, zeros=wz)
+            prep[lin.name] = dict(w=p, ws=ps, wz=pz)
         else:
             l1, l2, r = wl.lowrank_bits(w, lin)
             wc, ws, _, _ = cr.convrot_rotate_quantize(bf16(r), 0, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64)
@@ -165,8 +164,9 @@ def run(name, steps, warmup, cores="fp6"):
                      codes8=torch.empty((M, K), dtype=torch.int8, device=dev),
                      scales8=torch.empty(1, dtype=torch.float32, device=dev),
                      ws=torch.empty(cr.convrot_rq_workspace_size(M, K, 256, 0, 0), dtype=torch.uint8, device=dev))
-        elif kind == "int8_row":
-            o = dict(codes=torch.empty((M, K), dtype=torch.int8, device=dev),
+        elif kind in ("int8_row", "int8_row_f16"):
+            o = dict(codes=torch.empty((M, K), dtype=torch.float16 if kind == "int8_row_f16" else torch.int8,
+                                       device=dev),
                      scales=torch.empty(M, dtype=torch.float32, device=dev), ws=None)
         else:
             o = dict(codes=torch.empty(c4_shape(M, K), dtype=torch.uint8, device=dev),
@@ -187,8 +187,9 @@ def run(name, steps, warmup, cores="fp6"):
         elif kind == "dual_tensor":
             cr.convrot_rotate_quantize_dual(x, 256, layout4=lay4, codes4=o["codes"], scale4=o["scales"],
                                             codes8=o["codes8"], scale8=o["scales8"], workspace=o["ws"])
-        elif kind == "int8_row":
-            cr.convrot_rotate_quantize(x, 256, cr.Q.SYM_INT8, cr.GRAN.ROW, codes=o["codes"], scales=o["scales"])
+        elif kind in ("int8_row", "int8_row_f16"):
+            cr.convrot_rotate_quantize(x, 256, cr.Q.SYM_INT8, cr.GRAN.ROW, codes=o["codes"], scales=o["scales"],
+                                       layout=cr.LAYOUT.F16 if kind == "int8_row_f16" else cr.LAYOUT.NATURAL)
         else:
             lin = [l for l in w.linears if l.name == lname][0]
             uns = kind == "u4_g64"
@@ -209,8 +210,7 @@ def run(name, steps, warmup, cores="fp6"):
             a8, s8 = (o["codes8"], o["scales8"]) if "codes8" in o else (o["codes"], o["scales"])
             cr.int8_tensorwise_gemm(a8, s8, p["w"], p["ws"], M, N, K, out=y)
         elif lin.fmt == "w4a8":
-            cr.w4a8_gemm(o["codes"], o["scales"], cr.GRAN.ROW, p["w"], p["ws"], p["wz"], M, N, K, out=y,
-                         w_sum=p["wsum"])
+            cr.w4a8_gemm(o["codes"], o["scales"], cr.GRAN.ROW, p["w"], p["ws"], p["wz"], M, N, K, out=y)
         else:
             cr.w4a4_gemm(o["codes"], o["scales"], 2, p["w"], p["ws"], 2, M, N, K,
                          a_unsigned=lin.unsigned_shift != 0.0, a_shift=lin.unsigned_shift, w_sum=p["wsum"],
@@ -265,7 +265,7 @@ def run(name, steps, warmup, cores="fp6"):
         x_id, kind, _ = key
         M, K = w.acts[x_id][0], w.acts[x_id][1]
         us = kern[f"rq:{x_id}:{kind}"]
-        code_b = 1.0 if kind.startswith("int8") else (0.75 if f6 else 0.5)   # fp6 fragments: 6 bits per code
+        code_b = 1.0 if kind.startswith("int8") else 0.5      # algorithmic: 8 or 4 bits per code
         out_b = M * K * code_b + (M * K if kind == "dual_tensor" else 0)
         rqs[f"{x_id}:{kind}"] = {"us": us, "GBps": round((M * K * 2 + out_b) / us / 1e3, 1)}
     dom = max(layers, key=lambda n: layers[n]["us"])

@@ -96,7 +96,7 @@ typedef enum cr_layout {
                           /* last block hold unspecified codes (allocate ceil(rows/16)*16 rows)*/
   CR_LAYOUT_INT8 = 2,     /* w4a4_gemm only: int8 codes [rows, K] row-major (SYM_INT8), the    */
                           /* 8-bit-activation branch for W4A4-format weights                   */
-  CR_LAYOUT_F6 = 3        /* signed int4 codes (values -7..7) as fp6 E2M3 (bit 5 sign, bits    */
+  CR_LAYOUT_F6 = 3,       /* signed int4 codes (values -7..7) as fp6 E2M3 (bit 5 sign, bits    */
                           /* 4:3 exponent with bias 1, bits 2:0 mantissa; every code is exact; */
                           /* an unsigned code u in 0..15 is stored as the exact value u/2)     */
                           /* in 32 x 64 operand fragments [ceil(rows/32)][K/64][1536 B]: lane  */
@@ -106,6 +106,9 @@ typedef enum cr_layout {
                           /* of the fp6 matrix-core W4A4 GEMM (weights from w4_pack_weights_f6);*/
                           /* rows past `rows` in the last block hold unspecified codes (any     */
                           /* 6-bit field is a finite value; allocate ceil(rows/32)*32 rows)      */
+  CR_LAYOUT_F16 = 4       /* SYM_INT8 codes as IEEE fp16 values [rows, K] row-major (every code */
+                          /* -127..127 is exact; zero is +0): the activation operand of         */
+                          /* w4a8_gemm's fp16 matrix cores, used without conversion              */
 } cr_layout;
 
 /* Status text, e.g. "format not available" for CR_ERR_UNSUPPORTED_FORMAT. */
@@ -169,12 +172,14 @@ void convrot_reset_counters(void);
  *                "Qwen-Image-Edit-2511-W4A8-ConvRot" card, passage on LoRA merge
  *                versus bypass)
  *   codes        SYM_INT4 / UNSIGNED / ASYM: uint8 [rows, K/2] natural int4;
- *                SYM_INT8: int8 [rows, K]
+ *                SYM_INT8: int8 [rows, K] (CR_LAYOUT_F16: fp16 [rows, K])
  *   layout       CR_LAYOUT_NATURAL, or CR_LAYOUT_TILED for SYM_INT4 / UNSIGNED
  *                codes (the input layout of w4a4_gemm's int8-core path), or
  *                CR_LAYOUT_F6 for SYM_INT4 or UNSIGNED codes (the input of
  *                w4a4_gemm's fp6-core path; ceil(rows/32)(K/64) 1536 bytes;
- *                an unsigned code u is stored as the E2M3 value u/2)
+ *                an unsigned code u is stored as the E2M3 value u/2), or
+ *                CR_LAYOUT_F16 for rotated SYM_INT8 codes (the activation
+ *                operand of w4a8_gemm, same integers as fp16 values)
  *   scales       float32 [1] | [rows] | [rows, K/q_group]; ASYM: fp16 [rows, K/16]
  *   zeros        ASYM only: uint8 [rows, K/32], two uint4 zero points per byte
  *                (group 2j low nibble); NULL otherwise
@@ -247,11 +252,10 @@ cr_status convrot_rotate_quantize_dual(const void* x, int64_t rows, int64_t K, i
  *   packed_scales  ROW_GROUP(64): float32 [N/128][K/64][128];
  *                  ASYM: fp16 [N/128][K/64][4][128]; NULL for TENSOR / ROW
  *   packed_zeros   ASYM: uint8 [N/128][K/64][4][128], one zero point per byte; else NULL
- *   w_sum          optional float32 [N]. SYM_INT4: sum_k of the dequantized
- *                  weight row (float32 accumulation), the correction vector of
- *                  the unsigned-shift path. ASYM_UINT4: sum_k fp16(s (q - z)),
- *                  summed exactly and rounded once to float32, the correction
- *                  vector of w4a8_gemm's float outputs (required there).
+ *   w_sum          optional float32 [N], SYM_INT4 only: sum_k of the
+ *                  dequantized weight row (float32 accumulation), the
+ *                  correction vector of the unsigned-shift path; must be NULL
+ *                  for ASYM_UINT4
  * Shape: N % 128 == 0, K % 64 == 0 (K % 256 for ROW_GROUP 64 is not required).
  */
 size_t w4_packed_bytes(int64_t N, int64_t K, cr_qtype qtype, cr_gran gran, int q_group,
@@ -367,27 +371,32 @@ cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
  * w4a8_gemm - per-token INT8 activations x asymmetric uint4 g16 weights.
  *
  * Cites: "Qwen-Image-Edit-2511-W4A8-ConvRot" card, build table and file
- * layout (asym_w4a8_int8, group_size 16, convrot_groupsize 256).
+ * layout (asym_w4a8_int8, group_size 16, convrot_groupsize 256); the same
+ * card's passage on LoRA merge versus bypass (low-rank branch);
+ * "Qwen-Image-Edit-2511 INT4 (ComfyUI Optimized)", Environment Variables
+ * (FP32 low-rank activations).
  *
- *   a_codes    int8 [M, K] (SYM_INT8 from convrot_rotate_quantize)
+ *   a_codes    SYM_INT8 codes from convrot_rotate_quantize: a_layout
+ *              CR_LAYOUT_NATURAL int8 [M, K], or CR_LAYOUT_F16 fp16 [M, K]
+ *              (the same integers; no conversion in the GEMM)
  *   a_scales   float32 ROW [M] (or TENSOR [1])
- *   w_packed, w_scales (fp16), w_zeros (uint8), w_sum (float32 [N]): from
- *              w4_pack_weights (ASYM_UINT4); w_sum is required for CR_OUT_BF16 /
- *              CR_OUT_F32 and ignored (may be NULL) for CR_OUT_I32_RAW
- *   lora_act   optional bf16 [M, R] (R = 32 or 64, e.g. from convrot_rotate_quantize's
- *              lora_down with rotation), with lora_up bf16 [N, R]: the low-rank bypass
- *              of a LoRA kept beside the quantized weight ("Qwen-Image-Edit-2511-W4A8-
- *              ConvRot" card, passage on LoRA merge versus bypass): y += la @ lora_up^T
- *   y[m, n] = s_a[m] * sum_g s_w[n, g] * sum_{k in g} qa[m,k] (qw[n,k] - z[n,g]) (+ low rank) + bias[n]
- *   CR_OUT_I32_RAW gives sum_k qa (qw - z) exactly (int8 matrix cores).
- *   CR_OUT_BF16 / CR_OUT_F32 run on fp16 matrix cores with each weight
- *   s (q - z) rounded once to fp16 (relative 2^-11) and float32 accumulation.
+ *   w_packed, w_scales (fp16), w_zeros (uint8): from w4_pack_weights (ASYM_UINT4)
+ *   lora_act   optional [M, R], bf16 (lora_act_f32 = 0) or float32 (1), R = 32
+ *              or 64 (e.g. from convrot_rotate_quantize's lora_down with
+ *              rotation), with lora_up bf16 [N, R]: the low-rank bypass of a
+ *              LoRA kept beside the quantized weight, y += la @ lora_up^T
+ *   Every 16-deep group's partial P[m, n, g] = sum_{k in g} qa[m,k] (qw[n,k] -
+ *   z[n, g]) is formed exactly (fp16 matrix cores on the exact integers).
+ *   CR_OUT_BF16 / CR_OUT_F32: y[m, n] = s_a[m] * acc[m, n] (+ low rank) + bias[n]
+ *              with acc accumulated in float32, one fused multiply-add
+ *              acc += s_w[n, g] * P[m, n, g] per group in increasing k.
+ *   CR_OUT_I32_RAW: sum_g P[m, n, g] exactly (low rank, bias, scales ignored).
  * Shape: M >= 1, N % 128 == 0, K % 128 == 0, K <= 32768, ldc >= N (ldc % 8 == 0). group must be 16.
+ * workspace: unused (pass NULL, 0).
  */
-cr_status w4a8_gemm(const void* a_codes, const float* a_scales, cr_gran a_gran,
-                    const void* w_packed, const void* w_scales, const void* w_zeros,
-                    const float* w_sum, int group,
-                    const void* lora_act, const void* lora_up, int R,
+cr_status w4a8_gemm(const void* a_codes, cr_layout a_layout, const float* a_scales, cr_gran a_gran,
+                    const void* w_packed, const void* w_scales, const void* w_zeros, int group,
+                    const void* lora_act, int lora_act_f32, const void* lora_up, int R,
                     const void* bias, void* out, cr_out out_type, int64_t ldc,
                     int64_t M, int64_t N, int64_t K,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);

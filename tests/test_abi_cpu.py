@@ -102,7 +102,11 @@ def test_rq_validation(cr):
     assert _rq(cr, wsb=0) == 6                               # TENSOR needs workspace
     assert _rq(cr, q=1, layout=1) == 3                       # tiled layout is for int4 codes
     assert _rq(cr, layout=2) == 1
-    assert _rq(cr, layout=4) == 1
+    assert _rq(cr, layout=5) == 1
+    assert _rq(cr, layout=4) == 3                            # fp16-carried codes are int8 codes
+    assert _rq(cr, layout=4, q=1) == 4
+    assert _rq(cr, layout=4, q=1, g=1, ws=None, wsb=0) == 4
+    assert _rq(cr, layout=4, q=1, rot=0, g=2, qg=64, ws=None, wsb=0) == 3   # rotated codes only
     assert _rq(cr, layout=3) == 4                            # fp6 fragments of rotated int4 codes
     assert _rq(cr, layout=3, g=1) == 4
     assert _rq(cr, layout=3, q=1) == 3                       # not for int8 codes
@@ -176,8 +180,9 @@ def test_pack_validation(cr):
     assert L.w4_pack_weights(_p(A), _p(A), None, 128, 512, 3, 2, 16, _p(A), _p(A), _p(A), None, None) == 1
     assert L.w4_pack_weights(_p(A), _p(A), None, 128, 512, 1, 0, 0, _p(A), None, None, None, None) == 3
     assert L.w4_pack_weights(_p(A), _p(A), None, 128, 512, 0, 0, 0, _p(A), None, None, None, None) == 4
-    # ASYM_UINT4 g16 with its column sums
-    assert L.w4_pack_weights(_p(A), _p(A), _p(A), 128, 512, 3, 2, 16, _p(A), _p(A), _p(A), _p(A), None) == 4
+    # ASYM_UINT4 g16: no column sums (the W4A8 GEMM takes none)
+    assert L.w4_pack_weights(_p(A), _p(A), _p(A), 128, 512, 3, 2, 16, _p(A), _p(A), _p(A), _p(A), None) == 1
+    assert L.w4_pack_weights(_p(A), _p(A), _p(A), 128, 512, 3, 2, 16, _p(A), _p(A), _p(A), None, None) == 4
     assert cr.w4_packed_bytes(256, 512, 0, 0, 0, 0) == 256 * 256
     assert cr.w4_packed_f6_bytes(256, 512) == 256 * 512 * 3 // 4
     assert cr.w4_packed_f6_bytes(96, 512) == 0
@@ -208,7 +213,7 @@ def test_gemm_validation(cr):
     assert _w4a4(cr, la=A, lu=A, R=16) == 3
     assert _w4a4(cr, la=A, lu=A, R=64) == 4
     assert _w4a4(cr, ot=5) == 1
-    assert _w4a4(cr, layout=4) == 1
+    assert _w4a4(cr, layout=5) == 1
     assert _w4a4(cr, layout=3) == 4                          # fp6 fragments, tensor scales
     assert _w4a4(cr, layout=3, ag=1, wg=1) == 4
     assert _w4a4(cr, layout=3, ag=2, wg=2) == 4              # fp6 with 64-group scales
@@ -225,18 +230,19 @@ def test_gemm_validation(cr):
     assert _w4a4(cr, M=1 << 20, K=32768, ldc=256) == 2        # M*K/2 beyond 32-bit offsets
     assert _w4a4(cr) == 4
     L = cr.lib
-    def w4a8(ag=1, wsum=A, group=16, la=None, lu=None, R=0, ot=0):
-        return L.w4a8_gemm(_p(A), _p(A), ag, _p(A), _p(A), _p(A), _p(wsum), group, _p(la), _p(lu), R, None, _p(A),
-                           ot, 256, 64, 256, 512, None, 0, None)
+    def w4a8(ag=1, group=16, la=None, lu=None, R=0, ot=0, layout=0, la_f32=0):
+        return L.w4a8_gemm(_p(A), layout, _p(A), ag, _p(A), _p(A), _p(A), group, _p(la), la_f32, _p(lu), R, None,
+                           _p(A), ot, 256, 64, 256, 512, None, 0, None)
     assert w4a8(group=32) == 3
     assert w4a8(ag=2) == 3
-    # the float outputs need the column-sum vector, the exact int32 output does not
-    assert w4a8(wsum=None) == 1
-    assert w4a8(wsum=None, ot=2) == 4
-    # low-rank bypass: rank 32 or 64, both factors
+    assert w4a8(layout=1) == 1                               # int8 natural or fp16-carried codes only
+    assert w4a8(layout=4) == 4
+    assert w4a8(ot=2) == 4
+    # low-rank bypass: rank 32 or 64, both factors; bf16 or float32 activations
     assert w4a8(la=A, lu=A, R=16) == 3
     assert w4a8(la=A, R=32) == 3
     assert w4a8(la=A, lu=A, R=64) == 4
+    assert w4a8(la=A, lu=A, R=32, la_f32=1) == 4
     assert w4a8() == 4
     assert L.int8_tensorwise_gemm(_p(A), None, _p(A), _p(A), None, _p(A), 0, 256, 64, 256, 512,
                                   None, 0, None) == 1

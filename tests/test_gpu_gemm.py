@@ -33,14 +33,6 @@ def _check_out(y_bf16, y_f32, ref_y, f32_tol=1e-5):
     assert rel_l2(host(y_f32), ref_y) <= f32_tol, rel_l2(host(y_f32), ref_y)
 
 
-# The W4A8 float outputs come from weights dequantized to fp16(s * (q - z)) on
-# the fp16 matrix cores: one rounding per weight, |delta| <= 2^-11, which for
-# uncorrelated errors gives a relative L2 of about 2^-11 / sqrt(3) = 2.8e-4 on
-# the float32 output. The bar for it is 1e-3; the bf16 bar stays 2e-3 and the
-# exact int32 output (int8 matrix cores) stays bit-exact.
-W4A8_F32_TOL = 1e-3
-
-
 W4A4_CASES = [
     # M, N, K, a_gran, w_gran
     (1, 256, 512, "tensor", "tensor"),
@@ -222,11 +214,19 @@ def test_int8_tensorwise(cr, case):
     _check_out(yb, yf, ref["y"])
 
 
-W4A8_CASES = [(1, 128, 512), (50, 256, 1024), (128, 256, 3072), (333, 384, 768)]
+# M, N, K: one block, ragged M over several 256-row blocks, K past one 8192-deep int32 chunk
+W4A8_CASES = [(1, 128, 512), (50, 256, 1024), (128, 256, 3072), (333, 384, 768), (520, 256, 12288)]
+
+
+def _w4a8_args(cr, wp):
+    return dev(wp["tiles"].reshape(-1)), dev(wp["scales_tiles"].reshape(-1)), dev(wp["zeros_tiles"].reshape(-1))
 
 
 @pytest.mark.parametrize("case", W4A8_CASES)
 def test_w4a8(cr, case):
+    """int32 bit-exact and float outputs to the float32 / bf16 bars, from int8
+    and from fp16-carried activation codes (bit-identical outputs: the
+    conversion is exact)."""
     M, N, K = case
     say(f"w4a8 {case}")
     xb = wl.activation(25, M + K, M, K)
@@ -235,46 +235,78 @@ def test_w4a8(cr, case):
     wp = ol.prepare_w4a8(wb)
     ref = ol.w4a8_linear(xb, wb, wprep=wp)
     ref_b = ol.w4a8_linear(xb, wb, bias_bits=bias, wprep=wp)
-    a = dev(ref["x"]["codes"])
     sa = dev(ref["x"]["scales"])
-    w = dev(wp["tiles"].reshape(-1))
-    sw = dev(wp["scales_tiles"].reshape(-1))
-    zw = dev(wp["zeros_tiles"].reshape(-1))
-    ws = dev(wp["wsum16"])
-    raw = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, out_type=2)
-    assert np.array_equal(host(raw).astype(np.int64), ref["raw"])
-    yb = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, out_type=0, w_sum=ws)
-    yf = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, out_type=1, w_sum=ws)
-    _check_out(yb, yf, ref["y"], f32_tol=W4A8_F32_TOL)
-    ybias = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, bias=bf16_dev(bias), out_type=1, w_sum=ws)
-    assert rel_l2(host(ybias), ref_b["y"]) <= W4A8_F32_TOL
+    w, sw, zw = _w4a8_args(cr, wp)
+    for a in (dev(ref["x"]["codes"]), dev(ref["x"]["codes"].astype(np.float16))):
+        raw = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, out_type=2)
+        assert np.array_equal(host(raw).astype(np.int64), ref["raw"])
+        yb = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, out_type=0)
+        yf = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, out_type=1)
+        _check_out(yb, yf, ref["y"])
+        ybias = cr.w4a8_gemm(a, sa, 1, w, sw, zw, M, N, K, bias=bf16_dev(bias), out_type=1)
+        assert rel_l2(host(ybias), ref_b["y"]) <= 1e-5
+        if a.dtype == torch.int8:
+            y8 = (host(yb), host(yf))
+        else:
+            assert np.array_equal(host(yb), y8[0]) and np.array_equal(host(yf).view(np.uint32), y8[1].view(np.uint32))
 
 
-@pytest.mark.parametrize("R", [32, 64])
-def test_w4a8_lora_bypass(cr, R):
-    """A LoRA kept as a bf16 low-rank branch beside the W4A8 weight: la from
-    the rotate+quantize call on the unrotated input, the up-projection fused
-    into the GEMM epilogue; the output against the oracle's linear with the
-    same branch (bf16 la)."""
+@pytest.mark.parametrize("K", [256, 1024])
+def test_w4a8_float_partials_exact(cr, K):
+    """The float-output kernel forms each 16-group partial exactly: with unit
+    scales its float32 output is the integer sum itself, and with power-of-two
+    scales (token and channel-group) it is the exact dyadic value of
+    s_a sum_g s_w P, bit for bit (both fit float32 at these sizes)."""
+    M, N = 300, 256
+    say(f"w4a8 exact partials K={K}")
+    xb = wl.activation(31, K, M, K)
+    wb = wl.weight(31, K + 1, N, K)
+    wp = ol.prepare_w4a8(wb)
+    xa = ol.rotate_quantize(xb, 256, "int8", "row")
+    w, _, zw = _w4a8_args(cr, wp)
+    P = og.group_partials(xa["values"], wp["values"], 16, wp["zeros"])
+    ones16 = np.ones_like(wp["scales"], dtype=np.float16)
+    y = cr.w4a8_gemm(dev(xa["codes"]), dev(np.ones(M, np.float32)), 1, w, dev(opack.tile_pack_g16(ones16).reshape(-1)),
+                     zw, M, N, K, out_type=1)
+    assert np.array_equal(host(y).astype(np.int64), P.sum(axis=2))
+    rng = np.random.default_rng(K)
+    ea, ew = rng.integers(-3, 1, M), rng.integers(-3, 1, (N, K // 16))
+    sa2 = np.ldexp(1.0, ea).astype(np.float32)
+    sw2 = np.ldexp(1.0, ew).astype(np.float16)
+    y2 = cr.w4a8_gemm(dev(xa["codes"]), dev(sa2), 1, w, dev(opack.tile_pack_g16(sw2).reshape(-1)), zw, M, N, K,
+                      out_type=1)
+    exact = np.ldexp(1.0, ea)[:, None] * np.einsum("ng,mng->mn", np.ldexp(1.0, ew), P.astype(np.float64))
+    assert np.max(np.abs(exact)) < 2.0 ** 21
+    assert np.array_equal(host(y2).astype(np.float64), exact)
+    assert np.array_equal(host(y2), ol.epilogue_g16(P, sa2, "row", sw2))
+
+
+@pytest.mark.parametrize("R,la_f32", [(32, False), (64, False), (32, True)])
+def test_w4a8_lora_bypass(cr, R, la_f32):
+    """A LoRA kept as a low-rank branch beside the W4A8 weight: la from the
+    rotate+quantize call on the unrotated input (bf16, or float32 with the
+    FP32 switch), the up-projection fused into the GEMM epilogue; the output
+    against the oracle's linear with the same branch."""
     M, N, K = 333, 256, 3072
-    say(f"w4a8 lora R={R}")
+    say(f"w4a8 lora R={R} f32={la_f32}")
     xb = wl.activation(29, R, M, K)
     wb = wl.weight(29, R + 1, N, K)
     l1 = wl.weight(29, R + 2, N, R, std=0.05)
     l2 = wl.weight(29, R + 3, R, K, std=0.05)
     bias = wl.weight(29, R + 4, 1, N, std=0.5)[0]
     wp = ol.prepare_w4a8(wb)
-    ref = ol.w4a8_linear(xb, wb, wprep=wp, l1_bits=l1, l2_bits=l2, bias_bits=bias)
-    a, sa, _, la = cr.convrot_rotate_quantize(bf16_dev(xb), 256, cr.Q.SYM_INT8, cr.GRAN.ROW, lora_down=bf16_dev(l2))
-    assert np.array_equal(host(a).view(np.uint8), ref["x"]["codes"].view(np.uint8))
-    args = (a, sa, 1, dev(wp["tiles"].reshape(-1)), dev(wp["scales_tiles"].reshape(-1)),
-            dev(wp["zeros_tiles"].reshape(-1)), M, N, K)
-    kw = dict(w_sum=dev(wp["wsum16"]), lora_act=la, lora_up=bf16_dev(l1), bias=bf16_dev(bias))
-    yf = cr.w4a8_gemm(*args, out_type=1, **kw)
-    yb = cr.w4a8_gemm(*args, out_type=0, **kw)
-    _check_out(yb, yf, ref["y"], f32_tol=W4A8_F32_TOL)
-    plain = cr.w4a8_gemm(*args, out_type=1, w_sum=kw["w_sum"], bias=kw["bias"])
-    assert rel_l2(host(yf) - host(plain), ref["y"] - ol.w4a8_linear(xb, wb, wprep=wp, bias_bits=bias)["y"]) <= 1e-2
+    ref = ol.w4a8_linear(xb, wb, wprep=wp, l1_bits=l1, l2_bits=l2, bias_bits=bias, act_f32=la_f32)
+    a, sa, _, la = cr.convrot_rotate_quantize(bf16_dev(xb), 256, cr.Q.SYM_INT8, cr.GRAN.ROW, lora_down=bf16_dev(l2),
+                                              lora_act_f32=la_f32, layout=cr.LAYOUT.F16)
+    assert np.array_equal(host(a).astype(np.int64), ref["x"]["values"].astype(np.int64))
+    args = (a, sa, 1, *_w4a8_args(cr, wp), M, N, K)
+    # the epilogue on the oracle's la (identical inputs): float32 bar
+    la_ref = dev(ref["la"]) if la_f32 else bf16_dev(wl.bf16_bits_from_f32(ref["la"]))
+    kw = dict(lora_act=la_ref, lora_up=bf16_dev(l1), bias=bf16_dev(bias))
+    _check_out(cr.w4a8_gemm(*args, out_type=0, **kw), cr.w4a8_gemm(*args, out_type=1, **kw), ref["y"])
+    # end to end with the GPU's la (its rounding may differ by one ulp): bf16 bar
+    ye = cr.w4a8_gemm(*args, out_type=0, lora_act=la, lora_up=bf16_dev(l1), bias=bf16_dev(bias))
+    assert rel_l2(bf16_to_f32(host(ye)), ref["y"]) <= 2e-3
 
 
 @pytest.mark.parametrize("R", [32, 64])
@@ -300,25 +332,6 @@ def test_w4a4_lora_rank(cr, R):
     # end to end with the GPU's la (its bf16 rounding may differ by one ulp): bf16 bar
     ye = cr.w4a4_gemm(a, sa, 0, w, sw, 0, M, N, K, lora_act=la, lora_up=bf16_dev(l1), out_type=0)
     assert rel_l2(bf16_to_f32(host(ye)), ref["y"]) <= 2e-3
-
-
-def test_w4a8_float_outputs_match_fp16_weights(cr):
-    """The float outputs equal, to float32 accumulation rounding, the product
-    with each weight taken as fp16(s (q - z)): a reference built from the
-    oracle's codes with that one rounding, evaluated in float64."""
-    M, N, K = 200, 256, 1024
-    say("w4a8 fp16-weight reference")
-    xb = wl.activation(26, 7, M, K)
-    wb = wl.weight(26, 8, N, K)
-    wp = ol.prepare_w4a8(wb)
-    xa = ol.rotate_quantize(xb, 256, "int8", "row")
-    w16 = oq.dequant_asym(wp["values"], wp["scales"], wp["zeros"], 16).astype(np.float16).astype(np.float64)
-    ref = (np.asarray(xa["values"], np.float64) @ w16.T) * np.asarray(xa["scales"], np.float64)[:, None]
-    y = cr.w4a8_gemm(dev(xa["codes"]), dev(xa["scales"]), 1, dev(wp["tiles"].reshape(-1)),
-                     dev(wp["scales_tiles"].reshape(-1)), dev(wp["zeros_tiles"].reshape(-1)), M, N, K,
-                     out_type=1, w_sum=dev(wp["wsum16"]))
-    # float32 accumulation of (1152 + a) w: partial sums about 40x the result
-    assert rel_l2(host(y), ref) <= 1e-4
 
 
 def test_extreme_codes_no_overflow(cr):

@@ -15,6 +15,7 @@ import json
 import os
 
 import numpy as np
+from fractions import Fraction
 
 from oracle import linear, gemm, quant, pack
 import workloads as wl
@@ -124,77 +125,68 @@ def test_lora_down_rounding():
 
 
 # ---------------------------------------------------------------------------
-# weight_sum_w4a8: sum_k fp16(s (q - z)), exact, rounded once to float32
+# epilogue_g16 (W4A8): y = s_a[m] * sum_g s_w[n, g] * P[m, n, g]
 # ---------------------------------------------------------------------------
 
-def _w4a8_rows(groups):
-    """groups: per row, a list of (scale, [16 codes], zero) -> codes, scales16, zeros."""
-    codes = np.array([[c for _, cs, _ in row for c in cs] for row in groups], dtype=np.uint8)
-    scales = np.array([[s for s, _, _ in row] for row in groups], dtype=np.float16)
-    zeros = np.array([[z for _, _, z in row] for row in groups], dtype=np.uint8)
-    return codes, scales, zeros
+def _g16_case(seed, M=5, N=6, G=7):
+    rng = np.random.default_rng(seed)
+    P = rng.integers(-30480, 30481, (M, N, G)).astype(np.int64)
+    sa = (rng.random(M) * 0.01 + 1e-4).astype(np.float32)
+    return rng, P, sa
 
 
-def test_w4a8_wsum_power_of_two_scales_closed_form():
-    # with s a power of two, s (q - z) is exact in fp16 and the sum is s * sum(q - z)
-    rng = np.random.default_rng(5)
-    rows = []
-    for _ in range(3):
-        row = []
-        for _ in range(8):
-            row.append((2.0 ** -7, list(rng.integers(0, 16, 16)), int(rng.integers(0, 16))))
-        rows.append(row)
-    codes, scales, zeros = _w4a8_rows(rows)
-    got = linear.weight_sum_w4a8(codes, scales, zeros)
-    for r, row in enumerate(rows):
-        ints = sum(int(c) - z for _, cs, z in row for c in cs)
-        assert got[r] == np.float32(ints / 128.0)
+def test_epilogue_g16_equal_group_scales_reduce_to_the_scalar_epilogue():
+    # s_w[n, g] = c[n] for every g: the per-group sum collapses to c[n] * sum_g P
+    rng, P, sa = _g16_case(11)
+    c = (rng.random(P.shape[1]) * 0.02 + 1e-3).astype(np.float16)
+    w = np.repeat(c[:, None], P.shape[2], axis=1)
+    got = linear.epilogue_g16(P, sa, "row", w)
+    want = linear.epilogue_scalar(P.sum(axis=2), sa, "row", c.astype(np.float32), "row")
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
-def test_w4a8_wsum_fp16_tie_rounds_to_even():
-    # s = 1 + 2^-10 (exact in fp16), q - z = 3: 3 + 3 * 2^-10 lies halfway
-    # between the fp16 neighbours 3 + 2^-9 (odd) and 3 + 2^-8 (even)
-    s = 1.0 + 2.0 ** -10
-    codes, scales, zeros = _w4a8_rows([[(s, [3] * 16, 0)], [(s, [1] * 16, 0)]])
-    got = linear.weight_sum_w4a8(codes, scales, zeros)
-    assert got[0] == np.float32(16 * (3.0 + 2.0 ** -8))
-    assert got[1] == np.float32(16 * s)                 # q - z = 1: no rounding
+def test_epilogue_g16_power_of_two_scales_are_exact():
+    # distinct powers of two per (channel, group) and per token: every output
+    # is an exact dyadic value, so a scale taken from the wrong group or
+    # channel, or a dropped group, changes it
+    rng, P, sa_unused = _g16_case(12)
+    M, N, G = P.shape
+    ea = rng.integers(-9, -3, M)
+    ew = rng.integers(-12, -4, (N, G))
+    sa = np.ldexp(1.0, ea).astype(np.float32)
+    sw = np.ldexp(1.0, ew).astype(np.float16)
+    got = linear.epilogue_g16(P, sa, "row", sw)
+    for m in range(M):
+        for n in range(N):
+            tot = Fraction(0)
+            for g in range(G):
+                tot += Fraction(2) ** int(ew[n, g]) * int(P[m, n, g])
+            tot *= Fraction(2) ** int(ea[m])
+            assert got[m, n] == np.float32(float(tot))
 
 
-def test_w4a8_wsum_is_exact_before_the_float32_rounding():
-    # one group of 16 x 61440 then 240 terms of 2^-10: a float32 running sum
-    # loses every small term (ulp 2^-4 at 983040); the exact sum
-    # 983040.234375 rounds to 983040.25
-    big = [(4096.0, [15] * 16, 0)]
-    small = [(2.0 ** -10, [1] * 16, 0)] * 15
-    codes, scales, zeros = _w4a8_rows([big + small])
-    assert linear.weight_sum_w4a8(codes, scales, zeros)[0] == np.float32(983040.25)
-
-
-def test_w4a8_wsum_float32_tie_rounds_to_even():
-    # 18 groups of 16 x 61440 = 17694720 (ulp 2 above 2^24), plus 1 or 3:
-    # 17694721 -> 17694720 (even), 17694723 -> 17694724 (even)
-    big = [(4096.0, [15] * 16, 0)] * 18
-    codes, scales, zeros = _w4a8_rows([big + [(1.0, [1] + [0] * 15, 0)],
-                                       big + [(1.0, [3] + [0] * 15, 0)]])
-    got = linear.weight_sum_w4a8(codes, scales, zeros)
-    assert got[0] == np.float32(17694720.0)
-    assert got[1] == np.float32(17694724.0)
-
-
-def test_w4a8_wsum_brute_force_fractions():
-    from fractions import Fraction
-    rng = np.random.default_rng(9)
-    codes = rng.integers(0, 16, (3, 64)).astype(np.uint8)
-    scales = (rng.random((3, 4)) * 0.02 + 1e-3).astype(np.float16)
-    zeros = rng.integers(0, 16, (3, 4)).astype(np.uint8)
-    got = linear.weight_sum_w4a8(codes, scales, zeros)
-    for r in range(3):
-        tot = Fraction(0)
-        for k in range(64):
-            prod = float(scales[r, k // 16]) * (int(codes[r, k]) - int(zeros[r, k // 16]))
-            tot += Fraction(float(np.float16(prod)))
-        assert got[r] == np.float32(float(tot))
+def test_epilogue_g16_brute_force_against_codes():
+    # y from the integer codes by plain loops (exact rationals), against the
+    # oracle's W4A8 linear on a tiny layer: the zero point, the group of each
+    # scale and the token scale all enter
+    M, N, K = 3, 128, 256
+    x = wl.activation(93, 0, M, K)
+    w = wl.weight(93, 1, N, K)
+    out = linear.w4a8_linear(x, w)
+    qa = out["x"]["values"].astype(np.int64)
+    sa = out["x"]["scales"]
+    qw = out["w"]["values"].astype(np.int64)
+    sw = out["w"]["scales"]
+    z = out["w"]["zeros"].astype(np.int64)
+    for m in range(M):
+        for n in range(0, N, 17):
+            tot = Fraction(0)
+            for g in range(K // 16):
+                part = sum(int(qa[m, k]) * (int(qw[n, k]) - int(z[n, g])) for k in range(16 * g, 16 * g + 16))
+                tot += Fraction(float(sw[n, g])) * part
+            tot *= Fraction(float(sa[m]))
+            want = float(tot)
+            assert abs(float(out["y"][m, n]) - want) <= abs(want) * 2.0 ** -23 + 1e-30
 
 
 def test_a8w4_linear_brute_force():

@@ -57,6 +57,7 @@ class LAYOUT:
     TILED = 1
     INT8 = 2
     F6 = 3
+    F16 = 4
 
 
 class _Counters(ctypes.Structure):
@@ -81,7 +82,7 @@ _SIGS = {
     "w4_pack_weights_f6": (_i, [_vp, _i64, _i64, _vp, _vp]),
     "w4a4_gemm": (_i, [_vp, _i, _vp, _i, _i, _f, _vp, _vp, _i, _vp, _vp, _i, _vp, _i, _vp,
                        _vp, _i, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
-    "w4a8_gemm": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _i, _vp, _vp, _i, _vp, _vp, _i, _i64, _i64, _i64, _i64,
+    "w4a8_gemm": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp, _i, _vp, _i, _vp, _i, _vp, _vp, _i, _i64, _i64, _i64, _i64,
                        _vp, _sz, _vp]),
     "int8_tensorwise_gemm": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i64, _i64, _i64, _i64,
                                   _vp, _sz, _vp]),
@@ -164,7 +165,7 @@ def convrot_rotate_quantize(x, rot_group=256, qtype=Q.SYM_INT4, gran=GRAN.TENSOR
     dev = x.device
     if codes is None:
         if qtype == Q.SYM_INT8:
-            codes = torch.empty((rows, K), dtype=torch.int8, device=dev)
+            codes = torch.empty((rows, K), dtype=torch.float16 if layout == LAYOUT.F16 else torch.int8, device=dev)
         elif layout == LAYOUT.TILED:
             codes = torch.empty(((rows + 15) // 16, K // 64, 512), dtype=torch.uint8, device=dev)
         elif layout == LAYOUT.F6:
@@ -298,14 +299,18 @@ def w4a4_gemm(a_codes, a_scales, a_gran, w_packed, w_scales, w_gran, M, N, K,
 
 
 def w4a8_gemm(a_codes, a_scales, a_gran, w_packed, w_scales, w_zeros, M, N, K, group=16,
-              bias=None, out_type=OUT.BF16, out=None, stream=None, w_sum=None, lora_act=None, lora_up=None):
-    """w_sum (float32 [N], from w4_pack_weights(..., want_wsum=True)) is
-    required for the bf16 / float32 outputs. lora_act bf16 [M, R] with
-    lora_up bf16 [N, R] (R = 32 or 64) adds the low-rank bypass."""
+              bias=None, out_type=OUT.BF16, out=None, stream=None, lora_act=None, lora_up=None, a_layout=None):
+    """a_codes: int8 [M, K] (NATURAL) or float16 [M, K] (F16, the quantizer's
+    fp16-carried codes); a_layout defaults from the dtype. lora_act [M, R]
+    (bf16 or float32) with lora_up bf16 [N, R] (R = 32 or 64) adds the
+    low-rank bypass."""
+    if a_layout is None:
+        a_layout = LAYOUT.F16 if a_codes.dtype == torch.float16 else LAYOUT.NATURAL
     out = _out(M, N, out_type, a_codes.device, out)
     R = 0 if lora_up is None else lora_up.shape[1]
-    st = lib.w4a8_gemm(_ptr(a_codes), _ptr(a_scales), a_gran, _ptr(w_packed), _ptr(w_scales),
-                       _ptr(w_zeros), _ptr(w_sum), group, _ptr(lora_act), _ptr(lora_up), R, _ptr(bias),
+    lora_f32 = int(lora_act is not None and lora_act.dtype == torch.float32)
+    st = lib.w4a8_gemm(_ptr(a_codes), int(a_layout), _ptr(a_scales), a_gran, _ptr(w_packed), _ptr(w_scales),
+                       _ptr(w_zeros), group, _ptr(lora_act), lora_f32, _ptr(lora_up), R, _ptr(bias),
                        _ptr(out), out_type, out.stride(0),
                        M, N, K, None, 0, _stream(stream))
     _check(st, "w4a8_gemm")

@@ -155,10 +155,15 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
   cr_status st = rq_validate(x, rows, K, ldx, rot_group, qtype, gran, q_group, lora_down, R, lora_act,
                              codes, scales, zeros);
   if (st != CR_OK) return st;
-  if (!((int)layout == CR_LAYOUT_NATURAL || (int)layout == CR_LAYOUT_TILED || (int)layout == CR_LAYOUT_F6))
+  if (!((int)layout == CR_LAYOUT_NATURAL || (int)layout == CR_LAYOUT_TILED || (int)layout == CR_LAYOUT_F6 ||
+        (int)layout == CR_LAYOUT_F16))
     return CR_ERR_INVALID_ARGUMENT;
   if (layout == CR_LAYOUT_TILED && !(qtype == CR_Q_SYM_INT4 || qtype == CR_Q_UNSIGNED_INT4_SHIFT))
     return CR_ERR_UNSUPPORTED_FORMAT;
+  if (layout == CR_LAYOUT_F16) {   // rotated SYM_INT8 codes as fp16 values (the W4A8 activation operand)
+    if (qtype != CR_Q_SYM_INT8 || rot_group == 0) return CR_ERR_UNSUPPORTED_FORMAT;
+    if (rows * K * 2 >= ((int64_t)1 << 40)) return CR_ERR_UNSUPPORTED_SHAPE;
+  }
   if (layout == CR_LAYOUT_F6) {   // signed INT4 codes, or unsigned shifted ones (unrotated); rows pad to 32
     if (!(qtype == CR_Q_SYM_INT4 || qtype == CR_Q_UNSIGNED_INT4_SHIFT)) return CR_ERR_UNSUPPORTED_FORMAT;
     if (((rows + 31) / 32) * (K / 64) * 1536 >= ((int64_t)1 << 32)) return CR_ERR_UNSUPPORTED_SHAPE;
@@ -195,7 +200,7 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
   p.scales = scales;
   p.zeros = zeros;
   p.ws = static_cast<float*>(workspace);
-  p.tiled = layout == CR_LAYOUT_TILED ? 1 : (layout == CR_LAYOUT_F6 ? 2 : 0);
+  p.tiled = layout == CR_LAYOUT_TILED ? 1 : (layout == CR_LAYOUT_F6 ? 2 : (layout == CR_LAYOUT_F16 ? 3 : 0));
   const uint64_t nl = ((rot_group != 0 && gran == CR_GRAN_TENSOR && qtype != CR_Q_ASYM_UINT4) ? 2 : 1) +
                       ((rot_group != 0 && lora_down) ? 1 : 0);
   return finish_launch(cr::launch_rotate_quantize(p, stream), E_RQ, nl);
@@ -331,7 +336,7 @@ cr_status w4_pack_weights(const void* codes, const void* scales, const void* zer
     if (gran != CR_GRAN_ROW_GROUP || q_group != 16) return CR_ERR_UNSUPPORTED_FORMAT;
     if (!zeros || !packed_scales || !packed_zeros) return CR_ERR_INVALID_ARGUMENT;
     if (!aligned16(zeros) || !aligned16(packed_scales) || !aligned16(packed_zeros)) return CR_ERR_INVALID_ARGUMENT;
-    if (w_sum && !aligned16(w_sum)) return CR_ERR_INVALID_ARGUMENT;
+    if (w_sum) return CR_ERR_INVALID_ARGUMENT;             // the W4A8 GEMM needs no column sums
   } else {
     return CR_ERR_UNSUPPORTED_FORMAT;
   }
@@ -432,36 +437,38 @@ cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
   return finish_launch(cr::launch_gemm_w4a4(p, stream), E_W4A4, 1);
 }
 
-cr_status w4a8_gemm(const void* a_codes, const float* a_scales, cr_gran a_gran, const void* w_packed,
-                    const void* w_scales, const void* w_zeros, const float* w_sum, int group,
-                    const void* lora_act, const void* lora_up, int R, const void* bias,
+cr_status w4a8_gemm(const void* a_codes, cr_layout a_layout, const float* a_scales, cr_gran a_gran,
+                    const void* w_packed, const void* w_scales, const void* w_zeros, int group,
+                    const void* lora_act, int lora_act_f32, const void* lora_up, int R, const void* bias,
                     void* out, cr_out out_type, int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
   (void)workspace;
   (void)workspace_bytes;
   cr_status st = gemm_common(a_codes, w_packed, out, out_type, ldc, M, N, K, bias);
   if (st != CR_OK) return st;
+  if (!((int)a_layout == CR_LAYOUT_NATURAL || (int)a_layout == CR_LAYOUT_F16)) return CR_ERR_INVALID_ARGUMENT;
   if (!a_scales || !w_scales || !w_zeros) return CR_ERR_INVALID_ARGUMENT;
   if (!aligned16(a_scales) || !aligned16(w_scales) || !aligned16(w_zeros)) return CR_ERR_INVALID_ARGUMENT;
-  if (out_type != CR_OUT_I32_RAW && (!w_sum || !aligned16(w_sum))) return CR_ERR_INVALID_ARGUMENT;
   if (lora_act || lora_up) {
     if (!lora_act || !lora_up || (R != 32 && R != 64)) return CR_ERR_UNSUPPORTED_FORMAT;
     if (!aligned16(lora_act) || !aligned16(lora_up)) return CR_ERR_INVALID_ARGUMENT;
   }
   if (group != 16) return CR_ERR_UNSUPPORTED_FORMAT;
   if (!(a_gran == CR_GRAN_ROW || a_gran == CR_GRAN_TENSOR)) return CR_ERR_UNSUPPORTED_FORMAT;
+  if (M * K * (a_layout == CR_LAYOUT_F16 ? 2 : 1) >= ((int64_t)1 << 40)) return CR_ERR_UNSUPPORTED_SHAPE;
   st = device_check();
   if (st != CR_OK) return st;
   cr::GemmParams p{};
   p.a = static_cast<const uint8_t*>(a_codes);
+  p.a_f16 = a_layout == CR_LAYOUT_F16 ? 1 : 0;
   p.a_scales = a_scales;
   p.a_gran = a_gran;
   p.act = cr::ACT_I8;
   p.w = static_cast<const uint8_t*>(w_packed);
   p.w_scales16 = static_cast<const uint16_t*>(w_scales);
   p.w_zeros = static_cast<const uint8_t*>(w_zeros);
-  p.w_sum = w_sum;
   p.lora_act = lora_act;
+  p.lora_f32 = lora_act_f32 ? 1 : 0;
   p.lora_up = static_cast<const uint16_t*>(lora_up);
   p.R = R;
   p.bias = static_cast<const uint16_t*>(bias);

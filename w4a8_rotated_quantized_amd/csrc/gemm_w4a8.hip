@@ -4,186 +4,52 @@
 // "Qwen-Image-Edit-2511-W4A8-ConvRot" card, build table and file layout
 // (asym_w4a8_int8, group_size 16, convrot_groupsize 256, 8-bit activations).
 //
-// Two kernels:
-//  - the exact int32 output (CR_OUT_I32_RAW): every 16-deep group is one
-//    v_mfma_i32_32x32x16_i8 over the activation codes and the weight nibbles
-//    widened to the signed bytes q - z, accumulated in int32;
-//  - bf16 / float32 outputs: the fp16 matrix-core kernel further below.
+// Exact group partials on the fp16 matrix cores. Every 16-deep group is one
+// v_mfma_f32_32x32x16_f16 whose operands are small integers held exactly in
+// fp16: the activation codes a (|a| <= 127) and the weight codes minus their
+// zero point, q - z (|q - z| <= 15). Each product and each partial sum of a
+// group is an integer of magnitude <= 16 * 127 * 15 = 30480 < 2^24, so the
+// float32 result is the group partial P[m, n, g] = sum_{k in g} a (q - z)
+// exactly, whatever order the matrix core adds in. The outputs follow:
+//   float:  acc[m, n] += s_w[n, g] * P   (one float32 FMA per output and
+//           group, groups in increasing k), y = s_a[m] * acc (+ low rank)
+//           (+ bias);
+//   int32:  acc[m, n] += P as an integer (the exact sum_k a (q - z)).
+// Both come from the same partials, so the exact int32 output checks the
+// products that the float outputs scale.
+//
+// Operand roles: MFMA A = activations (32 tokens x 16 k), B = weights (16 k x
+// 32 channels). Lane l of a 32 x 32 result holds channel l % 32 and, in
+// register r, token 8 (r / 4) + 4 (l / 32) + r % 4: the group scale s_w[n, g]
+// is one value per lane.
+//
+// Activation codes arrive either as int8 [M, K] (each lane turns its 8 bytes
+// into fp16 in registers: a ^ 0x80 is the byte a + 128, 0x64 placed above it
+// is the fp16 value 1024 + (a + 128), and one packed subtraction of 1152 is
+// exact) or as the fp16 values of the same codes ([M, K], CR_LAYOUT_F16,
+// written by the quantizer), which the kernel uses as they are.
+// Weights (tile-packed, 4096-byte tiles of 128 channels x 64 k): a lane's
+// word holds the 8 nibbles of its k-half; 0x64 above a nibble is the fp16
+// value 1024 + q and one packed subtraction of 1024 + z gives q - z exactly.
+//
+// Block 256 x 128 outputs, 4 waves. A stage is one 64-deep k-tile of the
+// block's activation rows (16-byte slots XOR-swizzled per row so that reads
+// of consecutive rows hit distinct LDS banks), its weight tile, fp16 scales
+// and zero points, loaded straight into LDS by 16-byte global_load_lds.
 #include "common.h"
 #include "kernels.h"
 
 namespace cr {
 
-typedef long v1l;
-
-// 8 weight nibbles of one lane (byte i = q[i] | q[4+i] << 4) -> bytes q - z.
-CR_DEV long widen_asym(uint32_t x, uint32_t zz) {
-  uint32_t lo = (((x & 0x0F0F0F0Fu) | 0x80808080u) - zz) ^ 0x80808080u;
-  uint32_t hi = ((((x >> 4) & 0x0F0F0F0Fu) | 0x80808080u) - zz) ^ 0x80808080u;
-  return (long)(((uint64_t)hi << 32) | lo);
-}
-
-__global__ __launch_bounds__(256) void gemm_w4a8_raw_kernel(GemmParams p) {
-  constexpr int BM = 128, BN = 128;
-  constexpr int X_ST = 2 * 4 * (BM / 32) * 512;   // [kt][kg][mb][64 x 8 B]
-  constexpr int W_ST = 2 * 4096;                  // [kt][kg][nb][64 x 4 B]
-  constexpr int Z_ST = 2 * 4 * 128;               // zero points  [kt][kg][128]
-  constexpr int STAGE = X_ST + W_ST + Z_ST;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
-
-  const int tid = threadIdx.x;
-  const int l = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  const int ntm = (int)((p.M + BM - 1) / BM);
-  const int ntn = (int)(p.N / BN);
-  const int ntiles = ntm * ntn;
-  int t = blockIdx.x;
-  if ((ntiles & 7) == 0) t = (t & 7) * (ntiles >> 3) + (t >> 3);
-  constexpr int GM = 8;
-  const int band = t / (GM * ntn);
-  const int rows_in_band = min(GM, ntm - band * GM);
-  const int within = t - band * GM * ntn;
-  const int tn = within / rows_in_band;
-  const int tm = band * GM + within % rows_in_band;
-  const int64_t m0 = (int64_t)tm * BM;
-  const int64_t n0 = (int64_t)tn * BN;
-  const int64_t K = p.K;
-  const int nkb = (int)(K / 128);
-  const int64_t wtile0 = (n0 >> 7) * (K / 64);      // first tile of this channel block
-
-  u32x4 rx[4], rwt[2], rsz;
-  auto gload = [&](int kb) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int pc = tid + j * 256;            // 1024 pieces: row = pc >> 3, group-of-16 = pc & 7
-      int row = pc >> 3, part = pc & 7;
-      int64_t m = imin64(m0 + row, p.M - 1);
-      rx[j] = *reinterpret_cast<const u32x4*>(p.a + m * K + (int64_t)kb * 128 + part * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      rwt[j] = *reinterpret_cast<const u32x4*>(p.w + (wtile0 + kb * 2) * 4096 + (tid + j * 256) * 16);
-    if (tid < 64) rsz = *reinterpret_cast<const u32x4*>(p.w_zeros + (wtile0 + kb * 2) * 512 + tid * 16);
-  };
-  auto lstore = [&](int buf) {
-    uint8_t* Xs = smem + buf * STAGE;
-    uint8_t* Wsm = Xs + X_ST;
-    uint8_t* Zsm = Wsm + W_ST;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int pc = tid + j * 256;
-      int row = pc >> 3, part = pc & 7;
-      int kt = part >> 2, kg = part & 3;
-      uint8_t* base = Xs + ((kt * 4 + kg) * (BM / 32) + (row >> 5)) * 512;
-      *reinterpret_cast<u32x2*>(base + (row & 31) * 8) = u32x2{rx[j][0], rx[j][1]};
-      *reinterpret_cast<u32x2*>(base + ((row & 31) + 32) * 8) = u32x2{rx[j][2], rx[j][3]};
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(Wsm + (tid + j * 256) * 16) = rwt[j];
-    if (tid < 64) *reinterpret_cast<u32x4*>(Zsm + tid * 16) = rsz;
-  };
-
-  v16i acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0;
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nkb) gload(kb + 1);
-    const uint8_t* Xs = smem + buf * STAGE;
-    const uint8_t* Wsm = Xs + X_ST;
-    const uint8_t* Zsm = Wsm + W_ST;
-#pragma unroll 1
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll 1
-      for (int kg = 0; kg < 4; ++kg) {
-        long xa[2], wb[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          xa[i] = *reinterpret_cast<const long*>(Xs + ((kt * 4 + kg) * (BM / 32) + wm * 2 + i) * 512 + l * 8);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int nl = (wn * 2 + j) * 32 + (l & 31);
-          uint32_t z = Zsm[(kt * 4 + kg) * 128 + nl];
-          uint32_t x = *reinterpret_cast<const uint32_t*>(Wsm + kt * 4096 + kg * 1024 + (wn * 2 + j) * 256 + l * 4);
-          wb[j] = widen_asym(x, z * 0x01010101u);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x16_i8(xa[i], wb[j], acc[i][j], 0, 0, 0);
-      }
-    }
-    if (kb + 1 < nkb) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // lane owns channel n = l % 32 of each 32 x 32 block and tokens 8 (r / 4) + 4 (l / 32) + r % 4
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int64_t n = n0 + (wn * 2 + j) * 32 + (l & 31);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + (wm * 2 + i) * 32 + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-        if (m < p.M) reinterpret_cast<int32_t*>(p.out)[m * p.ldc + n] = acc[i][j][r];
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Float-output kernel on fp16 matrix cores (bf16 / float32 outputs).
-//
-// Applying a float group scale after every 16-deep int8 product costs two
-// VALU operations per output and group, far more than the matrix work. This
-// kernel instead dequantizes each weight once per block to fp16(s * (q - z))
-// in registers and lets v_mfma_f32_32x32x16_f16 accumulate over all of K in
-// float32. The only rounding added to the exact sum is that of s * (q - z)
-// to fp16 (relative 2^-11); the exact int32 output keeps the kernel above.
-//
-// Activation codes become fp16 without arithmetic: a ^ 0x80 is the unsigned
-// byte u = a + 128, and 0x64 placed above it is the fp16 value 1024 + u =
-// 1152 + a (v_perm_b32 builds two per instruction). The matrix cores thus
-// compute sum_k (1152 + a_k) w_k, and the epilogue subtracts 1152 * w_sum[n]
-// with w_sum[n] = sum_k fp16(s * (q - z)) (exact, from w4_pack_weights).
-// Weights: 0x64 above a nibble is 1024 + q; one packed fp16 subtraction of
-// 1024 + z is exact and one packed multiplication by s rounds once.
-//
-// Block: 256 x 128 outputs, 4 waves of 128 x 64 (4 x 2 blocks of 32 x 32).
-// Each 64-deep k-tile is one pipeline stage (3 in flight, loaded straight
-// into LDS by 16-byte global_load_lds): activations [row][4 x 16 B] with the
-// 16-byte slots XOR-swizzled per row, weights / scales / zero points in their
-// tile-packed order. A lane reads 16 activation bytes (one 16-deep group) at
-// once and feeds the two 8-deep halves to two MFMAs; in the first, lanes
-// 0-31 carry group 2p and lanes 32-63 group 2p + 1 (k 0..7 of each), in the
-// second k 8..15 of the same groups, and the weight fragments follow the same
-// assignment (the order of a dot product's terms is free). The weights are
-// operand A, so a lane ends with one token and four adjacent channels: one
-// activation scale per lane and 8-byte bf16 stores.
-// ---------------------------------------------------------------------------
 typedef _Float16 v8h_ __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h_ __attribute__((ext_vector_type(2)));
+typedef float v2f_ __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef const void __attribute__((address_space(1)))* gas_ptr_w8;
 typedef void __attribute__((address_space(3)))* las_ptr_w8;
 
-typedef float v2f_ __attribute__((ext_vector_type(2)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-
-CR_DEV uint32_t h2_sub_mul(uint32_t a, uint32_t b, uint32_t c) {
-  return __builtin_bit_cast(uint32_t, (__builtin_bit_cast(v2h_, a) - __builtin_bit_cast(v2h_, b)) *
-                                          __builtin_bit_cast(v2h_, c));
+CR_DEV uint32_t h2_sub(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h_, a) - __builtin_bit_cast(v2h_, b));
 }
 
 template <int N>
@@ -192,27 +58,60 @@ CR_DEV void w8_wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// 16-byte slot of group g in row r of an activation stage (4 groups of 16
-// bytes per row): XOR-swizzled so that 8 or 16 consecutive rows read at one
-// group hit distinct LDS banks.
+// int8 activation stage, rows of 64 bytes (4 slots of 16): slot of group g in row r
 CR_DEV int w8_slot(int r, int g) { return g ^ (((r >> 1) ^ (r >> 3)) & 3); }
 
-template <int OUT>
-__global__ __launch_bounds__(256, 2) void gemm_w4a8_h_kernel(GemmParams p) {
-  constexpr int BM = 256, BN = 128, NS = 3;
-  constexpr int A_ST = BM * 64;                 // [row][4 slots x 16 B]
-  constexpr int W_ST = 4096;                    // [kg][nb][64 x 4 B]
-  constexpr int S_ST = 1024;                    // fp16 scales [kg][128]
-  constexpr int Z_ST = 1024;                    // zero points [kg][128] (+512 B duplicate)
+// at most `ahead` later stages (L loads each) of this wave left in flight
+template <int L>
+CR_DEV void w8_wait_stage(int ahead) {
+  if (ahead >= 2) w8_wait_vm<2 * L>();
+  else if (ahead == 1) w8_wait_vm<L>();
+  else w8_wait_vm<0>();
+}
+
+// 8 int8 codes (two words, k order) -> 8 exact fp16 values
+CR_DEV v8h_ a8_to_h(uint32_t x0, uint32_t x1) {
+  const uint32_t u0 = x0 ^ 0x80808080u, u1 = x1 ^ 0x80808080u;
+  const uint32_t off = 0x64806480u;                     // fp16 pair (1152, 1152)
+  return __builtin_bit_cast(v8h_, u32x4{h2_sub(__builtin_amdgcn_perm(0x64646464u, u0, 0x04010400u), off),
+                                        h2_sub(__builtin_amdgcn_perm(0x64646464u, u0, 0x04030402u), off),
+                                        h2_sub(__builtin_amdgcn_perm(0x64646464u, u1, 0x04010400u), off),
+                                        h2_sub(__builtin_amdgcn_perm(0x64646464u, u1, 0x04030402u), off)});
+}
+
+// one lane's weight word (byte i = q[i] | q[4 + i] << 4) and zero point -> 8 exact fp16 values q - z
+CR_DEV v8h_ w4_to_h(uint32_t x, uint32_t z) {
+  const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+  const uint32_t zz = 0x64006400u | z | (z << 16);      // fp16 pair (1024 + z, 1024 + z)
+  return __builtin_bit_cast(v8h_, u32x4{h2_sub(__builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u), zz),
+                                        h2_sub(__builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u), zz),
+                                        h2_sub(__builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u), zz),
+                                        h2_sub(__builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u), zz)});
+}
+
+// TM x TN 32 x 32 blocks per wave, WN = 4 / WM waves along the channels.
+template <int TM, int TN, bool A16, int OUT>
+__global__ __launch_bounds__(256, 2) void gemm_w4a8_kernel(GemmParams p) {
+  constexpr int BM = 256, BN = 128, NW = 4;
+  constexpr int WN = BN / (32 * TN), WM = NW / WN;
+  static_assert(WM * WN == NW && WM * TM * 32 == BM, "wave tiles cover the block");
+  constexpr int AROW = A16 ? 128 : 64;                  // bytes of one activation row per stage
+  constexpr int A_ST = BM * AROW;
+  constexpr int W_ST = 4096, S_ST = 1024, Z_ST = 1024;  // weights, fp16 scales, zero points (+512 B copy)
   constexpr int STAGE = A_ST + W_ST + S_ST + Z_ST;
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem_w8h[];
-  uint8_t* smem = smem_w8h;
+  constexpr int NS = A16 ? 2 : 3;
+  constexpr int AL = A_ST / 1024 / NW;                  // activation wave-loads per wave and stage
+  constexpr bool RAW = OUT == CR_OUT_I32_RAW;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem_w8[];
+  uint8_t* smem = smem_w8;
 
   const int tid = threadIdx.x;
-  const int l = tid & 63;
+  const int l = tid & 63, lr = l & 31, h = l >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
 
+  // block -> tile: consecutive blocks round robin over the 8 XCDs, then bands
+  // of 4 tile rows walked column by column
   const int ntm = (int)((p.M + BM - 1) / BM);
   const int ntn = (int)(p.N / BN);
   const int ntiles = ntm * ntn;
@@ -228,258 +127,264 @@ __global__ __launch_bounds__(256, 2) void gemm_w4a8_h_kernel(GemmParams p) {
   const int64_t n0 = (int64_t)tn * BN;
   const int64_t K = p.K;
   const int64_t KT = K / 64;
-  const int nst = (int)KT;
-  const int64_t wt0 = (int64_t)tn * KT;          // first packed k-tile of this channel block
+  // k-tiles [k_lo, k_hi) of this launch (the whole K unless the int32 output is split)
+  const int kt0 = p.k_hi > 0 ? p.k_lo : 0;
+  const int nst = (p.k_hi > 0 ? p.k_hi : (int)KT) - kt0;
+  const int64_t wt0 = (int64_t)tn * KT + kt0;          // first packed k-tile of this channel block
 
-  // activation wave-load j of this wave: rows 16 (wave + 4 j) + l / 4, slot l % 4
-  int64_t aoff[4];
+  // activation wave-load j of this wave fills stage bytes [(wave + 4 j) KB, +1 KB):
+  // fp16 rows of 128 B (8 rows, slot = lane % 8 holds k-slot slot ^ (row % 8)),
+  // or int8 rows of 64 B (16 rows, slot = lane % 4 holds group w8_slot(row, slot))
+  // (byte offsets from the block's first row; rows past M read the last row, never stored)
+  uint32_t aoff[AL];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 16 * (wave + 4 * j) + (l >> 2);
-    aoff[j] = imin64(m0 + r, p.M - 1) * K + 16 * w8_slot(r, l & 3);
+  for (int j = 0; j < AL; ++j) {
+    const int idx = wave + NW * j;
+    if constexpr (A16) {
+      const int r = 8 * idx + (l >> 3);
+      aoff[j] = (uint32_t)((imin64(m0 + r, p.M - 1) - m0) * K * 2) + 16 * ((l & 7) ^ (r & 7));
+    } else {
+      const int r = 16 * idx + (l >> 2);
+      aoff[j] = (uint32_t)((imin64(m0 + r, p.M - 1) - m0) * K) + 16 * w8_slot(r, l & 3);
+    }
   }
 
   auto issue = [&](int s) {
     uint8_t* st = smem + (s % NS) * STAGE;
-    const uint8_t* ga = p.a + (int64_t)s * 64;
+    const uint8_t* ga = p.a + m0 * K * (A16 ? 2 : 1) + (int64_t)(kt0 + s) * AROW;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_global_load_lds((gas_ptr_w8)(ga + aoff[j]), (las_ptr_w8)(st + (wave + 4 * j) * 1024), 16, 0, 0);
+    for (int j = 0; j < AL; ++j)
+      __builtin_amdgcn_global_load_lds((gas_ptr_w8)(ga + aoff[j]), (las_ptr_w8)(st + (wave + NW * j) * 1024), 16, 0, 0);
     const int64_t tile = wt0 + s;
     __builtin_amdgcn_global_load_lds((gas_ptr_w8)(p.w + tile * 4096 + wave * 1024 + l * 16),
                                      (las_ptr_w8)(st + A_ST + wave * 1024), 16, 0, 0);
-    if (wave == 0)
-      __builtin_amdgcn_global_load_lds(
-          (gas_ptr_w8)(reinterpret_cast<const uint8_t*>(p.w_scales16) + tile * 1024 + l * 16),
-          (las_ptr_w8)(st + A_ST + W_ST), 16, 0, 0);
-    else if (wave == 1)
+    if constexpr (!RAW) {
+      if (wave == 0)
+        __builtin_amdgcn_global_load_lds(
+            (gas_ptr_w8)(reinterpret_cast<const uint8_t*>(p.w_scales16) + tile * 1024 + l * 16),
+            (las_ptr_w8)(st + A_ST + W_ST), 16, 0, 0);
+    }
+    if (wave == 1)
       __builtin_amdgcn_global_load_lds((gas_ptr_w8)(p.w_zeros + tile * 512 + (l & 31) * 16),
                                        (las_ptr_w8)(st + A_ST + W_ST + S_ST), 16, 0, 0);
   };
+  // loads per stage of this wave: AL + 1, plus the scales (wave 0) or zero points (wave 1)
+  auto wait_stage = [&](int ahead) {
+    if (wave == 1 || (!RAW && wave == 0)) w8_wait_stage<AL + 2>(ahead);
+    else w8_wait_stage<AL + 1>(ahead);
+  };
 
-  v16f acc[4][2];
+  // float outputs: sum_g s_w[n, g] P (one FMA per group); int32 output: the
+  // partials chained through the matrix op's accumulator, exact because at
+  // most 512 groups (|sum| <= 512 * 30480 < 2^24) are summed per launch
+  v16f acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
 
-  // fragment addresses inside a stage
-  const int lr = l & 31, h = l >> 5;
-  const int fl = ((lr >> 1) ^ (lr >> 3)) & 3;
-  int abase[2], wbase[2], sbase[2];
-#pragma unroll
-  for (int pp = 0; pp < 2; ++pp) {
-    const int g = 2 * pp + h;
-    abase[pp] = (wm * 128 + lr) * 64 + 16 * (g ^ fl);
-    wbase[pp] = A_ST + (g * 4 + wn * 2) * 256 + lr * 4;
-    sbase[pp] = g * 128 + wn * 64 + lr;
-  }
+  // lane-constant parts of the fragment addresses (row % 32 = lr in every 32-row block)
+  const int arow0 = (wm * TM * 32 + lr) * AROW;
+  const int asw8 = ((lr >> 1) ^ (lr >> 3)) & 3;
+  const int wcol0 = wn * TN;                            // first 32-channel block of this wave
 
-  issue(0);
-  if (nst > 1) issue(1);
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nst) issue(s);
   for (int s = 0; s < nst; ++s) {
-    if (s + 1 < nst) {
-      if (wave < 2) w8_wait_vm<6>();
-      else w8_wait_vm<5>();
-    } else {
-      w8_wait_vm<0>();
-    }
-    __builtin_amdgcn_s_barrier();
-    if (s + 2 < nst) issue(s + 2);
+    wait_stage(min(NS - 2, nst - 1 - s));             // this wave's loads of stage s have landed
+    __builtin_amdgcn_s_barrier();                      // ... and every wave's; stage s - 1 is consumed
+    if (s + NS - 1 < nst) issue(s + NS - 1);
     const uint8_t* st = smem + (s % NS) * STAGE;
-    const uint16_t* Ssm = reinterpret_cast<const uint16_t*>(st + A_ST + W_ST);
-    const uint8_t* Zsm = st + A_ST + W_ST + S_ST;
+    const uint8_t* Ws = st + A_ST;
+    const uint16_t* Ss = reinterpret_cast<const uint16_t*>(st + A_ST + W_ST);
+    const uint8_t* Zs = st + A_ST + W_ST + S_ST;
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-      u32x4 ar[4];
+    for (int g = 0; g < 4; ++g) {
+      v8h_ wf[TN];
+      float sc[TN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ar[i] = *reinterpret_cast<const u32x4*>(st + abase[pp] + i * 2048);
-      uint32_t wa[2][4], wb[2][4];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint32_t x0 = *reinterpret_cast<const uint32_t*>(st + wbase[pp] + j * 256);
-        const uint32_t x1 = *reinterpret_cast<const uint32_t*>(st + wbase[pp] + j * 256 + 128);
-        const uint32_t z = Zsm[sbase[pp] + j * 32];
-        const uint32_t sv = Ssm[sbase[pp] + j * 32];
-        const uint32_t zz = z * 0x00010001u + 0x64006400u;      // fp16 pair (1024 + z, 1024 + z)
-        const uint32_t ss = sv | (sv << 16);
-        const uint32_t x0l = x0 & 0x0F0F0F0Fu, x0h = (x0 >> 4) & 0x0F0F0F0Fu;
-        const uint32_t x1l = x1 & 0x0F0F0F0Fu, x1h = (x1 >> 4) & 0x0F0F0F0Fu;
-        wa[j][0] = h2_sub_mul(__builtin_amdgcn_perm(0x64646464u, x0l, 0x04010400u), zz, ss);
-        wa[j][1] = h2_sub_mul(__builtin_amdgcn_perm(0x64646464u, x0l, 0x04030402u), zz, ss);
-        wa[j][2] = h2_sub_mul(__builtin_amdgcn_perm(0x64646464u, x0h, 0x04010400u), zz, ss);
-        wa[j][3] = h2_sub_mul(__builtin_amdgcn_perm(0x64646464u, x0h, 0x04030402u), zz, ss);
-        wb[j][0] = h2_sub_mul(__builtin_amdgcn_perm(0x64646464u, x1l, 0x04010400u), zz, ss);
-        wb[j][1] = h2_sub_mul(__builtin_amdgcn_perm(0x64646464u, x1l, 0x04030402u), zz, ss);
-        wb[j][2] = h2_sub_mul(__builtin_amdgcn_perm(0x64646464u, x1h, 0x04010400u), zz, ss);
-        wb[j][3] = h2_sub_mul(__builtin_amdgcn_perm(0x64646464u, x1h, 0x04030402u), zz, ss);
+      for (int j = 0; j < TN; ++j) {
+        const int nb = wcol0 + j;
+        const uint32_t x = *reinterpret_cast<const uint32_t*>(Ws + g * 1024 + nb * 256 + l * 4);
+        wf[j] = w4_to_h(x, Zs[g * 128 + nb * 32 + lr]);
+        if constexpr (!RAW) sc[j] = (float)__builtin_bit_cast(_Float16, Ss[g * 128 + nb * 32 + lr]);
       }
+      v8h_ af[TM];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t u[4];
+      for (int i = 0; i < TM; ++i) {
+        if constexpr (A16) {
+          af[i] = __builtin_bit_cast(
+              v8h_, *reinterpret_cast<const u32x4*>(st + arow0 + i * 32 * AROW + 16 * ((2 * g + h) ^ (lr & 7))));
+        } else {
+          const u32x2 x = *reinterpret_cast<const u32x2*>(st + arow0 + i * 32 * AROW + 16 * (g ^ asw8) + 8 * h);
+          af[i] = a8_to_h(x[0], x[1]);
+        }
+      }
+      if constexpr (RAW) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) u[q] = ar[i][q] ^ 0x80808080u;   // a + 128 as unsigned bytes
-        // fp16 1152 + a: 0x64 above byte u is the fp16 value 1024 + u
-        const v8h_ fa = __builtin_bit_cast(v8h_, u32x4{__builtin_amdgcn_perm(0x64646464u, u[0], 0x04010400u),
-                                                       __builtin_amdgcn_perm(0x64646464u, u[0], 0x04030402u),
-                                                       __builtin_amdgcn_perm(0x64646464u, u[1], 0x04010400u),
-                                                       __builtin_amdgcn_perm(0x64646464u, u[1], 0x04030402u)});
-        const v8h_ fb = __builtin_bit_cast(v8h_, u32x4{__builtin_amdgcn_perm(0x64646464u, u[2], 0x04010400u),
-                                                       __builtin_amdgcn_perm(0x64646464u, u[2], 0x04030402u),
-                                                       __builtin_amdgcn_perm(0x64646464u, u[3], 0x04010400u),
-                                                       __builtin_amdgcn_perm(0x64646464u, u[3], 0x04030402u)});
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              __builtin_bit_cast(v8h_, u32x4{wa[j][0], wa[j][1], wa[j][2], wa[j][3]}), fa, acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              __builtin_bit_cast(v8h_, u32x4{wb[j][0], wb[j][1], wb[j][2], wb[j][3]}), fb, acc[i][j], 0, 0, 0);
+          for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], wf[j], acc[i][j], 0, 0, 0);
+      } else {
+        // software pipeline over the TM x TN blocks: the matrix op of block
+        // t + 1 is issued before the vector work on block t's partial, so two
+        // partials are live at a time and the op's latency is hidden
+        constexpr int T = TM * TN;
+        v16f Pc = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[0], wf[0], v16f{}, 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          v16f Pn;
+          if (t + 1 < T) Pn = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[(t + 1) / TN], wf[(t + 1) % TN], v16f{}, 0, 0, 0);
+          const int i = t / TN, j = t % TN;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(Pc[r], sc[j], acc[i][j][r]);
+          __builtin_amdgcn_sched_barrier(0x104);        // only LDS reads and scalar work may cross
+          if (t + 1 < T) Pc = Pn;
         }
       }
     }
   }
 
-  // D = W . A^T per 32 x 32 block: lane owns token m = l % 32 and channels
-  // 8 (r / 4) + 4 (l / 32) + r % 4. The activations entered as 1152 + a, so
-  // 1152 * w_sum[n] comes off first. Phase 1 turns every accumulator into its
-  // output value in place, phase 2 stores them: all epilogue loads (scales,
-  // column sums, bias, low-rank operands) are issued before the first store,
-  // so no load waits on a store. A missing bias reads w_sum's memory and is
-  // zeroed.
-  float sa[4];
+  // ---- epilogue: lane holds channel n of block j and tokens 8 q + 4 h + e of block i ----
+  const int64_t mw = m0 + wm * TM * 32;                 // first token of the wave
+  const int64_t nw0 = n0 + wcol0 * 32;                  // first channel of the wave
+  if constexpr (!RAW) {
+    // y = s_a[m] acc + bias[n], then the low-rank branch onto the finished values
+    const bool tensor = p.a_gran == CR_GRAN_TENSOR;
+    const float sa_t = tensor ? p.a_scales[0] : 0.f;
+    float bj[TN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t m = imin64(m0 + wm * 128 + i * 32 + lr, p.M - 1);
-    sa[i] = p.a_scales[p.a_gran == CR_GRAN_TENSOR ? 0 : m];
-  }
-  v4f cw[2][4];
-  u32x2 bw[2][4];
-  const bool has_bias = p.bias != nullptr;
-  const uint16_t* bsrc = has_bias ? p.bias : reinterpret_cast<const uint16_t*>(p.w_sum);
+    for (int j = 0; j < TN; ++j) bj[j] = p.bias ? bf16_lo(p.bias[nw0 + j * 32 + lr]) : 0.f;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < TM; ++i) {
+      v4f sa[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t n = n0 + (wn * 2 + j) * 32 + 8 * q + 4 * h;
-      cw[j][q] = *reinterpret_cast<const v4f*>(p.w_sum + n);
-      bw[j][q] = *reinterpret_cast<const u32x2*>(bsrc + n);
-    }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const v4f c = cw[j][q] * 1152.f;
-      const u32x2 bb = has_bias ? bw[j][q] : u32x2{0u, 0u};
-      const v4f b = v4f{bf16_lo(bb[0]), bf16_hi(bb[0]), bf16_lo(bb[1]), bf16_hi(bb[1])};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[i][j][4 * q + t] = (acc[i][j][4 * q + t] - c[t]) * sa[i] + b[t];
-    }
-  }
-  if (p.lora_act) {
-    // low-rank branch: y[m, n] += sum_r la[m, r] L1[n, r], one
-    // v_mfma_f32_32x32x16_bf16 per 16 ranks and 32 x 32 block, whose result
-    // layout is that of the main accumulators
-    const uint16_t* la = reinterpret_cast<const uint16_t*>(p.lora_act);
-    const int R = p.R;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint16_t* lu = p.lora_up + (n0 + (wn * 2 + j) * 32 + lr) * R + 8 * h;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint16_t* lam = la + imin64(m0 + wm * 128 + i * 32 + lr, p.M - 1) * R + 8 * h;
-        for (int r0 = 0; r0 < R; r0 += 16)        // accumulates onto the finished outputs
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(lu + r0)),
-              __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(lam + r0)), acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);          // one block's operands live at a time
-      }
-    }
-  }
-  if constexpr (OUT == CR_OUT_BF16) {
-    // bf16 (v_cvt_pk_bf16_f32, half to even) through LDS in two halves of 64
-    // token rows per wave, so that every store writes whole 128-byte output
-    // rows; the fragment layout would scatter 8-byte pieces over 32 rows per
-    // store instruction
-    constexpr int RS = 144;                          // LDS row stride of a half tile, 16-byte aligned
-    static_assert(4 * 64 * RS <= NS * STAGE, "half tiles fit the stage buffers");
-    __syncthreads();                                 // every wave is done with the stage buffers
-    uint8_t* tile = smem + wave * (64 * RS);
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-      for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const v16f& a = acc[2 * hh + ii][j];
-            const v2bf lo = __builtin_convertvector((v2f_){a[4 * q], a[4 * q + 1]}, v2bf);
-            const v2bf hi = __builtin_convertvector((v2f_){a[4 * q + 2], a[4 * q + 3]}, v2bf);
-            *reinterpret_cast<u32x2*>(tile + (ii * 32 + lr) * RS + (j * 32 + 8 * q + 4 * h) * 2) =
-                u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-          }
-      // this wave's half tile is complete (LDS keeps a wave's order, so the
-      // next half's writes also land after these reads)
-      __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0)
-#pragma unroll
-      for (int qq = 0; qq < 8; ++qq) {
-        const int r = (l >> 3) + 8 * qq;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * RS + (l & 7) * 16);
-        const int64_t m = m0 + wm * 128 + hh * 64 + r;
-        if (m < p.M)
-          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.out) + m * p.ldc + n0 + wn * 64 + (l & 7) * 8) = v;
-      }
-    }
-    return;
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t n = n0 + (wn * 2 + j) * 32 + 8 * q + 4 * h;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + wm * 128 + i * 32 + lr;
-        if (m >= p.M) continue;
-        const float y[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        if constexpr (OUT == CR_OUT_F32) {
-          *reinterpret_cast<v4f*>(reinterpret_cast<float*>(p.out) + m * p.ldc + n) = v4f{y[0], y[1], y[2], y[3]};
+      for (int q = 0; q < 4; ++q) {
+        const int64_t mq = mw + i * 32 + 8 * q + 4 * h;
+        if (tensor) {
+          sa[q] = v4f{sa_t, sa_t, sa_t, sa_t};
+        } else if (mq + 3 < p.M) {
+          sa[q] = *reinterpret_cast<const v4f*>(p.a_scales + mq);
         } else {
-          u32x2 o;
-          o[0] = f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
-          o[1] = f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16);
-          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + m * p.ldc + n) = o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sa[q][e] = p.a_scales[imin64(mq + e, p.M - 1)];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(acc[i][j][r], sa[r >> 2][r & 3], bj[j]);
+    }
+    if (p.lora_act) {
+      // y += sum_r la[m, r] L1[n, r]: A = la (tokens), B = L1 (channels)
+      const int R = p.R;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const uint16_t* lu = p.lora_up + (nw0 + j * 32 + lr) * R;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int64_t mr = imin64(mw + i * 32 + lr, p.M - 1);
+          if (!p.lora_f32) {
+            const uint16_t* la = reinterpret_cast<const uint16_t*>(p.lora_act) + mr * R;
+            for (int r0 = 0; r0 < R; r0 += 16)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(la + r0 + 8 * h)),
+                  __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(lu + r0 + 8 * h)), acc[i][j], 0, 0, 0);
+          } else {
+            const float* la = reinterpret_cast<const float*>(p.lora_act) + mr * R;
+            for (int r0 = 0; r0 < R; r0 += 2)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(la[r0 + h], __uint_as_float((uint32_t)lu[r0 + h] << 16),
+                                                               acc[i][j], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);            // one block's operands live at a time
         }
       }
     }
+  }
+  // Stores through LDS, 32 token rows of the wave at a time: the lane writes
+  // its column of each row, then whole 16-byte pieces of the rows go out
+  // (bf16 rounded half to even; int32 and float32 as they are).
+  constexpr int ES = (OUT == CR_OUT_BF16) ? 2 : 4;      // bytes per output element
+  constexpr int CS = TN * 32 * ES + 16;                 // LDS row stride of a 32-row chunk
+  constexpr int PR = TN * 32 * ES / 16;                 // 16-byte pieces per row
+  static_assert(NW * 32 * CS <= NS * STAGE, "store chunks fit the stage buffers");
+  __syncthreads();                                      // every wave is done with the stage buffers
+  uint8_t* chunk = smem + wave * (32 * CS);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        uint8_t* d = chunk + (8 * (r >> 2) + 4 * h + (r & 3)) * CS + (j * 32 + lr) * ES;   // rows r, r + 1
+        if constexpr (OUT == CR_OUT_BF16) {
+          const uint32_t pk =
+              __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f_){acc[i][j][r], acc[i][j][r + 1]}, v2bf));
+          *reinterpret_cast<uint16_t*>(d) = (uint16_t)pk;
+          *reinterpret_cast<uint16_t*>(d + CS) = (uint16_t)(pk >> 16);
+        } else if constexpr (RAW) {
+          *reinterpret_cast<int32_t*>(d) = (int)acc[i][j][r];
+          *reinterpret_cast<int32_t*>(d + CS) = (int)acc[i][j][r + 1];
+        } else {
+          *reinterpret_cast<float*>(d) = acc[i][j][r];
+          *reinterpret_cast<float*>(d + CS) = acc[i][j][r + 1];
+        }
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0): the chunk is in LDS (a wave's LDS ops stay in order)
+#pragma unroll
+    for (int q = 0; q < 32 * PR / 64; ++q) {
+      const int pc = q * 64 + l;
+      const int row = pc / PR, c = pc % PR;
+      u32x4 v = *reinterpret_cast<const u32x4*>(chunk + row * CS + c * 16);
+      const int64_t m = mw + i * 32 + row;
+      if (m < p.M) {
+        u32x4* o = reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(p.out) + (m * p.ldc + nw0) * ES + c * 16);
+        if (RAW && p.k_lo > 0) v += *o;                 // a later K chunk: add to the earlier chunks' sum
+        *o = v;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);                 // reads done before the next chunk overwrites
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <int OUT>
-static hipError_t launch_w4a8_h(const GemmParams& p, hipStream_t s) {
-  constexpr int lds = 3 * (256 * 64 + 4096 + 1024 + 1024);
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void*)gemm_w4a8_h_kernel<OUT>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+template <int TM, int TN, bool A16, int OUT>
+static hipError_t launch_w4a8_t(const GemmParams& p, hipStream_t s) {
+  constexpr int stage = 256 * (A16 ? 128 : 64) + 4096 + 1024 + 1024;
+  constexpr int lds = (A16 ? 2 : 3) * stage;
+  static const hipError_t attr = hipFuncSetAttribute((const void*)gemm_w4a8_kernel<TM, TN, A16, OUT>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
   const int64_t tiles = ((p.M + 255) / 256) * (p.N / 128);
-  hipLaunchKernelGGL((gemm_w4a8_h_kernel<OUT>), dim3((unsigned)tiles), dim3(256), lds, s, p);
+  hipLaunchKernelGGL((gemm_w4a8_kernel<TM, TN, A16, OUT>), dim3((unsigned)tiles), dim3(256), lds, s, p);
   return hipGetLastError();
+}
+
+// 2 x 2 waves of 128 x 64 outputs (int8 codes: each activation fragment is
+// converted once per two channel blocks)
+template <int OUT>
+static hipError_t launch_w4a8_out(const GemmParams& p, hipStream_t s) {
+  if (p.a_f16) return launch_w4a8_t<4, 2, true, OUT>(p, s);
+  return launch_w4a8_t<4, 2, false, OUT>(p, s);
 }
 
 hipError_t launch_gemm_w4a8(const GemmParams& p, hipStream_t s) {
   switch (p.out_type) {
-    case CR_OUT_BF16:
-      return launch_w4a8_h<CR_OUT_BF16>(p, s);
-    case CR_OUT_F32:
-      return launch_w4a8_h<CR_OUT_F32>(p, s);
+    case CR_OUT_BF16: return launch_w4a8_out<CR_OUT_BF16>(p, s);
+    case CR_OUT_F32: return launch_w4a8_out<CR_OUT_F32>(p, s);
     default: {
-      const int64_t tiles = ((p.M + 127) / 128) * (p.N / 128);
-      hipLaunchKernelGGL(gemm_w4a8_raw_kernel, dim3((unsigned)tiles), dim3(256), 0, s, p);
-      return hipGetLastError();
+      // the int32 output in K chunks of at most 8192 (128 k-tiles), each exact
+      // in float32 and added in int32 by the next launch
+      const int KT = (int)(p.K / 64);
+      for (int k0 = 0; k0 < KT; k0 += 128) {
+        GemmParams q = p;
+        q.k_lo = k0;
+        q.k_hi = k0 + 128 < KT ? k0 + 128 : KT;
+        const hipError_t e = launch_w4a8_out<CR_OUT_I32_RAW>(q, s);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
     }
   }
 }

@@ -26,7 +26,7 @@ struct RQParams {
   int rpb;              // rows per block (16 >> lg_spr)
   int lg_spr;           // log2(16-lane segments per row)
   int tiled;            // int4 codes: 0 natural, 1 [rows/16][K/64][512 B] int8-core fragments,
-                        // 2 fp6 E2M3 fragments [rows/32][K/64][1536 B]
+                        // 2 fp6 E2M3 fragments [rows/32][K/64][1536 B]; int8 codes: 3 fp16 values [rows, K]
   void* codes8;         // dual output: int8 codes [rows, K] (codes / scales hold the int4 set)
   void* scales8;
   const float* smooth;  // optional per-channel multiplier [K] applied to x first
@@ -103,6 +103,8 @@ struct GemmParams {
   // W4A8 only
   const uint16_t* w_scales16;
   const uint8_t* w_zeros;
+  int a_f16;                 // int8 activation codes carried as fp16 values [M, K]
+  int k_lo, k_hi;            // W4A8 int32 output: k-tiles [k_lo, k_hi) of this launch (k_hi 0: all)
 };
 hipError_t launch_gemm_int(const GemmParams& p, hipStream_t s);   // INT8 x INT8
 hipError_t launch_gemm_a8w4(const GemmParams& p, hipStream_t s);  // INT8 x tile-packed INT4

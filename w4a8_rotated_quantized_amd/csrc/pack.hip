@@ -119,39 +119,6 @@ __global__ __launch_bounds__(256) void wsum_kernel(PackParams p) {
   p.w_sum[n] = acc;
 }
 
-// ASYM_UINT4 g16: w_sum[n] = sum_k fp16(s[n, g] * (q[n, k] - z[n, g])), the
-// correction vector of the fp16 matrix-core W4A8 kernel. Each term is the
-// fp16 weight that kernel multiplies with (s * (q - z) is exact in float32,
-// then rounded once to fp16); every fp16 value is an integer multiple of
-// 2^-24, so the sum is taken exactly in int64 units of 2^-24 and rounded
-// once to float32. One block per row.
-__global__ __launch_bounds__(256) void wsum_asym_kernel(PackParams p) {
-  const int64_t n = blockIdx.x;
-  const int64_t K = p.K, G = K / 16;
-  const uint8_t* row = p.codes + n * (K / 2);
-  const _Float16* sc = reinterpret_cast<const _Float16*>(p.scales) + n * G;
-  const uint8_t* zr = p.zeros + n * (K / 32);
-  long long acc = 0;
-  for (int64_t g = threadIdx.x; g < G; g += 256) {
-    const float s = (float)sc[g];
-    const int z = (g & 1) ? (zr[g / 2] >> 4) : (zr[g / 2] & 0xF);
-    for (int j = 0; j < 8; ++j) {
-      const int b = row[g * 8 + j];
-      const float w0 = (float)(_Float16)(s * (float)((b & 0xF) - z));
-      const float w1 = (float)(_Float16)(s * (float)((b >> 4) - z));
-      acc += (long long)(w0 * 16777216.f) + (long long)(w1 * 16777216.f);
-    }
-  }
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  __shared__ long long part[4];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const long long t = part[0] + part[1] + part[2] + part[3];
-    p.w_sum[n] = (float)t * 5.9604644775390625e-08f;   // int64 -> float32 rounds to nearest even; 2^-24 is exact
-  }
-}
-
 static inline unsigned nblocks(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 // Natural signed int4 codes -> the fp6 E2M3 fragment layout of the fp6
@@ -195,7 +162,6 @@ hipError_t launch_pack(const PackParams& p, hipStream_t s) {
   if (p.qtype == CR_Q_ASYM_UINT4) {
     hipLaunchKernelGGL(pack_asym_kernel, dim3(nblocks(p.N * p.K / 8)), dim3(256), 0, s, p);
     hipLaunchKernelGGL(pack_g16_meta_kernel, dim3(nblocks(p.N * p.K / 16)), dim3(256), 0, s, p);
-    if (p.w_sum) hipLaunchKernelGGL(wsum_asym_kernel, dim3((unsigned)p.N), dim3(256), 0, s, p);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(pack_sym_kernel, dim3(nblocks(p.N * p.K / 16)), dim3(256), 0, s, p);

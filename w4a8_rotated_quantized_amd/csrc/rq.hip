@@ -154,10 +154,27 @@ CR_DEV void quant_store_f6(const float (&v)[16], float rs, const RQParams& a, in
   f6_store_words(o[0], o[1], o[2], a, row, grp, gL);
 }
 
+// INT8 codes as fp16 values ([rows, K], the activation operand of the fp16
+// matrix-core W4A8 GEMM): the rounded integer as a float (as f6_qval), then
+// converted exactly (|code| <= 127), 32 bytes per lane
+CR_DEV void quant_store_h16(const float (&v)[16], float rs, uint8_t* __restrict__ dst) {
+  uint32_t o[8];
+#pragma unroll
+  for (int e = 0; e < 16; e += 2) {
+    const float q0 = f6_qval(v[e], dreg_neg(e) ? -rs : rs);
+    const float q1 = f6_qval(v[e + 1], dreg_neg(e + 1) ? -rs : rs);
+    o[e >> 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(q0, q1));
+  }
+  *reinterpret_cast<u32x4*>(dst) = u32x4{o[0], o[1], o[2], o[3]};
+  *reinterpret_cast<u32x4*>(dst + 16) = u32x4{o[4], o[5], o[6], o[7]};
+}
+
 // codes of one lane in the layout the parameters ask for
 template <int QT>
 CR_DEV void store_codes(const float (&v)[16], float rs, const RQParams& a, int64_t row, int grp, int gL) {
   if (QT == CR_Q_SYM_INT4 && a.tiled == 2) quant_store_f6(v, rs, a, row, grp, gL);
+  else if (QT == CR_Q_SYM_INT8 && a.tiled == 3)
+    quant_store_h16(v, rs, reinterpret_cast<uint8_t*>(a.codes) + (row * a.K + grp * 256 + gL * 16) * 2);
   else quant_store<QT>(v, rs, code_dst<QT>(a, row, grp, gL));
 }
 
