@@ -1,37 +1,41 @@
-"""Benchmark of the ConvRot W4A4 tensorwise linear on one MI355X.
+"""Benchmark of the ConvRot low-bit linear layer path on one MI355X.
 
-Workload (the single MMDiT projection of the Qwen-Image MMDiT, per the
-per-family shape table of the "Qwen-Image-Edit-2511-W4A8-ConvRot" card):
-X bf16 [M, 3072] with M in {4096, 32} (image tokens and the small-token
-case), N(0,1) with 15 outlier channels x30, W [3072, 3072] ~ N(0, 0.02)
-prepared offline (rotated, quantized to INT4, tile-packed; untimed).
+Default workload: the mixed-precision MMDiT block (8192 image + 512 text
+tokens, hidden 3072), the largest single-GPU configuration:
+  * Q, K, MLP up (3072 -> 12288) and the post-GELU MLP down (12288 -> 3072)
+    in W4A4 tensorwise ConvRot (INT4 x INT4),
+  * V and attention output projections and the adaLN modulation linear
+    (3072 -> 6 x 3072, 2 rows: one per sample of a batch of 2) in INT8
+    tensorwise ConvRot,
+for the image and the text stream: 14 linears, 1971.8 GOP per step. The
+recipe follows the "Qwen-Image-Edit-2511 - INT4 tensorwise W4A4" page
+(intro: 480 INT4 and 359 INT8 layers; Measurements); the shapes follow the
+per-family shape table of the "Qwen-Image-Edit-2511-W4A8-ConvRot" card. All
+inputs are seeded synthetic tensors (workloads/): no model, dataset or
+checkpoint. Weights are prepared offline (rotated, quantized, packed at 4
+bits per INT4 code; untimed).
 
-One step = the whole hot path for both token counts, inputs resident in HBM:
-    rotate+quantize(X_4096) -> w4a4_gemm(4096)  ->  bf16 [4096, 3072]
-    rotate+quantize(X_32)   -> w4a4_gemm(32)    ->  bf16 [32, 3072]
-Every step uses a different copy of all buffers (inputs, weights, codes,
-outputs; ~10 copies, over 2x the 256 MB last-level cache), so each step
-reads cold HBM data.
-
-The INT4 codes travel as fp6 E2M3 values and the GEMMs run on the fp6
-matrix cores (exact: see gemm_f6.hip); `--cores int8` runs the int8-core
-path instead (int4 tile-packed codes widened to bytes).
+One step = every rotate+quantize pass and every GEMM of the block, on one
+stream, inputs resident in HBM; two buffer sets (weights included,
+~1.2 GB each, over 4x the 256 MB last-level cache) alternate, so every step
+reads cold data. The W4A4 GEMMs expand their 4-bit weight tiles into fp6
+E2M3 fragments in a workspace and run on the fp6 matrix cores (INT4 codes
+are exact E2M3 values, the float32 sums exact); the INT8 layers run on the
+int8 matrix cores; the 2-row modulation linears stream their weights.
 
 Metric: effective TOPS = sum 2*M*N*K / step time (the fused
-rotate+quantize+W4 GEMM throughput), also given as % of the 5.0 POP/s dense
-INT8 matrix peak. The roofline object reports the dominant kernel (the
-M=4096 GEMM) against the dense peak of the matrix instruction it runs on
-(fp6: 10.1 PFLOP/s; int8: 5.0 POP/s); its duration is the mean over K
-back-to-back launches, timed with HIP events on the launch stream
-(kernels_us.gemm_m4096_in_step: events around each launch inside the steps,
-which also hold the launch gap). The M=4096 rotate+quantize (two launches)
-is timed the same way for rq_m4096_GBps. The CPU baseline is the numpy oracle
-running the same step on this host.
+rotate+quant+W4 GEMM throughput), also as % of the 5.0 POP/s dense INT8
+matrix peak; GB/s of every rotate+quantize pass (algorithmic bytes: bf16 in,
+codes out at 4 or 8 bits per code). The roofline object reports the
+dominant kernel (the GEMM kernel of the slowest layer) against the dense peak
+of the matrix instruction it runs on, its duration the mean of back-to-back
+launches timed with HIP events on the launch stream. The same line carries
+the single MMDiT projection (M = 4096 and M = 32) as "c2". The CPU baseline
+is the numpy oracle running a bounded sample of the same block on this host.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--rot-group 256] [--cores fp6|int8]
-                       [--workload c2|c1|c3|c4|c5|c2a8]
-(--workload other than c2 prints that workload's throughput line instead;
-see bench_workloads.py)
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--cores fp6|int8]
+                       [--workload c4|c2|c1|c3|c5|c2a8|merge]
+(--workload other than c4 prints that workload's line; see bench_workloads.py)
 """
 import argparse
 import hashlib
@@ -43,32 +47,25 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-INT8_PEAK_TOPS = 5000.0       # MI355X dense INT8 matrix peak (5.0 POP/s)
-FP6_PEAK_TOPS = 10100.0       # MI355X dense fp6 / fp4 matrix peak (10.1 PFLOP/s)
-HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
-M_BIG, M_SMALL, N, K = 4096, 32, 3072, 3072
-ROT = 256          # ConvRot group size (--rot-group: 16, 64, 256 or 1024)
-CORES = "fp6"      # matrix cores of the W4A4 GEMMs (--cores)
+import bench_workloads as bw  # noqa: E402
+
 GEMM_SOURCES = {"fp6": ["gemm_f6.hip", "epilogue.h", "common.h", "kernels.h"],
                 "int8": ["gemm_w4a4.hip", "epilogue.h", "common.h", "kernels.h"]}
-TRAFFIC_PROFILE = {"fp6": "w4a4_f6_gemm_m4096_n3072_k3072_traffic.json",
-                   "int8": "w4a4_gemm_m4096_n3072_k3072_traffic.json"}
+TRAFFIC_PROFILE = {"fp6": "c4_img_mlp_gemm_f6_traffic.json", "int8": "c4_img_mlp_gemm_int8_traffic.json"}
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--rot-group", type=int, default=256, choices=(16, 64, 256, 1024),
-                    help="ConvRot group size of the c2 line (256 is the configuration the metric is quoted on)")
     ap.add_argument("--cores", default="fp6", choices=("fp6", "int8"),
-                    help="matrix cores of the W4A4 GEMMs: fp6 (E2M3 codes, default) or int8 (widened int4)")
-    ap.add_argument("--workload", default="c2",
-                    help="c2 (default: the headline line), or c1 / c3 / c4 / c5 / c2a8 / merge for the other workloads' "
-                         "throughput lines (bench_workloads.py)")
+                    help="matrix cores of the W4A4 GEMMs above 64 tokens: fp6 (default) or int8")
+    ap.add_argument("--workload", default="c4",
+                    help="c4 (default: the headline line), or c1 / c2 / c3 / c5 / c2a8 / merge for the other "
+                         "workloads' throughput lines (bench_workloads.py)")
     return ap.parse_args()
 
 
@@ -80,28 +77,36 @@ def source_sha(names):
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile():
+def traffic_from_profile(cores, layer):
     """HBM bytes per launch of the dominant kernel, from the committed
-    rocprofv3 counter summary, only if the kernel source is unchanged."""
-    p = os.path.join(ROOT, "profiles", TRAFFIC_PROFILE[CORES])
+    rocprofv3 counter summary, only if it covers this layer and the kernel
+    source is unchanged."""
+    p = os.path.join(ROOT, "profiles", TRAFFIC_PROFILE[cores])
     if not os.path.exists(p):
         return None
     with open(p) as f:
         d = json.load(f)
-    if d.get("source_sha") != source_sha(GEMM_SOURCES[CORES]):
+    if d.get("source_sha") != source_sha(GEMM_SOURCES[cores]) or d.get("layer") != layer:
         return None
     return d.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(budget_s):
-    """The oracle (numpy) running the same step on the host, repeated until
-    about budget_s seconds have passed."""
+    """The oracle (numpy) running a bounded sample of the block on the host:
+    all 14 layers on the first 512 rows of every activation tensor (all of
+    the text and modulation tensors) and the first 1536 output channels of
+    every weight. Weights prepared once, untimed."""
     import numpy as np
     import workloads as wl
     from oracle import linear as ol, gemm as og
-    xb_big = wl.activation(2, 0, M_BIG, K, n_outliers=15, outlier_scale=30.0)
-    xb_small = wl.activation(2, 2, M_SMALL, K, n_outliers=15, outlier_scale=30.0)
-    wp = ol.prepare_w4a4(wl.weight(2, 1, N, K), ROT)
+    w = wl.CONFIGS["c4"]()
+    NS = 1536
+    rows = {x: min(512, w.acts[x][0]) for x in w.acts}
+    acts = {x: wl.act_bits(w, x, rows=rows[x]) for x in w.acts}
+    wq = {}
+    for lin in w.linears:
+        qt = "int4" if lin.fmt == "w4a4" else "int8"
+        wq[lin.name] = ol.rotate_quantize(wl.weight_bits(w, lin, rows=NS), 256, qt, "tensor")
     try:
         import threadpoolctl
         np.ones((64, 64)) @ np.ones((64, 64))
@@ -109,217 +114,127 @@ def cpu_baseline(budget_s):
         cores = max([i.get("num_threads", 1) for i in info] + [1])
     except Exception:
         cores = os.cpu_count() or 1
+    ops1 = sum(2.0 * rows[l.x_id] * min(l.N, NS) * l.K for l in w.linears)
     reps, t0 = 0, time.perf_counter()
     while True:
-        for xb in (xb_big, xb_small):
-            r = ol.rotate_quantize(xb, ROT, "int4", "tensor")
-            acc = og.int_gemm(r["values"], wp["values"])
-            ol.epilogue_scalar(acc, r["scales"], "tensor", wp["scales"], "tensor")
+        rq = {}
+        for lin in w.linears:
+            qt = "int4" if lin.fmt == "w4a4" else "int8"
+            key = (lin.x_id, qt)
+            if key not in rq:
+                rq[key] = ol.rotate_quantize(acts[lin.x_id], 256, qt, "tensor")
+            xa, wp = rq[key], wq[lin.name]
+            acc = og.int_gemm(xa["values"], wp["values"])
+            ol.epilogue_scalar(acc, xa["scales"], "tensor", wp["scales"], "tensor")
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    ops = 2.0 * (M_BIG + M_SMALL) * N * K * reps
-    return {"value": ops / el / 1e12, "unit": "TOPS", "cores": int(cores), "kind": "oracle",
-            "sample": f"{reps} full oracle step(s) (M=4096 and M=32, K=N=3072) in {el:.1f} s "
-                      f"(numpy; elementwise stages single-threaded, BLAS threads={cores})"}
+    return {"value": ops1 * reps / el / 1e12, "unit": "TOPS", "cores": int(cores), "kind": "oracle",
+            "sample": f"{reps} pass(es) of the block's 14 layers on the first 512 image tokens, all 512 text "
+                      f"tokens and both modulation rows, first {NS} output channels of each weight "
+                      f"({ops1 / 1e9:.1f} GOP each) in {el:.1f} s (numpy; "
+                      f"rotation and quantization single-threaded, integer GEMM as float64 BLAS, "
+                      f"BLAS threads={cores})"}
 
 
-def setup(dev, nbytes_target=600e6):
-    """Weights prepared offline (untimed) and enough buffer sets of every
-    tensor that consecutive steps touch cold HBM data."""
-    import numpy as np
-    import torch
-    import w4a8_rotated_quantized_amd as cr
-    import workloads as wl
-
-    def bf16(a):
-        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-
-    xb_big = wl.activation(2, 0, M_BIG, K, n_outliers=15, outlier_scale=30.0)
-    xb_small = wl.activation(2, 2, M_SMALL, K, n_outliers=15, outlier_scale=30.0)
-    wb = wl.weight(2, 1, N, K)
-    w = bf16(wb)
-    wc, ws, _, _ = cr.convrot_rotate_quantize(w, ROT, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
-    if CORES == "fp6":
-        wp = cr.w4_pack_weights_f6(wc, N, K)
-        code_shape = lambda m: ((m + 31) // 32, K // 64, 1536)   # noqa: E731
-    else:
-        wp, _, _, _ = cr.w4_pack_weights(wc, ws, N, K, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
-        code_shape = lambda m: ((m + 15) // 16, K // 64, 512)    # noqa: E731
-    per_set = M_BIG * K * 2 + M_BIG * K // 2 + M_BIG * N * 2 + N * K // 2
-    nsets = max(2, int(np.ceil(nbytes_target / per_set)))
-    sets = []
-    xbig0, xsmall0 = bf16(xb_big), bf16(xb_small)
-    for _ in range(nsets):
-        sets.append({
-            "xb": xbig0.clone(), "xs": xsmall0.clone(), "wp": wp.clone(), "ws": ws.clone(),
-            "cb": torch.empty(code_shape(M_BIG), dtype=torch.uint8, device=dev),
-            "cs": torch.empty(code_shape(M_SMALL), dtype=torch.uint8, device=dev),
-            "sb": torch.empty(1, dtype=torch.float32, device=dev),
-            "ss": torch.empty(1, dtype=torch.float32, device=dev),
-            "wsb": torch.empty(cr.convrot_rq_workspace_size(M_BIG, K, ROT, 0, 0), dtype=torch.uint8, device=dev),
-            "wss": torch.empty(cr.convrot_rq_workspace_size(M_SMALL, K, ROT, 0, 0), dtype=torch.uint8, device=dev),
-            "yb": torch.empty((M_BIG, N), dtype=torch.bfloat16, device=dev),
-            "ys": torch.empty((M_SMALL, N), dtype=torch.bfloat16, device=dev),
-        })
-    return sets
-
-
-def _layout(cr):
-    return cr.LAYOUT.F6 if CORES == "fp6" else cr.LAYOUT.TILED
-
-
-def rq_big(cr, s):
-    cr.convrot_rotate_quantize(s["xb"], ROT, 0, 0, layout=_layout(cr), codes=s["cb"], scales=s["sb"],
-                               workspace=s["wsb"])
-
-
-def gemm_big(cr, s):
-    cr.w4a4_gemm(s["cb"], s["sb"], 0, s["wp"], s["ws"], 0, M_BIG, N, K, out=s["yb"])
-
-
-def rq_small(cr, s):
-    cr.convrot_rotate_quantize(s["xs"], ROT, 0, 0, layout=_layout(cr), codes=s["cs"], scales=s["ss"],
-                               workspace=s["wss"])
-
-
-def gemm_small(cr, s):
-    cr.w4a4_gemm(s["cs"], s["ss"], 0, s["wp"], s["ws"], 0, M_SMALL, N, K, out=s["ys"])
+def c2_line(steps, warmup, cores):
+    r = bw.Runner("c2", cores)
+    ms = r.time_steps(steps, warmup)
+    kern = r.per_call(max(3, steps // 2))
+    big = [l for l in r.w.linears if l.M == 4096][0]
+    t_gemm = r.gemm_kernel_alone(big, steps)
+    out = {"workload": r.w.name, "value": round(r.ops() / (ms * 1e-3) / 1e12, 2), "unit": "TOPS",
+           "ms_per_step": round(ms, 5),
+           "kernels_us": {k.replace(":x", ":m").replace(":int4_tensor", ""): round(v, 2) for k, v in kern.items()},
+           "gemm_m4096_kernel_us": round(t_gemm, 2),
+           "gemm_m4096_TOPS": round(2.0 * big.M * big.N * big.K / t_gemm / 1e6, 1)}
+    for lin in r.w.linears:
+        us = kern[f"gemm:{lin.name}"]
+        out[f"gemm_m{lin.M}_GBps"] = round(bw.gemm_bytes(lin) / us / 1e3, 1)
+    for key in r.rq_plan:
+        M, K = r.w.acts[key[0]][0], r.w.acts[key[0]][1]
+        us = kern[f"rq:{key[0]}:{key[1]}"]
+        out[f"rq_m{M}_GBps"] = round(bw.rq_bytes(M, K, key[1]) / us / 1e3, 1)
+    del r
+    return out
 
 
 def main():
-    global ROT, CORES
     args = parse()
-    ROT = args.rot_group
-    CORES = args.cores
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path has no multi-GPU part); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
-
-    if args.workload != "c2":
-        import bench_workloads
+    if args.workload != "c4":
         for name in args.workload.split(","):
-            bench_workloads.run(name, args.steps, args.warmup, cores=args.cores)
+            bw.run(name, args.steps, args.warmup, cores=args.cores)
         return
 
-    import numpy as np
     import torch
-    import w4a8_rotated_quantized_amd as cr
-
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(3)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
-    sets = setup(dev)
-    nsets = len(sets)
 
-    ev = {}
-
-    def step(i, record):
-        s = sets[i % nsets]
-        if record:
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-            e[0].record(stream)
-        rq_big(cr, s)
-        if record:
-            e[1].record(stream)
-        gemm_big(cr, s)
-        if record:
-            e[2].record(stream)
-        rq_small(cr, s)
-        if record:
-            e[3].record(stream)
-        gemm_small(cr, s)
-        if record:
-            e[4].record(stream)
-            ev.setdefault("e", []).append(e)
-
-    for i in range(args.warmup):
-        step(i, False)
-    torch.cuda.synchronize()
-
-    # timed region 1: plain back-to-back steps (the headline number)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i, False)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-
-    # timed region 2: the same steps with events around every kernel call
-    for i in range(args.steps):
-        step(i, True)
-    torch.cuda.synchronize()
-    parts = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev["e"]])
-    t_rq_big, t_gemm_call, t_rq_small, t_gemm_small = (float(np.mean(parts[:, j])) for j in range(4))
-
-    # timed region 3: the dominant kernel alone, launched back to back over the
-    # buffer sets (the events of region 2 also hold each launch's gap)
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    g0.record(stream)
-    for i in range(args.steps):
-        gemm_big(cr, sets[i % nsets])
-    g1.record(stream)
-    torch.cuda.synchronize()
-    t_gemm_big = g0.elapsed_time(g1) / args.steps
-    # the same for the M=4096 rotate+quantize (its two launches)
-    torch.cuda.synchronize()
-    g0.record(stream)
-    for i in range(args.steps):
-        rq_big(cr, sets[i % nsets])
-    g1.record(stream)
-    torch.cuda.synchronize()
-    t_rq_call, t_rq_big = t_rq_big, g0.elapsed_time(g1) / args.steps
-
-    ops_step = 2.0 * (M_BIG + M_SMALL) * N * K
-    eff_tops = ops_step / (ms_step * 1e-3) / 1e12
-    gemm_tops = 2.0 * M_BIG * N * K / (t_gemm_big * 1e-3) / 1e12
-    rq_bytes = M_BIG * K * 2 + M_BIG * K * (0.75 if CORES == "fp6" else 0.5) + 4   # bf16 in, codes (6 or 4 bits) out
-    rq_gbs = rq_bytes / (t_rq_big * 1e-3) / 1e9
-    cb = 0.75 if CORES == "fp6" else 0.5                      # bytes per code in the operand layout
-    small_bytes = N * K * cb + M_SMALL * K * cb + M_SMALL * N * 2
-    traffic = traffic_from_profile()
-    peak = FP6_PEAK_TOPS if CORES == "fp6" else INT8_PEAK_TOPS
+    r = bw.Runner("c4", args.cores)
+    ms = r.time_steps(args.steps, args.warmup)
+    kern = r.per_call(max(3, args.steps // 2))
+    eff = r.ops() / (ms * 1e-3) / 1e12
+    layers = {}
+    for lin, _ in r.gemm_plan:
+        us = kern[f"gemm:{lin.name}"]
+        layers[lin.name] = {"us": round(us, 2), "TOPS": round(2.0 * lin.M * lin.N * lin.K / us / 1e6, 1),
+                            "GBps": round(bw.gemm_bytes(lin) / us / 1e3, 1)}
+    rqs = {}
+    for key in r.rq_plan:
+        M, K = r.w.acts[key[0]][0], r.w.acts[key[0]][1]
+        us = kern[f"rq:{key[0]}:{key[1]}"]
+        gbs = bw.rq_bytes(M, K, key[1]) / us / 1e3
+        rqs[f"{key[0]}:{key[1]}"] = {"us": round(us, 2), "GBps": round(gbs, 1),
+                                     "pct_hbm": round(100.0 * gbs / bw.HBM_PEAK_GBS, 1)}
+    # dominant kernel: the GEMM kernel of the slowest layer, alone, back to back
+    dom = max(layers, key=lambda n: layers[n]["us"])
+    dlin = [l for l in r.w.linears if l.name == dom][0]
+    t_dom = r.gemm_kernel_alone(dlin, args.steps)
+    on_f6 = dlin.fmt == "w4a4" and args.cores == "fp6" and dlin.M > bw.SKINNY_M
+    peak = bw.FP6_PEAK_TOPS if on_f6 else bw.INT8_PEAK_TOPS
+    achieved = 2.0 * dlin.M * dlin.N * dlin.K / t_dom / 1e6
+    ops = r.ops()
+    nsets = r.nsets
+    name = r.w.name
+    del r
+    torch.cuda.empty_cache()
 
     line = {
         "metric": "effective TOPS of fused rotate+quant+W4 GEMM (% INT8 MFMA peak); GB/s",
-        "value": round(eff_tops, 2),
+        "value": round(eff, 2),
         "unit": "TOPS",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4",
+        "dtype": ("int4 x int4 (W4A4 layers: codes as fp6 E2M3 on the fp6 matrix cores, exact float32 sums) and "
+                  "int8 x int8 (INT8 layers: int8 matrix cores, int32 sums)" if args.cores == "fp6" else
+                  "int4 x int4 (widened to int8 on the int8 matrix cores) and int8 x int8, int32 sums"),
         "data": "synthetic",
-        "config": {"workload": f"MMDiT projection, W4A4 tensorwise ConvRot group {ROT}, "
-                               "X bf16 [M, 3072] (M = 4096 and 32), W [3072, 3072]",
-                   "M": [M_BIG, M_SMALL], "N": N, "K": K, "rot_group": ROT,
-                   "matrix_cores": CORES, "buffer_sets": nsets},
-        "pct_int8_peak": round(100.0 * eff_tops / INT8_PEAK_TOPS, 2),
-        "kernels_us": {"rq_m4096": round(t_rq_big * 1e3, 2), "gemm_m4096": round(t_gemm_big * 1e3, 2),
-                       "rq_m4096_in_step": round(t_rq_call * 1e3, 2),
-                       "gemm_m4096_in_step": round(t_gemm_call * 1e3, 2),
-                       "rq_m32": round(t_rq_small * 1e3, 2), "gemm_m32": round(t_gemm_small * 1e3, 2)},
-        "rq_m4096_GBps": round(rq_gbs, 1),
-        "rq_m4096_pct_hbm": round(100.0 * rq_gbs / HBM_PEAK_GBS, 1),
-        "gemm_m4096_TOPS": round(gemm_tops, 1),
-        "gemm_m32_GBps": round(small_bytes / (t_gemm_small * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(gemm_tops / peak, 4),
-                     "traffic": traffic},
+        "config": {"workload": name, "layers": 14, "total_GOP": round(ops / 1e9, 1),
+                   "tokens": {"image": 8192, "text": 512, "modulation_rows": 2}, "hidden": 3072,
+                   "w4a4_layers": "q, k, mlp_up, mlp_down (image and text)",
+                   "int8_layers": "v, out, mod (image and text)",
+                   "w4a4_weights": "tile-packed INT4, 2 per byte (expanded per call into fp6 fragments)",
+                   "w4a4_matrix_cores": args.cores, "buffer_sets": nsets},
+        "pct_int8_peak": round(100.0 * eff / bw.INT8_PEAK_TOPS, 2),
+        "gemm": layers,
+        "rotate_quantize": rqs,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic_from_profile(args.cores, dom),
+                     "kernel": ("gemm_f6_kernel" if on_f6 else "int8-core GEMM") + f" of {dom} "
+                               f"({dlin.M}x{dlin.N}x{dlin.K})", "kernel_us": round(t_dom, 2)},
     }
+    line["c2"] = c2_line(args.steps, args.warmup, args.cores)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line))

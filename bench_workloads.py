@@ -1,34 +1,57 @@
-"""Throughput of the other workloads (tiny layer, W4A8, mixed MMDiT block,
-low-rank corrected g64), one JSON line each, for `bench.py --workload NAME`.
+"""Workload runner of the benchmark: builds a workload's layers on the GPU
+path (weights prepared offline, untimed), keeps several cold buffer sets, and
+times whole steps and single calls with HIP events on the launch stream.
 
 A step runs every rotate+quantize the workload needs (one per activation
-tensor and format: layers that share an input share the pass) and every
-GEMM, in order, on one stream, with inputs resident in HBM. Weights are
-prepared offline (untimed). `value` = sum of 2*M*N*K over the layers / step
-time. Per-kernel times come from HIP events around each launch in a second
-pass; each GEMM is also reported as TOPS and, for M <= 64, as weight GB/s.
+tensor and code format: layers that share an input share the pass; an input
+that feeds both INT4 and INT8 layers is quantized once to both) and every
+GEMM, in order, on one stream, with inputs resident in HBM. Each step uses
+the next buffer set (inputs, weights, codes, workspaces, outputs), so
+consecutive steps read data the previous step did not touch.
+
+Formats on the measured path:
+  * W4A4 weights are stored tile-packed at 4 bits per code (w4_pack_weights).
+    With more than 64 tokens the activation codes are fp6 E2M3 fragments and
+    each GEMM call first expands the layer's weight tiles into fp6 fragments
+    in a workspace, then runs the fp6 matrix-core GEMM ("fp6" cores); with
+    64 tokens or fewer (and with cores="int8") the codes are tile-packed int4
+    and the int8 matrix cores read the 4-bit tiles directly.
+  * INT8 layers: int8 codes and weights on the int8 matrix cores.
+  * W4A8: int8 activation codes carried as fp16 values, asymmetric uint4 g16
+    weights, exact group partials on the fp16 matrix cores.
 """
 import json
 import sys
 import time
 
-INT8_PEAK_TOPS = 5000.0
-HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0       # MI355X dense INT8 matrix peak (5.0 POP/s)
+FP6_PEAK_TOPS = 10100.0       # MI355X dense fp6 / fp4 matrix peak (10.1 PFLOP/s)
+FP16_PEAK_TOPS = 2500.0       # MI355X dense fp16 / bf16 matrix peak (2.5 PFLOP/s)
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+
+SKINNY_M = 64                 # token counts up to this take the weight-streaming int8-core kernels
 
 
-def _plan(w):
-    """RQ passes (x_id, kind) and GEMMs for workload w. An activation that
-    feeds both per-tensor INT4 and INT8 layers is quantized once, to both
-    (convrot_rotate_quantize_dual)."""
-    def kind_of(lin):
-        return {"w4a4": "int4_tensor", "int8": "int8_tensor", "w4a8": "int8_row_f16", "a8w4": "int8_row",
-                "w4a4_g64": ("u4_g64" if lin.unsigned_shift else "s4_g64")}[lin.fmt]
+def _kind_of(lin, cores):
+    if lin.fmt == "w4a4":
+        return "int4_tensor"
+    if lin.fmt == "int8":
+        return "int8_tensor"
+    if lin.fmt == "w4a8":
+        return "int8_row_f16"
+    if lin.fmt == "a8w4":
+        return "int8_row"
+    return "u4_g64" if lin.unsigned_shift else "s4_g64"
+
+
+def plan(w, cores="fp6"):
+    """RQ passes (x_id, kind, layer) and GEMMs (lin, rq key) of workload w."""
     kinds = {}
     for lin in w.linears:
-        kinds.setdefault(lin.x_id, set()).add(kind_of(lin))
+        kinds.setdefault(lin.x_id, set()).add(_kind_of(lin, cores))
     rq, gemms = [], []
     for lin in w.linears:
-        kind = kind_of(lin)
+        kind = _kind_of(lin, cores)
         if kind in ("int4_tensor", "int8_tensor") and {"int4_tensor", "int8_tensor"} <= kinds[lin.x_id]:
             kind = "dual_tensor"
         key = (lin.x_id, kind, lin.name if lin.fmt == "w4a4_g64" else "")
@@ -36,6 +59,308 @@ def _plan(w):
             rq.append(key)
         gemms.append((lin, key))
     return rq, gemms
+
+
+def rq_bytes(M, K, kind):
+    """Algorithmic bytes of one rotate+quantize pass: bf16 in, codes out at
+    their bit width (4 for INT4, 8 for INT8, both for the dual pass), plus
+    the scales."""
+    codes = {"int4_tensor": 0.5, "s4_g64": 0.5, "u4_g64": 0.5, "int8_tensor": 1.0, "int8_row": 1.0,
+             "int8_row_f16": 1.0, "dual_tensor": 1.5}[kind]
+    scales = {"int4_tensor": 4, "int8_tensor": 4, "dual_tensor": 8, "int8_row": 4 * M, "int8_row_f16": 4 * M,
+              "s4_g64": 4 * M * K // 64, "u4_g64": 4 * M * K // 64}[kind]
+    return 2 * M * K + codes * M * K + scales
+
+
+def gemm_bytes(lin):
+    """Algorithmic bytes of one GEMM: activation codes and weights at their
+    bit width (INT4 0.5 B, INT8 1 B per code; W4A8 also fp16 scales and uint4
+    zero points per 16 weights; 64-group scales as float32) and the bf16 output."""
+    M, N, K = lin.M, lin.N, lin.K
+    if lin.fmt == "w4a4":
+        return 0.5 * M * K + 0.5 * N * K + 2 * M * N
+    if lin.fmt == "int8":
+        return M * K + N * K + 2 * M * N
+    if lin.fmt == "w4a8":
+        return M * K + N * K * (0.5 + 2.5 / 16) + 2 * M * N
+    if lin.fmt == "a8w4":
+        return M * K + 0.5 * N * K + 2 * M * N
+    return 0.5 * M * K + 0.5 * N * K + 4 * (M + N) * K // 64 + 2 * M * N + 2 * lin.rank * (M + N)
+
+
+class Runner:
+    """One workload on the GPU path with `nsets` cold buffer sets."""
+
+    def __init__(self, name, cores="fp6", nsets=2, rot=256, workload=None):
+        import numpy as np
+        import torch
+        import w4a8_rotated_quantized_amd as cr
+        import workloads as wl
+        self.np, self.torch, self.cr = np, torch, cr
+        self.dev = torch.device("cuda:0")
+        torch.cuda.set_device(self.dev)
+        self.stream = torch.cuda.current_stream()
+        self.w = workload if workload is not None else wl.CONFIGS[name]()
+        self.cores = cores
+        self.rot = rot
+        self.nsets = nsets
+        dev = self.dev
+        w = self.w
+        self.rq_plan, self.gemm_plan = plan(w, cores)
+
+        def bf16(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        t0 = time.time()
+        acts = {x: bf16(wl.act_bits(w, x)) for x in w.acts}
+        # offline weight preparation (untimed): rotate, quantize, pack
+        prep = {}
+        for lin in w.linears:
+            N, K = lin.N, lin.K
+            if lin.fmt in ("w4a4", "a8w4"):
+                wc, ws, _, _ = cr.convrot_rotate_quantize(bf16(wl.weight_bits(w, lin)), rot, cr.Q.SYM_INT4,
+                                                          cr.GRAN.TENSOR)
+                prep[lin.name] = dict(w=cr.w4_pack_weights(wc, ws, N, K)[0], ws=ws)
+            elif lin.fmt == "int8":
+                wc, ws, _, _ = cr.convrot_rotate_quantize(bf16(wl.weight_bits(w, lin)), rot, cr.Q.SYM_INT8,
+                                                          cr.GRAN.TENSOR)
+                prep[lin.name] = dict(w=wc, ws=ws)
+            elif lin.fmt == "w4a8":
+                wc, ws, wz, _ = cr.convrot_rotate_quantize(bf16(wl.weight_bits(w, lin)), 256, cr.Q.ASYM_UINT4,
+                                                           cr.GRAN.ROW_GROUP, 16)
+                p, ps, pz, _ = cr.w4_pack_weights(wc, ws, N, K, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16, zeros=wz)
+                prep[lin.name] = dict(w=p, ws=ps, wz=pz)
+            else:
+                l1, l2, r = wl.lowrank_bits(w, lin)
+                wc, ws, _, _ = cr.convrot_rotate_quantize(bf16(r), 0, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64)
+                p, ps, _, wsum = cr.w4_pack_weights(wc, ws, N, K, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64,
+                                                    want_wsum=True)
+                prep[lin.name] = dict(w=p, ws=ps, wsum=wsum, l1=bf16(l1), l2=bf16(l2))
+        torch.cuda.synchronize()
+        self.setup_s = time.time() - t0
+
+        def f6_codes(M):
+            return self.f6 and M > SKINNY_M
+        self.f6 = cores == "fp6"
+        self.f6_codes = f6_codes
+
+        def c4_shape(M, K):
+            return ((M + 31) // 32, K // 64, 1536) if f6_codes(M) else ((M + 15) // 16, K // 64, 512)
+
+        ws_bytes = max([cr.w4a4_gemm_workspace_size(l.N, l.K, cr.LAYOUT.F6, cr.LAYOUT.TILED)
+                        for l in w.linears if l.fmt in ("w4a4", "w4a4_g64")] + [16])
+        self.sets = []
+        for si in range(nsets):
+            st = {"acts": {k: (v if si == 0 else v.clone()) for k, v in acts.items()},
+                  "prep": {k: {kk: (vv if si == 0 else vv.clone()) for kk, vv in d.items()} for k, d in prep.items()},
+                  "gws": torch.empty(ws_bytes, dtype=torch.uint8, device=dev), "rq": {}}
+            for key in self.rq_plan:
+                x_id, kind, lname = key
+                M, K = w.acts[x_id][0], w.acts[x_id][1]
+                rq_ws = lambda q: torch.empty(max(16, cr.convrot_rq_workspace_size(M, K, rot, q, 0)),  # noqa: E731
+                                              dtype=torch.uint8, device=dev)
+                if kind == "int4_tensor":
+                    o = dict(codes=torch.empty(c4_shape(M, K), dtype=torch.uint8, device=dev),
+                             scales=torch.empty(1, dtype=torch.float32, device=dev), ws=rq_ws(0))
+                elif kind == "int8_tensor":
+                    o = dict(codes=torch.empty((M, K), dtype=torch.int8, device=dev),
+                             scales=torch.empty(1, dtype=torch.float32, device=dev), ws=rq_ws(1))
+                elif kind == "dual_tensor":
+                    o = dict(codes=torch.empty(c4_shape(M, K), dtype=torch.uint8, device=dev),
+                             scales=torch.empty(1, dtype=torch.float32, device=dev),
+                             codes8=torch.empty((M, K), dtype=torch.int8, device=dev),
+                             scales8=torch.empty(1, dtype=torch.float32, device=dev), ws=rq_ws(0))
+                elif kind in ("int8_row", "int8_row_f16"):
+                    o = dict(codes=torch.empty((M, K), dtype=torch.float16 if kind == "int8_row_f16" else torch.int8,
+                                               device=dev),
+                             scales=torch.empty(M, dtype=torch.float32, device=dev), ws=None)
+                else:
+                    o = dict(codes=torch.empty(c4_shape(M, K), dtype=torch.uint8, device=dev),
+                             scales=torch.empty((M, K // 64), dtype=torch.float32, device=dev), ws=None,
+                             la=torch.empty((M, 32), dtype=torch.bfloat16, device=dev))
+                st["rq"][key] = o
+            st["out"] = {lin.name: torch.empty((lin.M, lin.N), dtype=torch.bfloat16, device=dev) for lin in w.linears}
+            self.sets.append(st)
+        del acts, prep
+        torch.cuda.synchronize()
+
+        self.order = []          # (label, fn(set index)): every RQ right before the first GEMM that reads it
+        done = set()
+        for lin, key in self.gemm_plan:
+            if key not in done:
+                self.order.append((f"rq:{key[0]}:{key[1]}", lambda si, k=key: self.launch_rq(si, k)))
+                done.add(key)
+            self.order.append((f"gemm:{lin.name}", lambda si, l=lin, k=key: self.launch_gemm(si, l, k)))
+
+    # ------------------------------------------------------------------
+    def _lay4(self, M):
+        return self.cr.LAYOUT.F6 if self.f6_codes(M) else self.cr.LAYOUT.TILED
+
+    def launch_rq(self, si, key):
+        cr = self.cr
+        x_id, kind, lname = key
+        st = self.sets[si]
+        o, x = st["rq"][key], st["acts"][x_id]
+        M = x.shape[0]
+        if kind == "int4_tensor":
+            cr.convrot_rotate_quantize(x, self.rot, cr.Q.SYM_INT4, cr.GRAN.TENSOR, layout=self._lay4(M),
+                                       codes=o["codes"], scales=o["scales"], workspace=o["ws"])
+        elif kind == "int8_tensor":
+            cr.convrot_rotate_quantize(x, self.rot, cr.Q.SYM_INT8, cr.GRAN.TENSOR, codes=o["codes"],
+                                       scales=o["scales"], workspace=o["ws"])
+        elif kind == "dual_tensor":
+            cr.convrot_rotate_quantize_dual(x, self.rot, layout4=self._lay4(M), codes4=o["codes"],
+                                            scale4=o["scales"], codes8=o["codes8"], scale8=o["scales8"],
+                                            workspace=o["ws"])
+        elif kind in ("int8_row", "int8_row_f16"):
+            cr.convrot_rotate_quantize(x, 256, cr.Q.SYM_INT8, cr.GRAN.ROW, codes=o["codes"], scales=o["scales"],
+                                       layout=cr.LAYOUT.F16 if kind == "int8_row_f16" else cr.LAYOUT.NATURAL)
+        else:
+            lin = [l for l in self.w.linears if l.name == lname][0]
+            uns = kind == "u4_g64"
+            cr.convrot_rotate_quantize(x, 0, cr.Q.UNSIGNED_INT4_SHIFT if uns else cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP,
+                                       64, shift=lin.unsigned_shift, lora_down=st["prep"][lname]["l2"],
+                                       layout=self._lay4(M), codes=o["codes"], scales=o["scales"],
+                                       lora_act=o["la"])
+
+    def launch_gemm(self, si, lin, key, w_override=None):
+        """w_override: (weights, w_layout) to run the GEMM kernel on weights
+        already expanded to fp6 fragments (timing of the GEMM kernel alone)."""
+        cr = self.cr
+        st = self.sets[si]
+        o, p, y = st["rq"][key], st["prep"][lin.name], st["out"][lin.name]
+        M, N, K = lin.M, lin.N, lin.K
+        wq, wlay = (p["w"], cr.LAYOUT.TILED) if w_override is None else w_override
+        if lin.fmt == "w4a4":
+            cr.w4a4_gemm(o["codes"], o["scales"], 0, wq, p["ws"], 0, M, N, K, out=y, w_layout=wlay,
+                         workspace=st["gws"])
+        elif lin.fmt == "a8w4":
+            cr.w4a4_gemm(o["codes"], o["scales"], cr.GRAN.ROW, p["w"], p["ws"], 0, M, N, K, out=y,
+                         a_layout=cr.LAYOUT.INT8)
+        elif lin.fmt == "int8":
+            a8, s8 = (o["codes8"], o["scales8"]) if "codes8" in o else (o["codes"], o["scales"])
+            cr.int8_tensorwise_gemm(a8, s8, p["w"], p["ws"], M, N, K, out=y)
+        elif lin.fmt == "w4a8":
+            cr.w4a8_gemm(o["codes"], o["scales"], cr.GRAN.ROW, p["w"], p["ws"], p["wz"], M, N, K, out=y)
+        else:
+            cr.w4a4_gemm(o["codes"], o["scales"], 2, wq, p["ws"], 2, M, N, K,
+                         a_unsigned=lin.unsigned_shift != 0.0, a_shift=lin.unsigned_shift, w_sum=p["wsum"],
+                         lora_act=o["la"], lora_up=p["l1"], out=y, w_layout=wlay, workspace=st["gws"])
+
+    # ------------------------------------------------------------------
+    def step(self, i):
+        for _, fn in self.order:
+            fn(i % self.nsets)
+
+    def _events(self, n):
+        return [self.torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    def time_steps(self, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        e0, e1 = self._events(2)
+        e0.record(self.stream)
+        for i in range(steps):
+            self.step(i)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def per_call(self, reps):
+        """mean us of every call inside whole steps (events around each call)."""
+        np, torch = self.np, self.torch
+        per = {lab: [] for lab, _ in self.order}
+        for r in range(reps):
+            ev = self._events(len(self.order) + 1)
+            ev[0].record(self.stream)
+            for i, (_, fn) in enumerate(self.order):
+                fn(r % self.nsets)
+                ev[i + 1].record(self.stream)
+            torch.cuda.synchronize()
+            for i, (lab, _) in enumerate(self.order):
+                per[lab].append(ev[i].elapsed_time(ev[i + 1]) * 1e3)
+        return {lab: float(np.mean(v)) for lab, v in per.items()}
+
+    def back_to_back(self, fn, reps):
+        """mean us of fn(set index) launched reps times back to back over the sets."""
+        torch = self.torch
+        for i in range(2):
+            fn(i % self.nsets)
+        torch.cuda.synchronize()
+        e0, e1 = self._events(2)
+        e0.record(self.stream)
+        for i in range(reps):
+            fn(i % self.nsets)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    def gemm_kernel_fn(self, lin):
+        """fn(set index) launching the GEMM kernel of layer `lin` alone. For a
+        W4A4 layer on fp6 codes the weights are first expanded into each
+        set's workspace by an ordinary call; the returned fn then runs the
+        call on those fp6 fragments (no expansion pass)."""
+        cr = self.cr
+        key = [k for l, k in self.gemm_plan if l.name == lin.name][0]
+        for si in range(self.nsets):
+            self.launch_rq(si, key)
+        if lin.fmt not in ("w4a4", "w4a4_g64") or not self.f6_codes(lin.M):
+            return lambda si: self.launch_gemm(si, lin, key)
+        exp = []
+        for si in range(self.nsets):
+            self.launch_gemm(si, lin, key)     # fills set si's workspace with the expanded weights
+            n = (lin.N // 32) * (lin.K // 64) * 1536
+            exp.append(self.sets[si]["gws"][:n].view(lin.N // 32, lin.K // 64, 1536))
+        self.torch.cuda.synchronize()
+        return lambda si: self.launch_gemm(si, lin, key, (exp[si], cr.LAYOUT.F6))
+
+    def gemm_kernel_alone(self, lin, reps):
+        """mean us of the GEMM kernel of layer `lin` alone, back to back."""
+        return self.back_to_back(self.gemm_kernel_fn(lin), reps)
+
+    def ops(self):
+        return sum(2.0 * l.M * l.N * l.K for l in self.w.linears)
+
+
+def run(name, steps, warmup, cores="fp6"):
+    """One JSON line for workload `name` (bench.py --workload NAME)."""
+    if name == "merge":
+        return run_merge(steps, warmup)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(3)
+    r = Runner(name, cores)
+    ms = r.time_steps(steps, warmup)
+    kern = r.per_call(max(3, steps // 2))
+    layers = {}
+    for lin, _ in r.gemm_plan:
+        us = kern[f"gemm:{lin.name}"]
+        d = {"us": round(us, 2), "TOPS": round(2.0 * lin.M * lin.N * lin.K / us / 1e6, 1),
+             "GBps": round(gemm_bytes(lin) / us / 1e3, 1)}
+        layers[lin.name] = d
+    rqs = {}
+    for key in r.rq_plan:
+        x_id, kind, _ = key
+        M, K = r.w.acts[x_id][0], r.w.acts[x_id][1]
+        us = kern[f"rq:{x_id}:{kind}"]
+        rqs[f"{x_id}:{kind}"] = {"us": round(us, 2), "GBps": round(rq_bytes(M, K, kind) / us / 1e3, 1)}
+    dom = max(layers, key=lambda n: layers[n]["us"])
+    eff = r.ops() / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "effective TOPS of fused rotate+quant+W4 GEMM (% INT8 MFMA peak); GB/s",
+        "value": round(eff, 2), "unit": "TOPS", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4 / int8 codes (exact integer products)", "data": "synthetic",
+        "config": {"workload": r.w.name, "layers": len(r.w.linears), "total_GOP": round(r.ops() / 1e9, 1),
+                   "w4a4_matrix_cores": cores, "buffer_sets": r.nsets},
+        "pct_int8_peak": round(100.0 * eff / INT8_PEAK_TOPS, 2),
+        "gemm": layers, "rotate_quantize": rqs,
+        "dominant_gemm": {"layer": dom, **layers[dom]},
+        "setup_s": round(r.setup_s, 1),
+    }))
 
 
 def run_merge(steps, warmup):
@@ -77,209 +402,10 @@ def run_merge(steps, warmup):
     ms = e0.elapsed_time(e1) / steps
     # bytes: codes + scales + zeros in, bf16 weight out and back in, new codes/scales/zeros, packed set
     q_bytes = N * K // 2 + N * K // 16 * 2 + N * K // 32
-    moved = q_bytes + 2 * N * K + 2 * N * K + q_bytes + (N * K // 2 + N * K // 16 * 3 + 4 * N) + R * (N + K) * 2
+    moved = q_bytes + 2 * N * K + 2 * N * K + q_bytes + (N * K // 2 + N * K // 16 * 3) + R * (N + K) * 2
     print(json.dumps({
         "metric": "LoRA merge into a quantized weight (dequantize + rank-64 delta + requantize + pack)",
         "value": round(ms, 4), "unit": "ms per merge", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "higher_is_better": False, "data": "synthetic",
         "config": {"workload": "W4A8 asym g16 weight 12288x3072, ConvRot 256, LoRA rank 64"},
         "GBps": round(moved / ms / 1e6, 1)}))
-
-
-def run(name, steps, warmup, cores="fp6"):
-    """cores: matrix cores of the W4A4 layers (per-tensor and 64-group),
-    "fp6" (E2M3 fragments) or "int8" (tile-packed int4 widened to bytes)."""
-    if name == "merge":
-        return run_merge(steps, warmup)
-    import numpy as np
-    import torch
-    import w4a8_rotated_quantized_amd as cr
-    import workloads as wl
-
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        sys.exit(3)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
-    w = wl.CONFIGS[name]()
-    rq_plan, gemm_plan = _plan(w)
-    f6 = cores == "fp6"
-
-    def bf16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    t0 = time.time()
-    acts = {x: bf16(wl.act_bits(w, x)) for x in w.acts}
-    # offline weight preparation and the low-rank factors
-    prep = {}
-    for lin in w.linears:
-        N, K = lin.N, lin.K
-        if lin.fmt in ("w4a4", "a8w4"):
-            wc, ws, _, _ = cr.convrot_rotate_quantize(bf16(wl.weight_bits(w, lin)), 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
-            if lin.fmt == "w4a4" and f6:
-                prep[lin.name] = dict(w=cr.w4_pack_weights_f6(wc, N, K), ws=ws)
-            else:
-                prep[lin.name] = dict(w=cr.w4_pack_weights(wc, ws, N, K)[0], ws=ws)
-        elif lin.fmt == "int8":
-            wc, ws, _, _ = cr.convrot_rotate_quantize(bf16(wl.weight_bits(w, lin)), 256, cr.Q.SYM_INT8, cr.GRAN.TENSOR)
-            prep[lin.name] = dict(w=wc, ws=ws)
-        elif lin.fmt == "w4a8":
-            wc, ws, wz, _ = cr.convrot_rotate_quantize(bf16(wl.weight_bits(w, lin)), 256, cr.Q.ASYM_UINT4,
-                                                       cr.GRAN.ROW_GROUP, 16)
-            p, ps, pz, _ = cr.w4_pack_weights(wc, ws, N, K, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16, zeros=wz)
-            prep[lin.name] = dict(w=p, ws=ps, wz=pz)
-        else:
-            l1, l2, r = wl.lowrank_bits(w, lin)
-            wc, ws, _, _ = cr.convrot_rotate_quantize(bf16(r), 0, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64)
-            p, ps, _, wsum = cr.w4_pack_weights(wc, ws, N, K, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64, want_wsum=True)
-            if f6:
-                p = cr.w4_pack_weights_f6(wc, N, K)
-            prep[lin.name] = dict(w=p, ws=ps, wsum=wsum, l1=bf16(l1), l2=bf16(l2))
-    torch.cuda.synchronize()
-    setup_s = time.time() - t0
-
-    # RQ outputs, allocated once; per-tensor INT4 codes in the layout of the cores used
-    lay4 = cr.LAYOUT.F6 if f6 else cr.LAYOUT.TILED
-
-    def c4_shape(M, K):
-        return ((M + 31) // 32, K // 64, 1536) if f6 else ((M + 15) // 16, K // 64, 512)
-
-    rq_out = {}
-    for key in rq_plan:
-        x_id, kind, lname = key
-        M, K = w.acts[x_id][0], w.acts[x_id][1]
-        x = acts[x_id]
-        if kind == "int4_tensor":
-            o = dict(codes=torch.empty(c4_shape(M, K), dtype=torch.uint8, device=dev),
-                     scales=torch.empty(1, dtype=torch.float32, device=dev),
-                     ws=torch.empty(cr.convrot_rq_workspace_size(M, K, 256, 0, 0), dtype=torch.uint8, device=dev))
-        elif kind == "int8_tensor":
-            o = dict(codes=torch.empty((M, K), dtype=torch.int8, device=dev),
-                     scales=torch.empty(1, dtype=torch.float32, device=dev),
-                     ws=torch.empty(cr.convrot_rq_workspace_size(M, K, 256, 1, 0), dtype=torch.uint8, device=dev))
-        elif kind == "dual_tensor":
-            o = dict(codes=torch.empty(c4_shape(M, K), dtype=torch.uint8, device=dev),
-                     scales=torch.empty(1, dtype=torch.float32, device=dev),
-                     codes8=torch.empty((M, K), dtype=torch.int8, device=dev),
-                     scales8=torch.empty(1, dtype=torch.float32, device=dev),
-                     ws=torch.empty(cr.convrot_rq_workspace_size(M, K, 256, 0, 0), dtype=torch.uint8, device=dev))
-        elif kind in ("int8_row", "int8_row_f16"):
-            o = dict(codes=torch.empty((M, K), dtype=torch.float16 if kind == "int8_row_f16" else torch.int8,
-                                       device=dev),
-                     scales=torch.empty(M, dtype=torch.float32, device=dev), ws=None)
-        else:
-            o = dict(codes=torch.empty(c4_shape(M, K), dtype=torch.uint8, device=dev),
-                     scales=torch.empty((M, K // 64), dtype=torch.float32, device=dev), ws=None,
-                     la=torch.empty((M, 32), dtype=torch.bfloat16, device=dev))
-        rq_out[key] = o
-    outs = {lin.name: torch.empty((lin.M, lin.N), dtype=torch.bfloat16, device=dev) for lin in w.linears}
-
-    def launch_rq(key):
-        x_id, kind, lname = key
-        o, x = rq_out[key], acts[x_id]
-        if kind == "int4_tensor":
-            cr.convrot_rotate_quantize(x, 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR, layout=lay4,
-                                       codes=o["codes"], scales=o["scales"], workspace=o["ws"])
-        elif kind == "int8_tensor":
-            cr.convrot_rotate_quantize(x, 256, cr.Q.SYM_INT8, cr.GRAN.TENSOR, codes=o["codes"],
-                                       scales=o["scales"], workspace=o["ws"])
-        elif kind == "dual_tensor":
-            cr.convrot_rotate_quantize_dual(x, 256, layout4=lay4, codes4=o["codes"], scale4=o["scales"],
-                                            codes8=o["codes8"], scale8=o["scales8"], workspace=o["ws"])
-        elif kind in ("int8_row", "int8_row_f16"):
-            cr.convrot_rotate_quantize(x, 256, cr.Q.SYM_INT8, cr.GRAN.ROW, codes=o["codes"], scales=o["scales"],
-                                       layout=cr.LAYOUT.F16 if kind == "int8_row_f16" else cr.LAYOUT.NATURAL)
-        else:
-            lin = [l for l in w.linears if l.name == lname][0]
-            uns = kind == "u4_g64"
-            cr.convrot_rotate_quantize(x, 0, cr.Q.UNSIGNED_INT4_SHIFT if uns else cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP,
-                                       64, shift=lin.unsigned_shift, lora_down=prep[lname]["l2"],
-                                       layout=lay4, codes=o["codes"], scales=o["scales"],
-                                       lora_act=o["la"])
-
-    def launch_gemm(lin, key):
-        o, p, y = rq_out[key], prep[lin.name], outs[lin.name]
-        M, N, K = lin.M, lin.N, lin.K
-        if lin.fmt == "w4a4":
-            cr.w4a4_gemm(o["codes"], o["scales"], 0, p["w"], p["ws"], 0, M, N, K, out=y)
-        elif lin.fmt == "a8w4":
-            cr.w4a4_gemm(o["codes"], o["scales"], cr.GRAN.ROW, p["w"], p["ws"], 0, M, N, K, out=y,
-                         a_layout=cr.LAYOUT.INT8)
-        elif lin.fmt == "int8":
-            a8, s8 = (o["codes8"], o["scales8"]) if "codes8" in o else (o["codes"], o["scales"])
-            cr.int8_tensorwise_gemm(a8, s8, p["w"], p["ws"], M, N, K, out=y)
-        elif lin.fmt == "w4a8":
-            cr.w4a8_gemm(o["codes"], o["scales"], cr.GRAN.ROW, p["w"], p["ws"], p["wz"], M, N, K, out=y)
-        else:
-            cr.w4a4_gemm(o["codes"], o["scales"], 2, p["w"], p["ws"], 2, M, N, K,
-                         a_unsigned=lin.unsigned_shift != 0.0, a_shift=lin.unsigned_shift, w_sum=p["wsum"],
-                         lora_act=o["la"], lora_up=p["l1"], out=y)
-
-    order = []   # (label, fn): every RQ right before the first GEMM that reads it
-    done = set()
-    for lin, key in gemm_plan:
-        if key not in done:
-            order.append((f"rq:{key[0]}:{key[1]}", lambda k=key: launch_rq(k)))
-            done.add(key)
-        order.append((f"gemm:{lin.name}", lambda l=lin, k=key: launch_gemm(l, k)))
-
-    def step():
-        for _, fn in order:
-            fn()
-
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-
-    per = {lab: [] for lab, _ in order}
-    for _ in range(max(3, steps // 2)):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 1)]
-        ev[0].record(stream)
-        for i, (_, fn) in enumerate(order):
-            fn()
-            ev[i + 1].record(stream)
-        torch.cuda.synchronize()
-        for i, (lab, _) in enumerate(order):
-            per[lab].append(ev[i].elapsed_time(ev[i + 1]) * 1e3)
-    kern = {lab: round(float(np.mean(v)), 2) for lab, v in per.items()}
-
-    ops = sum(2.0 * l.M * l.N * l.K for l in w.linears)
-    layers = {}
-    for lin, _ in gemm_plan:
-        us = kern[f"gemm:{lin.name}"]
-        d = {"us": us, "TOPS": round(2.0 * lin.M * lin.N * lin.K / us / 1e6, 1)}
-        if lin.M <= 64:
-            wbytes = lin.N * lin.K // (1 if lin.fmt == "int8" else 2)
-            d["weight_GBps"] = round(wbytes / us / 1e3, 1)
-        layers[lin.name] = d
-    rqs = {}
-    for key in rq_plan:
-        x_id, kind, _ = key
-        M, K = w.acts[x_id][0], w.acts[x_id][1]
-        us = kern[f"rq:{x_id}:{kind}"]
-        code_b = 1.0 if kind.startswith("int8") else 0.5      # algorithmic: 8 or 4 bits per code
-        out_b = M * K * code_b + (M * K if kind == "dual_tensor" else 0)
-        rqs[f"{x_id}:{kind}"] = {"us": us, "GBps": round((M * K * 2 + out_b) / us / 1e3, 1)}
-    dom = max(layers, key=lambda n: layers[n]["us"])
-    eff = ops / (ms * 1e-3) / 1e12
-    line = {
-        "metric": "effective TOPS of fused rotate+quant+W4 GEMM (% INT8 MFMA peak); GB/s",
-        "value": round(eff, 2), "unit": "TOPS", "n_gpus": 1, "steps": steps, "warmup": warmup,
-        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int4" if name not in ("c3", "c2a8") else "int8/int4", "data": "synthetic",
-        "config": {"workload": w.name, "layers": len(w.linears), "total_GOP": round(ops / 1e9, 1),
-                   "w4a4_matrix_cores": cores},
-        "pct_int8_peak": round(100.0 * eff / INT8_PEAK_TOPS, 2),
-        "gemm": layers, "rotate_quantize": rqs,
-        "dominant_gemm": {"layer": dom, **layers[dom], "frac_int8_peak": round(layers[dom]["TOPS"] / INT8_PEAK_TOPS, 4)},
-        "setup_s": round(setup_s, 1),
-    }
-    print(json.dumps(line))

@@ -103,7 +103,7 @@ typedef enum cr_layout {
                           /* l (0..63) of a fragment covers row 32b + l%32 and columns          */
                           /* 64kt + 32(l/32) + i, i = 0..31, field i at bits 6i..6i+5 of its 24 */
                           /* bytes, bytes 0..15 at l*16 and bytes 16..23 at 1024 + l*8. Input   */
-                          /* of the fp6 matrix-core W4A4 GEMM (weights from w4_pack_weights_f6);*/
+                          /* of the fp6 matrix-core W4A4 GEMM (its weights in the same layout)  */
                           /* rows past `rows` in the last block hold unspecified codes (any     */
                           /* 6-bit field is a finite value; allocate ceil(rows/32)*32 rows)      */
   CR_LAYOUT_F16 = 4       /* SYM_INT8 codes as IEEE fp16 values [rows, K] row-major (every code */
@@ -316,33 +316,38 @@ cr_status convrot_dequantize_weights(const void* codes, const void* scales, cons
                                      void* out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * w4a4_gemm - INT4 activations x tile-packed INT4 weights on int8 matrix
- * cores (exact int4 -> int8 widening, int32 accumulation) with a fused
- * epilogue.
+ * w4a4_gemm - INT4 activations x tile-packed INT4 weights with a fused
+ * epilogue, on the int8 matrix cores (exact int4 -> int8 widening, int32
+ * accumulation) or on the fp6 matrix cores (int4 codes carried as exact
+ * E2M3 values, exact float32 sums).
  *
- * Cites: "Qwen-Image-Edit-2511 - INT4 tensorwise W4A4" page, Measurements
- * (fused rotation + INT4 matmul with a rank-one scale); "Qwen-Image-Edit-2511
- * INT4 (ComfyUI Optimized)", Fused LoRA-Up Epilogue, Kernel Engineering
- * (unsigned shifted activations, scale staging).
+ * Cites: "Qwen-Image-Edit-2511 - INT4 tensorwise W4A4" page, intro (packed
+ * signed INT4 weights, two per byte) and Measurements (fused rotation + INT4
+ * matmul with a rank-one scale); "Qwen-Image-Edit-2511 INT4 (ComfyUI
+ * Optimized)", Tile-Packed Weight Format, Fused LoRA-Up Epilogue, Kernel
+ * Engineering (unsigned shifted activations, scale staging).
  *
  *   a_codes     int4 codes (signed, or unsigned when a_unsigned) in a_layout:
- *               CR_LAYOUT_TILED (fast path) or CR_LAYOUT_NATURAL [M, K/2];
- *               or CR_LAYOUT_INT8: int8 codes [M, K] (SYM_INT8, TENSOR or ROW
- *               scales), the 8-bit-activation branch for these weights
+ *               CR_LAYOUT_TILED or CR_LAYOUT_NATURAL [M, K/2] (int8 matrix
+ *               cores); CR_LAYOUT_INT8: int8 codes [M, K] (SYM_INT8, TENSOR or
+ *               ROW scales), the 8-bit-activation branch for these weights
  *               ("Qwen3-4B ConvRot W4A4" page, INT8 branch comparison): no
  *               a_unsigned, no 64-group scales and no low-rank branch with it;
- *               or CR_LAYOUT_F6: fp6 E2M3 fragments (signed codes, or
- *               unsigned codes as u/2) with w_packed from w4_pack_weights_f6,
- *               run on the fp6 matrix cores (the products and their float32
- *               sums are exact, so the int32 output equals the int8-core
- *               path's): a_unsigned and the low-rank branch need ROW_GROUP(64)
- *               scales on both sides (w_scales and w_sum then come from
- *               w4_pack_weights with ROW_GROUP(64)); TENSOR / ROW scales take
+ *               CR_LAYOUT_F6: fp6 E2M3 fragments (signed codes, or unsigned
+ *               codes as u/2), run on the fp6 matrix cores (the products and
+ *               their float32 sums are exact, so the int32 output equals the
+ *               int8-core path's): a_unsigned and the low-rank branch need
+ *               ROW_GROUP(64) scales on both sides; TENSOR / ROW scales take
  *               signed codes and no low-rank branch
  *   a_scales    float32: TENSOR [1], ROW [M], ROW_GROUP(64) [M, K/64]
  *   a_unsigned  1 for UNSIGNED_INT4_SHIFT codes: y -= a_shift * w_sum[n]
- *   w_packed    from w4_pack_weights (SYM_INT4); from w4_pack_weights_f6
- *               with CR_LAYOUT_F6 activations
+ *   w_packed    w_layout CR_LAYOUT_TILED: the tile-packed INT4 weights of
+ *               w4_pack_weights (SYM_INT4, 4 bits per code), with any a_layout.
+ *               With CR_LAYOUT_F6 codes the call first expands the tiles into
+ *               fp6 fragments in `workspace` (one streaming pass, enqueued on
+ *               `stream` before the GEMM) and runs the fp6 GEMM on them.
+ *               w_layout CR_LAYOUT_F6: fragments already expanded by
+ *               w4_pack_weights_f6 (6 bits per code; CR_LAYOUT_F6 codes only)
  *   w_scales    TENSOR [1], ROW [N], ROW_GROUP(64): packed [N/128][K/64][128]
  *   scale pairs: (TENSOR|ROW) x (TENSOR|ROW), or ROW_GROUP x ROW_GROUP (group 64)
  *   w_sum       float32 [N], required iff a_unsigned
@@ -351,15 +356,20 @@ cr_status convrot_dequantize_weights(const void* codes, const void* scales, cons
  *   bias        optional bf16 [N]
  *   out         CR_OUT_BF16: bf16 [M, ldc]; CR_OUT_F32: float32; CR_OUT_I32_RAW:
  *               int32 sum_k qa*qw (lora/bias/scales ignored)
+ *   workspace   at least w4a4_gemm_workspace_size(N, K, a_layout, w_layout)
+ *               bytes (nonzero only for CR_LAYOUT_F6 codes with CR_LAYOUT_TILED
+ *               weights), 16-byte aligned; its contents are overwritten. Calls
+ *               sharing a workspace must be ordered on one stream.
  * Epilogue: y = s_a s_w acc  (or sum_g a_s[m,g] w_s[n,g] P[m,n,g]) - shift
  * term + low-rank + bias, evaluated in float32, stored once.
  * Shape: M >= 1, N % 128 == 0, K % 128 == 0, K <= 32768, ldc >= N (ldc % 8 == 0),
  * M*K/2 and N*K/2 below 2^32 bytes.
- * workspace: unused (pass NULL, 0).
  */
+size_t w4a4_gemm_workspace_size(int64_t N, int64_t K, cr_layout a_layout, cr_layout w_layout);
+
 cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scales, cr_gran a_gran,
                     int a_unsigned, float a_shift,
-                    const void* w_packed, const float* w_scales, cr_gran w_gran,
+                    const void* w_packed, cr_layout w_layout, const float* w_scales, cr_gran w_gran,
                     const float* w_sum,
                     const void* lora_act, int lora_act_f32, const void* lora_up, int R,
                     const void* bias,

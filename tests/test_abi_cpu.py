@@ -196,9 +196,11 @@ def test_pack_validation(cr):
 
 
 def _w4a4(cr, a=A, ag=0, wg=0, uns=0, wsum=None, la=None, lu=None, R=0, out=A, ot=0, ldc=256,
-          M=64, N=256, K=512, layout=1):
-    return cr.lib.w4a4_gemm(_p(a), layout, _p(A), ag, uns, 0.0, _p(A), _p(A), wg, _p(wsum), _p(la), 0, _p(lu), R,
-                            None, _p(out), ot, ldc, M, N, K, None, 0, None)
+          M=64, N=256, K=512, layout=1, wlayout=None, ws=None, wsb=0):
+    if wlayout is None:
+        wlayout = 3 if layout == 3 else 1
+    return cr.lib.w4a4_gemm(_p(a), layout, _p(A), ag, uns, 0.0, _p(A), wlayout, _p(A), wg, _p(wsum), _p(la), 0,
+                            _p(lu), R, None, _p(out), ot, ldc, M, N, K, _p(ws), wsb, None)
 
 
 def test_gemm_validation(cr):
@@ -214,6 +216,17 @@ def test_gemm_validation(cr):
     assert _w4a4(cr, la=A, lu=A, R=64) == 4
     assert _w4a4(cr, ot=5) == 1
     assert _w4a4(cr, layout=5) == 1
+    # fp6 codes with int4 tile-packed weights: expanded in the workspace first
+    need = cr.w4a4_gemm_workspace_size(256, 512, 3, 1)
+    assert need == (256 // 32) * (512 // 64) * 1536
+    assert cr.w4a4_gemm_workspace_size(256, 512, 1, 1) == 0
+    assert cr.w4a4_gemm_workspace_size(256, 512, 3, 3) == 0
+    assert _w4a4(cr, layout=3, wlayout=1) == 1                # workspace missing
+    assert _w4a4(cr, layout=3, wlayout=1, ws=A, wsb=need - 16) == 6
+    assert _w4a4(cr, layout=3, wlayout=1, ws=A + 8, wsb=need) == 1
+    assert _w4a4(cr, layout=3, wlayout=1, ws=A, wsb=need) == 4
+    assert _w4a4(cr, layout=1, wlayout=3) == 3                # fp6 weights need fp6 codes
+    assert _w4a4(cr, layout=1, wlayout=2) == 1
     assert _w4a4(cr, layout=3) == 4                          # fp6 fragments, tensor scales
     assert _w4a4(cr, layout=3, ag=1, wg=1) == 4
     assert _w4a4(cr, layout=3, ag=2, wg=2) == 4              # fp6 with 64-group scales

@@ -1,17 +1,19 @@
-"""Host-side checks of the benchmark contract: one GPU only, and the
-committed HBM-traffic summaries that bench.py reads for roofline.traffic
-are self-consistent (no GPU needed)."""
+"""Host-side checks of the benchmark contract: one GPU only, algorithmic
+bytes counted at the codes' bit width, and the committed HBM-traffic
+summaries that bench.py reads for roofline.traffic self-consistent (no GPU
+needed)."""
+import glob
 import json
 import os
 import subprocess
 import sys
 
-import pytest
-
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
+import bench_workloads as bw  # noqa: E402
+import workloads as wl  # noqa: E402
 
 
 def test_bench_refuses_more_than_one_gpu():
@@ -21,23 +23,47 @@ def test_bench_refuses_more_than_one_gpu():
     assert "one GPU" in r.stderr
 
 
-@pytest.mark.parametrize("cores", ["fp6", "int8"])
-def test_traffic_profiles_consistent(cores):
-    with open(os.path.join(ROOT, "profiles", bench.TRAFFIC_PROFILE[cores])) as f:
-        d = json.load(f)
-    M, N, K = 4096, 3072, 3072
-    code_bytes = 0.75 if cores == "fp6" else 0.5
-    # algorithmic bytes: activation codes + packed weights + bf16 output
-    assert d["algorithmic_bytes_per_launch"] == int(M * K * code_bytes + N * K * code_bytes + 2 * M * N)
-    assert d["hbm_bytes_per_launch"] == d["fetch_bytes_per_launch"] + d["write_bytes_per_launch"]
-    # every launch writes at least its bf16 output and reads at least its operands once
-    assert d["write_bytes_per_launch"] >= 0.99 * 2 * M * N
-    assert d["fetch_bytes_per_launch"] >= 0.99 * (M * K + N * K) * code_bytes
-    assert len(d["source_sha"]) == 16
-    # bench.py uses the summary only while the kernel sources hash the same
-    bench.CORES = cores
-    t = bench.traffic_from_profile()
-    if d["source_sha"] == bench.source_sha(bench.GEMM_SOURCES[cores]):
-        assert t == d["hbm_bytes_per_launch"]
-    else:
-        assert t is None
+def test_algorithmic_bytes_at_code_width():
+    M, K, N = 4096, 3072, 3072
+    # rotate+quantize: bf16 in, 4 or 8 bits per code out, plus the scales
+    assert bw.rq_bytes(M, K, "int4_tensor") == 2 * M * K + M * K // 2 + 4
+    assert bw.rq_bytes(M, K, "int8_tensor") == 2 * M * K + M * K + 4
+    assert bw.rq_bytes(M, K, "dual_tensor") == 2 * M * K + M * K // 2 + M * K + 8
+    assert bw.rq_bytes(M, K, "int8_row_f16") == 2 * M * K + M * K + 4 * M
+    # GEMM: codes and weights at 4 bits (INT4) or 8 bits (INT8), bf16 output
+    lin = wl.LinearSpec("p", "w4a4", M, N, K, "x")
+    assert bw.gemm_bytes(lin) == M * K // 2 + N * K // 2 + 2 * M * N
+    lin8 = wl.LinearSpec("p", "int8", M, N, K, "x")
+    assert bw.gemm_bytes(lin8) == M * K + N * K + 2 * M * N
+
+
+def test_c4_plan_matches_the_recipe():
+    # 14 linears; W4A4: q, k, mlp_up, mlp_down; INT8: v, out, mod (both streams);
+    # the attention input is quantized once for the INT4 and INT8 layers
+    w = wl.CONFIGS["c4"]()
+    rq, gemms = bw.plan(w)
+    assert len(gemms) == 14
+    fmts = {l.name: l.fmt for l in w.linears}
+    for s in ("img", "txt"):
+        assert [fmts[f"{s}_{n}"] for n in ("q", "k", "mlp_up", "mlp_down")] == ["w4a4"] * 4
+        assert [fmts[f"{s}_{n}"] for n in ("v", "out", "mod")] == ["int8"] * 3
+        assert (f"{s}_attn", "dual_tensor", "") in rq
+    assert abs(sum(2.0 * l.M * l.N * l.K for l in w.linears) / 1e9 - 1971.8) < 0.1
+
+
+def test_traffic_profiles_consistent():
+    for p in glob.glob(os.path.join(ROOT, "profiles", "*_traffic.json")):
+        with open(p) as f:
+            d = json.load(f)
+        assert d["hbm_bytes_per_launch"] == d["fetch_bytes_per_launch"] + d["write_bytes_per_launch"]
+        M, N, K = d["M"], d["N"], d["K"]
+        lin = wl.LinearSpec(d["layer"], d["fmt"], M, N, K, "x")
+        assert d["algorithmic_bytes_per_launch"] == int(bw.gemm_bytes(lin))
+        # every launch writes at least its bf16 output and reads at least its operands once
+        assert d["write_bytes_per_launch"] >= 0.99 * 2 * M * N
+        assert len(d["source_sha"]) == 16
+        cores = d["cores"]
+        if d["source_sha"] == bench.source_sha(bench.GEMM_SOURCES[cores]):
+            assert bench.traffic_from_profile(cores, d["layer"]) == d["hbm_bytes_per_launch"]
+        else:
+            assert bench.traffic_from_profile(cores, d["layer"]) is None

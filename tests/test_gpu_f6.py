@@ -127,6 +127,15 @@ def test_w4a4_f6_gemm(cr, case):
     wt = dev(wp["tiles"].reshape(-1))
     yf8 = cr.w4a4_gemm(at, sa, GR[ag], wt, sw, GR[wg], M, N, K, out_type=1)
     assert np.array_equal(host(yf).view(np.uint32), host(yf8).view(np.uint32))
+    # fp6 codes against the 4-bit tile-packed weights (expanded by the call in
+    # its workspace): the same results bit for bit
+    assert cr.w4a4_gemm_workspace_size(N, K, F6, 1) == (N // 32) * (K // 64) * 1536
+    raw_t = cr.w4a4_gemm(a, sa, GR[ag], wt, sw, GR[wg], M, N, K, out_type=2)
+    assert np.array_equal(host(raw_t).astype(np.int64), ref["raw"])
+    ws = torch.full((cr.w4a4_gemm_workspace_size(N, K, F6, 1),), 0x55, dtype=torch.uint8, device="cuda")
+    yb_t = cr.w4a4_gemm(a, sa, GR[ag], wt, sw, GR[wg], M, N, K, out_type=0, workspace=ws)
+    assert np.array_equal(host(yb_t), host(yb))
+    assert np.array_equal(bytes_of(ws), host(w).reshape(-1))      # the expansion is the fp6 weight image
 
 
 def test_w4a4_f6_ldc_padding(cr):
@@ -162,6 +171,11 @@ def test_w4a4_f6_layer_on_gpu(cr):
     assert np.array_equal(host(raw).astype(np.int64), ref["raw"])
     yb = cr.w4a4_gemm(a, sa, 0, wf, ws, 1, M, N, K, out_type=0)
     assert rel_l2(bf16_to_f32(host(yb)), ref["y"]) <= 2e-3
+    # the stored format: 4-bit tile-packed weights (w4_pack_weights), expanded per call
+    wt, _, _, _ = cr.w4_pack_weights(wn, ws, N, K, 0, 1)
+    assert np.array_equal(bytes_of(wt), ref["w"]["tiles"].reshape(-1))
+    assert np.array_equal(host(cr.w4a4_gemm(a, sa, 0, wt, ws, 1, M, N, K, out_type=2)), host(raw))
+    assert np.array_equal(host(cr.w4a4_gemm(a, sa, 0, wt, ws, 1, M, N, K, out_type=0)), host(yb))
 
 
 def test_f6_rejects_unsupported(cr):
@@ -263,6 +277,11 @@ def test_w4a4_f6_group64(cr, case):
     assert rel_l2(bf16_to_f32(host(yb)), ref["y"]) <= 2e-3
     # the bf16 output is the float32 one rounded to nearest even
     assert np.array_equal(host(yb), host(yf.to(torch.bfloat16)))
+    # the same against the 4-bit tile-packed weights, expanded by the call
+    wt = dev(wp["tiles"].reshape(-1))
+    assert np.array_equal(host(cr.w4a4_gemm(a, sa, 2, wt, sw, 2, M, N, K, out_type=2, **kw)), host(raw))
+    yf_t = cr.w4a4_gemm(a, sa, 2, wt, sw, 2, M, N, K, out_type=1, **kw)
+    assert np.array_equal(host(yf_t).view(np.uint32), host(yf).view(np.uint32))
 
 
 def test_w4a4_f6_group64_ldc_padding(cr):

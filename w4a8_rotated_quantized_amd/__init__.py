@@ -17,7 +17,7 @@ __all__ = [
     "ConvRotError", "lib", "Q", "GRAN", "OUT", "LAYOUT",
     "convrot_rotate_quantize", "convrot_rotate_quantize_dual", "convrot_dequantize_weights", "w4_pack_weights",
     "w4_pack_weights_f6", "w4_packed_f6_bytes",
-    "w4a4_gemm", "w4a8_gemm",
+    "w4a4_gemm", "w4a4_gemm_workspace_size", "w4a8_gemm",
     "int8_tensorwise_gemm", "convrot_rq_workspace_size", "w4_packed_bytes",
     "get_counters", "reset_counters", "device_check", "status_string",
 ]
@@ -80,7 +80,8 @@ _SIGS = {
     "w4_pack_weights": (_i, [_vp, _vp, _vp, _i64, _i64, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "w4_packed_f6_bytes": (_sz, [_i64, _i64]),
     "w4_pack_weights_f6": (_i, [_vp, _i64, _i64, _vp, _vp]),
-    "w4a4_gemm": (_i, [_vp, _i, _vp, _i, _i, _f, _vp, _vp, _i, _vp, _vp, _i, _vp, _i, _vp,
+    "w4a4_gemm_workspace_size": (_sz, [_i64, _i64, _i, _i]),
+    "w4a4_gemm": (_i, [_vp, _i, _vp, _i, _i, _f, _vp, _i, _vp, _i, _vp, _vp, _i, _vp, _i, _vp,
                        _vp, _i, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
     "w4a8_gemm": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp, _i, _vp, _i, _vp, _i, _vp, _vp, _i, _i64, _i64, _i64, _i64,
                        _vp, _sz, _vp]),
@@ -277,23 +278,37 @@ def _out(M, N, out_type, dev, out):
     return torch.empty((M, N), dtype=dt, device=dev)
 
 
+def w4a4_gemm_workspace_size(N, K, a_layout, w_layout) -> int:
+    return lib.w4a4_gemm_workspace_size(N, K, int(a_layout), int(w_layout))
+
+
 def w4a4_gemm(a_codes, a_scales, a_gran, w_packed, w_scales, w_gran, M, N, K,
               a_unsigned=False, a_shift=0.0, w_sum=None, lora_act=None, lora_up=None,
-              bias=None, out_type=OUT.BF16, out=None, a_layout=None, stream=None):
-    """a_layout defaults to F6 for [M/32, K/64, 1536] codes (weights from
-    w4_pack_weights_f6), TILED for [M/16, K/64, 512], else NATURAL."""
+              bias=None, out_type=OUT.BF16, out=None, a_layout=None, w_layout=None, workspace=None, stream=None):
+    """a_layout defaults to F6 for [M/32, K/64, 1536] codes, TILED for
+    [M/16, K/64, 512], else NATURAL. w_layout defaults to F6 for
+    [N/32, K/64, 1536] weights (w4_pack_weights_f6), else TILED
+    (w4_pack_weights). With F6 codes and TILED weights the call needs a
+    workspace of w4a4_gemm_workspace_size bytes (allocated here when not
+    given) into which it expands the weights before the fp6 GEMM."""
     if a_layout is None:
         if a_codes.dim() == 3:
             a_layout = LAYOUT.F6 if a_codes.shape[-1] == 1536 else LAYOUT.TILED
         else:
             a_layout = LAYOUT.NATURAL
+    if w_layout is None:
+        w_layout = LAYOUT.F6 if (w_packed.dim() == 3 and w_packed.shape[-1] == 1536) else LAYOUT.TILED
+    need = w4a4_gemm_workspace_size(N, K, a_layout, w_layout)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=a_codes.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     out = _out(M, N, out_type, a_codes.device, out)
     lora_f32 = int(lora_act is not None and lora_act.dtype == torch.float32)
     R = 0 if lora_up is None else lora_up.shape[1]
     st = lib.w4a4_gemm(_ptr(a_codes), int(a_layout), _ptr(a_scales), a_gran, int(bool(a_unsigned)), float(a_shift),
-                       _ptr(w_packed), _ptr(w_scales), w_gran, _ptr(w_sum),
+                       _ptr(w_packed), int(w_layout), _ptr(w_scales), w_gran, _ptr(w_sum),
                        _ptr(lora_act), lora_f32, _ptr(lora_up), R, _ptr(bias),
-                       _ptr(out), out_type, out.stride(0), M, N, K, None, 0, _stream(stream))
+                       _ptr(out), out_type, out.stride(0), M, N, K, _ptr(workspace), wsb, _stream(stream))
     _check(st, "w4a4_gemm")
     return out
 

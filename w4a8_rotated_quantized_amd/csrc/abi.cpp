@@ -374,21 +374,27 @@ static cr_status gemm_common(const void* a, const void* w, const void* out, cr_o
   return CR_OK;
 }
 
+size_t w4a4_gemm_workspace_size(int64_t N, int64_t K, cr_layout a_layout, cr_layout w_layout) {
+  if (a_layout != CR_LAYOUT_F6 || w_layout != CR_LAYOUT_TILED) return 0;
+  if (N < 128 || K < 128 || N % 128 || K % 128) return 0;
+  return (size_t)((N / 32) * (K / 64) * 1536);   // the weights as fp6 fragments
+}
+
 cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scales, cr_gran a_gran,
                     int a_unsigned, float a_shift,
-                    const void* w_packed, const float* w_scales, cr_gran w_gran, const float* w_sum,
-                    const void* lora_act, int lora_act_f32, const void* lora_up, int R, const void* bias,
-                    void* out, cr_out out_type, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                    const void* w_packed, cr_layout w_layout, const float* w_scales, cr_gran w_gran,
+                    const float* w_sum, const void* lora_act, int lora_act_f32, const void* lora_up, int R,
+                    const void* bias, void* out, cr_out out_type, int64_t ldc, int64_t M, int64_t N, int64_t K,
                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   cr_status st = gemm_common(a_codes, w_packed, out, out_type, ldc, M, N, K, bias);
   if (st != CR_OK) return st;
   if (!a_scales || !w_scales || !aligned16(a_scales) || !aligned16(w_scales)) return CR_ERR_INVALID_ARGUMENT;
   if ((int)a_gran < 0 || (int)a_gran > 2 || (int)w_gran < 0 || (int)w_gran > 2) return CR_ERR_INVALID_ARGUMENT;
   if ((int)a_layout < 0 || (int)a_layout > 3) return CR_ERR_INVALID_ARGUMENT;
+  if (!((int)w_layout == CR_LAYOUT_TILED || (int)w_layout == CR_LAYOUT_F6)) return CR_ERR_INVALID_ARGUMENT;
   const bool a8 = a_layout == CR_LAYOUT_INT8;
   const bool f6 = a_layout == CR_LAYOUT_F6;
+  if (w_layout == CR_LAYOUT_F6 && !f6) return CR_ERR_UNSUPPORTED_FORMAT;   // fp6 weights pair with fp6 codes
   if (f6) {   // fp6 fragments on both sides; unsigned codes and the low-rank branch with 64-group scales only
     if (a_gran != CR_GRAN_ROW_GROUP && (a_unsigned || lora_act || lora_up)) return CR_ERR_UNSUPPORTED_FORMAT;
     if (((M + 31) / 32) * (K / 64) * 1536 >= ((int64_t)1 << 32) || (N / 32) * (K / 64) * 1536 >= ((int64_t)1 << 32))
@@ -405,6 +411,11 @@ cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
   if (lora_act || lora_up) {
     if (!lora_act || !lora_up || (R != 32 && R != 64)) return CR_ERR_UNSUPPORTED_FORMAT;
     if (!aligned16(lora_act) || !aligned16(lora_up)) return CR_ERR_INVALID_ARGUMENT;
+  }
+  const size_t need = w4a4_gemm_workspace_size(N, K, a_layout, w_layout);
+  if (need > 0) {
+    if (!workspace || !aligned16(workspace)) return CR_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < need) return CR_ERR_WORKSPACE_TOO_SMALL;
   }
   st = device_check();
   if (st != CR_OK) return st;
@@ -433,7 +444,14 @@ cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
   p.grouped = grouped ? 1 : 0;
   p.a_tiled = a_layout == CR_LAYOUT_TILED ? 1 : 0;
   if (a8) return finish_launch(cr::launch_gemm_a8w4(p, stream), E_W4A4, 1);
-  if (f6) return finish_launch(cr::launch_gemm_f6(p, stream), E_W4A4, 1);
+  if (f6) {
+    if (need > 0) {   // int4 tiles -> fp6 fragments in the workspace, then the fp6 GEMM on them
+      hipError_t e = cr::launch_expand_f6(p.w, N, K, static_cast<uint8_t*>(workspace), stream);
+      if (e != hipSuccess) return hip_fail(e);
+      p.w = static_cast<const uint8_t*>(workspace);
+    }
+    return finish_launch(cr::launch_gemm_f6(p, stream), E_W4A4, need > 0 ? 2 : 1);
+  }
   return finish_launch(cr::launch_gemm_w4a4(p, stream), E_W4A4, 1);
 }
 

@@ -208,7 +208,13 @@ __global__ __launch_bounds__(256, 2) void gemm_w4a8_kernel(GemmParams p) {
         const int nb = wcol0 + j;
         const uint32_t x = *reinterpret_cast<const uint32_t*>(Ws + g * 1024 + nb * 256 + l * 4);
         wf[j] = w4_to_h(x, Zs[g * 128 + nb * 32 + lr]);
-        if constexpr (!RAW) sc[j] = (float)__builtin_bit_cast(_Float16, Ss[g * 128 + nb * 32 + lr]);
+        if constexpr (!RAW) {
+          // the scale as a float32 register: the 16 FMAs then run as plain
+          // v_fmac_f32 instead of mixed-precision FMAs
+          float f;
+          asm("v_cvt_f32_f16 %0, %1" : "=v"(f) : "v"((uint32_t)Ss[g * 128 + nb * 32 + lr]));
+          sc[j] = f;
+        }
       }
       v8h_ af[TM];
 #pragma unroll

@@ -61,6 +61,8 @@ struct PackParams {
 hipError_t launch_pack(const PackParams& p, hipStream_t s);
 // natural int4 [N, K/2] -> fp6 E2M3 fragments [N/32][K/64][1536 B]
 hipError_t launch_pack_f6(const uint8_t* codes, int64_t N, int64_t K, uint8_t* packed, hipStream_t s);
+// tile-packed int4 [N/128][K/64][4096 B] -> fp6 E2M3 fragments [N/32][K/64][1536 B]
+hipError_t launch_expand_f6(const uint8_t* tiles, int64_t N, int64_t K, uint8_t* packed, hipStream_t s);
 
 struct MergeParams {
   const uint8_t* codes;      // natural codes: int4 [N, K/2] (SYM_INT4, ASYM_UINT4) or int8 [N, K]

@@ -153,6 +153,46 @@ __global__ __launch_bounds__(256) void pack_f6_kernel(const uint8_t* __restrict_
   *reinterpret_cast<u32x2*>(frag + 1024 + lm * 8) = u32x2{o[4], o[5]};
 }
 
+// Tile-packed signed int4 weights (w4_pack_weights: [N/128][K/64][8][64
+// lanes][8 B], lane l of 16-row block nb holding row 16 nb + l % 16 and the
+// 16 codes k = 16 (l / 16) .. of the k-tile, two per byte in natural order)
+// -> the fp6 fragments of the fp6 matrix-core GEMM. The GEMM runs this once
+// per call into its workspace, so the weights stay at 4 bits per code in
+// memory. Fragment lane l of 32-row block b (row 32 b + l % 32, codes
+// 32 (l / 32) .. + 31 of the k-tile) is tile lanes 2 (l / 32) and
+// 2 (l / 32) + 1 of 16-row block 2 (b % 4) + (l % 32) / 16 of tile b / 4:
+// 16 bytes in natural order, converted as in pack_f6_kernel.
+__global__ __launch_bounds__(256) void expand_f6_kernel(const uint8_t* __restrict__ tiles, int64_t N, int64_t K,
+                                                        uint8_t* __restrict__ packed) {
+  const int64_t KT = K / 64;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= (N / 32) * KT * 64) return;     // one thread per fragment lane slot
+  const int lm = (int)(c & 63);
+  const int64_t rest = c >> 6;
+  const int64_t kt = rest % KT, rb = rest / KT;
+  const int r32 = lm & 31, h = lm >> 5;
+  const uint8_t* tile = tiles + ((rb >> 2) * KT + kt) * 4096 + (2 * (rb & 3) + (r32 >> 4)) * 512;
+  const u32x2 x0 = *reinterpret_cast<const u32x2*>(tile + (32 * h + (r32 & 15)) * 8);
+  const u32x2 x1 = *reinterpret_cast<const u32x2*>(tile + (32 * h + 16 + (r32 & 15)) * 8);
+  const u32x4 x = u32x4{x0[0], x0[1], x1[0], x1[1]};
+  v16f lo, hi;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t b = (x[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+    lo[j] = (float)((int)(b << 28) >> 28);
+    hi[j] = (float)((int)(b << 24) >> 28);
+  }
+  const auto o = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(lo, hi, 1.0f);
+  uint8_t* frag = packed + rest * 1536;
+  *reinterpret_cast<u32x4*>(frag + lm * 16) = u32x4{o[0], o[1], o[2], o[3]};
+  *reinterpret_cast<u32x2*>(frag + 1024 + lm * 8) = u32x2{o[4], o[5]};
+}
+
+hipError_t launch_expand_f6(const uint8_t* tiles, int64_t N, int64_t K, uint8_t* packed, hipStream_t s) {
+  hipLaunchKernelGGL(expand_f6_kernel, dim3(nblocks((N / 32) * (K / 64) * 64)), dim3(256), 0, s, tiles, N, K, packed);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_f6(const uint8_t* codes, int64_t N, int64_t K, uint8_t* packed, hipStream_t s) {
   hipLaunchKernelGGL(pack_f6_kernel, dim3(nblocks((N / 32) * (K / 64) * 64)), dim3(256), 0, s, codes, N, K, packed);
   return hipGetLastError();

@@ -194,6 +194,16 @@ def _c5(M: int = 8192):
     return w
 
 
+def _c2pair():
+    """The MMDiT projection of C2 at both token counts in one step: image
+    tokens (M = 4096, fp6 codes) and the small-token case (M = 32)."""
+    w = Workload(2, "MMDiT projection W4A4 tensorwise ConvRot (4096 + 32)x3072x3072")
+    for M in (4096, 32):
+        w.acts[f"x{M}"] = (M, 3072, "normal", 15, 30.0)
+        w.linears.append(LinearSpec(f"proj{M}", "w4a4", M, 3072, 3072, f"x{M}"))
+    return w
+
+
 def _c2a8():
     """The MMDiT projection of C2 on the 8-bit-activation branch: the same
     W4A4-format weights against per-token INT8 activations (M = 4096 and 32)."""
@@ -208,6 +218,7 @@ CONFIGS = {
     "c1": _c1,
     "c2_m32": lambda: _c2(32),
     "c2_m4096": lambda: _c2(4096),
+    "c2": _c2pair,
     "c3": _c3,
     "c4": _c4,
     "c5": _c5,
@@ -220,19 +231,25 @@ CONFIGS = {
 # both draw exactly the same inputs)
 # --------------------------------------------------------------------------
 
-def act_bits(w: Workload, name: str) -> np.ndarray:
-    """bf16 bits of activation tensor `name` of workload `w`."""
+def act_bits(w: Workload, name: str, rows: int | None = None) -> np.ndarray:
+    """bf16 bits of activation tensor `name` of workload `w`; `rows` draws
+    only its first rows (the same values: the generator fills the tensor row
+    by row; tensors with outlier columns are drawn whole and cut)."""
     M, K, kind, n_out, scale = w.acts[name]
     tid = 100 + sorted(w.acts).index(name)
+    if rows is not None and n_out:
+        return act_bits(w, name)[:rows]
+    Mr = M if rows is None else min(M, rows)
     if kind == "gelu":
-        return gelu_activation(w.config_id, tid, M, K)
-    return activation(w.config_id, tid, M, K, n_out, scale)
+        return gelu_activation(w.config_id, tid, Mr, K)
+    return activation(w.config_id, tid, Mr, K, n_out, scale)
 
 
-def weight_bits(w: Workload, lin: LinearSpec) -> np.ndarray:
-    """bf16 bits [N, K] of the weight of linear `lin` of workload `w`."""
+def weight_bits(w: Workload, lin: LinearSpec, rows: int | None = None) -> np.ndarray:
+    """bf16 bits [N, K] of the weight of linear `lin` of workload `w` (its
+    first `rows` output channels when given: the same values)."""
     tid = 200 + [l.name for l in w.linears].index(lin.name)
-    return weight(w.config_id, tid, lin.N, lin.K)
+    return weight(w.config_id, tid, lin.N if rows is None else min(lin.N, rows), lin.K)
 
 
 def lowrank_bits(w: Workload, lin: LinearSpec):
