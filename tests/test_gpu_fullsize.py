@@ -1,12 +1,19 @@
-"""Full-size parity of the benchmarked path: the single MMDiT projection
-(X bf16 [M, 3072] with M = 4096 and M = 32, W [3072, 3072]), run exactly as
-bench.py runs it (GPU rotate+quantize into the tiled code layout, then the
-W4A4 GEMM), against the oracle.
+"""Full-size parity of the benchmarked path, every output row compared.
 
-Bit-exact: every activation code and the per-tensor scale, every packed
-weight byte, and the int32 results on sampled rows (all N columns). bf16
-outputs: relative L2 <= 2e-3 against the oracle's float32 epilogue on the
-same rows.
+Each workload runs exactly as bench.py runs it (bench_workloads.Runner: the
+same rotate+quantize passes, code layouts, 4-bit weight tiles expanded per
+call, kernels and launch configurations), one step on one buffer set; then
+every layer is checked against the oracle:
+  * activation codes and scales bit-exact (every row);
+  * packed weights bit-exact;
+  * the exact integer result (CR_OUT_I32_RAW of the same call, the same
+    kernel configuration) bit-exact on every row;
+  * the step's bf16 output within 2e-3 relative L2 of the oracle's float32
+    epilogue, over all rows.
+The oracle's integer products are taken in row chunks as float64 BLAS on the
+integer codes (exact below 2^53); group-scaled outputs use the oracle's exact
+dequantized operands (s * q in float64), the same sum as the per-group form
+grouped by k instead of by group.
 """
 import numpy as np
 import pytest
@@ -15,8 +22,8 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 import workloads as wl  # noqa: E402
-from oracle import quant as oq, linear as ol, gemm as og, pack as opack  # noqa: E402
-from tests.gpu_helpers import bf16_dev, bf16_to_f32, bytes_of, dev, host, rel_l2, say  # noqa: E402
+from oracle import quant as oq, linear as ol, pack as opack  # noqa: E402
+from tests.gpu_helpers import bf16_to_f32, bytes_of, host, say  # noqa: E402
 
 
 @pytest.fixture(scope="module")
@@ -28,294 +35,195 @@ def cr():
     return m
 
 
-@pytest.fixture(scope="module")
-def c2_weights(cr):
-    N = K = 3072
-    wb = wl.weight(2, 1, N, K)
-    wp = ol.prepare_w4a4(wb)
-    wc, ws, _, _ = cr.convrot_rotate_quantize(bf16_dev(wb), 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
-    assert np.array_equal(bytes_of(wc), wp["codes"].reshape(-1))
-    assert host(ws)[0] == np.float32(wp["scales"]).reshape(-1)[0]
-    packed, _, _, _ = cr.w4_pack_weights(wc, ws, N, K)
-    assert np.array_equal(bytes_of(packed), wp["tiles"].reshape(-1))
-    return wp, packed, ws
-
-
-@pytest.mark.parametrize("M", [4096, 32])
-def test_c2_full_pipeline(cr, c2_weights, M):
-    N = K = 3072
-    say(f"c2 full size M={M}")
-    wp, packed, ws = c2_weights
-    xb = wl.activation(2, 0 if M == 4096 else 2, M, K, n_outliers=15, outlier_scale=30.0)
-    xa = ol.rotate_quantize(xb, 256, "int4", "tensor")
-    codes, sa, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR,
-                                                 layout=cr.LAYOUT.TILED)
-    ref_tiled = opack.tile_pack_a(xa["codes"])
-    got = bytes_of(codes).reshape(ref_tiled.shape)
-    if M % 16:
-        # rows past M in the last 16-row block are left unwritten: compare the valid rows only
-        got = opack.tile_unpack_a(got, M)
-        ref_tiled = xa["codes"]
-    assert np.array_equal(got, ref_tiled)
-    assert host(sa)[0] == np.float32(xa["scales"]).reshape(-1)[0]
-
-    rng = np.random.default_rng(1234)
-    rows = np.sort(rng.choice(M, size=min(M, 192), replace=False))
-    raw = host(cr.w4a4_gemm(codes, sa, 0, packed, ws, 0, M, N, K, out_type=cr.OUT.I32_RAW))
-    ref_raw = og.int_gemm(xa["values"][rows], wp["values"])
-    assert np.array_equal(raw[rows].astype(np.int64), ref_raw)
-    y = bf16_to_f32(host(cr.w4a4_gemm(codes, sa, 0, packed, ws, 0, M, N, K)))
-    ref_y = ol.epilogue_scalar(ref_raw, xa["scales"], "tensor", wp["scales"], "tensor")
-    assert rel_l2(y[rows], ref_y) <= 2e-3
-
-
-@pytest.mark.parametrize("M", [4096, 32])
-def test_c2_full_pipeline_f6(cr, c2_weights, M):
-    """The benchmarked path on the fp6 matrix cores: GPU rotate+quantize into
-    fp6 fragments, weights packed to fp6 fragments, GEMM (256 x 192 blocks at
-    M = 4096, the small-M kernel at 32)."""
-    N = K = 3072
-    say(f"c2 full size fp6 M={M}")
-    wp, _, ws = c2_weights
-    wc, _, _, _ = cr.convrot_rotate_quantize(bf16_dev(wl.weight(2, 1, N, K)), 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
-    wf = cr.w4_pack_weights_f6(wc, N, K)
-    assert np.array_equal(bytes_of(wf), opack.f6_pack(wp["values"]).reshape(-1))
-    xb = wl.activation(2, 0 if M == 4096 else 2, M, K, n_outliers=15, outlier_scale=30.0)
-    xa = ol.rotate_quantize(xb, 256, "int4", "tensor")
-    codes, sa, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR,
-                                                 layout=cr.LAYOUT.F6)
-    assert np.array_equal(opack.f6_unpack(host(codes), M), xa["values"])
-    assert host(sa)[0] == np.float32(xa["scales"]).reshape(-1)[0]
-    rng = np.random.default_rng(4321)
-    rows = np.sort(rng.choice(M, size=min(M, 192), replace=False))
-    raw = host(cr.w4a4_gemm(codes, sa, 0, wf, ws, 0, M, N, K, out_type=cr.OUT.I32_RAW))
-    ref_raw = og.int_gemm(xa["values"][rows], wp["values"])
-    assert np.array_equal(raw[rows].astype(np.int64), ref_raw)
-    y = bf16_to_f32(host(cr.w4a4_gemm(codes, sa, 0, wf, ws, 0, M, N, K)))
-    ref_y = ol.epilogue_scalar(ref_raw, xa["scales"], "tensor", wp["scales"], "tensor")
-    assert rel_l2(y[rows], ref_y) <= 2e-3
-
-
-# ---------------------------------------------------------------------------
-# the other workloads at full size (sampled outputs)
-# ---------------------------------------------------------------------------
-
-def _rows(M, n, seed):
-    return np.sort(np.random.default_rng(seed).choice(M, size=min(M, n), replace=False))
-
-
-def _cols(N, n, seed):
-    return np.sort(np.random.default_rng(seed + 1).choice(N, size=min(N, n), replace=False))
-
-
-def _lin(cfg, name):
-    w = wl.CONFIGS[cfg]()
-    return w, [l for l in w.linears if l.name == name][0]
-
-
 def _chunks(M, step=1024):
     return [(r, min(M, r + step)) for r in range(0, M, step)]
 
 
+class _Err:
+    """relative L2 error accumulated over row chunks"""
+    def __init__(self):
+        self.num = self.den = 0.0
+
+    def add(self, got, ref):
+        ref = np.asarray(ref, np.float64)
+        self.num += float(np.sum((np.asarray(got, np.float64) - ref) ** 2))
+        self.den += float(np.sum(ref ** 2))
+
+    def rel(self):
+        return float(np.sqrt(self.num / self.den))
+
+
+_RUNNERS = {}
+
+
+def _runner(name):
+    """one step of the workload as the benchmark runs it (one per module and workload)"""
+    import bench_workloads as bw
+    if name not in _RUNNERS:
+        for k in list(_RUNNERS):            # one workload's buffers on the device at a time
+            del _RUNNERS[k]
+        torch.cuda.empty_cache()
+        r = bw.Runner(name, nsets=1)
+        r.step(0)
+        torch.cuda.synchronize()
+        _RUNNERS[name] = r
+    return _RUNNERS[name]
+
+
+_ACT = {}
+
+
+def _oracle_act(w, x_id, qt, gran="tensor", rot=256, group=None, shift=0.0):
+    key = (w.config_id, x_id, qt, gran, rot, group, shift)
+    if key not in _ACT:
+        _ACT[key] = ol.rotate_quantize(wl.act_bits(w, x_id), rot, qt, gran, group, shift)
+    return _ACT[key]
+
+
+def _tensorwise_layer(cr, r, lin):
+    """W4A4 or INT8 tensorwise layer of a runner: codes, weights, int32, bf16."""
+    w = r.w
+    M, N, K = lin.M, lin.N, lin.K
+    st = r.sets[0]
+    key = [k for l, k in r.gemm_plan if l.name == lin.name][0]
+    o, p = st["rq"][key], st["prep"][lin.name]
+    qt = "int4" if lin.fmt == "w4a4" else "int8"
+    xa = _oracle_act(w, lin.x_id, qt)
+    wq = ol.rotate_quantize(wl.weight_bits(w, lin), 256, qt, "tensor")
+    if qt == "int4":
+        got = host(o["codes"])
+        if r.f6_codes(M):
+            assert np.array_equal(opack.f6_unpack(got, M), xa["values"]), "fp6 codes differ"
+        else:
+            assert np.array_equal(opack.tile_unpack_a(got, M), xa["codes"]), "tiled codes differ"
+        a, sa = o["codes"], o["scales"]
+        assert np.array_equal(bytes_of(p["w"]), opack.tile_pack_w4a4(wq["codes"]).reshape(-1)), "weight tiles"
+        raw = host(cr.w4a4_gemm(a, sa, 0, p["w"], p["ws"], 0, M, N, K, out_type=cr.OUT.I32_RAW,
+                                workspace=st["gws"]))
+    else:
+        a, sa = (o["codes8"], o["scales8"]) if "codes8" in o else (o["codes"], o["scales"])
+        assert np.array_equal(host(a), xa["codes"]), "int8 codes differ"
+        assert np.array_equal(host(p["w"]), wq["codes"]), "int8 weights differ"
+        raw = host(cr.int8_tensorwise_gemm(a, sa, p["w"], p["ws"], M, N, K, out_type=cr.OUT.I32_RAW))
+    assert host(sa)[0] == np.float32(xa["scales"]).reshape(-1)[0]
+    assert host(p["ws"])[0] == np.float32(wq["scales"]).reshape(-1)[0]
+    y = bf16_to_f32(host(st["out"][lin.name]))
+    A = xa["values"].astype(np.float64)
+    W = wq["values"].astype(np.float64)
+    err = _Err()
+    for r0, r1 in _chunks(M):
+        ref_raw = np.rint(A[r0:r1] @ W.T).astype(np.int64)
+        assert np.array_equal(raw[r0:r1].astype(np.int64), ref_raw), f"int32 rows {r0}..{r1}"
+        err.add(y[r0:r1], ol.epilogue_scalar(ref_raw, xa["scales"], "tensor", wq["scales"], "tensor"))
+    assert err.rel() <= 2e-3, err.rel()
+
+
+@pytest.mark.parametrize("name", ["proj4096", "proj32"])
+def test_c2_full(cr, name):
+    """The single MMDiT projection, M = 4096 (fp6 codes, 4-bit weight tiles
+    expanded per call, fp6 matrix cores) and M = 32 (tiled int4 codes,
+    weight-streaming int8-core kernel)."""
+    r = _runner("c2")
+    lin = [l for l in r.w.linears if l.name == name][0]
+    say(f"c2 full {name}")
+    _tensorwise_layer(cr, r, lin)
+
+
+C4_LAYERS = [f"{s}_{n}" for s in ("img", "txt") for n in ("q", "k", "v", "out", "mlp_up", "mlp_down", "mod")]
+
+
+@pytest.mark.parametrize("name", C4_LAYERS)
+def test_c4_layer_full(cr, name):
+    """Every linear of the mixed MMDiT block (W4A4: q, k, mlp_up, mlp_down;
+    INT8: v, out, mod; image and text streams)."""
+    r = _runner("c4")
+    lin = [l for l in r.w.linears if l.name == name][0]
+    say(f"c4 full {name} {lin.M}x{lin.N}x{lin.K}")
+    _tensorwise_layer(cr, r, lin)
+
+
 def test_c3_w4a8_full(cr):
     """W4A8: X [8192, 3072] int8 per token (fp16-carried codes, the layout the
-    GEMM runs on), W [12288, 3072] asym uint4 g16; every output row compared.
-    The oracle's y = s_a sum_g s_w[n, g] P[m, n, g] is evaluated in row chunks
-    as s_a (A @ W_hat^T) in float64, with W_hat = s_w (q - z) the oracle's
-    exact dequantized weight (the same sum, grouped by k instead of by g)."""
-    w, lin = _lin("c3", "mlp_up")
+    GEMM runs on), W [12288, 3072] asym uint4 g16."""
+    r = _runner("c3")
+    lin = r.w.linears[0]
     M, N, K = lin.M, lin.N, lin.K
     say(f"c3 full {M}x{N}x{K}")
-    xb, wb = wl.act_bits(w, lin.x_id), wl.weight_bits(w, lin)
-    xa = ol.rotate_quantize(xb, 256, "int8", "row")
-    wp = ol.prepare_w4a8(wb)
-    a, sa, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), 256, cr.Q.SYM_INT8, cr.GRAN.ROW, layout=cr.LAYOUT.F16)
-    assert np.array_equal(host(a).astype(np.int64), xa["values"].astype(np.int64))
-    assert np.array_equal(host(sa).view(np.uint32), np.asarray(xa["scales"], np.float32).view(np.uint32))
-    wc, ws, wz, _ = cr.convrot_rotate_quantize(bf16_dev(wb), 256, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16)
-    packed, pscales, pzeros, _ = cr.w4_pack_weights(wc, ws, N, K, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16, zeros=wz)
-    assert np.array_equal(bytes_of(packed), wp["tiles"].reshape(-1))
-    assert np.array_equal(host(pscales).view(np.uint16).reshape(-1), wp["scales_tiles"].view(np.uint16).reshape(-1))
-    assert np.array_equal(host(pzeros).reshape(-1), wp["zeros_tiles"].reshape(-1))
-    raw = host(cr.w4a8_gemm(a, sa, cr.GRAN.ROW, packed, pscales, pzeros, M, N, K, out_type=cr.OUT.I32_RAW))
-    yb = bf16_to_f32(host(cr.w4a8_gemm(a, sa, cr.GRAN.ROW, packed, pscales, pzeros, M, N, K)))
-    yf = host(cr.w4a8_gemm(a, sa, cr.GRAN.ROW, packed, pscales, pzeros, M, N, K, out_type=cr.OUT.F32))
+    st = r.sets[0]
+    key = r.gemm_plan[0][1]
+    o, p = st["rq"][key], st["prep"][lin.name]
+    xa = _oracle_act(r.w, lin.x_id, "int8", "row")
+    wp = ol.prepare_w4a8(wl.weight_bits(r.w, lin))
+    assert np.array_equal(host(o["codes"]).astype(np.int64), xa["values"].astype(np.int64))
+    assert np.array_equal(host(o["scales"]).view(np.uint32), np.asarray(xa["scales"], np.float32).view(np.uint32))
+    assert np.array_equal(bytes_of(p["w"]), wp["tiles"].reshape(-1))
+    assert np.array_equal(host(p["ws"]).view(np.uint16).reshape(-1), wp["scales_tiles"].view(np.uint16).reshape(-1))
+    assert np.array_equal(host(p["wz"]).reshape(-1), wp["zeros_tiles"].reshape(-1))
+    args = (o["codes"], o["scales"], cr.GRAN.ROW, p["w"], p["ws"], p["wz"], M, N, K)
+    raw = host(cr.w4a8_gemm(*args, out_type=cr.OUT.I32_RAW))
+    yf = host(cr.w4a8_gemm(*args, out_type=cr.OUT.F32))
+    yb = bf16_to_f32(host(st["out"][lin.name]))
     zexp = np.repeat(wp["zeros"].astype(np.int64), 16, axis=1)
     d = (wp["values"].astype(np.int64) - zexp).astype(np.float64)
     w_hat = oq.dequant_asym(wp["values"], wp["scales"], wp["zeros"], 16).astype(np.float64)
     A = xa["values"].astype(np.float64)
     s_a = np.asarray(xa["scales"], np.float64)
-    num = den = numf = 0.0
+    eb, ef = _Err(), _Err()
     for r0, r1 in _chunks(M):
-        assert np.array_equal(raw[r0:r1].astype(np.int64), (A[r0:r1] @ d.T).astype(np.int64))
-        ref = (s_a[r0:r1, None] * (A[r0:r1] @ w_hat.T)).astype(np.float32).astype(np.float64)
-        num += float(np.sum((yb[r0:r1] - ref) ** 2))
-        numf += float(np.sum((yf[r0:r1] - ref) ** 2))
-        den += float(np.sum(ref ** 2))
-    assert np.sqrt(num / den) <= 2e-3, np.sqrt(num / den)
-    assert np.sqrt(numf / den) <= 1e-5, np.sqrt(numf / den)
-
-
-def _int8_layer(cr, w, lin, rows_n=32):
-    M, N, K = lin.M, lin.N, lin.K
-    xb, wb = wl.act_bits(w, lin.x_id), wl.weight_bits(w, lin)
-    xa = ol.rotate_quantize(xb, 256, "int8", "tensor")
-    wq = ol.rotate_quantize(wb, 256, "int8", "tensor")
-    ws_need = cr.convrot_rq_workspace_size(M, K, 256, cr.Q.SYM_INT8, cr.GRAN.TENSOR)
-    a, sa, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), 256, cr.Q.SYM_INT8, cr.GRAN.TENSOR)
-    assert ws_need > 0
-    assert np.array_equal(host(a), xa["codes"])
-    assert host(sa)[0] == np.float32(xa["scales"]).reshape(-1)[0]
-    wc, wsc, _, _ = cr.convrot_rotate_quantize(bf16_dev(wb), 256, cr.Q.SYM_INT8, cr.GRAN.TENSOR)
-    assert np.array_equal(host(wc), wq["codes"])
-    rows = _rows(M, rows_n, 41)
-    raw = host(cr.int8_tensorwise_gemm(a, sa, wc, wsc, M, N, K, out_type=cr.OUT.I32_RAW))
-    ref_raw = og.int_gemm(xa["values"][rows], wq["values"])
-    assert np.array_equal(raw[rows].astype(np.int64), ref_raw)
-    y = bf16_to_f32(host(cr.int8_tensorwise_gemm(a, sa, wc, wsc, M, N, K)))
-    ref_y = ol.epilogue_scalar(ref_raw, xa["scales"], "tensor", wq["scales"], "tensor")
-    assert rel_l2(y[rows], ref_y) <= 2e-3
-
-
-def _w4a4_layer(cr, w, lin, rows_n=32):
-    M, N, K = lin.M, lin.N, lin.K
-    xb, wb = wl.act_bits(w, lin.x_id), wl.weight_bits(w, lin)
-    xa = ol.rotate_quantize(xb, 256, "int4", "tensor")
-    wp = ol.prepare_w4a4(wb)
-    codes, sa, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR,
-                                                 layout=cr.LAYOUT.TILED)
-    assert np.array_equal(opack.tile_unpack_a(bytes_of(codes).reshape((M + 15) // 16, K // 64, 512), M),
-                          xa["codes"])
-    assert host(sa)[0] == np.float32(xa["scales"]).reshape(-1)[0]
-    wc, ws, _, _ = cr.convrot_rotate_quantize(bf16_dev(wb), 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR)
-    packed, _, _, _ = cr.w4_pack_weights(wc, ws, N, K)
-    assert np.array_equal(bytes_of(packed), wp["tiles"].reshape(-1))
-    rows = _rows(M, rows_n, 51)
-    raw = host(cr.w4a4_gemm(codes, sa, 0, packed, ws, 0, M, N, K, out_type=cr.OUT.I32_RAW))
-    ref_raw = og.int_gemm(xa["values"][rows], wp["values"])
-    assert np.array_equal(raw[rows].astype(np.int64), ref_raw)
-    y = bf16_to_f32(host(cr.w4a4_gemm(codes, sa, 0, packed, ws, 0, M, N, K)))
-    ref_y = ol.epilogue_scalar(ref_raw, xa["scales"], "tensor", wp["scales"], "tensor")
-    assert rel_l2(y[rows], ref_y) <= 2e-3
-
-
-@pytest.mark.parametrize("name", ["img_v", "img_mod"])
-def test_c4_int8_layers_full(cr, name):
-    w, lin = _lin("c4", name)
-    say(f"c4 full {name} {lin.M}x{lin.N}x{lin.K}")
-    _int8_layer(cr, w, lin)
-
-
-@pytest.mark.parametrize("name", ["img_mlp_up", "img_mlp_down", "txt_q"])
-def test_c4_w4a4_layers_full(cr, name):
-    w, lin = _lin("c4", name)
-    say(f"c4 full {name} {lin.M}x{lin.N}x{lin.K}")
-    _w4a4_layer(cr, w, lin)
-
-
-def _w4a4_layer_f6(cr, w, lin, rows_n=32):
-    M, N, K = lin.M, lin.N, lin.K
-    xb, wb = wl.act_bits(w, lin.x_id), wl.weight_bits(w, lin)
-    xa = ol.rotate_quantize(xb, 256, "int4", "tensor")
-    wq = ol.rotate_quantize(wb, 256, "int4", "tensor")
-    codes, sa, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR,
-                                                 layout=cr.LAYOUT.F6)
-    assert np.array_equal(opack.f6_unpack(host(codes), M), xa["values"])
-    wf, ws, _, _ = cr.convrot_rotate_quantize(bf16_dev(wb), 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR,
-                                              layout=cr.LAYOUT.F6)
-    assert np.array_equal(bytes_of(wf), opack.f6_pack(wq["values"]).reshape(-1))
-    rows = _rows(M, rows_n, 53)
-    raw = host(cr.w4a4_gemm(codes, sa, 0, wf, ws, 0, M, N, K, out_type=cr.OUT.I32_RAW))
-    ref_raw = og.int_gemm(xa["values"][rows], wq["values"])
-    assert np.array_equal(raw[rows].astype(np.int64), ref_raw)
-    y = bf16_to_f32(host(cr.w4a4_gemm(codes, sa, 0, wf, ws, 0, M, N, K)))
-    ref_y = ol.epilogue_scalar(ref_raw, xa["scales"], "tensor", wq["scales"], "tensor")
-    assert rel_l2(y[rows], ref_y) <= 2e-3
-
-
-@pytest.mark.parametrize("name", ["img_mlp_up", "img_mlp_down", "txt_q"])
-def test_c4_w4a4_layers_full_f6(cr, name):
-    w, lin = _lin("c4", name)
-    say(f"c4 full fp6 {name} {lin.M}x{lin.N}x{lin.K}")
-    _w4a4_layer_f6(cr, w, lin)
+        assert np.array_equal(raw[r0:r1].astype(np.int64), np.rint(A[r0:r1] @ d.T).astype(np.int64))
+        ref = (s_a[r0:r1, None] * (A[r0:r1] @ w_hat.T)).astype(np.float32)
+        eb.add(yb[r0:r1], ref)
+        ef.add(yf[r0:r1], ref)
+    assert eb.rel() <= 2e-3, eb.rel()
+    assert ef.rel() <= 1e-5, ef.rel()
 
 
 @pytest.mark.parametrize("name", ["qkv", "mlp_down"])
 def test_c5_lowrank_g64_full(cr, name):
-    """Low-rank corrected W4A4 with 64-group scales (no rotation): rank-32
-    branch with the down-projection fused into the quantizer and the
-    up-projection into the GEMM epilogue; MLP down takes the unsigned
-    post-GELU path with the 0.171875 shift."""
-    w, lin = _lin("c5", name)
+    """Low-rank corrected W4A4 with 64-group scales (no rotation), as the
+    benchmark runs it: fp6 codes (unsigned post-GELU codes as u/2 for MLP
+    down, shift 0.171875), the rank-32 down-projection fused into the
+    quantizer, 4-bit weight tiles expanded per call, the up-projection fused
+    into the GEMM epilogue."""
+    r = _runner("c5")
+    lin = [l for l in r.w.linears if l.name == name][0]
     M, N, K = lin.M, lin.N, lin.K
     shift = lin.unsigned_shift
     uns = shift != 0.0
     say(f"c5 full {name} {M}x{N}x{K}")
-    xb = wl.act_bits(w, lin.x_id)
-    l1, l2, r = wl.lowrank_bits(w, lin)
-    xa = ol.rotate_quantize(xb, 0, "uint4_shift" if uns else "int4", "row_group", 64, shift)
-    la_ref = ol.lora_down(xb, l2)
-    wp = ol.prepare_w4a4(r, 0, "row_group", 64)
-    qt = cr.Q.UNSIGNED_INT4_SHIFT if uns else cr.Q.SYM_INT4
-    codes, sa, _, la = cr.convrot_rotate_quantize(bf16_dev(xb), 0, qt, cr.GRAN.ROW_GROUP, 64, shift=shift,
-                                                  lora_down=bf16_dev(l2), layout=cr.LAYOUT.TILED)
-    assert np.array_equal(opack.tile_unpack_a(bytes_of(codes).reshape((M + 15) // 16, K // 64, 512), M),
-                          xa["codes"])
-    assert np.array_equal(host(sa).view(np.uint32), np.asarray(xa["scales"], np.float32).view(np.uint32))
+    st = r.sets[0]
+    key = [k for l, k in r.gemm_plan if l.name == lin.name][0]
+    o, p = st["rq"][key], st["prep"][lin.name]
+    xb = wl.act_bits(r.w, lin.x_id)
+    l1, l2, res = wl.lowrank_bits(r.w, lin)
+    xa = _oracle_act(r.w, lin.x_id, "uint4_shift" if uns else "int4", "row_group", 0, 64, shift)
+    wp = ol.rotate_quantize(res, 0, "int4", "row_group", 64)
+    assert np.array_equal(opack.f6_unpack(host(o["codes"]), M) * (2 if uns else 1), xa["values"])
+    assert np.array_equal(host(o["scales"]).view(np.uint32), np.asarray(xa["scales"], np.float32).view(np.uint32))
+    assert np.array_equal(bytes_of(p["w"]), opack.tile_pack_w4a4(wp["codes"]).reshape(-1))
+    assert np.array_equal(host(p["ws"]).reshape(-1), opack.tile_pack_g64_scales(wp["scales"]).reshape(-1))
     # low-rank activations: bf16 of a float32 sum taken in another order -> within one bf16 ulp
+    la = host(o["la"])
     la_ref32 = ol.lora_down(xb, l2, act_f32=True).astype(np.float64)
     mag = np.abs(wl.f32_from_bf16_bits(xb)).astype(np.float64) @ np.abs(wl.f32_from_bf16_bits(l2)).astype(np.float64).T
-    got_la = wl.f32_from_bf16_bits(host(la)).astype(np.float64)
+    got_la = wl.f32_from_bf16_bits(la).astype(np.float64)
     assert np.all(np.abs(got_la - la_ref32) <= np.abs(la_ref32) * 2.0 ** -7 + mag * 2 ** -20 + 1e-30)
-    wc, ws, _, _ = cr.convrot_rotate_quantize(bf16_dev(r), 0, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64)
-    packed, pscales, _, wsum = cr.w4_pack_weights(wc, ws, N, K, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64,
-                                                  want_wsum=True)
-    assert np.array_equal(bytes_of(packed), wp["tiles"].reshape(-1))
-    assert np.array_equal(host(pscales).reshape(-1), wp["scales_tiles"].reshape(-1))
-    kw = dict(a_unsigned=uns, a_shift=shift, w_sum=wsum)
-    rows, cols = _rows(M, 16, 61), _cols(N, 1024, 61)
-    raw = host(cr.w4a4_gemm(codes, sa, 2, packed, pscales, 2, M, N, K, out_type=cr.OUT.I32_RAW, **kw))
-    ref_raw = og.int_gemm(xa["values"][rows], wp["values"])
-    assert np.array_equal(raw[rows].astype(np.int64), ref_raw)
-    y = bf16_to_f32(host(cr.w4a4_gemm(codes, sa, 2, packed, pscales, 2, M, N, K, lora_act=la,
-                                      lora_up=bf16_dev(l1), **kw)))
-    P = og.group_partials(xa["values"][rows], wp["values"][cols], 64)
-    ref_y = ol.epilogue_g64(P, np.asarray(xa["scales"])[rows], np.asarray(wp["scales"])[cols], shift,
-                            np.asarray(wp["wsum"])[cols], la_ref[rows], l1[cols])
-    assert rel_l2(y[np.ix_(rows, cols)], ref_y) <= 2e-3
-
-
-@pytest.mark.parametrize("name", ["qkv", "mlp_down"])
-def test_c5_lowrank_g64_full_f6(cr, name):
-    """The same layers on the fp6 matrix cores: codes (unsigned ones as u/2)
-    in fp6 fragments from the quantizer, weights through
-    w4_pack_weights_f6, 64-group scales and column sums from w4_pack_weights."""
-    w, lin = _lin("c5", name)
-    M, N, K = lin.M, lin.N, lin.K
-    shift = lin.unsigned_shift
-    uns = shift != 0.0
-    say(f"c5 full fp6 {name} {M}x{N}x{K}")
-    xb = wl.act_bits(w, lin.x_id)
-    l1, l2, r = wl.lowrank_bits(w, lin)
-    xa = ol.rotate_quantize(xb, 0, "uint4_shift" if uns else "int4", "row_group", 64, shift)
-    la_ref = ol.lora_down(xb, l2)
-    wp = ol.prepare_w4a4(r, 0, "row_group", 64)
-    qt = cr.Q.UNSIGNED_INT4_SHIFT if uns else cr.Q.SYM_INT4
-    codes, sa, _, la = cr.convrot_rotate_quantize(bf16_dev(xb), 0, qt, cr.GRAN.ROW_GROUP, 64, shift=shift,
-                                                  lora_down=bf16_dev(l2), layout=cr.LAYOUT.F6)
-    assert np.array_equal(opack.f6_unpack(host(codes), M) * (2 if uns else 1), xa["values"])
-    assert np.array_equal(host(sa).view(np.uint32), np.asarray(xa["scales"], np.float32).view(np.uint32))
-    wc, ws, _, _ = cr.convrot_rotate_quantize(bf16_dev(r), 0, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64)
-    _, pscales, _, wsum = cr.w4_pack_weights(wc, ws, N, K, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64, want_wsum=True)
-    wf = cr.w4_pack_weights_f6(wc, N, K)
-    assert np.array_equal(bytes_of(wf), opack.f6_pack(wp["values"]).reshape(-1))
-    kw = dict(a_unsigned=uns, a_shift=shift, w_sum=wsum)
-    rows, cols = _rows(M, 16, 62), _cols(N, 1024, 62)
-    raw = host(cr.w4a4_gemm(codes, sa, 2, wf, pscales, 2, M, N, K, out_type=cr.OUT.I32_RAW, **kw))
-    assert np.array_equal(raw[rows].astype(np.int64), og.int_gemm(xa["values"][rows], wp["values"]))
-    y = bf16_to_f32(host(cr.w4a4_gemm(codes, sa, 2, wf, pscales, 2, M, N, K, lora_act=la,
-                                      lora_up=bf16_dev(l1), **kw)))
-    P = og.group_partials(xa["values"][rows], wp["values"][cols], 64)
-    ref_y = ol.epilogue_g64(P, np.asarray(xa["scales"])[rows], np.asarray(wp["scales"])[cols], shift,
-                            np.asarray(wp["wsum"])[cols], la_ref[rows], l1[cols])
-    assert rel_l2(y[np.ix_(rows, cols)], ref_y) <= 2e-3
+    kw = dict(a_unsigned=uns, a_shift=shift, w_sum=p["wsum"])
+    raw = host(cr.w4a4_gemm(o["codes"], o["scales"], 2, p["w"], p["ws"], 2, M, N, K, out_type=cr.OUT.I32_RAW,
+                            workspace=st["gws"], **kw))
+    y = bf16_to_f32(host(st["out"][lin.name]))
+    wsum = ol.weight_sum(wp["values"], wp["scales"], "row_group", 64)
+    assert np.allclose(host(p["wsum"]), wsum, rtol=1e-5, atol=1e-5 * np.abs(wsum).max())
+    A = xa["values"].astype(np.float64)
+    W = wp["values"].astype(np.float64)
+    a_hat = A * np.repeat(np.asarray(xa["scales"], np.float64), 64, axis=1)
+    w_hat = W * np.repeat(np.asarray(wp["scales"], np.float64), 64, axis=1)
+    ones_m, ones_n = np.ones((M, 1)), np.ones((N, 1))
+    la_use = wl.f32_from_bf16_bits(la)            # the GPU's la (its own rounding is checked above)
+    err = _Err()
+    for r0, r1 in _chunks(M):
+        assert np.array_equal(raw[r0:r1].astype(np.int64), np.rint(A[r0:r1] @ W.T).astype(np.int64))
+        ydq = a_hat[r0:r1] @ w_hat.T
+        ref = ol.epilogue_g64(ydq[:, :, None], ones_m[r0:r1], ones_n, shift, wsum, la_use[r0:r1], l1)
+        err.add(y[r0:r1], ref)
+    assert err.rel() <= 2e-3, err.rel()

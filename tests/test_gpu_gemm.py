@@ -353,3 +353,30 @@ def test_extreme_codes_no_overflow(cr):
     raw8 = cr.int8_tensorwise_gemm(dev(q8.astype(np.int8)), one, dev(w8.astype(np.int8)), one, M, N, K8,
                                    out_type=2)
     assert np.array_equal(host(raw8).astype(np.int64), og.int_gemm(q8, w8))
+
+
+def test_gemm_determinism(cr):
+    """Repeated calls give bit-identical outputs: the fp6 W4A4 path (4-bit
+    weight tiles expanded per call), the int8-core W4A4 path, INT8 x INT8 and
+    W4A8, each twice on the same inputs."""
+    M, N, K = 1000, 768, 3072
+    say("gemm determinism")
+    xb = wl.activation(32, 0, M, K, n_outliers=3, outlier_scale=20.0)
+    wb = wl.weight(32, 1, N, K)
+    x, w = bf16_dev(xb), bf16_dev(wb)
+    wc, ws, _, _ = cr.convrot_rotate_quantize(w, 256, 0, 0)
+    wt = cr.w4_pack_weights(wc, ws, N, K)[0]
+    a6, s6, _, _ = cr.convrot_rotate_quantize(x, 256, 0, 0, layout=cr.LAYOUT.F6)
+    at, st, _, _ = cr.convrot_rotate_quantize(x, 256, 0, 0, layout=cr.LAYOUT.TILED)
+    a8, s8, _, _ = cr.convrot_rotate_quantize(x, 256, 1, 0)
+    w8, ws8, _, _ = cr.convrot_rotate_quantize(w, 256, 1, 0)
+    ah, sh, _, _ = cr.convrot_rotate_quantize(x, 256, 1, 1, layout=cr.LAYOUT.F16)
+    wa, wsa, wza, _ = cr.convrot_rotate_quantize(w, 256, 3, 2, 16)
+    pa, psa, pza, _ = cr.w4_pack_weights(wa, wsa, N, K, 3, 2, 16, zeros=wza)
+    calls = [lambda: cr.w4a4_gemm(a6, s6, 0, wt, ws, 0, M, N, K),
+             lambda: cr.w4a4_gemm(at, st, 0, wt, ws, 0, M, N, K),
+             lambda: cr.int8_tensorwise_gemm(a8, s8, w8, ws8, M, N, K),
+             lambda: cr.w4a8_gemm(ah, sh, 1, pa, psa, pza, M, N, K)]
+    for f in calls:
+        y0, y1 = host(f()), host(f())
+        assert np.array_equal(y0, y1)

@@ -9,7 +9,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 import workloads as wl  # noqa: E402
-from oracle import linear as ol, pack as opack  # noqa: E402
+from oracle import hadamard as oh, linear as ol, pack as opack  # noqa: E402
 from tests.gpu_helpers import bf16_dev, dev, host, bytes_of, say  # noqa: E402
 
 
@@ -441,3 +441,37 @@ def test_determinism(cr):
     a = cr.convrot_rotate_quantize(x, 256, 0, 0)
     b = cr.convrot_rotate_quantize(x, 256, 0, 0)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("qt,gran", [("int4", "tensor"), ("int4", "row"), ("int8", "tensor"), ("int8", "row")])
+def test_rotate_quantize_constructed_ties(cr, qt, gran):
+    """Round half to even through the GPU quantizer, on constructed ties: the
+    input is x = H v / 256 per 256-group (H H = 256 I), so the rotation
+    returns v exactly; v holds one value qmax 2^e per row (the maximum, so
+    r = qmax / A = 2^-e is exact) and values (k + 1/2) 2^e, whose codes must
+    come out as the even neighbour (v chosen so that x is exact in bf16)."""
+    qmax = 7 if qt == "int4" else 127
+    rows, K, e = 48, 512, -3
+    H = oh.regular_hadamard(256).astype(np.float64)
+    rng = np.random.default_rng(71 + qmax)
+    V = np.zeros((rows, K))
+    for r in range(rows):
+        V[r, rng.integers(0, 256)] = qmax * (1 if rng.random() < 0.5 else -1)
+        nt = 8 if qt == "int4" else 2          # keeps every x within bf16's 8 significant bits
+        kmax = qmax if qt == "int4" else 64
+        for j in rng.choice(256, nt, replace=False):
+            V[r, 256 + j] = (rng.integers(0, kmax) + 0.5) * (1 if rng.random() < 0.5 else -1)
+    V *= 2.0 ** e
+    X = np.concatenate([V[:, :256] @ H / 256.0, V[:, 256:] @ H / 256.0], axis=1)
+    xb = wl.bf16_bits_from_f32(X.astype(np.float32))
+    assert np.array_equal(wl.f32_from_bf16_bits(xb).astype(np.float64), X), "input not exact in bf16"
+    want = np.rint(V / 2.0 ** e).astype(np.int64)          # numpy rint: half to even
+    assert np.all(np.abs(want) <= qmax) and np.any(np.abs(V / 2.0 ** e - np.trunc(V / 2.0 ** e)) == 0.5)
+    ref = ol.rotate_quantize(xb, 256, qt, gran)
+    assert np.array_equal(ref["values"].astype(np.int64), want)
+    say(f"rq ties {qt} {gran}")
+    codes, scales, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), 256, QT[qt], GR[gran], 0)
+    got = host(codes)
+    vals = opack.unpack_int4(got, True) if qt == "int4" else got
+    assert np.array_equal(vals.astype(np.int64), want), "tie codes differ"
+    assert np.all(host(scales).reshape(-1) == np.float32(2.0 ** e / 16))
