@@ -206,6 +206,33 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
                                   hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * convrot_rotate_quantize_noalloc - convrot_rotate_quantize for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, formats and results (bit for bit) as
+ * convrot_rotate_quantize without the workspace pair: the block maxima of the
+ * per-tensor passes go to a fixed array of CONVROT_NOALLOC_SCRATCH_FLOATS
+ * floats (256 KiB) in device memory that the library holds on each GPU it runs
+ * on until the process ends. The call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine). Inputs whose per-tensor pass
+ * needs more block maxima than that, i.e. convrot_rq_workspace_size(...)
+ * above CONVROT_NOALLOC_SCRATCH_FLOATS * 4 bytes (one maximum per 16 rows x
+ * 1024 columns for large inputs: beyond about 2^30 elements, e.g. 65536 x
+ * 16384), return CR_ERR_WORKSPACE_TOO_SMALL with nothing enqueued. Every call on a GPU
+ * shares that GPU's array: calls that may overlap on one GPU (different
+ * streams, no ordering between them) race; calls ordered on one stream do
+ * not. The array's contents on entry are never read before being written.
+ */
+#define CONVROT_NOALLOC_SCRATCH_FLOATS 65536
+cr_status convrot_rotate_quantize_noalloc(const void* x, int64_t rows, int64_t K, int64_t ldx,
+                                          int rot_group, cr_qtype qtype, cr_gran gran, int q_group,
+                                          float shift, const float* smooth,
+                                          const void* lora_down, int R, void* lora_act, int lora_act_f32,
+                                          void* codes, cr_layout layout, void* scales, void* zeros,
+                                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * convrot_rotate_quantize_dual - per-tensor INT4 and INT8 codes of the same
  * rotated activation, from one rotation.
  *

@@ -261,3 +261,21 @@ def test_gemm_validation(cr):
                                   None, 0, None) == 1
     assert L.int8_tensorwise_gemm(_p(A), _p(A), _p(A), _p(A), None, _p(A), 0, 256, 64, 256, 512,
                                   None, 0, None) == 4
+
+
+def test_noalloc_validation(cr):
+    """The allocation-free rotate+quantize validates like the ordinary one and
+    refuses inputs whose per-tensor block maxima exceed its fixed scratch
+    array (checked before any device access: no device here)."""
+    L = cr.lib
+    def na(rows=64, K=512, q=0, g=0, layout=0):
+        return L.convrot_rotate_quantize_noalloc(_p(A), rows, K, K, 256, q, g, 0, 0.0, None, None, 0, None, 0,
+                                                 _p(A), layout, _p(A), None, None)
+    assert na() == 4                                          # valid: reaches the device check
+    assert na(q=1, layout=4) == 4
+    assert na(layout=5) == 1
+    need = cr.convrot_rq_workspace_size(1 << 21, 32768, 256, 0, 0)
+    assert need > 65536 * 4
+    assert na(rows=1 << 21, K=32768) == 6                     # beyond the scratch array
+    assert na(rows=1 << 21, K=32768, g=1) == 4                # per-row scales use no scratch
+    assert cr.convrot_rq_workspace_size(65536, 16384, 256, 0, 0) <= 65536 * 4

@@ -74,6 +74,8 @@ _SIGS = {
     "convrot_rq_workspace_size": (_sz, [_i64, _i64, _i, _i, _i, _i]),
     "convrot_rotate_quantize": (_i, [_vp, _i64, _i64, _i64, _i, _i, _i, _i, _f, _vp, _vp, _i, _vp, _i,
                                      _vp, _i, _vp, _vp, _vp, _sz, _vp]),
+    "convrot_rotate_quantize_noalloc": (_i, [_vp, _i64, _i64, _i64, _i, _i, _i, _i, _f, _vp, _vp, _i, _vp, _i,
+                                             _vp, _i, _vp, _vp, _vp]),
     "convrot_rotate_quantize_dual": (_i, [_vp, _i64, _i64, _i64, _i, _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "convrot_dequantize_weights": (_i, [_vp, _vp, _vp, _i64, _i64, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp]),
     "w4_packed_bytes": (_sz, [_i64, _i64, _i, _i, _i, _i]),

@@ -147,11 +147,13 @@ size_t convrot_rq_workspace_size(int64_t rows, int64_t K, int rot_group, cr_qtyp
   return (size_t)cr::rq_tensor_grid(rows, K, rot_group) * sizeof(float);   // one maximum per block of the first pass
 }
 
-cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx, int rot_group,
-                                  cr_qtype qtype, cr_gran gran, int q_group, float shift, const float* smooth,
-                                  const void* lora_down, int R, void* lora_act, int lora_act_f32,
-                                  void* codes, cr_layout layout, void* scales, void* zeros, void* workspace,
-                                  size_t workspace_bytes, hipStream_t stream) {
+// noalloc: the block maxima go to the library's fixed device scratch array
+// (the workspace arguments are ignored)
+static cr_status rotate_quantize_impl(const void* x, int64_t rows, int64_t K, int64_t ldx, int rot_group,
+                                      cr_qtype qtype, cr_gran gran, int q_group, float shift, const float* smooth,
+                                      const void* lora_down, int R, void* lora_act, int lora_act_f32,
+                                      void* codes, cr_layout layout, void* scales, void* zeros, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream, bool noalloc) {
   cr_status st = rq_validate(x, rows, K, ldx, rot_group, qtype, gran, q_group, lora_down, R, lora_act,
                              codes, scales, zeros);
   if (st != CR_OK) return st;
@@ -175,12 +177,20 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
       return CR_ERR_UNSUPPORTED_FORMAT;
   }
   const size_t need = convrot_rq_workspace_size(rows, K, rot_group, qtype, gran, q_group);
-  if (need > 0) {
+  if (noalloc) {
+    if (need > (size_t)cr::kNoallocScratchFloats * sizeof(float)) return CR_ERR_WORKSPACE_TOO_SMALL;
+  } else if (need > 0) {
     if (!workspace || !aligned16(workspace)) return CR_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < need) return CR_ERR_WORKSPACE_TOO_SMALL;
   }
   st = device_check();
   if (st != CR_OK) return st;
+  if (noalloc && need > 0) {
+    float* sp = nullptr;
+    const hipError_t e = cr::rq_noalloc_scratch(&sp);
+    if (e != hipSuccess) return hip_fail(e);
+    workspace = sp;
+  }
   cr::RQParams p{};
   p.x = static_cast<const uint16_t*>(x);
   p.rows = rows;
@@ -204,6 +214,25 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
   const uint64_t nl = ((rot_group != 0 && gran == CR_GRAN_TENSOR && qtype != CR_Q_ASYM_UINT4) ? 2 : 1) +
                       ((rot_group != 0 && lora_down) ? 1 : 0);
   return finish_launch(cr::launch_rotate_quantize(p, stream), E_RQ, nl);
+}
+
+cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_t ldx, int rot_group,
+                                  cr_qtype qtype, cr_gran gran, int q_group, float shift, const float* smooth,
+                                  const void* lora_down, int R, void* lora_act, int lora_act_f32,
+                                  void* codes, cr_layout layout, void* scales, void* zeros, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  return rotate_quantize_impl(x, rows, K, ldx, rot_group, qtype, gran, q_group, shift, smooth, lora_down, R,
+                              lora_act, lora_act_f32, codes, layout, scales, zeros, workspace, workspace_bytes,
+                              stream, false);
+}
+
+cr_status convrot_rotate_quantize_noalloc(const void* x, int64_t rows, int64_t K, int64_t ldx, int rot_group,
+                                          cr_qtype qtype, cr_gran gran, int q_group, float shift,
+                                          const float* smooth, const void* lora_down, int R, void* lora_act,
+                                          int lora_act_f32, void* codes, cr_layout layout, void* scales, void* zeros,
+                                          hipStream_t stream) {
+  return rotate_quantize_impl(x, rows, K, ldx, rot_group, qtype, gran, q_group, shift, smooth, lora_down, R,
+                              lora_act, lora_act_f32, codes, layout, scales, zeros, nullptr, 0, stream, true);
 }
 
 cr_status convrot_rotate_quantize_dual(const void* x, int64_t rows, int64_t K, int64_t ldx, int rot_group,

@@ -44,6 +44,10 @@ RQGeometry rq_geometry(int64_t rows, int64_t K, int gran_kind, int nr);
 // blocks of each per-tensor pass (one float of workspace each) for rotation group nr
 int rq_tensor_grid(int64_t rows, int64_t K, int nr);
 hipError_t launch_rotate_quantize(RQParams p, hipStream_t s);
+// device address of this GPU's fixed scratch array for the allocation-free
+// rotate+quantize (kNoallocScratchFloats block maxima)
+constexpr int kNoallocScratchFloats = 65536;
+hipError_t rq_noalloc_scratch(float** out);
 // per-tensor INT4 and INT8 codes of one rotation (two launches)
 hipError_t launch_rotate_quantize_dual(RQParams p, hipStream_t s);
 

@@ -30,11 +30,38 @@
 // those; a single pass with a grid-wide barrier measured slower on MI355X
 // because of the barrier's cross-XCD atomics), per row (blocks own whole
 // rows), per 64-group (a quad of lanes), asymmetric per 16-group (one lane).
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 #include "rotate.h"
 
 namespace cr {
+
+// Block maxima of the per-tensor passes for convrot_rotate_quantize_noalloc:
+// a fixed array in device memory (one copy per GPU, kept until the process
+// ends) used in place of a caller workspace. Host code never passes the
+// array's name to a kernel: rq_noalloc_scratch() returns its device address,
+// looked up once per device with that device current.
+static __device__ __align__(256) float scratch[kNoallocScratchFloats];
+
+hipError_t rq_noalloc_scratch(float** out) {
+  static std::mutex mu;
+  static float* ptr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = static_cast<float*>(p);
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
 
 // code bits: fl(fl(v * r) + 1.5*2^23); the low byte is the rounded integer
 CR_DEV uint32_t qbits(float v, float r) {
