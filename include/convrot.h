@@ -185,10 +185,17 @@ void convrot_reset_counters(void);
  *                (group 2j low nibble); NULL otherwise
  *   workspace    device scratch of at least convrot_rq_workspace_size(...)
  *                bytes (needed by TENSOR granularity; may be NULL when that
- *                size is 0). Contents on entry are ignored; it receives one
- *                maximum per block of the first of the two launches that
- *                per-tensor scaling takes. Calls sharing a workspace must not
- *                run concurrently.
+ *                size is 0). Per-tensor scaling takes one launch for inputs
+ *                of at most 64 groups of 256 (one workgroup), one launch
+ *                whose workgroups exchange their maxima through the
+ *                workspace while the grid fits one workgroup per compute
+ *                unit (e.g. 512 x 3072 on MI355X), else two launches (the
+ *                first writes one maximum per workgroup there). Any contents
+ *                on entry are valid: the exchange keeps an epoch counter in
+ *                the workspace and tags every value it writes with it, so the
+ *                workspace needs no clearing between calls (nor between
+ *                replays of a captured graph). Calls sharing a workspace must
+ *                not run concurrently.
  * Shape: rows >= 1, K % 256 == 0 and K % rot_group == 0 when rotating,
  *        K % 64 == 0 otherwise, K <= 32768.
  * Result is deterministic and bit-identical to the reference definition for
@@ -211,8 +218,9 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
  * serving loops, harnesses that forbid hipMalloc).
  *
  * Same arguments, formats and results (bit for bit) as
- * convrot_rotate_quantize without the workspace pair: the block maxima of the
- * per-tensor passes go to a fixed array of CONVROT_NOALLOC_SCRATCH_FLOATS
+ * convrot_rotate_quantize without the workspace pair: what the per-tensor
+ * passes keep in the workspace (block maxima, the one-launch exchange) goes
+ * to a fixed array of CONVROT_NOALLOC_SCRATCH_FLOATS
  * floats (256 KiB) in device memory that the library holds on each GPU it runs
  * on until the process ends. The call allocates nothing (no hipMalloc, no
  * hipFree, no allocating library routine). Inputs whose per-tensor pass
@@ -222,7 +230,8 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
  * 16384), return CR_ERR_WORKSPACE_TOO_SMALL with nothing enqueued. Every call on a GPU
  * shares that GPU's array: calls that may overlap on one GPU (different
  * streams, no ordering between them) race; calls ordered on one stream do
- * not. The array's contents on entry are never read before being written.
+ * not. The array's contents on entry are valid whatever they are (see the
+ * workspace of convrot_rotate_quantize).
  */
 #define CONVROT_NOALLOC_SCRATCH_FLOATS 65536
 cr_status convrot_rotate_quantize_noalloc(const void* x, int64_t rows, int64_t K, int64_t ldx,
@@ -245,8 +254,8 @@ cr_status convrot_rotate_quantize_noalloc(const void* x, int64_t rows, int64_t K
  * Equivalent, bit for bit, to convrot_rotate_quantize(x, ..., rot_group,
  * SYM_INT4, TENSOR, codes4, layout4, scale4) followed by the same call with
  * SYM_INT8, TENSOR, codes8 (natural int8 [rows, K]), scale8: both share the
- * maximum of the rotated tensor, which is computed once (two launches
- * instead of four).
+ * maximum of the rotated tensor, which is computed once (the launches of one
+ * per-tensor convrot_rotate_quantize instead of twice that).
  *   codes4   uint8 int4 codes, layout4 CR_LAYOUT_NATURAL [rows, K/2],
  *            CR_LAYOUT_TILED or CR_LAYOUT_F6; scale4 float32 [1]
  *   codes8   int8 [rows, K]; scale8 float32 [1]

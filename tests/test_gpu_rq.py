@@ -134,6 +134,93 @@ def test_rotate_quantize_tensor_mid(cr, rot, shape):
     assert np.array_equal(host(d8).view(np.uint8), r8["codes"].view(np.uint8))
 
 
+# Per-tensor plans on a 256-CU MI355X: at most 64 groups of 256 take one
+# workgroup; grids up to one workgroup per CU (256) with one or two groups per
+# segment (one for the 16 and 64 rotations) take one launch with the maxima
+# exchanged through the workspace; larger inputs take two launches. Cases
+# (shape, launches with the 256 rotation, with 16 and 64): (4, 4096) is 64
+# groups, (4, 4352) 68; (256, 4096) is exactly 256 workgroups of one group,
+# (272, 4096) one row block more; (672, 3072) is 252 workgroups of two
+# groups, (688, 3072) 258.
+PLAN_CASES = [((1, 256), 1, 1), ((2, 3072), 1, 1), ((4, 4096), 1, 1), ((4, 4352), 1, 1), ((256, 4096), 1, 1),
+              ((272, 4096), 1, 2), ((512, 3072), 1, 2), ((672, 3072), 1, 2), ((688, 3072), 2, 2),
+              ((4096, 3072), 2, 2)]
+
+
+@pytest.mark.parametrize("rot", [256, 64, 16])
+@pytest.mark.parametrize("case", PLAN_CASES, ids=lambda c: f"{c[0][0]}x{c[0][1]}")
+def test_rotate_quantize_tensor_plans(cr, rot, case):
+    """Every code layout, INT8 codes and the dual output at each plan
+    boundary, bit-exact against the oracle; launch counts as planned."""
+    (rows, K), l256, l_other = case
+    launches = l256 if rot == 256 else l_other
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        launches = None   # the plan follows the CU count
+    say(f"rq tensor plan rot {rot} {(rows, K)}")
+    xb = wl.activation(29, rows + K + rot, rows, K, n_outliers=max(1, K // 200), outlier_scale=25.0)
+    r4 = ol.rotate_quantize(xb, rot, "int4", "tensor")
+    r8 = ol.rotate_quantize(xb, rot, "int8", "tensor")
+    s4ref = np.asarray(r4["scales"], np.float32).reshape(-1).view(np.uint32)
+    s8ref = np.asarray(r8["scales"], np.float32).reshape(-1).view(np.uint32)
+    for layout in (0, 1, 3):
+        cr.reset_counters()
+        codes, scales, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), rot, 0, 0, layout=layout)
+        assert launches is None or cr.get_counters()["rotate_quantize"] == launches
+        got = host(codes)
+        if layout == 0:
+            assert np.array_equal(got, r4["codes"]), "natural codes differ"
+        elif layout == 1:
+            assert np.array_equal(opack.tile_unpack_a(got, rows), r4["codes"]), "tiled codes differ"
+        else:
+            assert np.array_equal(opack.f6_unpack(got, rows), r4["values"]), "fp6 codes differ"
+        assert np.array_equal(host(scales).view(np.uint32), s4ref)
+    c8, s8, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), rot, 1, 0)
+    assert np.array_equal(host(c8).view(np.uint8), r8["codes"].view(np.uint8))
+    assert np.array_equal(host(s8).view(np.uint32), s8ref)
+    h8, hs8, _, _ = cr.convrot_rotate_quantize(bf16_dev(xb), rot, 1, 0, layout=4)
+    assert np.array_equal(host(h8).view(np.uint16), r8["values"].astype(np.float16).view(np.uint16))
+    assert np.array_equal(host(hs8).view(np.uint32), s8ref)
+    for layout4 in (1, 3):
+        cr.reset_counters()
+        d4, ds4, d8, ds8 = cr.convrot_rotate_quantize_dual(bf16_dev(xb), rot, layout4=layout4)
+        assert launches is None or cr.get_counters()["rotate_quantize"] == launches
+        if layout4 == 1:
+            assert np.array_equal(opack.tile_unpack_a(host(d4), rows), r4["codes"])
+        else:
+            assert np.array_equal(opack.f6_unpack(host(d4), rows), r4["values"])
+        assert np.array_equal(host(ds4).view(np.uint32), s4ref)
+        assert np.array_equal(host(d8).view(np.uint8), r8["codes"].view(np.uint8))
+        assert np.array_equal(host(ds8).view(np.uint32), s8ref)
+
+
+def test_rotate_quantize_tensor_workspace_contents(cr):
+    """The one-launch exchange accepts any workspace contents and needs no
+    clearing: random bytes, an int64 count-up pattern, repeated calls (the
+    epoch moves on), a call with another grid size on the same workspace,
+    and a workspace shifted by 16 bytes all give the oracle's codes."""
+    shapes = [(300, 3072), (37, 3072), (700, 3072), (512, 3072)]
+    ref = {}
+    xs = {}
+    for rows, K in shapes:
+        xb = wl.activation(31, rows + K, rows, K, n_outliers=max(1, K // 200), outlier_scale=25.0)
+        xs[(rows, K)] = bf16_dev(xb)
+        r = ol.rotate_quantize(xb, 256, "int4", "tensor")
+        ref[(rows, K)] = (r["codes"], np.asarray(r["scales"], np.float32).reshape(-1).view(np.uint32))
+    need = max(cr.convrot_rq_workspace_size(r, K, 256, 0, 0) for r, K in shapes)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    rnd = torch.randint(0, 256, (need + 64,), dtype=torch.uint8, generator=g).to("cuda")
+    ramp = torch.arange((need + 64) // 8, dtype=torch.int64).view(torch.uint8).to("cuda")
+    for ws in (rnd, ramp):
+        seq = [shapes[0], shapes[0], shapes[1], shapes[0], shapes[2], shapes[1], shapes[0]]
+        for off in (0, 16):
+            w = ws[off:off + need]
+            for shp in seq:
+                say(f"rq workspace contents {shp} offset {off}")
+                codes, scales, _, _ = cr.convrot_rotate_quantize(xs[shp], 256, 0, 0, workspace=w)
+                assert np.array_equal(host(codes), ref[shp][0]), f"codes differ at {shp}"
+                assert np.array_equal(host(scales).view(np.uint32), ref[shp][1])
+
+
 def _check_lora_act(la, xb, l2, f32):
     la_ref32 = ol.lora_down(xb, l2, act_f32=True).astype(np.float64)
     mag = np.abs(wl.f32_from_bf16_bits(xb)).astype(np.float64) @ np.abs(wl.f32_from_bf16_bits(l2)).astype(np.float64).T

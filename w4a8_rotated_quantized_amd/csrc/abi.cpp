@@ -144,7 +144,7 @@ size_t convrot_rq_workspace_size(int64_t rows, int64_t K, int rot_group, cr_qtyp
   if (rot_group == 0 || gran != CR_GRAN_TENSOR || rows < 1 || K < 256 || K % 256) return 0;
   if (!(rot_group == 16 || rot_group == 64 || rot_group == 256 || (rot_group == 1024 && K % 1024 == 0))) return 0;
   if (!(qtype == CR_Q_SYM_INT4 || qtype == CR_Q_SYM_INT8)) return 0;
-  return (size_t)cr::rq_tensor_grid(rows, K, rot_group) * sizeof(float);   // one maximum per block of the first pass
+  return cr::rq_tensor_ws_bytes(rows, K, rot_group);
 }
 
 // noalloc: the block maxima go to the library's fixed device scratch array
@@ -211,7 +211,8 @@ static cr_status rotate_quantize_impl(const void* x, int64_t rows, int64_t K, in
   p.zeros = zeros;
   p.ws = static_cast<float*>(workspace);
   p.tiled = layout == CR_LAYOUT_TILED ? 1 : (layout == CR_LAYOUT_F6 ? 2 : (layout == CR_LAYOUT_F16 ? 3 : 0));
-  const uint64_t nl = ((rot_group != 0 && gran == CR_GRAN_TENSOR && qtype != CR_Q_ASYM_UINT4) ? 2 : 1) +
+  const uint64_t nl = ((rot_group != 0 && gran == CR_GRAN_TENSOR && qtype != CR_Q_ASYM_UINT4)
+                           ? (uint64_t)cr::rq_tensor_launches(rows, K, rot_group) : 1) +
                       ((rot_group != 0 && lora_down) ? 1 : 0);
   return finish_launch(cr::launch_rotate_quantize(p, stream), E_RQ, nl);
 }
@@ -266,7 +267,8 @@ cr_status convrot_rotate_quantize_dual(const void* x, int64_t rows, int64_t K, i
   p.scales8 = scale8;
   p.ws = static_cast<float*>(workspace);
   p.tiled = layout4 == CR_LAYOUT_TILED ? 1 : (layout4 == CR_LAYOUT_F6 ? 2 : 0);
-  return finish_launch(cr::launch_rotate_quantize_dual(p, stream), E_RQ, 2);
+  return finish_launch(cr::launch_rotate_quantize_dual(p, stream), E_RQ,
+                       (uint64_t)cr::rq_tensor_launches(rows, K, rot_group));
 }
 
 // ---------------------------------------------------------------------------

@@ -20,7 +20,7 @@ struct RQParams {
   void* codes;
   void* scales;
   void* zeros;
-  float* ws;            // TENSOR: one maximum per block of the first of the two passes
+  float* ws;            // TENSOR: block maxima (two-pass) or the one-pass exchange area
   int nblk;             // blocks of the TENSOR passes
   int G;                // 256-groups per row
   int rpb;              // rows per block (16 >> lg_spr)
@@ -41,14 +41,28 @@ struct RQGeometry {
 
 // gran_kind: 2 ROW (whole rows per block), 3 ROW_GROUP(64), 4 ASYM(16); nr: rotation group size
 RQGeometry rq_geometry(int64_t rows, int64_t K, int gran_kind, int nr);
-// blocks of each per-tensor pass (one float of workspace each) for rotation group nr
+// blocks of each pass of the two-pass per-tensor kernel (one float of workspace each)
 int rq_tensor_grid(int64_t rows, int64_t K, int nr);
+// per-tensor rotate+quantize on the current device: one block (TINY), one
+// launch with a grid-wide exchange of block maxima (ONEPASS, u groups per
+// segment, nb blocks) or two launches (TWOPASS)
+enum { RQT_TINY = 0, RQT_ONEPASS = 1, RQT_TWOPASS = 2 };
+struct TensorPlan {
+  int kind, u, nb;
+};
+TensorPlan rq_tensor_plan(int64_t rows, int64_t K, int nr);
+// launches of a per-tensor rotate+quantize on the current device (1 or 2)
+int rq_tensor_launches(int64_t rows, int64_t K, int nr);
+// largest grid of the one-pass kernel (also at most one block per CU)
+constexpr int kOnepassMaxBlocks = 2048;
+// workspace bytes of a per-tensor rotate+quantize, whichever plan a device takes
+size_t rq_tensor_ws_bytes(int64_t rows, int64_t K, int nr);
 hipError_t launch_rotate_quantize(RQParams p, hipStream_t s);
 // device address of this GPU's fixed scratch array for the allocation-free
 // rotate+quantize (kNoallocScratchFloats block maxima)
 constexpr int kNoallocScratchFloats = 65536;
 hipError_t rq_noalloc_scratch(float** out);
-// per-tensor INT4 and INT8 codes of one rotation (two launches)
+// per-tensor INT4 and INT8 codes of one rotation (plan as rq_tensor_plan)
 hipError_t launch_rotate_quantize_dual(RQParams p, hipStream_t s);
 
 struct PackParams {

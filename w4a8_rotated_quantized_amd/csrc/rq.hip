@@ -25,11 +25,14 @@
 // (digits b5b4 and b7b6, folded into sigma). All of it is undone exactly by
 // the sign of the quantization multiplier (fl(s*v*r) = s*fl(v*r)).
 //
-// Scale granularities: per tensor (a first launch writes one maximum per
-// block, a second recomputes the rotation and quantizes with the maximum of
-// those; a single pass with a grid-wide barrier measured slower on MI355X
-// because of the barrier's cross-XCD atomics), per row (blocks own whole
-// rows), per 64-group (a quad of lanes), asymmetric per 16-group (one lane).
+// Scale granularities: per tensor (small inputs: one block; inputs whose grid
+// fits one block per CU: one launch whose blocks keep their rotated values in
+// registers and exchange their maxima through the workspace; larger inputs:
+// a first launch writes one maximum per block, a second recomputes the
+// rotation and quantizes with the maximum of those), per row (blocks own
+// whole rows), per 64-group (a quad of lanes), asymmetric per 16-group (one
+// lane).
+#include <algorithm>
 #include <mutex>
 
 #include "common.h"
@@ -38,12 +41,17 @@
 
 namespace cr {
 
-// Block maxima of the per-tensor passes for convrot_rotate_quantize_noalloc:
-// a fixed array in device memory (one copy per GPU, kept until the process
+// Workspace of the per-tensor passes (block maxima, the one-launch exchange)
+// for convrot_rotate_quantize_noalloc: a fixed array in device memory (one copy per GPU, kept until the process
 // ends) used in place of a caller workspace. Host code never passes the
 // array's name to a kernel: rq_noalloc_scratch() returns its device address,
 // looked up once per device with that device current.
 static __device__ __align__(256) float scratch[kNoallocScratchFloats];
+
+// per-tensor scale: inputs of at most TINY_UNITS 256-groups take one block
+// (rq_tiny_kernel); larger ones take one launch (rq_onepass_kernel) while its
+// grid fits one block per CU, else two launches
+constexpr int TINY_UNITS = 64;
 
 hipError_t rq_noalloc_scratch(float** out) {
   static std::mutex mu;
@@ -766,6 +774,234 @@ __global__ __launch_bounds__(4 * RPB / 16 * 64) void rq_plain_kernel(RQParams a)
 }
 
 // ---------------------------------------------------------------------------
+// Per-tensor scale in ONE launch. Both kernels rotate every 256-group once,
+// keep the rotated values in registers until the maximum of the whole tensor
+// is known, then quantize them (no second read of X, no second rotation).
+//
+// rq_tiny: inputs of at most 64 groups (e.g. two rows of 3072). One block,
+// one group per 16-lane segment (segments past the end redo the last group:
+// same maximum, identical code bytes), maximum reduced in LDS.
+//
+// rq_onepass: the two-pass kernel's block -> data map (block b: 16 rows,
+// U consecutive groups) with a grid of at most one block per CU, so that the
+// whole grid is resident at once, and U of 1 or 2 (1 for the 16 and 64
+// rotations). Measured against the two launches: 512 x 3072 with U = 2
+// (192 blocks) 8.0 against 9.3 us, 32 x 3072 6.0 against 7.4 us; more
+// groups per lane lose (a single wave per SIMD rotates them one after the
+// other: 512 x 12288 with U = 6, 256 blocks, 13.5 against 11.0 us; two
+// blocks per CU with U = 4, 13.1 us). The block maxima meet in the workspace:
+//   bytes 0..7        epoch E (any initial value)
+//   bytes 16..31      result {tag, maximum}
+//   bytes 32 + 16 b   slot of block b {tag, maximum}
+// Every block reads E first, then writes its maximum and then the tag
+// mix(E + 1 + b 2^40) to its slot; block 0 waits for all tags, publishes the
+// maximum with the tag mix(E + 1 + (2^20 - 1) 2^40) and moves E on by one;
+// the other blocks wait for that tag. Every exchanged word is an agent-scope
+// atomic (coherent across XCDs by itself), and a tag is stored only after
+// the store of its maximum has completed (s_waitcnt): the order a release
+// gives these stores, without the L2 write-back a release adds for ordinary
+// stores, and without an L2 invalidation on the reading side (a release per
+// block and an acquire per slot measured 14-22 us at 384-512 blocks, against
+// 8-15 us). mix is a bijection
+// of 64-bit words, so a slot left by an earlier call (a smaller epoch) never
+// carries the expected tag, and any other leftover content does so with
+// probability 2^-64: the workspace needs no clearing, also under graph replay
+// (E lives in the workspace). Block 0 moves E on only after every block has
+// written its slot, i.e. after every block has read E. One workspace serves
+// one call at a time. Waits are bounded (about a second); a wait that runs out
+// (a grid that could not be resident at once) yields NaN scales.
+// ---------------------------------------------------------------------------
+
+CR_DEV uint64_t mix64(uint64_t z) {   // SplitMix64 output function (a bijection)
+  z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+  z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+  return z ^ (z >> 31);
+}
+CR_DEV uint64_t xtag(uint64_t e1, uint64_t id) { return mix64(e1 + (id << 40)); }
+constexpr uint64_t XRESULT = 0xFFFFFull;
+constexpr int XSPIN = 1 << 20;
+// the stores before it have completed (and the compiler keeps them there)
+CR_DEV void xstore_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+}
+// loads after it are issued after the loads before it have returned
+CR_DEV void xload_order() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+struct XSlot {
+  uint64_t tag;
+  float m;
+  uint32_t pad;
+};
+
+// scales and quantization multipliers of the per-tensor path from the maximum
+// A of the rotated tensor (NaN: the exchange ran out of time)
+template <int QT, bool DUAL, int NR>
+CR_DEV void write_tensor_scales(const RQParams& a, float A) {
+  const float qmax = (QT == CR_Q_SYM_INT8) ? 127.f : 7.f;
+  const bool lost = !(A >= 0.f);
+  const float sc = lost ? __int_as_float(0x7fc00000) : (A > 0.f) ? __fmul_rn(div_rn(A, qmax), RotSize<NR>::inv_sqrt) : 0.f;
+  reinterpret_cast<float*>(a.scales)[0] = sc;
+  if constexpr (DUAL) {
+    const float sc8 = lost ? __int_as_float(0x7fc00000) : (A > 0.f) ? __fmul_rn(div_rn(A, 127.f), RotSize<NR>::inv_sqrt) : 0.f;
+    reinterpret_cast<float*>(a.scales8)[0] = sc8;
+  }
+}
+
+template <int QT, bool DUAL, int NR>
+__global__ __launch_bounds__(1024) void rq_tiny_kernel(RQParams a) {
+  static_assert(NR != 1024, "the 1024 rotation spans four groups of a segment");
+  __shared__ float red[16];
+  const int tid = threadIdx.x;
+  const int seg = tid >> 4;
+  const LaneRot lr = lane_rot<NR>(tid & 15);
+  const float qmax = (QT == CR_Q_SYM_INT8) ? 127.f : 7.f;
+  const int G = a.G;
+  const int u = min(seg, (int)(a.rows * G) - 1);
+  const int64_t row = u / G;
+  const int grp = u % G;
+  const uint16_t* px = a.x + row * a.ldx + grp * 256 + lr.gL * 16;
+  u32x4 w[2];
+  w[0] = *reinterpret_cast<const u32x4*>(px);
+  w[1] = *reinterpret_cast<const u32x4*>(px + 8);
+  float v[16];
+  rotate_group<NR>(w, lr, v);
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; e += 2) m = amax3(m, fabsf(v[e]), fabsf(v[e + 1]));
+  m = wave_max(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  float A = red[0];
+  const int nw = (int)(blockDim.x >> 6);
+  for (int i = 1; i < nw; ++i) A = fmaxf(A, red[i]);
+  if (tid == 0) write_tensor_scales<QT, DUAL, NR>(a, A);
+  const float rq = lr.tau * ((A > 0.f) ? div_rn(qmax, A) : 0.f);
+  store_codes<QT>(v, rq, a, row, grp, lr.gL);
+  if constexpr (DUAL) {
+    RQParams a8 = a;
+    a8.codes = a.codes8;
+    const float rq8 = lr.tau * ((A > 0.f) ? div_rn(127.f, A) : 0.f);
+    quant_store<CR_Q_SYM_INT8>(v, rq8, code_dst<CR_Q_SYM_INT8>(a8, row, grp, lr.gL));
+  }
+}
+
+template <int QT, bool DUAL, int U, int NR>
+__global__ __launch_bounds__(256) void rq_onepass_kernel(RQParams a) {
+  static_assert(NR != 1024, "the 1024 rotation takes the two-pass kernel");
+  __shared__ float red[4];
+  __shared__ float gmax;
+  __shared__ uint64_t ep;
+  const int tid = threadIdx.x;
+  const int seg = tid >> 4;
+  const LaneRot lr = lane_rot<NR>(tid & 15);
+  const float qmax = (QT == CR_Q_SYM_INT8) ? 127.f : 7.f;
+  const int G = a.G;
+  const int GC = (G + U - 1) / U;
+  const int64_t row = imin64((int64_t)(blockIdx.x / (unsigned)GC) * 16 + seg, a.rows - 1);
+  const int g0 = (int)(blockIdx.x % (unsigned)GC) * U;
+  const uint16_t* xr = a.x + row * a.ldx + lr.gL * 16;
+  char* wsb = reinterpret_cast<char*>(a.ws);
+  uint64_t* E = reinterpret_cast<uint64_t*>(wsb);
+  XSlot* res = reinterpret_cast<XSlot*>(wsb + 16);
+  XSlot* slot = reinterpret_cast<XSlot*>(wsb + 32);
+
+  if (tid == 0) ep = __hip_atomic_load(E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  int grp[U];
+  u32x4 w[U][2];
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    grp[j] = min(g0 + j, G - 1);   // past the end: the last group again
+    const uint16_t* px = xr + grp[j] * 256;
+    w[j][0] = *reinterpret_cast<const u32x4*>(px);
+    w[j][1] = *reinterpret_cast<const u32x4*>(px + 8);
+  }
+  __builtin_amdgcn_sched_barrier(0);   // every load issued before the first use
+  float v[U][16];
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    rotate_group<NR>(w[j], lr, v[j]);
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) m = amax3(m, fabsf(v[j][e]), fabsf(v[j][e + 1]));
+  }
+  m = wave_max(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  const uint64_t e1 = ep + 1;
+  if (tid == 0) {
+    const float bm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __hip_atomic_store(&slot[blockIdx.x].m, bm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    xstore_order();
+    __hip_atomic_store(&slot[blockIdx.x].tag, xtag(e1, blockIdx.x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (blockIdx.x == 0) {
+    float g = 0.f;
+    bool ok = true;
+    for (int i = tid; i < (int)gridDim.x; i += 256) {
+      const uint64_t want = xtag(e1, (uint64_t)i);
+      int k = 0;
+      while (__hip_atomic_load(&slot[i].tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want && ++k < XSPIN)
+        __builtin_amdgcn_s_sleep(2);
+      ok = ok && k < XSPIN;
+      xload_order();
+      g = fmaxf(g, __hip_atomic_load(&slot[i].m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    }
+    g = wave_max(g);
+    __syncthreads();   // red[] of the block maximum is read
+    if ((tid & 63) == 0) red[tid >> 6] = g;
+    const int lost = __syncthreads_or(!ok);
+    if (tid == 0) {
+      float A = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      if (lost) A = __int_as_float(0x7fc00000);
+      gmax = A;
+      __hip_atomic_store(&res->m, A, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      xstore_order();
+      __hip_atomic_store(&res->tag, xtag(e1, XRESULT), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(E, e1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      write_tensor_scales<QT, DUAL, NR>(a, A);
+    }
+  } else if (tid == 0) {
+    const uint64_t want = xtag(e1, XRESULT);
+    int k = 0;
+    while (__hip_atomic_load(&res->tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want && ++k < XSPIN)
+      __builtin_amdgcn_s_sleep(2);
+    xload_order();
+    gmax = (k < XSPIN) ? __hip_atomic_load(&res->m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       : __int_as_float(0x7fc00000);
+  }
+  __syncthreads();
+  const float A = gmax;
+  const float rq = lr.tau * ((A > 0.f) ? div_rn(qmax, A) : 0.f);
+  const float rq8 = lr.tau * ((A > 0.f) ? div_rn(127.f, A) : 0.f);   // DUAL only
+  RQParams a8 = a;
+  a8.codes = a.codes8;
+  if (QT == CR_Q_SYM_INT4 && a.tiled == 2) {
+    // fp6 fragments: two groups per conversion, every lane of the row active
+#pragma unroll
+    for (int j = 0; j < U; j += 2) {
+      const int j1 = (j + 1 < U) ? j + 1 : j;
+      uint32_t w45[2];
+      const u32x4 o = f6_pack2(v[j], rq, v[j1], rq, w45);
+      f6_store_pair(o[0], o[1], o[2], a, row, grp[j], lr.gL);
+      if (j + 1 < U) f6_store_pair(o[3], w45[0], w45[1], a, row, grp[j1], lr.gL);
+      if constexpr (DUAL) {
+        quant_store<CR_Q_SYM_INT8>(v[j], rq8, code_dst<CR_Q_SYM_INT8>(a8, row, grp[j], lr.gL));
+        if (j + 1 < U) quant_store<CR_Q_SYM_INT8>(v[j1], rq8, code_dst<CR_Q_SYM_INT8>(a8, row, grp[j1], lr.gL));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      store_codes<QT>(v[j], rq, a, row, grp[j], lr.gL);
+      if constexpr (DUAL) quant_store<CR_Q_SYM_INT8>(v[j], rq8, code_dst<CR_Q_SYM_INT8>(a8, row, grp[j], lr.gL));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
@@ -836,6 +1072,84 @@ static int rq_tensor_j(int64_t rows, int64_t K, int nr) {
   if (units >= 2 * 256) return 2;
   return 1;
 }
+// compute units of the current device (cached per device)
+static int device_cus() {
+  static std::mutex mu;
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// one-pass groups per segment: the smallest whose grid fits the cap
+static int onepass_u(int64_t rb, int64_t G, int nr, int64_t cap) {
+  const int umax = (nr == 256) ? 2 : 1;
+  for (int u = 1; u <= umax; ++u)
+    if (rb * ((G + u - 1) / u) <= cap) return u;
+  return 0;
+}
+
+TensorPlan rq_tensor_plan(int64_t rows, int64_t K, int nr) {
+  const int64_t G = K / 256;
+  const int64_t rb = (rows + 15) / 16;
+  if (nr != 1024) {
+    if (rows * G <= TINY_UNITS) return TensorPlan{RQT_TINY, 1, 1};
+    const int64_t cap = std::min<int64_t>((int64_t)device_cus(), kOnepassMaxBlocks);
+    const int u = onepass_u(rb, G, nr, cap);
+    if (u > 0) return TensorPlan{RQT_ONEPASS, u, (int)(rb * ((G + u - 1) / u))};
+  }
+  return TensorPlan{RQT_TWOPASS, rq_tensor_j(rows, K, nr), rq_tensor_grid(rows, K, nr)};
+}
+
+int rq_tensor_launches(int64_t rows, int64_t K, int nr) {
+  return rq_tensor_plan(rows, K, nr).kind == RQT_TWOPASS ? 2 : 1;
+}
+
+size_t rq_tensor_ws_bytes(int64_t rows, int64_t K, int nr) {
+  const size_t two = (size_t)rq_tensor_grid(rows, K, nr) * sizeof(float);
+  if (nr == 1024) return two;
+  // any one-pass grid is at most the one of a single group per segment
+  const int64_t nb1 = ((rows + 15) / 16) * (K / 256);
+  const size_t one = 32 + 16 * (size_t)std::min<int64_t>(nb1, kOnepassMaxBlocks);
+  return std::max(two, one);
+}
+
+// resident blocks per CU of a one-pass instance (its grid needs one)
+template <typename KF>
+static int blocks_per_cu(KF kernel) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, 0) != hipSuccess) return 0;
+  return n;
+}
+
+template <int QT, bool DUAL, int U, int NR>
+static hipError_t launch_onepass_u(const RQParams& p, int nb, hipStream_t s) {
+  static const int occ = blocks_per_cu(rq_onepass_kernel<QT, DUAL, U, NR>);
+  if (occ < 1) return hipErrorLaunchOutOfResources;   // the exchange needs the whole grid resident
+  hipLaunchKernelGGL((rq_onepass_kernel<QT, DUAL, U, NR>), dim3((unsigned)nb), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int QT, bool DUAL, int NR>
+static hipError_t launch_tensor_onepass(const RQParams& p, const TensorPlan& t, hipStream_t s) {
+  if constexpr (NR == 256) {
+    if (t.u == 2) return launch_onepass_u<QT, DUAL, 2, NR>(p, t.nb, s);
+  }
+  return launch_onepass_u<QT, DUAL, 1, NR>(p, t.nb, s);
+}
+
+template <int QT, bool DUAL, int NR>
+static hipError_t launch_tensor_tiny(const RQParams& p, hipStream_t s) {
+  const int threads = (int)(((p.rows * p.G * 16) + 63) / 64 * 64);   // 16 lanes per group, whole waves
+  hipLaunchKernelGGL((rq_tiny_kernel<QT, DUAL, NR>), dim3(1), dim3((unsigned)threads), 0, s, p);
+  return hipGetLastError();
+}
 int rq_tensor_grid(int64_t rows, int64_t K, int nr) {   // blocks of each pass (one workspace float each)
   const int J = rq_tensor_j(rows, K, nr);
   const int64_t G = K / 256;
@@ -882,6 +1196,17 @@ static hipError_t launch_rotated(RQParams p, hipStream_t s) {
     }
   }
   if (p.gran == CR_GRAN_TENSOR) {
+    if constexpr (NR != 1024) {
+      const TensorPlan t = rq_tensor_plan(p.rows, p.K, NR);
+      if (t.kind == RQT_TINY) {
+        if (p.qtype == CR_Q_SYM_INT4) return launch_tensor_tiny<CR_Q_SYM_INT4, false, NR>(p, s);
+        return launch_tensor_tiny<CR_Q_SYM_INT8, false, NR>(p, s);
+      }
+      if (t.kind == RQT_ONEPASS) {
+        if (p.qtype == CR_Q_SYM_INT4) return launch_tensor_onepass<CR_Q_SYM_INT4, false, NR>(p, t, s);
+        return launch_tensor_onepass<CR_Q_SYM_INT8, false, NR>(p, t, s);
+      }
+    }
     const int gd = rq_tensor_grid(p.rows, p.K, NR);
     const int J = rq_tensor_j(p.rows, p.K, NR);
     p.nblk = gd;
@@ -935,6 +1260,11 @@ static hipError_t launch_rotated(RQParams p, hipStream_t s) {
 
 template <int NR>
 static hipError_t launch_dual(RQParams p, hipStream_t s) {
+  if constexpr (NR != 1024) {
+    const TensorPlan t = rq_tensor_plan(p.rows, p.K, NR);
+    if (t.kind == RQT_TINY) return launch_tensor_tiny<CR_Q_SYM_INT4, true, NR>(p, s);
+    if (t.kind == RQT_ONEPASS) return launch_tensor_onepass<CR_Q_SYM_INT4, true, NR>(p, t, s);
+  }
   const int gd = rq_tensor_grid(p.rows, p.K, NR);
   const int J = rq_tensor_j(p.rows, p.K, NR);
   p.nblk = gd;
