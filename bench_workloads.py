@@ -5,9 +5,13 @@ times whole steps and single calls with HIP events on the launch stream.
 A step runs every rotate+quantize the workload needs (one per activation
 tensor and code format: layers that share an input share the pass; an input
 that feeds both INT4 and INT8 layers is quantized once to both) and every
-GEMM, in order, on one stream, with inputs resident in HBM. Each step uses
-the next buffer set (inputs, weights, codes, workspaces, outputs), so
-consecutive steps read data the previous step did not touch.
+GEMM, with inputs resident in HBM. With the "chains" schedule each chain of
+layers (an independent token stream: the image and text tokens of an MMDiT
+block) runs in order on a stream of its own; the streams join before the step
+ends, and the next step starts after the whole of it. The "serial" schedule
+(step_serial) runs the same calls in order on one stream. Each step uses the
+next buffer set (inputs, weights, codes, workspaces, outputs), so consecutive
+steps read data the previous step did not touch.
 
 Formats on the measured path:
   * W4A4 weights are stored tile-packed at 4 bits per code (w4_pack_weights).
@@ -91,7 +95,7 @@ def gemm_bytes(lin):
 class Runner:
     """One workload on the GPU path with `nsets` cold buffer sets."""
 
-    def __init__(self, name, cores="fp6", nsets=2, rot=256, workload=None):
+    def __init__(self, name, cores="fp6", nsets=2, rot=256, workload=None, schedule="serial"):
         import numpy as np
         import torch
         import w4a8_rotated_quantized_amd as cr
@@ -107,6 +111,7 @@ class Runner:
         dev = self.dev
         w = self.w
         self.rq_plan, self.gemm_plan = plan(w, cores)
+        self.chains = list(dict.fromkeys(lin.chain for lin in w.linears))
 
         def bf16(a):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -135,7 +140,7 @@ class Runner:
                 wc, ws, _, _ = cr.convrot_rotate_quantize(bf16(r), 0, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64)
                 p, ps, _, wsum = cr.w4_pack_weights(wc, ws, N, K, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64,
                                                     want_wsum=True)
-                prep[lin.name] = dict(w=p, ws=ps, wsum=wsum, l1=bf16(l1), l2=bf16(l2))
+                prep[lin.name] = dict(w=p, ws=ps, wsum=wsum, l1=cr.w4_pack_lora_up(bf16(l1)), l2=bf16(l2))
         torch.cuda.synchronize()
         self.setup_s = time.time() - t0
 
@@ -153,7 +158,10 @@ class Runner:
         for si in range(nsets):
             st = {"acts": {k: (v if si == 0 else v.clone()) for k, v in acts.items()},
                   "prep": {k: {kk: (vv if si == 0 else vv.clone()) for kk, vv in d.items()} for k, d in prep.items()},
-                  "gws": torch.empty(ws_bytes, dtype=torch.uint8, device=dev), "rq": {}}
+                  "rq": {}}
+            # one GEMM workspace (weight expansion target) per chain: chains may run concurrently
+            st["gws_c"] = {c: torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for c in self.chains}
+            st["gws"] = st["gws_c"][self.chains[0]]
             for key in self.rq_plan:
                 x_id, kind, lname = key
                 M, K = w.acts[x_id][0], w.acts[x_id][1]
@@ -192,7 +200,23 @@ class Runner:
                 done.add(key)
             self.order.append((f"gemm:{lin.name}", lambda si, l=lin, k=key: self.launch_gemm(si, l, k)))
 
+        # Chains schedule of a step: every chain (independent token stream)
+        # in its order on a stream of its own.
+        self.corder = {c: [] for c in self.chains}
+        for lab, fn in self.order:
+            c = self._chain_of(lab)
+            self.corder[c].append(fn)
+        self.side = [torch.cuda.Stream() for _ in range(len(self.chains) - 1)]
+        self.schedule = schedule if len(self.chains) > 1 else "serial"
+
     # ------------------------------------------------------------------
+    def _chain_of(self, label):
+        kind, _, rest = label.partition(":")
+        if kind == "gemm":
+            return [l for l in self.w.linears if l.name == rest][0].chain
+        x_id = rest.split(":")[0]
+        return [l for l in self.w.linears if l.x_id == x_id][0].chain
+
     def _lay4(self, M):
         return self.cr.LAYOUT.F6 if self.f6_codes(M) else self.cr.LAYOUT.TILED
 
@@ -233,7 +257,7 @@ class Runner:
         wq, wlay = (p["w"], cr.LAYOUT.TILED) if w_override is None else w_override
         if lin.fmt == "w4a4":
             cr.w4a4_gemm(o["codes"], o["scales"], 0, wq, p["ws"], 0, M, N, K, out=y, w_layout=wlay,
-                         workspace=st["gws"])
+                         workspace=st["gws_c"][lin.chain])
         elif lin.fmt == "a8w4":
             cr.w4a4_gemm(o["codes"], o["scales"], cr.GRAN.ROW, p["w"], p["ws"], 0, M, N, K, out=y,
                          a_layout=cr.LAYOUT.INT8)
@@ -245,27 +269,62 @@ class Runner:
         else:
             cr.w4a4_gemm(o["codes"], o["scales"], 2, wq, p["ws"], 2, M, N, K,
                          a_unsigned=lin.unsigned_shift != 0.0, a_shift=lin.unsigned_shift, w_sum=p["wsum"],
-                         lora_act=o["la"], lora_up=p["l1"], out=y, w_layout=wlay, workspace=st["gws"])
+                         lora_act=o["la"], lora_up=p["l1"], out=y, w_layout=wlay, workspace=st["gws_c"][lin.chain])
 
     # ------------------------------------------------------------------
-    def step(self, i):
+    def step_serial(self, i):
+        """one step on one stream, every call in order (expansions inside the GEMM calls)"""
         for _, fn in self.order:
             fn(i % self.nsets)
+
+    def step(self, i):
+        """one step on the runner's schedule: "serial" (step_serial) or
+        "chains": chain 0 on the launch stream, the others on side streams
+        that start after an event recorded at the step's start and join the
+        launch stream before the step ends (the next step starts after the
+        whole of this one); launches are issued round robin over the chains."""
+        if self.schedule == "serial":
+            self.step_serial(i)
+            return
+        torch = self.torch
+        si = i % self.nsets
+        main = self.stream
+        start = torch.cuda.Event()
+        start.record(main)
+        for s in self.side:
+            s.wait_event(start)
+        streams = [main] + self.side
+        lists = [self.corder[c] for c in self.chains]
+        for pos in range(max(len(l) for l in lists)):
+            for s, l in zip(streams, lists):
+                if pos < len(l):
+                    with torch.cuda.stream(s):
+                        l[pos](si)
+        for s in self.side:
+            ev = torch.cuda.Event()
+            ev.record(s)
+            main.wait_event(ev)
 
     def _events(self, n):
         return [self.torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
-    def time_steps(self, steps, warmup):
+    def time_steps(self, steps, warmup, schedule=None):
+        """ms per step on `schedule` ("serial" or "chains"; None: the runner's)"""
         torch = self.torch
+        keep = self.schedule
+        if schedule is not None and len(self.chains) > 1:
+            self.schedule = schedule
+        step = self.step
         for i in range(warmup):
-            self.step(i)
+            step(i)
         torch.cuda.synchronize()
         e0, e1 = self._events(2)
         e0.record(self.stream)
         for i in range(steps):
-            self.step(i)
+            step(i)
         e1.record(self.stream)
         torch.cuda.synchronize()
+        self.schedule = keep
         return e0.elapsed_time(e1) / steps
 
     def per_call(self, reps):
@@ -312,7 +371,7 @@ class Runner:
         for si in range(self.nsets):
             self.launch_gemm(si, lin, key)     # fills set si's workspace with the expanded weights
             n = (lin.N // 32) * (lin.K // 64) * 1536
-            exp.append(self.sets[si]["gws"][:n].view(lin.N // 32, lin.K // 64, 1536))
+            exp.append(self.sets[si]["gws_c"][lin.chain][:n].view(lin.N // 32, lin.K // 64, 1536))
         self.torch.cuda.synchronize()
         return lambda si: self.launch_gemm(si, lin, key, (exp[si], cr.LAYOUT.F6))
 
@@ -334,6 +393,7 @@ def run(name, steps, warmup, cores="fp6"):
         sys.exit(3)
     r = Runner(name, cores)
     ms = r.time_steps(steps, warmup)
+    ms_chains = r.time_steps(steps, warmup, schedule="chains") if len(r.chains) > 1 else None
     kern = r.per_call(max(3, steps // 2))
     layers = {}
     for lin, _ in r.gemm_plan:
@@ -352,7 +412,9 @@ def run(name, steps, warmup, cores="fp6"):
     print(json.dumps({
         "metric": "effective TOPS of fused rotate+quant+W4 GEMM (% INT8 MFMA peak); GB/s",
         "value": round(eff, 2), "unit": "TOPS", "n_gpus": 1, "steps": steps, "warmup": warmup,
-        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "ms_per_step": round(ms, 5),
+        "ms_per_step_chains_on_streams": None if ms_chains is None else round(ms_chains, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "int4 / int8 codes (exact integer products)", "data": "synthetic",
         "config": {"workload": r.w.name, "layers": len(r.w.linears), "total_GOP": round(r.ops() / 1e9, 1),
                    "w4a4_matrix_cores": cores, "buffer_sets": r.nsets},

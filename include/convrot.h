@@ -321,6 +321,40 @@ size_t w4_packed_f6_bytes(int64_t N, int64_t K);
 cr_status w4_pack_weights_f6(const void* codes, int64_t N, int64_t K, void* packed, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * w4_pack_lora_up - the low-rank up-projection L1 into its tiled layout, the
+ * form w4a4_gemm and w4a8_gemm read.
+ *
+ * Cites: "Qwen-Image-Edit-2511 INT4 (ComfyUI Optimized)", Tile-Packed Weight
+ * Format (LoRA-up stored (N/128, R, 128) beside the weight tiles).
+ *
+ *   up      bf16 [N, R], row n = output channel (16-byte aligned)
+ *   packed  bf16 [N/128][R][128]: element (t, r, i) = up[128 t + i, r]
+ * A call of its own, so that a LoRA can be swapped without repacking the
+ * quantized weight. Shape: N % 128 == 0, R = 32 or 64. One launch on `stream`.
+ */
+cr_status w4_pack_lora_up(const void* up, int64_t N, int R, void* packed, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * w4_expand_weights_f6 - tile-packed INT4 weights -> CR_LAYOUT_F6 fragments:
+ * the expansion that w4a4_gemm runs in its workspace for CR_LAYOUT_F6 codes
+ * against CR_LAYOUT_TILED weights, as a call of its own, so that a caller
+ * can run it on another stream ahead of the GEMM (it reads weights only) and
+ * then call w4a4_gemm with w_layout CR_LAYOUT_F6 on the result.
+ *
+ * Cites: "Qwen-Image-Edit-2511 INT4 (ComfyUI Optimized)", Tile-Packed Weight
+ * Format (weights stored at 4 bits in the GEMM's operand tiles).
+ *
+ *   tiles   uint8 [N/128][K/64][4096]: SYM_INT4 codes from w4_pack_weights
+ *           (CR_GRAN_TENSOR or CR_GRAN_ROW), 4 bits per code; every code must
+ *           lie in [-7, 7] (as the quantizer produces them)
+ *   f6      uint8, w4_packed_f6_bytes(N, K) bytes: receives the same bytes as
+ *           w4_pack_weights_f6 of the natural codes
+ * Shape: N % 128 == 0, K % 128 == 0, K <= 32768. One streaming launch on
+ * `stream` (reads N K / 2 bytes, writes 3 N K / 4).
+ */
+cr_status w4_expand_weights_f6(const void* tiles, int64_t N, int64_t K, void* f6, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * convrot_dequantize_weights - quantized weights back to bf16 in the
  * original (unrotated) basis, plus an optional low-rank delta: merging a LoRA
  * into quantized weights.
@@ -388,7 +422,8 @@ cr_status convrot_dequantize_weights(const void* codes, const void* scales, cons
  *   scale pairs: (TENSOR|ROW) x (TENSOR|ROW), or ROW_GROUP x ROW_GROUP (group 64)
  *   w_sum       float32 [N], required iff a_unsigned
  *   lora_act    optional [M, R] (bf16, or float32 if lora_act_f32), R = 32 or 64;
- *   lora_up     bf16 [N, R] (row n = output channel): y += lora_act @ lora_up^T
+ *   lora_up     L1 (row n = output channel) in the tiled layout of
+ *               w4_pack_lora_up, bf16 [N/128][R][128]: y += lora_act @ L1^T
  *   bias        optional bf16 [N]
  *   out         CR_OUT_BF16: bf16 [M, ldc]; CR_OUT_F32: float32; CR_OUT_I32_RAW:
  *               int32 sum_k qa*qw (lora/bias/scales ignored)
@@ -429,8 +464,9 @@ cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
  *   w_packed, w_scales (fp16), w_zeros (uint8): from w4_pack_weights (ASYM_UINT4)
  *   lora_act   optional [M, R], bf16 (lora_act_f32 = 0) or float32 (1), R = 32
  *              or 64 (e.g. from convrot_rotate_quantize's lora_down with
- *              rotation), with lora_up bf16 [N, R]: the low-rank bypass of a
- *              LoRA kept beside the quantized weight, y += la @ lora_up^T
+ *              rotation), with lora_up = L1 in the tiled layout of
+ *              w4_pack_lora_up (bf16 [N/128][R][128]): the low-rank bypass of
+ *              a LoRA kept beside the quantized weight, y += la @ L1^T
  *   Every 16-deep group's partial P[m, n, g] = sum_{k in g} qa[m,k] (qw[n,k] -
  *   z[n, g]) is formed exactly (fp16 matrix cores on the exact integers).
  *   CR_OUT_BF16 / CR_OUT_F32: y[m, n] = s_a[m] * acc[m, n] (+ low rank) + bias[n]

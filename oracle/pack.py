@@ -33,6 +33,9 @@ Readings where the pages are silent:
   * per-group scales of the W4A4 g64 format: float32 [N/128][K/64][128]
     (the pages' wscales layout); W4A8 g16 scales (fp16) and zero points
     (one byte each) : [N/128][K/64][4][128].
+  * the low-rank up-projection L1 [N, R] (bf16) in the pages' tiled layout
+    [N/128][R][128]: for every block of 128 output channels, rank index r
+    major and the 128 channels contiguous.
 """
 from __future__ import annotations
 
@@ -197,6 +200,14 @@ def tile_pack_g16(per_group: np.ndarray) -> np.ndarray:
     a = np.asarray(per_group)
     N, G = a.shape
     return np.ascontiguousarray(a.reshape(N // 128, 128, G // 4, 4).transpose(0, 2, 3, 1))
+
+
+def tile_pack_lora_up(up: np.ndarray) -> np.ndarray:
+    """L1 [N, R] -> [N/128, R, 128] ([P3] Tile-Packed Weight Format, LoRA-up):
+    element (tn, r, i) is L1[128*tn + i, r]."""
+    a = np.asarray(up)
+    N, R = a.shape
+    return np.ascontiguousarray(a.reshape(N // 128, 128, R).transpose(0, 2, 1))
 
 
 def pack_zeros_u4(zeros: np.ndarray) -> np.ndarray:

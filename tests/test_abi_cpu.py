@@ -191,6 +191,16 @@ def test_pack_validation(cr):
     assert L.w4_pack_weights_f6(_p(A), 128, 448, _p(A), None) == 2
     assert L.w4_pack_weights_f6(None, 128, 512, _p(A), None) == 1
     assert L.w4_pack_weights_f6(_p(A), 128, 512, _p(A + 4), None) == 1
+    assert L.w4_pack_lora_up(_p(A), 256, 32, _p(A), None) == 4
+    assert L.w4_pack_lora_up(_p(A), 200, 32, _p(A), None) == 2
+    assert L.w4_pack_lora_up(_p(A), 256, 16, _p(A), None) == 3
+    assert L.w4_pack_lora_up(None, 256, 32, _p(A), None) == 1
+    assert L.w4_expand_weights_f6(_p(A), 128, 512, _p(A), None) == 4
+    assert L.w4_expand_weights_f6(_p(A), 100, 512, _p(A), None) == 2
+    assert L.w4_expand_weights_f6(_p(A), 128, 448, _p(A), None) == 2
+    assert L.w4_expand_weights_f6(_p(A), 128, 65536, _p(A), None) == 2
+    assert L.w4_expand_weights_f6(None, 128, 512, _p(A), None) == 1
+    assert L.w4_expand_weights_f6(_p(A + 4), 128, 512, _p(A), None) == 1
     assert cr.w4_packed_bytes(256, 512, 0, 2, 64, 1) == 256 * 8 * 4
     assert cr.w4_packed_bytes(256, 512, 3, 2, 16, 2) == 256 * 32
 

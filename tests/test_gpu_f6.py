@@ -136,6 +136,11 @@ def test_w4a4_f6_gemm(cr, case):
     yb_t = cr.w4a4_gemm(a, sa, GR[ag], wt, sw, GR[wg], M, N, K, out_type=0, workspace=ws)
     assert np.array_equal(host(yb_t), host(yb))
     assert np.array_equal(bytes_of(ws), host(w).reshape(-1))      # the expansion is the fp6 weight image
+    # the expansion as a call of its own: the same bytes, and the GEMM on them
+    f6w = cr.w4_expand_weights_f6(wt, N, K)
+    assert np.array_equal(bytes_of(f6w), host(w).reshape(-1))
+    yb_e = cr.w4a4_gemm(a, sa, GR[ag], f6w, sw, GR[wg], M, N, K, out_type=0)
+    assert np.array_equal(host(yb_e), host(yb))
 
 
 def test_w4a4_f6_ldc_padding(cr):
@@ -189,7 +194,8 @@ def test_f6_rejects_unsupported(cr):
     with pytest.raises(cr.ConvRotError, match="format not available"):
         cr.w4a4_gemm(a, s, 0, w, s, 0, M, N, K, a_unsigned=True, a_shift=0.171875, w_sum=s)
     with pytest.raises(cr.ConvRotError, match="format not available"):
-        cr.w4a4_gemm(a, s, 1, w, s, 1, M, N, K, lora_act=lr, lora_up=lr[:, :32].contiguous())
+        cr.w4a4_gemm(a, s, 1, w, s, 1, M, N, K, lora_act=lr,
+                     lora_up=torch.zeros((N // 128, 32, 128), dtype=torch.bfloat16, device="cuda"))
     x = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(cr.ConvRotError, match="format not available"):
         cr.convrot_rotate_quantize(x, 256, 1, 0, 0, layout=F6)  # INT8 codes
@@ -266,7 +272,7 @@ def test_w4a4_f6_group64(cr, case):
     la = lu = None
     if lora:
         la = dev(ref["la"]) if lora == "f32" else bf16_dev(wl.bf16_bits_from_f32(ref["la"]))
-        lu = bf16_dev(l1)
+        lu = bf16_dev(opack.tile_pack_lora_up(l1))
     kw = dict(a_unsigned=uns, a_shift=shift, w_sum=wsum, lora_act=la, lora_up=lu,
               bias=None if bias is None else bf16_dev(bias))
     raw = cr.w4a4_gemm(a, sa, 2, w, sw, 2, M, N, K, out_type=2, **kw)

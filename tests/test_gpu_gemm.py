@@ -177,7 +177,7 @@ def test_w4a4_group64_lowrank(cr, case):
     la = lu = None
     if lora:
         la = dev(ref["la"]) if lora == "f32" else bf16_dev(wl.bf16_bits_from_f32(ref["la"]))
-        lu = bf16_dev(l1)
+        lu = bf16_dev(opack.tile_pack_lora_up(l1))
     kw = dict(a_unsigned=uns, a_shift=shift, w_sum=wsum, lora_act=la, lora_up=lu,
               bias=None if bias is None else bf16_dev(bias))
     raw = cr.w4a4_gemm(a, sa, 2, w, sw, 2, M, N, K, out_type=2, **kw)
@@ -302,10 +302,10 @@ def test_w4a8_lora_bypass(cr, R, la_f32):
     args = (a, sa, 1, *_w4a8_args(cr, wp), M, N, K)
     # the epilogue on the oracle's la (identical inputs): float32 bar
     la_ref = dev(ref["la"]) if la_f32 else bf16_dev(wl.bf16_bits_from_f32(ref["la"]))
-    kw = dict(lora_act=la_ref, lora_up=bf16_dev(l1), bias=bf16_dev(bias))
+    kw = dict(lora_act=la_ref, lora_up=bf16_dev(opack.tile_pack_lora_up(l1)), bias=bf16_dev(bias))
     _check_out(cr.w4a8_gemm(*args, out_type=0, **kw), cr.w4a8_gemm(*args, out_type=1, **kw), ref["y"])
     # end to end with the GPU's la (its rounding may differ by one ulp): bf16 bar
-    ye = cr.w4a8_gemm(*args, out_type=0, lora_act=la, lora_up=bf16_dev(l1), bias=bf16_dev(bias))
+    ye = cr.w4a8_gemm(*args, out_type=0, lora_act=la, lora_up=bf16_dev(opack.tile_pack_lora_up(l1)), bias=bf16_dev(bias))
     assert rel_l2(bf16_to_f32(host(ye)), ref["y"]) <= 2e-3
 
 
@@ -326,11 +326,11 @@ def test_w4a4_lora_rank(cr, R):
     sw = dev(np.asarray(wp["scales"], np.float32).reshape(-1))
     # the epilogue on the oracle's la (identical inputs): float32 bar
     la_ref = bf16_dev(wl.bf16_bits_from_f32(ref["la"]))
-    yf = cr.w4a4_gemm(a, sa, 0, w, sw, 0, M, N, K, lora_act=la_ref, lora_up=bf16_dev(l1), out_type=1)
-    yb = cr.w4a4_gemm(a, sa, 0, w, sw, 0, M, N, K, lora_act=la_ref, lora_up=bf16_dev(l1), out_type=0)
+    yf = cr.w4a4_gemm(a, sa, 0, w, sw, 0, M, N, K, lora_act=la_ref, lora_up=bf16_dev(opack.tile_pack_lora_up(l1)), out_type=1)
+    yb = cr.w4a4_gemm(a, sa, 0, w, sw, 0, M, N, K, lora_act=la_ref, lora_up=bf16_dev(opack.tile_pack_lora_up(l1)), out_type=0)
     _check_out(yb, yf, ref["y"])
     # end to end with the GPU's la (its bf16 rounding may differ by one ulp): bf16 bar
-    ye = cr.w4a4_gemm(a, sa, 0, w, sw, 0, M, N, K, lora_act=la, lora_up=bf16_dev(l1), out_type=0)
+    ye = cr.w4a4_gemm(a, sa, 0, w, sw, 0, M, N, K, lora_act=la, lora_up=bf16_dev(opack.tile_pack_lora_up(l1)), out_type=0)
     assert rel_l2(bf16_to_f32(host(ye)), ref["y"]) <= 2e-3
 
 

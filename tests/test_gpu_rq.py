@@ -508,6 +508,18 @@ def test_pack_w4a8(cr, shape):
     assert np.array_equal(host(pzeros).reshape(-1), ref["zeros_tiles"].reshape(-1))
 
 
+@pytest.mark.parametrize("shape", [(128, 32), (384, 64), (3072, 32)])
+def test_pack_lora_up(cr, shape):
+    """L1 [N, R] -> [N/128, R, 128] on the GPU, byte-exact against the oracle."""
+    N, R = shape
+    say(f"pack lora_up {shape}")
+    rng = np.random.default_rng(N + R)
+    up = rng.integers(0, 1 << 16, size=(N, R), dtype=np.uint16)
+    got = cr.w4_pack_lora_up(bf16_dev(up))
+    assert tuple(got.shape) == (N // 128, R, 128)
+    assert np.array_equal(host(got).reshape(-1), opack.tile_pack_lora_up(up).reshape(-1))
+
+
 def test_pack_sampled_tiles_full_size(cr):
     # full-size MLP-up weight (12288 x 3072): GPU pack vs oracle pack of sampled tiles
     N, K = 12288, 3072

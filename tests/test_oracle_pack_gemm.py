@@ -99,6 +99,20 @@ def test_group_scale_tiles():
     assert tz[0, 2, 3, 9] == z[9, 11]
 
 
+def test_lora_up_tiles():
+    """[N/128][R][128]: one 128-channel block's rank vectors are R runs of
+    128 contiguous channels (positions worked out by hand)."""
+    up = np.arange(256 * 32, dtype=np.int64).reshape(256, 32)       # N=256, R=32: up[n, r] = 32 n + r
+    t = pack.tile_pack_lora_up(up)
+    assert t.shape == (2, 32, 128)
+    flat = t.reshape(-1)
+    assert flat[0] == 0 and flat[1] == 32 and flat[127] == 127 * 32      # r = 0 of channels 0..127
+    assert flat[128] == 1                                                 # r = 1 of channel 0
+    assert flat[32 * 128] == 128 * 32                                     # block 1 starts at channel 128
+    assert flat[32 * 128 + 5 * 128 + 7] == (128 + 7) * 32 + 5            # channel 135, r = 5
+    assert np.array_equal(np.sort(flat), np.arange(256 * 32))
+
+
 def _triple_loop(a, b):
     M, K = len(a), len(a[0])
     N = len(b)

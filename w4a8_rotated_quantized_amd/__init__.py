@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "ConvRotError", "lib", "Q", "GRAN", "OUT", "LAYOUT",
     "convrot_rotate_quantize", "convrot_rotate_quantize_dual", "convrot_dequantize_weights", "w4_pack_weights",
-    "w4_pack_weights_f6", "w4_packed_f6_bytes",
+    "w4_pack_weights_f6", "w4_packed_f6_bytes", "w4_expand_weights_f6", "w4_pack_lora_up",
     "w4a4_gemm", "w4a4_gemm_workspace_size", "w4a8_gemm",
     "int8_tensorwise_gemm", "convrot_rq_workspace_size", "w4_packed_bytes",
     "get_counters", "reset_counters", "device_check", "status_string",
@@ -82,6 +82,8 @@ _SIGS = {
     "w4_pack_weights": (_i, [_vp, _vp, _vp, _i64, _i64, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "w4_packed_f6_bytes": (_sz, [_i64, _i64]),
     "w4_pack_weights_f6": (_i, [_vp, _i64, _i64, _vp, _vp]),
+    "w4_expand_weights_f6": (_i, [_vp, _i64, _i64, _vp, _vp]),
+    "w4_pack_lora_up": (_i, [_vp, _i64, _i, _vp, _vp]),
     "w4a4_gemm_workspace_size": (_sz, [_i64, _i64, _i, _i]),
     "w4a4_gemm": (_i, [_vp, _i, _vp, _i, _i, _f, _vp, _i, _vp, _i, _vp, _vp, _i, _vp, _i, _vp,
                        _vp, _i, _i64, _i64, _i64, _i64, _vp, _sz, _vp]),
@@ -273,11 +275,41 @@ def w4_pack_weights_f6(codes, N, K, packed=None, stream=None):
     return packed
 
 
+def w4_pack_lora_up(up, packed=None, stream=None):
+    """Low-rank up-projection L1 bf16 [N, R] -> tiled bf16 [N/128, R, 128]
+    (the lora_up operand of w4a4_gemm and w4a8_gemm)."""
+    N, R = up.shape
+    if packed is None:
+        packed = torch.empty((N // 128, R, 128), dtype=torch.bfloat16, device=up.device)
+    st = lib.w4_pack_lora_up(_ptr(up), N, R, _ptr(packed), _stream(stream))
+    _check(st, "w4_pack_lora_up")
+    return packed
+
+
+def w4_expand_weights_f6(tiles, N, K, f6=None, stream=None):
+    """Tile-packed INT4 weights (w4_pack_weights) -> fp6 E2M3 fragments
+    uint8 [N/32, K/64, 1536] (w_layout F6 of w4a4_gemm)."""
+    if f6 is None:
+        f6 = torch.empty((N // 32, K // 64, 1536), dtype=torch.uint8, device=tiles.device)
+    st = lib.w4_expand_weights_f6(_ptr(tiles), N, K, _ptr(f6), _stream(stream))
+    _check(st, "w4_expand_weights_f6")
+    return f6
+
+
 def _out(M, N, out_type, dev, out):
     if out is not None:
         return out
     dt = {OUT.BF16: torch.bfloat16, OUT.F32: torch.float32, OUT.I32_RAW: torch.int32}[out_type]
     return torch.empty((M, N), dtype=dt, device=dev)
+
+
+def _lora_rank(lora_up, N):
+    """R of the tiled low-rank up-projection [N/128, R, 128] (0 without one)"""
+    if lora_up is None:
+        return 0
+    if lora_up.dim() != 3 or lora_up.shape[0] * 128 != N or lora_up.shape[2] != 128:
+        raise ValueError("lora_up must be tiled [N/128, R, 128] (w4_pack_lora_up)")
+    return lora_up.shape[1]
 
 
 def w4a4_gemm_workspace_size(N, K, a_layout, w_layout) -> int:
@@ -292,7 +324,8 @@ def w4a4_gemm(a_codes, a_scales, a_gran, w_packed, w_scales, w_gran, M, N, K,
     [N/32, K/64, 1536] weights (w4_pack_weights_f6), else TILED
     (w4_pack_weights). With F6 codes and TILED weights the call needs a
     workspace of w4a4_gemm_workspace_size bytes (allocated here when not
-    given) into which it expands the weights before the fp6 GEMM."""
+    given) into which it expands the weights before the fp6 GEMM.
+    lora_up is L1 tiled by w4_pack_lora_up [N/128, R, 128]."""
     if a_layout is None:
         if a_codes.dim() == 3:
             a_layout = LAYOUT.F6 if a_codes.shape[-1] == 1536 else LAYOUT.TILED
@@ -306,7 +339,7 @@ def w4a4_gemm(a_codes, a_scales, a_gran, w_packed, w_scales, w_gran, M, N, K,
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     out = _out(M, N, out_type, a_codes.device, out)
     lora_f32 = int(lora_act is not None and lora_act.dtype == torch.float32)
-    R = 0 if lora_up is None else lora_up.shape[1]
+    R = _lora_rank(lora_up, N)
     st = lib.w4a4_gemm(_ptr(a_codes), int(a_layout), _ptr(a_scales), a_gran, int(bool(a_unsigned)), float(a_shift),
                        _ptr(w_packed), int(w_layout), _ptr(w_scales), w_gran, _ptr(w_sum),
                        _ptr(lora_act), lora_f32, _ptr(lora_up), R, _ptr(bias),
@@ -319,12 +352,12 @@ def w4a8_gemm(a_codes, a_scales, a_gran, w_packed, w_scales, w_zeros, M, N, K, g
               bias=None, out_type=OUT.BF16, out=None, stream=None, lora_act=None, lora_up=None, a_layout=None):
     """a_codes: int8 [M, K] (NATURAL) or float16 [M, K] (F16, the quantizer's
     fp16-carried codes); a_layout defaults from the dtype. lora_act [M, R]
-    (bf16 or float32) with lora_up bf16 [N, R] (R = 32 or 64) adds the
-    low-rank bypass."""
+    (bf16 or float32) with L1 bf16 (R = 32 or 64) adds the
+    low-rank bypass; lora_up is L1 tiled by w4_pack_lora_up [N/128, R, 128]."""
     if a_layout is None:
         a_layout = LAYOUT.F16 if a_codes.dtype == torch.float16 else LAYOUT.NATURAL
     out = _out(M, N, out_type, a_codes.device, out)
-    R = 0 if lora_up is None else lora_up.shape[1]
+    R = _lora_rank(lora_up, N)
     lora_f32 = int(lora_act is not None and lora_act.dtype == torch.float32)
     st = lib.w4a8_gemm(_ptr(a_codes), int(a_layout), _ptr(a_scales), a_gran, _ptr(w_packed), _ptr(w_scales),
                        _ptr(w_zeros), group, _ptr(lora_act), lora_f32, _ptr(lora_up), R, _ptr(bias),

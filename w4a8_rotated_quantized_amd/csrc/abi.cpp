@@ -350,6 +350,27 @@ cr_status w4_pack_weights_f6(const void* codes, int64_t N, int64_t K, void* pack
                        E_PACK, 1);
 }
 
+cr_status w4_pack_lora_up(const void* up, int64_t N, int R, void* packed, hipStream_t stream) {
+  if (!up || !packed || !aligned16(up) || !aligned16(packed)) return CR_ERR_INVALID_ARGUMENT;
+  if (N < 128 || N % 128 || N >= DIM_MAX) return CR_ERR_UNSUPPORTED_SHAPE;
+  if (R != 32 && R != 64) return CR_ERR_UNSUPPORTED_FORMAT;
+  cr_status st = device_check();
+  if (st != CR_OK) return st;
+  return finish_launch(cr::launch_pack_lora_up(static_cast<const uint16_t*>(up), N, R, static_cast<uint16_t*>(packed),
+                                               stream),
+                       E_PACK, 1);
+}
+
+cr_status w4_expand_weights_f6(const void* tiles, int64_t N, int64_t K, void* f6, hipStream_t stream) {
+  if (!tiles || !f6 || !aligned16(tiles) || !aligned16(f6)) return CR_ERR_INVALID_ARGUMENT;
+  if (N < 128 || K < 128 || N % 128 || K % 128 || K > KMAX || N >= DIM_MAX) return CR_ERR_UNSUPPORTED_SHAPE;
+  if ((N / 32) * (K / 64) * 1536 >= ((int64_t)1 << 32)) return CR_ERR_UNSUPPORTED_SHAPE;
+  cr_status st = device_check();
+  if (st != CR_OK) return st;
+  return finish_launch(cr::launch_expand_f6(static_cast<const uint8_t*>(tiles), N, K, static_cast<uint8_t*>(f6), stream),
+                       E_PACK, 1);
+}
+
 cr_status w4_pack_weights(const void* codes, const void* scales, const void* zeros, int64_t N, int64_t K,
                           cr_qtype qtype, cr_gran gran, int q_group, void* packed, void* packed_scales,
                           void* packed_zeros, float* w_sum, hipStream_t stream) {

@@ -30,6 +30,23 @@ CR_DEV uint32_t f32_to_bf16_bits(float f) {
 
 CR_DEV int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
 
+// The low-rank up-projection L1 in its tiled layout [N/128][R][128] (for each
+// block of 128 output channels, rank-major runs of 128 channels: "Qwen-Image-
+// Edit-2511 INT4 (ComfyUI Optimized)", Tile-Packed Weight Format):
+// rank entries r .. r+7 of channel n as one bf16 operand fragment (eight
+// 2-byte reads 256 bytes apart; the 32 or 16 channels of a fragment row read
+// one contiguous run per entry), and one entry as a float.
+CR_DEV v8bf lora_up8(const uint16_t* up, int R, int64_t n, int r) {
+  const uint16_t* q = up + ((n >> 7) * R + r) * 128 + (n & 127);
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = (uint32_t)q[(2 * i) * 128] | ((uint32_t)q[(2 * i + 1) * 128] << 16);
+  return __builtin_bit_cast(v8bf, w);
+}
+CR_DEV float lora_up1(const uint16_t* up, int R, int64_t n, int r) {
+  return __uint_as_float((uint32_t)up[((n >> 7) * R + r) * 128 + (n & 127)] << 16);
+}
+
 CR_DEV float amax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // Correctly rounded float32 quotient: the double quotient of two float32

@@ -27,7 +27,8 @@ CR_DEV void store4(const GemmParams& p, int64_t m, int64_t n, const float (&y)[4
   }
 }
 
-// y += lora_act[m, :] . lora_up[n..n+3, :] for the 16x16 block (tokens mb.., channels nb..)
+// y += lora_act[m, :] . L1[n..n+3, :] for the 16x16 block (tokens mb.., channels nb..),
+// L1 in the tiled layout [N/128][R][128]
 CR_DEV void lora_up_block(const GemmParams& p, int64_t mb, int64_t nb, int l, float (&y)[4]) {
   const int64_t mrow = (mb + (l & 15) < p.M) ? mb + (l & 15) : p.M - 1;
   const int64_t nrow = nb + (l & 15);
@@ -36,16 +37,14 @@ CR_DEV void lora_up_block(const GemmParams& p, int64_t mb, int64_t nb, int l, fl
   if (!p.lora_f32) {
     for (int r0 = 0; r0 < R; r0 += 32) {
       const uint16_t* la = reinterpret_cast<const uint16_t*>(p.lora_act) + mrow * R + r0 + (l >> 4) * 8;
-      const uint16_t* lu = p.lora_up + nrow * R + r0 + (l >> 4) * 8;
-      v8bf a = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(lu));
+      v8bf a = lora_up8(p.lora_up, R, nrow, r0 + (l >> 4) * 8);
       v8bf b = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(la));
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
     }
   } else {
     const float* la = reinterpret_cast<const float*>(p.lora_act) + mrow * R;
-    const uint16_t* lu = p.lora_up + nrow * R;
     for (int r0 = 0; r0 < R; r0 += 4) {
-      float a = __uint_as_float((uint32_t)lu[r0 + (l >> 4)] << 16);
+      float a = lora_up1(p.lora_up, R, nrow, r0 + (l >> 4));
       float b = la[r0 + (l >> 4)];
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
     }

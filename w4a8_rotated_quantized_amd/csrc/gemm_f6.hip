@@ -332,7 +332,7 @@ CR_DEV void f6_lowrank_32(const GemmParams& p, int64_t m0w, int64_t n0w, int l, 
   const int R = p.R;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const uint16_t* lu = p.lora_up + (n0w + j * 32 + lr) * R;
+    const int64_t n = n0w + j * 32 + lr;   // L1 in the tiled layout [N/128][R][128]
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int64_t mr = imin64(m0w + i * 32 + lr, p.M - 1);
@@ -340,12 +340,12 @@ CR_DEV void f6_lowrank_32(const GemmParams& p, int64_t m0w, int64_t n0w, int l, 
         const uint16_t* la = reinterpret_cast<const uint16_t*>(p.lora_act) + mr * R;
         for (int r0 = 0; r0 < R; r0 += 16)
           y[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(lu + r0 + 8 * h)),
+              lora_up8(p.lora_up, R, n, r0 + 8 * h),
               __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(la + r0 + 8 * h)), y[i][j], 0, 0, 0);
       } else {
         const float* la = reinterpret_cast<const float*>(p.lora_act) + mr * R;
         for (int r0 = 0; r0 < R; r0 += 2)
-          y[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float((uint32_t)lu[r0 + h] << 16), la[r0 + h],
+          y[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(lora_up1(p.lora_up, R, n, r0 + h), la[r0 + h],
                                                          y[i][j], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);

@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256, 2) void gemm_w4a8_kernel(GemmParams p) {
       const int R = p.R;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const uint16_t* lu = p.lora_up + (nw0 + j * 32 + lr) * R;
+        const int64_t n = nw0 + j * 32 + lr;   // L1 in the tiled layout [N/128][R][128]
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
           const int64_t mr = imin64(mw + i * 32 + lr, p.M - 1);
@@ -296,11 +296,11 @@ __global__ __launch_bounds__(256, 2) void gemm_w4a8_kernel(GemmParams p) {
             for (int r0 = 0; r0 < R; r0 += 16)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                   __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(la + r0 + 8 * h)),
-                  __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(lu + r0 + 8 * h)), acc[i][j], 0, 0, 0);
+                  lora_up8(p.lora_up, R, n, r0 + 8 * h), acc[i][j], 0, 0, 0);
           } else {
             const float* la = reinterpret_cast<const float*>(p.lora_act) + mr * R;
             for (int r0 = 0; r0 < R; r0 += 2)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(la[r0 + h], __uint_as_float((uint32_t)lu[r0 + h] << 16),
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(la[r0 + h], lora_up1(p.lora_up, R, n, r0 + h),
                                                                acc[i][j], 0, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);            // one block's operands live at a time

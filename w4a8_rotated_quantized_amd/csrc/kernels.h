@@ -79,6 +79,8 @@ struct PackParams {
 hipError_t launch_pack(const PackParams& p, hipStream_t s);
 // natural int4 [N, K/2] -> fp6 E2M3 fragments [N/32][K/64][1536 B]
 hipError_t launch_pack_f6(const uint8_t* codes, int64_t N, int64_t K, uint8_t* packed, hipStream_t s);
+// low-rank up-projection L1 [N, R] bf16 -> tiled [N/128][R][128]
+hipError_t launch_pack_lora_up(const uint16_t* up, int64_t N, int R, uint16_t* out, hipStream_t s);
 // tile-packed int4 [N/128][K/64][4096 B] -> fp6 E2M3 fragments [N/32][K/64][1536 B]
 hipError_t launch_expand_f6(const uint8_t* tiles, int64_t N, int64_t K, uint8_t* packed, hipStream_t s);
 
@@ -111,7 +113,7 @@ struct GemmParams {
   const float* w_sum;
   const void* lora_act;
   int lora_f32;
-  const uint16_t* lora_up;
+  const uint16_t* lora_up;   // L1, tiled [N/128][R][128] bf16
   int R;
   const uint16_t* bias;
   void* out;

@@ -193,6 +193,23 @@ hipError_t launch_expand_f6(const uint8_t* tiles, int64_t N, int64_t K, uint8_t*
   return hipGetLastError();
 }
 
+// L1 [N, R] bf16 -> [N/128][R][128]: one thread per output element (the
+// writes are contiguous, the reads gather R-strided 2-byte entries)
+__global__ __launch_bounds__(256) void pack_lora_up_kernel(const uint16_t* __restrict__ up, int64_t N, int R,
+                                                           uint16_t* __restrict__ out) {
+  const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (o >= N * R) return;
+  const int64_t tn = o / (128 * (int64_t)R);
+  const int r = (int)((o / 128) % R);
+  const int i = (int)(o % 128);
+  out[o] = up[(tn * 128 + i) * R + r];
+}
+
+hipError_t launch_pack_lora_up(const uint16_t* up, int64_t N, int R, uint16_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(pack_lora_up_kernel, dim3(nblocks(N * R)), dim3(256), 0, s, up, N, R, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_f6(const uint8_t* codes, int64_t N, int64_t K, uint8_t* packed, hipStream_t s) {
   hipLaunchKernelGGL(pack_f6_kernel, dim3(nblocks((N / 32) * (K / 64) * 64)), dim3(256), 0, s, codes, N, K, packed);
   return hipGetLastError();

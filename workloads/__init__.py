@@ -122,6 +122,9 @@ class LinearSpec:
          "a8w4" (W4A4-format weights, tensorwise, x per-token int8 activations)
     x_id: which activation tensor feeds it (layers that share an input share
           one rotate+quantize pass).
+    chain: layers of one chain run in order; different chains are independent
+           (the image and text token streams of an MMDiT block) and may run
+           concurrently.
     """
     name: str
     fmt: str
@@ -132,6 +135,7 @@ class LinearSpec:
     rot: int = 256
     unsigned_shift: float = 0.0
     rank: int = 0
+    chain: str = ""
 
 
 @dataclass
@@ -172,15 +176,15 @@ def _c4(m_img: int = 8192, m_txt: int = 512, m_mod: int = 2):
         w.acts[f"{s}_mlp"] = (M, 3072, "normal", 0, 1.0)
         w.acts[f"{s}_gelu"] = (M, 12288, "gelu", 0, 1.0)
         w.linears += [
-            LinearSpec(f"{s}_q", "w4a4", M, 3072, 3072, f"{s}_attn"),
-            LinearSpec(f"{s}_k", "w4a4", M, 3072, 3072, f"{s}_attn"),
-            LinearSpec(f"{s}_v", "int8", M, 3072, 3072, f"{s}_attn"),
-            LinearSpec(f"{s}_out", "int8", M, 3072, 3072, f"{s}_attnout"),
-            LinearSpec(f"{s}_mlp_up", "w4a4", M, 12288, 3072, f"{s}_mlp"),
-            LinearSpec(f"{s}_mlp_down", "w4a4", M, 3072, 12288, f"{s}_gelu"),
+            LinearSpec(f"{s}_q", "w4a4", M, 3072, 3072, f"{s}_attn", chain=s),
+            LinearSpec(f"{s}_k", "w4a4", M, 3072, 3072, f"{s}_attn", chain=s),
+            LinearSpec(f"{s}_v", "int8", M, 3072, 3072, f"{s}_attn", chain=s),
+            LinearSpec(f"{s}_out", "int8", M, 3072, 3072, f"{s}_attnout", chain=s),
+            LinearSpec(f"{s}_mlp_up", "w4a4", M, 12288, 3072, f"{s}_mlp", chain=s),
+            LinearSpec(f"{s}_mlp_down", "w4a4", M, 3072, 12288, f"{s}_gelu", chain=s),
         ]
         w.acts[f"{s}_mod"] = (m_mod, 3072, "normal", 0, 1.0)
-        w.linears.append(LinearSpec(f"{s}_mod", "int8", m_mod, 18432, 3072, f"{s}_mod"))
+        w.linears.append(LinearSpec(f"{s}_mod", "int8", m_mod, 18432, 3072, f"{s}_mod", chain=s))
     return w
 
 
@@ -200,7 +204,7 @@ def _c2pair():
     w = Workload(2, "MMDiT projection W4A4 tensorwise ConvRot (4096 + 32)x3072x3072")
     for M in (4096, 32):
         w.acts[f"x{M}"] = (M, 3072, "normal", 15, 30.0)
-        w.linears.append(LinearSpec(f"proj{M}", "w4a4", M, 3072, 3072, f"x{M}"))
+        w.linears.append(LinearSpec(f"proj{M}", "w4a4", M, 3072, 3072, f"x{M}", chain=f"m{M}"))
     return w
 
 
