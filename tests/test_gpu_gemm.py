@@ -192,25 +192,31 @@ def test_w4a4_group64_lowrank(cr, case):
 
 
 # M <= 64: weight streaming; above: the direct-to-LDS kernel of 256 x 128
-# blocks (2600 x 3072: 264 of them, a ragged last row block)
-INT8_CASES = [(2, 256, 3072), (33, 384, 512), (64, 128, 256), (190, 256, 1024), (512, 384, 3072), (2600, 3072, 256)]
+# blocks (2600 x 3072: 264 of them, a ragged last row block; 8000 x 3072:
+# 768, the three-blocks-per-CU ring on a 256-CU part, ragged too; with a bias
+# the same shape keeps two blocks per CU)
+INT8_CASES = [(2, 256, 3072), (33, 384, 512), (64, 128, 256), (190, 256, 1024), (512, 384, 3072), (2600, 3072, 256),
+              (8000, 3072, 256)]
 
 
+@pytest.mark.parametrize("bias", [False, True])
 @pytest.mark.parametrize("case", INT8_CASES)
-def test_int8_tensorwise(cr, case):
+def test_int8_tensorwise(cr, case, bias):
     M, N, K = case
-    say(f"int8 {case}")
+    say(f"int8 {case} bias {bias}")
     xb = wl.activation(24, M + K, M, K, n_outliers=2, outlier_scale=15.0)
     wb = wl.weight(24, N + K, N, K)
-    ref = ol.int8_linear(xb, wb)
+    bb = wl.weight(25, N, 1, N).reshape(-1) if bias else None
+    ref = ol.int8_linear(xb, wb, bias_bits=bb)
     a = dev(ref["x"]["codes"])
     sa = dev(ref["x"]["scales"])
     w = dev(ref["w"]["codes"])
     sw = dev(ref["w"]["scales"])
+    b = bf16_dev(bb) if bias else None
     raw = cr.int8_tensorwise_gemm(a, sa, w, sw, M, N, K, out_type=2)
     assert np.array_equal(host(raw).astype(np.int64), ref["raw"])
-    yb = cr.int8_tensorwise_gemm(a, sa, w, sw, M, N, K, out_type=0)
-    yf = cr.int8_tensorwise_gemm(a, sa, w, sw, M, N, K, out_type=1)
+    yb = cr.int8_tensorwise_gemm(a, sa, w, sw, M, N, K, bias=b, out_type=0)
+    yf = cr.int8_tensorwise_gemm(a, sa, w, sw, M, N, K, bias=b, out_type=1)
     _check_out(yb, yf, ref["y"])
 
 

@@ -455,8 +455,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
 // k 16..31 of the 32-deep step), so both operands keep their natural
 // row-major int8 layout all the way into the matrix cores.
 // Block 256 tokens x 128 channels, 4 waves of 128 x 64 (4 x 2 blocks of
-// 32 x 32, int32 accumulators in VGPRs), two blocks per CU. Each 64-deep
-// k-tile is one stage of a 3-stage LDS ring filled by 16-byte
+// 32 x 32, int32 accumulators in VGPRs), two blocks per CU with a 3-stage
+// ring or three with a 2-stage ring (see launch_int8_lds). Each 64-deep
+// k-tile is one stage of the LDS ring filled by 16-byte
 // global_load_lds pieces: 256 activation rows and 128 weight rows of 64
 // bytes, the four 16-byte slots of a row XOR-swizzled by the row index so
 // that the 32 rows of a fragment read land on distinct banks. Each wave
@@ -478,9 +479,12 @@ CR_DEV void wait_vmcnt_i8() {   // s_waitcnt vmcnt(N), other counters untouched
 // 16-byte slot of k-chunk c (0..3) in row r of a 64-byte stage row
 CR_DEV int i8_slot(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
 
-template <int OUT>
-__global__ __launch_bounds__(256, 2) void gemm_int8_lds_kernel(GemmParams p) {
-  constexpr int BM = 256, BN = 128, NS = 3;
+// TW: per-tensor weight scale and no bias (the epilogue keeps one scalar
+// instead of per-channel scale and bias vectors)
+template <int OUT, int NS, int MINB, bool TW>
+__global__ __launch_bounds__(256, MINB) void gemm_int8_lds_kernel(GemmParams p) {
+  constexpr int BM = 256, BN = 128;
+  static_assert(NS == 2 || NS == 3, "two or three stages");
   constexpr int A_ST = BM * 64, W_ST = BN * 64, STAGE = A_ST + W_ST;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem_i8[];
   uint8_t* smem = smem_i8;
@@ -551,12 +555,12 @@ __global__ __launch_bounds__(256, 2) void gemm_int8_lds_kernel(GemmParams p) {
   }
 
   issue(0);
-  if (nst > 1) issue(1);
+  if (NS == 3 && nst > 1) issue(1);
   for (int s = 0; s < nst; ++s) {
-    if (s + 1 < nst) wait_vmcnt_i8<6>();
+    if (NS == 3 && s + 1 < nst) wait_vmcnt_i8<6>();   // stage s + 1 may stay in flight
     else wait_vmcnt_i8<0>();
     __builtin_amdgcn_s_barrier();
-    if (s + 2 < nst) issue(s + 2);
+    if (s + NS - 1 < nst) issue(s + NS - 1);
     const uint8_t* st = smem + (s % NS) * STAGE;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -590,9 +594,14 @@ __global__ __launch_bounds__(256, 2) void gemm_int8_lds_kernel(GemmParams p) {
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t n = n0 + (wn * 2 + j) * 32 + 8 * q + 4 * h;
-        sw[j][q] = wrow ? *reinterpret_cast<const v4f*>(p.w_scales + n) : v4f{sw_t, sw_t, sw_t, sw_t};
-        bw[j][q] = p.bias ? *reinterpret_cast<const u32x2*>(p.bias + n) : u32x2{0u, 0u};
+        if constexpr (TW) {
+          sw[j][q] = v4f{sw_t, sw_t, sw_t, sw_t};
+          bw[j][q] = u32x2{0u, 0u};
+        } else {
+          const int64_t n = n0 + (wn * 2 + j) * 32 + 8 * q + 4 * h;
+          sw[j][q] = wrow ? *reinterpret_cast<const v4f*>(p.w_scales + n) : v4f{sw_t, sw_t, sw_t, sw_t};
+          bw[j][q] = p.bias ? *reinterpret_cast<const u32x2*>(p.bias + n) : u32x2{0u, 0u};
+        }
       }
   }
   if constexpr (OUT == CR_OUT_BF16) {
@@ -665,15 +674,31 @@ __global__ __launch_bounds__(256, 2) void gemm_int8_lds_kernel(GemmParams p) {
   }
 }
 
+template <int OUT, int NS, int MINB, bool TW>
+static hipError_t launch_int8_lds_cfg(const GemmParams& p, int64_t tiles, hipStream_t s) {
+  constexpr int lds = NS * (256 * 64 + 128 * 64);
+  static const hipError_t attr = hipFuncSetAttribute((const void*)gemm_int8_lds_kernel<OUT, NS, MINB, TW>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((gemm_int8_lds_kernel<OUT, NS, MINB, TW>), dim3((unsigned)tiles), dim3(256), lds, s, p);
+  return hipGetLastError();
+}
+
+// Three-stage ring and two blocks per CU; when the tiles number more than
+// two but at most three per CU (8192 x 3072: 768 tiles), a two-stage ring and
+// three blocks per CU, so that every tile runs in the first round (two
+// blocks per CU leave the second round of 256 tiles on half the slots).
 template <int OUT>
 static hipError_t launch_int8_lds(const GemmParams& p, hipStream_t s) {
-  constexpr int lds = 3 * (256 * 64 + 128 * 64);
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void*)gemm_int8_lds_kernel<OUT>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (attr != hipSuccess) return attr;
   const int64_t tiles = ((p.M + 255) / 256) * (p.N / 128);
-  hipLaunchKernelGGL((gemm_int8_lds_kernel<OUT>), dim3((unsigned)tiles), dim3(256), lds, s, p);
-  return hipGetLastError();
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  // per-channel weight scales or a bias keep more epilogue registers: those
+  // stay at two blocks per CU (three would spill)
+  const bool tw = OUT == CR_OUT_I32_RAW || (p.w_gran == CR_GRAN_TENSOR && !p.bias);
+  if (!tw) return launch_int8_lds_cfg<OUT, 3, 2, false>(p, tiles, s);
+  if (cus > 0 && tiles > 2 * cus && tiles <= 3 * cus) return launch_int8_lds_cfg<OUT, 2, 3, true>(p, tiles, s);
+  return launch_int8_lds_cfg<OUT, 3, 2, true>(p, tiles, s);
 }
 
 // ---------------------------------------------------------------------------

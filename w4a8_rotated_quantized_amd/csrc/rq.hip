@@ -357,8 +357,9 @@ __global__ __launch_bounds__(256) void rq_rot_kernel(RQParams a) {
 
 // ---------------------------------------------------------------------------
 // rq_tensor: per-tensor scale with rotation on, two launches over the same
-// block -> data map (pass 1 then re-reads X from the L2 of the XCD that
-// read it in pass 0; the input fits the chip's combined L2 at C2 sizes).
+// block -> data map, the second walking it backwards within each XCD (pass
+// 1 then re-reads X from the L2 of the XCD that read it in pass 0, or from
+// the last-level cache, most recently read data first).
 // Block b owns 16 rows, row block b / GC, and J consecutive 256-groups
 // starting at group (b % GC) * J (GC = ceil(G / J)); segment seg (16 lanes)
 // takes row seg. A segment reads J * 512 contiguous bytes of its row, and a
@@ -386,14 +387,21 @@ __global__ __launch_bounds__(256) void rq_tensor_kernel(RQParams a) {
   const float qmax = (QT == CR_Q_SYM_INT8) ? 127.f : 7.f;
   const int G = a.G;
   const int GC = (G + J - 1) / J;
-  const int64_t row = imin64((int64_t)(blockIdx.x / (unsigned)GC) * 16 + seg, a.rows - 1);
-  const int g0 = (int)(blockIdx.x % (unsigned)GC) * J;
+  // passes 1 and 2 walk the blocks of pass 0 backwards within each XCD
+  // (blocks go round robin over the 8 XCDs): the data pass 0 read last,
+  // most likely still in that XCD's L2 or in the last-level cache, is read
+  // again first
+  const unsigned nb = gridDim.x;
+  unsigned b = blockIdx.x;
+  if (PASS >= 1) b = (nb % 8 == 0) ? (nb / 8 - 1 - b / 8) * 8 + b % 8 : nb - 1 - b;
+  const int64_t row = imin64((int64_t)(b / (unsigned)GC) * 16 + seg, a.rows - 1);
+  const int g0 = (int)(b % (unsigned)GC) * J;
   const uint16_t* xr = a.x + row * a.ldx + lr.gL * 16;
 
   // PASS 1: the block maxima of pass 0 are loaded before the rows (NWS
   // unconditional loads per thread, clamped indices), so that waiting for
   // them leaves the row loads in flight; NWS = 0 is the loop for grids
-  // beyond 256 * 16 blocks.
+  // beyond 256 * 32 blocks.
   float t = 0.f;
   if constexpr (PASS >= 1) {
     const int gd = (int)gridDim.x;
@@ -1162,6 +1170,7 @@ static void launch_tensor_j(const RQParams& p, int gd, hipStream_t s) {
   if (PASS == 0 || nws <= 1) hipLaunchKernelGGL((rq_tensor_kernel<QT, PASS, J, 1, NR>), dim3(gd), dim3(256), 0, s, p);
   else if (nws <= 4) hipLaunchKernelGGL((rq_tensor_kernel<QT, PASS, J, 4, NR>), dim3(gd), dim3(256), 0, s, p);
   else if (nws <= 16) hipLaunchKernelGGL((rq_tensor_kernel<QT, PASS, J, 16, NR>), dim3(gd), dim3(256), 0, s, p);
+  else if (nws <= 32) hipLaunchKernelGGL((rq_tensor_kernel<QT, PASS, J, 32, NR>), dim3(gd), dim3(256), 0, s, p);
   else hipLaunchKernelGGL((rq_tensor_kernel<QT, PASS, J, 0, NR>), dim3(gd), dim3(256), 0, s, p);
 }
 
