@@ -233,8 +233,9 @@ def main():
                    "int8_layers": "v, out, mod (image and text)",
                    "w4a4_weights": "tile-packed INT4, 2 per byte (expanded per call into fp6 fragments)",
                    "w4a4_matrix_cores": args.cores, "buffer_sets": nsets,
-                   "schedule": f"token streams {' and '.join(chains)} on streams of their own, "
-                               f"joined every step"},
+                   "schedule": f"token streams {' and '.join(chains)} on streams of their own, meeting "
+                               f"between the Q/K/V and the output projections (joint attention) and at "
+                               f"the end of every step"},
         "pct_int8_peak": round(100.0 * eff / bw.INT8_PEAK_TOPS, 2),
         "gemm": layers,
         "rotate_quantize": rqs,

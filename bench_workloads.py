@@ -7,8 +7,10 @@ tensor and code format: layers that share an input share the pass; an input
 that feeds both INT4 and INT8 layers is quantized once to both) and every
 GEMM, with inputs resident in HBM. With the "chains" schedule each chain of
 layers (an independent token stream: the image and text tokens of an MMDiT
-block) runs in order on a stream of its own; the streams join before the step
-ends, and the next step starts after the whole of it. The "serial" schedule
+block) runs in order on a stream of its own; the chains meet between phases
+(the joint attention between the Q/K/V projections and the output
+projections) and before the step ends, and the next step starts after the
+whole of it. The "serial" schedule
 (step_serial) runs the same calls in order on one stream. Each step uses the
 next buffer set (inputs, weights, codes, workspaces, outputs), so consecutive
 steps read data the previous step did not touch.
@@ -201,21 +203,24 @@ class Runner:
             self.order.append((f"gemm:{lin.name}", lambda si, l=lin, k=key: self.launch_gemm(si, l, k)))
 
         # Chains schedule of a step: every chain (independent token stream)
-        # in its order on a stream of its own.
-        self.corder = {c: [] for c in self.chains}
+        # in its order on a stream of its own, all chains meeting between
+        # phases (corder[phase][chain] = launches).
+        self.phases = sorted({lin.phase for lin in w.linears})
+        self.corder = {ph: {c: [] for c in self.chains} for ph in self.phases}
         for lab, fn in self.order:
-            c = self._chain_of(lab)
-            self.corder[c].append(fn)
+            lin = self._lin_of(lab)
+            self.corder[lin.phase][lin.chain].append(fn)
         self.side = [torch.cuda.Stream() for _ in range(len(self.chains) - 1)]
         self.schedule = schedule if len(self.chains) > 1 else "serial"
 
     # ------------------------------------------------------------------
-    def _chain_of(self, label):
+    def _lin_of(self, label):
+        """the layer a launch label belongs to (an RQ: the first layer reading its input)"""
         kind, _, rest = label.partition(":")
         if kind == "gemm":
-            return [l for l in self.w.linears if l.name == rest][0].chain
+            return [l for l in self.w.linears if l.name == rest][0]
         x_id = rest.split(":")[0]
-        return [l for l in self.w.linears if l.x_id == x_id][0].chain
+        return [l for l in self.w.linears if l.x_id == x_id][0]
 
     def _lay4(self, M):
         return self.cr.LAYOUT.F6 if self.f6_codes(M) else self.cr.LAYOUT.TILED
@@ -282,24 +287,36 @@ class Runner:
         "chains": chain 0 on the launch stream, the others on side streams
         that start after an event recorded at the step's start and join the
         launch stream before the step ends (the next step starts after the
-        whole of this one); launches are issued round robin over the chains."""
+        whole of this one); between phases every chain waits for all the
+        others; launches are issued round robin over the chains."""
         if self.schedule == "serial":
             self.step_serial(i)
             return
         torch = self.torch
         si = i % self.nsets
         main = self.stream
+        streams = [main] + self.side
         start = torch.cuda.Event()
         start.record(main)
         for s in self.side:
             s.wait_event(start)
-        streams = [main] + self.side
-        lists = [self.corder[c] for c in self.chains]
-        for pos in range(max(len(l) for l in lists)):
-            for s, l in zip(streams, lists):
-                if pos < len(l):
-                    with torch.cuda.stream(s):
-                        l[pos](si)
+        for k, ph in enumerate(self.phases):
+            if k > 0:                       # every chain waits for every chain's previous phase
+                evs = []
+                for s in streams:
+                    ev = torch.cuda.Event()
+                    ev.record(s)
+                    evs.append(ev)
+                for s in streams:
+                    for t, ev in zip(streams, evs):
+                        if t is not s:
+                            s.wait_event(ev)
+            lists = [self.corder[ph][c] for c in self.chains]
+            for pos in range(max(len(l) for l in lists)):
+                for s, l in zip(streams, lists):
+                    if pos < len(l):
+                        with torch.cuda.stream(s):
+                            l[pos](si)
         for s in self.side:
             ev = torch.cuda.Event()
             ev.record(s)

@@ -125,6 +125,10 @@ class LinearSpec:
     chain: layers of one chain run in order; different chains are independent
            (the image and text token streams of an MMDiT block) and may run
            concurrently.
+    phase: chains meet between phases: every layer of phase p runs after
+           every layer of phase p - 1 of all chains (the joint attention of an
+           MMDiT block reads the Q, K and V of both token streams, and each
+           stream's output projection reads the attention's output).
     """
     name: str
     fmt: str
@@ -136,6 +140,7 @@ class LinearSpec:
     unsigned_shift: float = 0.0
     rank: int = 0
     chain: str = ""
+    phase: int = 0
 
 
 @dataclass
@@ -179,12 +184,12 @@ def _c4(m_img: int = 8192, m_txt: int = 512, m_mod: int = 2):
             LinearSpec(f"{s}_q", "w4a4", M, 3072, 3072, f"{s}_attn", chain=s),
             LinearSpec(f"{s}_k", "w4a4", M, 3072, 3072, f"{s}_attn", chain=s),
             LinearSpec(f"{s}_v", "int8", M, 3072, 3072, f"{s}_attn", chain=s),
-            LinearSpec(f"{s}_out", "int8", M, 3072, 3072, f"{s}_attnout", chain=s),
-            LinearSpec(f"{s}_mlp_up", "w4a4", M, 12288, 3072, f"{s}_mlp", chain=s),
-            LinearSpec(f"{s}_mlp_down", "w4a4", M, 3072, 12288, f"{s}_gelu", chain=s),
+            LinearSpec(f"{s}_out", "int8", M, 3072, 3072, f"{s}_attnout", chain=s, phase=1),
+            LinearSpec(f"{s}_mlp_up", "w4a4", M, 12288, 3072, f"{s}_mlp", chain=s, phase=1),
+            LinearSpec(f"{s}_mlp_down", "w4a4", M, 3072, 12288, f"{s}_gelu", chain=s, phase=1),
         ]
         w.acts[f"{s}_mod"] = (m_mod, 3072, "normal", 0, 1.0)
-        w.linears.append(LinearSpec(f"{s}_mod", "int8", m_mod, 18432, 3072, f"{s}_mod", chain=s))
+        w.linears.append(LinearSpec(f"{s}_mod", "int8", m_mod, 18432, 3072, f"{s}_mod", chain=s, phase=1))
     return w
 
 
