@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--workload", default="c4",
                     help="c4 (default: the headline line), or c1 / c2 / c3 / c5 / c2a8 / merge for the other "
                          "workloads' throughput lines (bench_workloads.py)")
+    ap.add_argument("--rot-group", type=int, default=256, choices=(16, 64, 256, 1024),
+                    help="ConvRot group size of the W4A4 / INT8 tensorwise layers of --workload c1 / c2 / c4")
     return ap.parse_args()
 
 
@@ -172,7 +174,7 @@ def main():
         sys.exit(2)
     if args.workload != "c4":
         for name in args.workload.split(","):
-            bw.run(name, args.steps, args.warmup, cores=args.cores)
+            bw.run(name, args.steps, args.warmup, cores=args.cores, rot=args.rot_group)
         return
 
     import torch
@@ -180,7 +182,7 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(3)
 
-    r = bw.Runner("c4", args.cores, schedule="chains")  # image and text token streams concurrently
+    r = bw.Runner("c4", args.cores, rot=args.rot_group, schedule="chains")   # both token streams concurrently
     ms = r.time_steps(args.steps, args.warmup)
     ms_serial = r.time_steps(args.steps, args.warmup, schedule="serial")
     chains = list(r.chains)
@@ -229,6 +231,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "layers": 14, "total_GOP": round(ops / 1e9, 1),
                    "tokens": {"image": 8192, "text": 512, "modulation_rows": 2}, "hidden": 3072,
+                   "convrot_group": args.rot_group,
                    "w4a4_layers": "q, k, mlp_up, mlp_down (image and text)",
                    "int8_layers": "v, out, mod (image and text)",
                    "w4a4_weights": "tile-packed INT4, 2 per byte (expanded per call into fp6 fragments)",

@@ -400,7 +400,7 @@ class Runner:
         return sum(2.0 * l.M * l.N * l.K for l in self.w.linears)
 
 
-def run(name, steps, warmup, cores="fp6"):
+def run(name, steps, warmup, cores="fp6", rot=256):
     """One JSON line for workload `name` (bench.py --workload NAME)."""
     if name == "merge":
         return run_merge(steps, warmup)
@@ -408,7 +408,7 @@ def run(name, steps, warmup, cores="fp6"):
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(3)
-    r = Runner(name, cores)
+    r = Runner(name, cores, rot=rot)
     ms = r.time_steps(steps, warmup)
     ms_chains = r.time_steps(steps, warmup, schedule="chains") if len(r.chains) > 1 else None
     kern = r.per_call(max(3, steps // 2))
@@ -434,7 +434,7 @@ def run(name, steps, warmup, cores="fp6"):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "int4 / int8 codes (exact integer products)", "data": "synthetic",
         "config": {"workload": r.w.name, "layers": len(r.w.linears), "total_GOP": round(r.ops() / 1e9, 1),
-                   "w4a4_matrix_cores": cores, "buffer_sets": r.nsets},
+                   "w4a4_matrix_cores": cores, "buffer_sets": r.nsets, "convrot_group": rot},
         "pct_int8_peak": round(100.0 * eff / INT8_PEAK_TOPS, 2),
         "gemm": layers, "rotate_quantize": rqs,
         "dominant_gemm": {"layer": dom, **layers[dom]},
