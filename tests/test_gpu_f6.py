@@ -143,6 +143,25 @@ def test_w4a4_f6_gemm(cr, case):
     assert np.array_equal(host(yb_e), host(yb))
 
 
+def test_w4a4_f6_wide_blocks(cr):
+    """256 x 256 blocks (wide outputs, at least four rounds of tiles: 7950 x
+    8192 gives 1024, the last row block ragged): raw sums equal the exact
+    integer product, float32 outputs its scaled value."""
+    M, N, K = 7950, 8192, 128
+    say("w4a4 f6 256x256 blocks")
+    rng = np.random.default_rng(11)
+    qa = rng.integers(-7, 8, size=(M, K))
+    qw = rng.integers(-7, 8, size=(N, K))
+    ref = qa.astype(np.float64) @ qw.astype(np.float64).T          # exact: |sum| <= 128 * 49
+    a, w = dev(opack.f6_pack(qa)), dev(opack.f6_pack(qw))
+    sa, sw = dev(np.array([0.0123], np.float32)), dev(np.array([0.0456], np.float32))
+    raw = host(cr.w4a4_gemm(a, sa, 0, w, sw, 0, M, N, K, out_type=2))
+    assert np.array_equal(raw.astype(np.float64), ref)
+    yf = host(cr.w4a4_gemm(a, sa, 0, w, sw, 0, M, N, K, out_type=1))
+    s = float(np.float32(0.0123)) * float(np.float32(0.0456))
+    assert rel_l2(yf, ref * s) <= 1e-6
+
+
 def test_w4a4_f6_ldc_padding(cr):
     M, N, K, ldc = 150, 256, 512, 264
     say("w4a4 f6 ldc")
