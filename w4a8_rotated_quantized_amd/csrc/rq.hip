@@ -398,14 +398,24 @@ __global__ __launch_bounds__(256) void rq_tensor_kernel(RQParams a) {
   const int g0 = (int)(b % (unsigned)GC) * J;
   const uint16_t* xr = a.x + row * a.ldx + lr.gL * 16;
 
-  // PASS 1: the block maxima of pass 0 are loaded before the rows (NWS
-  // unconditional loads per thread, clamped indices), so that waiting for
-  // them leaves the row loads in flight; NWS = 0 is the loop for grids
-  // beyond 256 * 32 blocks.
+  // PASS 1: the block maxima of pass 0 are loaded before the rows (up to
+  // 256 * NWS of them, unconditional loads with clamped indices; for NWS >= 4
+  // 16-byte loads of four maxima, the workspace being 16-byte aligned, and
+  // the last three one by one), so that waiting for them leaves the row
+  // loads in flight; NWS = 0 is the loop for grids beyond 256 * 32 blocks.
   float t = 0.f;
   if constexpr (PASS >= 1) {
     const int gd = (int)gridDim.x;
-    if constexpr (NWS > 0) {
+    if constexpr (NWS >= 4) {
+      const v4f* w4 = reinterpret_cast<const v4f*>(a.ws);
+      const int n4 = gd >> 2;   // whole groups of four (gd > 256 here)
+#pragma unroll
+      for (int i = 0; i < NWS / 4; ++i) {
+        const v4f q = w4[min(tid + 256 * i, n4 - 1)];
+        t = fmaxf(t, fmaxf(fmaxf(q[0], q[1]), fmaxf(q[2], q[3])));
+      }
+      t = fmaxf(t, fmaxf(a.ws[gd - 1], fmaxf(a.ws[gd - 2], a.ws[gd - 3])));
+    } else if constexpr (NWS > 0) {
 #pragma unroll
       for (int i = 0; i < NWS; ++i) t = fmaxf(t, a.ws[min(tid + 256 * i, gd - 1)]);
     } else {
