@@ -195,7 +195,12 @@ void convrot_reset_counters(void);
  *                the workspace and tags every value it writes with it, so the
  *                workspace needs no clearing between calls (nor between
  *                replays of a captured graph). Calls sharing a workspace must
- *                not run concurrently.
+ *                not run concurrently. The exchange needs its whole grid
+ *                resident at once (at most one workgroup of 4 waves per
+ *                compute unit, so it shares the GPU with kernels on other
+ *                streams); if other work kept compute units from it until
+ *                its bounded wait (about a second) ended, the scale would
+ *                come out NaN rather than the call hanging.
  * Shape: rows >= 1, K % 256 == 0 and K % rot_group == 0 when rotating,
  *        K % 64 == 0 otherwise, K <= 32768.
  * Result is deterministic and bit-identical to the reference definition for
