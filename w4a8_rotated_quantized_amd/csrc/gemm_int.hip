@@ -454,15 +454,16 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
 // consecutive k-bytes of one row per lane (lanes 0-31 k 0..15, lanes 32-63
 // k 16..31 of the 32-deep step), so both operands keep their natural
 // row-major int8 layout all the way into the matrix cores.
-// Block 256 tokens x 128 channels, 4 waves of 128 x 64 (4 x 2 blocks of
-// 32 x 32, int32 accumulators in VGPRs), two blocks per CU with a 3-stage
-// ring or three with a 2-stage ring (see launch_int8_lds). Each 64-deep
-// k-tile is one stage of the LDS ring filled by 16-byte
-// global_load_lds pieces: 256 activation rows and 128 weight rows of 64
-// bytes, the four 16-byte slots of a row XOR-swizzled by the row index so
-// that the 32 rows of a fragment read land on distinct banks. Each wave
-// issues six loads per stage and waits (vmcnt) only for the stage it is
-// about to use, then one bare s_barrier per stage.
+// Block BM tokens x BN channels of waves with TM x TN blocks of 32 x 32
+// (int32 accumulators in VGPRs): 256 x 128 of 4 waves of 128 x 64, two
+// blocks per CU with a 3-stage ring or three with a 2-stage ring, or, for
+// mid-size M, 64 x 64 of 4 waves of 32 x 32 (see launch_int8_lds). Each
+// 64-deep k-tile is one stage of the LDS ring filled by 16-byte
+// global_load_lds pieces (1 KB wave-loads of 16 rows): BM activation rows
+// and BN weight rows of 64 bytes, the four 16-byte slots of a row
+// XOR-swizzled by the row index so that the 32 rows of a fragment read land
+// on distinct banks. Each wave waits (vmcnt) only for the stage it is about
+// to use, then one bare s_barrier per stage.
 // Operand roles: A = weights (32 channels), B = activations (32 tokens), so a
 // lane ends with one token and 4 consecutive channels per 8 accumulators:
 // one activation scale and one 8-byte bf16 (16-byte int32 / float) store.
@@ -481,18 +482,26 @@ CR_DEV int i8_slot(int r, int c) { return c ^ (((r >> 1) ^ (r >> 3)) & 3); }
 
 // TW: per-tensor weight scale and no bias (the epilogue keeps one scalar
 // instead of per-channel scale and bias vectors)
-template <int OUT, int NS, int MINB, bool TW>
-__global__ __launch_bounds__(256, MINB) void gemm_int8_lds_kernel(GemmParams p) {
-  constexpr int BM = 256, BN = 128;
+template <int OUT, int NS, int MINB, bool TW, int BM = 256, int BN = 128, int TM = 4, int TN = 2>
+__global__ __launch_bounds__((BM / (32 * TM)) * (BN / (32 * TN)) * 64, MINB) void gemm_int8_lds_kernel(GemmParams p) {
   static_assert(NS == 2 || NS == 3, "two or three stages");
+  static_assert(BM % (32 * TM) == 0 && BN % (32 * TN) == 0, "whole wave tiles");
+  constexpr int WN = BN / (32 * TN);                 // waves along the channels
+  constexpr int NW = (BM / (32 * TM)) * WN;
   constexpr int A_ST = BM * 64, W_ST = BN * 64, STAGE = A_ST + W_ST;
+  constexpr int NA = BM / 16, NL = (BM + BN) / 16;   // 1 KB wave-loads per stage (activation part first)
+  constexpr int LPW = (NL + NW - 1) / NW;            // wave-loads of the busiest waves
+  constexpr int NHI = NL - (LPW - 1) * NW;           // waves 0 .. NHI-1 take LPW, the others LPW - 1
+  // whole-row bf16 stores through LDS for the 256 x 128 block (pairs of
+  // 32-row blocks, 64 channels per wave); other shapes store 8-byte pieces
+  constexpr bool LDS_EPI = (TM % 2 == 0) && TN == 2;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem_i8[];
   uint8_t* smem = smem_i8;
 
   const int tid = threadIdx.x;
   const int l = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
 
   const int ntm = (int)((p.M + BM - 1) / BM);
   const int ntn = (int)(p.N / BN);
@@ -510,110 +519,114 @@ __global__ __launch_bounds__(256, MINB) void gemm_int8_lds_kernel(GemmParams p) 
   const int64_t K = p.K;
   const int nst = (int)(K / 64);
 
-  // wave-load j: rows 16 (wave + 4 j) + l / 4 of the stage, slot l % 4
-  int64_t offa[4], offw[2];
+  // wave-load idx = wave + NW j fills stage bytes [idx KB, +1 KB): rows
+  // 16 idx + l / 4 of the activation part (idx < NA), else of the weight
+  // part, slot l % 4
+  const uint8_t* src[LPW];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 16 * (wave + 4 * j) + (l >> 2);
-    offa[j] = imin64(m0 + r, p.M - 1) * K + 16 * i8_slot(r, l & 3);   // rows past M: never stored
-  }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = 16 * (wave + 4 * j) + (l >> 2);
-    offw[j] = (n0 + r) * K + 16 * i8_slot(r, l & 3);
+  for (int j = 0; j < LPW; ++j) {
+    const int idx = min(wave + NW * j, NL - 1);
+    if (idx < NA) {
+      const int r = 16 * idx + (l >> 2);
+      src[j] = p.a + imin64(m0 + r, p.M - 1) * K + 16 * i8_slot(r, l & 3);   // rows past M: never stored
+    } else {
+      const int r = 16 * (idx - NA) + (l >> 2);
+      src[j] = p.w + (n0 + r) * K + 16 * i8_slot(r, l & 3);
+    }
   }
   auto issue = [&](int s) {
     uint8_t* st = smem + (s % NS) * STAGE;
     const int64_t k0 = (int64_t)s * 64;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_global_load_lds((gas_ptr_i8)(p.a + offa[j] + k0), (las_ptr_i8)(st + (wave + 4 * j) * 1024),
-                                       16, 0, 0);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_global_load_lds((gas_ptr_i8)(p.w + offw[j] + k0),
-                                       (las_ptr_i8)(st + A_ST + (wave + 4 * j) * 1024), 16, 0, 0);
+    for (int j = 0; j < LPW; ++j)
+      if (j < LPW - 1 || wave < NHI)
+        __builtin_amdgcn_global_load_lds((gas_ptr_i8)(src[j] + k0), (las_ptr_i8)(st + (wave + NW * j) * 1024), 16,
+                                         0, 0);
   };
 
-  v16i acc[4][2];
+  v16i acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  // fragment rows: activations wm*128 + 32 i + l % 32, weights wn*64 + 32 j + l % 32
+  // fragment rows: activations wm*32*TM + 32 i + l % 32, weights wn*32*TN + 32 j + l % 32
   const int lr = l & 31, h = l >> 5;
   const int fl = ((lr >> 1) ^ (lr >> 3)) & 3;
   int abase[2], wbase[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     const int c = 2 * ks + h;                       // 16-byte k-chunk of this lane in step ks
-    abase[ks] = (wm * 128 + lr) * 64 + 16 * (c ^ fl);
-    wbase[ks] = A_ST + (wn * 64 + lr) * 64 + 16 * (c ^ fl);
+    abase[ks] = (wm * 32 * TM + lr) * 64 + 16 * (c ^ fl);
+    wbase[ks] = A_ST + (wn * 32 * TN + lr) * 64 + 16 * (c ^ fl);
   }
 
   issue(0);
   if (NS == 3 && nst > 1) issue(1);
   for (int s = 0; s < nst; ++s) {
-    if (NS == 3 && s + 1 < nst) wait_vmcnt_i8<6>();   // stage s + 1 may stay in flight
-    else wait_vmcnt_i8<0>();
+    if (NS == 3 && s + 1 < nst) {                    // stage s + 1 may stay in flight
+      if (wave < NHI) wait_vmcnt_i8<LPW>();
+      else wait_vmcnt_i8<LPW - 1>();
+    } else {
+      wait_vmcnt_i8<0>();
+    }
     __builtin_amdgcn_s_barrier();
     if (s + NS - 1 < nst) issue(s + NS - 1);
     const uint8_t* st = smem + (s % NS) * STAGE;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      v4i fa[4], fw[2];
+      v4i fa[TM], fw[TN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const v4i*>(st + abase[ks] + i * 2048);
+      for (int i = 0; i < TM; ++i) fa[i] = *reinterpret_cast<const v4i*>(st + abase[ks] + i * 2048);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fw[j] = *reinterpret_cast<const v4i*>(st + wbase[ks] + j * 2048);
+      for (int j = 0; j < TN; ++j) fw[j] = *reinterpret_cast<const v4i*>(st + wbase[ks] + j * 2048);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[j], fa[i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[j], fa[i], acc[i][j], 0, 0, 0);
     }
   }
 
   // lane owns token m = l % 32 of each 32 x 32 block and channels 8 (r / 4) + 4 h + r % 4.
   // Every epilogue input is loaded before the first store (a load between
   // stores would make each later store wait for the earlier ones).
-  float sa[4];
-  v4f sw[2][4];
-  u32x2 bw[2][4];
+  float sa[TM];
+  v4f sw[TN][4];
+  u32x2 bw[TN][4];
   if constexpr (OUT != CR_OUT_I32_RAW) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = imin64(m0 + wm * 128 + i * 32 + lr, p.M - 1);
+    for (int i = 0; i < TM; ++i) {
+      const int64_t m = imin64(m0 + wm * 32 * TM + i * 32 + lr, p.M - 1);
       sa[i] = p.a_scales[p.a_gran == CR_GRAN_TENSOR ? 0 : m];
     }
     const bool wrow = p.w_gran != CR_GRAN_TENSOR;
     const float sw_t = p.w_scales[0];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if constexpr (TW) {
           sw[j][q] = v4f{sw_t, sw_t, sw_t, sw_t};
           bw[j][q] = u32x2{0u, 0u};
         } else {
-          const int64_t n = n0 + (wn * 2 + j) * 32 + 8 * q + 4 * h;
+          const int64_t n = n0 + (wn * TN + j) * 32 + 8 * q + 4 * h;
           sw[j][q] = wrow ? *reinterpret_cast<const v4f*>(p.w_scales + n) : v4f{sw_t, sw_t, sw_t, sw_t};
           bw[j][q] = p.bias ? *reinterpret_cast<const u32x2*>(p.bias + n) : u32x2{0u, 0u};
         }
       }
   }
-  if constexpr (OUT == CR_OUT_BF16) {
-    // bf16 (v_cvt_pk_bf16_f32, half to even) through LDS in two halves of 64
+  if constexpr (OUT == CR_OUT_BF16 && LDS_EPI) {
+    // bf16 (v_cvt_pk_bf16_f32, half to even) through LDS in pieces of 64
     // token rows per wave, so that every store writes whole 128-byte output
     // rows instead of 8-byte pieces spread over 32 rows
     constexpr int RS = 144;                          // LDS row stride of a half tile, 16-byte aligned
-    static_assert(4 * 64 * RS <= NS * STAGE, "half tiles fit the stage buffers");
+    static_assert(NW * 64 * RS <= NS * STAGE, "half tiles fit the stage buffers");
     __syncthreads();                                 // every wave is done with the stage buffers
     uint8_t* tile = smem + wave * (64 * RS);
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < TM / 2; ++hh) {
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
@@ -636,7 +649,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_int8_lds_kernel(GemmParams p) 
       for (int qq = 0; qq < 8; ++qq) {
         const int r = (l >> 3) + 8 * qq;
         const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * RS + (l & 7) * 16);
-        const int64_t m = m0 + wm * 128 + hh * 64 + r;
+        const int64_t m = m0 + wm * 32 * TM + hh * 64 + r;
         if (m < p.M)
           *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.out) + m * p.ldc + n0 + wn * 64 + (l & 7) * 8) = v;
       }
@@ -644,13 +657,13 @@ __global__ __launch_bounds__(256, MINB) void gemm_int8_lds_kernel(GemmParams p) 
     return;
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < TN; ++j) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int64_t n = n0 + (wn * 2 + j) * 32 + 8 * q + 4 * h;
+      const int64_t n = n0 + (wn * TN + j) * 32 + 8 * q + 4 * h;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + wm * 128 + i * 32 + lr;
+      for (int i = 0; i < TM; ++i) {
+        const int64_t m = m0 + wm * 32 * TM + i * 32 + lr;
         if (m >= p.M) continue;
         if constexpr (OUT == CR_OUT_I32_RAW) {
           *reinterpret_cast<v4i*>(reinterpret_cast<int32_t*>(p.out) + m * p.ldc + n) =
@@ -674,13 +687,16 @@ __global__ __launch_bounds__(256, MINB) void gemm_int8_lds_kernel(GemmParams p) 
   }
 }
 
-template <int OUT, int NS, int MINB, bool TW>
+template <int OUT, int NS, int MINB, bool TW, int BM = 256, int BN = 128, int TM = 4, int TN = 2>
 static hipError_t launch_int8_lds_cfg(const GemmParams& p, int64_t tiles, hipStream_t s) {
-  constexpr int lds = NS * (256 * 64 + 128 * 64);
-  static const hipError_t attr = hipFuncSetAttribute((const void*)gemm_int8_lds_kernel<OUT, NS, MINB, TW>,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  constexpr int lds = NS * (BM + BN) * 64;
+  constexpr int threads = (BM / (32 * TM)) * (BN / (32 * TN)) * 64;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)gemm_int8_lds_kernel<OUT, NS, MINB, TW, BM, BN, TM, TN>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gemm_int8_lds_kernel<OUT, NS, MINB, TW>), dim3((unsigned)tiles), dim3(256), lds, s, p);
+  hipLaunchKernelGGL((gemm_int8_lds_kernel<OUT, NS, MINB, TW, BM, BN, TM, TN>), dim3((unsigned)tiles),
+                     dim3(threads), lds, s, p);
   return hipGetLastError();
 }
 
@@ -693,6 +709,12 @@ static hipError_t launch_int8_lds(const GemmParams& p, hipStream_t s) {
   const int64_t tiles = ((p.M + 255) / 256) * (p.N / 128);
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  // mid-size M (e.g. 512 text tokens x 3072: 48 blocks of 256 x 128): 64 x 64
+  // blocks of four 32 x 32 waves fill the chip instead
+  if (cus > 0 && tiles < cus) {
+    const int64_t t64 = ((p.M + 63) / 64) * (p.N / 64);
+    return launch_int8_lds_cfg<OUT, 3, 4, false, 64, 64, 1, 1>(p, t64, s);
+  }
   // per-channel weight scales or a bias keep more epilogue registers: those
   // stay at two blocks per CU (three would spill)
   const bool tw = OUT == CR_OUT_I32_RAW || (p.w_gran == CR_GRAN_TENSOR && !p.bias);
