@@ -708,7 +708,9 @@ template <int OUT>
 static hipError_t launch_int8_lds(const GemmParams& p, hipStream_t s) {
   const int64_t tiles = ((p.M + 255) / 256) * (p.N / 128);
   int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
   // mid-size M (e.g. 512 text tokens x 3072: 48 blocks of 256 x 128): 64 x 64
   // blocks of four 32 x 32 waves fill the chip instead
   if (cus > 0 && tiles < cus) {
