@@ -191,10 +191,12 @@ def test_w4a4_group64_lowrank(cr, case):
     _check_out(yb, yf, ref["y"])
 
 
-# M <= 64: weight streaming; above: the direct-to-LDS kernel of 256 x 128
-# blocks (2600 x 3072: 264 of them, a ragged last row block; 8000 x 3072:
-# 768, the three-blocks-per-CU ring on a 256-CU part, ragged too; with a bias
-# the same shape keeps two blocks per CU)
+# M <= 64: weight streaming; above: the direct-to-LDS kernel, on a 256-CU
+# part with 64 x 64 blocks while 256 x 128 tiles would not fill the CUs
+# (190 x 256: 12 blocks, a ragged last row block; 512 x 384: 48), then
+# 256 x 128 blocks (2600 x 3072: 264 of them, a ragged last row block;
+# 8000 x 3072: 768, the three-blocks-per-CU ring, ragged too; with a bias the
+# same shape keeps two blocks per CU)
 INT8_CASES = [(2, 256, 3072), (33, 384, 512), (64, 128, 256), (190, 256, 1024), (512, 384, 3072), (2600, 3072, 256),
               (8000, 3072, 256)]
 
