@@ -67,8 +67,9 @@ CR_DEV void f6_wait_vmcnt() {
 }
 
 // ---------------------------------------------------------------------------
-// Block BM x BN (tokens x channels) of waves with 64 x 64 tiles (2 x 2 MFMAs
-// of 32 x 32 x 64), WN waves along the channels. A stage holds BKT 64-deep
+// Block BM x BN (tokens x channels) of waves with TM x TN MFMAs of
+// 32 x 32 x 64 each (64 x 64 wave tiles in the large blocks, 32 x 32 in the
+// mid-size 64 x 64 block), WN waves along the channels. A stage holds BKT 64-deep
 // k-tiles of both operands ((BM + BN) * BKT * 48 bytes) and is filled by
 // direct global -> LDS loads in 1 KB wave-loads; S stages rotate, S - 1 of
 // them in flight ahead of the one being consumed.
@@ -656,14 +657,14 @@ static hipError_t launch_f6_out(const GemmParams& p, hipStream_t s) {
     }
     return hipGetLastError();
   }
-  // 256 x 192 blocks (one per CU, 12 waves) when they fill the chip: a third
-  // less operand traffic per output than 128 x 128 (measured on MI355X at
-  // 4096 x 3072 x 3072: 30.4 against 32.9 us); otherwise 128 x 128 blocks,
-  // three per CU
   // 256 x 256 blocks (16 waves, 147 KB of stages) for wide outputs with at
   // least four rounds of tiles (8192 x 12288: 1536): a sixth less operand
   // traffic per output than 256 x 192 (the operand stream through L2 and the
-  // last-level cache bounds these shapes)
+  // last-level cache bounds these shapes); 256 x 192 blocks (one per CU, 12
+  // waves) when they fill the chip: a third less operand traffic per output
+  // than 128 x 128 (measured on MI355X at 4096 x 3072 x 3072: 30.4 against
+  // 32.9 us); otherwise 128 x 128 blocks, three per CU, or 64 x 64 blocks
+  // for mid-size M
   if (p.N % 256 == 0 && ((p.M + 255) / 256) * (p.N / 256) >= 1024) {
     const int64_t tiles = ((p.M + 255) / 256) * (p.N / 256);
     hipLaunchKernelGGL((gemm_f6_kernel<256, 256, 2, 2, 2, 3, 1, OUT>), dim3((unsigned)tiles), dim3(1024), 0, s, p);
