@@ -34,6 +34,9 @@ INT8_PEAK_TOPS = 5000.0       # MI355X dense INT8 matrix peak (5.0 POP/s)
 FP6_PEAK_TOPS = 10100.0       # MI355X dense fp6 / fp4 matrix peak (10.1 PFLOP/s)
 FP16_PEAK_TOPS = 2500.0       # MI355X dense fp16 / bf16 matrix peak (2.5 PFLOP/s)
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+# float32 FMAs on the vector ALUs without packed math: 256 CUs x 4 SIMDs x 16
+# lanes x 2 flops x 2.4 GHz (the 157.3 TFLOP/s figure counts packed FMAs)
+VALU_FP32_TFLOPS = 78.6
 
 SKINNY_M = 64                 # token counts up to this take the weight-streaming int8-core kernels
 
@@ -92,6 +95,30 @@ def gemm_bytes(lin):
     if lin.fmt == "a8w4":
         return M * K + 0.5 * N * K + 2 * M * N
     return 0.5 * M * K + 0.5 * N * K + 4 * (M + N) * K // 64 + 2 * M * N + 2 * lin.rank * (M + N)
+
+
+def gemm_roofline(lin, us, cores="fp6"):
+    """Roofline of one GEMM kernel of `us` microseconds against what bounds it:
+    the weight bytes for M <= SKINNY_M, the vector ALUs for the per-group
+    scaling of W4A8 (one float32 FMA per output and 16-group) and of the
+    64-group format (per 64-group), else the matrix cores of its operand
+    type (fp6 for W4A4 codes carried as E2M3, int8 otherwise)."""
+    M, N, K = lin.M, lin.N, lin.K
+    if M <= SKINNY_M:
+        bound, unit, peak, work = "hbm", "GB/s", HBM_PEAK_GBS, gemm_bytes(lin)
+        achieved = work / us / 1e3
+    elif lin.fmt in ("w4a8", "w4a4_g64"):
+        group = 16 if lin.fmt == "w4a8" else 64
+        bound, unit, peak = "alu", "TFLOP/s", VALU_FP32_TFLOPS
+        work = 2.0 * M * N * (K // group)
+        achieved = work / us / 1e6
+    else:
+        on_f6 = lin.fmt == "w4a4" and cores == "fp6"
+        bound, unit, peak = "mfma", "TFLOP/s", (FP6_PEAK_TOPS if on_f6 else INT8_PEAK_TOPS)
+        work = 2.0 * M * N * K
+        achieved = work / us / 1e6
+    return {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": None, "kernel_us": round(us, 2)}
 
 
 class Runner:
@@ -425,6 +452,9 @@ def run(name, steps, warmup, cores="fp6", rot=256):
         us = kern[f"rq:{x_id}:{kind}"]
         rqs[f"{x_id}:{kind}"] = {"us": round(us, 2), "GBps": round(rq_bytes(M, K, kind) / us / 1e3, 1)}
     dom = max(layers, key=lambda n: layers[n]["us"])
+    dlin = [l for l in r.w.linears if l.name == dom][0]
+    roof = gemm_roofline(dlin, r.gemm_kernel_alone(dlin, max(5, steps)), cores)
+    roof["kernel"] = f"GEMM kernel of {dom} ({dlin.M}x{dlin.N}x{dlin.K}, {dlin.fmt}), alone, back to back"
     eff = r.ops() / (ms * 1e-3) / 1e12
     print(json.dumps({
         "metric": "effective TOPS of fused rotate+quant+W4 GEMM (% INT8 MFMA peak); GB/s",
@@ -438,6 +468,7 @@ def run(name, steps, warmup, cores="fp6", rot=256):
         "pct_int8_peak": round(100.0 * eff / INT8_PEAK_TOPS, 2),
         "gemm": layers, "rotate_quantize": rqs,
         "dominant_gemm": {"layer": dom, **layers[dom]},
+        "roofline": roof,
         "setup_s": round(r.setup_s, 1),
     }))
 

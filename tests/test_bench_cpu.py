@@ -37,6 +37,29 @@ def test_algorithmic_bytes_at_code_width():
     assert bw.gemm_bytes(lin8) == M * K + N * K + 2 * M * N
 
 
+def test_side_line_roofline_bounds():
+    """Each format is priced against what bounds it: weight bytes at small M,
+    one float32 FMA per output and group on the vector ALUs (78.6 TFLOP/s
+    without packed math) for W4A8 and the 64-group format, else the matrix
+    cores of its operand type."""
+    assert abs(bw.VALU_FP32_TFLOPS - 256 * 4 * 16 * 2 * 2.4e9 / 1e12) < 0.05
+    w4a8 = wl.LinearSpec("p", "w4a8", 8192, 12288, 3072, "x")
+    r = bw.gemm_roofline(w4a8, 600.0)
+    assert r["bound"] == "alu" and r["unit"] == "TFLOP/s"
+    assert abs(r["achieved"] - 2 * 8192 * 12288 * 192 / 600e-6 / 1e12) < 0.1
+    g64 = wl.LinearSpec("p", "w4a4_g64", 8192, 3072, 12288, "x")
+    assert bw.gemm_roofline(g64, 300.0)["achieved"] == round(2 * 8192 * 3072 * 192 / 300e-6 / 1e12, 1)
+    f6 = wl.LinearSpec("p", "w4a4", 4096, 3072, 3072, "x")
+    r = bw.gemm_roofline(f6, 30.0)
+    assert r["bound"] == "mfma" and r["peak"] == bw.FP6_PEAK_TOPS
+    assert bw.gemm_roofline(f6, 30.0, cores="int8")["peak"] == bw.INT8_PEAK_TOPS
+    a8 = wl.LinearSpec("p", "a8w4", 4096, 3072, 3072, "x")
+    assert bw.gemm_roofline(a8, 70.0)["peak"] == bw.INT8_PEAK_TOPS
+    small = wl.LinearSpec("p", "w4a4", 32, 3072, 3072, "x")
+    r = bw.gemm_roofline(small, 4.0)
+    assert r["bound"] == "hbm" and r["achieved"] == round(bw.gemm_bytes(small) / 4.0 / 1e3, 1)
+
+
 def test_c4_plan_matches_the_recipe():
     # 14 linears; W4A4: q, k, mlp_up, mlp_down; INT8: v, out, mod (both streams);
     # the attention input is quantized once for the INT4 and INT8 layers
