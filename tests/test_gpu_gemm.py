@@ -363,6 +363,31 @@ def test_extreme_codes_no_overflow(cr):
     assert np.array_equal(host(raw8).astype(np.int64), og.int_gemm(q8, w8))
 
 
+def test_extreme_codes_matrix_core_paths(cr):
+    """All codes at +-qmax over K = 32768 on the block kernels (M > 64): the
+    fp6 path's float32 sums (|sum| <= 32768 * 49 < 2^24) and the int8 64 x 64
+    blocks' int32 sums (127 * 127 * 32768 < 2^31) stay exact."""
+    M, N, K = 130, 256, 32768                     # 130 rows: a ragged last row block
+    qa = np.full((M, K), 7, np.int64)
+    qa[::2] = -7
+    qa[:, ::3] *= -1
+    qw = np.full((N, K), -7, np.int64)
+    qw[1::2] = 7
+    from oracle import pack as opack
+    one = dev(np.ones(1, np.float32))
+    af6 = dev(opack.f6_pack(qa))
+    wf6 = dev(opack.f6_pack(qw))
+    raw = cr.w4a4_gemm(af6, one, 0, wf6, one, 0, M, N, K, out_type=2)
+    assert np.array_equal(host(raw).astype(np.int64), og.int_gemm(qa, qw))
+    q8 = np.full((M, K), 127, np.int64)
+    q8[::3] = -127
+    w8 = np.full((N, K), -127, np.int64)
+    w8[:, 1::2] = 127
+    raw8 = cr.int8_tensorwise_gemm(dev(q8.astype(np.int8)), one, dev(w8.astype(np.int8)), one, M, N, K,
+                                   out_type=2)
+    assert np.array_equal(host(raw8).astype(np.int64), og.int_gemm(q8, w8))
+
+
 def test_gemm_determinism(cr):
     """Repeated calls give bit-identical outputs: the fp6 W4A4 path (4-bit
     weight tiles expanded per call), the int8-core W4A4 path, INT8 x INT8 and
