@@ -143,6 +143,37 @@ def test_w4a4_ldc_padding(cr):
     assert np.all(o[:, N:] == 7.0)          # nothing written past N
 
 
+@pytest.mark.parametrize("M", [65, 300, 2600])
+def test_int8_ldc_padding(cr, M):
+    """INT8 x INT8 into rows of a wider output (ldc = N + 64): 64 x 64 blocks
+    (65 rows: one row in the last row block; 300 rows) and 256 x 128 blocks
+    (2600 rows); int32, float32 and bf16 outputs; nothing written past N."""
+    N, K = 384, 512
+    if M == 2600:
+        N = 3072                                # enough 256 x 128 tiles to fill a 256-CU part
+    say(f"int8 ldc padding M {M} N {N}")
+    xb = wl.activation(27, M + K, M, K)
+    wb = wl.weight(27, N + K, N, K)
+    ref = ol.int8_linear(xb, wb)
+    a, sa = dev(ref["x"]["codes"]), dev(ref["x"]["scales"])
+    w, sw = dev(ref["w"]["codes"]), dev(ref["w"]["scales"])
+    raw = torch.full((M, N + 64), -5, dtype=torch.int32, device="cuda")
+    cr.int8_tensorwise_gemm(a, sa, w, sw, M, N, K, out_type=2, out=raw)
+    r = host(raw)
+    assert np.array_equal(r[:, :N].astype(np.int64), ref["raw"])
+    assert np.all(r[:, N:] == -5)
+    yf = torch.full((M, N + 64), 7.0, dtype=torch.float32, device="cuda")
+    cr.int8_tensorwise_gemm(a, sa, w, sw, M, N, K, out_type=1, out=yf)
+    o = host(yf)
+    assert rel_l2(o[:, :N], ref["y"]) <= 1e-5
+    assert np.all(o[:, N:] == 7.0)
+    yb = torch.full((M, N + 64), 3.0, dtype=torch.bfloat16, device="cuda")
+    cr.int8_tensorwise_gemm(a, sa, w, sw, M, N, K, out_type=0, out=yb)
+    ob = bf16_to_f32(host(yb))
+    assert rel_l2(ob[:, :N], ref["y"]) <= 2e-3
+    assert np.all(ob[:, N:] == 3.0)
+
+
 G64_CASES = [
     # M, N, K, unsigned, lora(None|bf16|f32), bias
     (16, 256, 512, False, None, False),
