@@ -162,6 +162,30 @@ def test_w4a4_f6_wide_blocks(cr):
     assert rel_l2(yf, ref * s) <= 1e-6
 
 
+@pytest.mark.parametrize("shape", [(7950, 8192, 128), (4000, 3072, 256)], ids=["256x256", "256x192"])
+def test_w4a4_f6_large_blocks_row_scales_bias(cr, shape):
+    """The large blocks' epilogues with per-row scales on both sides and a
+    bias: 256 x 256 blocks (7950 x 8192, ragged last row block) and 256 x 192
+    blocks (4000 x 3072: 256 tiles, ragged); bf16 rows through LDS within
+    2e-3, float32 within 1e-5 of y = s_a[m] s_w[n] sum + b[n] in float64."""
+    M, N, K = shape
+    say(f"w4a4 f6 large blocks row scales bias {shape}")
+    rng = np.random.default_rng(13)
+    qa = rng.integers(-7, 8, size=(M, K))
+    qw = rng.integers(-7, 8, size=(N, K))
+    raw = qa.astype(np.float64) @ qw.astype(np.float64).T
+    sa = (rng.random(M) * 0.02 + 0.001).astype(np.float32)
+    sw = (rng.random(N) * 0.05 + 0.001).astype(np.float32)
+    b = wl.bf16_bits_from_f32((rng.standard_normal(N) * 0.5).astype(np.float32))
+    ref = raw * sa.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :] + \
+        wl.f32_from_bf16_bits(b).astype(np.float64)[None, :]
+    a, w = dev(opack.f6_pack(qa)), dev(opack.f6_pack(qw))
+    yf = host(cr.w4a4_gemm(a, dev(sa), 1, w, dev(sw), 1, M, N, K, bias=bf16_dev(b), out_type=1))
+    assert rel_l2(yf, ref) <= 1e-5
+    yb = bf16_to_f32(host(cr.w4a4_gemm(a, dev(sa), 1, w, dev(sw), 1, M, N, K, bias=bf16_dev(b), out_type=0)))
+    assert rel_l2(yb, ref) <= 2e-3
+
+
 def test_w4a4_f6_ldc_padding(cr):
     M, N, K, ldc = 150, 256, 512, 264
     say("w4a4 f6 ldc")
