@@ -143,11 +143,12 @@ def test_w4a4_ldc_padding(cr):
     assert np.all(o[:, N:] == 7.0)          # nothing written past N
 
 
-@pytest.mark.parametrize("M", [65, 300, 2600])
+@pytest.mark.parametrize("M", [2, 65, 300, 2600])
 def test_int8_ldc_padding(cr, M):
-    """INT8 x INT8 into rows of a wider output (ldc = N + 64): 64 x 64 blocks
-    (65 rows: one row in the last row block; 300 rows) and 256 x 128 blocks
-    (2600 rows); int32, float32 and bf16 outputs; nothing written past N."""
+    """INT8 x INT8 into rows of a wider output (ldc = N + 64): the weight
+    streaming kernel (2 rows), 64 x 64 blocks (65 rows: one row in the last
+    row block; 300 rows) and 256 x 128 blocks (2600 rows); int32, float32 and
+    bf16 outputs; nothing written past N."""
     N, K = 384, 512
     if M == 2600:
         N = 3072                                # enough 256 x 128 tiles to fill a 256-CU part
@@ -222,14 +223,16 @@ def test_w4a4_group64_lowrank(cr, case):
     _check_out(yb, yf, ref["y"])
 
 
-# M <= 64: weight streaming; above: the direct-to-LDS kernel, on a 256-CU
-# part with 64 x 64 blocks while 256 x 128 tiles would not fill the CUs
-# (190 x 256: 12 blocks, a ragged last row block; 512 x 384: 48), then
-# 256 x 128 blocks (2600 x 3072: 264 of them, a ragged last row block;
-# 8000 x 3072: 768, the three-blocks-per-CU ring, ragged too; with a bias the
-# same shape keeps two blocks per CU)
-INT8_CASES = [(2, 256, 3072), (33, 384, 512), (64, 128, 256), (190, 256, 1024), (512, 384, 3072), (2600, 3072, 256),
-              (8000, 3072, 256)]
+# M <= 64: weight streaming on the matrix cores (M = 1 to 5 in one 16-row
+# block, the unused rows clamped; the four waves take runs of four 64-deep
+# k-tiles: K = 256 leaves three waves idle, 1280 ends in a partial round);
+# above: the direct-to-LDS kernel, on a 256-CU part with 64 x 64 blocks while 256 x 128
+# tiles would not fill the CUs (190 x 256: 12 blocks, a ragged last row
+# block; 512 x 384: 48), then 256 x 128 blocks (2600 x 3072: 264 of them, a
+# ragged last row block; 8000 x 3072: 768, the three-blocks-per-CU ring,
+# ragged too; with a bias the same shape keeps two blocks per CU)
+INT8_CASES = [(1, 128, 256), (2, 256, 3072), (3, 384, 1280), (4, 256, 5120), (5, 128, 512), (33, 384, 512),
+              (64, 128, 256), (190, 256, 1024), (512, 384, 3072), (2600, 3072, 256), (8000, 3072, 256)]
 
 
 @pytest.mark.parametrize("bias", [False, True])
@@ -417,6 +420,27 @@ def test_extreme_codes_matrix_core_paths(cr):
     raw8 = cr.int8_tensorwise_gemm(dev(q8.astype(np.int8)), one, dev(w8.astype(np.int8)), one, M, N, K,
                                    out_type=2)
     assert np.array_equal(host(raw8).astype(np.int64), og.int_gemm(q8, w8))
+
+
+@pytest.mark.parametrize("M", [1, 2, 3])
+def test_extreme_codes_int8_streaming(cr, M):
+    """All codes at +-127 over K = 32768 on the weight streaming kernel (one
+    to three tokens): the int32 sums stay exact (127 * 127 * 32768 < 2^31),
+    float32 outputs are their scaled values."""
+    N, K = 256, 32768
+    say(f"int8 streaming extreme codes M {M}")
+    q8 = np.full((M, K), 127, np.int64)
+    q8[:, ::5] = -127
+    w8 = np.full((N, K), -127, np.int64)
+    w8[::3, 1::2] = 127
+    w8[:, ::7] *= -1
+    one = dev(np.ones(1, np.float32))
+    a, w = dev(q8.astype(np.int8)), dev(w8.astype(np.int8))
+    want = og.int_gemm(q8, w8)
+    assert np.array_equal(host(cr.int8_tensorwise_gemm(a, one, w, one, M, N, K, out_type=2)).astype(np.int64), want)
+    sa, sw = dev(np.array([0.5], np.float32)), dev(np.array([0.25], np.float32))
+    yf = host(cr.int8_tensorwise_gemm(a, sa, w, sw, M, N, K, out_type=1)).astype(np.float64)
+    assert np.array_equal(yf, want.astype(np.float32).astype(np.float64) * 0.125)
 
 
 def test_gemm_determinism(cr):
