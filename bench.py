@@ -204,6 +204,12 @@ def main():
     dom = max(layers, key=lambda n: layers[n]["us"])
     dlin = [l for l in r.w.linears if l.name == dom][0]
     t_dom = r.gemm_kernel_alone(dlin, args.steps)
+    dom_fn = r.gemm_kernel_fn(dlin)
+    clock = {"steps": r.shader_clock(r.step, 200),
+             "dominant_kernel": r.shader_clock(lambda i: dom_fn(i % r.nsets), max(200, int(2e5 / t_dom))),
+             "nominal": 2400,
+             "source": "amdsmi current_gfxclks of every XCD, read every ~2 ms from a host thread while "
+                       "untimed whole steps (then the dominant kernel alone) keep the GPU busy"}
     on_f6 = dlin.fmt == "w4a4" and args.cores == "fp6" and dlin.M > bw.SKINNY_M
     peak = bw.FP6_PEAK_TOPS if on_f6 else bw.INT8_PEAK_TOPS
     achieved = 2.0 * dlin.M * dlin.N * dlin.K / t_dom / 1e6
@@ -242,6 +248,7 @@ def main():
         "pct_int8_peak": round(100.0 * eff / bw.INT8_PEAK_TOPS, 2),
         "gemm": layers,
         "rotate_quantize": rqs,
+        "shader_clock_MHz": clock,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic_from_profile(args.cores, dom),
                      "kernel": ("gemm_f6_kernel" if on_f6 else "int8-core GEMM") + f" of {dom} "

@@ -371,6 +371,64 @@ class Runner:
         self.schedule = keep
         return e0.elapsed_time(e1) / steps
 
+    def shader_clock(self, fn, calls):
+        """Shader clock (MHz) while `calls` launches of fn(i) keep the GPU busy:
+        the current clock of every XCD from the GPU's metrics table (amdsmi),
+        read from a host thread about every 2 ms from the fifth to the
+        nine-tenths launch (untimed). None when amdsmi is not available."""
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception:
+            return None
+        import threading
+        torch = self.torch
+        fn(0)
+        torch.cuda.synchronize()
+        first, last = calls // 5, (9 * calls) // 10
+        e_start, e_stop = torch.cuda.Event(), torch.cuda.Event()
+        stop_recorded = threading.Event()          # an event not yet recorded reads as complete
+        samples = []
+
+        def poll():
+            while not e_start.query():
+                time.sleep(0.0005)
+            while not (stop_recorded.is_set() and e_stop.query()):
+                try:
+                    m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                    v = m.get("current_gfxclks")
+                    if not isinstance(v, list):
+                        v = [m.get("current_gfxclk")]
+                    v = [x for x in v if isinstance(x, int) and 0 < x < 65535]
+                    if v:
+                        samples.append(v)
+                except Exception:
+                    pass
+                time.sleep(0.002)
+
+        th = threading.Thread(target=poll, daemon=True)
+        for i in range(calls):
+            fn(i)
+            if i == first:
+                e_start.record(self.stream)
+                if not th.is_alive():
+                    th.start()
+            if i == last:
+                e_stop.record(self.stream)
+                stop_recorded.set()
+        torch.cuda.synchronize()
+        th.join()
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+        if not samples:
+            return None
+        flat = [x for v in samples for x in v]
+        return {"mean": round(sum(flat) / len(flat)), "min": min(flat), "max": max(flat),
+                "readings": len(samples), "xcds": max(len(v) for v in samples)}
+
     def per_call(self, reps):
         """mean us of every call inside whole steps (events around each call)."""
         np, torch = self.np, self.torch

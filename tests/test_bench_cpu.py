@@ -90,3 +90,16 @@ def test_traffic_profiles_consistent():
             assert bench.traffic_from_profile(cores, d["layer"]) == d["hbm_bytes_per_launch"]
         else:
             assert bench.traffic_from_profile(cores, d["layer"]) is None
+
+
+def test_shader_clock_without_a_gpu():
+    """With no GPU the management library finds no device: the clock reading
+    is None and nothing is launched."""
+    calls = []
+
+    class NoGpu:
+        torch = None
+        stream = None
+
+    assert bw.Runner.shader_clock(NoGpu(), calls.append, 50) is None
+    assert calls == []
