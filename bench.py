@@ -148,7 +148,7 @@ def c2_line(steps, warmup, cores):
     ms_chains = r.time_steps(steps, warmup, schedule="chains")
     kern = r.per_call(max(3, steps // 2))
     big = [l for l in r.w.linears if l.M == 4096][0]
-    t_gemm = r.gemm_kernel_alone(big, steps)
+    t_gemm = r.gemm_kernel_median(big)
     out = {"workload": r.w.name, "value": round(r.ops() / (ms * 1e-3) / 1e12, 2), "unit": "TOPS",
            "ms_per_step": round(ms, 5), "ms_per_step_two_streams": round(ms_chains, 5),
            "schedule": "one stream",
@@ -200,10 +200,10 @@ def main():
         gbs = bw.rq_bytes(M, K, key[1]) / us / 1e3
         rqs[f"{key[0]}:{key[1]}"] = {"us": round(us, 2), "GBps": round(gbs, 1),
                                      "pct_hbm": round(100.0 * gbs / bw.HBM_PEAK_GBS, 1)}
-    # dominant kernel: the GEMM kernel of the slowest layer, alone, back to back
+    # dominant kernel: the GEMM kernel of the slowest layer, alone, back to back (median of 7 batches)
     dom = max(layers, key=lambda n: layers[n]["us"])
     dlin = [l for l in r.w.linears if l.name == dom][0]
-    t_dom = r.gemm_kernel_alone(dlin, args.steps)
+    t_dom = r.gemm_kernel_median(dlin)
     dom_fn = r.gemm_kernel_fn(dlin)
     clock = {"steps": r.shader_clock(r.step, 200),
              "dominant_kernel": r.shader_clock(lambda i: dom_fn(i % r.nsets), max(200, int(2e5 / t_dom))),

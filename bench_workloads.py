@@ -444,19 +444,24 @@ class Runner:
                 per[lab].append(ev[i].elapsed_time(ev[i + 1]) * 1e3)
         return {lab: float(np.mean(v)) for lab, v in per.items()}
 
-    def back_to_back(self, fn, reps):
-        """mean us of fn(set index) launched reps times back to back over the sets."""
-        torch = self.torch
-        for i in range(2):
+    def back_to_back(self, fn, reps, batches=1, warm=2):
+        """us per launch of fn(set index) launched reps times back to back over
+        the sets after `warm` untimed launches: the mean of one batch, or the
+        median over `batches` such batches."""
+        np, torch = self.np, self.torch
+        for i in range(warm):
             fn(i % self.nsets)
         torch.cuda.synchronize()
-        e0, e1 = self._events(2)
-        e0.record(self.stream)
-        for i in range(reps):
-            fn(i % self.nsets)
-        e1.record(self.stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps
+        per = []
+        for _ in range(batches):
+            e0, e1 = self._events(2)
+            e0.record(self.stream)
+            for i in range(reps):
+                fn(i % self.nsets)
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) * 1e3 / reps)
+        return float(np.median(per))
 
     def gemm_kernel_fn(self, lin):
         """fn(set index) launching the GEMM kernel of layer `lin` alone. For a
@@ -477,9 +482,17 @@ class Runner:
         self.torch.cuda.synchronize()
         return lambda si: self.launch_gemm(si, lin, key, (exp[si], cr.LAYOUT.F6))
 
-    def gemm_kernel_alone(self, lin, reps):
-        """mean us of the GEMM kernel of layer `lin` alone, back to back."""
-        return self.back_to_back(self.gemm_kernel_fn(lin), reps)
+    def gemm_kernel_alone(self, lin, reps, batches=1, warm=2):
+        """us of the GEMM kernel of layer `lin` alone, back to back (see back_to_back)."""
+        return self.back_to_back(self.gemm_kernel_fn(lin), reps, batches, warm)
+
+    def gemm_kernel_median(self, lin):
+        """us of the GEMM kernel of layer `lin` alone: the median over 7 batches
+        of at least 50 back-to-back launches (enough for ~10 ms each), after 10
+        untimed launches."""
+        fn = self.gemm_kernel_fn(lin)
+        once = self.back_to_back(fn, 5)
+        return self.back_to_back(fn, max(50, int(1e4 / once)), batches=7, warm=10)
 
     def ops(self):
         return sum(2.0 * l.M * l.N * l.K for l in self.w.linears)
@@ -511,8 +524,9 @@ def run(name, steps, warmup, cores="fp6", rot=256):
         rqs[f"{x_id}:{kind}"] = {"us": round(us, 2), "GBps": round(rq_bytes(M, K, kind) / us / 1e3, 1)}
     dom = max(layers, key=lambda n: layers[n]["us"])
     dlin = [l for l in r.w.linears if l.name == dom][0]
-    roof = gemm_roofline(dlin, r.gemm_kernel_alone(dlin, max(5, steps)), cores)
-    roof["kernel"] = f"GEMM kernel of {dom} ({dlin.M}x{dlin.N}x{dlin.K}, {dlin.fmt}), alone, back to back"
+    roof = gemm_roofline(dlin, r.gemm_kernel_median(dlin), cores)
+    roof["kernel"] = (f"GEMM kernel of {dom} ({dlin.M}x{dlin.N}x{dlin.K}, {dlin.fmt}), alone, back to back "
+                      f"(median of 7 batches)")
     eff = r.ops() / (ms * 1e-3) / 1e12
     print(json.dumps({
         "metric": "effective TOPS of fused rotate+quant+W4 GEMM (% INT8 MFMA peak); GB/s",
