@@ -184,6 +184,7 @@ void convrot_reset_counters(void);
  *   zeros        ASYM only: uint8 [rows, K/32], two uint4 zero points per byte
  *                (group 2j low nibble); NULL otherwise
  *   workspace    device scratch of at least convrot_rq_workspace_size(...)
+ *                (0 when the call needs none or refuses the shape)
  *                bytes (needed by TENSOR granularity; may be NULL when that
  *                size is 0). Per-tensor scaling takes one launch for inputs
  *                of at most 64 groups of 256 (one workgroup), one launch
@@ -297,7 +298,9 @@ cr_status convrot_rotate_quantize_dual(const void* x, int64_t rows, int64_t K, i
  *                  dequantized weight row (float32 accumulation), the
  *                  correction vector of the unsigned-shift path; must be NULL
  *                  for ASYM_UINT4
- * Shape: N % 128 == 0, K % 64 == 0 (K % 256 for ROW_GROUP 64 is not required).
+ * Shape: N % 128 == 0, K % 64 == 0 (K % 256 for ROW_GROUP 64 is not required),
+ * K <= 32768, N < 2^31. w4_packed_bytes returns 0 for a shape or format that
+ * w4_pack_weights refuses.
  */
 size_t w4_packed_bytes(int64_t N, int64_t K, cr_qtype qtype, cr_gran gran, int q_group,
                        int which /* 0 packed codes, 1 packed scales, 2 packed zeros */);
@@ -320,7 +323,8 @@ cr_status w4_pack_weights(const void* codes, const void* scales, const void* zer
  *            value and is not checked)
  *   packed   uint8, w4_packed_f6_bytes(N, K) = (N/32)(K/64) 1536 bytes
  * The weight scales (TENSOR [1] or ROW [N]) are used as they are.
- * Shape: N % 128 == 0, K % 128 == 0. One launch on `stream`.
+ * Shape: N % 128 == 0, K % 128 == 0, K <= 32768, N < 2^31 (w4_packed_f6_bytes
+ * returns 0 outside it). One launch on `stream`.
  */
 size_t w4_packed_f6_bytes(int64_t N, int64_t K);
 cr_status w4_pack_weights_f6(const void* codes, int64_t N, int64_t K, void* packed, hipStream_t stream);
@@ -433,6 +437,7 @@ cr_status convrot_dequantize_weights(const void* codes, const void* scales, cons
  *   out         CR_OUT_BF16: bf16 [M, ldc]; CR_OUT_F32: float32; CR_OUT_I32_RAW:
  *               int32 sum_k qa*qw (lora/bias/scales ignored)
  *   workspace   at least w4a4_gemm_workspace_size(N, K, a_layout, w_layout)
+ *               (0 when the call needs none or refuses the shape)
  *               bytes (nonzero only for CR_LAYOUT_F6 codes with CR_LAYOUT_TILED
  *               weights), 16-byte aligned; its contents are overwritten. Calls
  *               sharing a workspace must be ordered on one stream.

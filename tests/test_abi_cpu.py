@@ -172,6 +172,28 @@ def test_rq_workspace_size(cr):
     assert cr.convrot_rq_workspace_size(4096, 2560, 1024, cr.Q.SYM_INT4, cr.GRAN.TENSOR) == 0
 
 
+def test_size_queries_return_zero_for_refused_shapes(cr):
+    """Every size query answers 0 for a shape its call refuses (K above 32768,
+    rows or N at 2^31 and beyond) instead of multiplying out of range."""
+    big = 1 << 40
+    assert cr.convrot_rq_workspace_size(1 << 31, 3072, 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR) == 0
+    assert cr.convrot_rq_workspace_size(4096, 65536, 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR) == 0
+    assert cr.convrot_rq_workspace_size(big, big, 256, cr.Q.SYM_INT4, cr.GRAN.TENSOR) == 0
+    for which in (0, 1, 2):
+        assert cr.w4_packed_bytes(big, big, 3, 2, 16, which) == 0
+        assert cr.w4_packed_bytes(1 << 31, 512, 3, 2, 16, which) == 0
+        assert cr.w4_packed_bytes(256, 65536, 0, 2, 64, which) == 0
+    assert cr.w4_packed_f6_bytes(big, big) == 0
+    assert cr.w4_packed_f6_bytes(1 << 31, 512) == 0
+    assert cr.w4_packed_f6_bytes(256, 65536) == 0
+    assert cr.w4a4_gemm_workspace_size(big, big, cr.LAYOUT.F6, cr.LAYOUT.TILED) == 0
+    assert cr.w4a4_gemm_workspace_size(256, 65536, cr.LAYOUT.F6, cr.LAYOUT.TILED) == 0
+    # the largest accepted shapes still get their sizes
+    assert cr.w4_packed_bytes((1 << 31) - 128, 32768, 0, 0, 0, 0) == ((1 << 31) - 128) * 16384
+    assert cr.w4_packed_f6_bytes(12288, 32768) == 12288 * 32768 * 3 // 4
+    assert cr.w4a4_gemm_workspace_size(12288, 32768, cr.LAYOUT.F6, cr.LAYOUT.TILED) == 12288 * 32768 * 3 // 4
+
+
 def test_pack_validation(cr):
     L = cr.lib
     assert L.w4_pack_weights(_p(A), _p(A), None, 100, 512, 0, 0, 0, _p(A), None, None, None, None) == 2

@@ -142,6 +142,7 @@ size_t convrot_rq_workspace_size(int64_t rows, int64_t K, int rot_group, cr_qtyp
                                  int q_group) {
   (void)q_group;
   if (rot_group == 0 || gran != CR_GRAN_TENSOR || rows < 1 || K < 256 || K % 256) return 0;
+  if (rows >= DIM_MAX || K > KMAX) return 0;   // shapes convrot_rotate_quantize refuses
   if (!(rot_group == 16 || rot_group == 64 || rot_group == 256 || (rot_group == 1024 && K % 1024 == 0))) return 0;
   if (!(qtype == CR_Q_SYM_INT4 || qtype == CR_Q_SYM_INT8)) return 0;
   return cr::rq_tensor_ws_bytes(rows, K, rot_group);
@@ -322,7 +323,7 @@ cr_status convrot_dequantize_weights(const void* codes, const void* scales, cons
 // weight packing
 // ---------------------------------------------------------------------------
 size_t w4_packed_bytes(int64_t N, int64_t K, cr_qtype qtype, cr_gran gran, int q_group, int which) {
-  if (N < 128 || K < 64 || N % 128 || K % 64) return 0;
+  if (N < 128 || K < 64 || N % 128 || K % 64 || K > KMAX || N >= DIM_MAX) return 0;
   switch (which) {
     case 0: return (size_t)(N * K / 2);
     case 1:
@@ -335,7 +336,7 @@ size_t w4_packed_bytes(int64_t N, int64_t K, cr_qtype qtype, cr_gran gran, int q
 }
 
 size_t w4_packed_f6_bytes(int64_t N, int64_t K) {
-  if (N < 128 || K < 128 || N % 128 || K % 128) return 0;
+  if (N < 128 || K < 128 || N % 128 || K % 128 || K > KMAX || N >= DIM_MAX) return 0;
   return (size_t)((N / 32) * (K / 64) * 1536);
 }
 
@@ -428,7 +429,7 @@ static cr_status gemm_common(const void* a, const void* w, const void* out, cr_o
 
 size_t w4a4_gemm_workspace_size(int64_t N, int64_t K, cr_layout a_layout, cr_layout w_layout) {
   if (a_layout != CR_LAYOUT_F6 || w_layout != CR_LAYOUT_TILED) return 0;
-  if (N < 128 || K < 128 || N % 128 || K % 128) return 0;
+  if (N < 128 || K < 128 || N % 128 || K % 128 || K > KMAX || N >= DIM_MAX) return 0;
   return (size_t)((N / 32) * (K / 64) * 1536);   // the weights as fp6 fragments
 }
 
