@@ -53,6 +53,34 @@ def _kind_of(lin, cores):
     return "u4_g64" if lin.unsigned_shift else "s4_g64"
 
 
+def fuse_shared_inputs(w):
+    """The workload with every run of W4A4 tensorwise layers that read the
+    same input with the same token count, depth, chain and phase (an MMDiT
+    block's Q and K projections) merged into one layer: one GEMM call on
+    their weights side by side along N, each part keeping its own per-tensor
+    weight scale (carried as per-channel scales). Every output element is
+    computed by the same arithmetic as in the separate calls."""
+    import workloads as wl
+    out = wl.Workload(w.config_id, w.name, acts=dict(w.acts))
+    lins = list(w.linears)
+    i = 0
+    while i < len(lins):
+        a = lins[i]
+        grp = [a]
+        while (a.fmt == "w4a4" and i + len(grp) < len(lins)):
+            b = lins[i + len(grp)]
+            if (b.fmt, b.x_id, b.M, b.K, b.chain, b.phase, b.rot) != (a.fmt, a.x_id, a.M, a.K, a.chain, a.phase, a.rot):
+                break
+            grp.append(b)
+        if len(grp) == 1:
+            out.linears.append(a)
+        else:
+            out.linears.append(wl.LinearSpec("+".join(l.name for l in grp), "w4a4", a.M, sum(l.N for l in grp), a.K,
+                                             a.x_id, rot=a.rot, chain=a.chain, phase=a.phase, parts=tuple(grp)))
+        i += len(grp)
+    return out
+
+
 def plan(w, cores="fp6"):
     """RQ passes (x_id, kind, layer) and GEMMs (lin, rq key) of workload w."""
     kinds = {}
@@ -124,7 +152,7 @@ def gemm_roofline(lin, us, cores="fp6"):
 class Runner:
     """One workload on the GPU path with `nsets` cold buffer sets."""
 
-    def __init__(self, name, cores="fp6", nsets=2, rot=256, workload=None, schedule="serial"):
+    def __init__(self, name, cores="fp6", nsets=2, rot=256, workload=None, schedule="serial", fuse=False):
         import numpy as np
         import torch
         import w4a8_rotated_quantized_amd as cr
@@ -134,6 +162,9 @@ class Runner:
         torch.cuda.set_device(self.dev)
         self.stream = torch.cuda.current_stream()
         self.w = workload if workload is not None else wl.CONFIGS[name]()
+        w_def = self.w                 # the workload as defined (weights are drawn per defined linear)
+        if fuse:
+            self.w = fuse_shared_inputs(self.w)
         self.cores = cores
         self.rot = rot
         self.nsets = nsets
@@ -151,21 +182,31 @@ class Runner:
         prep = {}
         for lin in w.linears:
             N, K = lin.N, lin.K
-            if lin.fmt in ("w4a4", "a8w4"):
-                wc, ws, _, _ = cr.convrot_rotate_quantize(bf16(wl.weight_bits(w, lin)), rot, cr.Q.SYM_INT4,
+            if lin.parts:
+                # each part rotated, quantized (per-tensor scale) and packed on
+                # its own; tiles and scales side by side along N
+                tiles, scales = [], []
+                for part in lin.parts:
+                    wc, ws, _, _ = cr.convrot_rotate_quantize(bf16(wl.weight_bits(w_def, part)), rot, cr.Q.SYM_INT4,
+                                                              cr.GRAN.TENSOR)
+                    tiles.append(cr.w4_pack_weights(wc, ws, part.N, K)[0])
+                    scales.append(ws.expand(part.N))
+                prep[lin.name] = dict(w=torch.cat(tiles), ws=torch.cat(scales).contiguous(), w_gran=cr.GRAN.ROW)
+            elif lin.fmt in ("w4a4", "a8w4"):
+                wc, ws, _, _ = cr.convrot_rotate_quantize(bf16(wl.weight_bits(w_def, lin)), rot, cr.Q.SYM_INT4,
                                                           cr.GRAN.TENSOR)
                 prep[lin.name] = dict(w=cr.w4_pack_weights(wc, ws, N, K)[0], ws=ws)
             elif lin.fmt == "int8":
-                wc, ws, _, _ = cr.convrot_rotate_quantize(bf16(wl.weight_bits(w, lin)), rot, cr.Q.SYM_INT8,
+                wc, ws, _, _ = cr.convrot_rotate_quantize(bf16(wl.weight_bits(w_def, lin)), rot, cr.Q.SYM_INT8,
                                                           cr.GRAN.TENSOR)
                 prep[lin.name] = dict(w=wc, ws=ws)
             elif lin.fmt == "w4a8":
-                wc, ws, wz, _ = cr.convrot_rotate_quantize(bf16(wl.weight_bits(w, lin)), 256, cr.Q.ASYM_UINT4,
+                wc, ws, wz, _ = cr.convrot_rotate_quantize(bf16(wl.weight_bits(w_def, lin)), 256, cr.Q.ASYM_UINT4,
                                                            cr.GRAN.ROW_GROUP, 16)
                 p, ps, pz, _ = cr.w4_pack_weights(wc, ws, N, K, cr.Q.ASYM_UINT4, cr.GRAN.ROW_GROUP, 16, zeros=wz)
                 prep[lin.name] = dict(w=p, ws=ps, wz=pz)
             else:
-                l1, l2, r = wl.lowrank_bits(w, lin)
+                l1, l2, r = wl.lowrank_bits(w_def, lin)
                 wc, ws, _, _ = cr.convrot_rotate_quantize(bf16(r), 0, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64)
                 p, ps, _, wsum = cr.w4_pack_weights(wc, ws, N, K, cr.Q.SYM_INT4, cr.GRAN.ROW_GROUP, 64,
                                                     want_wsum=True)
@@ -186,7 +227,8 @@ class Runner:
         self.sets = []
         for si in range(nsets):
             st = {"acts": {k: (v if si == 0 else v.clone()) for k, v in acts.items()},
-                  "prep": {k: {kk: (vv if si == 0 else vv.clone()) for kk, vv in d.items()} for k, d in prep.items()},
+                  "prep": {k: {kk: (vv if si == 0 or not hasattr(vv, "clone") else vv.clone()) for kk, vv in d.items()}
+                           for k, d in prep.items()},
                   "rq": {}}
             # one GEMM workspace (weight expansion target) per chain: chains may run concurrently
             st["gws_c"] = {c: torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for c in self.chains}
@@ -288,7 +330,7 @@ class Runner:
         M, N, K = lin.M, lin.N, lin.K
         wq, wlay = (p["w"], cr.LAYOUT.TILED) if w_override is None else w_override
         if lin.fmt == "w4a4":
-            cr.w4a4_gemm(o["codes"], o["scales"], 0, wq, p["ws"], 0, M, N, K, out=y, w_layout=wlay,
+            cr.w4a4_gemm(o["codes"], o["scales"], 0, wq, p["ws"], p.get("w_gran", 0), M, N, K, out=y, w_layout=wlay,
                          workspace=st["gws_c"][lin.chain])
         elif lin.fmt == "a8w4":
             cr.w4a4_gemm(o["codes"], o["scales"], cr.GRAN.ROW, p["w"], p["ws"], 0, M, N, K, out=y,

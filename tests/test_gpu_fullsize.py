@@ -56,18 +56,20 @@ class _Err:
 _RUNNERS = {}
 
 
-def _runner(name):
-    """one step of the workload as the benchmark runs it (one per module and workload)"""
+def _runner(name, fuse=False):
+    """one step of the workload as the benchmark runs it (one per module and
+    workload); fuse: layers sharing an input run as one call, as in bench.py"""
     import bench_workloads as bw
-    if name not in _RUNNERS:
+    key = (name, fuse)
+    if key not in _RUNNERS:
         for k in list(_RUNNERS):            # one workload's buffers on the device at a time
             del _RUNNERS[k]
         torch.cuda.empty_cache()
-        r = bw.Runner(name, nsets=1, schedule="chains")   # token streams on streams of their own
+        r = bw.Runner(name, nsets=1, schedule="chains", fuse=fuse)   # token streams on streams of their own
         r.step(0)
         torch.cuda.synchronize()
-        _RUNNERS[name] = r
-    return _RUNNERS[name]
+        _RUNNERS[key] = r
+    return _RUNNERS[key]
 
 
 _ACT = {}
@@ -140,6 +142,44 @@ def test_c4_layer_full(cr, name):
     lin = [l for l in r.w.linears if l.name == name][0]
     say(f"c4 full {name} {lin.M}x{lin.N}x{lin.K}")
     _tensorwise_layer(cr, r, lin)
+
+
+@pytest.mark.parametrize("s", ["img", "txt"])
+def test_c4_fused_qk_full(cr, s):
+    """The Q and K projections of one token stream as the benchmark runs them:
+    one call on both weights side by side along N, per-channel scales holding
+    each part's own per-tensor scale. Weight tiles, int32 sums and bf16
+    outputs of both parts against the oracle, every output row."""
+    r = _runner("c4", fuse=True)
+    lin = [l for l in r.w.linears if l.name == f"{s}_q+{s}_k"][0]
+    w_def = wl.CONFIGS["c4"]()
+    M, N, K = lin.M, lin.N, lin.K
+    say(f"c4 fused {lin.name} {M}x{N}x{K}")
+    st = r.sets[0]
+    key = [k for l, k in r.gemm_plan if l.name == lin.name][0]
+    o, p = st["rq"][key], st["prep"][lin.name]
+    xa = _oracle_act(w_def, lin.x_id, "int4")
+    raw = host(cr.w4a4_gemm(o["codes"], o["scales"], 0, p["w"], p["ws"], cr.GRAN.ROW, M, N, K,
+                            out_type=cr.OUT.I32_RAW, workspace=st["gws"]))
+    y = bf16_to_f32(host(st["out"][lin.name]))
+    tiles, ws = bytes_of(p["w"]), host(p["ws"])
+    A = xa["values"].astype(np.float64)
+    n0 = off = 0
+    for part in lin.parts:
+        wq = ol.rotate_quantize(wl.weight_bits(w_def, part), 256, "int4", "tensor")
+        t = opack.tile_pack_w4a4(wq["codes"]).reshape(-1)
+        assert np.array_equal(tiles[off:off + t.size], t), f"{part.name} tiles"
+        assert np.all(ws[n0:n0 + part.N] == np.float32(wq["scales"]).reshape(-1)[0]), f"{part.name} scales"
+        W = wq["values"].astype(np.float64)
+        err = _Err()
+        for r0, r1 in _chunks(M):
+            ref_raw = np.rint(A[r0:r1] @ W.T).astype(np.int64)
+            assert np.array_equal(raw[r0:r1, n0:n0 + part.N].astype(np.int64), ref_raw), f"{part.name} rows {r0}"
+            err.add(y[r0:r1, n0:n0 + part.N],
+                    ol.epilogue_scalar(ref_raw, xa["scales"], "tensor", wq["scales"], "tensor"))
+        assert err.rel() <= 2e-3, (part.name, err.rel())
+        n0 += part.N
+        off += t.size
 
 
 def test_c3_w4a8_full(cr):

@@ -129,6 +129,9 @@ class LinearSpec:
            every layer of phase p - 1 of all chains (the joint attention of an
            MMDiT block reads the Q, K and V of both token streams, and each
            stream's output projection reads the attention's output).
+    parts: for a layer that runs several linears of the same input as one
+           call (their weights side by side along N), those linears; empty
+           for an ordinary layer.
     """
     name: str
     fmt: str
@@ -141,6 +144,7 @@ class LinearSpec:
     rank: int = 0
     chain: str = ""
     phase: int = 0
+    parts: tuple = ()
 
 
 @dataclass
