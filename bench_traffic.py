@@ -76,7 +76,7 @@ def _out(cores, ext):
 def run(layer, cores):
     import torch
     dev = torch.device("cuda:0")
-    r = bw.Runner("c4", cores)
+    r = bw.Runner("c4", cores, fuse=True)      # the step as bench.py runs it (fused Q/K calls)
     lin = [l for l in r.w.linears if l.name == layer][0]
     n = COPY_MIB * (1 << 20) // 2
     a = torch.randn(n, device=dev).to(torch.bfloat16)
