@@ -143,12 +143,14 @@ def test_w4a4_f6_gemm(cr, case):
     assert np.array_equal(host(yb_e), host(yb))
 
 
-def test_w4a4_f6_wide_blocks(cr):
-    """256 x 256 blocks (wide outputs, at least four rounds of tiles: 7950 x
-    8192 gives 1024, the last row block ragged): raw sums equal the exact
-    integer product, float32 outputs its scaled value."""
-    M, N, K = 7950, 8192, 128
-    say("w4a4 f6 256x256 blocks")
+@pytest.mark.parametrize("M", [7950, 6100])
+def test_w4a4_f6_wide_blocks(cr, M):
+    """256 x 256 blocks (wide outputs, at least three rounds of tiles on 256
+    CUs: 7950 x 8192 gives 1024 tiles, 6100 x 8192 exactly 768, the last row
+    block ragged in both): raw sums equal the exact integer product, float32
+    outputs its scaled value."""
+    N, K = 8192, 128
+    say(f"w4a4 f6 256x256 blocks M={M}")
     rng = np.random.default_rng(11)
     qa = rng.integers(-7, 8, size=(M, K))
     qw = rng.integers(-7, 8, size=(N, K))
@@ -162,10 +164,12 @@ def test_w4a4_f6_wide_blocks(cr):
     assert rel_l2(yf, ref * s) <= 1e-6
 
 
-@pytest.mark.parametrize("shape", [(7950, 8192, 128), (4000, 3072, 256)], ids=["256x256", "256x192"])
+@pytest.mark.parametrize("shape", [(7950, 8192, 128), (6100, 8192, 128), (4000, 3072, 256)],
+                         ids=["256x256", "256x256_three_rounds", "256x192"])
 def test_w4a4_f6_large_blocks_row_scales_bias(cr, shape):
     """The large blocks' epilogues with per-row scales on both sides and a
-    bias: 256 x 256 blocks (7950 x 8192, ragged last row block) and 256 x 192
+    bias: 256 x 256 blocks (7950 x 8192 and 6100 x 8192, ragged last row
+    blocks, four and three rounds of tiles) and 256 x 192
     blocks (4000 x 3072: 256 tiles, ragged); bf16 rows through LDS within
     2e-3, float32 within 1e-5 of y = s_a[m] s_w[n] sum + b[n] in float64."""
     M, N, K = shape

@@ -658,14 +658,14 @@ static hipError_t launch_f6_out(const GemmParams& p, hipStream_t s) {
     return hipGetLastError();
   }
   // 256 x 256 blocks (16 waves, 147 KB of stages) for wide outputs with at
-  // least four rounds of tiles (8192 x 12288: 1536): a sixth less operand
-  // traffic per output than 256 x 192 (the operand stream through L2 and the
-  // last-level cache bounds these shapes); 256 x 192 blocks (one per CU, 12
+  // least three rounds of tiles on the 256 CUs (8192 x 12288: 1536; 8192 x
+  // 6144: 768, measured 103 against 111-113 us with 256 x 192 blocks): a
+  // sixth less operand traffic per output than 256 x 192; 256 x 192 blocks (one per CU, 12
   // waves) when they fill the chip: a third less operand traffic per output
   // than 128 x 128 (measured on MI355X at 4096 x 3072 x 3072: 30.4 against
   // 32.9 us); otherwise 128 x 128 blocks, three per CU, or 64 x 64 blocks
   // for mid-size M
-  if (p.N % 256 == 0 && ((p.M + 255) / 256) * (p.N / 256) >= 1024) {
+  if (p.N % 256 == 0 && ((p.M + 255) / 256) * (p.N / 256) >= 768) {
     const int64_t tiles = ((p.M + 255) / 256) * (p.N / 256);
     hipLaunchKernelGGL((gemm_f6_kernel<256, 256, 2, 2, 2, 3, 1, OUT>), dim3((unsigned)tiles), dim3(1024), 0, s, p);
     return hipGetLastError();
