@@ -103,3 +103,27 @@ def test_shader_clock_without_a_gpu():
 
     assert bw.Runner.shader_clock(NoGpu(), calls.append, 50) is None
     assert calls == []
+
+
+def test_fuse_shared_inputs_merges_only_same_input_w4a4_runs():
+    """The block's Q and K projections (same input, shape, chain and phase,
+    W4A4) become one layer with both weights side by side; every other layer
+    stays as defined; the work, the inputs and the defined parts are kept."""
+    w = wl.CONFIGS["c4"]()
+    f = bw.fuse_shared_inputs(w)
+    names = [l.name for l in f.linears]
+    assert names == ["img_q+img_k", "img_v", "img_out", "img_mlp_up", "img_mlp_down", "img_mod",
+                     "txt_q+txt_k", "txt_v", "txt_out", "txt_mlp_up", "txt_mlp_down", "txt_mod"]
+    qk = f.linears[0]
+    assert (qk.M, qk.N, qk.K, qk.x_id, qk.chain, qk.phase) == (8192, 6144, 3072, "img_attn", "img", 0)
+    assert [p.name for p in qk.parts] == ["img_q", "img_k"] and all(p in w.linears for p in qk.parts)
+    assert sum(2 * l.M * l.N * l.K for l in f.linears) == sum(2 * l.M * l.N * l.K for l in w.linears)
+    assert f.acts == w.acts and f.config_id == w.config_id
+    # the weights of every defined linear are drawn as in the defined workload
+    assert all(not l.parts for l in w.linears)
+    # nothing to merge elsewhere: a single W4A4 layer, the low-rank format, INT8 layers
+    for name in ("c2", "c3", "c5"):
+        d = wl.CONFIGS[name]()
+        assert [l.name for l in bw.fuse_shared_inputs(d).linears] == [l.name for l in d.linears]
+    # the RQ plan is unchanged: one dual pass per stream's attention input
+    assert bw.plan(f)[0] == bw.plan(w)[0]
