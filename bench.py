@@ -99,6 +99,75 @@ def traffic_from_profile(cores, layer):
     return d.get("hbm_bytes_per_launch")
 
 
+def _blas_threads():
+    import numpy as np
+    try:
+        import threadpoolctl
+        np.ones((64, 64)) @ np.ones((64, 64))
+        info = threadpoolctl.threadpool_info()
+        return max([i.get("num_threads", 1) for i in info] + [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline_workload(name, budget_s, rot=256):
+    """The oracle (numpy) on a bounded sample of workload `name`, for the
+    side lines: every linear on the first 512 rows of its input and its first
+    1536 output channels, in the linear's own format (W4A4 tensorwise, INT8,
+    W4A8 asymmetric g16 against per-token INT8, 8-bit activations against
+    W4A4 weights, or the low-rank corrected 64-group format). Weights (and
+    the low-rank split) prepared once, untimed."""
+    import numpy as np  # noqa: F401
+    import workloads as wl
+    from oracle import linear as ol, gemm as og
+    w = wl.CONFIGS[name]()
+    NS, MR = 1536, 512
+    jobs = []
+    for lin in w.linears:
+        rows = min(MR, w.acts[lin.x_id][0])
+        x = wl.act_bits(w, lin.x_id, rows=rows)
+        ns = min(NS, lin.N)
+        r = rot                                 # the runner's rotation of the tensorwise formats
+        if lin.fmt == "w4a4":
+            wp = ol.prepare_w4a4(wl.weight_bits(w, lin, rows=ns), r)
+            jobs.append((lambda x=x, wp=wp, r=r: ol.w4a4_linear(x, None, r, wprep=wp), rows, ns, lin.K))
+        elif lin.fmt == "int8":
+            wq = ol.rotate_quantize(wl.weight_bits(w, lin, rows=ns), r, "int8", "tensor")
+
+            def f(x=x, wq=wq, r=r):
+                xa = ol.rotate_quantize(x, r, "int8", "tensor")
+                acc = og.int_gemm(xa["values"], wq["values"])
+                return ol.epilogue_scalar(acc, xa["scales"], "tensor", wq["scales"], "tensor")
+            jobs.append((f, rows, ns, lin.K))
+        elif lin.fmt == "a8w4":
+            wp = ol.prepare_w4a4(wl.weight_bits(w, lin, rows=ns), r)
+            jobs.append((lambda x=x, wp=wp, r=r: ol.a8w4_linear(x, None, r, a_gran="row", wprep=wp), rows, ns, lin.K))
+        elif lin.fmt == "w4a8":
+            wp = ol.prepare_w4a8(wl.weight_bits(w, lin, rows=ns), 256, 16)
+            jobs.append((lambda x=x, wp=wp: ol.w4a8_linear(x, None, 256, 16, wprep=wp), rows, ns, lin.K))
+        else:                                   # low-rank corrected, 64-group scales, rotation off
+            l1, l2, res = wl.lowrank_bits(w, lin)
+            wp = ol.prepare_w4a4(res[:ns], 0, "row_group", 64)
+            jobs.append((lambda x=x, wp=wp, l1=l1[:ns], l2=l2, sh=lin.unsigned_shift:
+                         ol.w4a4_linear(x, None, 0, "row_group", "row_group", 64, sh, l1, l2, wprep=wp),
+                         rows, ns, lin.K))
+    cores = _blas_threads()
+    ops1 = sum(2.0 * rows * ns * K for _, rows, ns, K in jobs)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for fn, _, _, _ in jobs:
+            fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": ops1 * reps / el / 1e12, "unit": "TOPS", "cores": int(cores), "kind": "oracle",
+            "sample": f"{reps} pass(es) of the workload's {len(jobs)} linear(s) on the first {MR} rows of each "
+                      f"input and the first {NS} output channels of each weight ({ops1 / 1e9:.1f} GOP each) in "
+                      f"{el:.1f} s (numpy; rotation and quantization single-threaded, integer products as "
+                      f"float64 BLAS, BLAS threads={cores})"}
+
+
 def cpu_baseline(budget_s):
     """The oracle (numpy) running a bounded sample of the block on the host:
     all 14 layers on the first 512 rows of every activation tensor (all of
@@ -180,7 +249,11 @@ def main():
         sys.exit(2)
     if args.workload != "c4":
         for name in args.workload.split(","):
-            bw.run(name, args.steps, args.warmup, cores=args.cores, rot=args.rot_group)
+            extra = None
+            if not args.no_cpu and name != "merge":
+                def extra(line, name=name):
+                    line["cpu_baseline"] = cpu_baseline_workload(name, args.cpu_seconds, args.rot_group)
+            bw.run(name, args.steps, args.warmup, cores=args.cores, rot=args.rot_group, extra=extra)
         return
 
     import torch

@@ -540,8 +540,9 @@ class Runner:
         return sum(2.0 * l.M * l.N * l.K for l in self.w.linears)
 
 
-def run(name, steps, warmup, cores="fp6", rot=256):
-    """One JSON line for workload `name` (bench.py --workload NAME)."""
+def run(name, steps, warmup, cores="fp6", rot=256, extra=None):
+    """One JSON line for workload `name` (bench.py --workload NAME); extra(line)
+    may add fields (bench.py's CPU baseline) before it is printed."""
     if name == "merge":
         return run_merge(steps, warmup)
     import torch
@@ -570,7 +571,7 @@ def run(name, steps, warmup, cores="fp6", rot=256):
     roof["kernel"] = (f"GEMM kernel of {dom} ({dlin.M}x{dlin.N}x{dlin.K}, {dlin.fmt}), alone, back to back "
                       f"(median of 7 batches)")
     eff = r.ops() / (ms * 1e-3) / 1e12
-    print(json.dumps({
+    line = {
         "metric": "effective TOPS of fused rotate+quant+W4 GEMM (% INT8 MFMA peak); GB/s",
         "value": round(eff, 2), "unit": "TOPS", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms, 5),
@@ -584,7 +585,11 @@ def run(name, steps, warmup, cores="fp6", rot=256):
         "dominant_gemm": {"layer": dom, **layers[dom]},
         "roofline": roof,
         "setup_s": round(r.setup_s, 1),
-    }))
+    }
+    del r
+    if extra is not None:
+        extra(line)
+    print(json.dumps(line))
 
 
 def run_merge(steps, warmup):
