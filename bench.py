@@ -99,6 +99,31 @@ def traffic_from_profile(cores, layer):
     return d.get("hbm_bytes_per_launch")
 
 
+def stream_copy_gbs():
+    """Bytes moved per second (read + write) by a device-to-device copy of
+    1 GiB, median of 5 (after 2 untimed), HIP events on the launch stream:
+    the box's streaming bandwidth that the quantizers are also reported
+    against."""
+    import torch
+    n = 1 << 29                                   # bf16 elements: 1 GiB
+    a = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    s = torch.cuda.current_stream()
+    ts = []
+    for i in range(7):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        b.copy_(a)
+        e1.record(s)
+        e1.synchronize()
+        if i >= 2:
+            ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    del a, b
+    torch.cuda.empty_cache()
+    return 2.0 * n * 2 / (ts[len(ts) // 2] * 1e-3) / 1e9
+
+
 def _blas_threads():
     import numpy as np
     try:
@@ -277,13 +302,15 @@ def main():
         us = kern[f"gemm:{lin.name}"]
         layers[lin.name] = {"us": round(us, 2), "TOPS": round(2.0 * lin.M * lin.N * lin.K / us / 1e6, 1),
                             "GBps": round(bw.gemm_bytes(lin) / us / 1e3, 1)}
+    copy_gbs = stream_copy_gbs()
     rqs = {}
     for key in r.rq_plan:
         M, K = r.w.acts[key[0]][0], r.w.acts[key[0]][1]
         us = kern[f"rq:{key[0]}:{key[1]}"]
         gbs = bw.rq_bytes(M, K, key[1]) / us / 1e3
         rqs[f"{key[0]}:{key[1]}"] = {"us": round(us, 2), "GBps": round(gbs, 1),
-                                     "pct_hbm": round(100.0 * gbs / bw.HBM_PEAK_GBS, 1)}
+                                     "pct_hbm": round(100.0 * gbs / bw.HBM_PEAK_GBS, 1),
+                                     "pct_stream_copy": round(100.0 * gbs / copy_gbs, 1)}
     # dominant kernel: the GEMM kernel of the slowest layer, alone, back to back (median of 7 batches)
     dom = max(layers, key=lambda n: layers[n]["us"])
     dlin = [l for l in r.w.linears if l.name == dom][0]
@@ -338,6 +365,7 @@ def main():
         "pct_int8_peak": round(100.0 * eff / bw.INT8_PEAK_TOPS, 2),
         "gemm": layers,
         "rotate_quantize": rqs,
+        "stream_copy_GBps": round(copy_gbs, 1),
         "shader_clock_MHz": clock,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic_from_profile(args.cores, dom),
