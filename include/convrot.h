@@ -129,6 +129,14 @@ typedef struct cr_counters {
 void convrot_get_counters(cr_counters* out);
 void convrot_reset_counters(void);
 
+/* Launch log: with CONVROT_LOG=1 in the environment (read once per process)
+ * every call that enqueues work writes one line to stderr:
+ *   [convrot] <entry point> sizes <a> <b> <c> formats <x> <y> <z>: <n> kernel(s), enqueued
+ * sizes are (rows or M, K or N, rotation group or K) and formats the call's
+ * enum arguments (quantizer type, granularity, layout; for the GEMMs the
+ * layouts or granularity and the output type), as each entry lists them.
+ * Calls refused by validation write nothing (their status says why). */
+
 /* ------------------------------------------------------------------------
  * convrot_rotate_quantize - online rotation + dynamic quantization of
  * activations, and the offline rotation + quantization of weights.

@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -60,7 +62,33 @@ cr_status device_check() {
   return CR_OK;
 }
 
+// CONVROT_LOG=1 in the environment (read once per process): one line on
+// stderr for every call that enqueues work, with the entry point, its sizes
+// and format arguments (as each entry tags them) and the kernels enqueued.
+bool log_on() {
+  static const bool on = [] {
+    const char* v = std::getenv("CONVROT_LOG");
+    return v && v[0] == '1' && v[1] == 0;
+  }();
+  return on;
+}
+struct CallInfo {
+  const char* name;
+  long long d[3];
+  int f[3];
+};
+thread_local CallInfo g_call{};
+struct CallTag {   // first statement of an entry point that enqueues work
+  CallTag(const char* name, int64_t d0, int64_t d1, int64_t d2, int f0 = 0, int f1 = 0, int f2 = 0) {
+    g_call = CallInfo{name, {(long long)d0, (long long)d1, (long long)d2}, {f0, f1, f2}};
+  }
+};
+
 cr_status finish_launch(hipError_t e, int entry, uint64_t n) {
+  if (log_on() && g_call.name)
+    std::fprintf(stderr, "[convrot] %s sizes %lld %lld %lld formats %d %d %d: %llu kernel(s), %s\n", g_call.name,
+                 g_call.d[0], g_call.d[1], g_call.d[2], g_call.f[0], g_call.f[1], g_call.f[2],
+                 (unsigned long long)n, e == hipSuccess ? "enqueued" : hipGetErrorString(e));
   if (e != hipSuccess) return hip_fail(e);
   g_launch[entry].fetch_add(n, std::memory_order_relaxed);
   return CR_OK;
@@ -223,6 +251,7 @@ cr_status convrot_rotate_quantize(const void* x, int64_t rows, int64_t K, int64_
                                   const void* lora_down, int R, void* lora_act, int lora_act_f32,
                                   void* codes, cr_layout layout, void* scales, void* zeros, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
+  CallTag tag_("convrot_rotate_quantize", rows, K, rot_group, qtype, gran, layout);
   return rotate_quantize_impl(x, rows, K, ldx, rot_group, qtype, gran, q_group, shift, smooth, lora_down, R,
                               lora_act, lora_act_f32, codes, layout, scales, zeros, workspace, workspace_bytes,
                               stream, false);
@@ -233,6 +262,7 @@ cr_status convrot_rotate_quantize_noalloc(const void* x, int64_t rows, int64_t K
                                           const float* smooth, const void* lora_down, int R, void* lora_act,
                                           int lora_act_f32, void* codes, cr_layout layout, void* scales, void* zeros,
                                           hipStream_t stream) {
+  CallTag tag_("convrot_rotate_quantize_noalloc", rows, K, rot_group, qtype, gran, layout);
   return rotate_quantize_impl(x, rows, K, ldx, rot_group, qtype, gran, q_group, shift, smooth, lora_down, R,
                               lora_act, lora_act_f32, codes, layout, scales, zeros, nullptr, 0, stream, true);
 }
@@ -240,6 +270,7 @@ cr_status convrot_rotate_quantize_noalloc(const void* x, int64_t rows, int64_t K
 cr_status convrot_rotate_quantize_dual(const void* x, int64_t rows, int64_t K, int64_t ldx, int rot_group,
                                        void* codes4, cr_layout layout4, float* scale4, void* codes8, float* scale8,
                                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  CallTag tag_("convrot_rotate_quantize_dual", rows, K, rot_group, layout4);
   if (rot_group == 0) return CR_ERR_UNSUPPORTED_FORMAT;       // the per-tensor rotated path only
   cr_status st = rq_validate(x, rows, K, ldx, rot_group, CR_Q_SYM_INT4, CR_GRAN_TENSOR, 0, nullptr, 0, nullptr,
                              codes4, scale4, nullptr);
@@ -279,6 +310,7 @@ cr_status convrot_dequantize_weights(const void* codes, const void* scales, cons
                                      cr_qtype qtype, cr_gran gran, int q_group, int rot_group,
                                      const void* delta_up, const void* delta_down, int R, void* out,
                                      hipStream_t stream) {
+  CallTag tag_("convrot_dequantize_weights", N, K, rot_group, qtype, gran, q_group);
   if (!codes || !scales || !out) return CR_ERR_INVALID_ARGUMENT;
   if (!aligned16(codes) || !aligned16(scales) || !aligned16(out)) return CR_ERR_INVALID_ARGUMENT;
   if ((int)qtype < 0 || (int)qtype > 3 || (int)gran < 0 || (int)gran > 2) return CR_ERR_INVALID_ARGUMENT;
@@ -341,6 +373,7 @@ size_t w4_packed_f6_bytes(int64_t N, int64_t K) {
 }
 
 cr_status w4_pack_weights_f6(const void* codes, int64_t N, int64_t K, void* packed, hipStream_t stream) {
+  CallTag tag_("w4_pack_weights_f6", N, K, 0);
   if (!codes || !packed || !aligned16(codes) || !aligned16(packed)) return CR_ERR_INVALID_ARGUMENT;
   if (N < 128 || K < 128 || N % 128 || K % 128 || K > KMAX || N >= DIM_MAX) return CR_ERR_UNSUPPORTED_SHAPE;
   if ((N / 32) * (K / 64) * 1536 >= ((int64_t)1 << 32)) return CR_ERR_UNSUPPORTED_SHAPE;
@@ -352,6 +385,7 @@ cr_status w4_pack_weights_f6(const void* codes, int64_t N, int64_t K, void* pack
 }
 
 cr_status w4_pack_lora_up(const void* up, int64_t N, int R, void* packed, hipStream_t stream) {
+  CallTag tag_("w4_pack_lora_up", N, R, 0);
   if (!up || !packed || !aligned16(up) || !aligned16(packed)) return CR_ERR_INVALID_ARGUMENT;
   if (N < 128 || N % 128 || N >= DIM_MAX) return CR_ERR_UNSUPPORTED_SHAPE;
   if (R != 32 && R != 64) return CR_ERR_UNSUPPORTED_FORMAT;
@@ -363,6 +397,7 @@ cr_status w4_pack_lora_up(const void* up, int64_t N, int R, void* packed, hipStr
 }
 
 cr_status w4_expand_weights_f6(const void* tiles, int64_t N, int64_t K, void* f6, hipStream_t stream) {
+  CallTag tag_("w4_expand_weights_f6", N, K, 0);
   if (!tiles || !f6 || !aligned16(tiles) || !aligned16(f6)) return CR_ERR_INVALID_ARGUMENT;
   if (N < 128 || K < 128 || N % 128 || K % 128 || K > KMAX || N >= DIM_MAX) return CR_ERR_UNSUPPORTED_SHAPE;
   if ((N / 32) * (K / 64) * 1536 >= ((int64_t)1 << 32)) return CR_ERR_UNSUPPORTED_SHAPE;
@@ -375,6 +410,7 @@ cr_status w4_expand_weights_f6(const void* tiles, int64_t N, int64_t K, void* f6
 cr_status w4_pack_weights(const void* codes, const void* scales, const void* zeros, int64_t N, int64_t K,
                           cr_qtype qtype, cr_gran gran, int q_group, void* packed, void* packed_scales,
                           void* packed_zeros, float* w_sum, hipStream_t stream) {
+  CallTag tag_("w4_pack_weights", N, K, 0, qtype, gran, q_group);
   if (!codes || !packed || !scales) return CR_ERR_INVALID_ARGUMENT;
   if (!aligned16(codes) || !aligned16(packed) || !aligned16(scales)) return CR_ERR_INVALID_ARGUMENT;
   if ((int)qtype < 0 || (int)qtype > 3 || (int)gran < 0 || (int)gran > 2) return CR_ERR_INVALID_ARGUMENT;
@@ -439,6 +475,7 @@ cr_status w4a4_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
                     const float* w_sum, const void* lora_act, int lora_act_f32, const void* lora_up, int R,
                     const void* bias, void* out, cr_out out_type, int64_t ldc, int64_t M, int64_t N, int64_t K,
                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  CallTag tag_("w4a4_gemm", M, N, K, a_layout, w_layout, out_type);
   cr_status st = gemm_common(a_codes, w_packed, out, out_type, ldc, M, N, K, bias);
   if (st != CR_OK) return st;
   if (!a_scales || !w_scales || !aligned16(a_scales) || !aligned16(w_scales)) return CR_ERR_INVALID_ARGUMENT;
@@ -513,6 +550,7 @@ cr_status w4a8_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
                     const void* lora_act, int lora_act_f32, const void* lora_up, int R, const void* bias,
                     void* out, cr_out out_type, int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
+  CallTag tag_("w4a8_gemm", M, N, K, a_layout, a_gran, out_type);
   (void)workspace;
   (void)workspace_bytes;
   cr_status st = gemm_common(a_codes, w_packed, out, out_type, ldc, M, N, K, bias);
@@ -555,6 +593,7 @@ cr_status w4a8_gemm(const void* a_codes, cr_layout a_layout, const float* a_scal
 cr_status int8_tensorwise_gemm(const void* a_codes, const float* a_scale, const void* w, const float* w_scale,
                                const void* bias, void* out, cr_out out_type, int64_t ldc, int64_t M, int64_t N,
                                int64_t K, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  CallTag tag_("int8_tensorwise_gemm", M, N, K, out_type);
   (void)workspace;
   (void)workspace_bytes;
   cr_status st = gemm_common(a_codes, w, out, out_type, ldc, M, N, K, bias);
